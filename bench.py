@@ -1,0 +1,156 @@
+"""Benchmark of the sparse-routed gated delta-rule hot path on one MI355X.
+
+Default workload: one Sparse Delta Memory layer at the 1.4B-layer shape
+(B=1, T=8192, H=2, N=57,600 slots of d_v=960, per-half top-32, W=R=32, bf16
+inputs, fp32 table).  One step = write addressing + read addressing + the
+sparse decay/update/read recurrence over all 8192 tokens (the kernel sequence
+of sdm_forward, issued through its component entry points so that the
+recurrence kernel can be timed on its own with HIP events).
+
+Prints ONE JSON line (see the keys below).  `value` is tokens/s of the whole
+step; `roofline` reports the dominant kernel (the recurrence) against HBM
+bandwidth using the algorithmic bytes it must move; `cpu_baseline` times the
+fp64 oracle on the host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def sdm_kernel_bytes(cfg, io_bytes):
+    """Algorithmic bytes the recurrence kernel moves per launch.
+
+    Per (token, head): W rows gathered + W rows scattered + R rows gathered of
+    d_v fp32 = (2W+R)*d_v*4; v read and y written (d_v each, io dtype); alpha,
+    beta (8 B); the write/read slot lists and weights (W+R)*8.
+    """
+    per = (2 * cfg.W + cfg.R) * cfg.d_v * 4 + 2 * cfg.d_v * io_bytes + 8 + (cfg.W + cfg.R) * 8
+    return per * cfg.B * cfg.T * cfg.H, per
+
+
+def bench_sdm(args, torch, sslp, wl):
+    cfg = wl.SDM_14B
+    dev = torch.device("cuda:0")
+    x = {k: v.to(dev) for k, v in wl.sdm_inputs(cfg).items()}
+    M = torch.zeros((cfg.B, cfg.H, cfg.N, cfg.d_v), dtype=torch.float32, device=dev)
+    shp = (cfg.B, cfg.T, cfg.H)
+    iw = torch.empty(shp + (cfg.W,), dtype=torch.int32, device=dev)
+    ww = torch.empty(shp + (cfg.W,), dtype=torch.float32, device=dev)
+    ir = torch.empty(shp + (cfg.R,), dtype=torch.int32, device=dev)
+    wr = torch.empty(shp + (cfg.R,), dtype=torch.float32, device=dev)
+    y = torch.empty(shp + (cfg.d_v,), dtype=cfg.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        sslp.sdm_address(x["sw1"], x["sw2"], cfg.k_w, cfg.W, idx=iw, wt=ww)
+        sslp.sdm_address(x["sr1"], x["sr2"], cfg.k_r, cfg.R, idx=ir, wt=wr)
+        if ev is not None:
+            ev[0].record(stream)
+        sslp.sdm_sparse_update(iw, ww, ir, wr, x["v"], x["alpha"], x["beta"], M, y=y)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    k_ms = [a.elapsed_time(b) for a, b in evs]
+    k_avg_ms = sum(k_ms) / len(k_ms)
+    nbytes, per = sdm_kernel_bytes(cfg, 2 if cfg.dtype == torch.bfloat16 else 4)
+    achieved = nbytes / (k_avg_ms * 1e-3) / 1e9
+    tokens = cfg.B * cfg.T * args.steps
+    return dict(
+        cfg=cfg, ms_per_step=total_ms / args.steps, value=tokens / (total_ms * 1e-3),
+        roofline=dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                      kernel="sdm_update_kernel", kernel_avg_ms=round(k_avg_ms, 4),
+                      bytes_per_launch=nbytes, bytes_per_token_head=per))
+
+
+def cpu_baseline_sdm(wl, torch):
+    import numpy as np
+
+    import oracle
+
+    cfg = wl.SDM_14B
+    x = wl.sdm_inputs(cfg)
+    n = {k: wl.to_numpy_f32(v) for k, v in x.items()}
+    M0 = np.zeros((cfg.B, cfg.H, cfg.N, cfg.d_v))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.sdm_forward(n["sw1"], n["sw2"], n["sr1"], n["sr2"], n["v"], n["alpha"], n["beta"],
+                           M0, cfg.k_w, cfg.k_r, cfg.W, cfg.R)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or reps >= 20:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=round(cfg.B * cfg.T * reps / el, 1), unit="tokens/s", cores=threads,
+                kind="oracle",
+                sample=f"full workload ({cfg.B * cfg.T} tokens x {cfg.H} heads) repeated {reps}x, "
+                       f"{el:.1f} s; fp64 C/OpenMP oracle (addressing over all threads, "
+                       f"recurrence over the {cfg.B * cfg.H} (b,h) units)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the per-GPU shard is the single-GPU workload", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_state_linear_product_amd as sslp
+    from sparse_state_linear_product_amd import workloads as wl
+
+    r = bench_sdm(args, torch, sslp, wl)
+    cfg = r["cfg"]
+    out = {
+        "metric": "tokens/s per layer + achieved HBM GB/s (sparse update), % roofline, 1 MI355X",
+        "value": round(r["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "N": cfg.N,
+                   "d_v": cfg.d_v, "k": cfg.k_w, "W": cfg.W, "R": cfg.R, "inputs": "bf16",
+                   "state": "fp32", "residual": "shared"},
+        "roofline": r["roofline"],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_sdm(wl, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,247 @@
+/*
+ * sslp.h -- C ABI of libsslp.so: the per-token sparse-routed gated delta-rule
+ * recurrence on AMD MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * Methods (all from public reading slides; citations name the slide):
+ *   SDM  "Sparse Delta Memory: Scaling the State of Linear RNNs through Sparsity"
+ *   GDN/KDA  "Linear Attention Architectures: Mechanisms, Trade-offs, and
+ *            Cross-Layer Routing"
+ *   SSE  "Scaling Linear Attention with Sparse State Expansion"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a DEVICE pointer except the shape structs,
+ *   which are host pointers read during the call.  The caller owns all
+ *   memory (inputs, in/out states, outputs, workspace); the library never
+ *   allocates, frees or synchronises.
+ * - Each call validates its arguments on the host BEFORE any HIP call, then
+ *   enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL is
+ *   the default stream) and returns.  Results are valid once the stream has
+ *   completed.  States are updated in place in stream order.
+ * - Tensors are dense, contiguous, row-major in the layouts written next to
+ *   each argument; device pointers must be 16-byte aligned.  Inputs must not
+ *   alias outputs unless stated.  Optional outputs may be NULL.
+ * - dtype: SSLP_FP32 or SSLP_BF16.  It applies to score halves, q/k/v and the
+ *   y/o outputs.  Gates (alpha, beta, lambda, logits), weights and states are
+ *   always fp32.
+ * - Values must be finite; behaviour on NaN/Inf inputs is unspecified.
+ * - Calls on different streams may run concurrently if they touch disjoint
+ *   memory.  The only global state is a thread-local last-error string.
+ * - Return value: SSLP_OK or a negative status below; sslp_last_error()
+ *   describes the last failure on the calling thread.
+ */
+#ifndef SSLP_H
+#define SSLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSLP_VERSION 1
+
+/* status codes */
+#define SSLP_OK 0
+#define SSLP_ERR_INVALID_ARG (-1) /* NULL required pointer, bad dimension, k > sqrtN, W > k^2, misalignment */
+#define SSLP_ERR_UNSUPPORTED (-2) /* dimension outside what the kernels support */
+#define SSLP_ERR_WORKSPACE (-3)   /* workspace NULL or smaller than the *_workspace_size() value */
+#define SSLP_ERR_HIP (-4)         /* a HIP launch or runtime call failed */
+
+/* dtype */
+#define SSLP_FP32 0
+#define SSLP_BF16 1
+
+/* SDM residual form (slide "A v1 inconsistency matters for reproducing the update") */
+#define SSLP_RESIDUAL_SHARED 0   /* figure form: v_hat = sum_n wt_n M~[i_n] shared by every slot (default) */
+#define SSLP_RESIDUAL_PER_SLOT 1 /* Eq. (4) as printed: residual v - M~[i] per slot */
+
+/* GDN/KDA decay granularity (slide "GDN and KDA change the granularity of forgetting") */
+#define SSLP_DECAY_SCALAR 0  /* Gated DeltaNet: one alpha per (b,t,h) */
+#define SSLP_DECAY_CHANNEL 1 /* Kimi Delta Attention: one alpha per (b,t,h,key channel) */
+
+/* ------------------------------------------------------------------------ */
+/* Sparse Delta Memory                                                       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * SDM problem shape.  N = sqrtN * sqrtN slots per (sequence, head); slot of
+ * the pair (a, b) is a*sqrtN + b with a indexing half 1.
+ *   B, T, H  batch, tokens, heads (>= 1; T may be 0 for a no-op, in which case
+ *            only M is required and the per-token pointers may be NULL)
+ *   sqrtN    length of each score half, 1..1024
+ *   d_v      value width, multiple of 4, <= 4096
+ *   k_w, k_r per-half top-k for writes / reads, 1..min(sqrtN, 64)
+ *   W, R     write / read budgets, 1..min(k^2, 128)
+ */
+typedef struct {
+    int B, T, H, sqrtN, d_v, k_w, k_r, W, R;
+} sslp_sdm_shape;
+
+/* Bytes of device workspace sdm_forward / sdm_sparse_update need (0 on bad shape). */
+size_t sdm_workspace_size(const sslp_sdm_shape* shape);
+
+/*
+ * sdm_forward -- product-key addressing for writes and reads, then the sparse
+ * decay / delta update / read-after-write recurrence over T tokens.
+ *
+ * Slides: "Product keys select addresses without scoring every slot" (steps
+ * 1-4: per-half top-k, k^2 candidate sums, top-W / top-R, softmax over the
+ * selected scores) and "Selected slots decay and update; other slots
+ * persist" Eqs. (3)-(5); residual per `residual_mode` (see above).
+ * Per token t, head h:  M~[i] = alpha_t M[i] for i in I^w_t only;
+ *   SHARED:   M[i_n] = M~[i_n] + beta_t wt_n (v_t - sum_m wt_m M~[i_m])
+ *   PER_SLOT: M[i_n] = M~[i_n] + beta_t wt_n (v_t - M~[i_n])
+ *   y_t = sum_m wt^r_m M[j_m]   (table after the write)
+ * Rows outside I^w_t are never written.  Ranking is (fp32 score desc, index
+ * asc) at both stages, the candidate score being the fp32 sum s1[a] + s2[b];
+ * -0 and +0 tie.  Indices are returned in rank order.
+ *
+ *   sw1, sw2  [B,T,H,sqrtN] dtype  write-address score halves
+ *   sr1, sr2  [B,T,H,sqrtN] dtype  read-address score halves (may alias sw1, sw2)
+ *   v         [B,T,H,d_v]   dtype  values
+ *   alpha     [B,T,H]       fp32   forget gate
+ *   beta      [B,T,H]       fp32   input gate
+ *   M         [B,H,N,d_v]   fp32   table, updated in place
+ *   y         [B,T,H,d_v]   dtype  reads (out)
+ *   idx_w, wt_w [B,T,H,W]   int32 / fp32  optional copies of the write addressing
+ *   idx_r, wt_r [B,T,H,R]   int32 / fp32  optional copies of the read addressing
+ *   workspace, ws_bytes     >= sdm_workspace_size(shape) bytes of device memory
+ */
+int sdm_forward(const sslp_sdm_shape* shape, int dtype, int residual_mode, const void* sw1,
+                const void* sw2, const void* sr1, const void* sr2, const void* v,
+                const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
+                float* wt_w, int32_t* idx_r, float* wt_r, void* workspace, size_t ws_bytes,
+                void* stream);
+
+/*
+ * sdm_decode_step -- one token for each of B independent sequences (shape->T
+ * must be 1): addressing, update and read of each sequence's own table.  Same
+ * arithmetic as sdm_forward with T = 1 (Sparse Delta Memory slides, same
+ * passages; decode is the use named on slide "Sparse arithmetic still pays
+ * for random memory access").
+ *   sw1, sw2, sr1, sr2 [B,H,sqrtN] dtype;  v [B,H,d_v] dtype;  alpha, beta [B,H] fp32;
+ *   M [B,H,N,d_v] fp32 in/out;  y [B,H,d_v] dtype out;
+ *   idx_w, wt_w [B,H,W] and idx_r, wt_r [B,H,R] optional outputs.
+ *   workspace, ws_bytes >= sdm_decode_workspace_size(shape) (may be NULL if that is 0).
+ */
+size_t sdm_decode_workspace_size(const sslp_sdm_shape* shape);
+int sdm_decode_step(const sslp_sdm_shape* shape, int dtype, int residual_mode, const void* sw1,
+                    const void* sw2, const void* sr1, const void* sr2, const void* v,
+                    const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
+                    float* wt_w, int32_t* idx_r, float* wt_r, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * sdm_address -- the addressing step alone (slide "Product keys select
+ * addresses without scoring every slot"), for B*T*H problems of the shape.
+ *   s1, s2 [B,T,H,sqrtN] dtype;  k per-half top-k;  budget 1..min(k^2,128);
+ *   idx [B,T,H,budget] int32 out (rank order);  wt [B,T,H,budget] fp32 out.
+ * The shape's k_w/k_r/W/R fields are ignored.
+ */
+int sdm_address(const sslp_sdm_shape* shape, int dtype, const void* s1, const void* s2, int k,
+                int budget, int32_t* idx, float* wt, void* stream);
+
+/*
+ * sdm_sparse_update -- the recurrence alone, given caller-supplied addressing
+ * (slides "Selected slots decay and update; other slots persist" Eqs.
+ * (3)-(5) and "A v1 inconsistency ...").  Weights are used as given (any
+ * sign, no normalisation), so with W = R = N, wt_w = k_t, wt_r = q_t and the
+ * shared residual it computes the dense gated delta rule.
+ *   idx_w [B,T,H,W] int32 slots in [0,N), DISTINCT within each token
+ *         (duplicates give unspecified results);  wt_w [B,T,H,W] fp32;
+ *   idx_r [B,T,H,R] int32 in [0,N);  wt_r [B,T,H,R] fp32;
+ *   v, alpha, beta, M, y as in sdm_forward;  shape->k_w, k_r are ignored and
+ *   W, R may be up to 128 regardless of k.
+ *   workspace, ws_bytes >= sdm_workspace_size(shape).
+ * Indices outside [0,N) are rejected only if detected on the host, which is
+ * never: the caller must guarantee the range.
+ */
+int sdm_sparse_update(const sslp_sdm_shape* shape, int dtype, int residual_mode,
+                      const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
+                      const float* wt_r, const void* v, const float* alpha, const float* beta,
+                      float* M, void* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Gated DeltaNet / Kimi Delta Attention (dense limit: every slot selected)  */
+/* ------------------------------------------------------------------------ */
+
+/*   B, T, H; d_k = d_v = 128 (other sizes SSLP_ERR_UNSUPPORTED); chunk = 64. */
+typedef struct {
+    int B, T, H, d_k, d_v, chunk;
+} sslp_gdn_shape;
+
+size_t gdn_workspace_size(const sslp_gdn_shape* shape);
+
+/*
+ * gdn_chunk_forward -- chunked forward of the gated delta rule (slides "GDN
+ * and KDA change the granularity of forgetting", Eqs. 15-20, and "DeltaNet
+ * writes a correction to the current association", Eq. 14).  With the state
+ * S = W^T of shape [d_k, d_v] (row = key channel), per token:
+ *   S~ = alpha_t S (SCALAR) or Diag(alpha_t) S (CHANNEL);
+ *   S  = S~ + beta_t k_t (v_t - S~^T k_t)^T;   o_t = S^T q_t (after the write).
+ * No query scaling and no key normalisation inside (the caller normalises).
+ *   q, k  [B,T,H,d_k] dtype;  v [B,T,H,d_v] dtype;
+ *   alpha [B,T,H] fp32 (SCALAR) or [B,T,H,d_k] fp32 (CHANNEL), in (0,1];
+ *   beta  [B,T,H] fp32;
+ *   S0    [B,H,d_k,d_v] fp32 initial state, or NULL for zeros;
+ *   S_out [B,H,d_k,d_v] fp32 final state (may alias S0);
+ *   o     [B,T,H,d_v] dtype out.
+ *   workspace, ws_bytes >= gdn_workspace_size(shape) (may be NULL if that is 0).
+ */
+int gdn_chunk_forward(const sslp_gdn_shape* shape, int dtype, int decay_mode, const void* q,
+                      const void* k, const void* v, const float* alpha, const float* beta,
+                      const float* S0, float* S_out, void* o, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sparse State Expansion                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*   B, T, H; N routed partitions 1..64 plus one shared; topk 1..min(N,8);
+ *   c = d = 128 (other sizes SSLP_ERR_UNSUPPORTED); chunk = 64. */
+typedef struct {
+    int B, T, H, N, topk, c, d, chunk;
+} sslp_sse_shape;
+
+size_t sse_workspace_size(const sslp_sse_shape* shape);
+
+/*
+ * sse_forward -- gated top-k partition routing, then the GLA recurrence of
+ * each visited partition with decay advancing only on visits, plus the
+ * always-active shared partition (slides "One gate controls both writes and
+ * reads" Eqs. (9)-(14), "A memory decays only when its partition is
+ * visited", "Varlen groups tokens while preserving causal order", backup
+ * "Selected gate mass is usually below one").  Per token:
+ *   e = softmax(logits_t) over N;  T_t = top-k of the logits (ties -> lowest index);
+ *   S^i = Diag(lambda_t) S^i + e_i k_t^T v_t  for i in T_t (others untouched);
+ *   S^N = Diag(lambda_t) S^N + k_sh_t^T v_t   (shared partition, every token);
+ *   o_t = sum_{i in T_t, rank order} e_i q_t S^i + q_sh_t S^N.
+ * The selected gate values are not renormalised.
+ *   gate_logits [B,T,H,N] fp32;
+ *   q, k [B,T,H,c] dtype (k already softmax-normalised over c by the caller);
+ *   v [B,T,H,d] dtype;  lambda [B,T,H,c] fp32 in (0,1];
+ *   q_sh, k_sh [B,T,H,c] dtype or NULL (then q, k are used);
+ *   S [B,H,N+1,c,d] fp32 states in/out (index N = shared partition);
+ *   o [B,T,H,d] dtype out;  sel [B,T,H,topk] int32 and e_sel [B,T,H,topk] fp32 optional.
+ *   workspace, ws_bytes >= sse_workspace_size(shape).
+ */
+int sse_forward(const sslp_sse_shape* shape, int dtype, const float* gate_logits, const void* q,
+                const void* k, const void* v, const float* lambda, const void* q_sh,
+                const void* k_sh, float* S, void* o, int32_t* sel, float* e_sel, void* workspace,
+                size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* utilities                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* sslp_last_error(void);
+/* SSLP_VERSION of the built library. */
+int sslp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSLP_H */

@@ -1,0 +1,255 @@
+"""Sparse-routed gated delta-rule recurrence on AMD MI355X (gfx950).
+
+Thin Python binding over libsslp.so (include/sslp.h).  Each function takes
+torch tensors that already live on the GPU, checks their dtype, shape and
+contiguity, and passes raw device pointers plus the current HIP stream to the
+C function of the same name; every step of the computation runs in the HIP
+kernels.  PyTorch provides device memory and streams only.  Workspaces are
+allocated with torch when the caller does not pass one.
+
+Functions (see include/sslp.h for the exact semantics):
+  sdm_forward, sdm_decode_step, sdm_address, sdm_sparse_update   Sparse Delta Memory
+  gdn_chunk_forward                                              Gated DeltaNet / KDA
+  sse_forward                                                    Sparse State Expansion
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (DECAY_CHANNEL, DECAY_SCALAR, RESIDUAL_PER_SLOT, RESIDUAL_SHARED, GdnShape,
+                   SdmShape, SseShape, SslpError, check, lib)
+
+__all__ = ["sdm_forward", "sdm_decode_step", "sdm_address", "sdm_sparse_update",
+           "gdn_chunk_forward", "sse_forward", "SslpError", "RESIDUAL_SHARED",
+           "RESIDUAL_PER_SLOT", "DECAY_SCALAR", "DECAY_CHANNEL", "version"]
+
+
+def version():
+    return lib().sslp_version()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return _lib.SSLP_FP32
+    if t.dtype == torch.bfloat16:
+        return _lib.SSLP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes, workspace, device):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace must hold {nbytes} bytes")
+        return workspace, workspace.numel() * workspace.element_size()
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+# ---------------------------------------------------------------------------
+# Sparse Delta Memory
+# ---------------------------------------------------------------------------
+def sdm_shape(B, T, H, sqrtN, d_v, k_w, k_r, W, R):
+    return SdmShape(B, T, H, sqrtN, d_v, k_w, k_r, W, R)
+
+
+def sdm_workspace_size(shape):
+    return lib().sdm_workspace_size(ctypes.byref(shape))
+
+
+def sdm_forward(sw1, sw2, sr1, sr2, v, alpha, beta, M, k_w, k_r, W, R, y=None,
+                residual_mode=RESIDUAL_SHARED, idx_w=None, wt_w=None, idx_r=None, wt_r=None,
+                workspace=None, stream=None):
+    """Addressing + recurrence over T tokens; M [B,H,N,d_v] fp32 is updated in place.
+
+    sw1, sw2, sr1, sr2: [B,T,H,sqrtN]; v: [B,T,H,d_v] (same dtype); alpha, beta: [B,T,H]
+    fp32.  Returns y [B,T,H,d_v] (allocated if not given)."""
+    B, T, H, sqrt_n = sw1.shape
+    d_v = v.shape[-1]
+    dt = sw1.dtype
+    for name, t in (("sw2", sw2), ("sr1", sr1), ("sr2", sr2)):
+        _need(t, dt, (B, T, H, sqrt_n), name)
+    _need(v, dt, (B, T, H, d_v), "v")
+    _need(alpha, torch.float32, (B, T, H), "alpha")
+    _need(beta, torch.float32, (B, T, H), "beta")
+    _need(M, torch.float32, (B, H, sqrt_n * sqrt_n, d_v), "M")
+    if y is None:
+        y = torch.empty((B, T, H, d_v), dtype=dt, device=v.device)
+    _need(y, dt, (B, T, H, d_v), "y")
+    shape = sdm_shape(B, T, H, sqrt_n, d_v, k_w, k_r, W, R)
+    ws, nbytes = _workspace(lib().sdm_workspace_size(ctypes.byref(shape)), workspace, v.device)
+    rc = lib().sdm_forward(ctypes.byref(shape), _dtype_code(sw1), int(residual_mode), _ptr(sw1),
+                           _ptr(sw2), _ptr(sr1), _ptr(sr2), _ptr(v), _ptr(alpha), _ptr(beta),
+                           _ptr(M), _ptr(y), _ptr(idx_w), _ptr(wt_w), _ptr(idx_r), _ptr(wt_r),
+                           _ptr(ws), nbytes, _stream(stream))
+    check("sdm_forward", rc)
+    return y
+
+
+def sdm_decode_step(sw1, sw2, sr1, sr2, v, alpha, beta, M, k_w, k_r, W, R, y=None,
+                    residual_mode=RESIDUAL_SHARED, idx_w=None, wt_w=None, idx_r=None, wt_r=None,
+                    workspace=None, stream=None):
+    """One token for each of B sequences.  sw*, sr*: [B,H,sqrtN]; v: [B,H,d_v];
+    alpha, beta: [B,H]; M: [B,H,N,d_v] fp32 in place.  Returns y [B,H,d_v]."""
+    B, H, sqrt_n = sw1.shape
+    d_v = v.shape[-1]
+    dt = sw1.dtype
+    for name, t in (("sw2", sw2), ("sr1", sr1), ("sr2", sr2)):
+        _need(t, dt, (B, H, sqrt_n), name)
+    _need(v, dt, (B, H, d_v), "v")
+    _need(alpha, torch.float32, (B, H), "alpha")
+    _need(beta, torch.float32, (B, H), "beta")
+    _need(M, torch.float32, (B, H, sqrt_n * sqrt_n, d_v), "M")
+    if y is None:
+        y = torch.empty((B, H, d_v), dtype=dt, device=v.device)
+    _need(y, dt, (B, H, d_v), "y")
+    shape = sdm_shape(B, 1, H, sqrt_n, d_v, k_w, k_r, W, R)
+    ws, nbytes = _workspace(lib().sdm_decode_workspace_size(ctypes.byref(shape)), workspace,
+                           v.device)
+    rc = lib().sdm_decode_step(ctypes.byref(shape), _dtype_code(sw1), int(residual_mode),
+                               _ptr(sw1), _ptr(sw2), _ptr(sr1), _ptr(sr2), _ptr(v), _ptr(alpha),
+                               _ptr(beta), _ptr(M), _ptr(y), _ptr(idx_w), _ptr(wt_w), _ptr(idx_r),
+                               _ptr(wt_r), _ptr(ws), nbytes, _stream(stream))
+    check("sdm_decode_step", rc)
+    return y
+
+
+def sdm_address(s1, s2, k, budget, idx=None, wt=None, stream=None):
+    """Product-key addressing alone.  s1, s2: [B,T,H,sqrtN].  Returns (idx, wt)."""
+    B, T, H, sqrt_n = s1.shape
+    _need(s2, s1.dtype, s1.shape, "s2")
+    if idx is None:
+        idx = torch.empty((B, T, H, budget), dtype=torch.int32, device=s1.device)
+    if wt is None:
+        wt = torch.empty((B, T, H, budget), dtype=torch.float32, device=s1.device)
+    _need(idx, torch.int32, (B, T, H, budget), "idx")
+    _need(wt, torch.float32, (B, T, H, budget), "wt")
+    shape = sdm_shape(B, T, H, sqrt_n, 1, 1, 1, 1, 1)
+    rc = lib().sdm_address(ctypes.byref(shape), _dtype_code(s1), _ptr(s1), _ptr(s2), int(k),
+                           int(budget), _ptr(idx), _ptr(wt), _stream(stream))
+    check("sdm_address", rc)
+    return idx, wt
+
+
+def sdm_sparse_update(idx_w, wt_w, idx_r, wt_r, v, alpha, beta, M, y=None,
+                      residual_mode=RESIDUAL_SHARED, workspace=None, stream=None):
+    """The recurrence alone with caller-supplied addressing (raw weights)."""
+    B, T, H, W = idx_w.shape
+    R = idx_r.shape[-1]
+    d_v = v.shape[-1]
+    N = M.shape[2]
+    sqrt_n = int(round(N ** 0.5))
+    if sqrt_n * sqrt_n != N:
+        raise ValueError("M.shape[2] must be a perfect square")
+    _need(idx_w, torch.int32, (B, T, H, W), "idx_w")
+    _need(wt_w, torch.float32, (B, T, H, W), "wt_w")
+    _need(idx_r, torch.int32, (B, T, H, R), "idx_r")
+    _need(wt_r, torch.float32, (B, T, H, R), "wt_r")
+    _need(alpha, torch.float32, (B, T, H), "alpha")
+    _need(beta, torch.float32, (B, T, H), "beta")
+    _need(M, torch.float32, (B, H, N, d_v), "M")
+    if y is None:
+        y = torch.empty((B, T, H, d_v), dtype=v.dtype, device=v.device)
+    _need(y, v.dtype, (B, T, H, d_v), "y")
+    shape = sdm_shape(B, T, H, sqrt_n, d_v, 1, 1, W, R)
+    ws, nbytes = _workspace(lib().sdm_workspace_size(ctypes.byref(shape)), workspace, v.device)
+    rc = lib().sdm_sparse_update(ctypes.byref(shape), _dtype_code(v), int(residual_mode),
+                                 _ptr(idx_w), _ptr(wt_w), _ptr(idx_r), _ptr(wt_r), _ptr(v),
+                                 _ptr(alpha), _ptr(beta), _ptr(M), _ptr(y), _ptr(ws), nbytes,
+                                 _stream(stream))
+    check("sdm_sparse_update", rc)
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet / KDA
+# ---------------------------------------------------------------------------
+def gdn_chunk_forward(q, k, v, alpha, beta, S0=None, S_out=None, o=None, decay_mode=None,
+                      chunk=64, workspace=None, stream=None):
+    """q, k: [B,T,H,d_k]; v: [B,T,H,d_v]; alpha [B,T,H] (GDN) or [B,T,H,d_k] (KDA) fp32;
+    beta [B,T,H] fp32; S0 [B,H,d_k,d_v] fp32 or None.  Returns (o, S_out)."""
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dt = q.dtype
+    _need(k, dt, (B, T, H, d_k), "k")
+    _need(v, dt, (B, T, H, d_v), "v")
+    if decay_mode is None:
+        decay_mode = DECAY_CHANNEL if alpha.dim() == 4 else DECAY_SCALAR
+    ashape = (B, T, H, d_k) if decay_mode == DECAY_CHANNEL else (B, T, H)
+    _need(alpha, torch.float32, ashape, "alpha")
+    _need(beta, torch.float32, (B, T, H), "beta")
+    if S0 is not None:
+        _need(S0, torch.float32, (B, H, d_k, d_v), "S0")
+    if S_out is None:
+        S_out = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device)
+    _need(S_out, torch.float32, (B, H, d_k, d_v), "S_out")
+    if o is None:
+        o = torch.empty((B, T, H, d_v), dtype=dt, device=q.device)
+    _need(o, dt, (B, T, H, d_v), "o")
+    shape = GdnShape(B, T, H, d_k, d_v, chunk)
+    ws, nbytes = _workspace(lib().gdn_workspace_size(ctypes.byref(shape)), workspace, q.device)
+    rc = lib().gdn_chunk_forward(ctypes.byref(shape), _dtype_code(q), int(decay_mode), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(S_out),
+                                 _ptr(o), _ptr(ws), nbytes, _stream(stream))
+    check("gdn_chunk_forward", rc)
+    return o, S_out
+
+
+# ---------------------------------------------------------------------------
+# Sparse State Expansion
+# ---------------------------------------------------------------------------
+def sse_forward(gate_logits, q, k, v, lam, S, topk, q_sh=None, k_sh=None, o=None, sel=None,
+                e_sel=None, chunk=64, workspace=None, stream=None):
+    """gate_logits [B,T,H,N] fp32; q, k [B,T,H,c]; v [B,T,H,d]; lam [B,T,H,c] fp32;
+    S [B,H,N+1,c,d] fp32 updated in place.  Returns o [B,T,H,d]."""
+    B, T, H, N = gate_logits.shape
+    c, d = q.shape[-1], v.shape[-1]
+    dt = q.dtype
+    _need(gate_logits, torch.float32, (B, T, H, N), "gate_logits")
+    _need(k, dt, (B, T, H, c), "k")
+    _need(v, dt, (B, T, H, d), "v")
+    _need(lam, torch.float32, (B, T, H, c), "lam")
+    _need(S, torch.float32, (B, H, N + 1, c, d), "S")
+    if q_sh is not None:
+        _need(q_sh, dt, (B, T, H, c), "q_sh")
+    if k_sh is not None:
+        _need(k_sh, dt, (B, T, H, c), "k_sh")
+    if o is None:
+        o = torch.empty((B, T, H, d), dtype=dt, device=q.device)
+    _need(o, dt, (B, T, H, d), "o")
+    if sel is not None:
+        _need(sel, torch.int32, (B, T, H, topk), "sel")
+    if e_sel is not None:
+        _need(e_sel, torch.float32, (B, T, H, topk), "e_sel")
+    shape = SseShape(B, T, H, N, topk, c, d, chunk)
+    ws, nbytes = _workspace(lib().sse_workspace_size(ctypes.byref(shape)), workspace, q.device)
+    rc = lib().sse_forward(ctypes.byref(shape), _dtype_code(q), _ptr(gate_logits), _ptr(q),
+                           _ptr(k), _ptr(v), _ptr(lam), _ptr(q_sh), _ptr(k_sh), _ptr(S), _ptr(o),
+                           _ptr(sel), _ptr(e_sel), _ptr(ws), nbytes, _stream(stream))
+    check("sse_forward", rc)
+    return o

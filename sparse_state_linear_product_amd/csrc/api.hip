@@ -1,0 +1,354 @@
+// C ABI of libsslp.so (declared in include/sslp.h): argument validation on the
+// host, workspace carving, and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/sslp.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return SSLP_OK;
+    return fail(SSLP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+#define REQUIRE(cond, code, ...)                      \
+    do {                                              \
+        if (!(cond)) return fail((code), __VA_ARGS__); \
+    } while (0)
+
+#define REQUIRE_PTR(p)                                                                    \
+    do {                                                                                  \
+        REQUIRE((p) != nullptr, SSLP_ERR_INVALID_ARG, "%s must not be NULL", #p);        \
+        REQUIRE(aligned16(p), SSLP_ERR_INVALID_ARG, "%s must be 16-byte aligned", #p);   \
+    } while (0)
+
+#define REQUIRE_ALIGNED(p) \
+    REQUIRE(aligned16(p), SSLP_ERR_INVALID_ARG, "%s must be 16-byte aligned", #p)
+
+constexpr int kMaxSqrtN = 1024;
+constexpr int kMaxTopK = 64;
+constexpr int kMaxBudget = 128;
+constexpr int kMaxDv = 4096;
+
+// checks shared by every SDM entry point; `need_k` checks k_w/k_r and W<=k^2
+int check_sdm_shape(const sslp_sdm_shape* s, bool need_k) {
+    REQUIRE(s != nullptr, SSLP_ERR_INVALID_ARG, "shape must not be NULL");
+    REQUIRE(s->B >= 1 && s->H >= 1 && s->T >= 0, SSLP_ERR_INVALID_ARG,
+            "B, H must be >= 1 and T >= 0 (B=%d T=%d H=%d)", s->B, s->T, s->H);
+    REQUIRE(s->sqrtN >= 1, SSLP_ERR_INVALID_ARG, "sqrtN must be >= 1 (got %d)", s->sqrtN);
+    REQUIRE(s->sqrtN <= kMaxSqrtN, SSLP_ERR_UNSUPPORTED, "sqrtN %d > %d", s->sqrtN, kMaxSqrtN);
+    REQUIRE(s->d_v >= 1, SSLP_ERR_INVALID_ARG, "d_v must be >= 1 (got %d)", s->d_v);
+    REQUIRE(s->d_v % 4 == 0 && s->d_v <= kMaxDv, SSLP_ERR_UNSUPPORTED,
+            "d_v must be a multiple of 4 and <= %d (got %d)", kMaxDv, s->d_v);
+    REQUIRE(s->W >= 1 && s->R >= 1, SSLP_ERR_INVALID_ARG, "W, R must be >= 1 (W=%d R=%d)", s->W,
+            s->R);
+    REQUIRE(s->W <= kMaxBudget && s->R <= kMaxBudget, SSLP_ERR_UNSUPPORTED,
+            "W, R must be <= %d (W=%d R=%d)", kMaxBudget, s->W, s->R);
+    const long long N = (long long)s->sqrtN * s->sqrtN;
+    REQUIRE(s->W <= N && s->R <= N, SSLP_ERR_INVALID_ARG, "W, R must be <= N=%lld", N);
+    if (need_k) {
+        REQUIRE(s->k_w >= 1 && s->k_r >= 1, SSLP_ERR_INVALID_ARG, "k_w, k_r must be >= 1");
+        REQUIRE(s->k_w <= s->sqrtN && s->k_r <= s->sqrtN, SSLP_ERR_INVALID_ARG,
+                "k_w, k_r must be <= sqrtN (k_w=%d k_r=%d sqrtN=%d)", s->k_w, s->k_r, s->sqrtN);
+        REQUIRE(s->k_w <= kMaxTopK && s->k_r <= kMaxTopK, SSLP_ERR_UNSUPPORTED,
+                "k_w, k_r must be <= %d", kMaxTopK);
+        REQUIRE(s->W <= s->k_w * s->k_w, SSLP_ERR_INVALID_ARG, "W=%d > k_w^2=%d", s->W,
+                s->k_w * s->k_w);
+        REQUIRE(s->R <= s->k_r * s->k_r, SSLP_ERR_INVALID_ARG, "R=%d > k_r^2=%d", s->R,
+                s->k_r * s->k_r);
+    }
+    return SSLP_OK;
+}
+
+int check_dtype(int dtype) {
+    REQUIRE(dtype == SSLP_FP32 || dtype == SSLP_BF16, SSLP_ERR_INVALID_ARG,
+            "dtype must be SSLP_FP32 or SSLP_BF16 (got %d)", dtype);
+    return SSLP_OK;
+}
+
+size_t addressing_bytes(const sslp_sdm_shape* s, int T) {
+    const size_t bth = (size_t)s->B * T * s->H;
+    return align_up(bth * s->W * 4) * 2 + align_up(bth * s->R * 4) * 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sslp_last_error(void) { return g_err; }
+int sslp_version(void) { return SSLP_VERSION; }
+
+size_t sdm_workspace_size(const sslp_sdm_shape* s) {
+    if (check_sdm_shape(s, false) != SSLP_OK) return 0;
+    return addressing_bytes(s, s->T);
+}
+
+size_t sdm_decode_workspace_size(const sslp_sdm_shape* s) {
+    if (check_sdm_shape(s, false) != SSLP_OK) return 0;
+    return addressing_bytes(s, 1);
+}
+
+int sdm_address(const sslp_sdm_shape* s, int dtype, const void* s1, const void* s2, int k,
+                int budget, int32_t* idx, float* wt, void* stream) {
+    g_err[0] = 0;
+    REQUIRE(s != nullptr, SSLP_ERR_INVALID_ARG, "shape must not be NULL");
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE(s->B >= 1 && s->H >= 1 && s->T >= 0, SSLP_ERR_INVALID_ARG, "bad B/T/H");
+    REQUIRE(s->sqrtN >= 1, SSLP_ERR_INVALID_ARG, "sqrtN must be >= 1");
+    REQUIRE(s->sqrtN <= kMaxSqrtN, SSLP_ERR_UNSUPPORTED, "sqrtN %d > %d", s->sqrtN, kMaxSqrtN);
+    REQUIRE(k >= 1 && k <= s->sqrtN, SSLP_ERR_INVALID_ARG, "k must be in [1, sqrtN] (got %d)", k);
+    REQUIRE(k <= kMaxTopK, SSLP_ERR_UNSUPPORTED, "k must be <= %d", kMaxTopK);
+    REQUIRE(budget >= 1 && budget <= k * k, SSLP_ERR_INVALID_ARG,
+            "budget must be in [1, k^2] (got %d)", budget);
+    REQUIRE(budget <= kMaxBudget, SSLP_ERR_UNSUPPORTED, "budget must be <= %d", kMaxBudget);
+    REQUIRE_PTR(s1);
+    REQUIRE_PTR(s2);
+    REQUIRE_PTR(idx);
+    REQUIRE_PTR(wt);
+    const long long P = (long long)s->B * s->T * s->H;
+    REQUIRE(P < (1ll << 31), SSLP_ERR_UNSUPPORTED, "too many problems");
+    hipStream_t st = (hipStream_t)stream;
+    return hip_status(sslp::launch_sdm_address((int)P, s->sqrtN, dtype, s1, s2, k, budget, idx, wt,
+                                               st),
+                      "sdm_address launch");
+}
+
+int sdm_sparse_update(const sslp_sdm_shape* s, int dtype, int residual_mode, const int32_t* idx_w,
+                      const float* wt_w, const int32_t* idx_r, const float* wt_r, const void* v,
+                      const float* alpha, const float* beta, float* M, void* y, void* workspace,
+                      size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_sdm_shape(s, false)) return rc;
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE(residual_mode == SSLP_RESIDUAL_SHARED || residual_mode == SSLP_RESIDUAL_PER_SLOT,
+            SSLP_ERR_INVALID_ARG, "residual_mode must be 0 or 1 (got %d)", residual_mode);
+    REQUIRE_PTR(M);
+    REQUIRE_ALIGNED(workspace);
+    if (s->T == 0) return SSLP_OK;  // per-token tensors are empty (and may be NULL)
+    REQUIRE_PTR(idx_w);
+    REQUIRE_PTR(wt_w);
+    REQUIRE_PTR(idx_r);
+    REQUIRE_PTR(wt_r);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(alpha);
+    REQUIRE_PTR(beta);
+    REQUIRE_PTR(y);
+    const size_t need = sdm_workspace_size(s);
+    REQUIRE(ws_bytes >= need && (need == 0 || workspace != nullptr), SSLP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if (s->T == 0) return SSLP_OK;
+    sslp::SdmUpdateArgs a{};
+    a.B = s->B;
+    a.T = s->T;
+    a.H = s->H;
+    a.N = s->sqrtN * s->sqrtN;
+    a.dv = s->d_v;
+    a.W = s->W;
+    a.R = s->R;
+    a.dtype = dtype;
+    a.residual_mode = residual_mode;
+    a.idx_w = idx_w;
+    a.wt_w = wt_w;
+    a.idx_r = idx_r;
+    a.wt_r = wt_r;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.M = M;
+    a.y = y;
+    return hip_status(sslp::launch_sdm_update(a, (hipStream_t)stream), "sdm update launch");
+}
+
+static int sdm_run(const sslp_sdm_shape* s, int T, int dtype, int residual_mode, const void* sw1,
+                   const void* sw2, const void* sr1, const void* sr2, const void* v,
+                   const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
+                   float* wt_w, int32_t* idx_r, float* wt_r, void* workspace, size_t ws_bytes,
+                   size_t need, void* stream) {
+    if (int rc = check_sdm_shape(s, true)) return rc;
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE(residual_mode == SSLP_RESIDUAL_SHARED || residual_mode == SSLP_RESIDUAL_PER_SLOT,
+            SSLP_ERR_INVALID_ARG, "residual_mode must be 0 or 1 (got %d)", residual_mode);
+    REQUIRE_PTR(M);
+    if (T == 0) return SSLP_OK;  // per-token tensors are empty (and may be NULL)
+    REQUIRE_PTR(sw1);
+    REQUIRE_PTR(sw2);
+    REQUIRE_PTR(sr1);
+    REQUIRE_PTR(sr2);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(alpha);
+    REQUIRE_PTR(beta);
+    REQUIRE_PTR(y);
+    REQUIRE_ALIGNED(idx_w);
+    REQUIRE_ALIGNED(wt_w);
+    REQUIRE_ALIGNED(idx_r);
+    REQUIRE_ALIGNED(wt_r);
+    REQUIRE_ALIGNED(workspace);
+    REQUIRE(ws_bytes >= need && (need == 0 || workspace != nullptr), SSLP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    const long long P = (long long)s->B * T * s->H;
+    REQUIRE(P < (1ll << 31), SSLP_ERR_UNSUPPORTED, "too many problems");
+    // addressing outputs: caller buffers when given, else workspace
+    char* ws = static_cast<char*>(workspace);
+    const size_t bw = align_up((size_t)P * s->W * 4), br = align_up((size_t)P * s->R * 4);
+    int32_t* iw = idx_w ? idx_w : reinterpret_cast<int32_t*>(ws);
+    float* ww = wt_w ? wt_w : reinterpret_cast<float*>(ws + bw);
+    int32_t* ir = idx_r ? idx_r : reinterpret_cast<int32_t*>(ws + 2 * bw);
+    float* wr = wt_r ? wt_r : reinterpret_cast<float*>(ws + 2 * bw + br);
+    hipStream_t st = (hipStream_t)stream;
+    if (int rc = hip_status(
+            sslp::launch_sdm_address((int)P, s->sqrtN, dtype, sw1, sw2, s->k_w, s->W, iw, ww, st),
+            "sdm write addressing launch"))
+        return rc;
+    if (int rc = hip_status(
+            sslp::launch_sdm_address((int)P, s->sqrtN, dtype, sr1, sr2, s->k_r, s->R, ir, wr, st),
+            "sdm read addressing launch"))
+        return rc;
+    sslp::SdmUpdateArgs a{};
+    a.B = s->B;
+    a.T = T;
+    a.H = s->H;
+    a.N = s->sqrtN * s->sqrtN;
+    a.dv = s->d_v;
+    a.W = s->W;
+    a.R = s->R;
+    a.dtype = dtype;
+    a.residual_mode = residual_mode;
+    a.idx_w = iw;
+    a.wt_w = ww;
+    a.idx_r = ir;
+    a.wt_r = wr;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.M = M;
+    a.y = y;
+    return hip_status(sslp::launch_sdm_update(a, st), "sdm update launch");
+}
+
+int sdm_forward(const sslp_sdm_shape* s, int dtype, int residual_mode, const void* sw1,
+                const void* sw2, const void* sr1, const void* sr2, const void* v,
+                const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
+                float* wt_w, int32_t* idx_r, float* wt_r, void* workspace, size_t ws_bytes,
+                void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_sdm_shape(s, true)) return rc;
+    return sdm_run(s, s->T, dtype, residual_mode, sw1, sw2, sr1, sr2, v, alpha, beta, M, y, idx_w,
+                   wt_w, idx_r, wt_r, workspace, ws_bytes, sdm_workspace_size(s), stream);
+}
+
+int sdm_decode_step(const sslp_sdm_shape* s, int dtype, int residual_mode, const void* sw1,
+                    const void* sw2, const void* sr1, const void* sr2, const void* v,
+                    const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
+                    float* wt_w, int32_t* idx_r, float* wt_r, void* workspace, size_t ws_bytes,
+                    void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_sdm_shape(s, true)) return rc;
+    REQUIRE(s->T == 1, SSLP_ERR_INVALID_ARG, "sdm_decode_step needs shape->T == 1 (got %d)", s->T);
+    return sdm_run(s, 1, dtype, residual_mode, sw1, sw2, sr1, sr2, v, alpha, beta, M, y, idx_w,
+                   wt_w, idx_r, wt_r, workspace, ws_bytes, sdm_decode_workspace_size(s), stream);
+}
+
+// ---------------------------------------------------------------------------
+// GDN / KDA and SSE: argument checks (kernels follow)
+// ---------------------------------------------------------------------------
+static int check_gdn_shape(const sslp_gdn_shape* s) {
+    REQUIRE(s != nullptr, SSLP_ERR_INVALID_ARG, "shape must not be NULL");
+    REQUIRE(s->B >= 1 && s->H >= 1 && s->T >= 0, SSLP_ERR_INVALID_ARG, "bad B/T/H");
+    REQUIRE(s->d_k >= 1 && s->d_v >= 1 && s->chunk >= 1, SSLP_ERR_INVALID_ARG,
+            "d_k, d_v, chunk must be >= 1");
+    REQUIRE(s->d_k == 128 && s->d_v == 128 && s->chunk == 64, SSLP_ERR_UNSUPPORTED,
+            "only d_k = d_v = 128 and chunk = 64 are supported (got %d, %d, %d)", s->d_k, s->d_v,
+            s->chunk);
+    return SSLP_OK;
+}
+
+size_t gdn_workspace_size(const sslp_gdn_shape* s) {
+    if (check_gdn_shape(s) != SSLP_OK) return 0;
+    return 0;
+}
+
+int gdn_chunk_forward(const sslp_gdn_shape* s, int dtype, int decay_mode, const void* q,
+                      const void* k, const void* v, const float* alpha, const float* beta,
+                      const float* S0, float* S_out, void* o, void* workspace, size_t ws_bytes,
+                      void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_gdn_shape(s)) return rc;
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE(decay_mode == SSLP_DECAY_SCALAR || decay_mode == SSLP_DECAY_CHANNEL,
+            SSLP_ERR_INVALID_ARG, "decay_mode must be 0 or 1 (got %d)", decay_mode);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(alpha);
+    REQUIRE_PTR(beta);
+    REQUIRE_ALIGNED(S0);
+    REQUIRE_PTR(S_out);
+    REQUIRE_PTR(o);
+    (void)workspace;
+    (void)ws_bytes;
+    (void)stream;
+    return fail(SSLP_ERR_UNSUPPORTED, "gdn_chunk_forward: kernel not built into this library");
+}
+
+static int check_sse_shape(const sslp_sse_shape* s) {
+    REQUIRE(s != nullptr, SSLP_ERR_INVALID_ARG, "shape must not be NULL");
+    REQUIRE(s->B >= 1 && s->H >= 1 && s->T >= 0, SSLP_ERR_INVALID_ARG, "bad B/T/H");
+    REQUIRE(s->N >= 1 && s->topk >= 1 && s->topk <= s->N, SSLP_ERR_INVALID_ARG,
+            "need 1 <= topk <= N (topk=%d N=%d)", s->topk, s->N);
+    REQUIRE(s->N <= 64 && s->topk <= 8, SSLP_ERR_UNSUPPORTED, "need N <= 64 and topk <= 8");
+    REQUIRE(s->c >= 1 && s->d >= 1 && s->chunk >= 1, SSLP_ERR_INVALID_ARG,
+            "c, d, chunk must be >= 1");
+    REQUIRE(s->c == 128 && s->d == 128 && s->chunk == 64, SSLP_ERR_UNSUPPORTED,
+            "only c = d = 128 and chunk = 64 are supported");
+    return SSLP_OK;
+}
+
+size_t sse_workspace_size(const sslp_sse_shape* s) {
+    if (check_sse_shape(s) != SSLP_OK) return 0;
+    return 0;
+}
+
+int sse_forward(const sslp_sse_shape* s, int dtype, const float* gate_logits, const void* q,
+                const void* k, const void* v, const float* lambda, const void* q_sh,
+                const void* k_sh, float* S, void* o, int32_t* sel, float* e_sel, void* workspace,
+                size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_sse_shape(s)) return rc;
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE_PTR(gate_logits);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(lambda);
+    REQUIRE_ALIGNED(q_sh);
+    REQUIRE_ALIGNED(k_sh);
+    REQUIRE_PTR(S);
+    REQUIRE_PTR(o);
+    REQUIRE_ALIGNED(sel);
+    REQUIRE_ALIGNED(e_sel);
+    (void)workspace;
+    (void)ws_bytes;
+    (void)stream;
+    return fail(SSLP_ERR_UNSUPPORTED, "sse_forward: kernel not built into this library");
+}
+
+}  // extern "C"

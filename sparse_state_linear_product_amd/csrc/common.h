@@ -1,0 +1,148 @@
+// Device and host helpers shared by the libsslp HIP kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SSLP_DEVICE __device__ __forceinline__
+
+namespace sslp {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// element types: fp32 or bf16 (stored as raw uint16 bits)
+// ---------------------------------------------------------------------------
+struct bf16_t {
+    uint16_t bits;
+};
+
+SSLP_DEVICE float to_f32(float x) { return x; }
+SSLP_DEVICE float to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x.bits) << 16); }
+
+// round-to-nearest-even fp32 -> bf16 (finite inputs)
+SSLP_DEVICE bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    bf16_t r;
+    r.bits = (uint16_t)(u >> 16);
+    return r;
+}
+template <typename T>
+SSLP_DEVICE T from_f32(float f);
+template <>
+SSLP_DEVICE float from_f32<float>(float f) { return f; }
+template <>
+SSLP_DEVICE bf16_t from_f32<bf16_t>(float f) { return f32_to_bf16(f); }
+
+// ---------------------------------------------------------------------------
+// ranking keys: a 64-bit unsigned key whose integer order is the rank order
+// "score descending, then index ascending", so that a descending sort of keys
+// is the ranking.  -0 is folded onto +0 so that the two tie.
+// ---------------------------------------------------------------------------
+SSLP_DEVICE uint32_t order_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;  // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+SSLP_DEVICE float order_bits_to_float(uint32_t o) {
+    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+    return __uint_as_float(u);
+}
+SSLP_DEVICE uint64_t make_key(float score, uint32_t index) {
+    return ((uint64_t)order_bits(score) << 32) | (uint64_t)(~index);
+}
+SSLP_DEVICE float key_score(uint64_t key) { return order_bits_to_float((uint32_t)(key >> 32)); }
+SSLP_DEVICE uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
+
+// ---------------------------------------------------------------------------
+// wave-level helpers
+// ---------------------------------------------------------------------------
+SSLP_DEVICE uint64_t shfl_xor_u64(uint64_t v, int mask) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl_xor(lo, mask, kWave);
+    hi = __shfl_xor(hi, mask, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+SSLP_DEVICE uint64_t shfl_u64(uint64_t v, int src) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl(lo, src, kWave);
+    hi = __shfl(hi, src, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+SSLP_DEVICE float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+SSLP_DEVICE uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = shfl_xor_u64(x, m);
+        x = o > x ? o : x;
+    }
+    return x;
+}
+
+// Orders LDS/global accesses of one wavefront: a compiler barrier plus
+// wavefront-scope release/acquire (the hardware keeps a wave's memory
+// operations in order, so no wait instruction is needed).
+SSLP_DEVICE void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bitonic sort, descending, of 64*E keys held E per lane: element e of lane l
+// sits at position p = e*64 + l.  Compare-exchange partners at distance j < 64
+// live in another lane (exchanged with shuffles); larger distances are inside
+// the lane.
+template <int E>
+SSLP_DEVICE void bitonic_sort_desc(uint64_t (&a)[E], int lane) {
+    constexpr int n = 64 * E;
+#pragma unroll
+    for (int kk = 2; kk <= n; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            if (j >= 64) {
+                const int je = j >> 6;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int e2 = e ^ je;
+                    if (e2 > e) {
+                        const bool desc = (((e << 6) & kk) == 0);
+                        const uint64_t x = a[e], y = a[e2];
+                        const bool sw = desc ? (x < y) : (x > y);
+                        a[e] = sw ? y : x;
+                        a[e2] = sw ? x : y;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const uint64_t mine = a[e];
+                    const uint64_t other = shfl_xor_u64(mine, j);
+                    const int p = (e << 6) | lane;
+                    const bool desc = ((p & kk) == 0);
+                    const bool lower = ((lane & j) == 0);
+                    const bool keep_max = (lower == desc);
+                    const uint64_t mx = mine > other ? mine : other;
+                    const uint64_t mn = mine > other ? other : mine;
+                    a[e] = keep_max ? mx : mn;
+                }
+            }
+        }
+    }
+}
+
+// element at runtime position p (p = e*64 + lane) of a register-held array,
+// broadcast to the whole wave
+template <int E>
+SSLP_DEVICE uint64_t wave_get(const uint64_t (&a)[E], int p) {
+    const int e = p >> 6, l = p & 63;
+    uint64_t v = 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) v = (i == e) ? a[i] : v;
+    return shfl_u64(v, l);
+}
+
+}  // namespace sslp

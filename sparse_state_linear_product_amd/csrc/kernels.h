@@ -1,0 +1,34 @@
+// Host-side launchers of the libsslp kernels (one per .hip file).  Each
+// enqueues on `st` and returns the launch status; argument validation is done
+// by the C-ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sslp {
+
+// ---- Sparse Delta Memory ----
+// number of pairs (i,j), i,j < k, with (i+1)(j+1) <= budget
+int address_set_size(int k, int budget);
+
+hipError_t launch_sdm_address(int P, int sqrtN, int dtype, const void* s1, const void* s2, int k,
+                              int budget, int32_t* idx, float* wt, hipStream_t st);
+
+struct SdmUpdateArgs {
+    int B, T, H, N, dv, W, R;
+    int dtype;          // 0 fp32, 1 bf16 for v and y
+    int residual_mode;  // 0 shared, 1 per-slot
+    const int32_t* idx_w;
+    const float* wt_w;
+    const int32_t* idx_r;
+    const float* wt_r;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    float* M;
+    void* y;
+};
+hipError_t launch_sdm_update(const SdmUpdateArgs& a, hipStream_t st);
+
+}  // namespace sslp

@@ -1,0 +1,240 @@
+// K1: product-key addressing for Sparse Delta Memory, one wavefront per problem.
+//
+// Slides "Sparse Delta Memory: Scaling the State of Linear RNNs through
+// Sparsity", "Product keys select addresses without scoring every slot":
+// slot (a,b) scores k'_1[a] + k'_2[b]; keep each half's top-k, form the k^2
+// candidate sums, select the top `budget`, softmax over the selected scores.
+//
+// Ranking everywhere is (fp32 score desc, index asc) encoded as a 64-bit key
+// (common.h), so selection results are unique and reproducible bit for bit.
+//
+// Algorithm per problem (one wave64):
+//  1. both halves -> keys, wave bitonic sort (EH keys per lane), top-k of each
+//     half is then held by lanes 0..k-1 (k <= 64) and staged in LDS;
+//  2. D = {(i,j) : (i+1)(j+1) <= budget} over the two sorted top-k lists.  With
+//     no rounding ties the top-budget candidates all lie in D, because a pair
+//     outside D is dominated (both ranks smaller or equal) by more than
+//     `budget` pairs whose fp32 sums are >= its own.  D is sorted (ED keys
+//     per lane) and tau = its budget-th key;
+//  3. F = #{all k^2 candidates with key >= tau} is counted exactly.  F ==
+//     budget proves D's top-budget is the answer.  Otherwise (rounding ties
+//     let a pair outside D win on the slot index) the exact top-budget is
+//     extracted from all k^2 candidates by repeated wave max;
+//  4. softmax in fp32 over the selected scores.
+#include "common.h"
+#include "kernels.h"
+
+namespace sslp {
+
+namespace {
+
+struct AddrArgs {
+    const void* s1;
+    const void* s2;
+    int32_t* idx;
+    float* wt;
+    int P, sqrtN, k, budget, nD;
+};
+
+constexpr int kWavesPerBlock = 4;
+
+template <typename in_t, int EH, int ED>
+__global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
+    __shared__ float s_score[kWavesPerBlock][2][64];
+    __shared__ int s_index[kWavesPerBlock][2][64];
+    __shared__ uint64_t s_d[kWavesPerBlock][64 * ED];
+
+    const int wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int p = blockIdx.x * kWavesPerBlock + wv;
+    if (p >= a.P) return;  // whole wave leaves; no block barrier is used below
+
+    const int n = a.sqrtN, k = a.k, budget = a.budget;
+    const in_t* h1 = static_cast<const in_t*>(a.s1) + (size_t)p * n;
+    const in_t* h2 = static_cast<const in_t*>(a.s2) + (size_t)p * n;
+
+    // 1. per-half sort; key 0 is below every finite score's key (padding)
+    {
+        uint64_t x1[EH], x2[EH];
+#pragma unroll
+        for (int e = 0; e < EH; ++e) {
+            const int pos = e * 64 + lane;
+            x1[e] = pos < n ? make_key(to_f32(h1[pos]), (uint32_t)pos) : 0ull;
+            x2[e] = pos < n ? make_key(to_f32(h2[pos]), (uint32_t)pos) : 0ull;
+        }
+        bitonic_sort_desc<EH>(x1, lane);
+        bitonic_sort_desc<EH>(x2, lane);
+        if (lane < k) {
+            s_score[wv][0][lane] = key_score(x1[0]);
+            s_index[wv][0][lane] = (int)key_index(x1[0]);
+            s_score[wv][1][lane] = key_score(x2[0]);
+            s_index[wv][1][lane] = (int)key_index(x2[0]);
+        }
+    }
+    wave_sync();
+
+    // 2. the dominance set D, row i of the first half's ranks holding
+    //    j < min(k, budget / (i+1)) entries
+    {
+        int cnt = 0;
+        if (lane < k) {
+            cnt = budget / (lane + 1);
+            cnt = cnt < k ? cnt : k;
+        }
+        // exclusive prefix sum of cnt over the lanes
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += o;
+        }
+        const int off = incl - cnt;
+        if (lane < k) {
+            const float sa = s_score[wv][0][lane];
+            const uint32_t ia = (uint32_t)s_index[wv][0][lane];
+            for (int j = 0; j < cnt; ++j) {
+                const float sum = sa + s_score[wv][1][j];  // one fp32 RNE add
+                const uint32_t slot = ia * (uint32_t)n + (uint32_t)s_index[wv][1][j];
+                s_d[wv][off + j] = make_key(sum, slot);
+            }
+        }
+    }
+    wave_sync();
+
+    uint64_t d[ED];
+#pragma unroll
+    for (int e = 0; e < ED; ++e) {
+        const int pos = e * 64 + lane;
+        d[e] = pos < a.nD ? s_d[wv][pos] : 0ull;
+    }
+    bitonic_sort_desc<ED>(d, lane);
+    const uint64_t tau = wave_get<ED>(d, budget - 1);
+
+    // 3. exact count of candidates at or above tau
+    int F = 0;
+    const int kk = k * k;
+    for (int base = 0; base < kk; base += 64) {
+        const int x = base + lane;
+        bool ge = false;
+        if (x < kk) {
+            const int i = x / k, j = x - (x / k) * k;
+            const float sum = s_score[wv][0][i] + s_score[wv][1][j];
+            const uint32_t slot =
+                (uint32_t)s_index[wv][0][i] * (uint32_t)n + (uint32_t)s_index[wv][1][j];
+            ge = make_key(sum, slot) >= tau;
+        }
+        F += __popcll(__ballot(ge));
+    }
+
+    int32_t* out_i = a.idx + (size_t)p * budget;
+    float* out_w = a.wt + (size_t)p * budget;
+    if (F == budget) {
+        // 4. softmax over the selected fp32 scores (rank 0 holds the maximum)
+        const float smax = key_score(wave_get<ED>(d, 0));
+        float w[ED];
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < ED; ++e) {
+            const int pos = e * 64 + lane;
+            w[e] = pos < budget ? __expf(key_score(d[e]) - smax) : 0.f;
+            part += w[e];
+        }
+        const float z = wave_sum(part);
+#pragma unroll
+        for (int e = 0; e < ED; ++e) {
+            const int pos = e * 64 + lane;
+            if (pos < budget) {
+                out_i[pos] = (int32_t)key_index(d[e]);
+                out_w[pos] = w[e] / z;
+            }
+        }
+        return;
+    }
+
+    // rare path: exact top-`budget` of all k^2 candidates by repeated maximum
+    uint64_t bound = ~0ull;  // exclusive upper bound (no finite key reaches it)
+    float smax = 0.f, z = 0.f;
+    float wl0 = 0.f, wl1 = 0.f;  // weight of rank r kept by lane r % 64 (budget <= 128)
+    for (int r = 0; r < budget; ++r) {
+        uint64_t best = 0ull;
+        for (int base = 0; base < kk; base += 64) {
+            const int x = base + lane;
+            if (x < kk) {
+                const int i = x / k, j = x - (x / k) * k;
+                const float sum = s_score[wv][0][i] + s_score[wv][1][j];
+                const uint32_t slot =
+                    (uint32_t)s_index[wv][0][i] * (uint32_t)n + (uint32_t)s_index[wv][1][j];
+                const uint64_t key = make_key(sum, slot);
+                if (key < bound && key > best) best = key;
+            }
+        }
+        best = wave_max_u64(best);
+        bound = best;
+        const float sc = key_score(best);
+        if (r == 0) smax = sc;
+        const float w = __expf(sc - smax);
+        z += w;
+        if (lane == 0) out_i[r] = (int32_t)key_index(best);
+        if (lane == (r & 63)) {
+            if (r < 64) wl0 = w;
+            else wl1 = w;
+        }
+    }
+    if (lane < budget) out_w[lane] = wl0 / z;
+    if (lane + 64 < budget) out_w[lane + 64] = wl1 / z;
+}
+
+int ceil_pow2_units(int n) {  // smallest power of two >= ceil(n/64), at least 1
+    int e = 1;
+    while (64 * e < n) e <<= 1;
+    return e;
+}
+
+template <typename in_t, int EH>
+hipError_t dispatch_ed(int ED, dim3 grid, hipStream_t st, const AddrArgs& a) {
+    switch (ED) {
+        case 1: sdm_address_kernel<in_t, EH, 1><<<grid, 256, 0, st>>>(a); break;
+        case 2: sdm_address_kernel<in_t, EH, 2><<<grid, 256, 0, st>>>(a); break;
+        case 4: sdm_address_kernel<in_t, EH, 4><<<grid, 256, 0, st>>>(a); break;
+        case 8: sdm_address_kernel<in_t, EH, 8><<<grid, 256, 0, st>>>(a); break;
+        case 16: sdm_address_kernel<in_t, EH, 16><<<grid, 256, 0, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename in_t>
+hipError_t dispatch_eh(int EH, int ED, dim3 grid, hipStream_t st, const AddrArgs& a) {
+    switch (EH) {
+        case 1: return dispatch_ed<in_t, 1>(ED, grid, st, a);
+        case 2: return dispatch_ed<in_t, 2>(ED, grid, st, a);
+        case 4: return dispatch_ed<in_t, 4>(ED, grid, st, a);
+        case 8: return dispatch_ed<in_t, 8>(ED, grid, st, a);
+        case 16: return dispatch_ed<in_t, 16>(ED, grid, st, a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int address_set_size(int k, int budget) {
+    int nD = 0;
+    for (int i = 0; i < k; ++i) {
+        int c = budget / (i + 1);
+        nD += c < k ? c : k;
+    }
+    return nD;
+}
+
+hipError_t launch_sdm_address(int P, int sqrtN, int dtype, const void* s1, const void* s2, int k,
+                              int budget, int32_t* idx, float* wt, hipStream_t st) {
+    if (P <= 0) return hipSuccess;
+    AddrArgs a{s1, s2, idx, wt, P, sqrtN, k, budget, address_set_size(k, budget)};
+    const int EH = ceil_pow2_units(sqrtN);
+    const int ED = ceil_pow2_units(a.nD);
+    dim3 grid((P + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (dtype == 0) return dispatch_eh<float>(EH, ED, grid, st, a);
+    return dispatch_eh<bf16_t>(EH, ED, grid, st, a);
+}
+
+}  // namespace sslp

@@ -1,0 +1,119 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_state_linear_product_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sslp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|void)\s*\*?\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("sdm_forward", "sdm_decode_step", "sse_forward", "gdn_chunk_forward",
+                     "sdm_address", "sdm_sparse_update", "sslp_last_error", "sslp_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"missing exports: {missing}"
+    assert set(_lib.SIGNATURES) >= set(declared_functions())
+    assert lib.sslp_version() == 1
+
+
+def _sdm(B=1, T=4, H=1, sqrtN=8, d_v=16, k_w=4, k_r=4, W=4, R=4):
+    return _lib.SdmShape(B, T, H, sqrtN, d_v, k_w, k_r, W, R)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # aligned non-NULL pointer; never dereferenced (rejected first)
+MISALIGNED = ctypes.c_void_p(0x1004)
+
+
+def _fwd(shape, dtype=0, mode=0, ptrs=None, ws_bytes=1 << 20):
+    ptrs = ptrs or [FAKE] * 9 + [None] * 4 + [FAKE]
+    return _lib.lib().sdm_forward(ctypes.byref(shape), dtype, mode, *ptrs, ws_bytes, None)
+
+
+@pytest.mark.parametrize("shape,code,msg", [
+    (_sdm(W=20), _lib.SSLP_ERR_INVALID_ARG, "W=20 > k_w^2"),
+    (_sdm(k_w=9), _lib.SSLP_ERR_INVALID_ARG, "k_w, k_r must be <= sqrtN"),
+    (_sdm(B=0), _lib.SSLP_ERR_INVALID_ARG, "B, H must be >= 1"),
+    (_sdm(T=-1), _lib.SSLP_ERR_INVALID_ARG, "B, H must be >= 1"),
+    (_sdm(d_v=6), _lib.SSLP_ERR_UNSUPPORTED, "multiple of 4"),
+    (_sdm(sqrtN=2000, k_w=4, k_r=4), _lib.SSLP_ERR_UNSUPPORTED, "sqrtN 2000"),
+    (_sdm(sqrtN=100, k_w=80, k_r=4), _lib.SSLP_ERR_UNSUPPORTED, "<= 64"),
+    (_sdm(sqrtN=100, k_w=20, k_r=20, W=200), _lib.SSLP_ERR_UNSUPPORTED, "<= 128"),
+])
+def test_sdm_forward_shape_errors(shape, code, msg):
+    assert _fwd(shape) == code
+    assert msg in _lib.lib().sslp_last_error().decode()
+
+
+def test_sdm_forward_pointer_errors():
+    lib = _lib.lib()
+    ptrs = [FAKE] * 9 + [None] * 4 + [FAKE]
+    for i, name in enumerate(["sw1", "sw2", "sr1", "sr2", "v", "alpha", "beta", "M", "y"]):
+        p = list(ptrs)
+        p[i] = None
+        assert _fwd(_sdm(), ptrs=p) == _lib.SSLP_ERR_INVALID_ARG
+        assert f"{name} must not be NULL" in lib.sslp_last_error().decode()
+        p[i] = MISALIGNED
+        assert _fwd(_sdm(), ptrs=p) == _lib.SSLP_ERR_INVALID_ARG
+        assert "aligned" in lib.sslp_last_error().decode()
+
+
+def test_sdm_forward_workspace_and_flags():
+    lib = _lib.lib()
+    s = _sdm()
+    need = lib.sdm_workspace_size(ctypes.byref(s))
+    assert need > 0
+    assert _fwd(s, ws_bytes=need - 1) == _lib.SSLP_ERR_WORKSPACE
+    assert _fwd(s, dtype=7) == _lib.SSLP_ERR_INVALID_ARG
+    assert _fwd(s, mode=2) == _lib.SSLP_ERR_INVALID_ARG
+    assert lib.sdm_workspace_size(ctypes.byref(_sdm(W=65))) == 0  # W > N
+
+
+def test_sdm_decode_requires_single_token():
+    lib = _lib.lib()
+    s = _sdm(T=3)
+    rc = lib.sdm_decode_step(ctypes.byref(s), 0, 0, *([FAKE] * 9 + [None] * 4 + [FAKE]), 1 << 20,
+                             None)
+    assert rc == _lib.SSLP_ERR_INVALID_ARG and "T == 1" in lib.sslp_last_error().decode()
+
+
+def test_sdm_address_errors():
+    lib = _lib.lib()
+    s = _sdm()
+    assert lib.sdm_address(ctypes.byref(s), 0, FAKE, FAKE, 9, 4, FAKE, FAKE, None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+    assert lib.sdm_address(ctypes.byref(s), 0, FAKE, FAKE, 4, 17, FAKE, FAKE, None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+    assert lib.sdm_address(ctypes.byref(s), 0, None, FAKE, 4, 4, FAKE, FAKE, None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+
+
+def test_gdn_and_sse_shape_errors():
+    lib = _lib.lib()
+    g = _lib.GdnShape(1, 8, 1, 64, 128, 64)
+    assert lib.gdn_chunk_forward(ctypes.byref(g), 1, 0, *([FAKE] * 9), 0, None) == \
+        _lib.SSLP_ERR_UNSUPPORTED
+    g = _lib.GdnShape(1, 8, 1, 128, 128, 64)
+    assert lib.gdn_chunk_forward(ctypes.byref(g), 1, 5, *([FAKE] * 9), 0, None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+    s = _lib.SseShape(1, 8, 1, 8, 9, 128, 128, 64)
+    assert lib.sse_forward(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == _lib.SSLP_ERR_INVALID_ARG
+    s = _lib.SseShape(1, 8, 1, 8, 2, 64, 128, 64)
+    assert lib.sse_forward(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == _lib.SSLP_ERR_UNSUPPORTED
