@@ -295,18 +295,29 @@ int gdn_chunk_forward(const sslp_gdn_shape* s, int dtype, int decay_mode, const 
     if (int rc = check_dtype(dtype)) return rc;
     REQUIRE(decay_mode == SSLP_DECAY_SCALAR || decay_mode == SSLP_DECAY_CHANNEL,
             SSLP_ERR_INVALID_ARG, "decay_mode must be 0 or 1 (got %d)", decay_mode);
-    REQUIRE_PTR(q);
-    REQUIRE_PTR(k);
-    REQUIRE_PTR(v);
-    REQUIRE_PTR(alpha);
-    REQUIRE_PTR(beta);
+    REQUIRE_ALIGNED(q);
+    REQUIRE_ALIGNED(k);
+    REQUIRE_ALIGNED(v);
+    REQUIRE_ALIGNED(alpha);
+    REQUIRE_ALIGNED(beta);
+    REQUIRE_ALIGNED(o);
     REQUIRE_ALIGNED(S0);
+    REQUIRE(dtype == SSLP_BF16, SSLP_ERR_UNSUPPORTED,
+            "gdn_chunk_forward supports bf16 q/k/v only (got dtype %d)", dtype);
     REQUIRE_PTR(S_out);
-    REQUIRE_PTR(o);
+    if (s->T > 0) {
+        REQUIRE_PTR(q);
+        REQUIRE_PTR(k);
+        REQUIRE_PTR(v);
+        REQUIRE_PTR(alpha);
+        REQUIRE_PTR(beta);
+        REQUIRE_PTR(o);
+    }
     (void)workspace;
     (void)ws_bytes;
-    (void)stream;
-    return fail(SSLP_ERR_UNSUPPORTED, "gdn_chunk_forward: kernel not built into this library");
+    return hip_status(sslp::launch_gdn_chunk(s->B, s->T, s->H, s->d_v, dtype, decay_mode, q, k, v,
+                                             alpha, beta, S0, S_out, o, (hipStream_t)stream),
+                      "gdn_chunk_forward launch");
 }
 
 static int check_sse_shape(const sslp_sse_shape* s) {

@@ -1,0 +1,702 @@
+// K4: chunked forward of the gated delta rule (Gated DeltaNet: scalar decay;
+// Kimi Delta Attention: per-key-channel decay), MFMA on gfx950.
+//
+// Slides "Linear Attention Architectures: Mechanisms, Trade-offs, and
+// Cross-Layer Routing", "GDN and KDA change the granularity of forgetting"
+// (Eqs. 15-20) and "DeltaNet writes a correction to the current association"
+// (Eq. 14).  With S = W^T ([d_k, d_v], row = key channel) one token is
+//     S~ = D_t S,   S = S~ + beta_t k_t (v_t - S~^T k_t)^T,   o_t = S^T q_t,
+// D_t = alpha_t I (GDN) or Diag(alpha_t) (KDA).
+//
+// Chunked form (same result up to rounding).  Inside a chunk of C = 64 tokens
+// with incoming state S0 and cumulative log-decay g_t (scalar or per channel),
+// let u_t = beta_t (v_t - predicted value).  Unrolling the recurrence gives
+//     (I + A) U = diag(beta) (V - Kt S0),   A[t,j] = beta_t sum_i k_t[i] e^{g_t[i]-g_j[i]} k_j[i], j<t
+//     O = Qt S0 + P U,                      P[t,j] = sum_i q_t[i] e^{g_t[i]-g_j[i]} k_j[i], j<=t
+//     S_C = e^{g_C} S0 + Kh^T U
+// with Kt = K*e^{g_t}, Qt = Q*e^{g_t}, Kh = K*e^{g_C-g_t}.  The slides'
+// sparse-memory training appendix uses the same unit-diagonal triangular
+// system (slide "Backup: sparse interactions drive the triangular solve").
+//
+// Work split.  One workgroup (4 waves) owns (batch, head, 32-column block of
+// d_v) and walks the chunks in order, keeping its [128 x 32] fp32 state slice
+// in MFMA accumulator registers.  The dense contractions (K K^T, Q K^T, K S0,
+// Q S0, T X, P U, Kh^T U) run on v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation; T = (I+A)^{-1} is formed in fp32: 16x16 diagonal blocks by
+// forward substitution, off-diagonal blocks through
+//     I + A = D (I + L),  L = D^{-1} A_off,  T = (I - L + L^2 - L^3) D^{-1}
+// on v_mfma_f32_16x16x4_f32.  KDA factors the per-channel decay into the
+// operands relative to the first token of each 16-token block, so every
+// scale factor is a product of alphas bounded by alpha_min^-15.
+#include "common.h"
+#include "kernels.h"
+
+namespace sslp {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int C = 64;     // chunk length
+constexpr int DK = 128;   // key width
+constexpr int DVB = 32;   // d_v columns per workgroup
+constexpr int NTH = 256;  // threads per workgroup
+constexpr int LDK = DK + 8;   // bf16 row stride of [C][DK] tiles
+constexpr int LDF = C + 4;    // fp32 row stride of [C][C] tiles
+constexpr int LDX = DVB + 4;  // fp32 row stride of [C][DVB] tiles
+
+struct __align__(16) Smem {
+    uint16_t k[C][LDK];   // GDN: K;  KDA: Kp = K * e^{g_t - g_r}
+    uint16_t km[C][LDK];  // KDA: Km = K * e^{g_r - g_t}
+    uint16_t q[C][LDK];   // GDN: Q;  KDA: Qp = Q * e^{g_t - g_r}
+    union {
+        struct {
+            float A[C][LDF];   // A, then L = D^{-1} A_off in its lower blocks
+            float Tm[C][LDF];  // T = (I + A)^{-1}
+        } s;
+        float alpha[C][DK];  // KDA: the chunk's raw alphas (staging)
+    } u;
+    float P[C][LDF];      // decayed Q K^T, causal
+    float X[C][LDX];      // diag(beta)(V - Kt S0)
+    union {
+        float U[C][LDX];  // T X
+        struct {
+            float pa[4][DK];  // KDA: product of the block's alphas
+            float px[4][DK];  // KDA: same without the block's first token
+            float af[4][DK];  // KDA: the block's first alpha
+        } blk;
+    } uw;
+    float V[C][LDX];      // V block (fp32)
+    uint16_t St[DVB][LDK];  // incoming state, transposed, bf16
+    float L3[16][17];     // (L^3) block (3,0)
+    float g[C];           // GDN: cumulative log decay
+    float beta[C];
+    float F[4][DK];       // KDA: e^{g_{16m}}
+    float Hf[4][DK];      // KDA: e^{g_C - g_{16m}}
+    float D[6][DK];       // KDA: e^{g_{16m} - g_{16n}}, pairs (1,0),(2,1),(3,2),(2,0),(3,1),(3,0)
+    float gC[DK];         // KDA: e^{g_C}
+};
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+
+SSLP_DEVICE __bf16 bf(float f) { return __builtin_bit_cast(__bf16, f32_to_bf16(f).bits); }
+SSLP_DEVICE float bf2f(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+SSLP_DEVICE f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+SSLP_DEVICE f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+SSLP_DEVICE bf16x8_t load_bf16x8(const uint16_t* p) {
+    return *reinterpret_cast<const bf16x8_t*>(p);
+}
+
+// fp32 16x16x16 product of LDS blocks on one wave: acc += Aop * Bop
+SSLP_DEVICE f32x4_t mm16_f32(const float* pa, int lda, const float* pb, int ldb, f32x4_t acc,
+                             int lane) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int kk = 4 * s + (lane >> 4);
+        acc = mfma_f32(pa[(lane & 15) * lda + kk], pb[kk * ldb + (lane & 15)], acc);
+    }
+    return acc;
+}
+SSLP_DEVICE void store16(float* p, int ld, f32x4_t c, int lane, float scale) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[((lane >> 4) * 4 + j) * ld + (lane & 15)] = scale * c[j];
+}
+
+template <typename io_t>
+struct Prefetch {
+    static constexpr int EPS = 16 / sizeof(io_t);  // elements per 16-byte segment
+    static constexpr int KSEG = C * DK / EPS / NTH; // segments per thread for K (and Q)
+    static constexpr int VSEG = (C * DVB / EPS + NTH - 1) / NTH;
+    uint4 k[KSEG], q[KSEG], v[VSEG];
+    float a_s, b_s;  // GDN alpha / beta for token tid (tid < C)
+    float4 a_c[C * DK / 4 / NTH];  // KDA alpha
+};
+
+struct GdnArgs {
+    int B, T, H, dv;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const float* S0;
+    float* S_out;
+    void* o;
+};
+
+template <typename io_t, bool KDA>
+__global__ __launch_bounds__(NTH) void gdn_chunk_kernel(GdnArgs a) {
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nblk = a.dv / DVB;
+    const int cb = blockIdx.x % nblk;
+    const int bh = blockIdx.x / nblk;
+    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+    const int n0 = cb * DVB;
+    const int T = a.T, H = a.H, dv = a.dv;
+    const io_t* qg = static_cast<const io_t*>(a.q);
+    const io_t* kg = static_cast<const io_t*>(a.k);
+    const io_t* vg = static_cast<const io_t*>(a.v);
+    io_t* og = static_cast<io_t*>(a.o);
+    using PF = Prefetch<io_t>;
+    constexpr int EPS = PF::EPS;
+    const int nchunks = (T + C - 1) / C;
+
+    // ---- state slice in accumulator layout: tiles (tm = 2w + x, tn = y) ----
+    f32x4_t S[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
+                const int n = 16 * y + (lane & 15);
+                S[x][y][j] =
+                    a.S0 ? a.S0[(((size_t)b * H + h) * DK + i) * dv + n0 + n] : 0.f;
+            }
+
+    auto issue = [&](PF& pf, int c) {
+        const int t0 = c * C;
+#pragma unroll
+        for (int s = 0; s < PF::KSEG; ++s) {
+            const int seg = tid + NTH * s;
+            const int row = seg / (DK / EPS), col = (seg % (DK / EPS)) * EPS;
+            const int t = t0 + row;
+            if (t < T) {
+                const size_t off = (((size_t)b * T + t) * H + h) * DK + col;
+                pf.k[s] = *reinterpret_cast<const uint4*>(kg + off);
+                pf.q[s] = *reinterpret_cast<const uint4*>(qg + off);
+            } else {
+                pf.k[s] = make_uint4(0, 0, 0, 0);
+                pf.q[s] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < PF::VSEG; ++s) {
+            const int seg = tid + NTH * s;
+            const int row = seg / (DVB / EPS), col = (seg % (DVB / EPS)) * EPS;
+            const int t = t0 + row;
+            if (row < C && t < T)
+                pf.v[s] = *reinterpret_cast<const uint4*>(
+                    vg + (((size_t)b * T + t) * H + h) * dv + n0 + col);
+            else
+                pf.v[s] = make_uint4(0, 0, 0, 0);
+        }
+        if (tid < C) {
+            const int t = t0 + tid;
+            const size_t bth = ((size_t)b * T + t) * H + h;
+            pf.b_s = t < T ? a.beta[bth] : 0.f;
+            if (!KDA) pf.a_s = t < T ? a.alpha[bth] : 1.f;
+        }
+        if (KDA) {
+#pragma unroll
+            for (int s = 0; s < C * DK / 4 / NTH; ++s) {
+                const int seg = tid + NTH * s;
+                const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
+                const int t = t0 + row;
+                pf.a_c[s] = t < T ? *reinterpret_cast<const float4*>(
+                                        a.alpha + (((size_t)b * T + t) * H + h) * DK + col)
+                                  : make_float4(1.f, 1.f, 1.f, 1.f);
+            }
+        }
+    };
+
+    // raw inputs of a chunk -> LDS (K, Q as bf16; V, beta fp32; alpha in LDS
+    // staging: GDN log-decay in g, KDA alpha in A's storage)
+    auto commit = [&](const PF& pf) {
+#pragma unroll
+        for (int s = 0; s < PF::KSEG; ++s) {
+            const int seg = tid + NTH * s;
+            const int row = seg / (DK / EPS), col = (seg % (DK / EPS)) * EPS;
+            if constexpr (sizeof(io_t) == 2) {
+                *reinterpret_cast<uint4*>(&sm.k[row][col]) = pf.k[s];
+                *reinterpret_cast<uint4*>(&sm.q[row][col]) = pf.q[s];
+            } else {
+                const float* fk = reinterpret_cast<const float*>(&pf.k[s]);
+                const float* fq = reinterpret_cast<const float*>(&pf.q[s]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sm.k[row][col + e] = f32_to_bf16(fk[e]).bits;
+                    sm.q[row][col + e] = f32_to_bf16(fq[e]).bits;
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < PF::VSEG; ++s) {
+            const int seg = tid + NTH * s;
+            const int row = seg / (DVB / EPS), col = (seg % (DVB / EPS)) * EPS;
+            if (row < C) {
+                const io_t* e = reinterpret_cast<const io_t*>(&pf.v[s]);
+#pragma unroll
+                for (int x = 0; x < EPS; ++x) sm.V[row][col + x] = to_f32(e[x]);
+            }
+        }
+        if (tid < C) {
+            sm.beta[tid] = pf.b_s;
+            if (!KDA) sm.g[tid] = __logf(pf.a_s);
+        }
+        if (KDA) {
+#pragma unroll
+            for (int s = 0; s < C * DK / 4 / NTH; ++s) {
+                const int seg = tid + NTH * s;
+                const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
+                *reinterpret_cast<float4*>(&sm.u.alpha[row][col]) = pf.a_c[s];
+            }
+        }
+    };
+
+    // state slice (bf16, transposed) for the B operands of K S0 and Q S0
+    auto publish_state = [&]() {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
+                    const int n = 16 * y + (lane & 15);
+                    sm.St[n][i] = f32_to_bf16(S[x][y][j]).bits;
+                }
+    };
+
+    PF pf;
+    issue(pf, 0);
+    commit(pf);
+    publish_state();
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const int Tc = (T - t0) < C ? (T - t0) : C;
+        if (c + 1 < nchunks) issue(pf, c + 1);  // next chunk's inputs, in flight
+
+        // ---------------- decay bookkeeping ----------------
+        float decC_s = 1.f;  // GDN: e^{g_C}
+        if constexpr (!KDA) {
+            if (w == 0) {  // inclusive prefix sum of log alpha over the 64 tokens
+                float x = sm.g[lane];
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const float y = __shfl_up(x, d, 64);
+                    if (lane >= d) x += y;
+                }
+                sm.g[lane] = x;
+            }
+            __syncthreads();
+            decC_s = __expf(sm.g[C - 1]);
+        } else {
+            // thread (channel i, half hf) walks the 32 tokens of blocks 2hf, 2hf+1:
+            // E+ = product of alphas after the block's first token, E- = 1/E+
+            const int i = tid & (DK - 1), hf = tid >> 7;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const int blk = 2 * hf + bb;
+                float ep = 1.f, em = 1.f, pall = 1.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = 16 * blk + r;
+                    const float al = sm.u.alpha[t][i];
+                    pall *= al;
+                    if (r > 0) {
+                        ep *= al;
+                        em *= __frcp_rn(al);
+                    }
+                    const float kv = bf2f(sm.k[t][i]), qv = bf2f(sm.q[t][i]);
+                    sm.k[t][i] = f32_to_bf16(kv * ep).bits;
+                    sm.km[t][i] = f32_to_bf16(kv * em).bits;
+                    sm.q[t][i] = f32_to_bf16(qv * ep).bits;
+                }
+                sm.uw.blk.pa[blk][i] = pall;
+                sm.uw.blk.px[blk][i] = ep;
+                sm.uw.blk.af[blk][i] = sm.u.alpha[16 * blk][i];
+            }
+        }
+        __syncthreads();
+        if constexpr (KDA) {
+            // per channel: F[m] = e^{g_{16m}}, H[m] = e^{g_C - g_{16m}},
+            // D[m][n] = e^{g_{16m} - g_{16n}}, all as products of alphas
+            if (tid < DK) {
+                const int i = tid;
+                float pa[4], px[4], af[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    pa[m] = sm.uw.blk.pa[m][i];
+                    px[m] = sm.uw.blk.px[m][i];
+                    af[m] = sm.uw.blk.af[m][i];
+                }
+                float pre = 1.f;  // product of the whole blocks before m
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    sm.F[m][i] = pre * af[m];
+                    pre *= pa[m];
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    float post = px[m];
+#pragma unroll
+                    for (int mm = m + 1; mm < 4; ++mm) post *= pa[mm];
+                    sm.Hf[m][i] = post;
+                }
+                const int pm[6] = {1, 2, 3, 2, 3, 3}, pn[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll
+                for (int p = 0; p < 6; ++p) {
+                    float d = px[pn[p]] * af[pm[p]];
+#pragma unroll
+                    for (int bb = pn[p] + 1; bb < pm[p]; ++bb) d *= pa[bb];
+                    sm.D[p][i] = d;
+                }
+                sm.gC[i] = pre;
+            }
+            __syncthreads();
+        }
+
+        // ---------------- phase 1: K K^T, Q K^T, K S0, Q S0 ----------------
+        // G rows block w (tiles tn <= w) and P' rows block 3-w (tiles tn <= 3-w)
+        f32x4_t gt[4], pt[4];
+        const int pr = 3 - w;
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
+            gt[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            pt[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            const int kc = 32 * s + (lane >> 4) * 8;
+            const bf16x8_t ak = load_bf16x8(&sm.k[16 * w + (lane & 15)][kc]);
+            const bf16x8_t aq = load_bf16x8(&sm.q[16 * pr + (lane & 15)][kc]);
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) {
+                const int jrow = 16 * tn + (lane & 15);
+                bf16x8_t bk;
+                if constexpr (!KDA) {
+                    bk = load_bf16x8(&sm.k[jrow][kc]);
+                    if (tn <= w) gt[tn] = mfma_bf16(ak, bk, gt[tn]);
+                    if (tn <= pr) pt[tn] = mfma_bf16(aq, bk, pt[tn]);
+                } else {
+                    const uint16_t* kmr = &sm.km[jrow][kc];
+                    if (tn <= w) {
+                        bf16x8_t bb;
+                        if (tn == w) {
+                            bb = load_bf16x8(kmr);
+                        } else {
+                            const int p = (w - tn == 1) ? (w - 1) : (w - tn == 2 ? 1 + w : 5);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) bb[e] = bf(bf2f(kmr[e]) * sm.D[p][kc + e]);
+                        }
+                        gt[tn] = mfma_bf16(ak, bb, gt[tn]);
+                    }
+                    if (tn <= pr) {
+                        bf16x8_t bb;
+                        if (tn == pr) {
+                            bb = load_bf16x8(kmr);
+                        } else {
+                            const int p = (pr - tn == 1) ? (pr - 1) : (pr - tn == 2 ? 1 + pr : 5);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) bb[e] = bf(bf2f(kmr[e]) * sm.D[p][kc + e]);
+                        }
+                        pt[tn] = mfma_bf16(aq, bb, pt[tn]);
+                    }
+                }
+            }
+        }
+        // K S0 and Q S0 for row block w
+        f32x4_t ks[2], qs[2];
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+            ks[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            qs[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            const int kc = 32 * s + (lane >> 4) * 8;
+            bf16x8_t ak, aq;
+            if constexpr (!KDA) {
+                ak = load_bf16x8(&sm.k[16 * w + (lane & 15)][kc]);
+                aq = load_bf16x8(&sm.q[16 * w + (lane & 15)][kc]);
+            } else {  // Kt = Kp * F[w], Qt = Qp * F[w]
+                const uint16_t* kr = &sm.k[16 * w + (lane & 15)][kc];
+                const uint16_t* qr = &sm.q[16 * w + (lane & 15)][kc];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = sm.F[w][kc + e];
+                    ak[e] = bf(bf2f(kr[e]) * f);
+                    aq[e] = bf(bf2f(qr[e]) * f);
+                }
+            }
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                const bf16x8_t bs = load_bf16x8(&sm.St[16 * y + (lane & 15)][kc]);
+                ks[y] = mfma_bf16(ak, bs, ks[y]);
+                qs[y] = mfma_bf16(aq, bs, qs[y]);
+            }
+        }
+        __syncthreads();
+        // write A (strictly lower, beta and decay applied) and P (causal) tiles
+        {
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 16 * w + (lane >> 4) * 4 + j;
+                    const int jj = 16 * tn + (lane & 15);
+                    float av = 0.f;
+                    if (tn <= w && jj < t) {
+                        av = gt[tn][j] * sm.beta[t];
+                        if (!KDA) av *= __expf(sm.g[t] - sm.g[jj]);
+                    }
+                    sm.u.s.A[t][jj] = av;
+                    const int tp = 16 * pr + (lane >> 4) * 4 + j;
+                    float pv = 0.f;
+                    if (tn <= pr && jj <= tp) {
+                        pv = pt[tn][j];
+                        if (!KDA) pv *= __expf(sm.g[tp] - sm.g[jj]);
+                    }
+                    sm.P[tp][jj] = pv;
+                }
+            }
+        }
+        // X = diag(beta) (V - Kt S0) for rows of block w
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * w + (lane >> 4) * 4 + j;
+                const int n = 16 * y + (lane & 15);
+                float kt = ks[y][j];
+                if (!KDA) kt *= __expf(sm.g[t]);
+                sm.X[t][n] = sm.beta[t] * (sm.V[t][n] - kt);
+            }
+        __syncthreads();
+
+        // ---------------- T = (I + A)^{-1} ----------------
+        if (w == 0) {
+            // diagonal blocks by forward substitution; lane = (block bb, column cc)
+            const int bb = lane >> 4, cc = lane & 15;
+            float tv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+                for (int jj = 0; jj < r; ++jj) acc = fmaf(-sm.u.s.A[16 * bb + r][16 * bb + jj], tv[jj], acc);
+                tv[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.u.s.Tm[16 * bb + r][16 * bb + cc] = tv[r];
+        } else {
+            // zero the strictly upper blocks of T
+            for (int e = tid - 64; e < 6 * 256; e += NTH - 64) {
+                const int blkid = e >> 8, within = e & 255;
+                const int bi = (blkid < 3) ? 0 : (blkid < 5 ? 1 : 2);
+                const int bj = (blkid < 3) ? 1 + blkid : (blkid < 5 ? blkid - 1 : 3);
+                sm.u.s.Tm[16 * bi + (within >> 4)][16 * bj + (within & 15)] = 0.f;
+            }
+        }
+        __syncthreads();
+        {
+            // stage 1: L_ij = T_ii A_ij (in place in A); pairs (1,0),(2,1),(3,2),(2,0),(3,1),(3,0)
+            const int pi[6] = {1, 2, 3, 2, 3, 3}, pj[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll
+            for (int rep = 0; rep < 2; ++rep) {
+                const int p = w + 4 * rep;
+                if (p < 6) {
+                    const int i = pi[p], j = pj[p];
+                    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    acc = mm16_f32(&sm.u.s.Tm[16 * i][16 * i], LDF, &sm.u.s.A[16 * i][16 * j], LDF, acc, lane);
+                    store16(&sm.u.s.A[16 * i][16 * j], LDF, acc, lane, 1.f);
+                }
+            }
+        }
+        __syncthreads();
+        {
+            // stage 2: L^2 blocks (2,0), (3,1), (3,0) into T's (then overwritten) blocks
+            f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (w == 0) {
+                acc = mm16_f32(&sm.u.s.A[32][16], LDF, &sm.u.s.A[16][0], LDF, acc, lane);  // L21 L10
+                store16(&sm.u.s.Tm[32][0], LDF, acc, lane, 1.f);
+            } else if (w == 1) {
+                acc = mm16_f32(&sm.u.s.A[48][32], LDF, &sm.u.s.A[32][16], LDF, acc, lane);  // L32 L21
+                store16(&sm.u.s.Tm[48][16], LDF, acc, lane, 1.f);
+            } else if (w == 2) {
+                acc = mm16_f32(&sm.u.s.A[48][16], LDF, &sm.u.s.A[16][0], LDF, acc, lane);  // L31 L10
+                acc = mm16_f32(&sm.u.s.A[48][32], LDF, &sm.u.s.A[32][0], LDF, acc, lane);  // + L32 L20
+                store16(&sm.u.s.Tm[48][0], LDF, acc, lane, 1.f);
+            }
+        }
+        __syncthreads();
+        if (w == 0) {
+            // stage 3: (L^3)_30 = L32 (L^2)_20
+            f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc = mm16_f32(&sm.u.s.A[48][32], LDF, &sm.u.s.Tm[32][0], LDF, acc, lane);
+            store16(&sm.L3[0][0], 17, acc, lane, 1.f);
+        }
+        __syncthreads();
+        {
+            // stage 4: T_ij = M_ij T_jj with M = -L + L^2 - L^3 (block-wise)
+            const int pi[6] = {1, 2, 3, 2, 3, 3}, pj[6] = {0, 1, 2, 0, 1, 0};
+            f32x4_t res[2];
+#pragma unroll
+            for (int rep = 0; rep < 2; ++rep) {
+                res[rep] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                const int p = w + 4 * rep;
+                if (p < 6) {
+                    const int i = pi[p], j = pj[p];
+                    const bool has2 = (p >= 3);
+                    const bool has3 = (p == 5);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int kk = 4 * s + (lane >> 4);
+                        const int r = lane & 15;
+                        float m = -sm.u.s.A[16 * i + r][16 * j + kk];
+                        if (has2) m += sm.u.s.Tm[16 * i + r][16 * j + kk];
+                        if (has3) m -= sm.L3[r][kk];
+                        res[rep] = mfma_f32(m, sm.u.s.Tm[16 * j + kk][16 * j + (lane & 15)], res[rep]);
+                    }
+                }
+            }
+            __syncthreads();  // all reads of the L^2 scratch done before T overwrites it
+#pragma unroll
+            for (int rep = 0; rep < 2; ++rep) {
+                const int p = w + 4 * rep;
+                if (p < 6) store16(&sm.u.s.Tm[16 * pi[p]][16 * pj[p]], LDF, res[rep], lane, 1.f);
+            }
+        }
+        __syncthreads();
+
+        // ---------------- U = T X ----------------
+        {
+            f32x4_t ut[2];
+#pragma unroll
+            for (int y = 0; y < 2; ++y) ut[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (s == 1 && w < 2) continue;  // T[t][j] = 0 for j >= 32 when t < 32
+                const int kc = 32 * s + (lane >> 4) * 8;
+                bf16x8_t at;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) at[e] = bf(sm.u.s.Tm[16 * w + (lane & 15)][kc + e]);
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    bf16x8_t bx;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bx[e] = bf(sm.X[kc + e][16 * y + (lane & 15)]);
+                    ut[y] = mfma_bf16(at, bx, ut[y]);
+                }
+            }
+#pragma unroll
+            for (int y = 0; y < 2; ++y) store16(&sm.uw.U[16 * w][16 * y], LDX, ut[y], lane, 1.f);
+        }
+        __syncthreads();
+
+        // ---------------- O = Qt S0 + P U ----------------
+        {
+            f32x4_t ot[2];
+#pragma unroll
+            for (int y = 0; y < 2; ++y) ot[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (s == 1 && w < 2) continue;
+                const int kc = 32 * s + (lane >> 4) * 8;
+                bf16x8_t ap;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ap[e] = bf(sm.P[16 * w + (lane & 15)][kc + e]);
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    bf16x8_t bu;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bu[e] = bf(sm.uw.U[kc + e][16 * y + (lane & 15)]);
+                    ot[y] = mfma_bf16(ap, bu, ot[y]);
+                }
+            }
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 16 * w + (lane >> 4) * 4 + j;
+                    const int n = 16 * y + (lane & 15);
+                    float qv = qs[y][j];
+                    if (!KDA) qv *= __expf(sm.g[t]);
+                    if (t < Tc)
+                        og[(((size_t)b * T + t0 + t) * H + h) * dv + n0 + n] =
+                            from_f32<io_t>(qv + ot[y][j]);
+                }
+        }
+
+        // ---------------- S = e^{g_C} S0 + Kh^T U ----------------
+        {
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
+                        S[x][y][j] *= KDA ? sm.gC[i] : decC_s;
+                    }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int kc = 32 * s + (lane >> 4) * 8;  // tokens
+                bf16x8_t bu[2];
+#pragma unroll
+                for (int y = 0; y < 2; ++y)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float u = sm.uw.U[kc + e][16 * y + (lane & 15)];
+                        if (!KDA) u *= __expf(sm.g[C - 1] - sm.g[kc + e]);
+                        bu[y][e] = bf(u);
+                    }
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    const int i = 16 * (2 * w + x) + (lane & 15);
+                    bf16x8_t ak;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int t = kc + e;
+                        if constexpr (!KDA) {
+                            ak[e] = __builtin_bit_cast(__bf16, sm.k[t][i]);
+                        } else {
+                            ak[e] = bf(bf2f(sm.km[t][i]) * sm.Hf[t >> 4][i]);
+                        }
+                    }
+#pragma unroll
+                    for (int y = 0; y < 2; ++y) S[x][y] = mfma_bf16(ak, bu[y], S[x][y]);
+                }
+            }
+        }
+        __syncthreads();  // everyone is done with this chunk's LDS contents
+        if (c + 1 < nchunks) commit(pf);
+        publish_state();
+        __syncthreads();
+    }
+
+    // final state slice
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
+                const int n = 16 * y + (lane & 15);
+                a.S_out[(((size_t)b * H + h) * DK + i) * dv + n0 + n] = S[x][y][j];
+            }
+}
+
+}  // namespace
+
+hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, const void* q,
+                            const void* k, const void* v, const float* alpha, const float* beta,
+                            const float* S0, float* S_out, void* o, hipStream_t st) {
+    GdnArgs a{B, T, H, dv, q, k, v, alpha, beta, S0, S_out, o};
+    dim3 grid((unsigned)(B * H * (dv / DVB)));
+    if (dtype != 1) return hipErrorInvalidValue;  // bf16 inputs only (checked by the C ABI)
+    if (kda) gdn_chunk_kernel<bf16_t, true><<<grid, NTH, 0, st>>>(a);
+    else gdn_chunk_kernel<bf16_t, false><<<grid, NTH, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace sslp

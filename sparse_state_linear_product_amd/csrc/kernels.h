@@ -31,4 +31,9 @@ struct SdmUpdateArgs {
 };
 hipError_t launch_sdm_update(const SdmUpdateArgs& a, hipStream_t st);
 
+// ---- Gated DeltaNet / KDA ----
+hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, const void* q,
+                            const void* k, const void* v, const float* alpha, const float* beta,
+                            const float* S0, float* S_out, void* o, hipStream_t st);
+
 }  // namespace sslp
