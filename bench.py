@@ -85,6 +85,84 @@ def bench_sdm(args, torch, sslp, wl):
                       bytes_per_launch=nbytes, bytes_per_token_head=per))
 
 
+def time_call(torch, fn, reps, warmup=2):
+    """Average milliseconds of fn() on the current stream (HIP events)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def gdn_flops(B, T, H, dk, dv, C=64):
+    """Lean chunked-WY FLOP count per call: 2*(2C*dk + 1.5C*dv + 3*dk*dv) per token-head."""
+    return 2 * (2 * C * dk + 1.5 * C * dv + 3 * dk * dv) * B * T * H
+
+
+def gdn_bytes(B, T, H, dk, dv, kda):
+    """q, k, v bf16 in; o bf16 out; alpha (per token or per channel) and beta fp32; state out."""
+    per = 2 * (2 * dk + dv) + 2 * dv + 4 * (dk if kda else 1) + 4
+    return per * B * T * H + 4 * B * H * dk * dv
+
+
+def bench_rows(args, torch, sslp, wl):
+    rows = {}
+    dev = torch.device("cuda:0")
+    for cfg in (wl.GDN, wl.KDA):
+        x = {k: v.to(dev) for k, v in wl.gdn_inputs(cfg).items()}
+        o = torch.empty_like(x["v"])
+        S = torch.empty((cfg.B, cfg.H, cfg.d_k, cfg.d_v), dtype=torch.float32, device=dev)
+        ms = time_call(torch, lambda: sslp.gdn_chunk_forward(x["q"], x["k"], x["v"], x["alpha"],
+                                                             x["beta"], S_out=S, o=o), args.steps)
+        fl = gdn_flops(cfg.B, cfg.T, cfg.H, cfg.d_k, cfg.d_v)
+        by = gdn_bytes(cfg.B, cfg.T, cfg.H, cfg.d_k, cfg.d_v, cfg.kda)
+        rows[cfg.name] = dict(ms=round(ms, 4), tokens_per_s=round(cfg.B * cfg.T / (ms * 1e-3), 1),
+                              tflops=round(fl / (ms * 1e-3) / 1e12, 2),
+                              mfma_frac=round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                              gbs=round(by / (ms * 1e-3) / 1e9, 1),
+                              hbm_frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              flops_per_call=fl, bytes_per_call=by)
+        del x, o, S
+    # SDM decode: 64 independent sequences on the 1.4B-layer table shape
+    cfg = wl.SDM_DECODE
+    M = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d_v), dtype=torch.float32, device=dev)
+    M.normal_(generator=torch.Generator(device=dev).manual_seed(cfg.seed))
+    pre = wl.sdm_inputs(cfg, T=wl.DECODE_PREFIX, seed=cfg.seed + 1)
+    pre = {k: v.to(dev) for k, v in pre.items()}
+    sslp.sdm_forward(pre["sw1"], pre["sw2"], pre["sr1"], pre["sr2"], pre["v"], pre["alpha"],
+                     pre["beta"], M, cfg.k_w, cfg.k_r, cfg.W, cfg.R)
+    del pre
+    steps = {k: v.to(dev) for k, v in wl.sdm_inputs(cfg, T=args.decode_steps).items()}
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    y = torch.empty((cfg.B, cfg.H, cfg.d_v), dtype=cfg.dtype, device=dev)
+    sl = [{k: v[:, t].contiguous() for k, v in steps.items()} for t in range(args.decode_steps)]
+
+    def run_steps():
+        for s in sl:
+            sslp.sdm_decode_step(s["sw1"], s["sw2"], s["sr1"], s["sr2"], s["v"], s["alpha"],
+                                 s["beta"], M, cfg.k_w, cfg.k_r, cfg.W, cfg.R, y=y, workspace=ws)
+
+    ms = time_call(torch, run_steps, 1, warmup=1) / args.decode_steps
+    nbytes, per = sdm_kernel_bytes(cfg, 2)
+    nbytes = per * cfg.B * cfg.H
+    rows[cfg.name] = dict(ms_per_step=round(ms, 4), tokens_per_s=round(cfg.B / (ms * 1e-3), 1),
+                          gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          bytes_per_step=nbytes, steps=args.decode_steps)
+    del M
+    torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline_sdm(wl, torch):
     import numpy as np
 
@@ -116,6 +194,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows")
+    ap.add_argument("--decode-steps", type=int, default=50)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -147,6 +227,8 @@ def main():
                    "state": "fp32", "residual": "shared"},
         "roofline": r["roofline"],
     }
+    if not args.no_rows:
+        out["rows"] = bench_rows(args, torch, sslp, wl)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_sdm(wl, torch)
     print(json.dumps(out), flush=True)

@@ -167,7 +167,8 @@ int sdm_sparse_update(const sslp_sdm_shape* shape, int dtype, int residual_mode,
 /* Gated DeltaNet / Kimi Delta Attention (dense limit: every slot selected)  */
 /* ------------------------------------------------------------------------ */
 
-/*   B, T, H; d_k = d_v = 128 (other sizes SSLP_ERR_UNSUPPORTED); chunk = 64. */
+/*   B, T, H; d_k = d_v = 128 and chunk = 64 (other sizes SSLP_ERR_UNSUPPORTED);
+ *   bf16 q/k/v (SSLP_FP32 is SSLP_ERR_UNSUPPORTED). */
 typedef struct {
     int B, T, H, d_k, d_v, chunk;
 } sslp_gdn_shape;
@@ -199,8 +200,8 @@ int gdn_chunk_forward(const sslp_gdn_shape* shape, int dtype, int decay_mode, co
 /* Sparse State Expansion                                                    */
 /* ------------------------------------------------------------------------ */
 
-/*   B, T, H; N routed partitions 1..64 plus one shared; topk 1..min(N,8);
- *   c = d = 128 (other sizes SSLP_ERR_UNSUPPORTED); chunk = 64. */
+/*   B, T, H; N routed partitions 1..8 plus one shared; topk 1..min(N,4);
+ *   c = d = 128 and chunk = 64 (other sizes SSLP_ERR_UNSUPPORTED); bf16 q/k/v. */
 typedef struct {
     int B, T, H, N, topk, c, d, chunk;
 } sslp_sse_shape;

@@ -90,6 +90,21 @@ size_t addressing_bytes(const sslp_sdm_shape* s, int T) {
     return align_up(bth * s->W * 4) * 2 + align_up(bth * s->R * 4) * 2;
 }
 
+long long slots(const sslp_sdm_shape* s) { return (long long)s->sqrtN * s->sqrtN; }
+
+// bytes the recurrence itself needs (records of the pipelined kernel)
+size_t recurrence_bytes(const sslp_sdm_shape* s, int T) {
+    if (!sslp::sdm_pipe_supported(s->W, s->R, s->d_v, slots(s))) return 0;
+    return align_up(sslp::sdm_pipe_record_bytes(s->B, T, s->H, s->W, s->R));
+}
+
+hipError_t run_recurrence(const sslp::SdmUpdateArgs& a, const sslp_sdm_shape* s, void* rec,
+                          hipStream_t st) {
+    if (sslp::sdm_pipe_supported(s->W, s->R, s->d_v, slots(s)))
+        return sslp::launch_sdm_update_pipe(a, rec, st);
+    return sslp::launch_sdm_update(a, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,12 +114,12 @@ int sslp_version(void) { return SSLP_VERSION; }
 
 size_t sdm_workspace_size(const sslp_sdm_shape* s) {
     if (check_sdm_shape(s, false) != SSLP_OK) return 0;
-    return addressing_bytes(s, s->T);
+    return addressing_bytes(s, s->T) + recurrence_bytes(s, s->T);
 }
 
 size_t sdm_decode_workspace_size(const sslp_sdm_shape* s) {
     if (check_sdm_shape(s, false) != SSLP_OK) return 0;
-    return addressing_bytes(s, 1);
+    return addressing_bytes(s, 1) + recurrence_bytes(s, 1);
 }
 
 int sdm_address(const sslp_sdm_shape* s, int dtype, const void* s1, const void* s2, int k,
@@ -175,7 +190,7 @@ int sdm_sparse_update(const sslp_sdm_shape* s, int dtype, int residual_mode, con
     a.beta = beta;
     a.M = M;
     a.y = y;
-    return hip_status(sslp::launch_sdm_update(a, (hipStream_t)stream), "sdm update launch");
+    return hip_status(run_recurrence(a, s, workspace, (hipStream_t)stream), "sdm update launch");
 }
 
 static int sdm_run(const sslp_sdm_shape* s, int T, int dtype, int residual_mode, const void* sw1,
@@ -241,7 +256,7 @@ static int sdm_run(const sslp_sdm_shape* s, int T, int dtype, int residual_mode,
     a.beta = beta;
     a.M = M;
     a.y = y;
-    return hip_status(sslp::launch_sdm_update(a, st), "sdm update launch");
+    return hip_status(run_recurrence(a, s, ws + addressing_bytes(s, T), st), "sdm update launch");
 }
 
 int sdm_forward(const sslp_sdm_shape* s, int dtype, int residual_mode, const void* sw1,
@@ -325,7 +340,7 @@ static int check_sse_shape(const sslp_sse_shape* s) {
     REQUIRE(s->B >= 1 && s->H >= 1 && s->T >= 0, SSLP_ERR_INVALID_ARG, "bad B/T/H");
     REQUIRE(s->N >= 1 && s->topk >= 1 && s->topk <= s->N, SSLP_ERR_INVALID_ARG,
             "need 1 <= topk <= N (topk=%d N=%d)", s->topk, s->N);
-    REQUIRE(s->N <= 64 && s->topk <= 8, SSLP_ERR_UNSUPPORTED, "need N <= 64 and topk <= 8");
+    REQUIRE(s->N <= 8 && s->topk <= 4, SSLP_ERR_UNSUPPORTED, "need N <= 8 and topk <= 4");
     REQUIRE(s->c >= 1 && s->d >= 1 && s->chunk >= 1, SSLP_ERR_INVALID_ARG,
             "c, d, chunk must be >= 1");
     REQUIRE(s->c == 128 && s->d == 128 && s->chunk == 64, SSLP_ERR_UNSUPPORTED,
@@ -345,21 +360,26 @@ int sse_forward(const sslp_sse_shape* s, int dtype, const float* gate_logits, co
     g_err[0] = 0;
     if (int rc = check_sse_shape(s)) return rc;
     if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE(dtype == SSLP_BF16, SSLP_ERR_UNSUPPORTED,
+            "sse_forward supports bf16 q/k/v only (got dtype %d)", dtype);
+    REQUIRE_PTR(S);
+    REQUIRE_ALIGNED(q_sh);
+    REQUIRE_ALIGNED(k_sh);
+    REQUIRE_ALIGNED(sel);
+    REQUIRE_ALIGNED(e_sel);
+    if (s->T == 0) return SSLP_OK;
     REQUIRE_PTR(gate_logits);
     REQUIRE_PTR(q);
     REQUIRE_PTR(k);
     REQUIRE_PTR(v);
     REQUIRE_PTR(lambda);
-    REQUIRE_ALIGNED(q_sh);
-    REQUIRE_ALIGNED(k_sh);
-    REQUIRE_PTR(S);
     REQUIRE_PTR(o);
-    REQUIRE_ALIGNED(sel);
-    REQUIRE_ALIGNED(e_sel);
     (void)workspace;
     (void)ws_bytes;
-    (void)stream;
-    return fail(SSLP_ERR_UNSUPPORTED, "sse_forward: kernel not built into this library");
+    return hip_status(sslp::launch_sse(s->B, s->T, s->H, s->N, s->topk, s->d, dtype, gate_logits,
+                                       q, k, v, lambda, q_sh, k_sh, S, o, sel, e_sel,
+                                       (hipStream_t)stream),
+                      "sse_forward launch");
 }
 
 }  // extern "C"

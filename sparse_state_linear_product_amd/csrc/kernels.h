@@ -31,9 +31,21 @@ struct SdmUpdateArgs {
 };
 hipError_t launch_sdm_update(const SdmUpdateArgs& a, hipStream_t st);
 
+// pipelined recurrence (sdm_pipe.hip): supported budgets/shapes, workspace for
+// its per-token records, and the launcher (records kernel + update kernel)
+bool sdm_pipe_supported(int W, int R, int dv, long long N);
+size_t sdm_pipe_record_bytes(int B, int T, int H, int W, int R);
+hipError_t launch_sdm_update_pipe(const SdmUpdateArgs& a, void* rec, hipStream_t st);
+
 // ---- Gated DeltaNet / KDA ----
 hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, const void* q,
                             const void* k, const void* v, const float* alpha, const float* beta,
                             const float* S0, float* S_out, void* o, hipStream_t st);
+
+// ---- Sparse State Expansion ----
+hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
+                      const float* logits, const void* q, const void* k, const void* v,
+                      const float* lam, const void* q_sh, const void* k_sh, float* S, void* o,
+                      int32_t* sel, float* e_sel, hipStream_t st);
 
 }  // namespace sslp

@@ -1,0 +1,447 @@
+// K5 + K6: Sparse State Expansion forward -- gated top-k routing over N state
+// partitions, per-chunk bucketing of the routed tokens, and the GLA recurrence
+// of every visited partition with decay advancing only on visits, plus the
+// always-active shared partition.
+//
+// Slides "Scaling Linear Attention with Sparse State Expansion": "One gate
+// controls both writes and reads" (Eqs. (9)-(14)): e_t = softmax(logits),
+// T_t = top-k, S^i_t = Lambda_t S^i_{t-1} + e^i_t k_t^T v_t for i in T_t (else
+// unchanged), o_t = sum_{i in T_t} e^i_t q_t S^i_t; "A memory decays only when
+// its partition is visited"; "Varlen groups tokens while preserving causal
+// order" (group by partition, keep time order, one batched pass, then sum);
+// backup "Selected gate mass is usually below one" (no renormalisation).
+// The shared partition (index N) is visited by every token with weight 1 and
+// its own key/query (the slides leave its formula out; reading stated in the
+// header).
+//
+// Execution.  One workgroup per (batch, head, 32-column block of d) walks the
+// sequence in chunks of 64 tokens.  Per chunk, wave 0 routes the tokens (fp32
+// softmax and top-k, ties to the lowest index) and builds, for every routed
+// partition, the time-ordered list of its visits inside the chunk (ballot +
+// popcount counting sort).  Then every partition is advanced independently by
+// its own wavefront: routed partition i by wave 2+i (32 columns), the shared
+// partition by waves 0 and 1 (16 columns each).  A wave processes its visits
+// in blocks of up to 16 as one GLA step in chunked form:
+//     o_p   = e_p [ (q_p * AF E+_p) S + sum_{p'<=p} e_p' (q_p * E+_p).(k_p' * E-_p') v_p' ]
+//     S_new = (AF PX) S + sum_p' (k_p' * PX E-_p')^T e_p' v_p'
+// with AF the first visit's decay, E+_p the product of decays after it
+// (E-_p = 1/E+_p, PX = E+ of the last visit): every factor is a product of at
+// most 15 decays.  The state stays in MFMA accumulator registers; the three
+// products run on 16x16x32 / 16x16x16 bf16 MFMA with fp32 accumulation.  The
+// k+1 contributions of a token are summed in a fixed order (routed in rank
+// order, then shared) once all partitions are done with the chunk.
+#include "common.h"
+#include "kernels.h"
+
+namespace sslp {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int C = 64;     // chunk length (tokens)
+constexpr int CR = 128;   // partition rows (key width c)
+constexpr int DB = 32;    // columns of d per workgroup
+constexpr int MAXN = 8;   // routed partitions supported
+constexpr int LDQ = CR + 8;
+constexpr int LDV = 20;
+
+struct __align__(16) WaveScratch {
+    uint16_t qs[16][LDQ];  // q * E+ (bf16)
+    uint16_t ks[16][LDQ];  // k * E- (bf16)
+    uint16_t vt[32][LDV];  // gated values, transposed: vt[n][p] = e_p v_p[n]
+    float af[CR];          // decay of the block's first visit
+    float px[CR];          // product of the decays after the first visit
+};
+
+template <int TOPK>
+struct __align__(16) Smem {
+    WaveScratch ws[MAXN + 2];
+    float contrib[C][TOPK][DB];  // routed contributions by rank
+    float osh[C][DB];            // shared-partition contribution
+    int16_t vis[MAXN][C];        // visits of each routed partition (local token ids)
+    int8_t vrank[MAXN][C];       // rank of the partition in the visiting token's top-k
+    float vgate[MAXN][C];        // its gate value
+    int cnt[MAXN];
+};
+
+SSLP_DEVICE __bf16 bfv(float f) { return __builtin_bit_cast(__bf16, f32_to_bf16(f).bits); }
+SSLP_DEVICE short bfs(float f) { return (short)f32_to_bf16(f).bits; }
+SSLP_DEVICE float bf2f(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+template <typename io_t>
+SSLP_DEVICE float ld(const io_t* p) {
+    return to_f32(*p);
+}
+
+struct SseArgs {
+    int B, T, H, N, topk, dv;
+    const float* logits;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* lam;
+    const void* q_sh;
+    const void* k_sh;
+    float* S;
+    void* o;
+    int32_t* sel;
+    float* e_sel;
+};
+
+// One block of up to 16 visits of one partition on one wave.
+//   NY      number of 16-column tiles this wave owns (2 routed, 1 shared)
+//   St      the partition state slice, accumulator layout: tile (m, y) holds
+//           rows 16m + 4(lane/16) + j, column 16y + lane%16
+//   tok[p]  local token ids of the visits (p < L), gate[p] their weights
+template <typename io_t, int NY>
+SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs& a,
+                           const io_t* qg, const io_t* kg, const io_t* vg, int b, int h, int t0,
+                           int col0, const int* tok, const float* gate, int L, int lane,
+                           f32x4_t (&ot)[NY]) {
+    const int T = a.T, H = a.H;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    // ---- a. decay-scaled operands (lane owns rows lane and lane + 64) ----
+    {
+        float ep0 = 1.f, ep1 = 1.f, em0 = 1.f, em1 = 1.f, af0 = 1.f, af1 = 1.f;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
+            if (p < L) {
+                const size_t bth = ((size_t)b * T + t0 + tok[p]) * H + h;
+                const float l0 = a.lam[bth * CR + lane], l1 = a.lam[bth * CR + lane + 64];
+                q0 = ld(qg + bth * CR + lane);
+                q1 = ld(qg + bth * CR + lane + 64);
+                k0 = ld(kg + bth * CR + lane);
+                k1 = ld(kg + bth * CR + lane + 64);
+                if (p == 0) {
+                    af0 = l0;
+                    af1 = l1;
+                } else {
+                    ep0 *= l0;
+                    ep1 *= l1;
+                    em0 *= __frcp_rn(l0);
+                    em1 *= __frcp_rn(l1);
+                }
+            }
+            ws.qs[p][lane] = f32_to_bf16(q0 * ep0).bits;
+            ws.qs[p][lane + 64] = f32_to_bf16(q1 * ep1).bits;
+            ws.ks[p][lane] = f32_to_bf16(k0 * em0).bits;
+            ws.ks[p][lane + 64] = f32_to_bf16(k1 * em1).bits;
+        }
+        ws.af[lane] = af0;
+        ws.af[lane + 64] = af1;
+        ws.px[lane] = ep0;
+        ws.px[lane + 64] = ep1;
+        // gated values, transposed
+#pragma unroll
+        for (int e = 0; e < NY * 16 * 16 / 64; ++e) {
+            const int idx = lane + 64 * e;
+            const int p = idx >> (NY == 2 ? 5 : 4), n = idx & (NY * 16 - 1);
+            float val = 0.f;
+            if (p < L) {
+                const size_t bth = ((size_t)b * T + t0 + tok[p]) * H + h;
+                val = gate[p] * ld(vg + bth * a.dv + col0 + n);
+            }
+            ws.vt[n][p] = f32_to_bf16(val).bits;
+        }
+    }
+    wave_sync();
+    // ---- b. state decayed by the first visit (per row) ----
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float4 f = *reinterpret_cast<const float4*>(&ws.af[16 * m + 4 * g4]);
+#pragma unroll
+        for (int y = 0; y < NY; ++y) {
+            St[m][y][0] *= f.x;
+            St[m][y][1] *= f.y;
+            St[m][y][2] *= f.z;
+            St[m][y][3] *= f.w;
+        }
+    }
+    // ---- c. O^T = S^T (Qs)^T, k-slots of group g4 = rows {32s+4g4+j, 32s+16+4g4+j} ----
+#pragma unroll
+    for (int y = 0; y < NY; ++y) ot[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        bf16x8_t bq;
+        {
+            const uint16_t* r0 = &ws.qs[l16][32 * s + 4 * g4];
+            const uint16_t* r1 = &ws.qs[l16][32 * s + 16 + 4 * g4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bq[j] = __builtin_bit_cast(__bf16, r0[j]);
+                bq[4 + j] = __builtin_bit_cast(__bf16, r1[j]);
+            }
+        }
+#pragma unroll
+        for (int y = 0; y < NY; ++y) {
+            bf16x8_t as;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                as[j] = bfv(St[2 * s][y][j]);
+                as[4 + j] = bfv(St[2 * s + 1][y][j]);
+            }
+            ot[y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as, bq, ot[y], 0, 0, 0);
+        }
+    }
+    // ---- d. Pm^T[p'][p] = Ks Qs^T, causal within the block ----
+    f32x4_t pm = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(&ws.ks[l16][32 * s + 8 * g4]);
+        const bf16x8_t bq = *reinterpret_cast<const bf16x8_t*>(&ws.qs[l16][32 * s + 8 * g4]);
+        pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq, pm, 0, 0, 0);
+    }
+    s16x4_t bp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int pp = 4 * g4 + j;  // p' (row), column p = l16
+        bp[j] = bfs((pp <= l16 && l16 < L) ? pm[j] : 0.f);
+    }
+    // ---- e. O^T += Ve^T Pm^T ----
+#pragma unroll
+    for (int y = 0; y < NY; ++y) {
+        s16x4_t av;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = (short)ws.vt[16 * y + l16][4 * g4 + i];
+        ot[y] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bp, ot[y], 0, 0, 0);
+    }
+    // ---- g. S = PX * S + (Ks * PX)^T Ve ----
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float4 f = *reinterpret_cast<const float4*>(&ws.px[16 * m + 4 * g4]);
+        const float pxr = ws.px[16 * m + l16];
+        s16x4_t ak;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ak[i] = bfs(bf2f(ws.ks[4 * g4 + i][16 * m + l16]) * pxr);
+#pragma unroll
+        for (int y = 0; y < NY; ++y) {
+            St[m][y][0] *= f.x;
+            St[m][y][1] *= f.y;
+            St[m][y][2] *= f.z;
+            St[m][y][3] *= f.w;
+            s16x4_t bv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[i] = (short)ws.vt[16 * y + l16][4 * g4 + i];
+            St[m][y] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, bv, St[m][y], 0, 0, 0);
+        }
+    }
+    wave_sync();
+}
+
+template <typename io_t, int TOPK>
+__global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
+    __shared__ Smem<TOPK> sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nblk = a.dv / DB;
+    const int cb = blockIdx.x % nblk;
+    const int bh = blockIdx.x / nblk;
+    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+    const int n0 = cb * DB;
+    const int T = a.T, H = a.H, N = a.N, topk = a.topk, dv = a.dv;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const io_t* qg = static_cast<const io_t*>(a.q);
+    const io_t* kg = static_cast<const io_t*>(a.k);
+    const io_t* vg = static_cast<const io_t*>(a.v);
+    const io_t* qsh = a.q_sh ? static_cast<const io_t*>(a.q_sh) : qg;
+    const io_t* ksh = a.k_sh ? static_cast<const io_t*>(a.k_sh) : kg;
+    io_t* og = static_cast<io_t*>(a.o);
+
+    // role of this wave: 0,1 shared partition (16 columns each); 2+i routed partition i
+    const bool shared = w < 2;
+    const int part = shared ? N : w - 2;
+    const bool active = shared || part < N;
+    constexpr int NYR = 2;
+    f32x4_t Sr[8][NYR];  // routed state slice (32 columns) or shared (first tile used)
+    const int colw = shared ? 16 * w : 0;  // column offset inside the block
+    float* Sg = a.S + (((size_t)b * H + h) * (N + 1) + part) * CR * dv;
+    if (active) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int y = 0; y < NYR; ++y)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * m + 4 * g4 + j;
+                    const int n = colw + 16 * y + l16;
+                    Sr[m][y][j] = (shared && y > 0) ? 0.f : Sg[(size_t)r * dv + n0 + n];
+                }
+    }
+
+    const int nchunks = (T + C - 1) / C;
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const int Tc = (T - t0) < C ? (T - t0) : C;
+        // ---------------- routing and bucketing (wave 0) ----------------
+        if (w == 0) {
+            const int t = lane;
+            int sel[TOPK];
+            float gsel[TOPK];
+#pragma unroll
+            for (int r = 0; r < TOPK; ++r) {
+                sel[r] = -1;
+                gsel[r] = 0.f;
+            }
+            if (t < Tc) {
+                const size_t bth = ((size_t)b * T + t0 + t) * H + h;
+                const float* lg = a.logits + bth * N;
+                float lv[MAXN];
+                float mx = lg[0];
+#pragma unroll
+                for (int i = 0; i < MAXN; ++i) {
+                    lv[i] = i < N ? lg[i] : 0.f;
+                    if (i < N && lv[i] > mx) mx = lv[i];
+                }
+                float z = 0.f;
+#pragma unroll
+                for (int i = 0; i < MAXN; ++i)
+                    if (i < N) z += __expf(lv[i] - mx);
+                unsigned taken = 0;
+#pragma unroll
+                for (int r = 0; r < TOPK; ++r) {
+                    if (r < topk) {
+                        int best = -1;
+#pragma unroll
+                        for (int i = 0; i < MAXN; ++i)
+                            if (i < N && !((taken >> i) & 1u) && (best < 0 || lv[i] > lv[best]))
+                                best = i;
+                        taken |= 1u << best;
+                        sel[r] = best;
+                        gsel[r] = __expf(lv[best] - mx) / z;
+                    }
+                }
+                if (cb == 0) {
+#pragma unroll
+                    for (int r = 0; r < TOPK; ++r)
+                        if (r < topk) {
+                            if (a.sel) a.sel[bth * topk + r] = sel[r];
+                            if (a.e_sel) a.e_sel[bth * topk + r] = gsel[r];
+                        }
+                }
+            }
+            for (int i = 0; i < N; ++i) {
+                bool hit = false;
+                int rk = 0;
+                float gv = 0.f;
+#pragma unroll
+                for (int r = 0; r < TOPK; ++r)
+                    if (sel[r] == i) {
+                        hit = true;
+                        rk = r;
+                        gv = gsel[r];
+                    }
+                const unsigned long long m = __ballot(hit);
+                if (hit) {
+                    const int pos = __popcll(m & ((1ull << lane) - 1ull));
+                    sm.vis[i][pos] = (int16_t)t;
+                    sm.vrank[i][pos] = (int8_t)rk;
+                    sm.vgate[i][pos] = gv;
+                }
+                if (lane == 0) sm.cnt[i] = __popcll(m);
+            }
+        }
+        __syncthreads();
+        // ---------------- every partition advances over its visits ----------------
+        if (active) {
+            WaveScratch& ws = sm.ws[w];
+            if (shared) {
+                for (int bb = 0; bb * 16 < Tc; ++bb) {
+                    int tok[16];
+                    float gate[16];
+#pragma unroll
+                    for (int p = 0; p < 16; ++p) {
+                        tok[p] = 16 * bb + p;
+                        gate[p] = 1.f;
+                    }
+                    const int L = (Tc - 16 * bb) < 16 ? (Tc - 16 * bb) : 16;
+                    f32x4_t Ssh[8][1];
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) Ssh[m][0] = Sr[m][0];
+                    f32x4_t ot[1];
+                    gla_block<io_t, 1>(Ssh, ws, a, qsh, ksh, vg, b, h, t0, n0 + colw, tok, gate, L,
+                                       lane, ot);
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) Sr[m][0] = Ssh[m][0];
+                    // O^T tile: column p = l16, rows n = 4 g4 + j
+                    if (l16 < L) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) sm.osh[16 * bb + l16][colw + 4 * g4 + j] = ot[0][j];
+                    }
+                }
+            } else {
+                const int cnt = sm.cnt[part];
+                for (int p0 = 0; p0 < cnt; p0 += 16) {
+                    int tok[16];
+                    float gate[16];
+#pragma unroll
+                    for (int p = 0; p < 16; ++p) {
+                        const bool ok = p0 + p < cnt;
+                        tok[p] = ok ? sm.vis[part][p0 + p] : 0;
+                        gate[p] = ok ? sm.vgate[part][p0 + p] : 0.f;
+                    }
+                    const int L = (cnt - p0) < 16 ? (cnt - p0) : 16;
+                    f32x4_t ot[NYR];
+                    gla_block<io_t, NYR>(Sr, ws, a, qg, kg, vg, b, h, t0, n0, tok, gate, L, lane,
+                                         ot);
+                    if (l16 < L) {
+                        const int tp = sm.vis[part][p0 + l16];
+                        const int rk = sm.vrank[part][p0 + l16];
+                        const float e = sm.vgate[part][p0 + l16];
+#pragma unroll
+                        for (int y = 0; y < NYR; ++y)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                sm.contrib[tp][rk][16 * y + 4 * g4 + j] = e * ot[y][j];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // ---------------- fixed-order combine: routed by rank, then shared ----------------
+        for (int idx = tid; idx < C * DB; idx += blockDim.x) {
+            const int t = idx / DB, n = idx - (idx / DB) * DB;
+            if (t < Tc) {
+                float acc = 0.f;
+#pragma unroll
+                for (int r = 0; r < TOPK; ++r)
+                    if (r < topk) acc += sm.contrib[t][r][n];
+                acc += sm.osh[t][n];
+                og[(((size_t)b * T + t0 + t) * H + h) * dv + n0 + n] = from_f32<io_t>(acc);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (active) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int y = 0; y < NYR; ++y)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * m + 4 * g4 + j;
+                    const int n = colw + 16 * y + l16;
+                    if (!(shared && y > 0)) Sg[(size_t)r * dv + n0 + n] = Sr[m][y][j];
+                }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
+                      const float* logits, const void* q, const void* k, const void* v,
+                      const float* lam, const void* q_sh, const void* k_sh, float* S, void* o,
+                      int32_t* sel, float* e_sel, hipStream_t st) {
+    if (dtype != 1 || N > MAXN || topk > 4 || dv % DB != 0) return hipErrorInvalidValue;
+    SseArgs a{B, T, H, N, topk, dv, logits, q, k, v, lam, q_sh, k_sh, S, o, sel, e_sel};
+    dim3 grid((unsigned)(B * H * (dv / DB)));
+    dim3 block(64 * (N + 2));
+    if (topk <= 2) sse_chunk_kernel<bf16_t, 2><<<grid, block, 0, st>>>(a);
+    else sse_chunk_kernel<bf16_t, 4><<<grid, block, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace sslp

@@ -1,0 +1,102 @@
+"""GPU parity of the SSE routing + varlen GLA kernel against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_state_linear_product_amd import workloads as wl
+from tests.helpers import TOL_BF16, TOL_FP32, announce, maxrel
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _run(x, N, topk, S0=None, q_sh=None, k_sh=None):
+    import sparse_state_linear_product_amd as sslp
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    B, T, H, _ = x["logits"].shape
+    S = (torch.zeros((B, H, N + 1, 128, 128)) if S0 is None else S0.clone()).to(DEV).contiguous()
+    sel = torch.empty((B, T, H, topk), dtype=torch.int32, device=DEV)
+    e_sel = torch.empty((B, T, H, topk), dtype=torch.float32, device=DEV)
+    o = sslp.sse_forward(xd["logits"], xd["q"], xd["k"], xd["v"], xd["lam"], S, topk,
+                         q_sh=None if q_sh is None else q_sh.to(DEV),
+                         k_sh=None if k_sh is None else k_sh.to(DEV), sel=sel, e_sel=e_sel)
+    torch.cuda.synchronize()
+    return dict(o=o.cpu(), S=S.cpu(), sel=sel.cpu().numpy(), e_sel=e_sel.cpu().numpy())
+
+
+def _ref(x, topk, S0=None, q_sh=None, k_sh=None):
+    n = {k: wl.to_numpy_f32(v) for k, v in x.items()}
+    return oracle.sse(n["logits"], n["q"], n["k"], n["v"], n["lam"], topk,
+                      q_sh=None if q_sh is None else wl.to_numpy_f32(q_sh),
+                      k_sh=None if k_sh is None else wl.to_numpy_f32(k_sh),
+                      S0=None if S0 is None else S0.double().numpy())
+
+
+def _check(x, N, topk, tag, S0=None, q_sh=None, k_sh=None):
+    got = _run(x, N, topk, S0, q_sh, k_sh)
+    ref = _ref(x, topk, S0, q_sh, k_sh)
+    np.testing.assert_array_equal(got["sel"], ref["sel"], err_msg=f"{tag}: selection")
+    e_e = np.abs(got["e_sel"] - ref["e_sel"]).max()
+    e_o = maxrel(got["o"].double().numpy(), ref["o"])
+    e_S = maxrel(got["S"].double().numpy(), ref["S"])
+    print(f"  {tag}: e_sel {e_e:.2e} o {e_o:.2e} S {e_S:.2e}", flush=True)
+    assert e_e <= TOL_FP32
+    assert e_o <= TOL_BF16 and e_S <= TOL_BF16, f"{tag}: o {e_o} S {e_S}"
+    # partitions never selected by any token keep their state bitwise
+    S0n = np.zeros(got["S"].shape, np.float32) if S0 is None else S0.numpy()
+    B, T, H, _ = x["logits"].shape
+    for b in range(B):
+        for h in range(H):
+            used = set(ref["sel"][b, :, h].ravel().tolist())
+            for i in range(N):
+                if i not in used:
+                    assert np.array_equal(got["S"].numpy()[b, h, i], S0n[b, h, i])
+
+
+@pytest.mark.parametrize("T", [1, 23, 64, 130, 400])
+def test_sse_small(T):
+    announce(f"sse_forward N=8 k=2 B=2 H=2 T={T}")
+    x = wl.sse_inputs(wl.SSE, T=T, B=2, H=2, seed=200 + T)
+    _check(x, 8, 2, f"sse T={T}")
+
+
+@pytest.mark.parametrize("N,topk", [(1, 1), (4, 1), (5, 3), (8, 4), (2, 2)])
+def test_sse_partition_counts(N, topk):
+    announce(f"sse_forward N={N} k={topk}")
+    cfg = wl.SseConfig("p", 1, 150, 2, N, topk, 128, 128, torch.bfloat16, 300 + 10 * N + topk)
+    x = wl.sse_inputs(cfg)
+    _check(x, N, topk, f"N={N} k={topk}")
+
+
+def test_sse_initial_state_and_separate_shared_qk():
+    announce("sse_forward with S0 and separate shared q/k")
+    x = wl.sse_inputs(wl.SSE, T=200, B=1, H=2, seed=9)
+    g = torch.Generator().manual_seed(10)
+    S0 = torch.randn((1, 2, 9, 128, 128), generator=g) * 0.1
+    q_sh = torch.randn((1, 200, 2, 128), generator=g).bfloat16()
+    k_sh = torch.softmax(torch.randn((1, 200, 2, 128), generator=g), -1).bfloat16()
+    _check(x, 8, 2, "S0 + shared q/k", S0=S0, q_sh=q_sh, k_sh=k_sh)
+
+
+def test_sse_idle_partition_and_unit_decay():
+    # one partition is never selected (its state must stay bitwise), and a
+    # decay of exactly 1 on a channel with no write keeps that row exactly
+    announce("sse idle partition / unit decay channel")
+    x = wl.sse_inputs(wl.SSE, T=128, B=1, H=1, seed=12)
+    x["logits"][..., 5] = -30.0
+    x["lam"][..., 7] = 1.0
+    x["k"][..., 7] = 0.0
+    g = torch.Generator().manual_seed(13)
+    S0 = torch.randn((1, 1, 9, 128, 128), generator=g)
+    got = _run(x, 8, 2, S0=S0)
+    assert torch.equal(got["S"][0, 0, 5], S0[0, 0, 5])
+    assert torch.equal(got["S"][0, 0, :, 7], S0[0, 0, :, 7])
+
+
+@pytest.mark.slow
+def test_sse_full_config():
+    cfg = wl.SSE
+    announce(f"{cfg.name} full size")
+    x = wl.sse_inputs(cfg)
+    _check(x, cfg.N, cfg.topk, cfg.name)
