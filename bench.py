@@ -132,6 +132,20 @@ def bench_rows(args, torch, sslp, wl):
                               hbm_frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               flops_per_call=fl, bytes_per_call=by)
         del x, o, S
+    # SSE: B=4, T=4096, H=16, 8 routed + 1 shared partition, top-2, c=d=128
+    cfg = wl.SSE
+    x = {k: v.to(dev) for k, v in wl.sse_inputs(cfg).items()}
+    S = torch.zeros((cfg.B, cfg.H, cfg.N + 1, cfg.c, cfg.d), dtype=torch.float32, device=dev)
+    o = torch.empty_like(x["v"])
+    ms = time_call(torch, lambda: sslp.sse_forward(x["logits"], x["q"], x["k"], x["v"], x["lam"],
+                                                   S, cfg.topk, o=o), args.steps)
+    per = 2 * (2 * cfg.c + cfg.d) + 4 * cfg.c + 4 * cfg.N + 2 * cfg.d
+    by = per * cfg.B * cfg.T * cfg.H + 2 * 4 * cfg.B * cfg.H * (cfg.N + 1) * cfg.c * cfg.d
+    rows[cfg.name] = dict(ms=round(ms, 4), tokens_per_s=round(cfg.B * cfg.T / (ms * 1e-3), 1),
+                          gbs=round(by / (ms * 1e-3) / 1e9, 1),
+                          hbm_frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          bytes_per_call=by)
+    del x, S, o
     # SDM decode: 64 independent sequences on the 1.4B-layer table shape
     cfg = wl.SDM_DECODE
     M = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d_v), dtype=torch.float32, device=dev)

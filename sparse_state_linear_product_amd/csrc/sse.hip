@@ -202,12 +202,18 @@ SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs&
         bp[j] = bfs((pp <= l16 && l16 < L) ? pm[j] : 0.f);
     }
     // ---- e. O^T += Ve^T Pm^T ----
+    // (own accumulator, added with VALU: a 16x16x16 MFMA must not take the
+    // accumulator of a 16x16x32 MFMA as its C operand -- the compiler's
+    // hazard handling left that chain unpadded and the C input was stale)
 #pragma unroll
     for (int y = 0; y < NY; ++y) {
         s16x4_t av;
 #pragma unroll
         for (int i = 0; i < 4; ++i) av[i] = (short)ws.vt[16 * y + l16][4 * g4 + i];
-        ot[y] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bp, ot[y], 0, 0, 0);
+        const f32x4_t oe = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            av, bp, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ot[y][j] += oe[j];
     }
     // ---- g. S = PX * S + (Ks * PX)^T Ve ----
 #pragma unroll
