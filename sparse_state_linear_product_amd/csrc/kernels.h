@@ -33,7 +33,7 @@ hipError_t launch_sdm_update(const SdmUpdateArgs& a, hipStream_t st);
 
 // pipelined recurrence (sdm_pipe.hip): supported budgets/shapes, workspace for
 // its per-token records, and the launcher (records kernel + update kernel)
-bool sdm_pipe_supported(int W, int R, int dv, long long N);
+bool sdm_pipe_supported(int B, int T, int H, int W, int R, int dv, long long N);
 size_t sdm_pipe_record_bytes(int B, int T, int H, int W, int R);
 hipError_t launch_sdm_update_pipe(const SdmUpdateArgs& a, void* rec, hipStream_t st);
 

@@ -88,6 +88,14 @@ SMALL = [
     (1, 6, 1, 1000, 8, 64, 64, 128, 128, "f32", 0),
     (3, 17, 1, 5, 4, 5, 2, 25, 1, "f32", 0),
     (1, 1, 1, 1, 4, 1, 1, 1, 1, "f32", 0),
+    # W = R = 32 and T >= 64 take the pipelined kernel: ragged token blocks,
+    # tiny tables (every token's rows collide with the last few tokens' writes,
+    # so nearly every row is forwarded), several column slices
+    (2, 100, 2, 8, 24, 8, 8, 32, 32, "f32", 0),
+    (1, 65, 1, 6, 16, 6, 6, 32, 32, "bf16", 1),
+    (1, 64, 2, 7, 8, 7, 7, 32, 32, "f32", 1),
+    (1, 300, 3, 240, 40, 32, 32, 32, 32, "bf16", 0),
+    (1, 177, 1, 40, 32, 16, 16, 32, 32, "bf16", 1),
 ]
 
 
@@ -305,12 +313,13 @@ def test_sdm_decode_full_size():
     torch.cuda.empty_cache()
 
 
-def test_forward_equals_component_calls():
+@pytest.mark.parametrize("T,W", [(48, 16), (80, 32)])
+def test_forward_equals_component_calls(T, W):
     # sdm_forward is the kernel sequence write-addressing, read-addressing,
     # recurrence; the benchmark issues the same sequence through the component
     # entry points to time the recurrence on its own
     sslp = _sslp()
-    cfg = wl.SdmConfig("compose", 1, 48, 2, 32, 40, 8, 8, 16, 16, torch.bfloat16, 55)
+    cfg = wl.SdmConfig("compose", 1, T, 2, 32, 40, 8, 8, W, W, torch.bfloat16, 55)
     announce("sdm_forward == sdm_address x2 + sdm_sparse_update")
     x = {k: v.to(DEV) for k, v in wl.sdm_inputs(cfg).items()}
     M1 = torch.zeros((cfg.B, cfg.H, cfg.N, cfg.d_v), device=DEV)
