@@ -81,7 +81,8 @@ def bench_sdm(args, torch, sslp, wl):
         cfg=cfg, ms_per_step=total_ms / args.steps, value=tokens / (total_ms * 1e-3),
         roofline=dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                      kernel="sdm_update_kernel", kernel_avg_ms=round(k_avg_ms, 4),
+                      kernel="sdm_sparse_update: sdm_records_kernel + sdm_update_pipe_kernel",
+                      kernel_avg_ms=round(k_avg_ms, 4),
                       bytes_per_launch=nbytes, bytes_per_token_head=per))
 
 
@@ -210,6 +211,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows")
     ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device copy, the reference dispatch for "
+                         "scaling hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -221,6 +225,14 @@ def main():
     import sparse_state_linear_product_amd as sslp
     from sparse_state_linear_product_amd import workloads as wl
 
+    if args.calibrate_copy:
+        n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     r = bench_sdm(args, torch, sslp, wl)
     cfg = r["cfg"]
     out = {
