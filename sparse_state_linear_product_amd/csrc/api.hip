@@ -92,16 +92,16 @@ size_t addressing_bytes(const sslp_sdm_shape* s, int T) {
 
 long long slots(const sslp_sdm_shape* s) { return (long long)s->sqrtN * s->sqrtN; }
 
-// bytes the recurrence itself needs (records of the pipelined kernel)
+// bytes the recurrence itself needs (the chunk plans of the chunk-parallel kernel)
 size_t recurrence_bytes(const sslp_sdm_shape* s, int T) {
-    if (!sslp::sdm_pipe_supported(s->B, T, s->H, s->W, s->R, s->d_v, slots(s))) return 0;
-    return align_up(sslp::sdm_pipe_record_bytes(s->B, T, s->H, s->W, s->R));
+    if (!sslp::sdm_chunked_supported(s->B, T, s->H, s->W, s->R, s->d_v, slots(s))) return 0;
+    return align_up(sslp::sdm_chunk_plan_bytes(s->B, T, s->H));
 }
 
-hipError_t run_recurrence(const sslp::SdmUpdateArgs& a, const sslp_sdm_shape* s, void* rec,
+hipError_t run_recurrence(const sslp::SdmUpdateArgs& a, const sslp_sdm_shape* s, void* plan,
                           hipStream_t st) {
-    if (sslp::sdm_pipe_supported(a.B, a.T, a.H, s->W, s->R, s->d_v, slots(s)))
-        return sslp::launch_sdm_update_pipe(a, rec, st);
+    if (sslp::sdm_chunked_supported(a.B, a.T, a.H, s->W, s->R, s->d_v, slots(s)))
+        return sslp::launch_sdm_update_chunked(a, plan, st);
     return sslp::launch_sdm_update(a, st);
 }
 

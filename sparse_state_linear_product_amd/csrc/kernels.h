@@ -31,11 +31,11 @@ struct SdmUpdateArgs {
 };
 hipError_t launch_sdm_update(const SdmUpdateArgs& a, hipStream_t st);
 
-// pipelined recurrence (sdm_pipe.hip): supported budgets/shapes, workspace for
-// its per-token records, and the launcher (records kernel + update kernel)
-bool sdm_pipe_supported(int B, int T, int H, int W, int R, int dv, long long N);
-size_t sdm_pipe_record_bytes(int B, int T, int H, int W, int R);
-hipError_t launch_sdm_update_pipe(const SdmUpdateArgs& a, void* rec, hipStream_t st);
+// chunk-parallel recurrence (sdm_chunk.hip): supported shapes, workspace for
+// its per-chunk plans, and the launcher (plan kernel + apply kernel)
+bool sdm_chunked_supported(int B, int T, int H, int W, int R, int dv, long long N);
+size_t sdm_chunk_plan_bytes(int B, int T, int H);
+hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* plan, hipStream_t st);
 
 // ---- Gated DeltaNet / KDA ----
 hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, const void* q,

@@ -1,0 +1,815 @@
+// K2 (chunk-parallel): the Sparse Delta Memory recurrence given the addressing,
+// computed 16 tokens at a time.
+//
+// Same operation as the per-token kernel in sdm_update.hip (slides "Sparse
+// Delta Memory: Scaling the State of Linear RNNs through Sparsity", Eqs.
+// (3)-(5), with the shared-prediction figure form or the per-slot form of the
+// residual); here the token recurrence is unrolled over a chunk of C = 16
+// tokens so that no per-token dependency chain remains.
+//
+// Within a chunk every quantity is linear in the chunk-start table M0 and the
+// residuals.  For a slot s, let its write visits in the chunk be tokens
+// tau_1 < tau_2 < ..., each visit multiplying the slot by a decay d (alpha_tau
+// for the shared form, alpha_tau (1 - beta_tau w) for the per-slot form) and
+// adding beta_tau w res_tau.  Then, with P(s, range) the product of d over the
+// visits in the range:
+//   shared form:  res_t = v_t - sum_i alpha_t w_ti M_{t-1}[n_ti]
+//                 M_{t-1}[n] = P(n, <t) M0[n] + sum_{tau<t} P(n, (tau,t)) beta_tau w_tau,n res_tau
+//   so (I + A) res = v - g, g_t = sum_i c_ti M0[n_ti], c_ti = alpha_t w_ti P(n_ti, <t),
+//   A[t][tau] = sum over slots written by both: alpha_t w_ti P(n, (tau,t)) beta_tau w_tau,n;
+//   per-slot form: res_t = v_t (A = 0, c = 0), the per-slot factor lives in d.
+//   reads  y_t = sum_k e_tk M0[m_tk] + sum_{tau<=t} Bm[t][tau] res_tau
+//   final  M_C[s] = P(s, all) M0[s] + sum_visits P(s, (tau, end]) beta_tau w res_tau.
+// A plan kernel derives, per (b, h, chunk), everything that does not depend on
+// the table (row offsets, c, e, T = (I + A)^-1, Bm, per-slot final
+// coefficients, and which rows of the NEXT chunk hold a slot this chunk
+// writes); the apply kernel then streams the table: one wavefront per 8-column
+// slice of a head gathers the chunk's 16 x 64 rows with LDS-DMA
+// (global_load_lds_dwordx4), forms g, h, res = T (v - g), y = h + Bm res,
+// and writes every written slot once with its final value.
+//
+// Pipelining: the rows of chunk c+1 are DMA'd while chunk c is computed, i.e.
+// before chunk c's write-back; rows of chunk c+1 that chunk c writes are then
+// overwritten in LDS with their final values (the plan lists them), after the
+// DMA has landed.  Rows written by earlier chunks were stored before the DMA
+// was issued, by the same wavefront, whose vector memory operations are
+// performed in order.
+#include <utility>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace sslp {
+
+namespace {
+
+constexpr int CC = 16;        // tokens per chunk
+constexpr int CW = 8;         // columns per wavefront
+constexpr int NW = 32;        // write rows per token
+constexpr int NR = 32;        // read rows per token
+constexpr int NQ = NW + NR;   // rows per token
+constexpr int NE = CC * NW;   // write entries per chunk
+
+// plan block of one (b, h, chunk), 32-bit words.  Rows are padded so that the
+// apply kernel's LDS reads of them are free of bank conflicts.
+constexpr int OFFS_LD = 36, COEF_LD = 68, TB_LD = 20;
+constexpr int PL_OFFS = 0;                          // row byte offsets, [q&1][t][q>>1] (ld 36)
+constexpr int PL_COEF = PL_OFFS + 32 * OFFS_LD;     // [t][q] (ld 68): c (q < 32) or e (q >= 32)
+constexpr int PL_TM = PL_COEF + CC * COEF_LD;       // [t][tau] (ld 20): (I + A)^-1
+constexpr int PL_BM = PL_TM + CC * TB_LD;           // [t][tau] (ld 20)
+constexpr int PL_FIN = PL_BM + CC * TB_LD;          // [i][t][4]: P, f, first, packed lists
+constexpr int PL_EXTRA = PL_FIN + NE * 4;           // [512][2]: (tau, f) of earlier visits
+constexpr int PL_FWD = PL_EXTRA + 1024;             // [1024]: staging rows q*16+t of the next chunk
+constexpr int PL_WORDS = 7168;                      // 28 KB
+static_assert(PL_FWD + 1024 <= PL_WORDS, "plan layout");
+static_assert((PL_WORDS * 4) % 1024 == 0, "plan blocks are DMA'd in 1 KB pieces");
+
+// row (q, t) is staged by DMA j = q/2 of wave j%4 (see the apply kernel); a
+// lane's 8 offsets for its wave are contiguous: position (j%4)*8 + j/4
+SSLP_DEVICE int offs_word(int q, int t) {
+    const int j = q >> 1;
+    return PL_OFFS + ((q & 1) * 16 + t) * OFFS_LD + (j & 3) * 8 + (j >> 2);
+}
+SSLP_DEVICE int coef_word(int t, int q) { return PL_COEF + t * COEF_LD + q; }
+SSLP_DEVICE int fin_word(int i, int t) { return PL_FIN + (i * CC + t) * 4; }
+constexpr uint32_t NOT_LAST = 0xFFFFFFFFu;  // FIN "first" of an entry that is not a slot's last visit
+
+struct PlanArgs {
+    int B, T, H, N, dv, nch, mode;
+    const int32_t* idx_w;
+    const float* wt_w;
+    const int32_t* idx_r;
+    const float* wt_r;
+    const float* alpha;
+    const float* beta;
+    uint32_t* plan;  // [B, H, nch, PL_WORDS]
+};
+
+// ---------------------------------------------------------------------------
+// plan kernel: one workgroup of 256 threads per (b, h, chunk)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
+    __shared__ uint64_t key[NE];       // write entries sorted by (slot, token, rank)
+    __shared__ float s_d[NE];          // decay of the visit at sorted position p
+    __shared__ int s_gs[NE], s_ge[NE];  // slot group [gs, ge) of sorted position p
+    __shared__ int s_pos[NE];          // sorted position of write entry e = t*32 + i
+    __shared__ int s_scan[NE];         // group starts, then their inclusive prefix count
+    __shared__ float s_ww[NE];         // write weights by entry
+    __shared__ int s_ir[CC * NR];      // read slots by entry (-1: no token)
+    __shared__ float s_wr[CC * NR];
+    __shared__ int s_rgs[CC * NR], s_rend[CC * NR];  // write visits of a read slot up to its token
+    __shared__ float s_al[CC], s_be[CC];
+    __shared__ float s_A[CC][CC + 1];
+    __shared__ int s_fcnt[NE], s_fbeg[NE], s_ffill[NE];
+
+    const int tid = threadIdx.x;
+    const int nch = a.nch;
+    const int c = blockIdx.x % nch, bh = blockIdx.x / nch;
+    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+    const int t0 = c * CC;
+    const int ntok = a.T - t0 < CC ? a.T - t0 : CC;
+    uint32_t* out = a.plan + (size_t)blockIdx.x * PL_WORDS;
+    const uint64_t NONE = ~0ull;
+
+    // S1: load the chunk's addressing
+    for (int e = tid; e < NE; e += 256) {
+        const int t = e >> 5, i = e & 31;
+        if (t < ntok) {
+            const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
+            key[e] = ((uint64_t)(uint32_t)a.idx_w[bth * NW + i] << 9) | (uint64_t)e;
+            s_ww[e] = a.wt_w[bth * NW + i];
+            s_ir[e] = a.idx_r[bth * NR + i];
+            s_wr[e] = a.wt_r[bth * NR + i];
+        } else {
+            key[e] = NONE;
+            s_ww[e] = 0.f;
+            s_ir[e] = -1;
+            s_wr[e] = 0.f;
+        }
+        s_fcnt[e] = 0;
+        s_ffill[e] = 0;
+    }
+    if (tid < CC) {
+        const bool ok = tid < ntok;
+        const size_t bth = ((size_t)b * a.T + t0 + tid) * a.H + h;
+        s_al[tid] = ok ? a.alpha[bth] : 1.f;
+        s_be[tid] = ok ? a.beta[bth] : 0.f;
+    }
+    __syncthreads();
+
+    // S2: bitonic sort of the 512 keys, ascending
+    for (int k = 2; k <= NE; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int x = tid; x < NE; x += 256) {
+                const int y = x ^ j;
+                if (y > x) {
+                    const uint64_t kx = key[x], ky = key[y];
+                    const bool up = (x & k) == 0;
+                    if ((kx > ky) == up) {
+                        key[x] = ky;
+                        key[y] = kx;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // S3: groups of equal slot (a slot is written at most once per token, so
+    // a group lists its visits in token order), per-visit decays
+    for (int p = tid; p < NE; p += 256) {
+        const uint64_t kp = key[p];
+        const bool valid = kp != NONE;
+        const int e = (int)(kp & 511u);
+        const int t = e >> 5;
+        int gs = p, ge = p + 1;
+        if (valid) {
+            const uint64_t sl = kp >> 9;
+            while (gs > 0 && (key[gs - 1] >> 9) == sl) --gs;
+            while (ge < NE && key[ge] != NONE && (key[ge] >> 9) == sl) ++ge;
+            s_pos[e] = p;
+            s_d[p] = a.mode == 0 ? s_al[t] : s_al[t] * (1.f - s_be[t] * s_ww[e]);
+        } else {
+            s_d[p] = 1.f;
+        }
+        s_gs[p] = gs;
+        s_ge[p] = ge;
+        s_scan[p] = (valid && gs == p) ? 1 : 0;
+    }
+    __syncthreads();
+    // inclusive prefix count of group starts (Hillis-Steele)
+    for (int off = 1; off < NE; off <<= 1) {
+        int v0 = 0, v1 = 0;
+        const int p0 = tid, p1 = tid + 256;
+        v0 = s_scan[p0] + (p0 >= off ? s_scan[p0 - off] : 0);
+        v1 = s_scan[p1] + (p1 >= off ? s_scan[p1 - off] : 0);
+        __syncthreads();
+        s_scan[p0] = v0;
+        s_scan[p1] = v1;
+        __syncthreads();
+    }
+
+    // S4: read entries: the write visits of their slot at or before their token
+    for (int e = tid; e < CC * NR; e += 256) {
+        const int t = e >> 5;
+        const int sl = s_ir[e];
+        int rgs = 0, rend = 0;
+        if (sl >= 0) {
+            // lower bound of (slot << 9) among the sorted keys
+            const uint64_t want = (uint64_t)(uint32_t)sl << 9;
+            int lo = 0, hi = NE;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (key[mid] < want) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo < NE && key[lo] != NONE && (key[lo] >> 9) == (uint64_t)(uint32_t)sl) {
+                rgs = lo;
+                rend = lo;
+                const int ge = s_ge[lo];
+                while (rend < ge && (int)((key[rend] & 511u) >> 5) <= t) ++rend;
+            }
+        }
+        s_rgs[e] = rgs;
+        s_rend[e] = rend;
+    }
+
+    // S5: forward targets: rows of the next chunk whose slot this chunk writes
+    // (counted per group, at the group's last visit)
+    const int t1 = t0 + CC;
+    const int ntok1 = c + 1 < nch ? (a.T - t1 < CC ? a.T - t1 : CC) : 0;
+    int fgrp[4];
+    for (int x = 0; x < 4; ++x) {
+        const int ne = tid + 256 * x;  // 0..1023: q = ne / 16 ... as (t, q)
+        const int t = ne >> 6, q = ne & 63;
+        fgrp[x] = -1;
+        if (t < ntok1) {
+            const size_t bth = ((size_t)b * a.T + t1 + t) * a.H + h;
+            const int sl = q < NW ? a.idx_w[bth * NW + q] : a.idx_r[bth * NR + (q - NW)];
+            const uint64_t want = (uint64_t)(uint32_t)sl << 9;
+            int lo = 0, hi = NE;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (key[mid] < want) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo < NE && key[lo] != NONE && (key[lo] >> 9) == (uint64_t)(uint32_t)sl) {
+                fgrp[x] = s_ge[lo] - 1;
+                atomicAdd(&s_fcnt[fgrp[x]], 1);
+            }
+        }
+    }
+    __syncthreads();
+    // exclusive prefix of the forward counts over sorted positions
+    for (int p = tid; p < NE; p += 256) s_fbeg[p] = s_fcnt[p];
+    __syncthreads();
+    for (int off = 1; off < NE; off <<= 1) {
+        const int p0 = tid, p1 = tid + 256;
+        const int v0 = s_fbeg[p0] + (p0 >= off ? s_fbeg[p0 - off] : 0);
+        const int v1 = s_fbeg[p1] + (p1 >= off ? s_fbeg[p1 - off] : 0);
+        __syncthreads();
+        s_fbeg[p0] = v0;
+        s_fbeg[p1] = v1;
+        __syncthreads();
+    }
+    for (int x = 0; x < 4; ++x) {
+        if (fgrp[x] >= 0) {
+            const int ne = tid + 256 * x;
+            const int t = ne >> 6, q = ne & 63;
+            const int g = fgrp[x];
+            const int slot = atomicAdd(&s_ffill[g], 1);
+            out[PL_FWD + s_fbeg[g] - s_fcnt[g] + slot] = (uint32_t)(q * CC + t);
+        }
+    }
+
+    // S6: per write entry: gather coefficient, final-value data at the last visit
+    for (int e = tid; e < NE; e += 256) {
+        const int t = e >> 5, i = e & 31;
+        uint32_t* fin = out + fin_word(i, t);
+        if (t >= ntok) {
+            out[coef_word(t, i)] = 0u;
+            fin[0] = fin[1] = fin[3] = 0u;
+            fin[2] = NOT_LAST;
+            continue;
+        }
+        const int p = s_pos[e];
+        const int gs = s_gs[p], ge = s_ge[p];
+        float pre = 1.f, post = 1.f;
+        for (int l = gs; l < p; ++l) pre *= s_d[l];
+        for (int l = p + 1; l < ge; ++l) post *= s_d[l];
+        const float w = s_ww[e];
+        out[coef_word(t, i)] = __float_as_uint(a.mode == 0 ? s_al[t] * w * pre : 0.f);
+        const float f = post * s_be[t] * w;
+        if (p == ge - 1) {
+            const float P = pre * s_d[p];
+            const int e1 = (int)(key[gs] & 511u);
+            const uint32_t first = (uint32_t)((e1 & 31) * CC + (e1 >> 5));
+            const int xstart = gs - (s_scan[gs] - 1);  // earlier visits of earlier groups
+            const int xcnt = ge - gs - 1;
+            float suf = 1.f;  // product of decays after visit l
+            for (int l = ge - 2; l >= gs; --l) {
+                suf *= s_d[l + 1];
+                const int el = (int)(key[l] & 511u);
+                out[PL_EXTRA + 2 * (xstart + (l - gs))] = (uint32_t)(el >> 5);
+                out[PL_EXTRA + 2 * (xstart + (l - gs)) + 1] =
+                    __float_as_uint(suf * s_be[el >> 5] * s_ww[el]);
+            }
+            const int fcnt = s_fcnt[p], fbeg = s_fbeg[p] - fcnt;
+            fin[0] = __float_as_uint(P);
+            fin[1] = __float_as_uint(f);
+            fin[2] = first;
+            fin[3] = (uint32_t)xstart | ((uint32_t)xcnt << 10) | ((uint32_t)fbeg << 16) |
+                     ((uint32_t)fcnt << 26);
+        } else {
+            // not the last visit: the slot is written once, at its last visit
+            fin[0] = 0u;
+            fin[1] = __float_as_uint(f);
+            fin[2] = NOT_LAST;
+            fin[3] = 0u;
+        }
+    }
+
+    // S7: read coefficients e = w * P(m, <= t)
+    for (int e = tid; e < CC * NR; e += 256) {
+        const int t = e >> 5, k = e & 31;
+        float pr = 1.f;
+        for (int l = s_rgs[e]; l < s_rend[e]; ++l) pr *= s_d[l];
+        out[coef_word(t, NW + k)] = __float_as_uint(t < ntok ? s_wr[e] * pr : 0.f);
+    }
+
+    // S8: A[t][tau] (shared form) and Bm[t][tau], one thread per pair, sums in a fixed order
+    {
+        const int t = tid >> 4, tau = tid & 15;
+        float av = 0.f, bv = 0.f;
+        if (t < ntok && tau <= t) {
+            if (a.mode == 0 && tau < t) {
+                for (int i = 0; i < NW; ++i) {
+                    const int e = t * NW + i;
+                    const int p = s_pos[e];
+                    float between = 1.f;  // decays of the visits strictly between
+                    for (int l = p - 1; l >= s_gs[p]; --l) {
+                        const int el = (int)(key[l] & 511u);
+                        if ((el >> 5) == tau) {
+                            av += s_al[t] * s_ww[e] * between * s_be[tau] * s_ww[el];
+                            break;
+                        }
+                        between *= s_d[l];
+                    }
+                }
+            }
+            for (int k = 0; k < NR; ++k) {
+                const int e = t * NR + k;
+                float after = 1.f;  // decays of the visits after tau's, up to token t
+                for (int l = s_rend[e] - 1; l >= s_rgs[e]; --l) {
+                    const int el = (int)(key[l] & 511u);
+                    if ((el >> 5) == tau) {
+                        bv += s_wr[e] * after * s_be[tau] * s_ww[el];
+                        break;
+                    }
+                    after *= s_d[l];
+                }
+            }
+        }
+        s_A[t][tau] = av;
+        out[PL_BM + t * TB_LD + tau] = __float_as_uint(bv);
+    }
+    __syncthreads();
+
+    // S9: T = (I + A)^-1 by forward substitution, one column per thread
+    if (tid < CC) {
+        const int j = tid;
+        float col[CC];
+#pragma unroll
+        for (int t = 0; t < CC; ++t) {
+            float v = (t == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int tau = 0; tau < t; ++tau) v -= s_A[t][tau] * col[tau];
+            col[t] = v;
+            out[PL_TM + t * TB_LD + j] = __float_as_uint(v);
+        }
+    }
+
+    // S10: byte offsets of every staged row
+    for (int x = tid; x < CC * NQ; x += 256) {
+        const int t = x >> 6, q = x & 63;
+        uint32_t off = 0u;
+        if (t < ntok) {
+            const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
+            const int sl = q < NW ? a.idx_w[bth * NW + q] : a.idx_r[bth * NR + (q - NW)];
+            off = (uint32_t)sl * (uint32_t)a.dv * 4u;
+        }
+        out[offs_word(q, t)] = off;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// apply kernel helpers
+// ---------------------------------------------------------------------------
+typedef void __attribute__((address_space(3))) * lds_ptr_t;
+typedef float __attribute__((address_space(3))) * lds_f32_ptr_t;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+SSLP_DEVICE void dma16(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+SSLP_DEVICE void dma4(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 4, 0, 0);
+}
+SSLP_DEVICE void wait_vm0() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+    __builtin_amdgcn_sched_barrier(0);
+}
+SSLP_DEVICE uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_f32_ptr_t)p; }
+
+// LDS reads of DMA'd data are issued as inline asm: the compiler cannot tell
+// them from reads that alias an LDS-DMA in flight and would drain the vector
+// memory queue before each.  Their results are tied to an explicit wait
+// (lds_wait) placed before first use; "memory" keeps program order.  OFF is a
+// byte offset folded into the instruction.
+template <int OFF = 0>
+SSLP_DEVICE uint32_t lds_u32(uint32_t a) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF) : "memory");
+    return v;
+}
+template <int OFF = 0>
+SSLP_DEVICE float lds_f32(uint32_t a) {
+    return __uint_as_float(lds_u32<OFF>(a));
+}
+template <int OFF = 0>
+SSLP_DEVICE f32x2 lds_f32x2(uint32_t a) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    f32x2 v;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF) : "memory");
+    return v;
+}
+template <int OFF = 0>
+SSLP_DEVICE f32x4 lds_f32x4(uint32_t a) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    f32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF) : "memory");
+    return v;
+}
+template <int OFF = 0>
+SSLP_DEVICE u32x4 lds_u32x4(uint32_t a) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF) : "memory");
+    return v;
+}
+SSLP_DEVICE void lds_write_f32x2(uint32_t a, f32x2 v) {
+    asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+SSLP_DEVICE void lds_write_f32x4(uint32_t a, f32x4 v) {
+    asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+// wait for all LDS operations; each operand then passes through an empty
+// volatile asm ordered after the wait, so that no use of it is scheduled before
+template <typename X>
+SSLP_DEVICE void tie(X& x) {
+    asm volatile("" : "+v"(x));
+}
+template <typename... V>
+SSLP_DEVICE void lds_wait(V&... v) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+    (tie(v), ...);
+}
+template <typename X, int N>
+SSLP_DEVICE void tie_all(X (&x)[N]) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) tie(x[k]);
+}
+
+SSLP_DEVICE float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+SSLP_DEVICE float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// compile-time loops that pass the index as a template argument
+template <int N, typename F, int... I>
+SSLP_DEVICE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+SSLP_DEVICE void static_for(F&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// ---------------------------------------------------------------------------
+// apply kernel: one workgroup of 4 wavefronts per (b, h, 8-column slice).
+// DMA j (j = 0..31) stages rows q = 2j, 2j+1 of the chunk's 16 tokens; wave w
+// owns the DMAs j = w + 4m: it gathers those rows, forms the partial row sums
+// over them, and writes back the write rows among them.  Four wavefronts keep
+// four times as many gathers in flight per CU as one, and split the compute.
+// ---------------------------------------------------------------------------
+constexpr int NWAVE = 4;
+
+template <typename io_t>
+__global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateArgs a,
+                                                                     const uint32_t* __restrict__ plan,
+                                                                     int nslice, int total, int nch) {
+    constexpr int VB = CC * CW * (int)sizeof(io_t);  // value bytes of a chunk
+    constexpr int VDMA = VB / 256;                   // dword DMAs per chunk
+    constexpr int ROWB = CC * CW * 4;                // bytes of one staged row index q (16 tokens)
+    constexpr int NPIECE = PL_WORDS / 256;           // 1 KB plan pieces
+    static_assert(VB % 256 == 0, "values are DMA'd in 256-byte pieces");
+    static_assert(NPIECE % NWAVE == 0, "plan pieces split evenly over the wavefronts");
+
+    __shared__ __align__(16) float stage[2][NQ * CC][CW];  // rows (q, t) at q*16 + t
+    __shared__ __align__(16) uint32_t pbuf[3][PL_WORDS];
+    __shared__ __align__(16) uint32_t vbuf[2][VB / 4];
+    __shared__ __align__(16) float part[NWAVE][2][CC][CW];  // partial g, h per wave
+    __shared__ __align__(16) float xr[CC][CW];             // v - g
+    __shared__ __align__(16) float xs[CC][CW];             // residuals
+
+    // XCD-aware placement: the 16 slices of a 128-column group share an XCD
+    const int id = blockIdx.x;
+    const int xcd = id & 7, kq = id >> 3;
+    const int L = (kq >> 4) * 128 + xcd * 16 + (kq & 15);
+    if (L >= total) return;
+    const int bh = L / nslice, slice = L - (L / nslice) * nslice;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col0 = slice * CW;
+    const int T = a.T, H = a.H, dv = a.dv;
+    const int b = bh / H, h = bh - (bh / H) * H;
+    const char* tabc = reinterpret_cast<const char*>(a.M + (size_t)bh * a.N * dv);
+    char* tabw = reinterpret_cast<char*>(a.M + (size_t)bh * a.N * dv);
+    const char* vin = static_cast<const char*>(a.v);
+    char* yout = static_cast<char*>(a.y);
+    const uint32_t* planb = plan + (size_t)bh * nch * PL_WORDS;
+
+    const uint32_t stage0 = lds_addr(&stage[0][0][0]);
+    const uint32_t pbuf0 = lds_addr(&pbuf[0][0]);
+    const uint32_t vbuf0 = lds_addr(&vbuf[0][0]);
+    const uint32_t part0 = lds_addr(&part[0][0][0][0]);
+    const uint32_t xr0 = lds_addr(&xr[0][0]);
+    const uint32_t xs0 = lds_addr(&xs[0][0]);
+    constexpr uint32_t STAGE_BYTES = NQ * CC * CW * 4;
+    constexpr uint32_t PLAN_BYTES = PL_WORDS * 4;
+
+    // DMA lane mapping (also the write-back mapping): lane l covers 16 bytes
+    // (half l%2) of row (q = 2j + l/32, t = (l/2) % 16)
+    const int dq = lane >> 5, dt = (lane >> 1) & 15, dh = lane & 1;
+    const uint32_t colbyte = 4u * (uint32_t)(col0 + 4 * dh);
+    // this lane's 8 row offsets for its wave's DMAs j = wave + 4m, m = 0..7
+    const uint32_t offs_lane = 4u * (uint32_t)(PL_OFFS + (dq * 16 + dt) * OFFS_LD + wave * 8);
+
+    auto plan_dma = [&](int ch) {  // this wave's pieces of chunk ch's plan -> pbuf[ch % 3]
+        const uint32_t* src = planb + (size_t)ch * PL_WORDS;
+        uint32_t* dst = &pbuf[ch % 3][0];
+#pragma unroll
+        for (int k = 0; k < NPIECE / NWAVE; ++k) {
+            const int s = wave + NWAVE * k;
+            dma16(src + s * 256 + 4 * lane, dst + s * 256);
+        }
+    };
+    auto row_dma = [&](int ch) {  // this wave's rows of chunk ch -> stage[ch % 2]
+        const uint32_t ob = pbuf0 + (uint32_t)(ch % 3) * PLAN_BYTES + offs_lane;
+        u32x4 o[2];
+        o[0] = lds_u32x4<0>(ob);
+        o[1] = lds_u32x4<16>(ob);
+        lds_wait(o[0], o[1]);
+        float* dst = &stage[ch % 2][0][0];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int j = wave + 4 * m;
+            dma16(tabc + o[m >> 2][m & 3] + colbyte, dst + j * 256);
+        }
+        if (wave == 0) {
+            const int tb = ch * CC;
+#pragma unroll
+            for (int s = 0; s < VDMA; ++s) {
+                const int byte = (s * 64 + lane) * 4;
+                const int tt = tb + byte / (CW * (int)sizeof(io_t));
+                const char* src = tt < T ? vin + ((((size_t)b * T + tt) * H + h) * dv + col0) * sizeof(io_t) +
+                                               byte % (CW * (int)sizeof(io_t))
+                                         : vin;
+                dma4(src, &vbuf[ch % 2][s * 64]);
+            }
+        }
+    };
+
+    // -- prologue: plans of chunks 0 and 1, rows and values of chunk 0 --
+    plan_dma(0);
+    if (nch > 1) plan_dma(1);
+    wait_vm0();
+    __syncthreads();
+    row_dma(0);
+    wait_vm0();
+    __syncthreads();
+
+    // compute mapping: lane (t, qt) = (lane/4, lane%4) owns columns 2qt, 2qt+1 of token t
+    const int ct = lane >> 2, qt = lane & 3;
+    const uint32_t cofs = (uint32_t)((ct * CW + 2 * qt) * 4);  // (token, column pair) in a row
+    const uint32_t xq = (uint32_t)(2 * qt * 4);
+
+    for (int c = 0; c < nch; ++c) {
+        const int ntok = T - c * CC < CC ? T - c * CC : CC;
+        const uint32_t P = pbuf0 + (uint32_t)(c % 3) * PLAN_BYTES;
+        const uint32_t S = stage0 + (uint32_t)(c % 2) * STAGE_BYTES;
+        if (c + 1 < nch) row_dma(c + 1);
+        if (c + 2 < nch) plan_dma(c + 2);
+
+        // ---- partial g, h over this wave's rows: q = 2j, 2j+1 for j = wave + 4m ----
+        {
+            f32x2 cf[8], rw[16];
+            const uint32_t cfa = P + 4u * (uint32_t)coef_word(ct, 2 * wave);  // + 32 bytes per m
+            const uint32_t rowa = S + cofs + (uint32_t)(2 * wave * ROWB);     // + 8 rows per m
+            static_for<8>([&](auto m) {
+                cf[m] = lds_f32x2<32 * m>(cfa);
+                rw[2 * m] = lds_f32x2<8 * m * ROWB>(rowa);
+                rw[2 * m + 1] = lds_f32x2<(8 * m + 1) * ROWB>(rowa);
+            });
+            lds_wait();
+            tie_all(cf);
+            tie_all(rw);
+            f32x2 g = {0.f, 0.f}, hh = {0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                f32x2& acc = m < 4 ? g : hh;
+                acc.x = fmaf(cf[m].x, rw[2 * m].x, acc.x);
+                acc.y = fmaf(cf[m].x, rw[2 * m].y, acc.y);
+                acc.x = fmaf(cf[m].y, rw[2 * m + 1].x, acc.x);
+                acc.y = fmaf(cf[m].y, rw[2 * m + 1].y, acc.y);
+            }
+            lds_write_f32x2(part0 + (uint32_t)((wave * 2 + 0) * CC * CW * 4) + cofs, g);
+            lds_write_f32x2(part0 + (uint32_t)((wave * 2 + 1) * CC * CW * 4) + cofs, hh);
+        }
+        __syncthreads();
+
+        // ---- wave 0: g, h, r = v - g, res = T r, y = h + Bm res ----
+        const bool tok_ok = ct < ntok;
+        if (wave == 0) {
+            f32x2 pg[NWAVE], ph[NWAVE];
+            static_for<NWAVE>([&](auto w) {
+                pg[w] = lds_f32x2<(w * 2 + 0) * CC * CW * 4>(part0 + cofs);
+                ph[w] = lds_f32x2<(w * 2 + 1) * CC * CW * 4>(part0 + cofs);
+            });
+            float v0, v1;
+            const uint32_t va = vbuf0 + (uint32_t)((c % 2) * VB + (ct * CW + 2 * qt) * (int)sizeof(io_t));
+            if (sizeof(io_t) == 2) {
+                uint32_t w = lds_u32(va);
+                lds_wait(w);
+                v0 = bf16lo(w);
+                v1 = bf16hi(w);
+            } else {
+                f32x2 w = lds_f32x2(va);
+                lds_wait(w);
+                v0 = w.x;
+                v1 = w.y;
+            }
+            tie_all(pg);
+            tie_all(ph);
+            const float g0 = (pg[0].x + pg[1].x) + (pg[2].x + pg[3].x);
+            const float g1 = (pg[0].y + pg[1].y) + (pg[2].y + pg[3].y);
+            const float h0 = (ph[0].x + ph[1].x) + (ph[2].x + ph[3].x);
+            const float h1 = (ph[0].y + ph[1].y) + (ph[2].y + ph[3].y);
+            f32x2 r;
+            r.x = tok_ok ? v0 - g0 : 0.f;
+            r.y = tok_ok ? v1 - g1 : 0.f;
+            lds_write_f32x2(xr0 + cofs, r);
+            f32x2 res;
+            {
+                f32x4 tm[4];
+                f32x2 rr[CC];
+                const uint32_t ta = P + 4u * (uint32_t)(PL_TM + ct * TB_LD);
+                static_for<4>([&](auto k) { tm[k] = lds_f32x4<16 * k>(ta); });
+                static_for<CC>([&](auto k) { rr[k] = lds_f32x2<k * CW * 4>(xr0 + xq); });
+                lds_wait();
+                tie_all(tm);
+                tie_all(rr);
+                float s0[2] = {0.f, 0.f}, s1[2] = {0.f, 0.f};
+#pragma unroll
+                for (int tau = 0; tau < CC; ++tau) {
+                    const float tv = tm[tau >> 2][tau & 3];
+                    s0[tau & 1] = fmaf(tv, rr[tau].x, s0[tau & 1]);
+                    s1[tau & 1] = fmaf(tv, rr[tau].y, s1[tau & 1]);
+                }
+                res.x = s0[0] + s0[1];
+                res.y = s1[0] + s1[1];
+            }
+            lds_write_f32x2(xs0 + cofs, res);
+            {
+                f32x4 bm[4];
+                f32x2 rs[CC];
+                const uint32_t ba = P + 4u * (uint32_t)(PL_BM + ct * TB_LD);
+                static_for<4>([&](auto k) { bm[k] = lds_f32x4<16 * k>(ba); });
+                static_for<CC>([&](auto k) { rs[k] = lds_f32x2<k * CW * 4>(xs0 + xq); });
+                lds_wait();
+                tie_all(bm);
+                tie_all(rs);
+                float s0[2] = {h0, 0.f}, s1[2] = {h1, 0.f};
+#pragma unroll
+                for (int tau = 0; tau < CC; ++tau) {
+                    const float bv = bm[tau >> 2][tau & 3];
+                    s0[tau & 1] = fmaf(bv, rs[tau].x, s0[tau & 1]);
+                    s1[tau & 1] = fmaf(bv, rs[tau].y, s1[tau & 1]);
+                }
+                const float y0 = s0[0] + s0[1], y1 = s1[0] + s1[1];
+                if (tok_ok) {
+                    char* dst = yout + ((((size_t)b * T + c * CC + ct) * H + h) * dv + col0 + 2 * qt) * sizeof(io_t);
+                    if (sizeof(io_t) == 2) {
+                        const uint32_t w = (uint32_t)f32_to_bf16(y0).bits | ((uint32_t)f32_to_bf16(y1).bits << 16);
+                        *reinterpret_cast<uint32_t*>(dst) = w;
+                    } else {
+                        *reinterpret_cast<float2*>(dst) = make_float2(y0, y1);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- write-back of this wave's write rows (j = wave + 4m, m = 0..3):
+        //      each written slot once, at its last visit; the slot's chunk-start
+        //      row is the entry's own staged row unless visited earlier ----
+        const bool wb_ok = dt < ntok;
+        const uint32_t fina = P + 4u * (uint32_t)fin_word(2 * wave + dq, dt);  // + m * 2048 bytes
+        const uint32_t own = S + (uint32_t)((((2 * wave + dq) * CC + dt) * CW + 4 * dh) * 4);  // + m * 4096
+        f32x4 rj = lds_f32x4(xs0 + (uint32_t)((dt * CW + 4 * dh) * 4));
+        u32x4 offv = lds_u32x4(P + offs_lane);
+        u32x4 fin[4];
+        f32x4 m0[4];
+        static_for<4>([&](auto m) {
+            fin[m] = lds_u32x4<m * 8 * CC * 16>(fina);
+            m0[m] = lds_f32x4<m * 8 * ROWB>(own);
+        });
+        lds_wait(rj, offv);
+        tie_all(fin);
+        tie_all(m0);
+        auto final_value = [&](const u32x4& fn, f32x4 mv, int q) {
+            if (fn.z != (uint32_t)(q * CC + dt)) {
+                mv = lds_f32x4(S + (fn.z * CW + 4 * dh) * 4);
+                lds_wait(mv);
+            }
+            const float Pv = __uint_as_float(fn.x), f = __uint_as_float(fn.y);
+            f32x4 val;
+            val.x = fmaf(f, rj.x, Pv * mv.x);
+            val.y = fmaf(f, rj.y, Pv * mv.y);
+            val.z = fmaf(f, rj.z, Pv * mv.z);
+            val.w = fmaf(f, rj.w, Pv * mv.w);
+            const uint32_t xst = fn.w & 1023u, xcnt = (fn.w >> 10) & 63u;
+            for (uint32_t x = 0; x < xcnt; ++x) {
+                uint32_t tau = lds_u32(P + 4u * (PL_EXTRA + 2 * (xst + x)));
+                float fx = lds_f32(P + 4u * (PL_EXTRA + 2 * (xst + x) + 1));
+                lds_wait(tau, fx);
+                f32x4 rt = lds_f32x4(xs0 + (tau * CW + 4 * dh) * 4);
+                lds_wait(rt);
+                val.x = fmaf(fx, rt.x, val.x);
+                val.y = fmaf(fx, rt.y, val.y);
+                val.z = fmaf(fx, rt.z, val.z);
+                val.w = fmaf(fx, rt.w, val.w);
+            }
+            return val;
+        };
+        bool any_fwd = false;
+        f32x4 keep[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            keep[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!wb_ok || fin[m].z == NOT_LAST) continue;
+            const int q = 2 * (wave + 4 * m) + dq;
+            keep[m] = final_value(fin[m], m0[m], q);
+            *reinterpret_cast<f32x4*>(tabw + offv[m] + colbyte) = keep[m];
+            any_fwd |= (fin[m].w >> 26) != 0u;
+        }
+
+        // ---- rows of chunk c+1 (and plan c+2) have landed in every wave: forward
+        //      this chunk's final values into the rows of chunk c+1 holding the same slot ----
+        wait_vm0();
+        __syncthreads();
+        if (__ballot(any_fwd) != 0ull) {
+            const uint32_t Sn = stage0 + (uint32_t)((c + 1) % 2) * STAGE_BYTES;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t fbeg = (fin[m].w >> 16) & 1023u, fcnt = fin[m].w >> 26;
+                if (!wb_ok || fin[m].z == NOT_LAST) continue;
+                for (uint32_t x = 0; x < fcnt; ++x) {
+                    uint32_t pos = lds_u32(P + 4u * (PL_FWD + fbeg + x));
+                    lds_wait(pos);
+                    lds_write_f32x4(Sn + (pos * CW + 4 * dh) * 4, keep[m]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    wait_vm0();
+}
+
+}  // namespace
+
+// One workgroup per CU (its LDS footprint): meant for long sequences spread
+// over few column slices; decode steps and many-slice batches are left to the
+// per-token kernel, whose occupancy hides the latency instead.
+bool sdm_chunked_supported(int B, int T, int H, int W, int R, int dv, long long N) {
+    if (W != NW || R != NR || dv % CW != 0) return false;
+    if ((unsigned long long)N * (unsigned long long)dv * 4ull >= (1ull << 31)) return false;
+    if (N >= (1ll << 31)) return false;
+    return T >= 64 && (long long)B * H * (dv / CW) <= 1024;
+}
+
+size_t sdm_chunk_plan_bytes(int B, int T, int H) {
+    const long long nch = (T + CC - 1) / CC;
+    return (size_t)B * H * nch * PL_WORDS * 4;
+}
+
+hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* planws, hipStream_t st) {
+    uint32_t* plan = static_cast<uint32_t*>(planws);
+    const int nch = (a.T + CC - 1) / CC;
+    PlanArgs pa{a.B, a.T, a.H, a.N, a.dv, nch, a.residual_mode, a.idx_w, a.wt_w, a.idx_r, a.wt_r,
+                a.alpha, a.beta, plan};
+    sdm_chunk_plan_kernel<<<(unsigned)(a.B * a.H * nch), 256, 0, st>>>(pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nslice = a.dv / CW;
+    const int total = a.B * a.H * nslice;
+    const int grid = ((total + 127) / 128) * 128;
+    if (a.dtype != 0)
+        sdm_chunk_apply_kernel<bf16_t><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
+    else
+        sdm_chunk_apply_kernel<float><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
+    return hipGetLastError();
+}
+
+}  // namespace sslp
