@@ -51,28 +51,37 @@ constexpr int NQ = NW + NR;   // rows per token
 constexpr int NE = CC * NW;   // write entries per chunk
 
 // plan block of one (b, h, chunk), 32-bit words.  Rows are padded so that the
-// apply kernel's LDS reads of them are free of bank conflicts.
+// apply kernel's LDS reads of them are free of bank conflicts.  The fixed part
+// and the first PL_TAILWIN words of the tail are staged in LDS; tail words past
+// that (only with heavy slot reuse) are read from memory.
 constexpr int OFFS_LD = 36, COEF_LD = 68, TB_LD = 20;
-constexpr int PL_OFFS = 0;                          // row byte offsets, [q&1][t][q>>1] (ld 36)
+constexpr int PL_OFFS = 0;                          // row byte offsets (see offs_word)
 constexpr int PL_COEF = PL_OFFS + 32 * OFFS_LD;     // [t][q] (ld 68): c (q < 32) or e (q >= 32)
 constexpr int PL_TM = PL_COEF + CC * COEF_LD;       // [t][tau] (ld 20): (I + A)^-1
 constexpr int PL_BM = PL_TM + CC * TB_LD;           // [t][tau] (ld 20)
-constexpr int PL_FIN = PL_BM + CC * TB_LD;          // [i][t][4]: P, f, first, packed lists
-constexpr int PL_EXTRA = PL_FIN + NE * 4;           // [512][2]: (tau, f) of earlier visits
-constexpr int PL_FWD = PL_EXTRA + 1024;             // [1024]: staging rows q*16+t of the next chunk
-constexpr int PL_WORDS = 7168;                      // 28 KB
-static_assert(PL_FWD + 1024 <= PL_WORDS, "plan layout");
-static_assert((PL_WORDS * 4) % 1024 == 0, "plan blocks are DMA'd in 1 KB pieces");
+constexpr int PL_FIN = PL_BM + CC * TB_LD;          // [i][t][2]: P, f of write entry (t, i)
+constexpr int PL_LAST = PL_FIN + NE * 2;            // [t] bit i: entry (t, i) is its slot's last visit
+constexpr int PL_EXC = PL_LAST + CC;                // [t] bit i: entry (t, i) has an exception record
+constexpr int PL_EXCB = PL_EXC + CC;                // [t] index of token t's first exception record
+constexpr int PL_HDR = PL_EXCB + CC;                // tail offsets of the extra pairs and forward rows
+constexpr int PL_TAIL = 4096;                       // exception records, extra pairs, forward rows
+constexpr int PL_TAILWIN = 2048;
+constexpr int PL_DMA_WORDS = PL_TAIL + PL_TAILWIN;  // 24 KB staged per chunk
+constexpr int PL_WORDS = PL_TAIL + 2 * NE + 2 * NE + 2 * NE;  // worst-case tail
+static_assert(PL_HDR + 4 <= PL_TAIL, "plan layout");
+static_assert((PL_DMA_WORDS * 4) % 1024 == 0 && (PL_WORDS * 4) % 16 == 0, "plan DMA pieces");
+// exception record: (first, packed); packed = extra index (9 bits) | extra count << 9
+// (5 bits) | forward index << 14 (10 bits) | forward count << 24 (6 bits)
 
-// row (q, t) is staged by DMA j = q/2 of wave j%4 (see the apply kernel); a
-// lane's 8 offsets for its wave are contiguous: position (j%4)*8 + j/4
+constexpr int NWAVE = 8;             // wavefronts per apply workgroup
+constexpr int JW = 32 / NWAVE;       // row DMAs per wavefront and chunk
+// row (q, t) is staged by DMA j = q/2 of wave j % NWAVE; a lane's JW offsets for
+// its wave are contiguous
 SSLP_DEVICE int offs_word(int q, int t) {
     const int j = q >> 1;
-    return PL_OFFS + ((q & 1) * 16 + t) * OFFS_LD + (j & 3) * 8 + (j >> 2);
+    return PL_OFFS + ((q & 1) * 16 + t) * OFFS_LD + (j % NWAVE) * JW + j / NWAVE;
 }
 SSLP_DEVICE int coef_word(int t, int q) { return PL_COEF + t * COEF_LD + q; }
-SSLP_DEVICE int fin_word(int i, int t) { return PL_FIN + (i * CC + t) * 4; }
-constexpr uint32_t NOT_LAST = 0xFFFFFFFFu;  // FIN "first" of an entry that is not a slot's last visit
 
 struct PlanArgs {
     int B, T, H, N, dv, nch, mode;
@@ -101,6 +110,12 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     __shared__ float s_al[CC], s_be[CC];
     __shared__ float s_A[CC][CC + 1];
     __shared__ int s_fcnt[NE], s_fbeg[NE], s_ffill[NE];
+    __shared__ int s_fwdl[2 * NE];                      // forward rows, grouped per slot
+    __shared__ float s_P[NE], s_f[NE];                  // by entry
+    __shared__ uint32_t s_first[NE], s_pk[NE];          // by entry (exception data)
+    __shared__ int s_exc[NE];                           // exception flags, then their prefix count
+    __shared__ uint32_t s_xt[NE];                       // extra pairs (tau, f), by extra index
+    __shared__ float s_xf[NE];
 
     const int tid = threadIdx.x;
     const int nch = a.nch;
@@ -258,18 +273,20 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
             const int t = ne >> 6, q = ne & 63;
             const int g = fgrp[x];
             const int slot = atomicAdd(&s_ffill[g], 1);
-            out[PL_FWD + s_fbeg[g] - s_fcnt[g] + slot] = (uint32_t)(q * CC + t);
+            s_fwdl[s_fbeg[g] - s_fcnt[g] + slot] = q * CC + t;
         }
     }
 
     // S6: per write entry: gather coefficient, final-value data at the last visit
     for (int e = tid; e < NE; e += 256) {
         const int t = e >> 5, i = e & 31;
-        uint32_t* fin = out + fin_word(i, t);
+        s_P[e] = 0.f;
+        s_f[e] = 0.f;
+        s_exc[e] = 0;
+        s_first[e] = 0u;
+        s_pk[e] = 0u;
         if (t >= ntok) {
             out[coef_word(t, i)] = 0u;
-            fin[0] = fin[1] = fin[3] = 0u;
-            fin[2] = NOT_LAST;
             continue;
         }
         const int p = s_pos[e];
@@ -279,34 +296,78 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         for (int l = p + 1; l < ge; ++l) post *= s_d[l];
         const float w = s_ww[e];
         out[coef_word(t, i)] = __float_as_uint(a.mode == 0 ? s_al[t] * w * pre : 0.f);
-        const float f = post * s_be[t] * w;
-        if (p == ge - 1) {
-            const float P = pre * s_d[p];
-            const int e1 = (int)(key[gs] & 511u);
-            const uint32_t first = (uint32_t)((e1 & 31) * CC + (e1 >> 5));
-            const int xstart = gs - (s_scan[gs] - 1);  // earlier visits of earlier groups
-            const int xcnt = ge - gs - 1;
-            float suf = 1.f;  // product of decays after visit l
-            for (int l = ge - 2; l >= gs; --l) {
-                suf *= s_d[l + 1];
-                const int el = (int)(key[l] & 511u);
-                out[PL_EXTRA + 2 * (xstart + (l - gs))] = (uint32_t)(el >> 5);
-                out[PL_EXTRA + 2 * (xstart + (l - gs)) + 1] =
-                    __float_as_uint(suf * s_be[el >> 5] * s_ww[el]);
-            }
-            const int fcnt = s_fcnt[p], fbeg = s_fbeg[p] - fcnt;
-            fin[0] = __float_as_uint(P);
-            fin[1] = __float_as_uint(f);
-            fin[2] = first;
-            fin[3] = (uint32_t)xstart | ((uint32_t)xcnt << 10) | ((uint32_t)fbeg << 16) |
-                     ((uint32_t)fcnt << 26);
-        } else {
-            // not the last visit: the slot is written once, at its last visit
-            fin[0] = 0u;
-            fin[1] = __float_as_uint(f);
-            fin[2] = NOT_LAST;
-            fin[3] = 0u;
+        if (p != ge - 1) continue;  // the slot is written once, at its last visit
+        s_P[e] = pre * s_d[p];
+        s_f[e] = post * s_be[t] * w;
+        const int xstart = gs - (s_scan[gs] - 1);  // earlier visits of earlier groups
+        const int xcnt = ge - gs - 1;
+        float suf = 1.f;  // product of decays after visit l
+        for (int l = ge - 2; l >= gs; --l) {
+            suf *= s_d[l + 1];
+            const int el = (int)(key[l] & 511u);
+            s_xt[xstart + (l - gs)] = (uint32_t)(el >> 5);
+            s_xf[xstart + (l - gs)] = suf * s_be[el >> 5] * s_ww[el];
         }
+        const int fcnt = s_fcnt[p], fbeg = s_fbeg[p] - fcnt;
+        if (xcnt > 0 || fcnt > 0) {
+            const int e1 = (int)(key[gs] & 511u);
+            s_exc[e] = 1;
+            s_first[e] = (uint32_t)((e1 & 31) * CC + (e1 >> 5));
+            s_pk[e] = (uint32_t)xstart | ((uint32_t)xcnt << 9) | ((uint32_t)fbeg << 14) |
+                      ((uint32_t)fcnt << 24);
+        }
+    }
+    __syncthreads();
+    // token masks of last visits and exception records
+    if (tid < CC) {
+        uint32_t lm = 0u, em = 0u;
+        for (int i = 0; i < NW && tid < ntok; ++i) {
+            const int e = tid * NW + i, p = s_pos[e];
+            lm |= (s_ge[p] - 1 == p) ? (1u << i) : 0u;
+            em |= s_exc[e] ? (1u << i) : 0u;
+        }
+        out[PL_LAST + tid] = lm;
+        out[PL_EXC + tid] = em;
+    }
+    __syncthreads();
+    // inclusive prefix count of exception flags (entry order)
+    for (int off = 1; off < NE; off <<= 1) {
+        const int p0 = tid, p1 = tid + 256;
+        const int v0 = s_exc[p0] + (p0 >= off ? s_exc[p0 - off] : 0);
+        const int v1 = s_exc[p1] + (p1 >= off ? s_exc[p1 - off] : 0);
+        __syncthreads();
+        s_exc[p0] = v0;
+        s_exc[p1] = v1;
+        __syncthreads();
+    }
+    {
+        const int n_exc = s_exc[NE - 1];
+        const int extra_base = 2 * n_exc;
+        const int nxp = ntok * NW - s_scan[NE - 1];  // valid entries - slot groups = extra pairs
+        const int fwd_base = extra_base + 2 * nxp;
+        const int n_fwd = s_fbeg[NE - 1];
+        if (tid == 0) {
+            out[PL_HDR + 0] = (uint32_t)extra_base;
+            out[PL_HDR + 1] = (uint32_t)fwd_base;
+            out[PL_HDR + 2] = (uint32_t)n_exc;
+            out[PL_HDR + 3] = (uint32_t)(fwd_base + n_fwd);
+        }
+        if (tid < CC) out[PL_EXCB + tid] = (uint32_t)(tid == 0 ? 0 : s_exc[tid * NW - 1]);
+        for (int e = tid; e < NE; e += 256) {
+            const int t = e >> 5, i = e & 31;
+            out[PL_FIN + (i * CC + t) * 2 + 0] = __float_as_uint(s_P[e]);
+            out[PL_FIN + (i * CC + t) * 2 + 1] = __float_as_uint(s_f[e]);
+            const int prev = e == 0 ? 0 : s_exc[e - 1];
+            if (s_exc[e] != prev) {  // entry e has exception record `prev`
+                out[PL_TAIL + 2 * prev + 0] = s_first[e];
+                out[PL_TAIL + 2 * prev + 1] = s_pk[e];
+            }
+        }
+        for (int x = tid; x < nxp; x += 256) {
+            out[PL_TAIL + extra_base + 2 * x + 0] = s_xt[x];
+            out[PL_TAIL + extra_base + 2 * x + 1] = __float_as_uint(s_xf[x]);
+        }
+        for (int x = tid; x < n_fwd; x += 256) out[PL_TAIL + fwd_base + x] = (uint32_t)s_fwdl[x];
     }
 
     // S7: read coefficients e = w * P(m, <= t)
@@ -478,14 +539,13 @@ SSLP_DEVICE void static_for(F&& f) {
 }
 
 // ---------------------------------------------------------------------------
-// apply kernel: one workgroup of 4 wavefronts per (b, h, 8-column slice).
+// apply kernel: one workgroup of NWAVE wavefronts per (b, h, 8-column slice).
 // DMA j (j = 0..31) stages rows q = 2j, 2j+1 of the chunk's 16 tokens; wave w
-// owns the DMAs j = w + 4m: it gathers those rows, forms the partial row sums
-// over them, and writes back the write rows among them.  Four wavefronts keep
-// four times as many gathers in flight per CU as one, and split the compute.
+// owns the DMAs j = w + NWAVE m: it gathers those rows, forms the partial row
+// sums over them, and writes back the write rows among them.  Several
+// wavefronts per CU keep that many times more gathers in flight than one, and
+// split the compute.
 // ---------------------------------------------------------------------------
-constexpr int NWAVE = 4;
-
 template <typename io_t>
 __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateArgs a,
                                                                      const uint32_t* __restrict__ plan,
@@ -493,12 +553,13 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
     constexpr int VB = CC * CW * (int)sizeof(io_t);  // value bytes of a chunk
     constexpr int VDMA = VB / 256;                   // dword DMAs per chunk
     constexpr int ROWB = CC * CW * 4;                // bytes of one staged row index q (16 tokens)
-    constexpr int NPIECE = PL_WORDS / 256;           // 1 KB plan pieces
+    constexpr int NPIECE = PL_DMA_WORDS / 256;       // 1 KB plan pieces per chunk
+    constexpr int WB = 16 / NWAVE;                   // write-row DMAs per wave (j < 16)
     static_assert(VB % 256 == 0, "values are DMA'd in 256-byte pieces");
-    static_assert(NPIECE % NWAVE == 0, "plan pieces split evenly over the wavefronts");
+    static_assert(NPIECE % NWAVE == 0 && JW == 4 && WB >= 1, "work split over the wavefronts");
 
     __shared__ __align__(16) float stage[2][NQ * CC][CW];  // rows (q, t) at q*16 + t
-    __shared__ __align__(16) uint32_t pbuf[3][PL_WORDS];
+    __shared__ __align__(16) uint32_t pbuf[3][PL_DMA_WORDS];
     __shared__ __align__(16) uint32_t vbuf[2][VB / 4];
     __shared__ __align__(16) float part[NWAVE][2][CC][CW];  // partial g, h per wave
     __shared__ __align__(16) float xr[CC][CW];             // v - g
@@ -527,14 +588,14 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
     const uint32_t xr0 = lds_addr(&xr[0][0]);
     const uint32_t xs0 = lds_addr(&xs[0][0]);
     constexpr uint32_t STAGE_BYTES = NQ * CC * CW * 4;
-    constexpr uint32_t PLAN_BYTES = PL_WORDS * 4;
+    constexpr uint32_t PLAN_BYTES = PL_DMA_WORDS * 4;
 
     // DMA lane mapping (also the write-back mapping): lane l covers 16 bytes
     // (half l%2) of row (q = 2j + l/32, t = (l/2) % 16)
     const int dq = lane >> 5, dt = (lane >> 1) & 15, dh = lane & 1;
     const uint32_t colbyte = 4u * (uint32_t)(col0 + 4 * dh);
-    // this lane's 8 row offsets for its wave's DMAs j = wave + 4m, m = 0..7
-    const uint32_t offs_lane = 4u * (uint32_t)(PL_OFFS + (dq * 16 + dt) * OFFS_LD + wave * 8);
+    // this lane's JW row offsets for its wave's DMAs j = wave + NWAVE m
+    const uint32_t offs_lane = 4u * (uint32_t)(PL_OFFS + (dq * 16 + dt) * OFFS_LD + wave * JW);
 
     auto plan_dma = [&](int ch) {  // this wave's pieces of chunk ch's plan -> pbuf[ch % 3]
         const uint32_t* src = planb + (size_t)ch * PL_WORDS;
@@ -546,18 +607,12 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
         }
     };
     auto row_dma = [&](int ch) {  // this wave's rows of chunk ch -> stage[ch % 2]
-        const uint32_t ob = pbuf0 + (uint32_t)(ch % 3) * PLAN_BYTES + offs_lane;
-        u32x4 o[2];
-        o[0] = lds_u32x4<0>(ob);
-        o[1] = lds_u32x4<16>(ob);
-        lds_wait(o[0], o[1]);
+        u32x4 o = lds_u32x4(pbuf0 + (uint32_t)(ch % 3) * PLAN_BYTES + offs_lane);
+        lds_wait(o);
         float* dst = &stage[ch % 2][0][0];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int j = wave + 4 * m;
-            dma16(tabc + o[m >> 2][m & 3] + colbyte, dst + j * 256);
-        }
-        if (wave == 0) {
+        for (int m = 0; m < JW; ++m) dma16(tabc + o[m] + colbyte, dst + (wave + NWAVE * m) * 256);
+        if (wave == NWAVE - 1) {
             const int tb = ch * CC;
 #pragma unroll
             for (int s = 0; s < VDMA; ++s) {
@@ -592,23 +647,23 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
         if (c + 1 < nch) row_dma(c + 1);
         if (c + 2 < nch) plan_dma(c + 2);
 
-        // ---- partial g, h over this wave's rows: q = 2j, 2j+1 for j = wave + 4m ----
+        // ---- partial g, h over this wave's rows: q = 2j, 2j+1 for j = wave + NWAVE m ----
         {
-            f32x2 cf[8], rw[16];
-            const uint32_t cfa = P + 4u * (uint32_t)coef_word(ct, 2 * wave);  // + 32 bytes per m
-            const uint32_t rowa = S + cofs + (uint32_t)(2 * wave * ROWB);     // + 8 rows per m
-            static_for<8>([&](auto m) {
-                cf[m] = lds_f32x2<32 * m>(cfa);
-                rw[2 * m] = lds_f32x2<8 * m * ROWB>(rowa);
-                rw[2 * m + 1] = lds_f32x2<(8 * m + 1) * ROWB>(rowa);
+            f32x2 cf[JW], rw[2 * JW];
+            const uint32_t cfa = P + 4u * (uint32_t)coef_word(ct, 2 * wave);  // + 2 NWAVE words per m
+            const uint32_t rowa = S + cofs + (uint32_t)(2 * wave * ROWB);     // + 2 NWAVE rows per m
+            static_for<JW>([&](auto m) {
+                cf[m] = lds_f32x2<8 * NWAVE * m>(cfa);
+                rw[2 * m] = lds_f32x2<2 * NWAVE * m * ROWB>(rowa);
+                rw[2 * m + 1] = lds_f32x2<(2 * NWAVE * m + 1) * ROWB>(rowa);
             });
             lds_wait();
             tie_all(cf);
             tie_all(rw);
             f32x2 g = {0.f, 0.f}, hh = {0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                f32x2& acc = m < 4 ? g : hh;
+            for (int m = 0; m < JW; ++m) {
+                f32x2& acc = (wave + NWAVE * m) < 16 ? g : hh;  // write rows are q < 32
                 acc.x = fmaf(cf[m].x, rw[2 * m].x, acc.x);
                 acc.y = fmaf(cf[m].x, rw[2 * m].y, acc.y);
                 acc.x = fmaf(cf[m].y, rw[2 * m + 1].x, acc.x);
@@ -642,10 +697,14 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
             }
             tie_all(pg);
             tie_all(ph);
-            const float g0 = (pg[0].x + pg[1].x) + (pg[2].x + pg[3].x);
-            const float g1 = (pg[0].y + pg[1].y) + (pg[2].y + pg[3].y);
-            const float h0 = (ph[0].x + ph[1].x) + (ph[2].x + ph[3].x);
-            const float h1 = (ph[0].y + ph[1].y) + (ph[2].y + ph[3].y);
+            float g0 = 0.f, g1 = 0.f, h0 = 0.f, h1 = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) {
+                g0 += pg[w].x;
+                g1 += pg[w].y;
+                h0 += ph[w].x;
+                h1 += ph[w].y;
+            }
             f32x2 r;
             r.x = tok_ok ? v0 - g0 : 0.f;
             r.y = tok_ok ? v1 - g1 : 0.f;
@@ -701,39 +760,68 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
         }
         __syncthreads();
 
-        // ---- write-back of this wave's write rows (j = wave + 4m, m = 0..3):
-        //      each written slot once, at its last visit; the slot's chunk-start
-        //      row is the entry's own staged row unless visited earlier ----
+        // ---- write-back of this wave's write rows (j = wave + NWAVE m < 16): each
+        //      written slot once, at its last visit; entries with an exception
+        //      record were visited earlier in the chunk or feed the next chunk ----
         const bool wb_ok = dt < ntok;
-        const uint32_t fina = P + 4u * (uint32_t)fin_word(2 * wave + dq, dt);  // + m * 2048 bytes
-        const uint32_t own = S + (uint32_t)((((2 * wave + dq) * CC + dt) * CW + 4 * dh) * 4);  // + m * 4096
+        const uint32_t* tailg = planb + (size_t)c * PL_WORDS + PL_TAIL;
+        auto tail = [&](uint32_t k) -> uint32_t {  // tail word k (LDS window, else memory)
+            if (k < (uint32_t)PL_TAILWIN) {
+                uint32_t v = lds_u32(P + 4u * (PL_TAIL + k));
+                lds_wait(v);
+                return v;
+            }
+            return tailg[k];
+        };
+        const uint32_t q0 = (uint32_t)(2 * wave + dq);  // + 2 NWAVE per m
         f32x4 rj = lds_f32x4(xs0 + (uint32_t)((dt * CW + 4 * dh) * 4));
         u32x4 offv = lds_u32x4(P + offs_lane);
-        u32x4 fin[4];
-        f32x4 m0[4];
-        static_for<4>([&](auto m) {
-            fin[m] = lds_u32x4<m * 8 * CC * 16>(fina);
-            m0[m] = lds_f32x4<m * 8 * ROWB>(own);
+        u32x4 hdr = lds_u32x4(P + 4u * PL_HDR);
+        uint32_t lm = lds_u32(P + 4u * (uint32_t)(PL_LAST + dt));
+        uint32_t em = lds_u32(P + 4u * (uint32_t)(PL_EXC + dt));
+        uint32_t eb = lds_u32(P + 4u * (uint32_t)(PL_EXCB + dt));
+        f32x2 pf[WB];
+        f32x4 m0[WB];
+        const uint32_t fina = P + 4u * (uint32_t)(PL_FIN + (q0 * CC + dt) * 2);  // + 2 NWAVE rows per m
+        const uint32_t own = S + (uint32_t)(((q0 * CC + dt) * CW + 4 * dh) * 4);
+        static_for<WB>([&](auto m) {
+            pf[m] = lds_f32x2<2 * NWAVE * m * CC * 8>(fina);
+            m0[m] = lds_f32x4<2 * NWAVE * m * ROWB>(own);
         });
-        lds_wait(rj, offv);
-        tie_all(fin);
+        lds_wait(rj, offv, hdr, lm, em, eb);
+        tie_all(pf);
         tie_all(m0);
-        auto final_value = [&](const u32x4& fn, f32x4 mv, int q) {
-            if (fn.z != (uint32_t)(q * CC + dt)) {
-                mv = lds_f32x4(S + (fn.z * CW + 4 * dh) * 4);
-                lds_wait(mv);
+        const uint32_t extra_base = hdr.x, fwd_base = hdr.y;
+        bool any_fwd = false;
+        f32x4 keep[WB];
+        uint32_t kpk[WB];
+#pragma unroll
+        for (int m = 0; m < WB; ++m) {
+            const uint32_t q = q0 + 2 * NWAVE * m;
+            kpk[m] = 0u;
+            keep[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!wb_ok || !((lm >> q) & 1u)) continue;
+            f32x4 mv = m0[m];
+            const float Pv = pf[m].x, f = pf[m].y;
+            uint32_t pk = 0u;
+            if ((em >> q) & 1u) {
+                const uint32_t k = eb + (uint32_t)__builtin_popcount(em & ((1u << q) - 1u));
+                const uint32_t first = tail(2 * k);
+                pk = tail(2 * k + 1);
+                if (first != q * CC + dt) {
+                    mv = lds_f32x4(S + (first * CW + 4 * dh) * 4);
+                    lds_wait(mv);
+                }
             }
-            const float Pv = __uint_as_float(fn.x), f = __uint_as_float(fn.y);
             f32x4 val;
             val.x = fmaf(f, rj.x, Pv * mv.x);
             val.y = fmaf(f, rj.y, Pv * mv.y);
             val.z = fmaf(f, rj.z, Pv * mv.z);
             val.w = fmaf(f, rj.w, Pv * mv.w);
-            const uint32_t xst = fn.w & 1023u, xcnt = (fn.w >> 10) & 63u;
+            const uint32_t xst = pk & 511u, xcnt = (pk >> 9) & 31u;
             for (uint32_t x = 0; x < xcnt; ++x) {
-                uint32_t tau = lds_u32(P + 4u * (PL_EXTRA + 2 * (xst + x)));
-                float fx = lds_f32(P + 4u * (PL_EXTRA + 2 * (xst + x) + 1));
-                lds_wait(tau, fx);
+                const uint32_t tau = tail(extra_base + 2 * (xst + x));
+                const float fx = __uint_as_float(tail(extra_base + 2 * (xst + x) + 1));
                 f32x4 rt = lds_f32x4(xs0 + (tau * CW + 4 * dh) * 4);
                 lds_wait(rt);
                 val.x = fmaf(fx, rt.x, val.x);
@@ -741,18 +829,10 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
                 val.z = fmaf(fx, rt.z, val.z);
                 val.w = fmaf(fx, rt.w, val.w);
             }
-            return val;
-        };
-        bool any_fwd = false;
-        f32x4 keep[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            keep[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (!wb_ok || fin[m].z == NOT_LAST) continue;
-            const int q = 2 * (wave + 4 * m) + dq;
-            keep[m] = final_value(fin[m], m0[m], q);
-            *reinterpret_cast<f32x4*>(tabw + offv[m] + colbyte) = keep[m];
-            any_fwd |= (fin[m].w >> 26) != 0u;
+            *reinterpret_cast<f32x4*>(tabw + offv[m] + colbyte) = val;
+            keep[m] = val;
+            kpk[m] = pk;
+            any_fwd |= (pk >> 24) != 0u;
         }
 
         // ---- rows of chunk c+1 (and plan c+2) have landed in every wave: forward
@@ -762,12 +842,10 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
         if (__ballot(any_fwd) != 0ull) {
             const uint32_t Sn = stage0 + (uint32_t)((c + 1) % 2) * STAGE_BYTES;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint32_t fbeg = (fin[m].w >> 16) & 1023u, fcnt = fin[m].w >> 26;
-                if (!wb_ok || fin[m].z == NOT_LAST) continue;
+            for (int m = 0; m < WB; ++m) {
+                const uint32_t fbeg = (kpk[m] >> 14) & 1023u, fcnt = kpk[m] >> 24;
                 for (uint32_t x = 0; x < fcnt; ++x) {
-                    uint32_t pos = lds_u32(P + 4u * (PL_FWD + fbeg + x));
-                    lds_wait(pos);
+                    const uint32_t pos = tail(fwd_base + fbeg + x);
                     lds_write_f32x4(Sn + (pos * CW + 4 * dh) * 4, keep[m]);
                 }
             }
