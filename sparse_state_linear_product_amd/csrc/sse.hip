@@ -30,6 +30,8 @@
 // products run on 16x16x32 / 16x16x16 bf16 MFMA with fp32 accumulation.  The
 // k+1 contributions of a token are summed in a fixed order (routed in rank
 // order, then shared) once all partitions are done with the chunk.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -95,57 +97,79 @@ struct SseArgs {
 //   NY      number of 16-column tiles this wave owns (2 routed, 1 shared)
 //   St      the partition state slice, accumulator layout: tile (m, y) holds
 //           rows 16m + 4(lane/16) + j, column 16y + lane%16
-//   tok[p]  local token ids of the visits (p < L), gate[p] their weights
+//   visits  local token ids and gate weights of the visits (p < L)
 template <typename io_t, int NY>
 SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs& a,
                            const io_t* qg, const io_t* kg, const io_t* vg, int b, int h, int t0,
-                           int col0, const int* tok, const float* gate, int L, int lane,
-                           f32x4_t (&ot)[NY]) {
+                           int col0, const int16_t* vtok, const float* vgate, int tbase, int L,
+                           int lane, f32x4_t (&ot)[NY]) {
+    // visit p: token tok(p) of the chunk with gate gate(p) (LDS lists, or
+    // consecutive tokens from tbase with gate 1)
+    auto tok = [&](int p) { return vtok ? (int)vtok[p] : tbase + p; };
+    auto gate = [&](int p) { return vgate ? vgate[p] : 1.f; };
     const int T = a.T, H = a.H;
     const int g4 = lane >> 4, l16 = lane & 15;
-    // ---- a. decay-scaled operands (lane owns rows lane and lane + 64) ----
+    // ---- a. decay-scaled operands (lane owns rows 2 lane, 2 lane + 1); the
+    //      loads of 8 visits are issued before any of them is used ----
     {
-        float ep0 = 1.f, ep1 = 1.f, em0 = 1.f, em1 = 1.f, af0 = 1.f, af1 = 1.f;
+        constexpr int NV = NY * 16 * 16 / 64;
+        float vv[NV];
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
-            if (p < L) {
-                const size_t bth = ((size_t)b * T + t0 + tok[p]) * H + h;
-                const float l0 = a.lam[bth * CR + lane], l1 = a.lam[bth * CR + lane + 64];
-                q0 = ld(qg + bth * CR + lane);
-                q1 = ld(qg + bth * CR + lane + 64);
-                k0 = ld(kg + bth * CR + lane);
-                k1 = ld(kg + bth * CR + lane + 64);
-                if (p == 0) {
-                    af0 = l0;
-                    af1 = l1;
-                } else {
-                    ep0 *= l0;
-                    ep1 *= l1;
-                    em0 *= __frcp_rn(l0);
-                    em1 *= __frcp_rn(l1);
-                }
-            }
-            ws.qs[p][lane] = f32_to_bf16(q0 * ep0).bits;
-            ws.qs[p][lane + 64] = f32_to_bf16(q1 * ep1).bits;
-            ws.ks[p][lane] = f32_to_bf16(k0 * em0).bits;
-            ws.ks[p][lane + 64] = f32_to_bf16(k1 * em1).bits;
-        }
-        ws.af[lane] = af0;
-        ws.af[lane + 64] = af1;
-        ws.px[lane] = ep0;
-        ws.px[lane + 64] = ep1;
-        // gated values, transposed
-#pragma unroll
-        for (int e = 0; e < NY * 16 * 16 / 64; ++e) {
+        for (int e = 0; e < NV; ++e) {
             const int idx = lane + 64 * e;
             const int p = idx >> (NY == 2 ? 5 : 4), n = idx & (NY * 16 - 1);
-            float val = 0.f;
-            if (p < L) {
-                const size_t bth = ((size_t)b * T + t0 + tok[p]) * H + h;
-                val = gate[p] * ld(vg + bth * a.dv + col0 + n);
+            const int tp = p < L ? tok(p) : tok(0);
+            const size_t bth = ((size_t)b * T + t0 + tp) * H + h;
+            vv[e] = ld(vg + bth * a.dv + col0 + n);
+        }
+        float ep0 = 1.f, ep1 = 1.f, em0 = 1.f, em1 = 1.f, af0 = 1.f, af1 = 1.f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float2 lam[8];
+            uint32_t qw[8], kw[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int p = 8 * half + u;
+                const int tp = p < L ? tok(p) : tok(0);
+                const size_t bth = ((size_t)b * T + t0 + tp) * H + h;
+                lam[u] = *reinterpret_cast<const float2*>(a.lam + bth * CR + 2 * lane);
+                qw[u] = *reinterpret_cast<const uint32_t*>(qg + bth * CR + 2 * lane);
+                kw[u] = *reinterpret_cast<const uint32_t*>(kg + bth * CR + 2 * lane);
             }
-            ws.vt[n][p] = f32_to_bf16(val).bits;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int p = 8 * half + u;
+                float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
+                if (p < L) {
+                    const float l0 = lam[u].x, l1 = lam[u].y;
+                    q0 = __uint_as_float(qw[u] << 16);
+                    q1 = __uint_as_float(qw[u] & 0xFFFF0000u);
+                    k0 = __uint_as_float(kw[u] << 16);
+                    k1 = __uint_as_float(kw[u] & 0xFFFF0000u);
+                    if (p == 0) {
+                        af0 = l0;
+                        af1 = l1;
+                    } else {
+                        ep0 *= l0;
+                        ep1 *= l1;
+                        em0 *= __frcp_rn(l0);
+                        em1 *= __frcp_rn(l1);
+                    }
+                }
+                *reinterpret_cast<uint32_t*>(&ws.qs[p][2 * lane]) =
+                    (uint32_t)f32_to_bf16(q0 * ep0).bits | ((uint32_t)f32_to_bf16(q1 * ep1).bits << 16);
+                *reinterpret_cast<uint32_t*>(&ws.ks[p][2 * lane]) =
+                    (uint32_t)f32_to_bf16(k0 * em0).bits | ((uint32_t)f32_to_bf16(k1 * em1).bits << 16);
+            }
+        }
+        *reinterpret_cast<float2*>(&ws.af[2 * lane]) = make_float2(af0, af1);
+        *reinterpret_cast<float2*>(&ws.px[2 * lane]) = make_float2(ep0, ep1);
+        // gated values, transposed
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+            const int idx = lane + 64 * e;
+            const int p = idx >> (NY == 2 ? 5 : 4), n = idx & (NY * 16 - 1);
+            ws.vt[n][p] = f32_to_bf16(p < L ? gate(p) * vv[e] : 0.f).bits;
         }
     }
     wave_sync();
@@ -260,178 +284,162 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
     const bool shared = w < 2;
     const int part = shared ? N : w - 2;
     const bool active = shared || part < N;
-    constexpr int NYR = 2;
-    f32x4_t Sr[8][NYR];  // routed state slice (32 columns) or shared (first tile used)
     const int colw = shared ? 16 * w : 0;  // column offset inside the block
     float* Sg = a.S + (((size_t)b * H + h) * (N + 1) + part) * CR * dv;
-    if (active) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int y = 0; y < NYR; ++y)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * m + 4 * g4 + j;
-                    const int n = colw + 16 * y + l16;
-                    Sr[m][y][j] = (shared && y > 0) ? 0.f : Sg[(size_t)r * dv + n0 + n];
-                }
-    }
-
     const int nchunks = (T + C - 1) / C;
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const int Tc = (T - t0) < C ? (T - t0) : C;
-        // ---------------- routing and bucketing (wave 0) ----------------
-        if (w == 0) {
-            const int t = lane;
-            int sel[TOPK];
-            float gsel[TOPK];
+
+    // The chunk loop, instantiated per role so that a wave keeps only its own
+    // state slice (accumulator layout) live: NY = 1 (shared, 16 columns) or
+    // NY = 2 (routed, 32 columns).  Both instantiations pass the same barriers.
+    auto run = [&](auto& St, auto nyc) {
+        constexpr int NY = decltype(nyc)::value;
+        if (active) {
 #pragma unroll
-            for (int r = 0; r < TOPK; ++r) {
-                sel[r] = -1;
-                gsel[r] = 0.f;
-            }
-            if (t < Tc) {
-                const size_t bth = ((size_t)b * T + t0 + t) * H + h;
-                const float* lg = a.logits + bth * N;
-                float lv[MAXN];
-                float mx = lg[0];
+            for (int m = 0; m < 8; ++m)
 #pragma unroll
-                for (int i = 0; i < MAXN; ++i) {
-                    lv[i] = i < N ? lg[i] : 0.f;
-                    if (i < N && lv[i] > mx) mx = lv[i];
-                }
-                float z = 0.f;
+                for (int y = 0; y < NY; ++y)
 #pragma unroll
-                for (int i = 0; i < MAXN; ++i)
-                    if (i < N) z += __expf(lv[i] - mx);
-                unsigned taken = 0;
+                    for (int j = 0; j < 4; ++j)
+                        St[m][y][j] = Sg[(size_t)(16 * m + 4 * g4 + j) * dv + n0 + colw + 16 * y + l16];
+        }
+        for (int c = 0; c < nchunks; ++c) {
+            const int t0 = c * C;
+            const int Tc = (T - t0) < C ? (T - t0) : C;
+            // ---------------- routing and bucketing (wave 0) ----------------
+            if (w == 0) {
+                const int t = lane;
+                int sel[TOPK];
+                float gsel[TOPK];
 #pragma unroll
                 for (int r = 0; r < TOPK; ++r) {
-                    if (r < topk) {
-                        int best = -1;
+                    sel[r] = -1;
+                    gsel[r] = 0.f;
+                }
+                if (t < Tc) {
+                    const size_t bth = ((size_t)b * T + t0 + t) * H + h;
+                    const float* lg = a.logits + bth * N;
+                    float lv[MAXN];
+                    float mx = lg[0];
 #pragma unroll
-                        for (int i = 0; i < MAXN; ++i)
-                            if (i < N && !((taken >> i) & 1u) && (best < 0 || lv[i] > lv[best]))
-                                best = i;
-                        taken |= 1u << best;
-                        sel[r] = best;
-                        gsel[r] = __expf(lv[best] - mx) / z;
+                    for (int i = 0; i < MAXN; ++i) {
+                        lv[i] = i < N ? lg[i] : 0.f;
+                        if (i < N && lv[i] > mx) mx = lv[i];
+                    }
+                    float z = 0.f;
+#pragma unroll
+                    for (int i = 0; i < MAXN; ++i)
+                        if (i < N) z += __expf(lv[i] - mx);
+                    unsigned taken = 0;
+#pragma unroll
+                    for (int r = 0; r < TOPK; ++r) {
+                        if (r < topk) {
+                            int best = -1;
+#pragma unroll
+                            for (int i = 0; i < MAXN; ++i)
+                                if (i < N && !((taken >> i) & 1u) && (best < 0 || lv[i] > lv[best]))
+                                    best = i;
+                            taken |= 1u << best;
+                            sel[r] = best;
+                            gsel[r] = __expf(lv[best] - mx) / z;
+                        }
+                    }
+                    if (cb == 0) {
+#pragma unroll
+                        for (int r = 0; r < TOPK; ++r)
+                            if (r < topk) {
+                                if (a.sel) a.sel[bth * topk + r] = sel[r];
+                                if (a.e_sel) a.e_sel[bth * topk + r] = gsel[r];
+                            }
                     }
                 }
-                if (cb == 0) {
+                for (int i = 0; i < N; ++i) {
+                    bool hit = false;
+                    int rk = 0;
+                    float gv = 0.f;
 #pragma unroll
                     for (int r = 0; r < TOPK; ++r)
-                        if (r < topk) {
-                            if (a.sel) a.sel[bth * topk + r] = sel[r];
-                            if (a.e_sel) a.e_sel[bth * topk + r] = gsel[r];
+                        if (sel[r] == i) {
+                            hit = true;
+                            rk = r;
+                            gv = gsel[r];
                         }
-                }
-            }
-            for (int i = 0; i < N; ++i) {
-                bool hit = false;
-                int rk = 0;
-                float gv = 0.f;
-#pragma unroll
-                for (int r = 0; r < TOPK; ++r)
-                    if (sel[r] == i) {
-                        hit = true;
-                        rk = r;
-                        gv = gsel[r];
+                    const unsigned long long m = __ballot(hit);
+                    if (hit) {
+                        const int pos = __popcll(m & ((1ull << lane) - 1ull));
+                        sm.vis[i][pos] = (int16_t)t;
+                        sm.vrank[i][pos] = (int8_t)rk;
+                        sm.vgate[i][pos] = gv;
                     }
-                const unsigned long long m = __ballot(hit);
-                if (hit) {
-                    const int pos = __popcll(m & ((1ull << lane) - 1ull));
-                    sm.vis[i][pos] = (int16_t)t;
-                    sm.vrank[i][pos] = (int8_t)rk;
-                    sm.vgate[i][pos] = gv;
+                    if (lane == 0) sm.cnt[i] = __popcll(m);
                 }
-                if (lane == 0) sm.cnt[i] = __popcll(m);
             }
+            __syncthreads();
+            // ---------------- every partition advances over its visits ----------------
+            if (active) {
+                WaveScratch& ws = sm.ws[w];
+                if constexpr (NY == 1) {
+                    for (int bb = 0; bb * 16 < Tc; ++bb) {
+                        const int L = (Tc - 16 * bb) < 16 ? (Tc - 16 * bb) : 16;
+                        f32x4_t ot[1];
+                        gla_block<io_t, 1>(St, ws, a, qsh, ksh, vg, b, h, t0, n0 + colw, nullptr,
+                                           nullptr, 16 * bb, L, lane, ot);
+                        // O^T tile: column p = l16, rows n = 4 g4 + j
+                        if (l16 < L) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) sm.osh[16 * bb + l16][colw + 4 * g4 + j] = ot[0][j];
+                        }
+                    }
+                } else {
+                    const int cnt = sm.cnt[part];
+                    for (int p0 = 0; p0 < cnt; p0 += 16) {
+                        const int L = (cnt - p0) < 16 ? (cnt - p0) : 16;
+                        f32x4_t ot[NY];
+                        gla_block<io_t, NY>(St, ws, a, qg, kg, vg, b, h, t0, n0, &sm.vis[part][p0],
+                                            &sm.vgate[part][p0], 0, L, lane, ot);
+                        if (l16 < L) {
+                            const int tp = sm.vis[part][p0 + l16];
+                            const int rk = sm.vrank[part][p0 + l16];
+                            const float e = sm.vgate[part][p0 + l16];
+#pragma unroll
+                            for (int y = 0; y < NY; ++y)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    sm.contrib[tp][rk][16 * y + 4 * g4 + j] = e * ot[y][j];
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            // ---------------- fixed-order combine: routed by rank, then shared ----------------
+            for (int idx = tid; idx < C * DB; idx += blockDim.x) {
+                const int t = idx / DB, n = idx - (idx / DB) * DB;
+                if (t < Tc) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int r = 0; r < TOPK; ++r)
+                        if (r < topk) acc += sm.contrib[t][r][n];
+                    acc += sm.osh[t][n];
+                    og[(((size_t)b * T + t0 + t) * H + h) * dv + n0 + n] = from_f32<io_t>(acc);
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        // ---------------- every partition advances over its visits ----------------
         if (active) {
-            WaveScratch& ws = sm.ws[w];
-            if (shared) {
-                for (int bb = 0; bb * 16 < Tc; ++bb) {
-                    int tok[16];
-                    float gate[16];
 #pragma unroll
-                    for (int p = 0; p < 16; ++p) {
-                        tok[p] = 16 * bb + p;
-                        gate[p] = 1.f;
-                    }
-                    const int L = (Tc - 16 * bb) < 16 ? (Tc - 16 * bb) : 16;
-                    f32x4_t Ssh[8][1];
+            for (int m = 0; m < 8; ++m)
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) Ssh[m][0] = Sr[m][0];
-                    f32x4_t ot[1];
-                    gla_block<io_t, 1>(Ssh, ws, a, qsh, ksh, vg, b, h, t0, n0 + colw, tok, gate, L,
-                                       lane, ot);
+                for (int y = 0; y < NY; ++y)
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) Sr[m][0] = Ssh[m][0];
-                    // O^T tile: column p = l16, rows n = 4 g4 + j
-                    if (l16 < L) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) sm.osh[16 * bb + l16][colw + 4 * g4 + j] = ot[0][j];
-                    }
-                }
-            } else {
-                const int cnt = sm.cnt[part];
-                for (int p0 = 0; p0 < cnt; p0 += 16) {
-                    int tok[16];
-                    float gate[16];
-#pragma unroll
-                    for (int p = 0; p < 16; ++p) {
-                        const bool ok = p0 + p < cnt;
-                        tok[p] = ok ? sm.vis[part][p0 + p] : 0;
-                        gate[p] = ok ? sm.vgate[part][p0 + p] : 0.f;
-                    }
-                    const int L = (cnt - p0) < 16 ? (cnt - p0) : 16;
-                    f32x4_t ot[NYR];
-                    gla_block<io_t, NYR>(Sr, ws, a, qg, kg, vg, b, h, t0, n0, tok, gate, L, lane,
-                                         ot);
-                    if (l16 < L) {
-                        const int tp = sm.vis[part][p0 + l16];
-                        const int rk = sm.vrank[part][p0 + l16];
-                        const float e = sm.vgate[part][p0 + l16];
-#pragma unroll
-                        for (int y = 0; y < NYR; ++y)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                sm.contrib[tp][rk][16 * y + 4 * g4 + j] = e * ot[y][j];
-                    }
-                }
-            }
+                    for (int j = 0; j < 4; ++j)
+                        Sg[(size_t)(16 * m + 4 * g4 + j) * dv + n0 + colw + 16 * y + l16] = St[m][y][j];
         }
-        __syncthreads();
-        // ---------------- fixed-order combine: routed by rank, then shared ----------------
-        for (int idx = tid; idx < C * DB; idx += blockDim.x) {
-            const int t = idx / DB, n = idx - (idx / DB) * DB;
-            if (t < Tc) {
-                float acc = 0.f;
-#pragma unroll
-                for (int r = 0; r < TOPK; ++r)
-                    if (r < topk) acc += sm.contrib[t][r][n];
-                acc += sm.osh[t][n];
-                og[(((size_t)b * T + t0 + t) * H + h) * dv + n0 + n] = from_f32<io_t>(acc);
-            }
-        }
-        __syncthreads();
-    }
-
-    if (active) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int y = 0; y < NYR; ++y)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * m + 4 * g4 + j;
-                    const int n = colw + 16 * y + l16;
-                    if (!(shared && y > 0)) Sg[(size_t)r * dv + n0 + n] = Sr[m][y][j];
-                }
+    };
+    if (shared) {
+        f32x4_t St[8][1];
+        run(St, std::integral_constant<int, 1>{});
+    } else {
+        f32x4_t St[8][2];
+        run(St, std::integral_constant<int, 2>{});
     }
 }
 
