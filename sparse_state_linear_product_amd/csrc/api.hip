@@ -348,9 +348,14 @@ static int check_sse_shape(const sslp_sse_shape* s) {
     return SSLP_OK;
 }
 
+// routing results (selected partitions, their gates) when the caller does not take them
+static size_t sse_route_bytes(const sslp_sse_shape* s) {
+    return align_up((size_t)s->B * s->T * s->H * s->topk * 4);
+}
+
 size_t sse_workspace_size(const sslp_sse_shape* s) {
     if (check_sse_shape(s) != SSLP_OK) return 0;
-    return 0;
+    return 2 * sse_route_bytes(s);
 }
 
 int sse_forward(const sslp_sse_shape* s, int dtype, const float* gate_logits, const void* q,
@@ -374,8 +379,14 @@ int sse_forward(const sslp_sse_shape* s, int dtype, const float* gate_logits, co
     REQUIRE_PTR(v);
     REQUIRE_PTR(lambda);
     REQUIRE_PTR(o);
-    (void)workspace;
-    (void)ws_bytes;
+    if (sel == nullptr || e_sel == nullptr) {
+        REQUIRE(workspace != nullptr && ws_bytes >= sse_workspace_size(s), SSLP_ERR_WORKSPACE,
+                "workspace of %zu bytes needed (got %zu)", sse_workspace_size(s), ws_bytes);
+        REQUIRE_ALIGNED(workspace);
+        char* ws = static_cast<char*>(workspace);
+        if (sel == nullptr) sel = reinterpret_cast<int32_t*>(ws);
+        if (e_sel == nullptr) e_sel = reinterpret_cast<float*>(ws + sse_route_bytes(s));
+    }
     return hip_status(sslp::launch_sse(s->B, s->T, s->H, s->N, s->topk, s->d, dtype, gate_logits,
                                        q, k, v, lambda, q_sh, k_sh, S, o, sel, e_sel,
                                        (hipStream_t)stream),

@@ -262,6 +262,38 @@ SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs&
     wave_sync();
 }
 
+// Routing of every token (one thread per (b, t, h)): e = softmax(logits) over
+// the N partitions in fp32, top-k by logit with ties to the lowest index
+// (the selected gate values are not renormalised).
+__global__ __launch_bounds__(256) void sse_route_kernel(const float* __restrict__ logits, int P,
+                                                        int N, int topk, int32_t* __restrict__ sel,
+                                                        float* __restrict__ esel) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= P) return;
+    const float* lg = logits + (size_t)p * N;
+    float lv[MAXN];
+    float mx = lg[0];
+#pragma unroll
+    for (int i = 0; i < MAXN; ++i) {
+        lv[i] = i < N ? lg[i] : 0.f;
+        if (i < N && lv[i] > mx) mx = lv[i];
+    }
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXN; ++i)
+        if (i < N) z += __expf(lv[i] - mx);
+    unsigned taken = 0;
+    for (int r = 0; r < topk; ++r) {
+        int best = -1;
+#pragma unroll
+        for (int i = 0; i < MAXN; ++i)
+            if (i < N && !((taken >> i) & 1u) && (best < 0 || lv[i] > lv[best])) best = i;
+        taken |= 1u << best;
+        sel[(size_t)p * topk + r] = best;
+        esel[(size_t)p * topk + r] = __expf(lv[best] - mx) / z;
+    }
+}
+
 template <typename io_t, int TOPK>
 __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
     __shared__ Smem<TOPK> sm;
@@ -317,40 +349,12 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
                 }
                 if (t < Tc) {
                     const size_t bth = ((size_t)b * T + t0 + t) * H + h;
-                    const float* lg = a.logits + bth * N;
-                    float lv[MAXN];
-                    float mx = lg[0];
 #pragma unroll
-                    for (int i = 0; i < MAXN; ++i) {
-                        lv[i] = i < N ? lg[i] : 0.f;
-                        if (i < N && lv[i] > mx) mx = lv[i];
-                    }
-                    float z = 0.f;
-#pragma unroll
-                    for (int i = 0; i < MAXN; ++i)
-                        if (i < N) z += __expf(lv[i] - mx);
-                    unsigned taken = 0;
-#pragma unroll
-                    for (int r = 0; r < TOPK; ++r) {
+                    for (int r = 0; r < TOPK; ++r)
                         if (r < topk) {
-                            int best = -1;
-#pragma unroll
-                            for (int i = 0; i < MAXN; ++i)
-                                if (i < N && !((taken >> i) & 1u) && (best < 0 || lv[i] > lv[best]))
-                                    best = i;
-                            taken |= 1u << best;
-                            sel[r] = best;
-                            gsel[r] = __expf(lv[best] - mx) / z;
+                            sel[r] = a.sel[bth * topk + r];
+                            gsel[r] = a.e_sel[bth * topk + r];
                         }
-                    }
-                    if (cb == 0) {
-#pragma unroll
-                        for (int r = 0; r < TOPK; ++r)
-                            if (r < topk) {
-                                if (a.sel) a.sel[bth * topk + r] = sel[r];
-                                if (a.e_sel) a.e_sel[bth * topk + r] = gsel[r];
-                            }
-                    }
                 }
                 for (int i = 0; i < N; ++i) {
                     bool hit = false;
@@ -451,6 +455,10 @@ hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
                       int32_t* sel, float* e_sel, hipStream_t st) {
     if (dtype != 1 || N > MAXN || topk > 4 || dv % DB != 0) return hipErrorInvalidValue;
     SseArgs a{B, T, H, N, topk, dv, logits, q, k, v, lam, q_sh, k_sh, S, o, sel, e_sel};
+    const int P = B * T * H;
+    sse_route_kernel<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(logits, P, N, topk, sel, e_sel);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     dim3 grid((unsigned)(B * H * (dv / DB)));
     dim3 block(64 * (N + 2));
     if (topk <= 2) sse_chunk_kernel<bf16_t, 2><<<grid, block, 0, st>>>(a);
