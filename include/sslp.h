@@ -173,6 +173,10 @@ typedef struct {
     int B, T, H, d_k, d_v, chunk;
 } sslp_gdn_shape;
 
+/* Workspace bytes of gdn_chunk_forward: one record per (batch, head, chunk of
+ * 64 tokens) holding the state-independent part of the chunk (about 89 KB:
+ * the triangular-solve products, decayed operands and intra-chunk scores).
+ * 0 for an invalid shape or T = 0. */
 size_t gdn_workspace_size(const sslp_gdn_shape* shape);
 
 /*
@@ -189,7 +193,9 @@ size_t gdn_workspace_size(const sslp_gdn_shape* shape);
  *   S0    [B,H,d_k,d_v] fp32 initial state, or NULL for zeros;
  *   S_out [B,H,d_k,d_v] fp32 final state (may alias S0);
  *   o     [B,T,H,d_v] dtype out.
- *   workspace, ws_bytes >= gdn_workspace_size(shape) (may be NULL if that is 0).
+ *   workspace, ws_bytes >= gdn_workspace_size(shape) (may be NULL if that is 0),
+ *   else SSLP_ERR_WORKSPACE.  All chunks are prepared in parallel first, then
+ *   one pass over the chunks carries the state.
  */
 int gdn_chunk_forward(const sslp_gdn_shape* shape, int dtype, int decay_mode, const void* q,
                       const void* k, const void* v, const float* alpha, const float* beta,

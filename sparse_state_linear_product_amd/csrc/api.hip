@@ -298,7 +298,7 @@ static int check_gdn_shape(const sslp_gdn_shape* s) {
 
 size_t gdn_workspace_size(const sslp_gdn_shape* s) {
     if (check_gdn_shape(s) != SSLP_OK) return 0;
-    return 0;
+    return align_up(sslp::gdn_record_bytes(s->B, s->T, s->H));
 }
 
 int gdn_chunk_forward(const sslp_gdn_shape* s, int dtype, int decay_mode, const void* q,
@@ -328,10 +328,13 @@ int gdn_chunk_forward(const sslp_gdn_shape* s, int dtype, int decay_mode, const 
         REQUIRE_PTR(beta);
         REQUIRE_PTR(o);
     }
-    (void)workspace;
-    (void)ws_bytes;
+    const size_t need = gdn_workspace_size(s);
+    REQUIRE(ws_bytes >= need && (need == 0 || workspace != nullptr), SSLP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    REQUIRE_ALIGNED(workspace);
     return hip_status(sslp::launch_gdn_chunk(s->B, s->T, s->H, s->d_v, dtype, decay_mode, q, k, v,
-                                             alpha, beta, S0, S_out, o, (hipStream_t)stream),
+                                             alpha, beta, S0, S_out, o, workspace,
+                                             (hipStream_t)stream),
                       "gdn_chunk_forward launch");
 }
 

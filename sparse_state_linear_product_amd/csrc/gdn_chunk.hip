@@ -17,17 +17,24 @@
 // with Kt = K*e^{g_t}, Qt = Q*e^{g_t}, Kh = K*e^{g_C-g_t}.  The slides'
 // sparse-memory training appendix uses the same unit-diagonal triangular
 // system (slide "Backup: sparse interactions drive the triangular solve").
+// With T = (I + A)^{-1}, U = U0 + Wn S0 where U0 = T diag(beta) V and
+// Wn = -T diag(beta) Kt do not depend on the state.
 //
-// Work split.  One workgroup (4 waves) owns (batch, head, 32-column block of
-// d_v) and walks the chunks in order, keeping its [128 x 32] fp32 state slice
-// in MFMA accumulator registers.  The dense contractions (K K^T, Q K^T, K S0,
-// Q S0, T X, P U, Kh^T U) run on v_mfma_f32_16x16x32_bf16 with fp32
-// accumulation; T = (I+A)^{-1} is formed in fp32: 16x16 diagonal blocks by
-// forward substitution, off-diagonal blocks through
-//     I + A = D (I + L),  L = D^{-1} A_off,  T = (I - L + L^2 - L^3) D^{-1}
-// on v_mfma_f32_16x16x4_f32.  KDA factors the per-channel decay into the
-// operands relative to the first token of each 16-token block, so every
-// scale factor is a product of alphas bounded by alpha_min^-15.
+// Two kernels:
+//  * gdn_prep_kernel, one workgroup per (batch, head, chunk), all chunks in
+//    parallel: decay bookkeeping, K K^T and Q K^T on MFMA, T = (I+A)^{-1} in
+//    fp32 (16x16 diagonal blocks by forward substitution, off-diagonal blocks
+//    through I + A = D (I + L), L = D^{-1} A_off, T = (I - L + L^2 - L^3) D^{-1}
+//    on v_mfma_f32_16x16x4_f32), then U0, Wn (MFMA) and the decayed operands
+//    Qt, Kh, P, e^{g_C} into a per-chunk record.
+//  * gdn_state_kernel, one workgroup (4 waves) per (batch, head, 32-column
+//    block of d_v), walks the chunks in order with its [128 x 32] fp32 state
+//    slice in MFMA accumulators: U = U0 + Wn S0, O = Qt S0 + P U,
+//    S = e^{g_C} S0 + Kh^T U, prefetching the next chunk's record.
+// KDA factors the per-channel decay of K K^T and Q K^T into the operands
+// relative to the first token of each 16-token block, so every scale factor
+// is a product of alphas bounded by alpha_min^-15; Qt, Kh, e^{g_C} are
+// products of alphas at most 1.
 #include "common.h"
 #include "kernels.h"
 
@@ -40,16 +47,27 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;     // chunk length
 constexpr int DK = 128;   // key width
-constexpr int DVB = 32;   // d_v columns per workgroup
+constexpr int DVB = 32;   // d_v columns per state workgroup
 constexpr int NTH = 256;  // threads per workgroup
 constexpr int LDK = DK + 8;   // bf16 row stride of [C][DK] tiles
 constexpr int LDF = C + 4;    // fp32 row stride of [C][C] tiles
 constexpr int LDX = DVB + 4;  // fp32 row stride of [C][DVB] tiles
+constexpr int LDP = C + 8;    // bf16 row stride of [C][C] tiles
+
+// per-chunk record written by gdn_prep_kernel (bytes)
+constexpr int REC_WN = 0;                      // [C][DK] bf16: -T diag(beta) Kt
+constexpr int REC_QT = REC_WN + C * DK * 2;    // [C][DK] bf16: Qt
+constexpr int REC_KH = REC_QT + C * DK * 2;    // [C][DK] bf16: Kh
+constexpr int REC_P = REC_KH + C * DK * 2;     // [C][C] bf16: P (causal)
+constexpr int REC_U0 = REC_P + C * C * 2;      // [C][DK] fp32: T diag(beta) V  (d_v = DK)
+constexpr int REC_GC = REC_U0 + C * DK * 4;    // [DK] fp32: e^{g_C}
+constexpr int REC_BYTES = REC_GC + DK * 4;
 
 struct __align__(16) Smem {
     uint16_t k[C][LDK];   // GDN: K;  KDA: Kp = K * e^{g_t - g_r}
     uint16_t km[C][LDK];  // KDA: Km = K * e^{g_r - g_t}
     uint16_t q[C][LDK];   // GDN: Q;  KDA: Qp = Q * e^{g_t - g_r}
+    uint16_t v[C][LDK];   // diag(beta) V (bf16)
     union {
         struct {
             float A[C][LDF];   // A, then L = D^{-1} A_off in its lower blocks
@@ -58,17 +76,13 @@ struct __align__(16) Smem {
         float alpha[C][DK];  // KDA: the chunk's raw alphas (staging)
     } u;
     float P[C][LDF];      // decayed Q K^T, causal
-    float X[C][LDX];      // diag(beta)(V - Kt S0)
     union {
-        float U[C][LDX];  // T X
         struct {
             float pa[4][DK];  // KDA: product of the block's alphas
             float px[4][DK];  // KDA: same without the block's first token
             float af[4][DK];  // KDA: the block's first alpha
         } blk;
     } uw;
-    float V[C][LDX];      // V block (fp32)
-    uint16_t St[DVB][LDK];  // incoming state, transposed, bf16
     float L3[16][17];     // (L^3) block (3,0)
     float g[C];           // GDN: cumulative log decay
     float beta[C];
@@ -106,18 +120,8 @@ SSLP_DEVICE void store16(float* p, int ld, f32x4_t c, int lane, float scale) {
     for (int j = 0; j < 4; ++j) p[((lane >> 4) * 4 + j) * ld + (lane & 15)] = scale * c[j];
 }
 
-template <typename io_t>
-struct Prefetch {
-    static constexpr int EPS = 16 / sizeof(io_t);  // elements per 16-byte segment
-    static constexpr int KSEG = C * DK / EPS / NTH; // segments per thread for K (and Q)
-    static constexpr int VSEG = (C * DVB / EPS + NTH - 1) / NTH;
-    uint4 k[KSEG], q[KSEG], v[VSEG];
-    float a_s, b_s;  // GDN alpha / beta for token tid (tid < C)
-    float4 a_c[C * DK / 4 / NTH];  // KDA alpha
-};
-
 struct GdnArgs {
-    int B, T, H, dv;
+    int B, T, H, dv, nch;
     const void* q;
     const void* k;
     const void* v;
@@ -126,154 +130,62 @@ struct GdnArgs {
     const float* S0;
     float* S_out;
     void* o;
+    uint8_t* rec;  // [B, H, nch] records of REC_BYTES
 };
 
-template <typename io_t, bool KDA>
-__global__ __launch_bounds__(NTH) void gdn_chunk_kernel(GdnArgs a) {
+// ---------------------------------------------------------------------------
+// prep kernel: one workgroup per (b, h, chunk)
+// ---------------------------------------------------------------------------
+template <bool KDA>
+__global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int nblk = a.dv / DVB;
-    const int cb = blockIdx.x % nblk;
-    const int bh = blockIdx.x / nblk;
+    const int nch = a.nch;
+    const int c = blockIdx.x % nch, bh = blockIdx.x / nch;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-    const int n0 = cb * DVB;
     const int T = a.T, H = a.H, dv = a.dv;
-    const io_t* qg = static_cast<const io_t*>(a.q);
-    const io_t* kg = static_cast<const io_t*>(a.k);
-    const io_t* vg = static_cast<const io_t*>(a.v);
-    io_t* og = static_cast<io_t*>(a.o);
-    using PF = Prefetch<io_t>;
-    constexpr int EPS = PF::EPS;
-    const int nchunks = (T + C - 1) / C;
+    const int t0 = c * C;
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+    const uint16_t* kg = static_cast<const uint16_t*>(a.k);
+    const uint16_t* vg = static_cast<const uint16_t*>(a.v);
+    uint8_t* rec = a.rec + (size_t)blockIdx.x * REC_BYTES;
 
-    // ---- state slice in accumulator layout: tiles (tm = 2w + x, tn = y) ----
-    f32x4_t S[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
-                const int n = 16 * y + (lane & 15);
-                S[x][y][j] =
-                    a.S0 ? a.S0[(((size_t)b * H + h) * DK + i) * dv + n0 + n] : 0.f;
-            }
-
-    auto issue = [&](PF& pf, int c) {
-        const int t0 = c * C;
-#pragma unroll
-        for (int s = 0; s < PF::KSEG; ++s) {
-            const int seg = tid + NTH * s;
-            const int row = seg / (DK / EPS), col = (seg % (DK / EPS)) * EPS;
+    // ---- the chunk's inputs (zero past the sequence end, alpha 1, beta 0) ----
+    for (int seg = tid; seg < C * DK / 8; seg += NTH) {
+        const int row = seg / (DK / 8), col = (seg % (DK / 8)) * 8;
+        const int t = t0 + row;
+        uint4 kk = make_uint4(0, 0, 0, 0), qq = kk, vv = kk;
+        if (t < T) {
+            const size_t off = (((size_t)b * T + t) * H + h) * DK + col;
+            kk = *reinterpret_cast<const uint4*>(kg + off);
+            qq = *reinterpret_cast<const uint4*>(qg + off);
+            vv = *reinterpret_cast<const uint4*>(vg + (((size_t)b * T + t) * H + h) * dv + col);
+        }
+        *reinterpret_cast<uint4*>(&sm.k[row][col]) = kk;
+        *reinterpret_cast<uint4*>(&sm.q[row][col]) = qq;
+        *reinterpret_cast<uint4*>(&sm.v[row][col]) = vv;
+    }
+    if (tid < C) {
+        const int t = t0 + tid;
+        const size_t bth = ((size_t)b * T + t) * H + h;
+        sm.beta[tid] = t < T ? a.beta[bth] : 0.f;
+        if (!KDA) sm.g[tid] = __logf(t < T ? a.alpha[bth] : 1.f);
+    }
+    if (KDA) {
+        for (int seg = tid; seg < C * DK / 4; seg += NTH) {
+            const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
             const int t = t0 + row;
-            if (t < T) {
-                const size_t off = (((size_t)b * T + t) * H + h) * DK + col;
-                pf.k[s] = *reinterpret_cast<const uint4*>(kg + off);
-                pf.q[s] = *reinterpret_cast<const uint4*>(qg + off);
-            } else {
-                pf.k[s] = make_uint4(0, 0, 0, 0);
-                pf.q[s] = make_uint4(0, 0, 0, 0);
-            }
+            *reinterpret_cast<float4*>(&sm.u.alpha[row][col]) =
+                t < T ? *reinterpret_cast<const float4*>(a.alpha + (((size_t)b * T + t) * H + h) * DK + col)
+                      : make_float4(1.f, 1.f, 1.f, 1.f);
         }
-#pragma unroll
-        for (int s = 0; s < PF::VSEG; ++s) {
-            const int seg = tid + NTH * s;
-            const int row = seg / (DVB / EPS), col = (seg % (DVB / EPS)) * EPS;
-            const int t = t0 + row;
-            if (row < C && t < T)
-                pf.v[s] = *reinterpret_cast<const uint4*>(
-                    vg + (((size_t)b * T + t) * H + h) * dv + n0 + col);
-            else
-                pf.v[s] = make_uint4(0, 0, 0, 0);
-        }
-        if (tid < C) {
-            const int t = t0 + tid;
-            const size_t bth = ((size_t)b * T + t) * H + h;
-            pf.b_s = t < T ? a.beta[bth] : 0.f;
-            if (!KDA) pf.a_s = t < T ? a.alpha[bth] : 1.f;
-        }
-        if (KDA) {
-#pragma unroll
-            for (int s = 0; s < C * DK / 4 / NTH; ++s) {
-                const int seg = tid + NTH * s;
-                const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
-                const int t = t0 + row;
-                pf.a_c[s] = t < T ? *reinterpret_cast<const float4*>(
-                                        a.alpha + (((size_t)b * T + t) * H + h) * DK + col)
-                                  : make_float4(1.f, 1.f, 1.f, 1.f);
-            }
-        }
-    };
-
-    // raw inputs of a chunk -> LDS (K, Q as bf16; V, beta fp32; alpha in LDS
-    // staging: GDN log-decay in g, KDA alpha in A's storage)
-    auto commit = [&](const PF& pf) {
-#pragma unroll
-        for (int s = 0; s < PF::KSEG; ++s) {
-            const int seg = tid + NTH * s;
-            const int row = seg / (DK / EPS), col = (seg % (DK / EPS)) * EPS;
-            if constexpr (sizeof(io_t) == 2) {
-                *reinterpret_cast<uint4*>(&sm.k[row][col]) = pf.k[s];
-                *reinterpret_cast<uint4*>(&sm.q[row][col]) = pf.q[s];
-            } else {
-                const float* fk = reinterpret_cast<const float*>(&pf.k[s]);
-                const float* fq = reinterpret_cast<const float*>(&pf.q[s]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sm.k[row][col + e] = f32_to_bf16(fk[e]).bits;
-                    sm.q[row][col + e] = f32_to_bf16(fq[e]).bits;
-                }
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < PF::VSEG; ++s) {
-            const int seg = tid + NTH * s;
-            const int row = seg / (DVB / EPS), col = (seg % (DVB / EPS)) * EPS;
-            if (row < C) {
-                const io_t* e = reinterpret_cast<const io_t*>(&pf.v[s]);
-#pragma unroll
-                for (int x = 0; x < EPS; ++x) sm.V[row][col + x] = to_f32(e[x]);
-            }
-        }
-        if (tid < C) {
-            sm.beta[tid] = pf.b_s;
-            if (!KDA) sm.g[tid] = __logf(pf.a_s);
-        }
-        if (KDA) {
-#pragma unroll
-            for (int s = 0; s < C * DK / 4 / NTH; ++s) {
-                const int seg = tid + NTH * s;
-                const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
-                *reinterpret_cast<float4*>(&sm.u.alpha[row][col]) = pf.a_c[s];
-            }
-        }
-    };
-
-    // state slice (bf16, transposed) for the B operands of K S0 and Q S0
-    auto publish_state = [&]() {
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int y = 0; y < 2; ++y)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
-                    const int n = 16 * y + (lane & 15);
-                    sm.St[n][i] = f32_to_bf16(S[x][y][j]).bits;
-                }
-    };
-
-    PF pf;
-    issue(pf, 0);
-    commit(pf);
-    publish_state();
+    }
     __syncthreads();
-
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const int Tc = (T - t0) < C ? (T - t0) : C;
-        if (c + 1 < nchunks) issue(pf, c + 1);  // next chunk's inputs, in flight
+    // X = diag(beta) V (bf16, in place)
+    for (int e = tid; e < C * DK; e += NTH) {
+        const int row = e / DK, col = e % DK;
+        sm.v[row][col] = f32_to_bf16(sm.beta[row] * bf2f(sm.v[row][col])).bits;
+    }
 
         // ---------------- decay bookkeeping ----------------
         float decC_s = 1.f;  // GDN: e^{g_C}
@@ -355,7 +267,8 @@ __global__ __launch_bounds__(NTH) void gdn_chunk_kernel(GdnArgs a) {
             __syncthreads();
         }
 
-        // ---------------- phase 1: K K^T, Q K^T, K S0, Q S0 ----------------
+
+        // ---------------- K K^T and Q K^T ----------------
         // G rows block w (tiles tn <= w) and P' rows block 3-w (tiles tn <= 3-w)
         f32x4_t gt[4], pt[4];
         const int pr = 3 - w;
@@ -372,9 +285,8 @@ __global__ __launch_bounds__(NTH) void gdn_chunk_kernel(GdnArgs a) {
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) {
                 const int jrow = 16 * tn + (lane & 15);
-                bf16x8_t bk;
                 if constexpr (!KDA) {
-                    bk = load_bf16x8(&sm.k[jrow][kc]);
+                    const bf16x8_t bk = load_bf16x8(&sm.k[jrow][kc]);
                     if (tn <= w) gt[tn] = mfma_bf16(ak, bk, gt[tn]);
                     if (tn <= pr) pt[tn] = mfma_bf16(aq, bk, pt[tn]);
                 } else {
@@ -404,73 +316,29 @@ __global__ __launch_bounds__(NTH) void gdn_chunk_kernel(GdnArgs a) {
                 }
             }
         }
-        // K S0 and Q S0 for row block w
-        f32x4_t ks[2], qs[2];
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            ks[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            qs[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-            const int kc = 32 * s + (lane >> 4) * 8;
-            bf16x8_t ak, aq;
-            if constexpr (!KDA) {
-                ak = load_bf16x8(&sm.k[16 * w + (lane & 15)][kc]);
-                aq = load_bf16x8(&sm.q[16 * w + (lane & 15)][kc]);
-            } else {  // Kt = Kp * F[w], Qt = Qp * F[w]
-                const uint16_t* kr = &sm.k[16 * w + (lane & 15)][kc];
-                const uint16_t* qr = &sm.q[16 * w + (lane & 15)][kc];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float f = sm.F[w][kc + e];
-                    ak[e] = bf(bf2f(kr[e]) * f);
-                    aq[e] = bf(bf2f(qr[e]) * f);
-                }
-            }
-#pragma unroll
-            for (int y = 0; y < 2; ++y) {
-                const bf16x8_t bs = load_bf16x8(&sm.St[16 * y + (lane & 15)][kc]);
-                ks[y] = mfma_bf16(ak, bs, ks[y]);
-                qs[y] = mfma_bf16(aq, bs, qs[y]);
-            }
-        }
         __syncthreads();
         // write A (strictly lower, beta and decay applied) and P (causal) tiles
-        {
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * w + (lane >> 4) * 4 + j;
-                    const int jj = 16 * tn + (lane & 15);
-                    float av = 0.f;
-                    if (tn <= w && jj < t) {
-                        av = gt[tn][j] * sm.beta[t];
-                        if (!KDA) av *= __expf(sm.g[t] - sm.g[jj]);
-                    }
-                    sm.u.s.A[t][jj] = av;
-                    const int tp = 16 * pr + (lane >> 4) * 4 + j;
-                    float pv = 0.f;
-                    if (tn <= pr && jj <= tp) {
-                        pv = pt[tn][j];
-                        if (!KDA) pv *= __expf(sm.g[tp] - sm.g[jj]);
-                    }
-                    sm.P[tp][jj] = pv;
-                }
-            }
-        }
-        // X = diag(beta) (V - Kt S0) for rows of block w
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
+        for (int tn = 0; tn < 4; ++tn) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * w + (lane >> 4) * 4 + j;
-                const int n = 16 * y + (lane & 15);
-                float kt = ks[y][j];
-                if (!KDA) kt *= __expf(sm.g[t]);
-                sm.X[t][n] = sm.beta[t] * (sm.V[t][n] - kt);
+                const int jj = 16 * tn + (lane & 15);
+                float av = 0.f;
+                if (tn <= w && jj < t) {
+                    av = gt[tn][j] * sm.beta[t];
+                    if (!KDA) av *= __expf(sm.g[t] - sm.g[jj]);
+                }
+                sm.u.s.A[t][jj] = av;
+                const int tp = 16 * pr + (lane >> 4) * 4 + j;
+                float pv = 0.f;
+                if (tn <= pr && jj <= tp) {
+                    pv = pt[tn][j];
+                    if (!KDA) pv *= __expf(sm.g[tp] - sm.g[jj]);
+                }
+                sm.P[tp][jj] = pv;
             }
+        }
         __syncthreads();
 
         // ---------------- T = (I + A)^{-1} ----------------
@@ -567,108 +435,267 @@ __global__ __launch_bounds__(NTH) void gdn_chunk_kernel(GdnArgs a) {
         }
         __syncthreads();
 
-        // ---------------- U = T X ----------------
-        {
-            f32x4_t ut[2];
-#pragma unroll
-            for (int y = 0; y < 2; ++y) ut[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s == 1 && w < 2) continue;  // T[t][j] = 0 for j >= 32 when t < 32
-                const int kc = 32 * s + (lane >> 4) * 8;
-                bf16x8_t at;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) at[e] = bf(sm.u.s.Tm[16 * w + (lane & 15)][kc + e]);
-#pragma unroll
-                for (int y = 0; y < 2; ++y) {
-                    bf16x8_t bx;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bx[e] = bf(sm.X[kc + e][16 * y + (lane & 15)]);
-                    ut[y] = mfma_bf16(at, bx, ut[y]);
-                }
-            }
-#pragma unroll
-            for (int y = 0; y < 2; ++y) store16(&sm.uw.U[16 * w][16 * y], LDX, ut[y], lane, 1.f);
-        }
-        __syncthreads();
 
-        // ---------------- O = Qt S0 + P U ----------------
+        // ---------------- U0 = T X and Wn = -T diag(beta) Kt, rows block w ----------------
         {
-            f32x4_t ot[2];
+            float* u0 = reinterpret_cast<float*>(rec + REC_U0);
+            uint16_t* wn = reinterpret_cast<uint16_t*>(rec + REC_WN);
+#pragma unroll 2
+            for (int y = 0; y < DK / 16; ++y) {
+                f32x4_t au = f32x4_t{0.f, 0.f, 0.f, 0.f}, aw = au;
+                const int n = 16 * y + (lane & 15);
 #pragma unroll
-            for (int y = 0; y < 2; ++y) ot[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < 2; ++s) {
+                    if (s == 1 && w < 2) continue;  // T[t][j] = 0 for j >= 32 when t < 32
+                    const int kc = 32 * s + (lane >> 4) * 8;
+                    bf16x8_t at, bx, bk;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s == 1 && w < 2) continue;
-                const int kc = 32 * s + (lane >> 4) * 8;
-                bf16x8_t ap;
+                    for (int e = 0; e < 8; ++e) {
+                        const int t = kc + e;
+                        at[e] = bf(sm.u.s.Tm[16 * w + (lane & 15)][t]);
+                        bx[e] = __builtin_bit_cast(__bf16, sm.v[t][n]);
+                        float kt;
+                        if constexpr (!KDA) kt = bf2f(sm.k[t][n]) * __expf(sm.g[t]);
+                        else kt = bf2f(sm.k[t][n]) * sm.F[t >> 4][n];
+                        bk[e] = bf(sm.beta[t] * kt);
+                    }
+                    au = mfma_bf16(at, bx, au);
+                    aw = mfma_bf16(at, bk, aw);
+                }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ap[e] = bf(sm.P[16 * w + (lane & 15)][kc + e]);
-#pragma unroll
-                for (int y = 0; y < 2; ++y) {
-                    bf16x8_t bu;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bu[e] = bf(sm.uw.U[kc + e][16 * y + (lane & 15)]);
-                    ot[y] = mfma_bf16(ap, bu, ot[y]);
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 16 * w + (lane >> 4) * 4 + j;
+                    u0[t * DK + n] = au[j];
+                    wn[t * DK + n] = f32_to_bf16(-aw[j]).bits;
                 }
             }
+        }
+        // ---------------- Qt, Kh, P, e^{g_C} ----------------
+        {
+            uint16_t* qt = reinterpret_cast<uint16_t*>(rec + REC_QT);
+            uint16_t* kh = reinterpret_cast<uint16_t*>(rec + REC_KH);
+            for (int seg = tid; seg < C * DK / 8; seg += NTH) {
+                const int t = seg / (DK / 8), i0 = (seg % (DK / 8)) * 8;
+                uint32_t qw[4], kw[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float q0, q1, k0, k1;
+                    if constexpr (!KDA) {
+                        const float fq = __expf(sm.g[t]), fk = __expf(sm.g[C - 1] - sm.g[t]);
+                        q0 = bf2f(sm.q[t][i0 + e]) * fq;
+                        q1 = bf2f(sm.q[t][i0 + e + 1]) * fq;
+                        k0 = bf2f(sm.k[t][i0 + e]) * fk;
+                        k1 = bf2f(sm.k[t][i0 + e + 1]) * fk;
+                    } else {
+                        q0 = bf2f(sm.q[t][i0 + e]) * sm.F[t >> 4][i0 + e];
+                        q1 = bf2f(sm.q[t][i0 + e + 1]) * sm.F[t >> 4][i0 + e + 1];
+                        k0 = bf2f(sm.km[t][i0 + e]) * sm.Hf[t >> 4][i0 + e];
+                        k1 = bf2f(sm.km[t][i0 + e + 1]) * sm.Hf[t >> 4][i0 + e + 1];
+                    }
+                    qw[e / 2] = (uint32_t)f32_to_bf16(q0).bits | ((uint32_t)f32_to_bf16(q1).bits << 16);
+                    kw[e / 2] = (uint32_t)f32_to_bf16(k0).bits | ((uint32_t)f32_to_bf16(k1).bits << 16);
+                }
+                *reinterpret_cast<uint4*>(qt + t * DK + i0) = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+                *reinterpret_cast<uint4*>(kh + t * DK + i0) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+            }
+            uint16_t* pb = reinterpret_cast<uint16_t*>(rec + REC_P);
+            for (int e = tid; e < C * C / 2; e += NTH) {
+                const int t = e / (C / 2), j = (e % (C / 2)) * 2;
+                *reinterpret_cast<uint32_t*>(pb + t * C + j) =
+                    (uint32_t)f32_to_bf16(sm.P[t][j]).bits | ((uint32_t)f32_to_bf16(sm.P[t][j + 1]).bits << 16);
+            }
+            float* gc = reinterpret_cast<float*>(rec + REC_GC);
+            if (tid < DK) gc[tid] = KDA ? sm.gC[tid] : decC_s;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// state kernel: one workgroup (4 waves) per (b, h, 32-column block of d_v)
+// ---------------------------------------------------------------------------
+struct __align__(16) StateSmem {
+    uint16_t wn[C][LDK];
+    uint16_t qt[C][LDK];
+    uint16_t kh[C][LDK];
+    uint16_t p[C][LDP];
+    float u0[C][LDX];
+    float U[C][LDX];
+    float gc[DK];
+    uint16_t St[DVB][LDK];  // incoming state, transposed, bf16
+};
+static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
+
+struct StatePrefetch {
+    uint4 wn[4], qt[4], kh[4], p[2], u0[2];
+    float4 gc;
+};
+
+template <typename io_t>
+__global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
+    __shared__ StateSmem ss;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nblk = a.dv / DVB;
+    const int cb = blockIdx.x % nblk;
+    const int bh = blockIdx.x / nblk;
+    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+    const int n0 = cb * DVB;
+    const int T = a.T, H = a.H, dv = a.dv, nch = a.nch;
+    io_t* og = static_cast<io_t*>(a.o);
+    const uint8_t* recb = a.rec + (size_t)bh * nch * REC_BYTES;
+
+    // state slice in accumulator layout: tiles (tm = 2w + x, tn = y)
+    f32x4_t S[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
+                const int n = 16 * y + (lane & 15);
+                S[x][y][j] = a.S0 ? a.S0[(((size_t)b * H + h) * DK + i) * dv + n0 + n] : 0.f;
+            }
+
+    auto issue = [&](StatePrefetch& pf, int c) {
+        const uint8_t* r = recb + (size_t)c * REC_BYTES;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int seg = tid + NTH * s;  // 16-byte piece of a [C][DK] bf16 tile
+            pf.wn[s] = reinterpret_cast<const uint4*>(r + REC_WN)[seg];
+            pf.qt[s] = reinterpret_cast<const uint4*>(r + REC_QT)[seg];
+            pf.kh[s] = reinterpret_cast<const uint4*>(r + REC_KH)[seg];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) pf.p[s] = reinterpret_cast<const uint4*>(r + REC_P)[tid + NTH * s];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int seg = tid + NTH * s;  // row seg / 8, columns 4 (seg % 8) .. of the slice
+            pf.u0[s] = *reinterpret_cast<const uint4*>(r + REC_U0 +
+                                                       ((seg >> 3) * DK + n0 + 4 * (seg & 7)) * 4);
+        }
+        if (tid < DK / 4) pf.gc = reinterpret_cast<const float4*>(r + REC_GC)[tid];
+    };
+    auto commit = [&](const StatePrefetch& pf) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int seg = tid + NTH * s;
+            const int row = seg / (DK / 8), col = (seg % (DK / 8)) * 8;
+            *reinterpret_cast<uint4*>(&ss.wn[row][col]) = pf.wn[s];
+            *reinterpret_cast<uint4*>(&ss.qt[row][col]) = pf.qt[s];
+            *reinterpret_cast<uint4*>(&ss.kh[row][col]) = pf.kh[s];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int seg = tid + NTH * s;
+            const int row = seg / (C / 8), col = (seg % (C / 8)) * 8;
+            *reinterpret_cast<uint4*>(&ss.p[row][col]) = pf.p[s];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int seg = tid + NTH * s;
+            *reinterpret_cast<uint4*>(&ss.u0[seg >> 3][4 * (seg & 7)]) = pf.u0[s];
+        }
+        if (tid < DK / 4) *reinterpret_cast<float4*>(&ss.gc[4 * tid]) = pf.gc;
+    };
+    auto publish_state = [&]() {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int y = 0; y < 2; ++y)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * w + (lane >> 4) * 4 + j;
+                    const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
                     const int n = 16 * y + (lane & 15);
-                    float qv = qs[y][j];
-                    if (!KDA) qv *= __expf(sm.g[t]);
-                    if (t < Tc)
-                        og[(((size_t)b * T + t0 + t) * H + h) * dv + n0 + n] =
-                            from_f32<io_t>(qv + ot[y][j]);
+                    ss.St[n][i] = f32_to_bf16(S[x][y][j]).bits;
                 }
-        }
+    };
 
-        // ---------------- S = e^{g_C} S0 + Kh^T U ----------------
-        {
+    StatePrefetch pf;
+    if (nch > 0) {  // T = 0: no records (the workspace may be empty); the state is copied
+        issue(pf, 0);
+        commit(pf);
+    }
+    publish_state();
+    __syncthreads();
+
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = c * C;
+        const int Tc = (T - t0) < C ? (T - t0) : C;
+        if (c + 1 < nch) issue(pf, c + 1);  // next chunk's record, in flight
+
+        // ---- U = U0 + Wn S0 and Qt S0 for rows block w ----
+        f32x4_t u[2], o[2];
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+        for (int y = 0; y < 2; ++y) {
+            o[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int y = 0; y < 2; ++y)
+            for (int j = 0; j < 4; ++j) u[y][j] = ss.u0[16 * w + (lane >> 4) * 4 + j][16 * y + (lane & 15)];
+        }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
-                        S[x][y][j] *= KDA ? sm.gC[i] : decC_s;
-                    }
+        for (int s = 0; s < DK / 32; ++s) {
+            const int kc = 32 * s + (lane >> 4) * 8;
+            const bf16x8_t aw = load_bf16x8(&ss.wn[16 * w + (lane & 15)][kc]);
+            const bf16x8_t aq = load_bf16x8(&ss.qt[16 * w + (lane & 15)][kc]);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int kc = 32 * s + (lane >> 4) * 8;  // tokens
-                bf16x8_t bu[2];
+            for (int y = 0; y < 2; ++y) {
+                const bf16x8_t bs = load_bf16x8(&ss.St[16 * y + (lane & 15)][kc]);
+                u[y] = mfma_bf16(aw, bs, u[y]);
+                o[y] = mfma_bf16(aq, bs, o[y]);
+            }
+        }
 #pragma unroll
-                for (int y = 0; y < 2; ++y)
+        for (int y = 0; y < 2; ++y) store16(&ss.U[16 * w][16 * y], LDX, u[y], lane, 1.f);
+        __syncthreads();
+
+        // ---- O = Qt S0 + P U (causal) ----
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        float u = sm.uw.U[kc + e][16 * y + (lane & 15)];
-                        if (!KDA) u *= __expf(sm.g[C - 1] - sm.g[kc + e]);
-                        bu[y][e] = bf(u);
-                    }
+        for (int s = 0; s < 2; ++s) {
+            if (s == 1 && w < 2) continue;
+            const int kc = 32 * s + (lane >> 4) * 8;
+            const bf16x8_t ap = load_bf16x8(&ss.p[16 * w + (lane & 15)][kc]);
 #pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int i = 16 * (2 * w + x) + (lane & 15);
-                    bf16x8_t ak;
+            for (int y = 0; y < 2; ++y) {
+                bf16x8_t bu;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int t = kc + e;
-                        if constexpr (!KDA) {
-                            ak[e] = __builtin_bit_cast(__bf16, sm.k[t][i]);
-                        } else {
-                            ak[e] = bf(bf2f(sm.km[t][i]) * sm.Hf[t >> 4][i]);
-                        }
-                    }
+                for (int e = 0; e < 8; ++e) bu[e] = bf(ss.U[kc + e][16 * y + (lane & 15)]);
+                o[y] = mfma_bf16(ap, bu, o[y]);
+            }
+        }
 #pragma unroll
-                    for (int y = 0; y < 2; ++y) S[x][y] = mfma_bf16(ak, bu[y], S[x][y]);
-                }
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * w + (lane >> 4) * 4 + j;
+                const int n = 16 * y + (lane & 15);
+                if (t < Tc) og[(((size_t)b * T + t0 + t) * H + h) * dv + n0 + n] = from_f32<io_t>(o[y][j]);
+            }
+
+        // ---- S = e^{g_C} S0 + Kh^T U ----
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) S[x][y][j] *= ss.gc[16 * (2 * w + x) + (lane >> 4) * 4 + j];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int kc = 32 * s + (lane >> 4) * 8;  // tokens
+            bf16x8_t bu[2];
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bu[y][e] = bf(ss.U[kc + e][16 * y + (lane & 15)]);
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int i = 16 * (2 * w + x) + (lane & 15);
+                bf16x8_t ak;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ak[e] = __builtin_bit_cast(__bf16, ss.kh[kc + e][i]);
+#pragma unroll
+                for (int y = 0; y < 2; ++y) S[x][y] = mfma_bf16(ak, bu[y], S[x][y]);
             }
         }
         __syncthreads();  // everyone is done with this chunk's LDS contents
-        if (c + 1 < nchunks) commit(pf);
+        if (c + 1 < nch) commit(pf);
         publish_state();
         __syncthreads();
     }
@@ -688,14 +715,24 @@ __global__ __launch_bounds__(NTH) void gdn_chunk_kernel(GdnArgs a) {
 
 }  // namespace
 
+size_t gdn_record_bytes(int B, int T, int H) {
+    const long long nch = (T + C - 1) / C;
+    return (size_t)B * H * nch * REC_BYTES;
+}
+
 hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, const void* q,
                             const void* k, const void* v, const float* alpha, const float* beta,
-                            const float* S0, float* S_out, void* o, hipStream_t st) {
-    GdnArgs a{B, T, H, dv, q, k, v, alpha, beta, S0, S_out, o};
-    dim3 grid((unsigned)(B * H * (dv / DVB)));
-    if (dtype != 1) return hipErrorInvalidValue;  // bf16 inputs only (checked by the C ABI)
-    if (kda) gdn_chunk_kernel<bf16_t, true><<<grid, NTH, 0, st>>>(a);
-    else gdn_chunk_kernel<bf16_t, false><<<grid, NTH, 0, st>>>(a);
+                            const float* S0, float* S_out, void* o, void* rec, hipStream_t st) {
+    if (dtype != 1 || dv != DK) return hipErrorInvalidValue;  // bf16, d_k = d_v = 128 (checked by the C ABI)
+    const int nch = (T + C - 1) / C;
+    GdnArgs a{B, T, H, dv, nch, q, k, v, alpha, beta, S0, S_out, o, static_cast<uint8_t*>(rec)};
+    if (nch > 0) {
+        if (kda) gdn_prep_kernel<true><<<(unsigned)(B * H * nch), NTH, 0, st>>>(a);
+        else gdn_prep_kernel<false><<<(unsigned)(B * H * nch), NTH, 0, st>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    gdn_state_kernel<bf16_t><<<(unsigned)(B * H * (dv / DVB)), NTH, 0, st>>>(a);
     return hipGetLastError();
 }
 

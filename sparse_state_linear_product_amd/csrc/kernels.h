@@ -38,9 +38,12 @@ size_t sdm_chunk_plan_bytes(int B, int T, int H);
 hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* plan, hipStream_t st);
 
 // ---- Gated DeltaNet / KDA ----
+// per-chunk records of the state-independent part (workspace), and the
+// launcher (prep kernel over all chunks + state kernel over the chunk sequence)
+size_t gdn_record_bytes(int B, int T, int H);
 hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, const void* q,
                             const void* k, const void* v, const float* alpha, const float* beta,
-                            const float* S0, float* S_out, void* o, hipStream_t st);
+                            const float* S0, float* S_out, void* o, void* rec, hipStream_t st);
 
 // ---- Sparse State Expansion ----
 hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
