@@ -57,7 +57,7 @@ constexpr int LDP = C + 8;    // bf16 row stride of [C][C] tiles
 // per-chunk record written by gdn_prep_kernel (bytes)
 constexpr int REC_WN = 0;                      // [C][DK] bf16: -T diag(beta) Kt
 constexpr int REC_QT = REC_WN + C * DK * 2;    // [C][DK] bf16: Qt
-constexpr int REC_KH = REC_QT + C * DK * 2;    // [C][DK] bf16: Kh
+constexpr int REC_KH = REC_QT + C * DK * 2;    // [DK][C] bf16: Kh transposed
 constexpr int REC_P = REC_KH + C * DK * 2;     // [C][C] bf16: P (causal)
 constexpr int REC_U0 = REC_P + C * C * 2;      // [C][DK] fp32: T diag(beta) V  (d_v = DK)
 constexpr int REC_GC = REC_U0 + C * DK * 4;    // [DK] fp32: e^{g_C}
@@ -67,7 +67,9 @@ struct __align__(16) Smem {
     uint16_t k[C][LDK];   // GDN: K;  KDA: Kp = K * e^{g_t - g_r}
     uint16_t km[C][LDK];  // KDA: Km = K * e^{g_r - g_t}
     uint16_t q[C][LDK];   // GDN: Q;  KDA: Qp = Q * e^{g_t - g_r}
-    uint16_t v[C][LDK];   // diag(beta) V (bf16)
+    uint16_t xt[DK][LDP];   // (diag(beta) V)^T, bf16 (B operand of U0 = T X)
+    uint16_t kbt[DK][LDP];  // (diag(beta) Kt)^T, bf16 (B operand of Wn)
+    uint16_t tb[C][LDP];    // T, bf16 (A operand)
     union {
         struct {
             float A[C][LDF];   // A, then L = D^{-1} A_off in its lower blocks
@@ -75,7 +77,6 @@ struct __align__(16) Smem {
         } s;
         float alpha[C][DK];  // KDA: the chunk's raw alphas (staging)
     } u;
-    float P[C][LDF];      // decayed Q K^T, causal
     union {
         struct {
             float pa[4][DK];  // KDA: product of the block's alphas
@@ -163,7 +164,9 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
         }
         *reinterpret_cast<uint4*>(&sm.k[row][col]) = kk;
         *reinterpret_cast<uint4*>(&sm.q[row][col]) = qq;
-        *reinterpret_cast<uint4*>(&sm.v[row][col]) = vv;
+        const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.xt[col + e][row] = ve[e];  // raw V, transposed
     }
     if (tid < C) {
         const int t = t0 + tid;
@@ -181,10 +184,10 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
         }
     }
     __syncthreads();
-    // X = diag(beta) V (bf16, in place)
+    // X = diag(beta) V (bf16, transposed, in place)
     for (int e = tid; e < C * DK; e += NTH) {
-        const int row = e / DK, col = e % DK;
-        sm.v[row][col] = f32_to_bf16(sm.beta[row] * bf2f(sm.v[row][col])).bits;
+        const int n = e / C, t = e % C;
+        sm.xt[n][t] = f32_to_bf16(sm.beta[t] * bf2f(sm.xt[n][t])).bits;
     }
 
         // ---------------- decay bookkeeping ----------------
@@ -336,8 +339,16 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
                     pv = pt[tn][j];
                     if (!KDA) pv *= __expf(sm.g[tp] - sm.g[jj]);
                 }
-                sm.P[tp][jj] = pv;
+                reinterpret_cast<uint16_t*>(rec + REC_P)[tp * C + jj] = f32_to_bf16(pv).bits;
             }
+        }
+        // (diag(beta) Kt)^T for Wn: Kt = K e^{g_t} (GDN) or Kp F[block] (KDA)
+        for (int e = tid; e < C * DK; e += NTH) {
+            const int i = e / C, t = e % C;
+            float kt;
+            if constexpr (!KDA) kt = bf2f(sm.k[t][i]) * __expf(sm.g[t]);
+            else kt = bf2f(sm.k[t][i]) * sm.F[t >> 4][i];
+            sm.kbt[i][t] = f32_to_bf16(sm.beta[t] * kt).bits;
         }
         __syncthreads();
 
@@ -437,9 +448,17 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
 
 
         // ---------------- U0 = T X and Wn = -T diag(beta) Kt, rows block w ----------------
+        for (int e = tid; e < C * C; e += NTH) {
+            const int t = e / C, j = e % C;
+            sm.tb[t][j] = f32_to_bf16(sm.u.s.Tm[t][j]).bits;
+        }
+        __syncthreads();
         {
             float* u0 = reinterpret_cast<float*>(rec + REC_U0);
             uint16_t* wn = reinterpret_cast<uint16_t*>(rec + REC_WN);
+            bf16x8_t at[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) at[s] = load_bf16x8(&sm.tb[16 * w + (lane & 15)][32 * s + (lane >> 4) * 8]);
 #pragma unroll 2
             for (int y = 0; y < DK / 16; ++y) {
                 f32x4_t au = f32x4_t{0.f, 0.f, 0.f, 0.f}, aw = au;
@@ -448,19 +467,8 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
                 for (int s = 0; s < 2; ++s) {
                     if (s == 1 && w < 2) continue;  // T[t][j] = 0 for j >= 32 when t < 32
                     const int kc = 32 * s + (lane >> 4) * 8;
-                    bf16x8_t at, bx, bk;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int t = kc + e;
-                        at[e] = bf(sm.u.s.Tm[16 * w + (lane & 15)][t]);
-                        bx[e] = __builtin_bit_cast(__bf16, sm.v[t][n]);
-                        float kt;
-                        if constexpr (!KDA) kt = bf2f(sm.k[t][n]) * __expf(sm.g[t]);
-                        else kt = bf2f(sm.k[t][n]) * sm.F[t >> 4][n];
-                        bk[e] = bf(sm.beta[t] * kt);
-                    }
-                    au = mfma_bf16(at, bx, au);
-                    aw = mfma_bf16(at, bk, aw);
+                    au = mfma_bf16(at[s], load_bf16x8(&sm.xt[n][kc]), au);
+                    aw = mfma_bf16(at[s], load_bf16x8(&sm.kbt[n][kc]), aw);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -470,39 +478,44 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
                 }
             }
         }
-        // ---------------- Qt, Kh, P, e^{g_C} ----------------
+        // ---------------- Qt, Kh^T, e^{g_C} ----------------
         {
             uint16_t* qt = reinterpret_cast<uint16_t*>(rec + REC_QT);
             uint16_t* kh = reinterpret_cast<uint16_t*>(rec + REC_KH);
             for (int seg = tid; seg < C * DK / 8; seg += NTH) {
                 const int t = seg / (DK / 8), i0 = (seg % (DK / 8)) * 8;
-                uint32_t qw[4], kw[4];
+                uint32_t qw[4];
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    float q0, q1, k0, k1;
+                    float q0, q1;
                     if constexpr (!KDA) {
-                        const float fq = __expf(sm.g[t]), fk = __expf(sm.g[C - 1] - sm.g[t]);
+                        const float fq = __expf(sm.g[t]);
                         q0 = bf2f(sm.q[t][i0 + e]) * fq;
                         q1 = bf2f(sm.q[t][i0 + e + 1]) * fq;
-                        k0 = bf2f(sm.k[t][i0 + e]) * fk;
-                        k1 = bf2f(sm.k[t][i0 + e + 1]) * fk;
                     } else {
                         q0 = bf2f(sm.q[t][i0 + e]) * sm.F[t >> 4][i0 + e];
                         q1 = bf2f(sm.q[t][i0 + e + 1]) * sm.F[t >> 4][i0 + e + 1];
-                        k0 = bf2f(sm.km[t][i0 + e]) * sm.Hf[t >> 4][i0 + e];
-                        k1 = bf2f(sm.km[t][i0 + e + 1]) * sm.Hf[t >> 4][i0 + e + 1];
                     }
                     qw[e / 2] = (uint32_t)f32_to_bf16(q0).bits | ((uint32_t)f32_to_bf16(q1).bits << 16);
-                    kw[e / 2] = (uint32_t)f32_to_bf16(k0).bits | ((uint32_t)f32_to_bf16(k1).bits << 16);
                 }
                 *reinterpret_cast<uint4*>(qt + t * DK + i0) = make_uint4(qw[0], qw[1], qw[2], qw[3]);
-                *reinterpret_cast<uint4*>(kh + t * DK + i0) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
             }
-            uint16_t* pb = reinterpret_cast<uint16_t*>(rec + REC_P);
-            for (int e = tid; e < C * C / 2; e += NTH) {
-                const int t = e / (C / 2), j = (e % (C / 2)) * 2;
-                *reinterpret_cast<uint32_t*>(pb + t * C + j) =
-                    (uint32_t)f32_to_bf16(sm.P[t][j]).bits | ((uint32_t)f32_to_bf16(sm.P[t][j + 1]).bits << 16);
+            for (int seg = tid; seg < C * DK / 8; seg += NTH) {
+                const int i = seg / (C / 8), t0e = (seg % (C / 8)) * 8;
+                uint32_t kw[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float k0, k1;
+                    if constexpr (!KDA) {
+                        k0 = bf2f(sm.k[t0e + e][i]) * __expf(sm.g[C - 1] - sm.g[t0e + e]);
+                        k1 = bf2f(sm.k[t0e + e + 1][i]) * __expf(sm.g[C - 1] - sm.g[t0e + e + 1]);
+                    } else {
+                        k0 = bf2f(sm.km[t0e + e][i]) * sm.Hf[(t0e + e) >> 4][i];
+                        k1 = bf2f(sm.km[t0e + e + 1][i]) * sm.Hf[(t0e + e + 1) >> 4][i];
+                    }
+                    kw[e / 2] = (uint32_t)f32_to_bf16(k0).bits | ((uint32_t)f32_to_bf16(k1).bits << 16);
+                }
+                *reinterpret_cast<uint4*>(kh + i * C + t0e) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
             }
             float* gc = reinterpret_cast<float*>(rec + REC_GC);
             if (tid < DK) gc[tid] = KDA ? sm.gC[tid] : decC_s;
@@ -515,10 +528,10 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
 struct __align__(16) StateSmem {
     uint16_t wn[C][LDK];
     uint16_t qt[C][LDK];
-    uint16_t kh[C][LDK];
+    uint16_t kh[DK][LDP];   // Kh^T
     uint16_t p[C][LDP];
     float u0[C][LDX];
-    float U[C][LDX];
+    uint16_t ut[DVB][LDP];  // U^T, bf16
     float gc[DK];
     uint16_t St[DVB][LDK];  // incoming state, transposed, bf16
 };
@@ -581,7 +594,7 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
             const int row = seg / (DK / 8), col = (seg % (DK / 8)) * 8;
             *reinterpret_cast<uint4*>(&ss.wn[row][col]) = pf.wn[s];
             *reinterpret_cast<uint4*>(&ss.qt[row][col]) = pf.qt[s];
-            *reinterpret_cast<uint4*>(&ss.kh[row][col]) = pf.kh[s];
+            *reinterpret_cast<uint4*>(&ss.kh[seg / (C / 8)][(seg % (C / 8)) * 8]) = pf.kh[s];
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -642,8 +655,12 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
                 o[y] = mfma_bf16(aq, bs, o[y]);
             }
         }
+        // U^T (bf16): element (t, n) -> ut[n][t]
 #pragma unroll
-        for (int y = 0; y < 2; ++y) store16(&ss.U[16 * w][16 * y], LDX, u[y], lane, 1.f);
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ss.ut[16 * y + (lane & 15)][16 * w + (lane >> 4) * 4 + j] = f32_to_bf16(u[y][j]).bits;
         __syncthreads();
 
         // ---- O = Qt S0 + P U (causal) ----
@@ -654,10 +671,7 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
             const bf16x8_t ap = load_bf16x8(&ss.p[16 * w + (lane & 15)][kc]);
 #pragma unroll
             for (int y = 0; y < 2; ++y) {
-                bf16x8_t bu;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bu[e] = bf(ss.U[kc + e][16 * y + (lane & 15)]);
-                o[y] = mfma_bf16(ap, bu, o[y]);
+                o[y] = mfma_bf16(ap, load_bf16x8(&ss.ut[16 * y + (lane & 15)][kc]), o[y]);
             }
         }
 #pragma unroll
@@ -681,15 +695,10 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
             const int kc = 32 * s + (lane >> 4) * 8;  // tokens
             bf16x8_t bu[2];
 #pragma unroll
-            for (int y = 0; y < 2; ++y)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bu[y][e] = bf(ss.U[kc + e][16 * y + (lane & 15)]);
+            for (int y = 0; y < 2; ++y) bu[y] = load_bf16x8(&ss.ut[16 * y + (lane & 15)][kc]);
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-                const int i = 16 * (2 * w + x) + (lane & 15);
-                bf16x8_t ak;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ak[e] = __builtin_bit_cast(__bf16, ss.kh[kc + e][i]);
+                const bf16x8_t ak = load_bf16x8(&ss.kh[16 * (2 * w + x) + (lane & 15)][kc]);
 #pragma unroll
                 for (int y = 0; y < 2; ++y) S[x][y] = mfma_bf16(ak, bu[y], S[x][y]);
             }
