@@ -15,6 +15,7 @@ fp64 oracle on the host.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -23,6 +24,29 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+SDM_SRC = os.path.join(ROOT, "sparse_state_linear_product_amd", "csrc", "sdm_chunk.hip")
+SDM_PROFILE = os.path.join(ROOT, "profiles", "sdm_chunk_apply_1p4b_prefill.md")
+
+
+def measured_traffic(src=SDM_SRC, profile=SDM_PROFILE):
+    """HBM bytes per launch from the committed counter summary, or None.
+
+    The summary records the scaled FETCH_SIZE + WRITE_SIZE bytes of one
+    sdm_sparse_update launch (plan + apply kernels) together with the sha256 of
+    the kernel source it was taken on; once the source changes the counters no
+    longer describe the kernel and the figure is withheld.
+    """
+    import hashlib
+    try:
+        text = open(profile).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    m_s = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not (m_b and m_s) or m_s.group(1) != sha:
+        return None
+    return int(m_b.group(1))
 
 
 def sdm_kernel_bytes(cfg, io_bytes):
@@ -80,8 +104,8 @@ def bench_sdm(args, torch, sslp, wl):
     return dict(
         cfg=cfg, ms_per_step=total_ms / args.steps, value=tokens / (total_ms * 1e-3),
         roofline=dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                      kernel="sdm_sparse_update: sdm_records_kernel + sdm_update_pipe_kernel",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
+                      kernel="sdm_sparse_update: sdm_chunk_plan_kernel + sdm_chunk_apply_kernel",
                       kernel_avg_ms=round(k_avg_ms, 4),
                       bytes_per_launch=nbytes, bytes_per_token_head=per))
 

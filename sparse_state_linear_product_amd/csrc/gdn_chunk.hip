@@ -547,8 +547,13 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
     __shared__ StateSmem ss;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nblk = a.dv / DVB;
-    const int cb = blockIdx.x % nblk;
-    const int bh = blockIdx.x / nblk;
+    // XCD-aware placement: consecutive workgroup ids go to the 8 XCDs in turn,
+    // so renumber them to keep the column blocks of one (batch, head) -- which
+    // read the same chunk records at the same pace -- inside one XCD's L2.
+    int id = blockIdx.x;
+    if ((gridDim.x & 7u) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
+    const int cb = id % nblk;
+    const int bh = id / nblk;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const int n0 = cb * DVB;
     const int T = a.T, H = a.H, dv = a.dv, nch = a.nch;

@@ -14,11 +14,12 @@
 // its own key/query (the slides leave its formula out; reading stated in the
 // header).
 //
-// Execution.  One workgroup per (batch, head, 32-column block of d) walks the
-// sequence in chunks of 64 tokens.  Per chunk, wave 0 routes the tokens (fp32
-// softmax and top-k, ties to the lowest index) and builds, for every routed
-// partition, the time-ordered list of its visits inside the chunk (ballot +
-// popcount counting sort).  Then every partition is advanced independently by
+// Execution.  sse_route_kernel first routes every token on its own thread
+// (fp32 softmax and top-k, ties to the lowest index) into the sel / e_sel
+// arrays.  Then one workgroup per (batch, head, 32-column block of d) walks the
+// sequence in chunks of 64 tokens.  Per chunk, wave 0 reads the routing and
+// builds, for every routed partition, the time-ordered list of its visits
+// inside the chunk (ballot + popcount counting sort).  Then every partition is advanced independently by
 // its own wavefront: routed partition i by wave 2+i (32 columns), the shared
 // partition by waves 0 and 1 (16 columns each).  A wave processes its visits
 // in blocks of up to 16 as one GLA step in chunked form:
