@@ -19,12 +19,10 @@ struct bf16_t {
 SSLP_DEVICE float to_f32(float x) { return x; }
 SSLP_DEVICE float to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x.bits) << 16); }
 
-// round-to-nearest-even fp32 -> bf16 (finite inputs)
+// round-to-nearest-even fp32 -> bf16 (the gfx950 conversion instruction)
 SSLP_DEVICE bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
     bf16_t r;
-    r.bits = (uint16_t)(u >> 16);
+    r.bits = __builtin_bit_cast(uint16_t, (__bf16)f);
     return r;
 }
 template <typename T>

@@ -96,6 +96,10 @@ SMALL = [
     (1, 64, 2, 7, 8, 7, 7, 32, 32, "f32", 1),
     (1, 300, 3, 240, 40, 32, 32, 32, 32, "bf16", 0),
     (1, 177, 1, 40, 32, 16, 16, 32, 32, "bf16", 1),
+    # mid-size tables: tens of forwarded rows per chunk, and around the in-LDS
+    # forward capacity (some chunks pass rows through LDS, others patch directly)
+    (1, 200, 2, 100, 16, 32, 32, 32, 32, "f32", 0),
+    (1, 160, 1, 64, 24, 32, 32, 32, 32, "bf16", 1),
 ]
 
 
