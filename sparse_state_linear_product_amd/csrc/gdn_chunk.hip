@@ -91,6 +91,8 @@ struct __align__(16) Smem {
     float Hf[4][DK];      // KDA: e^{g_C - g_{16m}}
     float D[6][DK];       // KDA: e^{g_{16m} - g_{16n}}, pairs (1,0),(2,1),(3,2),(2,0),(3,1),(3,0)
     float gC[DK];         // KDA: e^{g_C}
+    float eg[C];          // GDN: e^{g_t}
+    float ehg[C];         // GDN: e^{g_C - g_t}
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 
@@ -138,57 +140,91 @@ struct GdnArgs {
 // prep kernel: one workgroup per (b, h, chunk)
 // ---------------------------------------------------------------------------
 template <bool KDA>
-__global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
+__global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nch = a.nch;
-    const int c = blockIdx.x % nch, bh = blockIdx.x / nch;
-    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const int T = a.T, H = a.H, dv = a.dv;
-    const int t0 = c * C;
     const uint16_t* qg = static_cast<const uint16_t*>(a.q);
     const uint16_t* kg = static_cast<const uint16_t*>(a.k);
     const uint16_t* vg = static_cast<const uint16_t*>(a.v);
-    uint8_t* rec = a.rec + (size_t)blockIdx.x * REC_BYTES;
 
-    // ---- the chunk's inputs (zero past the sequence end, alpha 1, beta 0) ----
-    for (int seg = tid; seg < C * DK / 8; seg += NTH) {
-        const int row = seg / (DK / 8), col = (seg % (DK / 8)) * 8;
-        const int t = t0 + row;
-        uint4 kk = make_uint4(0, 0, 0, 0), qq = kk, vv = kk;
-        if (t < T) {
-            const size_t off = (((size_t)b * T + t) * H + h) * DK + col;
-            kk = *reinterpret_cast<const uint4*>(kg + off);
-            qq = *reinterpret_cast<const uint4*>(qg + off);
-            vv = *reinterpret_cast<const uint4*>(vg + (((size_t)b * T + t) * H + h) * dv + col);
-        }
-        *reinterpret_cast<uint4*>(&sm.k[row][col]) = kk;
-        *reinterpret_cast<uint4*>(&sm.q[row][col]) = qq;
-        const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv);
+    // A workgroup walks the chunks blockIdx.x, blockIdx.x + gridDim.x, ...; the
+    // next chunk's inputs are loaded into registers while the current one is
+    // computed (zero past the sequence end, alpha 1, beta 0).
+    constexpr int NSG = C * DK / 8 / NTH;      // 16-byte pieces of q, k, v per thread
+    constexpr int NSA = KDA ? C * DK / 4 / NTH : 0;  // float4 pieces of alpha per thread
+    uint4 pk[NSG], pq[NSG], pv[NSG];
+    float4 pa[NSA > 0 ? NSA : 1];
+    float pbeta = 0.f, palpha = 1.f;
+    auto fetch = [&](int task) {
+        const int c = task % nch, bh = task / nch;
+        const int b = bh / H, h = bh - (bh / H) * H;
+        const int t0 = c * C;
+        // piece i of a thread: token row = lane, columns 8 (w + 4 i) .. + 7, so that
+        // the transposed stores of V below hit 64 different rows at once
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm.xt[col + e][row] = ve[e];  // raw V, transposed
-    }
-    if (tid < C) {
-        const int t = t0 + tid;
-        const size_t bth = ((size_t)b * T + t) * H + h;
-        sm.beta[tid] = t < T ? a.beta[bth] : 0.f;
-        if (!KDA) sm.g[tid] = __logf(t < T ? a.alpha[bth] : 1.f);
-    }
-    if (KDA) {
-        for (int seg = tid; seg < C * DK / 4; seg += NTH) {
-            const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
+        for (int i = 0; i < NSG; ++i) {
+            const int row = lane, col = 8 * (w + (NTH / 64) * i);
             const int t = t0 + row;
-            *reinterpret_cast<float4*>(&sm.u.alpha[row][col]) =
-                t < T ? *reinterpret_cast<const float4*>(a.alpha + (((size_t)b * T + t) * H + h) * DK + col)
-                      : make_float4(1.f, 1.f, 1.f, 1.f);
+            pk[i] = pq[i] = pv[i] = make_uint4(0, 0, 0, 0);
+            if (t < T) {
+                const size_t off = (((size_t)b * T + t) * H + h) * DK + col;
+                pk[i] = *reinterpret_cast<const uint4*>(kg + off);
+                pq[i] = *reinterpret_cast<const uint4*>(qg + off);
+                pv[i] = *reinterpret_cast<const uint4*>(vg + (((size_t)b * T + t) * H + h) * dv + col);
+            }
+        }
+        if constexpr (KDA) {
+#pragma unroll
+            for (int i = 0; i < NSA; ++i) {
+                const int seg = tid + NTH * i;
+                const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
+                const int t = t0 + row;
+                pa[i] = t < T ? *reinterpret_cast<const float4*>(a.alpha + (((size_t)b * T + t) * H + h) * DK + col)
+                              : make_float4(1.f, 1.f, 1.f, 1.f);
+            }
+        }
+        {  // every wave: the gates of token row = lane
+            const int t = t0 + lane;
+            const size_t bth = ((size_t)b * T + t) * H + h;
+            pbeta = t < T ? a.beta[bth] : 0.f;
+            if (!KDA) palpha = t < T ? a.alpha[bth] : 1.f;
+        }
+    };
+    if ((int)blockIdx.x < ntask) fetch(blockIdx.x);
+    for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int c = task % nch, bh = task / nch;
+    const int b = bh / H, h = bh - (bh / H) * H;
+    (void)c;
+    (void)b;
+    (void)h;
+    uint8_t* rec = a.rec + (size_t)task * REC_BYTES;
+    __syncthreads();  // the previous chunk's use of the shared arrays is over
+    // X = diag(beta) V, stored transposed (bf16); K, Q as they are
+#pragma unroll
+    for (int i = 0; i < NSG; ++i) {
+        const int row = lane, col = 8 * (w + (NTH / 64) * i);
+        *reinterpret_cast<uint4*>(&sm.k[row][col]) = pk[i];
+        *reinterpret_cast<uint4*>(&sm.q[row][col]) = pq[i];
+        const uint16_t* ve = reinterpret_cast<const uint16_t*>(&pv[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.xt[col + e][row] = f32_to_bf16(pbeta * bf2f(ve[e])).bits;
+    }
+    if constexpr (KDA) {
+#pragma unroll
+        for (int i = 0; i < NSA; ++i) {
+            const int seg = tid + NTH * i;
+            const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
+            *reinterpret_cast<float4*>(&sm.u.alpha[row][col]) = pa[i];
         }
     }
-    __syncthreads();
-    // X = diag(beta) V (bf16, transposed, in place)
-    for (int e = tid; e < C * DK; e += NTH) {
-        const int n = e / C, t = e % C;
-        sm.xt[n][t] = f32_to_bf16(sm.beta[t] * bf2f(sm.xt[n][t])).bits;
+    if (tid < C) {  // wave 0: lane = token
+        sm.beta[tid] = pbeta;
+        if (!KDA) sm.g[tid] = __logf(palpha);
     }
+    if (task + (int)gridDim.x < ntask) fetch(task + gridDim.x);  // in flight during this chunk
+    __syncthreads();
 
         // ---------------- decay bookkeeping ----------------
         float decC_s = 1.f;  // GDN: e^{g_C}
@@ -204,6 +240,10 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
             }
             __syncthreads();
             decC_s = __expf(sm.g[C - 1]);
+            if (tid < C) {
+                sm.eg[tid] = __expf(sm.g[tid]);
+                sm.ehg[tid] = __expf(sm.g[C - 1] - sm.g[tid]);
+            }
         } else {
             // thread (channel i, half hf) walks the 32 tokens of blocks 2hf, 2hf+1:
             // E+ = product of alphas after the block's first token, E- = 1/E+
@@ -346,7 +386,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
         for (int e = tid; e < C * DK; e += NTH) {
             const int i = e / C, t = e % C;
             float kt;
-            if constexpr (!KDA) kt = bf2f(sm.k[t][i]) * __expf(sm.g[t]);
+            if constexpr (!KDA) kt = bf2f(sm.k[t][i]) * sm.eg[t];
             else kt = bf2f(sm.k[t][i]) * sm.F[t >> 4][i];
             sm.kbt[i][t] = f32_to_bf16(sm.beta[t] * kt).bits;
         }
@@ -489,7 +529,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
                 for (int e = 0; e < 8; e += 2) {
                     float q0, q1;
                     if constexpr (!KDA) {
-                        const float fq = __expf(sm.g[t]);
+                        const float fq = sm.eg[t];
                         q0 = bf2f(sm.q[t][i0 + e]) * fq;
                         q1 = bf2f(sm.q[t][i0 + e + 1]) * fq;
                     } else {
@@ -507,8 +547,8 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
                 for (int e = 0; e < 8; e += 2) {
                     float k0, k1;
                     if constexpr (!KDA) {
-                        k0 = bf2f(sm.k[t0e + e][i]) * __expf(sm.g[C - 1] - sm.g[t0e + e]);
-                        k1 = bf2f(sm.k[t0e + e + 1][i]) * __expf(sm.g[C - 1] - sm.g[t0e + e + 1]);
+                        k0 = bf2f(sm.k[t0e + e][i]) * sm.ehg[t0e + e];
+                        k1 = bf2f(sm.k[t0e + e + 1][i]) * sm.ehg[t0e + e + 1];
                     } else {
                         k0 = bf2f(sm.km[t0e + e][i]) * sm.Hf[(t0e + e) >> 4][i];
                         k1 = bf2f(sm.km[t0e + e + 1][i]) * sm.Hf[(t0e + e + 1) >> 4][i];
@@ -520,6 +560,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a) {
             float* gc = reinterpret_cast<float*>(rec + REC_GC);
             if (tid < DK) gc[tid] = KDA ? sm.gC[tid] : decC_s;
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -729,6 +770,19 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
 
 }  // namespace
 
+// one prep workgroup per compute unit (its LDS footprint allows no more)
+int prep_grid() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 size_t gdn_record_bytes(int B, int T, int H) {
     const long long nch = (T + C - 1) / C;
     return (size_t)B * H * nch * REC_BYTES;
@@ -741,8 +795,10 @@ hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, con
     const int nch = (T + C - 1) / C;
     GdnArgs a{B, T, H, dv, nch, q, k, v, alpha, beta, S0, S_out, o, static_cast<uint8_t*>(rec)};
     if (nch > 0) {
-        if (kda) gdn_prep_kernel<true><<<(unsigned)(B * H * nch), NTH, 0, st>>>(a);
-        else gdn_prep_kernel<false><<<(unsigned)(B * H * nch), NTH, 0, st>>>(a);
+        const int ntask = B * H * nch;
+        const int grid = ntask < prep_grid() ? ntask : prep_grid();
+        if (kda) gdn_prep_kernel<true><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
+        else gdn_prep_kernel<false><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
