@@ -84,6 +84,13 @@ SSLP_DEVICE uint64_t wave_max_u64(uint64_t x) {
 // Orders LDS/global accesses of one wavefront: a compiler barrier plus
 // wavefront-scope release/acquire (the hardware keeps a wave's memory
 // operations in order, so no wait instruction is needed).
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// operations, then meets the others.  Unlike __syncthreads(), whose fence also
+// waits for every outstanding global load and store, it lets loads issued
+// ahead of time (register or LDS-DMA prefetch) stay in flight across it.  Any
+// wait for global memory a barrier must cover is written out before it.
+SSLP_DEVICE void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
 SSLP_DEVICE void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

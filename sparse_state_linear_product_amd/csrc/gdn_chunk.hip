@@ -200,7 +200,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
     (void)b;
     (void)h;
     uint8_t* rec = a.rec + (size_t)task * REC_BYTES;
-    __syncthreads();  // the previous chunk's use of the shared arrays is over
+    block_sync_lds();  // the previous chunk's use of the shared arrays is over
     // X = diag(beta) V, stored transposed (bf16); K, Q as they are
 #pragma unroll
     for (int i = 0; i < NSG; ++i) {
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
         if (!KDA) sm.g[tid] = __logf(palpha);
     }
     if (task + (int)gridDim.x < ntask) fetch(task + gridDim.x);  // in flight during this chunk
-    __syncthreads();
+    block_sync_lds();
 
         // ---------------- decay bookkeeping ----------------
         float decC_s = 1.f;  // GDN: e^{g_C}
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                 }
                 sm.g[lane] = x;
             }
-            __syncthreads();
+            block_sync_lds();
             decC_s = __expf(sm.g[C - 1]);
             if (tid < C) {
                 sm.eg[tid] = __expf(sm.g[tid]);
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                 sm.uw.blk.af[blk][i] = sm.u.alpha[16 * blk][i];
             }
         }
-        __syncthreads();
+        block_sync_lds();
         if constexpr (KDA) {
             // per channel: F[m] = e^{g_{16m}}, H[m] = e^{g_C - g_{16m}},
             // D[m][n] = e^{g_{16m} - g_{16n}}, all as products of alphas
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                 }
                 sm.gC[i] = pre;
             }
-            __syncthreads();
+            block_sync_lds();
         }
 
 
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                 }
             }
         }
-        __syncthreads();
+        block_sync_lds();
         // write A (strictly lower, beta and decay applied) and P (causal) tiles
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
             else kt = bf2f(sm.k[t][i]) * sm.F[t >> 4][i];
             sm.kbt[i][t] = f32_to_bf16(sm.beta[t] * kt).bits;
         }
-        __syncthreads();
+        block_sync_lds();
 
         // ---------------- T = (I + A)^{-1} ----------------
         if (w == 0) {
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                 sm.u.s.Tm[16 * bi + (within >> 4)][16 * bj + (within & 15)] = 0.f;
             }
         }
-        __syncthreads();
+        block_sync_lds();
         {
             // stage 1: L_ij = T_ii A_ij (in place in A); pairs (1,0),(2,1),(3,2),(2,0),(3,1),(3,0)
             const int pi[6] = {1, 2, 3, 2, 3, 3}, pj[6] = {0, 1, 2, 0, 1, 0};
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                 }
             }
         }
-        __syncthreads();
+        block_sync_lds();
         {
             // stage 2: L^2 blocks (2,0), (3,1), (3,0) into T's (then overwritten) blocks
             f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -446,14 +446,14 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                 store16(&sm.u.s.Tm[48][0], LDF, acc, lane, 1.f);
             }
         }
-        __syncthreads();
+        block_sync_lds();
         if (w == 0) {
             // stage 3: (L^3)_30 = L32 (L^2)_20
             f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
             acc = mm16_f32(&sm.u.s.A[48][32], LDF, &sm.u.s.Tm[32][0], LDF, acc, lane);
             store16(&sm.L3[0][0], 17, acc, lane, 1.f);
         }
-        __syncthreads();
+        block_sync_lds();
         {
             // stage 4: T_ij = M_ij T_jj with M = -L + L^2 - L^3 (block-wise)
             const int pi[6] = {1, 2, 3, 2, 3, 3}, pj[6] = {0, 1, 2, 0, 1, 0};
@@ -477,14 +477,14 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                     }
                 }
             }
-            __syncthreads();  // all reads of the L^2 scratch done before T overwrites it
+            block_sync_lds();  // all reads of the L^2 scratch done before T overwrites it
 #pragma unroll
             for (int rep = 0; rep < 2; ++rep) {
                 const int p = w + 4 * rep;
                 if (p < 6) store16(&sm.u.s.Tm[16 * pi[p]][16 * pj[p]], LDF, res[rep], lane, 1.f);
             }
         }
-        __syncthreads();
+        block_sync_lds();
 
 
         // ---------------- U0 = T X and Wn = -T diag(beta) Kt, rows block w ----------------
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
             const int t = e / C, j = e % C;
             sm.tb[t][j] = f32_to_bf16(sm.u.s.Tm[t][j]).bits;
         }
-        __syncthreads();
+        block_sync_lds();
         {
             float* u0 = reinterpret_cast<float*>(rec + REC_U0);
             uint16_t* wn = reinterpret_cast<uint16_t*>(rec + REC_WN);
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
         commit(pf);
     }
     publish_state();
-    __syncthreads();
+    block_sync_lds();
 
     for (int c = 0; c < nch; ++c) {
         const int t0 = c * C;
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 ss.ut[16 * y + (lane & 15)][16 * w + (lane >> 4) * 4 + j] = f32_to_bf16(u[y][j]).bits;
-        __syncthreads();
+        block_sync_lds();
 
         // ---- O = Qt S0 + P U (causal) ----
 #pragma unroll
@@ -749,10 +749,10 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
                 for (int y = 0; y < 2; ++y) S[x][y] = mfma_bf16(ak, bu[y], S[x][y]);
             }
         }
-        __syncthreads();  // everyone is done with this chunk's LDS contents
+        block_sync_lds();  // everyone is done with this chunk's LDS contents
         if (c + 1 < nch) commit(pf);
         publish_state();
-        __syncthreads();
+        block_sync_lds();
     }
 
     // final state slice

@@ -630,10 +630,10 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
     plan_dma(0);
     if (nch > 1) plan_dma(1);
     wait_vm0();
-    __syncthreads();
+    block_sync_lds();
     row_dma(0);
     wait_vm0();
-    __syncthreads();
+    block_sync_lds();
 
     // compute mapping: lane (t, qt) = (lane/4, lane%4) owns columns 2qt, 2qt+1 of token t
     const int ct = lane >> 2, qt = lane & 3;
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
             lds_write_f32x2(part0 + (uint32_t)((wave * 2 + 0) * CC * CW * 4) + cofs, g);
             lds_write_f32x2(part0 + (uint32_t)((wave * 2 + 1) * CC * CW * 4) + cofs, hh);
         }
-        __syncthreads();
+        block_sync_lds();
 
         // ---- wave 0: g, h, r = v - g, res = T r, y = h + Bm res ----
         const bool tok_ok = ct < ntok;
@@ -758,7 +758,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
                 }
             }
         }
-        __syncthreads();
+        block_sync_lds();
 
         // ---- write-back of this wave's write rows (j = wave + NWAVE m < 16): each
         //      written slot once, at its last visit; entries with an exception
@@ -838,7 +838,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
         // ---- rows of chunk c+1 (and plan c+2) have landed in every wave: forward
         //      this chunk's final values into the rows of chunk c+1 holding the same slot ----
         wait_vm0();
-        __syncthreads();
+        block_sync_lds();
         if (__ballot(any_fwd) != 0ull) {
             const uint32_t Sn = stage0 + (uint32_t)((c + 1) % 2) * STAGE_BYTES;
 #pragma unroll
@@ -850,7 +850,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
                 }
             }
         }
-        __syncthreads();
+        block_sync_lds();
     }
     wait_vm0();
 }

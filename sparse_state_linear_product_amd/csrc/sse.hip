@@ -378,7 +378,7 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
                     if (lane == 0) sm.cnt[i] = __popcll(m);
                 }
             }
-            __syncthreads();
+            block_sync_lds();
             // ---------------- every partition advances over its visits ----------------
             if (active) {
                 WaveScratch& ws = sm.ws[w];
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
                     }
                 }
             }
-            __syncthreads();
+            block_sync_lds();
             // ---------------- fixed-order combine: routed by rank, then shared ----------------
             for (int idx = tid; idx < C * DB; idx += blockDim.x) {
                 const int t = idx / DB, n = idx - (idx / DB) * DB;
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
                     og[(((size_t)b * T + t0 + t) * H + h) * dv + n0 + n] = from_f32<io_t>(acc);
                 }
             }
-            __syncthreads();
+            block_sync_lds();
         }
         if (active) {
 #pragma unroll
