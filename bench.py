@@ -171,6 +171,27 @@ def bench_rows(args, torch, sslp, wl):
                           hbm_frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           bytes_per_call=by)
     del x, S, o
+    # SSE decode: 64 independent sequences, N=8 routed + 1 shared states of 128x128 per head;
+    # a step reads and writes the 2 selected and the shared state of every (sequence, head)
+    cfg = wl.SSE_DECODE
+    S = torch.empty((cfg.B, cfg.H, cfg.N + 1, cfg.c, cfg.d), dtype=torch.float32, device=dev)
+    S.normal_(generator=torch.Generator(device=dev).manual_seed(cfg.seed))
+    steps = {k: v.to(dev) for k, v in wl.sse_inputs(cfg, T=args.decode_steps).items()}
+    sl = [{k: v[:, t].contiguous() for k, v in steps.items()} for t in range(args.decode_steps)]
+    o = torch.empty((cfg.B, cfg.H, cfg.d), dtype=cfg.dtype, device=dev)
+
+    def sse_steps():
+        for s in sl:
+            sslp.sse_decode_step(s["logits"], s["q"], s["k"], s["v"], s["lam"], S, cfg.topk, o=o)
+
+    ms = time_call(torch, sse_steps, 1, warmup=1) / args.decode_steps
+    per = 2 * (cfg.topk + 1) * cfg.c * cfg.d * 4 + 4 * cfg.N + 2 * (2 * cfg.c + cfg.d) + 4 * cfg.c + 2 * cfg.d
+    nbytes = per * cfg.B * cfg.H
+    rows[cfg.name] = dict(ms_per_step=round(ms, 4), tokens_per_s=round(cfg.B / (ms * 1e-3), 1),
+                          gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          bytes_per_step=nbytes, steps=args.decode_steps)
+    del S, steps, sl, o
     # SDM decode: 64 independent sequences on the 1.4B-layer table shape
     cfg = wl.SDM_DECODE
     M = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d_v), dtype=torch.float32, device=dev)

@@ -245,6 +245,23 @@ int sse_forward(const sslp_sse_shape* shape, int dtype, const float* gate_logits
                 const void* k_sh, float* S, void* o, int32_t* sel, float* e_sel, void* workspace,
                 size_t ws_bytes, void* stream);
 
+/*
+ * sse_decode_step -- one token of every sequence (shape->T must be 1): the same
+ * operation as sse_forward with T = 1, reading and writing only the topk
+ * selected states and the shared one (the SSE slides' note on decoding under
+ * "Varlen groups tokens while preserving causal order": only the selected
+ * recurrent states are updated).  Layouts as in sse_forward with T = 1:
+ *   gate_logits [B,1,H,N] fp32; q, k, q_sh, k_sh [B,1,H,c] dtype; v [B,1,H,d];
+ *   lambda [B,1,H,c] fp32; S [B,H,N+1,c,d] fp32 in/out; o [B,1,H,d] dtype out;
+ *   sel [B,1,H,topk] int32 and e_sel [B,1,H,topk] fp32 optional (written when
+ *   given).  No workspace.  Errors: SSLP_ERR_INVALID_ARG when T != 1, else as
+ *   sse_forward.  Steps of one sequence must be issued in order on one stream.
+ */
+int sse_decode_step(const sslp_sse_shape* shape, int dtype, const float* gate_logits,
+                    const void* q, const void* k, const void* v, const float* lambda,
+                    const void* q_sh, const void* k_sh, float* S, void* o, int32_t* sel,
+                    float* e_sel, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* utilities                                                                 */
 /* ------------------------------------------------------------------------ */

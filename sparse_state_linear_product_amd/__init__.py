@@ -10,7 +10,7 @@ allocated with torch when the caller does not pass one.
 Functions (see include/sslp.h for the exact semantics):
   sdm_forward, sdm_decode_step, sdm_address, sdm_sparse_update   Sparse Delta Memory
   gdn_chunk_forward                                              Gated DeltaNet / KDA
-  sse_forward                                                    Sparse State Expansion
+  sse_forward, sse_decode_step                                   Sparse State Expansion
 """
 import ctypes
 
@@ -21,7 +21,7 @@ from ._lib import (DECAY_CHANNEL, DECAY_SCALAR, RESIDUAL_PER_SLOT, RESIDUAL_SHAR
                    SdmShape, SseShape, SslpError, check, lib)
 
 __all__ = ["sdm_forward", "sdm_decode_step", "sdm_address", "sdm_sparse_update",
-           "gdn_chunk_forward", "sse_forward", "SslpError", "RESIDUAL_SHARED",
+           "gdn_chunk_forward", "sse_forward", "sse_decode_step", "SslpError", "RESIDUAL_SHARED",
            "RESIDUAL_PER_SLOT", "DECAY_SCALAR", "DECAY_CHANNEL", "version"]
 
 
@@ -252,4 +252,37 @@ def sse_forward(gate_logits, q, k, v, lam, S, topk, q_sh=None, k_sh=None, o=None
                            _ptr(k), _ptr(v), _ptr(lam), _ptr(q_sh), _ptr(k_sh), _ptr(S), _ptr(o),
                            _ptr(sel), _ptr(e_sel), _ptr(ws), nbytes, _stream(stream))
     check("sse_forward", rc)
+    return o
+
+
+def sse_decode_step(gate_logits, q, k, v, lam, S, topk, q_sh=None, k_sh=None, o=None, sel=None,
+                    e_sel=None, stream=None):
+    """One token per sequence: gate_logits [B,H,N] fp32; q, k [B,H,c]; v [B,H,d];
+    lam [B,H,c] fp32; S [B,H,N+1,c,d] fp32 updated in place (only the selected and
+    the shared states).  Returns o [B,H,d]."""
+    B, H, N = gate_logits.shape
+    c, d = q.shape[-1], v.shape[-1]
+    dt = q.dtype
+    _need(gate_logits, torch.float32, (B, H, N), "gate_logits")
+    _need(q, dt, (B, H, c), "q")
+    _need(k, dt, (B, H, c), "k")
+    _need(v, dt, (B, H, d), "v")
+    _need(lam, torch.float32, (B, H, c), "lam")
+    _need(S, torch.float32, (B, H, N + 1, c, d), "S")
+    if q_sh is not None:
+        _need(q_sh, dt, (B, H, c), "q_sh")
+    if k_sh is not None:
+        _need(k_sh, dt, (B, H, c), "k_sh")
+    if o is None:
+        o = torch.empty((B, H, d), dtype=dt, device=q.device)
+    _need(o, dt, (B, H, d), "o")
+    if sel is not None:
+        _need(sel, torch.int32, (B, H, topk), "sel")
+    if e_sel is not None:
+        _need(e_sel, torch.float32, (B, H, topk), "e_sel")
+    shape = SseShape(B, 1, H, N, topk, c, d, 64)
+    rc = lib().sse_decode_step(ctypes.byref(shape), _dtype_code(q), _ptr(gate_logits), _ptr(q),
+                               _ptr(k), _ptr(v), _ptr(lam), _ptr(q_sh), _ptr(k_sh), _ptr(S),
+                               _ptr(o), _ptr(sel), _ptr(e_sel), _stream(stream))
+    check("sse_decode_step", rc)
     return o

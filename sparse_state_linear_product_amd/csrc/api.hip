@@ -396,4 +396,30 @@ int sse_forward(const sslp_sse_shape* s, int dtype, const float* gate_logits, co
                       "sse_forward launch");
 }
 
+int sse_decode_step(const sslp_sse_shape* s, int dtype, const float* gate_logits, const void* q,
+                    const void* k, const void* v, const float* lambda, const void* q_sh,
+                    const void* k_sh, float* S, void* o, int32_t* sel, float* e_sel, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_sse_shape(s)) return rc;
+    REQUIRE(s->T == 1, SSLP_ERR_INVALID_ARG, "sse_decode_step takes T = 1 (got %d)", s->T);
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE(dtype == SSLP_BF16, SSLP_ERR_UNSUPPORTED,
+            "sse_decode_step supports bf16 q/k/v only (got dtype %d)", dtype);
+    REQUIRE_PTR(S);
+    REQUIRE_PTR(gate_logits);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(lambda);
+    REQUIRE_PTR(o);
+    REQUIRE_ALIGNED(q_sh);
+    REQUIRE_ALIGNED(k_sh);
+    REQUIRE_ALIGNED(sel);
+    REQUIRE_ALIGNED(e_sel);
+    return hip_status(sslp::launch_sse_decode(s->B, s->H, s->N, s->topk, s->d, gate_logits, q, k,
+                                              v, lambda, q_sh, k_sh, S, o, sel, e_sel,
+                                              (hipStream_t)stream),
+                      "sse_decode_step launch");
+}
+
 }  // extern "C"

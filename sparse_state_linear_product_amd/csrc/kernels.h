@@ -50,5 +50,10 @@ hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
                       const float* logits, const void* q, const void* k, const void* v,
                       const float* lam, const void* q_sh, const void* k_sh, float* S, void* o,
                       int32_t* sel, float* e_sel, hipStream_t st);
+// one decode step (one token per sequence), touching only the selected states
+hipError_t launch_sse_decode(int B, int H, int N, int topk, int dv, const float* logits,
+                             const void* q, const void* k, const void* v, const float* lam,
+                             const void* q_sh, const void* k_sh, float* S, void* o, int32_t* sel,
+                             float* e_sel, hipStream_t st);
 
 }  // namespace sslp

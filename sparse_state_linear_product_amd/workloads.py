@@ -82,6 +82,8 @@ SDM_14B = SdmConfig("sdm_prefill_1p4b_B1_T8192_H2_N57600_dv960", 1, 8192, 2, 240
                     32, BF16, 1004)
 SDM_DECODE = SdmConfig("sdm_decode_1p4b_seq64_H2_N57600_dv960", 64, 1, 2, 240, 960, 32, 32, 32, 32,
                        BF16, 1005)
+# SSE decode: 64 independent sequences, one token each per step, at the SSE layer shape
+SSE_DECODE = SseConfig("sse_decode_seq64_H16_N8k2_c128", 64, 1, 16, 8, 2, 128, 128, BF16, 1013)
 DECODE_PREFIX = 256  # tokens of seeded prefix written into each decode table by the benchmark
 
 

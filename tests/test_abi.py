@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("sdm_forward", "sdm_decode_step", "sse_forward", "gdn_chunk_forward",
+    for required in ("sdm_forward", "sdm_decode_step", "sse_forward", "sse_decode_step",
+                     "gdn_chunk_forward",
                      "sdm_address", "sdm_sparse_update", "sslp_last_error", "sslp_version"):
         assert required in names
 
@@ -117,3 +118,11 @@ def test_gdn_and_sse_shape_errors():
     assert lib.sse_forward(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == _lib.SSLP_ERR_INVALID_ARG
     s = _lib.SseShape(1, 8, 1, 8, 2, 64, 128, 64)
     assert lib.sse_forward(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == _lib.SSLP_ERR_UNSUPPORTED
+    # the decode step takes exactly one token per sequence
+    s = _lib.SseShape(2, 2, 1, 8, 2, 128, 128, 64)
+    assert lib.sse_decode_step(ctypes.byref(s), 1, *([FAKE] * 11), None) == _lib.SSLP_ERR_INVALID_ARG
+    s = _lib.SseShape(2, 1, 1, 8, 9, 128, 128, 64)
+    assert lib.sse_decode_step(ctypes.byref(s), 1, *([FAKE] * 11), None) == _lib.SSLP_ERR_INVALID_ARG
+    s = _lib.SseShape(2, 1, 1, 8, 2, 128, 128, 64)
+    assert lib.sse_decode_step(ctypes.byref(s), 0, *([FAKE] * 11), None) == _lib.SSLP_ERR_UNSUPPORTED
+    assert lib.sse_decode_step(ctypes.byref(s), 1, *([None] * 11), None) == _lib.SSLP_ERR_INVALID_ARG

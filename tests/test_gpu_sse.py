@@ -100,3 +100,67 @@ def test_sse_full_config():
     announce(f"{cfg.name} full size")
     x = wl.sse_inputs(cfg)
     _check(x, cfg.N, cfg.topk, cfg.name)
+
+
+# ---------------- decode step (one token per sequence) ----------------
+
+def _decode_run(x, N, topk, S0, q_sh=None, k_sh=None):
+    import sparse_state_linear_product_amd as sslp
+    B, T, H, _ = x["logits"].shape
+    S = S0.clone().to(DEV).contiguous()
+    os, sels, es = [], [], []
+    for t in range(T):
+        st = {k: v[:, t].contiguous().to(DEV) for k, v in x.items()}
+        sel = torch.empty((B, H, topk), dtype=torch.int32, device=DEV)
+        e_sel = torch.empty((B, H, topk), dtype=torch.float32, device=DEV)
+        o = sslp.sse_decode_step(st["logits"], st["q"], st["k"], st["v"], st["lam"], S, topk,
+                                 q_sh=None if q_sh is None else q_sh[:, t].contiguous().to(DEV),
+                                 k_sh=None if k_sh is None else k_sh[:, t].contiguous().to(DEV),
+                                 sel=sel, e_sel=e_sel)
+        os.append(o)
+        sels.append(sel)
+        es.append(e_sel)
+    torch.cuda.synchronize()
+    return dict(o=torch.stack(os, 1).cpu(), S=S.cpu(), sel=torch.stack(sels, 1).cpu().numpy(),
+                e_sel=torch.stack(es, 1).cpu().numpy())
+
+
+@pytest.mark.parametrize("N,topk,B,H,T", [(8, 2, 3, 2, 6), (5, 3, 2, 3, 4), (1, 1, 2, 1, 3),
+                                          (8, 4, 1, 2, 5)])
+def test_sse_decode_steps_match_oracle(N, topk, B, H, T):
+    announce(f"sse_decode_step N={N} k={topk} B={B} H={H} steps={T}")
+    cfg = wl.SseConfig("dec", B, T, H, N, topk, 128, 128, torch.bfloat16, 700 + 10 * N + topk)
+    x = wl.sse_inputs(cfg)
+    g = torch.Generator().manual_seed(701 + N)
+    S0 = torch.randn((B, H, N + 1, 128, 128), generator=g) * 0.1
+    got = _decode_run(x, N, topk, S0)
+    ref = _ref(x, topk, S0)
+    np.testing.assert_array_equal(got["sel"], ref["sel"], err_msg="decode selection")
+    e_e = np.abs(got["e_sel"] - ref["e_sel"]).max()
+    e_o = maxrel(got["o"].double().numpy(), ref["o"])
+    e_S = maxrel(got["S"].double().numpy(), ref["S"])
+    print(f"  decode N={N} k={topk}: e_sel {e_e:.2e} o {e_o:.2e} S {e_S:.2e}", flush=True)
+    assert e_e <= TOL_FP32
+    assert e_o <= TOL_BF16 and e_S <= TOL_BF16
+
+
+def test_sse_decode_touches_only_selected_states_and_separate_shared_qk():
+    announce("sse_decode_step: untouched states bitwise, separate shared q/k")
+    B, H, N, topk = 2, 3, 8, 2
+    cfg = wl.SseConfig("dec1", B, 1, H, N, topk, 128, 128, torch.bfloat16, 777)
+    x = wl.sse_inputs(cfg)
+    g = torch.Generator().manual_seed(778)
+    S0 = torch.randn((B, H, N + 1, 128, 128), generator=g)
+    q_sh = torch.randn((B, 1, H, 128), generator=g).bfloat16()
+    k_sh = torch.softmax(torch.randn((B, 1, H, 128), generator=g), -1).bfloat16()
+    got = _decode_run(x, N, topk, S0, q_sh=q_sh, k_sh=k_sh)
+    ref = _ref(x, topk, S0, q_sh=q_sh, k_sh=k_sh)
+    np.testing.assert_array_equal(got["sel"], ref["sel"])
+    assert maxrel(got["o"].double().numpy(), ref["o"]) <= TOL_BF16
+    assert maxrel(got["S"].double().numpy(), ref["S"]) <= TOL_BF16
+    for b in range(B):
+        for h in range(H):
+            used = set(got["sel"][b, 0, h].tolist()) | {N}
+            for i in range(N + 1):
+                if i not in used:
+                    assert torch.equal(got["S"][b, h, i], S0[b, h, i]), (b, h, i)
