@@ -229,13 +229,10 @@ static int sdm_run(const sslp_sdm_shape* s, int T, int dtype, int residual_mode,
     int32_t* ir = idx_r ? idx_r : reinterpret_cast<int32_t*>(ws + 2 * bw);
     float* wr = wt_r ? wt_r : reinterpret_cast<float*>(ws + 2 * bw + br);
     hipStream_t st = (hipStream_t)stream;
-    if (int rc = hip_status(
-            sslp::launch_sdm_address((int)P, s->sqrtN, dtype, sw1, sw2, s->k_w, s->W, iw, ww, st),
-            "sdm write addressing launch"))
-        return rc;
-    if (int rc = hip_status(
-            sslp::launch_sdm_address((int)P, s->sqrtN, dtype, sr1, sr2, s->k_r, s->R, ir, wr, st),
-            "sdm read addressing launch"))
+    if (int rc = hip_status(sslp::launch_sdm_address_pair((int)P, s->sqrtN, dtype, sw1, sw2, s->k_w,
+                                                          s->W, iw, ww, sr1, sr2, s->k_r, s->R, ir,
+                                                          wr, st),
+                            "sdm addressing launch"))
         return rc;
     sslp::SdmUpdateArgs a{};
     a.B = s->B;

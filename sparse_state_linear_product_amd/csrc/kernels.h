@@ -14,6 +14,11 @@ int address_set_size(int k, int budget);
 
 hipError_t launch_sdm_address(int P, int sqrtN, int dtype, const void* s1, const void* s2, int k,
                               int budget, int32_t* idx, float* wt, hipStream_t st);
+// write and read addressing of the same problems (one launch for small batches)
+hipError_t launch_sdm_address_pair(int P, int sqrtN, int dtype, const void* sw1, const void* sw2,
+                                   int k_w, int W, int32_t* iw, float* ww, const void* sr1,
+                                   const void* sr2, int k_r, int R, int32_t* ir, float* wr,
+                                   hipStream_t st);
 
 struct SdmUpdateArgs {
     int B, T, H, N, dv, W, R;

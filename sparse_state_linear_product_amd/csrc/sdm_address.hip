@@ -184,6 +184,148 @@ __global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
     if (lane + 64 < budget) out_w[lane + 64] = wl1 / z;
 }
 
+// ---------------------------------------------------------------------------
+// Latency-oriented variant for small batches (a decode step): one workgroup of
+// 256 threads per problem, and the write and read problems of a step in one
+// launch.  Ranks are found by counting (rank of key x = number of keys above
+// it; keys are distinct), which is exact under the same total order as the
+// wavefront kernel:
+//   1. rank each half's sqrtN keys, keep ranks < k (the per-half top-k);
+//   2. the dominance set D (as above), ranked by counting; tau = its
+//      budget-th key;
+//   3. F = #{k^2 candidates with key >= tau}; F == budget proves D's top-budget
+//      is the answer, else all k^2 candidates are ranked by counting;
+//   4. softmax over the selected scores.
+// Limits: sqrtN <= 256, k <= 64, budget <= 64, |D| <= 256 (wg_address_fits).
+// ---------------------------------------------------------------------------
+constexpr int WG = 256;
+
+struct AddrPairArgs {
+    const void* s1[2];
+    const void* s2[2];
+    int32_t* idx[2];
+    float* wt[2];
+    int k[2], budget[2], nD[2];
+    int P, sqrtN;
+};
+
+template <typename in_t>
+__global__ __launch_bounds__(WG) void sdm_address_wg_kernel(AddrPairArgs a) {
+    __shared__ uint64_t s_half[2][WG];
+    __shared__ float s_hsc[2][64];
+    __shared__ int s_hix[2][64];
+    __shared__ uint64_t s_cand[4096];  // D, or all k^2 candidates on the rare path
+    __shared__ uint64_t s_sel[64];
+    __shared__ uint64_t s_tau;
+    __shared__ int s_F;
+    __shared__ float s_part[WG / 64];
+
+    const int t = threadIdx.x;
+    const int set = blockIdx.x >= (unsigned)a.P ? 1 : 0;
+    const int p = (int)blockIdx.x - set * a.P;
+    const int n = a.sqrtN, k = a.k[set], budget = a.budget[set], nD = a.nD[set];
+    const in_t* h1 = static_cast<const in_t*>(a.s1[set]) + (size_t)p * n;
+    const in_t* h2 = static_cast<const in_t*>(a.s2[set]) + (size_t)p * n;
+
+    // 1. per-half top-k by rank counting
+    uint64_t x1 = 0ull, x2 = 0ull;
+    if (t < n) {
+        x1 = make_key(to_f32(h1[t]), (uint32_t)t);
+        x2 = make_key(to_f32(h2[t]), (uint32_t)t);
+    }
+    s_half[0][t] = x1;
+    s_half[1][t] = x2;
+    if (t == 0) {
+        s_F = 0;
+        s_tau = 0ull;  // below every key: only read if D had fewer than budget entries
+    }
+    __syncthreads();
+    if (t < n) {
+        int r1 = 0, r2 = 0;
+        for (int j = 0; j < n; ++j) {
+            r1 += s_half[0][j] > x1;
+            r2 += s_half[1][j] > x2;
+        }
+        if (r1 < k) {
+            s_hsc[0][r1] = key_score(x1);
+            s_hix[0][r1] = t;
+        }
+        if (r2 < k) {
+            s_hsc[1][r2] = key_score(x2);
+            s_hix[1][r2] = t;
+        }
+    }
+    __syncthreads();
+
+    // 2. D = {(i, j) : (i+1)(j+1) <= budget}, ranked by counting
+    uint64_t dkey = 0ull;
+    if (t < nD) {
+        int i = 0, off = 0;
+        for (;; ++i) {
+            int c = budget / (i + 1);
+            c = c < k ? c : k;
+            if (t < off + c) break;
+            off += c;
+        }
+        const int j = t - off;
+        const float sum = s_hsc[0][i] + s_hsc[1][j];  // one fp32 RNE add
+        dkey = make_key(sum, (uint32_t)s_hix[0][i] * (uint32_t)n + (uint32_t)s_hix[1][j]);
+        s_cand[t] = dkey;
+    }
+    __syncthreads();
+    if (t < nD) {
+        int r = 0;
+        for (int u = 0; u < nD; ++u) r += s_cand[u] > dkey;
+        if (r < budget) s_sel[r] = dkey;
+        if (r == budget - 1) s_tau = dkey;
+    }
+    __syncthreads();
+
+    // 3. exact count of all k^2 candidates at or above tau
+    const uint64_t tau = s_tau;
+    const int kk = k * k;
+    int F = 0;
+    for (int x = t; x < kk; x += WG) {
+        const int i = x / k, j = x - (x / k) * k;
+        const float sum = s_hsc[0][i] + s_hsc[1][j];
+        F += make_key(sum, (uint32_t)s_hix[0][i] * (uint32_t)n + (uint32_t)s_hix[1][j]) >= tau;
+    }
+    F = (int)wave_sum((float)F);
+    if ((t & 63) == 0) atomicAdd(&s_F, F);
+    __syncthreads();
+    if (s_F != budget) {
+        // rare path (rounding ties): rank all k^2 candidates
+        __syncthreads();
+        for (int x = t; x < kk; x += WG) {
+            const int i = x / k, j = x - (x / k) * k;
+            const float sum = s_hsc[0][i] + s_hsc[1][j];
+            s_cand[x] = make_key(sum, (uint32_t)s_hix[0][i] * (uint32_t)n + (uint32_t)s_hix[1][j]);
+        }
+        __syncthreads();
+        for (int x = t; x < kk; x += WG) {
+            const uint64_t kx = s_cand[x];
+            int r = 0;
+            for (int y = 0; y < kk; ++y) r += s_cand[y] > kx;
+            if (r < budget) s_sel[r] = kx;
+        }
+        __syncthreads();
+    }
+
+    // 4. softmax over the selected scores (rank 0 holds the maximum)
+    int32_t* out_i = a.idx[set] + (size_t)p * budget;
+    float* out_w = a.wt[set] + (size_t)p * budget;
+    if (t < 64) {
+        const float smax = key_score(s_sel[0]);
+        const float w = t < budget ? __expf(key_score(s_sel[t]) - smax) : 0.f;
+        const float z = wave_sum(w);
+        if (t < budget) {
+            out_i[t] = (int32_t)key_index(s_sel[t]);
+            out_w[t] = w / z;
+        }
+    }
+    (void)s_part;
+}
+
 int ceil_pow2_units(int n) {  // smallest power of two >= ceil(n/64), at least 1
     int e = 1;
     while (64 * e < n) e <<= 1;
@@ -226,9 +368,41 @@ int address_set_size(int k, int budget) {
     return nD;
 }
 
+static bool wg_address_fits(int sqrtN, int k, int budget) {
+    return sqrtN <= WG && k <= 64 && budget <= 64 && address_set_size(k, budget) <= WG;
+}
+
+// below this many problems the one-workgroup-per-problem kernel has the lower latency
+constexpr int kWgMaxProblems = 1024;
+
+hipError_t launch_sdm_address_pair(int P, int sqrtN, int dtype, const void* sw1, const void* sw2,
+                                   int k_w, int W, int32_t* iw, float* ww, const void* sr1,
+                                   const void* sr2, int k_r, int R, int32_t* ir, float* wr,
+                                   hipStream_t st) {
+    if (P <= 0) return hipSuccess;
+    if (P <= kWgMaxProblems && wg_address_fits(sqrtN, k_w, W) && wg_address_fits(sqrtN, k_r, R)) {
+        AddrPairArgs a{{sw1, sr1}, {sw2, sr2}, {iw, ir}, {ww, wr}, {k_w, k_r}, {W, R},
+                       {address_set_size(k_w, W), address_set_size(k_r, R)}, P, sqrtN};
+        if (dtype == 0) sdm_address_wg_kernel<float><<<(unsigned)(2 * P), WG, 0, st>>>(a);
+        else sdm_address_wg_kernel<bf16_t><<<(unsigned)(2 * P), WG, 0, st>>>(a);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_sdm_address(P, sqrtN, dtype, sw1, sw2, k_w, W, iw, ww, st);
+    if (e != hipSuccess) return e;
+    return launch_sdm_address(P, sqrtN, dtype, sr1, sr2, k_r, R, ir, wr, st);
+}
+
 hipError_t launch_sdm_address(int P, int sqrtN, int dtype, const void* s1, const void* s2, int k,
                               int budget, int32_t* idx, float* wt, hipStream_t st) {
     if (P <= 0) return hipSuccess;
+    if (P <= kWgMaxProblems && wg_address_fits(sqrtN, k, budget)) {  // one set: blocks 0..P-1
+        const int nD = address_set_size(k, budget);
+        AddrPairArgs g{{s1, s1}, {s2, s2}, {idx, idx}, {wt, wt}, {k, k}, {budget, budget}, {nD, nD},
+                       P, sqrtN};
+        if (dtype == 0) sdm_address_wg_kernel<float><<<(unsigned)P, WG, 0, st>>>(g);
+        else sdm_address_wg_kernel<bf16_t><<<(unsigned)P, WG, 0, st>>>(g);
+        return hipGetLastError();
+    }
     AddrArgs a{s1, s2, idx, wt, P, sqrtN, k, budget, address_set_size(k, budget)};
     const int EH = ceil_pow2_units(sqrtN);
     const int ED = ceil_pow2_units(a.nD);

@@ -137,6 +137,14 @@ def _address_cases():
     g2 = r.standard_normal((2, 100, 2, 240)).astype(np.float32)
     cases.append(("gauss_240_k32_w32", g1, g2, 32, 32))
     cases.append(("gauss_240_k8_w64", g1, g2, 8, 64))
+    # more than 1024 problems: the one-wavefront-per-problem kernel (fewer: one
+    # workgroup per problem); the same exact selection either way
+    q3 = r.integers(-3, 4, (2, 400, 2, 240)).astype(np.float32)
+    q4 = r.integers(-3, 4, (2, 400, 2, 240)).astype(np.float32)
+    cases.append(("quantized_240_k32_w32_P1600", q3, q4, 32, 32))
+    g3 = r.standard_normal((3, 300, 2, 240)).astype(np.float32)
+    g4 = r.standard_normal((3, 300, 2, 240)).astype(np.float32)
+    cases.append(("gauss_240_k32_w32_P1800", g3, g4, 32, 32))
     return cases
 
 
