@@ -242,9 +242,19 @@ __global__ __launch_bounds__(WG) void sdm_address_wg_kernel(AddrPairArgs a) {
     __syncthreads();
     if (t < n) {
         int r1 = 0, r2 = 0;
-        for (int j = 0; j < n; ++j) {
-            r1 += s_half[0][j] > x1;
-            r2 += s_half[1][j] > x2;
+        // 8 keys of each half per step (padding keys are 0, below every key)
+        for (int j = 0; j < n; j += 8) {
+            uint64_t ka[8], kb[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                ka[u] = s_half[0][j + u];
+                kb[u] = s_half[1][j + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                r1 += ka[u] > x1;
+                r2 += kb[u] > x2;
+            }
         }
         if (r1 < k) {
             s_hsc[0][r1] = key_score(x1);
@@ -270,12 +280,18 @@ __global__ __launch_bounds__(WG) void sdm_address_wg_kernel(AddrPairArgs a) {
         const int j = t - off;
         const float sum = s_hsc[0][i] + s_hsc[1][j];  // one fp32 RNE add
         dkey = make_key(sum, (uint32_t)s_hix[0][i] * (uint32_t)n + (uint32_t)s_hix[1][j]);
-        s_cand[t] = dkey;
     }
+    s_cand[t] = dkey;  // every entry is written; those past nD hold key 0 (below all keys)
     __syncthreads();
     if (t < nD) {
         int r = 0;
-        for (int u = 0; u < nD; ++u) r += s_cand[u] > dkey;
+        for (int u = 0; u < nD; u += 8) {  // entries past nD are 0 (set below)
+            uint64_t ku[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ku[e] = s_cand[u + e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r += ku[e] > dkey;
+        }
         if (r < budget) s_sel[r] = dkey;
         if (r == budget - 1) s_tau = dkey;
     }
