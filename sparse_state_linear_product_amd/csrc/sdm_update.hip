@@ -200,15 +200,17 @@ __global__ __launch_bounds__(256) void sdm_decode_update_kernel(SdmUpdateArgs a)
         }
     }
     __syncthreads();
-    // read after writing (Eq. 5)
+    // read after writing (Eq. 5); lane q < W compares write slot q with the read
+    // slot, so each read row finds the write row holding its slot in one step
+    const int myw = lane < W ? s_wslot[lane] : -2;
     float4 y = z4;
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
         const int n = w + 4 * r;
         if (n < R) {
             float4 m = mr[r];
-            for (int q = 0; q < W; ++q)
-                if (s_wslot[q] == rs[r]) m = s_new[q][lane];
+            const unsigned long long hit = __ballot(myw == rs[r]);
+            if (hit) m = s_new[__ffsll((long long)hit) - 1][lane];
             y.x = fmaf(wr[r], m.x, y.x);
             y.y = fmaf(wr[r], m.y, y.y);
             y.z = fmaf(wr[r], m.z, y.z);
