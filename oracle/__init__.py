@@ -16,6 +16,8 @@ sdm_recurrence  sparse decay / delta update / read given the addressing
 sdm_forward     addressing for writes and reads, then the recurrence
 gdn             sequential Gated DeltaNet / KDA (Linear Attention
                 Architectures slides, Eqs. 14-20)
+gdn2            sequential GDN2: key-side erase b, value-side write w
+                (same slides, Eqs. 21-24)
 sse             Sparse State Expansion per-token definition, or its masking
                 execution (Sparse State Expansion slides, Eqs. (9)-(14))
 """
@@ -65,6 +67,8 @@ def _load():
     lib.orc_gdn.restype = ctypes.c_int
     lib.orc_gdn.argtypes = [ctypes.c_int] * 6 + [_f32p, _f32p, _f32p, _f32p, _f32p,
                                                  _Nullable(np.float64), _f64p, _f64p]
+    lib.orc_gdn2.restype = ctypes.c_int
+    lib.orc_gdn2.argtypes = [ctypes.c_int] * 5 + [_f32p] * 6 + [_Nullable(np.float64), _f64p, _f64p]
     lib.orc_sse.restype = ctypes.c_int
     lib.orc_sse.argtypes = [ctypes.c_int] * 7 + [_f32p, _f32p, _f32p, _f32p, _f32p,
                                                  _Nullable(np.float32), _Nullable(np.float32),
@@ -146,6 +150,24 @@ def gdn(q, k, v, alpha, beta, S0=None, kda=False):
     rc = _load().orc_gdn(B, T, H, dk, dv, 1 if kda else 0, q, k, v, alpha, beta, s0, S, o)
     if rc != 0:
         raise ValueError("orc_gdn: invalid arguments")
+    return S, o
+
+
+def gdn2(q, k, v, alpha, b, w, S0=None):
+    """Sequential GDN2: per-channel decay alpha and erase vector b [B,T,H,dk], write
+    vector w [B,T,H,dv] (slide "GDN2 separates key-side erase and value-side write").
+
+    Returns (S float64 [B,H,dk,dv], o float64 [B,T,H,dv]).
+    """
+    q, k, v, alpha, b, w = _f32(q), _f32(k), _f32(v), _f32(alpha), _f32(b), _f32(w)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv), np.float64)
+    o = np.zeros((B, T, H, dv), np.float64)
+    s0 = None if S0 is None else np.ascontiguousarray(S0, np.float64)
+    rc = _load().orc_gdn2(B, T, H, dk, dv, q, k, v, alpha, b, w, s0, S, o)
+    if rc != 0:
+        raise ValueError("orc_gdn2: invalid arguments")
     return S, o
 
 

@@ -79,3 +79,57 @@ int orc_gdn(int B, int T, int H, int dk, int dv, int kda, const float* q, const 
         }
     return 0;
 }
+
+/*
+ * GDN2 (slide "GDN2 separates key-side erase and value-side write",
+ * Eqs. 21-24): with the KDA decay on the key channels,
+ *   W~ = W_old D_alpha,  e = b (.) kappa,  z = w (.) v,
+ *   W_new = W~ + (z - W~ e) kappa^T,
+ * b in (0,1)^{dk} steering what is erased and w in (0,1)^{dv} what is
+ * written; the outer product keeps kappa.  b = w = beta 1 is KDA.  In the
+ * transposed state S = W^T: S~ = Diag(alpha) S, r = z - S~^T e,
+ * S = S~ + kappa r^T, and the read o = S^T q after the write.
+ *   q, k, alpha, bvec : [B,T,H,dk]    v, wvec : [B,T,H,dv]
+ */
+int orc_gdn2(int B, int T, int H, int dk, int dv, const float* q, const float* k, const float* v,
+             const float* alpha, const float* bvec, const float* wvec, const double* S0, double* S,
+             double* o) {
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            size_t sb = ((size_t)b * H + h) * (size_t)dk * dv;
+            double* st = S + sb;
+            if (S0)
+                memcpy(st, S0 + sb, sizeof(double) * (size_t)dk * dv);
+            else
+                memset(st, 0, sizeof(double) * (size_t)dk * dv);
+            double* r = (double*)malloc(sizeof(double) * dv);
+            for (int t = 0; t < T; ++t) {
+                size_t bth = ((size_t)b * T + t) * H + h;
+                const float* qt = q + bth * dk;
+                const float* kt = k + bth * dk;
+                const float* vt = v + bth * dv;
+                const float* at = alpha + bth * dk;
+                const float* bt = bvec + bth * dk;
+                const float* wt = wvec + bth * dv;
+                for (int i = 0; i < dk; ++i)
+                    for (int c = 0; c < dv; ++c) st[(size_t)i * dv + c] *= (double)at[i];
+                /* r = z - S~^T e with e = b (.) kappa, z = w (.) v */
+                for (int c = 0; c < dv; ++c) r[c] = (double)wt[c] * (double)vt[c];
+                for (int i = 0; i < dk; ++i) {
+                    const double e = (double)bt[i] * (double)kt[i];
+                    for (int c = 0; c < dv; ++c) r[c] -= e * st[(size_t)i * dv + c];
+                }
+                /* S = S~ + kappa r^T */
+                for (int i = 0; i < dk; ++i)
+                    for (int c = 0; c < dv; ++c) st[(size_t)i * dv + c] += (double)kt[i] * r[c];
+                double* ot = o + bth * dv;
+                for (int c = 0; c < dv; ++c) ot[c] = 0.0;
+                for (int i = 0; i < dk; ++i)
+                    for (int c = 0; c < dv; ++c) ot[c] += (double)qt[i] * st[(size_t)i * dv + c];
+            }
+            free(r);
+        }
+    return 0;
+}

@@ -132,3 +132,98 @@ def test_sequential_equals_chunked_form(kda):
     S2, o2 = _chunked_wy(q, k, v, a, beta, S0, kda, C=16)
     np.testing.assert_allclose(S, S2, rtol=0, atol=1e-10)
     np.testing.assert_allclose(o, o2, rtol=0, atol=1e-10)
+
+
+# ---------------- GDN2: key-side erase b, value-side write w ----------------
+
+def test_gdn2_with_b_w_equal_beta_is_kda():
+    # slide "GDN2 separates key-side erase and value-side write": b = w = beta 1 recovers KDA
+    q, k, v, a, beta, S0 = _rand(21, 2, 19, 2, 8, 6, True)
+    bb = np.repeat(beta[..., None], 8, axis=-1)
+    ww = np.repeat(beta[..., None], 6, axis=-1)
+    S2, o2 = oracle.gdn2(q, k, v, a, bb, ww, S0)
+    S1, o1 = oracle.gdn(q, k, v, a, beta, S0, kda=True)
+    np.testing.assert_allclose(S2, S1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+
+
+def test_gdn2_first_token_closed_form():
+    # from an empty state the residual is the write target: S = kappa (w . v)^T, o = (kappa.q)(w . v)
+    rng = np.random.default_rng(22)
+    dk, dv = 6, 5
+    q = rng.standard_normal((1, 1, 1, dk)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 1, dk)).astype(np.float32)
+    v = rng.standard_normal((1, 1, 1, dv)).astype(np.float32)
+    a = rng.uniform(0.5, 1, (1, 1, 1, dk)).astype(np.float32)
+    b = rng.uniform(0, 1, (1, 1, 1, dk)).astype(np.float32)
+    w = rng.uniform(0, 1, (1, 1, 1, dv)).astype(np.float32)
+    S, o = oracle.gdn2(q, k, v, a, b, w)
+    z = w[0, 0, 0].astype(np.float64) * v[0, 0, 0]
+    kk = k[0, 0, 0].astype(np.float64)
+    np.testing.assert_allclose(S[0, 0], np.outer(kk, z), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(o[0, 0, 0], (kk @ q[0, 0, 0].astype(np.float64)) * z, rtol=1e-13)
+
+
+def test_gdn2_erase_and_write_roles():
+    # one stored association S0 = e_j u0^T, alpha = 1, same unit key e_j:
+    # b = 1 erases it before the write (S = e_j (w.v)^T), b = 0 keeps it (S = e_j (u0 + w.v)^T);
+    # w = 0 with b = 1 erases the key's association entirely (S^T e_j = 0)
+    dk, dv, j = 4, 3, 2
+    rng = np.random.default_rng(23)
+    u0 = rng.standard_normal(dv)
+    S0 = np.zeros((1, 1, dk, dv))
+    S0[0, 0, j] = u0
+    e = np.zeros((1, 1, 1, dk), np.float32)
+    e[..., j] = 1
+    v = rng.standard_normal((1, 1, 1, dv)).astype(np.float32)
+    w = rng.uniform(0.2, 1, (1, 1, 1, dv)).astype(np.float32)
+    one = np.ones((1, 1, 1, dk), np.float32)
+    z = (w * v)[0, 0, 0].astype(np.float64)
+    S, _ = oracle.gdn2(e, e, v, one, one, w, S0)
+    np.testing.assert_allclose(S[0, 0, j], z, atol=1e-15)
+    S, _ = oracle.gdn2(e, e, v, one, 0 * one, w, S0)
+    np.testing.assert_allclose(S[0, 0, j], u0 + z, atol=1e-15)
+    S, _ = oracle.gdn2(e, e, v, one, one, 0 * w, S0)
+    np.testing.assert_allclose(S[0, 0, j], 0.0, atol=1e-15)
+
+
+def _chunked_gdn2(q, k, v, alpha, b, w, S0, C):
+    """Chunked form written from the GDN2 recurrence: with cumulative log-decay lam,
+      (I + A) U = W.V - ((B.K) * e^lam) S0,  A[t,j] = (b_t.k_t).(e^{lam_t-lam_j} k_j), j<t
+      o_t = (q_t * e^{lam_t}) S0 + sum_{j<=t} (q_t.(e^{lam_t-lam_j} k_j)) u_j
+      S_C = e^{lam_C} S0 + sum_j (e^{lam_C-lam_j} k_j) u_j^T
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    q, k, v, b, w = (x.astype(np.float64) for x in (q, k, v, b, w))
+    la = np.log(alpha.astype(np.float64))
+    S_out = np.zeros((B, H, dk, dv))
+    o = np.zeros((B, T, H, dv))
+    for bi in range(B):
+        for h in range(H):
+            S = S0[bi, h].copy()
+            for c0 in range(0, T, C):
+                sl = slice(c0, min(T, c0 + C))
+                K, Q, V = k[bi, sl, h], q[bi, sl, h], v[bi, sl, h]
+                E, Wv = b[bi, sl, h] * K, w[bi, sl, h] * V
+                lam = np.cumsum(la[bi, sl, h], axis=0)
+                L = K.shape[0]
+                D = np.exp(lam[:, None, :] - lam[None, :, :])
+                A = np.tril(np.einsum("ti,tji,ji->tj", E, D, K), -1)
+                P = np.einsum("ti,tji,ji->tj", Q, D, K)
+                U = np.linalg.solve(np.eye(L) + A, Wv - (E * np.exp(lam)) @ S)
+                o[bi, sl, h] = (Q * np.exp(lam)) @ S + np.tril(P) @ U
+                S = np.exp(lam[-1])[:, None] * S + (K * np.exp(lam[-1] - lam)).T @ U
+            S_out[bi, h] = S
+    return S_out, o
+
+
+def test_gdn2_sequential_equals_chunked_form():
+    q, k, v, a, _, S0 = _rand(24, 2, 41, 2, 8, 6, True)
+    rng = np.random.default_rng(25)
+    b = rng.uniform(0, 1, (2, 41, 2, 8)).astype(np.float32)
+    w = rng.uniform(0, 1, (2, 41, 2, 6)).astype(np.float32)
+    S, o = oracle.gdn2(q, k, v, a, b, w, S0)
+    S2, o2 = _chunked_gdn2(q, k, v, a, b, w, S0, C=16)
+    np.testing.assert_allclose(S, S2, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-10)
