@@ -157,6 +157,23 @@ def bench_rows(args, torch, sslp, wl):
                               hbm_frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               flops_per_call=fl, bytes_per_call=by)
         del x, o, S
+    # GDN2: KDA decay, erase vector b [d_k] and write vector w [d_v] per token in place of beta
+    cfg = wl.GDN2
+    x = {k: v.to(dev) for k, v in wl.gdn2_inputs(cfg).items()}
+    o = torch.empty_like(x["v"])
+    S = torch.empty((cfg.B, cfg.H, cfg.d_k, cfg.d_v), dtype=torch.float32, device=dev)
+    ms = time_call(torch, lambda: sslp.gdn2_chunk_forward(x["q"], x["k"], x["v"], x["alpha"],
+                                                          x["erase"], x["write"], S_out=S, o=o),
+                   args.steps)
+    fl = gdn_flops(cfg.B, cfg.T, cfg.H, cfg.d_k, cfg.d_v)
+    by = gdn_bytes(cfg.B, cfg.T, cfg.H, cfg.d_k, cfg.d_v, True) + 4 * (cfg.d_k + cfg.d_v - 1) * cfg.B * cfg.T * cfg.H
+    rows[cfg.name] = dict(ms=round(ms, 4), tokens_per_s=round(cfg.B * cfg.T / (ms * 1e-3), 1),
+                          tflops=round(fl / (ms * 1e-3) / 1e12, 2),
+                          mfma_frac=round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                          gbs=round(by / (ms * 1e-3) / 1e9, 1),
+                          hbm_frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          flops_per_call=fl, bytes_per_call=by)
+    del x, o, S
     # SSE: B=4, T=4096, H=16, 8 routed + 1 shared partition, top-2, c=d=128
     cfg = wl.SSE
     x = {k: v.to(dev) for k, v in wl.sse_inputs(cfg).items()}

@@ -202,6 +202,23 @@ int gdn_chunk_forward(const sslp_gdn_shape* shape, int dtype, int decay_mode, co
                       const float* S0, float* S_out, void* o, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/*
+ * gdn2_chunk_forward -- GDN2 (slides "Linear Attention Architectures", "GDN2
+ * separates key-side erase and value-side write", Eqs. 21-24), chunked like
+ * gdn_chunk_forward with the per-channel (KDA) decay.  In the transposed
+ * state S = W^T [d_k, d_v], per token:
+ *   S~ = Diag(alpha_t) S;  r = (w_t (.) v_t) - S~^T (b_t (.) k_t);
+ *   S = S~ + k_t r^T;      o_t = S^T q_t.
+ * b = w = beta 1 is KDA.
+ *   q, k [B,T,H,d_k] dtype; v [B,T,H,d_v] dtype;
+ *   alpha, erase (b) [B,T,H,d_k] fp32; write (w) [B,T,H,d_v] fp32;
+ *   S0, S_out, o, workspace (gdn_workspace_size), errors: as gdn_chunk_forward.
+ */
+int gdn2_chunk_forward(const sslp_gdn_shape* shape, int dtype, const void* q, const void* k,
+                       const void* v, const float* alpha, const float* erase, const float* write,
+                       const float* S0, float* S_out, void* o, void* workspace, size_t ws_bytes,
+                       void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Sparse State Expansion                                                    */
 /* ------------------------------------------------------------------------ */

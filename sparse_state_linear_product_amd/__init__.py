@@ -9,7 +9,7 @@ allocated with torch when the caller does not pass one.
 
 Functions (see include/sslp.h for the exact semantics):
   sdm_forward, sdm_decode_step, sdm_address, sdm_sparse_update   Sparse Delta Memory
-  gdn_chunk_forward                                              Gated DeltaNet / KDA
+  gdn_chunk_forward, gdn2_chunk_forward                          Gated DeltaNet / KDA / GDN2
   sse_forward, sse_decode_step                                   Sparse State Expansion
 """
 import ctypes
@@ -21,8 +21,9 @@ from ._lib import (DECAY_CHANNEL, DECAY_SCALAR, RESIDUAL_PER_SLOT, RESIDUAL_SHAR
                    SdmShape, SseShape, SslpError, check, lib)
 
 __all__ = ["sdm_forward", "sdm_decode_step", "sdm_address", "sdm_sparse_update",
-           "gdn_chunk_forward", "sse_forward", "sse_decode_step", "SslpError", "RESIDUAL_SHARED",
-           "RESIDUAL_PER_SLOT", "DECAY_SCALAR", "DECAY_CHANNEL", "version"]
+           "gdn_chunk_forward", "gdn2_chunk_forward", "sse_forward", "sse_decode_step",
+           "SslpError", "RESIDUAL_SHARED", "RESIDUAL_PER_SLOT", "DECAY_SCALAR", "DECAY_CHANNEL",
+           "version"]
 
 
 def version():
@@ -217,6 +218,35 @@ def gdn_chunk_forward(q, k, v, alpha, beta, S0=None, S_out=None, o=None, decay_m
                                  _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(S_out),
                                  _ptr(o), _ptr(ws), nbytes, _stream(stream))
     check("gdn_chunk_forward", rc)
+    return o, S_out
+
+
+def gdn2_chunk_forward(q, k, v, alpha, erase, write, S0=None, S_out=None, o=None, chunk=64,
+                       workspace=None, stream=None):
+    """GDN2: q, k [B,T,H,d_k]; v [B,T,H,d_v]; alpha and erase (b) [B,T,H,d_k] fp32;
+    write (w) [B,T,H,d_v] fp32; S0 [B,H,d_k,d_v] fp32 or None.  Returns (o, S_out)."""
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dt = q.dtype
+    _need(k, dt, (B, T, H, d_k), "k")
+    _need(v, dt, (B, T, H, d_v), "v")
+    _need(alpha, torch.float32, (B, T, H, d_k), "alpha")
+    _need(erase, torch.float32, (B, T, H, d_k), "erase")
+    _need(write, torch.float32, (B, T, H, d_v), "write")
+    if S0 is not None:
+        _need(S0, torch.float32, (B, H, d_k, d_v), "S0")
+    if S_out is None:
+        S_out = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device)
+    _need(S_out, torch.float32, (B, H, d_k, d_v), "S_out")
+    if o is None:
+        o = torch.empty((B, T, H, d_v), dtype=dt, device=q.device)
+    _need(o, dt, (B, T, H, d_v), "o")
+    shape = GdnShape(B, T, H, d_k, d_v, chunk)
+    ws, nbytes = _workspace(lib().gdn_workspace_size(ctypes.byref(shape)), workspace, q.device)
+    rc = lib().gdn2_chunk_forward(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(alpha), _ptr(erase), _ptr(write), _ptr(S0), _ptr(S_out),
+                                  _ptr(o), _ptr(ws), nbytes, _stream(stream))
+    check("gdn2_chunk_forward", rc)
     return o, S_out
 
 

@@ -46,6 +46,7 @@ SIGNATURES = {
     "sdm_sparse_update": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 10 + [_sz, _vp], _i),
     "gdn_workspace_size": ([ctypes.POINTER(GdnShape)], _sz),
     "gdn_chunk_forward": ([ctypes.POINTER(GdnShape), _i, _i] + [_vp] * 9 + [_sz, _vp], _i),
+    "gdn2_chunk_forward": ([ctypes.POINTER(GdnShape), _i] + [_vp] * 10 + [_sz, _vp], _i),
     "sse_workspace_size": ([ctypes.POINTER(SseShape)], _sz),
     "sse_forward": ([ctypes.POINTER(SseShape), _i] + [_vp] * 12 + [_sz, _vp], _i),
     "sse_decode_step": ([ctypes.POINTER(SseShape), _i] + [_vp] * 11 + [_vp], _i),

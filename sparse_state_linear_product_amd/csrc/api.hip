@@ -335,6 +335,43 @@ int gdn_chunk_forward(const sslp_gdn_shape* s, int dtype, int decay_mode, const 
                       "gdn_chunk_forward launch");
 }
 
+int gdn2_chunk_forward(const sslp_gdn_shape* s, int dtype, const void* q, const void* k,
+                       const void* v, const float* alpha, const float* erase, const float* write,
+                       const float* S0, float* S_out, void* o, void* workspace, size_t ws_bytes,
+                       void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_gdn_shape(s)) return rc;
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE_ALIGNED(q);
+    REQUIRE_ALIGNED(k);
+    REQUIRE_ALIGNED(v);
+    REQUIRE_ALIGNED(alpha);
+    REQUIRE_ALIGNED(erase);
+    REQUIRE_ALIGNED(write);
+    REQUIRE_ALIGNED(o);
+    REQUIRE_ALIGNED(S0);
+    REQUIRE(dtype == SSLP_BF16, SSLP_ERR_UNSUPPORTED,
+            "gdn2_chunk_forward supports bf16 q/k/v only (got dtype %d)", dtype);
+    REQUIRE_PTR(S_out);
+    if (s->T > 0) {
+        REQUIRE_PTR(q);
+        REQUIRE_PTR(k);
+        REQUIRE_PTR(v);
+        REQUIRE_PTR(alpha);
+        REQUIRE_PTR(erase);
+        REQUIRE_PTR(write);
+        REQUIRE_PTR(o);
+    }
+    const size_t need = gdn_workspace_size(s);
+    REQUIRE(ws_bytes >= need && (need == 0 || workspace != nullptr), SSLP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    REQUIRE_ALIGNED(workspace);
+    return hip_status(sslp::launch_gdn_chunk(s->B, s->T, s->H, s->d_v, dtype, 2, q, k, v, alpha,
+                                             nullptr, S0, S_out, o, workspace, (hipStream_t)stream,
+                                             erase, write),
+                      "gdn2_chunk_forward launch");
+}
+
 static int check_sse_shape(const sslp_sse_shape* s) {
     REQUIRE(s != nullptr, SSLP_ERR_INVALID_ARG, "shape must not be NULL");
     REQUIRE(s->B >= 1 && s->H >= 1 && s->T >= 0, SSLP_ERR_INVALID_ARG, "bad B/T/H");

@@ -134,13 +134,22 @@ struct GdnArgs {
     float* S_out;
     void* o;
     uint8_t* rec;  // [B, H, nch] records of REC_BYTES
+    const float* bvec;  // GDN2: erase vector [B,T,H,DK]
+    const float* wvec;  // GDN2: write vector [B,T,H,dv]
 };
 
 // ---------------------------------------------------------------------------
 // prep kernel: one workgroup per (b, h, chunk)
 // ---------------------------------------------------------------------------
-template <bool KDA>
+// MODE 0: GDN (scalar decay), 1: KDA (per-channel decay), 2: GDN2 (KDA decay,
+// erase vector b on the key side of the residual, write vector w on the value
+// side, slide "GDN2 separates key-side erase and value-side write"): the same
+// chunked form with beta = 1, the erase-side keys b (.) k in A and Wn, and
+// X = w (.) V in U0.
+template <int MODE>
 __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
+    constexpr bool KDA = MODE != 0;
+    constexpr bool G2 = MODE == 2;
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nch = a.nch;
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
         {  // every wave: the gates of token row = lane
             const int t = t0 + lane;
             const size_t bth = ((size_t)b * T + t) * H + h;
-            pbeta = t < T ? a.beta[bth] : 0.f;
+            pbeta = t < T ? (G2 ? 1.f : a.beta[bth]) : 0.f;
             if (!KDA) palpha = t < T ? a.alpha[bth] : 1.f;
         }
     };
@@ -196,9 +205,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
     for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int c = task % nch, bh = task / nch;
     const int b = bh / H, h = bh - (bh / H) * H;
-    (void)c;
-    (void)b;
-    (void)h;
+
     uint8_t* rec = a.rec + (size_t)task * REC_BYTES;
     block_sync_lds();  // the previous chunk's use of the shared arrays is over
     // X = diag(beta) V, stored transposed (bf16); K, Q as they are
@@ -208,8 +215,23 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
         *reinterpret_cast<uint4*>(&sm.k[row][col]) = pk[i];
         *reinterpret_cast<uint4*>(&sm.q[row][col]) = pq[i];
         const uint16_t* ve = reinterpret_cast<const uint16_t*>(&pv[i]);
+        float sc[8];
+        if constexpr (G2) {  // X = w (.) V
+            const int t = c * C + row;
+            float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), w1 = w0;
+            if (t < T) {
+                const float* wr = a.wvec + (((size_t)b * T + t) * H + h) * dv + col;
+                w0 = *reinterpret_cast<const float4*>(wr);
+                w1 = *reinterpret_cast<const float4*>(wr + 4);
+            }
+            sc[0] = w0.x, sc[1] = w0.y, sc[2] = w0.z, sc[3] = w0.w;
+            sc[4] = w1.x, sc[5] = w1.y, sc[6] = w1.z, sc[7] = w1.w;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm.xt[col + e][row] = f32_to_bf16(pbeta * bf2f(ve[e])).bits;
+            for (int e = 0; e < 8; ++e) sc[e] = pbeta;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.xt[col + e][row] = f32_to_bf16(sc[e] * bf2f(ve[e])).bits;
     }
     if constexpr (KDA) {
 #pragma unroll
@@ -262,7 +284,12 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                         em *= __frcp_rn(al);
                     }
                     const float kv = bf2f(sm.k[t][i]), qv = bf2f(sm.q[t][i]);
-                    sm.k[t][i] = f32_to_bf16(kv * ep).bits;
+                    float ke = kv;  // the key of A's rows and of Wn: b (.) k for GDN2
+                    if constexpr (G2) {
+                        const int tt = c * C + t;
+                        ke *= tt < T ? a.bvec[(((size_t)b * T + tt) * H + h) * DK + i] : 0.f;
+                    }
+                    sm.k[t][i] = f32_to_bf16(ke * ep).bits;
                     sm.km[t][i] = f32_to_bf16(kv * em).bits;
                     sm.q[t][i] = f32_to_bf16(qv * ep).bits;
                 }
@@ -790,15 +817,18 @@ size_t gdn_record_bytes(int B, int T, int H) {
 
 hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, const void* q,
                             const void* k, const void* v, const float* alpha, const float* beta,
-                            const float* S0, float* S_out, void* o, void* rec, hipStream_t st) {
+                            const float* S0, float* S_out, void* o, void* rec, hipStream_t st,
+                            const float* bvec, const float* wvec) {
     if (dtype != 1 || dv != DK) return hipErrorInvalidValue;  // bf16, d_k = d_v = 128 (checked by the C ABI)
     const int nch = (T + C - 1) / C;
-    GdnArgs a{B, T, H, dv, nch, q, k, v, alpha, beta, S0, S_out, o, static_cast<uint8_t*>(rec)};
+    GdnArgs a{B, T, H, dv, nch, q, k, v, alpha, beta, S0, S_out, o, static_cast<uint8_t*>(rec),
+              bvec, wvec};
     if (nch > 0) {
         const int ntask = B * H * nch;
         const int grid = ntask < prep_grid() ? ntask : prep_grid();
-        if (kda) gdn_prep_kernel<true><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
-        else gdn_prep_kernel<false><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
+        if (kda == 2) gdn_prep_kernel<2><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
+        else if (kda == 1) gdn_prep_kernel<1><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
+        else gdn_prep_kernel<0><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

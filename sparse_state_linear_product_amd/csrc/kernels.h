@@ -46,9 +46,12 @@ hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* plan, hipStre
 // per-chunk records of the state-independent part (workspace), and the
 // launcher (prep kernel over all chunks + state kernel over the chunk sequence)
 size_t gdn_record_bytes(int B, int T, int H);
+// kda: 0 GDN (alpha [B,T,H]), 1 KDA (alpha [B,T,H,dk]), 2 GDN2 (KDA decay, erase
+// vector bvec [B,T,H,dk] and write vector wvec [B,T,H,dv] in place of beta)
 hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, const void* q,
                             const void* k, const void* v, const float* alpha, const float* beta,
-                            const float* S0, float* S_out, void* o, void* rec, hipStream_t st);
+                            const float* S0, float* S_out, void* o, void* rec, hipStream_t st,
+                            const float* bvec = nullptr, const float* wvec = nullptr);
 
 // ---- Sparse State Expansion ----
 hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,

@@ -77,6 +77,7 @@ class SseConfig:
 SDM_TINY = SdmConfig("sdm_tiny_fp32", 1, 256, 1, 8, 16, 4, 4, 4, 4, F32, 1001)
 GDN = GdnConfig("gdn_chunk_B4_T4096_H16_d128", 4, 4096, 16, 128, 128, BF16, False, 1002)
 KDA = GdnConfig("kda_chunk_B4_T4096_H16_d128", 4, 4096, 16, 128, 128, BF16, True, 1012)
+GDN2 = GdnConfig("gdn2_chunk_B4_T4096_H16_d128", 4, 4096, 16, 128, 128, BF16, True, 1014)
 SSE = SseConfig("sse_B4_T4096_H16_N8k2_c128", 4, 4096, 16, 8, 2, 128, 128, BF16, 1003)
 SDM_14B = SdmConfig("sdm_prefill_1p4b_B1_T8192_H2_N57600_dv960", 1, 8192, 2, 240, 960, 32, 32, 32,
                     32, BF16, 1004)
@@ -130,6 +131,18 @@ def gdn_inputs(cfg: GdnConfig, T=None, seed=None, B=None, H=None):
     ashape = (B, T, H, cfg.d_k) if cfg.kda else (B, T, H)
     alpha = _uniform(ashape, 0.9, 1.0, g)
     return dict(q=q, k=k, v=v, alpha=alpha, beta=beta)
+
+
+def gdn2_inputs(cfg: GdnConfig, T=None, seed=None, B=None, H=None):
+    """GDN2: the KDA draws (q, k, v, beta, alpha per channel), then the erase
+    vector b = sigmoid(N(0,1)) per key channel and the write vector
+    w = sigmoid(N(0,1)) per value column.  Shapes [B,T,H,*]; beta is unused."""
+    x = gdn_inputs(cfg, T=T, seed=seed, B=B, H=H)
+    T, B, H = x["q"].shape[1], x["q"].shape[0], x["q"].shape[2]
+    g = _gen((cfg.seed if seed is None else seed) + 7919)
+    x["erase"] = torch.sigmoid(torch.randn((B, T, H, cfg.d_k), generator=g, dtype=F32))
+    x["write"] = torch.sigmoid(torch.randn((B, T, H, cfg.d_v), generator=g, dtype=F32))
+    return x
 
 
 def sse_inputs(cfg: SseConfig, T=None, seed=None, B=None, H=None):

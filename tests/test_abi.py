@@ -114,6 +114,13 @@ def test_gdn_and_sse_shape_errors():
     g = _lib.GdnShape(1, 8, 1, 128, 128, 64)
     assert lib.gdn_chunk_forward(ctypes.byref(g), 1, 5, *([FAKE] * 9), 0, None) == \
         _lib.SSLP_ERR_INVALID_ARG
+    g = _lib.GdnShape(1, 8, 1, 128, 128, 64)
+    assert lib.gdn2_chunk_forward(ctypes.byref(g), 0, *([FAKE] * 10), 0, None) == \
+        _lib.SSLP_ERR_UNSUPPORTED
+    assert lib.gdn2_chunk_forward(ctypes.byref(g), 1, *([FAKE] * 9), None, 0, None) == \
+        _lib.SSLP_ERR_WORKSPACE
+    assert lib.gdn2_chunk_forward(ctypes.byref(g), 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, 1 << 30, None) == _lib.SSLP_ERR_INVALID_ARG
     s = _lib.SseShape(1, 8, 1, 8, 9, 128, 128, 64)
     assert lib.sse_forward(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == _lib.SSLP_ERR_INVALID_ARG
     s = _lib.SseShape(1, 8, 1, 8, 2, 64, 128, 64)

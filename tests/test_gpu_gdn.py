@@ -87,3 +87,64 @@ def test_gdn_full_config(kda):
     announce(f"{cfg.name} full size")
     x = wl.gdn_inputs(cfg)
     _check(x, kda, tag=cfg.name)
+
+
+# ---------------- GDN2: erase vector b, write vector w ----------------
+
+def _run2(x, S0=None):
+    import sparse_state_linear_product_amd as sslp
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    o, S = sslp.gdn2_chunk_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["erase"],
+                                   xd["write"], S0=None if S0 is None else S0.to(DEV).contiguous())
+    torch.cuda.synchronize()
+    return o.cpu(), S.cpu()
+
+
+def _ref2(x, S0=None):
+    n = {k: wl.to_numpy_f32(v) for k, v in x.items()}
+    return oracle.gdn2(n["q"], n["k"], n["v"], n["alpha"], n["erase"], n["write"],
+                       S0=None if S0 is None else S0.double().numpy())
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 100, 300])
+def test_gdn2_small(T):
+    announce(f"gdn2_chunk_forward B=2 H=3 T={T}")
+    x = wl.gdn2_inputs(wl.GDN2, T=T, B=2, H=3, seed=500 + T)
+    o, S = _run2(x)
+    Sr, orf = _ref2(x)
+    e_o, e_S = maxrel(o.double().numpy(), orf), maxrel(S.double().numpy(), Sr)
+    print(f"  gdn2 T={T}: o {e_o:.2e} S {e_S:.2e}", flush=True)
+    assert np.isfinite(o.float().numpy()).all() and np.isfinite(S.numpy()).all()
+    assert e_o <= TOL_BF16 and e_S <= TOL_BF16
+
+
+def test_gdn2_with_initial_state_and_kda_reduction():
+    # with S0; and b = w = beta on every channel, which the slide states is KDA
+    announce("gdn2_chunk_forward with S0; b = w = beta 1 vs the KDA oracle")
+    x = wl.gdn2_inputs(wl.GDN2, T=150, B=1, H=2, seed=41)
+    S0 = torch.randn((1, 2, 128, 128), generator=torch.Generator().manual_seed(42)) * 0.5
+    o, S = _run2(x, S0)
+    Sr, orf = _ref2(x, S0)
+    assert maxrel(o.double().numpy(), orf) <= TOL_BF16
+    assert maxrel(S.double().numpy(), Sr) <= TOL_BF16
+    x["erase"] = x["beta"][..., None].expand(-1, -1, -1, 128).contiguous()
+    x["write"] = x["beta"][..., None].expand(-1, -1, -1, 128).contiguous()
+    o, S = _run2(x, S0)
+    n = {k: wl.to_numpy_f32(v) for k, v in x.items()}
+    Sk, ok = oracle.gdn(n["q"], n["k"], n["v"], n["alpha"], n["beta"], S0=S0.double().numpy(),
+                        kda=True)
+    e_o, e_S = maxrel(o.double().numpy(), ok), maxrel(S.double().numpy(), Sk)
+    print(f"  gdn2 as KDA: o {e_o:.2e} S {e_S:.2e}", flush=True)
+    assert e_o <= TOL_BF16 and e_S <= TOL_BF16
+
+
+def test_gdn2_empty_sequence_copies_state():
+    import sparse_state_linear_product_amd as sslp
+    announce("gdn2_chunk_forward T=0")
+    x = wl.gdn2_inputs(wl.GDN2, T=0, B=1, H=2, seed=43)
+    S0 = torch.randn((1, 2, 128, 128), generator=torch.Generator().manual_seed(44))
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    o, S = sslp.gdn2_chunk_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["erase"], xd["write"],
+                                   S0=S0.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(S.cpu(), S0)
