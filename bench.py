@@ -187,6 +187,14 @@ def bench_rows(args, torch, sslp, wl):
                           gbs=round(by / (ms * 1e-3) / 1e9, 1),
                           hbm_frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           bytes_per_call=by)
+    # the same workload as the masking execution (every partition steps over every token)
+    ms = time_call(torch, lambda: sslp.sse_forward(x["logits"], x["q"], x["k"], x["v"], x["lam"],
+                                                   S, cfg.topk, o=o, masking=True), args.steps)
+    rows[cfg.name + "_masking"] = dict(ms=round(ms, 4),
+                                       tokens_per_s=round(cfg.B * cfg.T / (ms * 1e-3), 1),
+                                       gbs=round(by / (ms * 1e-3) / 1e9, 1),
+                                       hbm_frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                       bytes_per_call=by)
     del x, S, o
     # SSE decode: 64 independent sequences, N=8 routed + 1 shared states of 128x128 per head;
     # a step reads and writes the 2 selected and the shared state of every (sequence, head)

@@ -263,6 +263,21 @@ int sse_forward(const sslp_sse_shape* shape, int dtype, const float* gate_logits
                 size_t ws_bytes, void* stream);
 
 /*
+ * sse_forward_masking -- the same operation as sse_forward, run as the masking
+ * execution that the SSE slides contrast with varlen grouping ("Varlen groups
+ * tokens while preserving causal order"): every routed partition steps over
+ * every token of the sequence; a token that does not select partition i
+ * writes nothing to S^i, reads nothing from it, and leaves its decay at 1, so
+ * S^i still decays only on its visits.  In exact arithmetic the results equal
+ * sse_forward's; the work grows by N / topk on the routed partitions.
+ * Arguments, layouts, workspace and errors as sse_forward.
+ */
+int sse_forward_masking(const sslp_sse_shape* shape, int dtype, const float* gate_logits,
+                        const void* q, const void* k, const void* v, const float* lambda,
+                        const void* q_sh, const void* k_sh, float* S, void* o, int32_t* sel,
+                        float* e_sel, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * sse_decode_step -- one token of every sequence (shape->T must be 1): the same
  * operation as sse_forward with T = 1, reading and writing only the topk
  * selected states and the shared one (the SSE slides' note on decoding under

@@ -10,7 +10,7 @@ allocated with torch when the caller does not pass one.
 Functions (see include/sslp.h for the exact semantics):
   sdm_forward, sdm_decode_step, sdm_address, sdm_sparse_update   Sparse Delta Memory
   gdn_chunk_forward, gdn2_chunk_forward                          Gated DeltaNet / KDA / GDN2
-  sse_forward, sse_decode_step                                   Sparse State Expansion
+  sse_forward (masking=True: sse_forward_masking), sse_decode_step  Sparse State Expansion
 """
 import ctypes
 
@@ -254,9 +254,11 @@ def gdn2_chunk_forward(q, k, v, alpha, erase, write, S0=None, S_out=None, o=None
 # Sparse State Expansion
 # ---------------------------------------------------------------------------
 def sse_forward(gate_logits, q, k, v, lam, S, topk, q_sh=None, k_sh=None, o=None, sel=None,
-                e_sel=None, chunk=64, workspace=None, stream=None):
+                e_sel=None, chunk=64, workspace=None, stream=None, masking=False):
     """gate_logits [B,T,H,N] fp32; q, k [B,T,H,c]; v [B,T,H,d]; lam [B,T,H,c] fp32;
-    S [B,H,N+1,c,d] fp32 updated in place.  Returns o [B,T,H,d]."""
+    S [B,H,N+1,c,d] fp32 updated in place.  Returns o [B,T,H,d].
+    masking=True calls sse_forward_masking (every partition steps over every
+    token, unselected ones masked) instead of the grouped visits."""
     B, T, H, N = gate_logits.shape
     c, d = q.shape[-1], v.shape[-1]
     dt = q.dtype
@@ -278,10 +280,11 @@ def sse_forward(gate_logits, q, k, v, lam, S, topk, q_sh=None, k_sh=None, o=None
         _need(e_sel, torch.float32, (B, T, H, topk), "e_sel")
     shape = SseShape(B, T, H, N, topk, c, d, chunk)
     ws, nbytes = _workspace(lib().sse_workspace_size(ctypes.byref(shape)), workspace, q.device)
-    rc = lib().sse_forward(ctypes.byref(shape), _dtype_code(q), _ptr(gate_logits), _ptr(q),
-                           _ptr(k), _ptr(v), _ptr(lam), _ptr(q_sh), _ptr(k_sh), _ptr(S), _ptr(o),
-                           _ptr(sel), _ptr(e_sel), _ptr(ws), nbytes, _stream(stream))
-    check("sse_forward", rc)
+    name = "sse_forward_masking" if masking else "sse_forward"
+    rc = getattr(lib(), name)(ctypes.byref(shape), _dtype_code(q), _ptr(gate_logits), _ptr(q),
+                              _ptr(k), _ptr(v), _ptr(lam), _ptr(q_sh), _ptr(k_sh), _ptr(S),
+                              _ptr(o), _ptr(sel), _ptr(e_sel), _ptr(ws), nbytes, _stream(stream))
+    check(name, rc)
     return o
 
 

@@ -49,6 +49,7 @@ SIGNATURES = {
     "gdn2_chunk_forward": ([ctypes.POINTER(GdnShape), _i] + [_vp] * 10 + [_sz, _vp], _i),
     "sse_workspace_size": ([ctypes.POINTER(SseShape)], _sz),
     "sse_forward": ([ctypes.POINTER(SseShape), _i] + [_vp] * 12 + [_sz, _vp], _i),
+    "sse_forward_masking": ([ctypes.POINTER(SseShape), _i] + [_vp] * 12 + [_sz, _vp], _i),
     "sse_decode_step": ([ctypes.POINTER(SseShape), _i] + [_vp] * 11 + [_vp], _i),
     "sslp_last_error": ([], ctypes.c_char_p),
     "sslp_version": ([], _i),

@@ -395,15 +395,15 @@ size_t sse_workspace_size(const sslp_sse_shape* s) {
     return 2 * sse_route_bytes(s);
 }
 
-int sse_forward(const sslp_sse_shape* s, int dtype, const float* gate_logits, const void* q,
-                const void* k, const void* v, const float* lambda, const void* q_sh,
-                const void* k_sh, float* S, void* o, int32_t* sel, float* e_sel, void* workspace,
-                size_t ws_bytes, void* stream) {
+static int sse_run(const char* name, int masking, const sslp_sse_shape* s, int dtype,
+                   const float* gate_logits, const void* q, const void* k, const void* v,
+                   const float* lambda, const void* q_sh, const void* k_sh, float* S, void* o,
+                   int32_t* sel, float* e_sel, void* workspace, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     if (int rc = check_sse_shape(s)) return rc;
     if (int rc = check_dtype(dtype)) return rc;
     REQUIRE(dtype == SSLP_BF16, SSLP_ERR_UNSUPPORTED,
-            "sse_forward supports bf16 q/k/v only (got dtype %d)", dtype);
+            "%s supports bf16 q/k/v only (got dtype %d)", name, dtype);
     REQUIRE_PTR(S);
     REQUIRE_ALIGNED(q_sh);
     REQUIRE_ALIGNED(k_sh);
@@ -426,8 +426,24 @@ int sse_forward(const sslp_sse_shape* s, int dtype, const float* gate_logits, co
     }
     return hip_status(sslp::launch_sse(s->B, s->T, s->H, s->N, s->topk, s->d, dtype, gate_logits,
                                        q, k, v, lambda, q_sh, k_sh, S, o, sel, e_sel,
-                                       (hipStream_t)stream),
-                      "sse_forward launch");
+                                       (hipStream_t)stream, masking),
+                      name);
+}
+
+int sse_forward(const sslp_sse_shape* s, int dtype, const float* gate_logits, const void* q,
+                const void* k, const void* v, const float* lambda, const void* q_sh,
+                const void* k_sh, float* S, void* o, int32_t* sel, float* e_sel, void* workspace,
+                size_t ws_bytes, void* stream) {
+    return sse_run("sse_forward", 0, s, dtype, gate_logits, q, k, v, lambda, q_sh, k_sh, S, o, sel,
+                   e_sel, workspace, ws_bytes, stream);
+}
+
+int sse_forward_masking(const sslp_sse_shape* s, int dtype, const float* gate_logits,
+                        const void* q, const void* k, const void* v, const float* lambda,
+                        const void* q_sh, const void* k_sh, float* S, void* o, int32_t* sel,
+                        float* e_sel, void* workspace, size_t ws_bytes, void* stream) {
+    return sse_run("sse_forward_masking", 1, s, dtype, gate_logits, q, k, v, lambda, q_sh, k_sh, S,
+                   o, sel, e_sel, workspace, ws_bytes, stream);
 }
 
 int sse_decode_step(const sslp_sse_shape* s, int dtype, const float* gate_logits, const void* q,

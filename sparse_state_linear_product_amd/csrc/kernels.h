@@ -54,10 +54,12 @@ hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, con
                             const float* bvec = nullptr, const float* wvec = nullptr);
 
 // ---- Sparse State Expansion ----
+// masking = 1: the masked execution (every routed partition over every token,
+// unselected tokens with gate 0 and decay 1) instead of the grouped visits
 hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
                       const float* logits, const void* q, const void* k, const void* v,
                       const float* lam, const void* q_sh, const void* k_sh, float* S, void* o,
-                      int32_t* sel, float* e_sel, hipStream_t st);
+                      int32_t* sel, float* e_sel, hipStream_t st, int masking = 0);
 // one decode step (one token per sequence), touching only the selected states
 hipError_t launch_sse_decode(int B, int H, int N, int topk, int dv, const float* logits,
                              const void* q, const void* k, const void* v, const float* lam,

@@ -92,6 +92,7 @@ struct SseArgs {
     void* o;
     int32_t* sel;
     float* e_sel;
+    int masking;  // 1: every routed partition runs over every token (masked execution)
 };
 
 // One block of up to 16 visits of one partition on one wave.
@@ -103,7 +104,7 @@ template <typename io_t, int NY>
 SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs& a,
                            const io_t* qg, const io_t* kg, const io_t* vg, int b, int h, int t0,
                            int col0, const int16_t* vtok, const float* vgate, int tbase, int L,
-                           int lane, f32x4_t (&ot)[NY]) {
+                           int lane, f32x4_t (&ot)[NY], const int8_t* vmask = nullptr) {
     // visit p: token tok(p) of the chunk with gate gate(p) (LDS lists, or
     // consecutive tokens from tbase with gate 1)
     auto tok = [&](int p) { return vtok ? (int)vtok[p] : tbase + p; };
@@ -142,7 +143,10 @@ SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs&
                 const int p = 8 * half + u;
                 float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
                 if (p < L) {
-                    const float l0 = lam[u].x, l1 = lam[u].y;
+                    // masked execution: a token that does not select the partition leaves
+                    // its state undecayed (and writes nothing: its gate is 0)
+                    const bool frozen = vmask != nullptr && vmask[p] < 0;
+                    const float l0 = frozen ? 1.f : lam[u].x, l1 = frozen ? 1.f : lam[u].y;
                     q0 = __uint_as_float(qw[u] << 16);
                     q1 = __uint_as_float(qw[u] & 0xFFFF0000u);
                     k0 = __uint_as_float(kw[u] << 16);
@@ -368,6 +372,16 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
                             rk = r;
                             gv = gsel[r];
                         }
+                    if (a.masking) {
+                        // every token, in order; rank -1 marks the ones that do not select i
+                        if (t < Tc) {
+                            sm.vis[i][t] = (int16_t)t;
+                            sm.vrank[i][t] = (int8_t)(hit ? rk : -1);
+                            sm.vgate[i][t] = hit ? gv : 0.f;
+                        }
+                        if (lane == 0) sm.cnt[i] = Tc;
+                        continue;
+                    }
                     const unsigned long long m = __ballot(hit);
                     if (hit) {
                         const int pos = __popcll(m & ((1ull << lane) - 1ull));
@@ -400,10 +414,11 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
                         const int L = (cnt - p0) < 16 ? (cnt - p0) : 16;
                         f32x4_t ot[NY];
                         gla_block<io_t, NY>(St, ws, a, qg, kg, vg, b, h, t0, n0, &sm.vis[part][p0],
-                                            &sm.vgate[part][p0], 0, L, lane, ot);
-                        if (l16 < L) {
+                                            &sm.vgate[part][p0], 0, L, lane, ot,
+                                            a.masking ? &sm.vrank[part][p0] : nullptr);
+                        const int rk = l16 < L ? sm.vrank[part][p0 + l16] : -1;
+                        if (rk >= 0) {
                             const int tp = sm.vis[part][p0 + l16];
-                            const int rk = sm.vrank[part][p0 + l16];
                             const float e = sm.vgate[part][p0 + l16];
 #pragma unroll
                             for (int y = 0; y < NY; ++y)
@@ -453,9 +468,9 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
 hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
                       const float* logits, const void* q, const void* k, const void* v,
                       const float* lam, const void* q_sh, const void* k_sh, float* S, void* o,
-                      int32_t* sel, float* e_sel, hipStream_t st) {
+                      int32_t* sel, float* e_sel, hipStream_t st, int masking) {
     if (dtype != 1 || N > MAXN || topk > 4 || dv % DB != 0) return hipErrorInvalidValue;
-    SseArgs a{B, T, H, N, topk, dv, logits, q, k, v, lam, q_sh, k_sh, S, o, sel, e_sel};
+    SseArgs a{B, T, H, N, topk, dv, logits, q, k, v, lam, q_sh, k_sh, S, o, sel, e_sel, masking};
     const int P = B * T * H;
     sse_route_kernel<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(logits, P, N, topk, sel, e_sel);
     hipError_t e = hipGetLastError();

@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("sdm_forward", "sdm_decode_step", "sse_forward", "sse_decode_step",
+    for required in ("sdm_forward", "sdm_decode_step", "sse_forward", "sse_forward_masking",
+                     "sse_decode_step",
                      "gdn_chunk_forward",
                      "sdm_address", "sdm_sparse_update", "sslp_last_error", "sslp_version"):
         assert required in names
@@ -125,6 +126,16 @@ def test_gdn_and_sse_shape_errors():
     assert lib.sse_forward(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == _lib.SSLP_ERR_INVALID_ARG
     s = _lib.SseShape(1, 8, 1, 8, 2, 64, 128, 64)
     assert lib.sse_forward(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == _lib.SSLP_ERR_UNSUPPORTED
+    # the masking execution validates exactly like the grouped one
+    assert lib.sse_forward_masking(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == \
+        _lib.SSLP_ERR_UNSUPPORTED
+    s = _lib.SseShape(1, 8, 1, 8, 9, 128, 128, 64)
+    assert lib.sse_forward_masking(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+    s = _lib.SseShape(1, 8, 1, 8, 2, 128, 128, 64)
+    assert lib.sse_forward_masking(ctypes.byref(s), 0, *([FAKE] * 12), 0, None) == \
+        _lib.SSLP_ERR_UNSUPPORTED
+    assert b"sse_forward_masking" in lib.sslp_last_error()
     # the decode step takes exactly one token per sequence
     s = _lib.SseShape(2, 2, 1, 8, 2, 128, 128, 64)
     assert lib.sse_decode_step(ctypes.byref(s), 1, *([FAKE] * 11), None) == _lib.SSLP_ERR_INVALID_ARG

@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _run(x, N, topk, S0=None, q_sh=None, k_sh=None):
+def _run(x, N, topk, S0=None, q_sh=None, k_sh=None, masking=False):
     import sparse_state_linear_product_amd as sslp
     xd = {k: v.to(DEV) for k, v in x.items()}
     B, T, H, _ = x["logits"].shape
@@ -20,22 +20,23 @@ def _run(x, N, topk, S0=None, q_sh=None, k_sh=None):
     e_sel = torch.empty((B, T, H, topk), dtype=torch.float32, device=DEV)
     o = sslp.sse_forward(xd["logits"], xd["q"], xd["k"], xd["v"], xd["lam"], S, topk,
                          q_sh=None if q_sh is None else q_sh.to(DEV),
-                         k_sh=None if k_sh is None else k_sh.to(DEV), sel=sel, e_sel=e_sel)
+                         k_sh=None if k_sh is None else k_sh.to(DEV), sel=sel, e_sel=e_sel,
+                         masking=masking)
     torch.cuda.synchronize()
     return dict(o=o.cpu(), S=S.cpu(), sel=sel.cpu().numpy(), e_sel=e_sel.cpu().numpy())
 
 
-def _ref(x, topk, S0=None, q_sh=None, k_sh=None):
+def _ref(x, topk, S0=None, q_sh=None, k_sh=None, masking=False):
     n = {k: wl.to_numpy_f32(v) for k, v in x.items()}
     return oracle.sse(n["logits"], n["q"], n["k"], n["v"], n["lam"], topk,
                       q_sh=None if q_sh is None else wl.to_numpy_f32(q_sh),
                       k_sh=None if k_sh is None else wl.to_numpy_f32(k_sh),
-                      S0=None if S0 is None else S0.double().numpy())
+                      S0=None if S0 is None else S0.double().numpy(), masking=masking)
 
 
-def _check(x, N, topk, tag, S0=None, q_sh=None, k_sh=None):
-    got = _run(x, N, topk, S0, q_sh, k_sh)
-    ref = _ref(x, topk, S0, q_sh, k_sh)
+def _check(x, N, topk, tag, S0=None, q_sh=None, k_sh=None, masking=False):
+    got = _run(x, N, topk, S0, q_sh, k_sh, masking)
+    ref = _ref(x, topk, S0, q_sh, k_sh, masking)
     np.testing.assert_array_equal(got["sel"], ref["sel"], err_msg=f"{tag}: selection")
     e_e = np.abs(got["e_sel"] - ref["e_sel"]).max()
     e_o = maxrel(got["o"].double().numpy(), ref["o"])
@@ -100,6 +101,43 @@ def test_sse_full_config():
     announce(f"{cfg.name} full size")
     x = wl.sse_inputs(cfg)
     _check(x, cfg.N, cfg.topk, cfg.name)
+
+
+# ---------------- masking execution ----------------
+
+@pytest.mark.parametrize("N,topk,T", [(8, 2, 1), (8, 2, 23), (8, 2, 130), (5, 3, 70), (4, 1, 65),
+                                      (8, 4, 64)])
+def test_sse_masking_matches_masking_oracle(N, topk, T):
+    announce(f"sse_forward_masking N={N} k={topk} T={T}")
+    cfg = wl.SseConfig("m", 2, T, 2, N, topk, 128, 128, torch.bfloat16, 900 + 10 * N + topk + T)
+    x = wl.sse_inputs(cfg)
+    _check(x, N, topk, f"masking N={N} k={topk} T={T}", masking=True)
+
+
+def test_sse_masking_agrees_with_varlen_and_keeps_idle_states():
+    # the two executions compute the same thing: identical routing, outputs
+    # and states within the bf16 bound, and a never-selected partition (all of
+    # its steps masked, decay frozen at 1) keeps its state bitwise
+    announce("sse_forward_masking vs sse_forward, S0 and separate shared q/k")
+    x = wl.sse_inputs(wl.SSE, T=200, B=1, H=2, seed=31)
+    x["logits"][..., 6] = -30.0
+    g = torch.Generator().manual_seed(32)
+    S0 = torch.randn((1, 2, 9, 128, 128), generator=g) * 0.1
+    q_sh = torch.randn((1, 200, 2, 128), generator=g).bfloat16()
+    k_sh = torch.softmax(torch.randn((1, 200, 2, 128), generator=g), -1).bfloat16()
+    a = _run(x, 8, 2, S0, q_sh, k_sh, masking=True)
+    b = _run(x, 8, 2, S0, q_sh, k_sh, masking=False)
+    np.testing.assert_array_equal(a["sel"], b["sel"])
+    np.testing.assert_array_equal(a["e_sel"], b["e_sel"])
+    e_o = maxrel(a["o"].double().numpy(), b["o"].double().numpy())
+    e_S = maxrel(a["S"].double().numpy(), b["S"].double().numpy())
+    print(f"  masking vs varlen: o {e_o:.2e} S {e_S:.2e}", flush=True)
+    assert e_o <= TOL_BF16 and e_S <= TOL_BF16
+    assert torch.equal(a["S"][0, :, 6], S0[0, :, 6])
+    # the shared partition runs the same steps in both executions
+    assert torch.equal(a["S"][0, :, 8], b["S"][0, :, 8])
+    ref = _ref(x, 2, S0, q_sh, k_sh, masking=True)
+    assert maxrel(a["o"].double().numpy(), ref["o"]) <= TOL_BF16
 
 
 # ---------------- decode step (one token per sequence) ----------------
