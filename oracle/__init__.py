@@ -14,6 +14,11 @@ sdm_recurrence  sparse decay / delta update / read given the addressing
                 (Sparse Delta Memory slides, Eqs. (3)-(5) and the
                 shared-prediction figure form)
 sdm_forward     addressing for writes and reads, then the recurrence
+sdm_recurrence_backward  gradient of the recurrence by undoing writes (same
+                slides, backup "Backup: undoing writes avoids repeated
+                full-table snapshots")
+sdm_address_backward     gradient of the addressing softmax w.r.t. the halves
+sdm_backward    both, for the whole SDM forward
 gdn             sequential Gated DeltaNet / KDA (Linear Attention
                 Architectures slides, Eqs. 14-20)
 gdn2            sequential GDN2: key-side erase b, value-side write w
@@ -64,6 +69,14 @@ def _load():
     lib.orc_sdm_recurrence.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_longlong,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        _i32p, _f64p, _i32p, _f64p, _f32p, _f32p, _f32p, _f64p, _f64p]
+    lib.orc_sdm_recurrence_backward.restype = ctypes.c_int
+    lib.orc_sdm_recurrence_backward.argtypes = (
+        [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+         ctypes.c_int, ctypes.c_int, _i32p, _f64p, _i32p, _f64p, _f32p, _f32p, _f32p]
+        + [_f64p] * 8)
+    lib.orc_sdm_address_backward.restype = ctypes.c_int
+    lib.orc_sdm_address_backward.argtypes = [ctypes.c_int] * 3 + [_i32p, _f64p, _f64p, _f64p,
+                                                                  _f64p]
     lib.orc_gdn.restype = ctypes.c_int
     lib.orc_gdn.argtypes = [ctypes.c_int] * 6 + [_f32p, _f32p, _f32p, _f32p, _f32p,
                                                  _Nullable(np.float64), _f64p, _f64p]
@@ -133,6 +146,73 @@ def sdm_forward(sw1, sw2, sr1, sr2, v, alpha, beta, M0, k_w, k_r, W, R, residual
     idx_r, wt_r = sdm_address(sr1, sr2, k_r, R)
     M, y = sdm_recurrence(idx_w, wt_w, idx_r, wt_r, v, alpha, beta, M0, residual_mode)
     return dict(M=M, y=y, idx_w=idx_w, wt_w=wt_w, idx_r=idx_r, wt_r=wt_r)
+
+
+def sdm_recurrence_backward(idx_w, wt_w, idx_r, wt_r, v, alpha, beta, M0, dy, dM=None,
+                            residual_mode=0):
+    """Gradient of sdm_recurrence by undoing writes.
+
+    dy: [B,T,H,dv] gradient of y; dM: [B,H,N,dv] gradient of the final table
+    (None = zeros).  Returns dict with dv [B,T,H,dv], dalpha, dbeta [B,T,H],
+    dwt_w [B,T,H,W], dwt_r [B,T,H,R] and dM0 [B,H,N,dv] (gradient of M0), all
+    float64.
+    """
+    idx_w = np.ascontiguousarray(idx_w, np.int32)
+    idx_r = np.ascontiguousarray(idx_r, np.int32)
+    wt_w = np.ascontiguousarray(wt_w, np.float64)
+    wt_r = np.ascontiguousarray(wt_r, np.float64)
+    v, alpha, beta = _f32(v), _f32(alpha), _f32(beta)
+    B, T, H, W = idx_w.shape
+    R = idx_r.shape[-1]
+    dvw = v.shape[-1]
+    M0 = np.ascontiguousarray(M0, np.float64)
+    N = M0.shape[2]
+    dy = np.ascontiguousarray(dy, np.float64)
+    G = np.zeros(M0.shape, np.float64) if dM is None else np.array(dM, np.float64, order="C")
+    out = dict(dv=np.zeros((B, T, H, dvw)), dalpha=np.zeros((B, T, H)),
+               dbeta=np.zeros((B, T, H)), dwt_w=np.zeros((B, T, H, W)),
+               dwt_r=np.zeros((B, T, H, R)))
+    rc = _load().orc_sdm_recurrence_backward(B, T, H, N, dvw, W, R, int(residual_mode), idx_w,
+                                             wt_w, idx_r, wt_r, v, alpha, beta, M0, dy, G,
+                                             out["dv"], out["dalpha"], out["dbeta"],
+                                             out["dwt_w"], out["dwt_r"])
+    if rc != 0:
+        raise ValueError("orc_sdm_recurrence_backward: invalid arguments")
+    out["dM0"] = G
+    return out
+
+
+def sdm_address_backward(idx, wt, dwt, sqrt_n):
+    """Gradient of the addressing softmax, selection held fixed.
+
+    idx, wt, dwt: [..., budget].  Returns (ds1, ds2) float64 [..., sqrtN].
+    """
+    idx = np.ascontiguousarray(idx, np.int32)
+    wt = np.ascontiguousarray(wt, np.float64)
+    dwt = np.ascontiguousarray(dwt, np.float64)
+    lead, budget = idx.shape[:-1], idx.shape[-1]
+    p = int(np.prod(lead)) if lead else 1
+    ds1 = np.zeros(lead + (sqrt_n,))
+    ds2 = np.zeros(lead + (sqrt_n,))
+    rc = _load().orc_sdm_address_backward(p, int(sqrt_n), budget, idx, wt, dwt, ds1, ds2)
+    if rc != 0:
+        raise ValueError("orc_sdm_address_backward: invalid arguments")
+    return ds1, ds2
+
+
+def sdm_backward(sw1, sw2, sr1, sr2, v, alpha, beta, M0, k_w, k_r, W, R, dy, dM=None,
+                 residual_mode=0):
+    """Gradient of sdm_forward w.r.t. every input: the recurrence by undoing
+    writes, then the addressing softmax (selection fixed).  Returns the dict of
+    sdm_recurrence_backward plus dsw1, dsw2, dsr1, dsr2 [B,T,H,sqrtN]."""
+    sqrt_n = np.shape(sw1)[-1]
+    idx_w, wt_w = sdm_address(sw1, sw2, k_w, W)
+    idx_r, wt_r = sdm_address(sr1, sr2, k_r, R)
+    g = sdm_recurrence_backward(idx_w, wt_w, idx_r, wt_r, v, alpha, beta, M0, dy, dM,
+                                residual_mode)
+    g["dsw1"], g["dsw2"] = sdm_address_backward(idx_w, wt_w, g["dwt_w"], sqrt_n)
+    g["dsr1"], g["dsr2"] = sdm_address_backward(idx_r, wt_r, g["dwt_r"], sqrt_n)
+    return g
 
 
 def gdn(q, k, v, alpha, beta, S0=None, kda=False):

@@ -172,3 +172,169 @@ int orc_sdm_recurrence(int B, int T, int H, long long N, int dv, int W, int R, i
         }
     return 0;
 }
+
+/*
+ * Gradient of the recurrence above (its vector-Jacobian product), computed the
+ * way the Sparse Delta Memory slides' backup "Backup: undoing writes avoids
+ * repeated full-table snapshots" describes: the forward keeps, per token, the
+ * rows its write set held before the token (T * W * dv values per (b, h)
+ * instead of one table per chunk); the backward walks the tokens in reverse
+ * with the table at M_t, and steps it back to M_{t-1} by restoring those rows.
+ *
+ *   idx_w .. beta : as orc_sdm_recurrence (the forward is re-run here)
+ *   M0            : [B,H,N,dv] initial table (read only)
+ *   dy            : [B,T,H,dv] gradient of the reads
+ *   dM            : [B,H,N,dv] in: gradient of the final table M_T;
+ *                               out: gradient of the initial table M_0
+ *   dv_out        : [B,T,H,dv]  gradient of v
+ *   dalpha, dbeta : [B,T,H]     gradients of the gates
+ *   dwt_w, dwt_r  : [B,T,H,W], [B,T,H,R] gradients of the addressing weights
+ *
+ * Per token t in reverse (G = gradient of M_t, one row per slot):
+ *   read    y = sum_m wr_m M_t[j_m]:   dwr_m = <M_t[j_m], dy_t>;  G[j_m] += wr_m dy_t
+ *   write   with P_n = M_{t-1}[i_n] (restored), Mt_n = alpha P_n, G_n = G[i_n]:
+ *     SHARED   r = v - sum_n w_n Mt_n,  M_t[i_n] = Mt_n + beta w_n r:
+ *              dr = sum_n beta w_n G_n;  dv = dr;  dbeta = sum_n w_n <G_n, r>;
+ *              dw_n = beta <G_n, r> - <Mt_n, dr>;  dMt_n = G_n - w_n dr
+ *     PER_SLOT M_t[i_n] = Mt_n + beta w_n (v - Mt_n):
+ *              dv = sum_n beta w_n G_n;  dbeta = sum_n w_n <G_n, v - Mt_n>;
+ *              dw_n = beta <G_n, v - Mt_n>;  dMt_n = (1 - beta w_n) G_n
+ *     dalpha = sum_n <P_n, dMt_n>;  G[i_n] = alpha dMt_n;  table row i_n = P_n.
+ * Rows outside the token's write set pass G through unchanged.
+ */
+int orc_sdm_recurrence_backward(int B, int T, int H, long long N, int dv, int W, int R,
+                                int residual_mode, const int32_t* idx_w, const double* wt_w,
+                                const int32_t* idx_r, const double* wt_r, const float* v,
+                                const float* alpha, const float* beta, const double* M0,
+                                const double* dy, double* dM, double* dv_out, double* dalpha,
+                                double* dbeta, double* dwt_w, double* dwt_r) {
+    if (B < 0 || T < 0 || H <= 0 || N <= 0 || dv <= 0 || W <= 0 || R <= 0) return -1;
+    if (residual_mode != 0 && residual_mode != 1) return -1;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const size_t tsz = (size_t)N * dv;
+            double* tab = (double*)malloc(sizeof(double) * tsz);
+            double* G = dM + ((size_t)b * H + h) * tsz;
+            double* saved = (double*)malloc(sizeof(double) * ((size_t)T * W * dv + 1));
+            double* mt = (double*)malloc(sizeof(double) * (size_t)W * dv);
+            double* r = (double*)malloc(sizeof(double) * dv);
+            double* dr = (double*)malloc(sizeof(double) * dv);
+            memcpy(tab, M0 + ((size_t)b * H + h) * tsz, sizeof(double) * tsz);
+            /* forward, keeping each token's pre-write rows */
+            for (int t = 0; t < T; ++t) {
+                size_t bth = ((size_t)b * T + t) * H + h;
+                const int32_t* iw = idx_w + bth * W;
+                const double* gw = wt_w + bth * W;
+                const float* vt = v + bth * dv;
+                double a = alpha[bth], be = beta[bth];
+                double* sv = saved + (size_t)t * W * dv;
+                for (int n = 0; n < W; ++n)
+                    for (int c = 0; c < dv; ++c) {
+                        sv[(size_t)n * dv + c] = tab[(size_t)iw[n] * dv + c];
+                        mt[(size_t)n * dv + c] = a * sv[(size_t)n * dv + c];
+                    }
+                for (int c = 0; c < dv; ++c) {
+                    double s = 0.0;
+                    for (int n = 0; n < W; ++n) s += gw[n] * mt[(size_t)n * dv + c];
+                    r[c] = (double)vt[c] - s;
+                }
+                for (int n = 0; n < W; ++n)
+                    for (int c = 0; c < dv; ++c) {
+                        double res = residual_mode == 0 ? r[c] : (double)vt[c] - mt[(size_t)n * dv + c];
+                        tab[(size_t)iw[n] * dv + c] = mt[(size_t)n * dv + c] + be * gw[n] * res;
+                    }
+            }
+            /* reverse sweep; tab holds M_t on entry to step t */
+            for (int t = T - 1; t >= 0; --t) {
+                size_t bth = ((size_t)b * T + t) * H + h;
+                const int32_t* iw = idx_w + bth * W;
+                const double* gw = wt_w + bth * W;
+                const int32_t* ir = idx_r + bth * R;
+                const double* gr = wt_r + bth * R;
+                const float* vt = v + bth * dv;
+                const double* dyt = dy + bth * dv;
+                double a = alpha[bth], be = beta[bth];
+                const double* sv = saved + (size_t)t * W * dv;
+                /* read after writing */
+                for (int m = 0; m < R; ++m) {
+                    double s = 0.0;
+                    for (int c = 0; c < dv; ++c) s += tab[(size_t)ir[m] * dv + c] * dyt[c];
+                    dwt_r[bth * R + m] = s;
+                    for (int c = 0; c < dv; ++c) G[(size_t)ir[m] * dv + c] += gr[m] * dyt[c];
+                }
+                /* the write, from the restored rows */
+                for (int n = 0; n < W; ++n)
+                    for (int c = 0; c < dv; ++c) mt[(size_t)n * dv + c] = a * sv[(size_t)n * dv + c];
+                for (int c = 0; c < dv; ++c) {
+                    double s = 0.0, g = 0.0;
+                    for (int n = 0; n < W; ++n) {
+                        s += gw[n] * mt[(size_t)n * dv + c];
+                        g += be * gw[n] * G[(size_t)iw[n] * dv + c];
+                    }
+                    r[c] = (double)vt[c] - s;
+                    dr[c] = g;
+                    dv_out[bth * dv + c] = g;
+                }
+                double db = 0.0, da = 0.0;
+                for (int n = 0; n < W; ++n) {
+                    double* gn = G + (size_t)iw[n] * dv;
+                    const double* mn = mt + (size_t)n * dv;
+                    double gres = 0.0, mdr = 0.0;
+                    for (int c = 0; c < dv; ++c) {
+                        double res = residual_mode == 0 ? r[c] : (double)vt[c] - mn[c];
+                        gres += gn[c] * res;
+                        mdr += mn[c] * dr[c];
+                    }
+                    db += gw[n] * gres;
+                    dwt_w[bth * W + n] = residual_mode == 0 ? be * gres - mdr : be * gres;
+                    for (int c = 0; c < dv; ++c) {
+                        double dmt = residual_mode == 0 ? gn[c] - gw[n] * dr[c]
+                                                        : (1.0 - be * gw[n]) * gn[c];
+                        da += sv[(size_t)n * dv + c] * dmt;
+                        gn[c] = a * dmt;
+                        tab[(size_t)iw[n] * dv + c] = sv[(size_t)n * dv + c];
+                    }
+                }
+                dalpha[bth] = da;
+                dbeta[bth] = db;
+            }
+            free(tab);
+            free(saved);
+            free(mt);
+            free(r);
+            free(dr);
+        }
+    return 0;
+}
+
+/*
+ * Gradient of the addressing weights with respect to the score halves
+ * (slide "Product keys select addresses without scoring every slot"): the
+ * weights are a softmax of the selected scores s1[a] + s2[b], so with the
+ * selection held fixed
+ *   ds_m = wt_m (dwt_m - sum_j wt_j dwt_j),  ds1[a_m] += ds_m,  ds2[b_m] += ds_m,
+ * where slot idx_m = a_m * sqrtN + b_m.  Halves outside every selected pair
+ * get 0.
+ *   idx, wt, dwt : [P, budget];  ds1, ds2 : [P, sqrtN] out.
+ */
+int orc_sdm_address_backward(int P, int sqrtN, int budget, const int32_t* idx, const double* wt,
+                             const double* dwt, double* ds1, double* ds2) {
+    if (P < 0 || sqrtN <= 0 || budget <= 0) return -1;
+    for (int p = 0; p < P; ++p) {
+        const int32_t* ip = idx + (size_t)p * budget;
+        const double* w = wt + (size_t)p * budget;
+        const double* dw = dwt + (size_t)p * budget;
+        double* d1 = ds1 + (size_t)p * sqrtN;
+        double* d2 = ds2 + (size_t)p * sqrtN;
+        for (int a = 0; a < sqrtN; ++a) d1[a] = d2[a] = 0.0;
+        double dot = 0.0;
+        for (int m = 0; m < budget; ++m) dot += w[m] * dw[m];
+        for (int m = 0; m < budget; ++m) {
+            double ds = w[m] * (dw[m] - dot);
+            d1[ip[m] / sqrtN] += ds;
+            d2[ip[m] % sqrtN] += ds;
+        }
+    }
+    return 0;
+}
