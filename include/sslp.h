@@ -164,6 +164,82 @@ int sdm_sparse_update(const sslp_sdm_shape* shape, int dtype, int residual_mode,
                       float* M, void* y, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Sparse Delta Memory training: backward by undoing writes                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * sdm_forward_train -- sdm_forward that also keeps what the backward needs:
+ * the addressing (idx_w, wt_w, idx_r, wt_r, now required) and, per token, the
+ * write rows as they were before the token (Sparse Delta Memory slides, backup
+ * "Backup: undoing writes avoids repeated full-table snapshots": the forward
+ * updates the table in place and retains the sparse update information).
+ *   saved [B,T,H,W,d_v] fp32 out: saved[b,t,h,n,:] = M_{t-1}[idx_w[b,t,h,n], :]
+ *   (T W d_v values per head, instead of one table per chunk).
+ * Other arguments as sdm_forward; no workspace.  The recurrence runs one token
+ * at a time (the chunk-parallel kernel has no per-token states to keep).
+ */
+int sdm_forward_train(const sslp_sdm_shape* shape, int dtype, int residual_mode, const void* sw1,
+                      const void* sw2, const void* sr1, const void* sr2, const void* v,
+                      const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
+                      float* wt_w, int32_t* idx_r, float* wt_r, float* saved, void* stream);
+
+/*
+ * sdm_sparse_update_train -- sdm_sparse_update that also writes `saved` as
+ * sdm_forward_train does (addressing given by the caller; W, R up to 128).
+ */
+int sdm_sparse_update_train(const sslp_sdm_shape* shape, int dtype, int residual_mode,
+                            const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
+                            const float* wt_r, const void* v, const float* alpha,
+                            const float* beta, float* M, void* y, float* saved, void* stream);
+
+/* Workspace bytes of sdm_backward: per-token partial sums of the scalar
+ * gradients for each 16-column slice of d_v, and the weight gradients when the
+ * caller does not ask for them.  0 for an invalid shape. */
+size_t sdm_backward_workspace_size(const sslp_sdm_shape* shape);
+
+/*
+ * sdm_backward -- gradient of the SDM forward (Eqs. (3)-(5), either residual
+ * form) by undoing writes (backup "Backup: undoing writes avoids repeated
+ * full-table snapshots"): the tokens are walked in reverse with the table at
+ * M_t; each token's saved rows step it back to M_{t-1}.  With G the gradient
+ * of the table, per token t (reverse):
+ *   G[j_m] += wt^r_m dy_t and dwt_r_m = <M_t[j_m], dy_t> for the read slots;
+ *   then through the write with P_n = saved rows, M~_n = alpha_t P_n:
+ *   SHARED:   r = v_t - sum_n wt_n M~_n;  dv_t = dr = sum_n beta_t wt_n G[i_n];
+ *             dbeta_t = sum_n wt_n <G[i_n], r>;  dwt_n = beta_t <G[i_n], r> - <M~_n, dr>;
+ *             dM~_n = G[i_n] - wt_n dr
+ *   PER_SLOT: dv_t = sum_n beta_t wt_n G[i_n];  dbeta_t = sum_n wt_n <G[i_n], v_t - M~_n>;
+ *             dwt_n = beta_t <G[i_n], v_t - M~_n>;  dM~_n = (1 - beta_t wt_n) G[i_n]
+ *   dalpha_t = sum_n <P_n, dM~_n>;  G[i_n] = alpha_t dM~_n;  M[i_n] = P_n.
+ * The score-half gradients follow from the softmax of the selected scores
+ * s1[a] + s2[b] with the selection held fixed (slide "Product keys select
+ * addresses without scoring every slot"): ds_m = wt_m (dwt_m - sum_j wt_j dwt_j),
+ * added into ds1[a_m] and ds2[b_m]; halves in no selected pair get 0.
+ *
+ *   idx_w, wt_w, idx_r, wt_r  the forward's addressing (read slots, like write
+ *                             slots, distinct within a token);
+ *   v, alpha, beta            the forward's inputs;
+ *   M      [B,H,N,d_v] fp32   in: the table after the forward; out: the table
+ *                             before it (every write undone);
+ *   saved  [B,T,H,W,d_v] fp32 from sdm_forward_train / sdm_sparse_update_train;
+ *   dy     [B,T,H,d_v] dtype  gradient of y;
+ *   dM     [B,H,N,d_v] fp32   in: gradient of the final table (zeros if none);
+ *                             out: gradient of the initial table;
+ *   dv     [B,T,H,d_v] dtype out;  dalpha, dbeta [B,T,H] fp32 out;
+ *   dwt_w [B,T,H,W], dwt_r [B,T,H,R] fp32 optional out;
+ *   dsw1, dsw2 / dsr1, dsr2 [B,T,H,sqrtN] fp32 optional out, each pair both or
+ *                             neither (NULL skips that addressing backward);
+ *   workspace, ws_bytes >= sdm_backward_workspace_size(shape).
+ * The scalar gradients are added over d_v in a fixed order (deterministic).
+ */
+int sdm_backward(const sslp_sdm_shape* shape, int dtype, int residual_mode, const int32_t* idx_w,
+                 const float* wt_w, const int32_t* idx_r, const float* wt_r, const void* v,
+                 const float* alpha, const float* beta, float* M, const float* saved,
+                 const void* dy, float* dM, void* dv, float* dalpha, float* dbeta, float* dwt_w,
+                 float* dwt_r, float* dsw1, float* dsw2, float* dsr1, float* dsr2, void* workspace,
+                 size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Gated DeltaNet / Kimi Delta Attention (dense limit: every slot selected)  */
 /* ------------------------------------------------------------------------ */
 

@@ -9,6 +9,7 @@ allocated with torch when the caller does not pass one.
 
 Functions (see include/sslp.h for the exact semantics):
   sdm_forward, sdm_decode_step, sdm_address, sdm_sparse_update   Sparse Delta Memory
+  sdm_forward_train, sdm_sparse_update_train, sdm_backward       SDM training (undo writes)
   gdn_chunk_forward, gdn2_chunk_forward                          Gated DeltaNet / KDA / GDN2
   sse_forward (masking=True: sse_forward_masking), sse_decode_step  Sparse State Expansion
 """
@@ -21,6 +22,8 @@ from ._lib import (DECAY_CHANNEL, DECAY_SCALAR, RESIDUAL_PER_SLOT, RESIDUAL_SHAR
                    SdmShape, SseShape, SslpError, check, lib)
 
 __all__ = ["sdm_forward", "sdm_decode_step", "sdm_address", "sdm_sparse_update",
+           "sdm_forward_train", "sdm_sparse_update_train", "sdm_backward",
+           "sdm_backward_workspace_bytes",
            "gdn_chunk_forward", "gdn2_chunk_forward", "sse_forward", "sse_decode_step",
            "SslpError", "RESIDUAL_SHARED", "RESIDUAL_PER_SLOT", "DECAY_SCALAR", "DECAY_CHANNEL",
            "version"]
@@ -185,6 +188,138 @@ def sdm_sparse_update(idx_w, wt_w, idx_r, wt_r, v, alpha, beta, M, y=None,
                                  _stream(stream))
     check("sdm_sparse_update", rc)
     return y
+
+
+def sdm_backward_workspace_bytes(B, T, H, sqrtN, d_v, W, R):
+    return lib().sdm_backward_workspace_size(ctypes.byref(sdm_shape(B, T, H, sqrtN, d_v, 1, 1,
+                                                                     W, R)))
+
+
+def sdm_forward_train(sw1, sw2, sr1, sr2, v, alpha, beta, M, k_w, k_r, W, R, y=None,
+                      residual_mode=RESIDUAL_SHARED, out=None, stream=None):
+    """sdm_forward that keeps what sdm_backward needs.  M is updated in place.
+
+    Returns (y, dict(idx_w, wt_w, idx_r, wt_r, saved)); saved [B,T,H,W,d_v] fp32
+    holds each token's write rows as they were before the token.  `out` may pass
+    such a dict of preallocated tensors to fill."""
+    B, T, H, sqrt_n = sw1.shape
+    d_v = v.shape[-1]
+    dt = sw1.dtype
+    for name, t in (("sw2", sw2), ("sr1", sr1), ("sr2", sr2)):
+        _need(t, dt, (B, T, H, sqrt_n), name)
+    _need(v, dt, (B, T, H, d_v), "v")
+    _need(alpha, torch.float32, (B, T, H), "alpha")
+    _need(beta, torch.float32, (B, T, H), "beta")
+    _need(M, torch.float32, (B, H, sqrt_n * sqrt_n, d_v), "M")
+    if y is None:
+        y = torch.empty((B, T, H, d_v), dtype=dt, device=v.device)
+    _need(y, dt, (B, T, H, d_v), "y")
+    dev = v.device
+    if out is None:
+        out = dict(idx_w=torch.empty((B, T, H, W), dtype=torch.int32, device=dev),
+                   wt_w=torch.empty((B, T, H, W), dtype=torch.float32, device=dev),
+                   idx_r=torch.empty((B, T, H, R), dtype=torch.int32, device=dev),
+                   wt_r=torch.empty((B, T, H, R), dtype=torch.float32, device=dev),
+                   saved=torch.empty((B, T, H, W, d_v), dtype=torch.float32, device=dev))
+    ctx = out
+    _need(ctx["idx_w"], torch.int32, (B, T, H, W), "idx_w")
+    _need(ctx["wt_w"], torch.float32, (B, T, H, W), "wt_w")
+    _need(ctx["idx_r"], torch.int32, (B, T, H, R), "idx_r")
+    _need(ctx["wt_r"], torch.float32, (B, T, H, R), "wt_r")
+    _need(ctx["saved"], torch.float32, (B, T, H, W, d_v), "saved")
+    shape = sdm_shape(B, T, H, sqrt_n, d_v, k_w, k_r, W, R)
+    rc = lib().sdm_forward_train(ctypes.byref(shape), _dtype_code(sw1), int(residual_mode),
+                                 _ptr(sw1), _ptr(sw2), _ptr(sr1), _ptr(sr2), _ptr(v), _ptr(alpha),
+                                 _ptr(beta), _ptr(M), _ptr(y), _ptr(ctx["idx_w"]),
+                                 _ptr(ctx["wt_w"]), _ptr(ctx["idx_r"]), _ptr(ctx["wt_r"]),
+                                 _ptr(ctx["saved"]), _stream(stream))
+    check("sdm_forward_train", rc)
+    return y, ctx
+
+
+def sdm_sparse_update_train(idx_w, wt_w, idx_r, wt_r, v, alpha, beta, M, y=None, saved=None,
+                            residual_mode=RESIDUAL_SHARED, stream=None):
+    """sdm_sparse_update that also returns saved [B,T,H,W,d_v] (pre-write rows)."""
+    B, T, H, W = idx_w.shape
+    R = idx_r.shape[-1]
+    d_v = v.shape[-1]
+    N = M.shape[2]
+    sqrt_n = int(round(N ** 0.5))
+    if sqrt_n * sqrt_n != N:
+        raise ValueError("M.shape[2] must be a perfect square")
+    _need(idx_w, torch.int32, (B, T, H, W), "idx_w")
+    _need(wt_w, torch.float32, (B, T, H, W), "wt_w")
+    _need(idx_r, torch.int32, (B, T, H, R), "idx_r")
+    _need(wt_r, torch.float32, (B, T, H, R), "wt_r")
+    _need(alpha, torch.float32, (B, T, H), "alpha")
+    _need(beta, torch.float32, (B, T, H), "beta")
+    _need(M, torch.float32, (B, H, N, d_v), "M")
+    if y is None:
+        y = torch.empty((B, T, H, d_v), dtype=v.dtype, device=v.device)
+    if saved is None:
+        saved = torch.empty((B, T, H, W, d_v), dtype=torch.float32, device=v.device)
+    _need(y, v.dtype, (B, T, H, d_v), "y")
+    _need(saved, torch.float32, (B, T, H, W, d_v), "saved")
+    shape = sdm_shape(B, T, H, sqrt_n, d_v, 1, 1, W, R)
+    rc = lib().sdm_sparse_update_train(ctypes.byref(shape), _dtype_code(v), int(residual_mode),
+                                       _ptr(idx_w), _ptr(wt_w), _ptr(idx_r), _ptr(wt_r), _ptr(v),
+                                       _ptr(alpha), _ptr(beta), _ptr(M), _ptr(y), _ptr(saved),
+                                       _stream(stream))
+    check("sdm_sparse_update_train", rc)
+    return y, saved
+
+
+def sdm_backward(ctx, v, alpha, beta, M, dy, dM=None, residual_mode=RESIDUAL_SHARED,
+                 score_grads=True, workspace=None, stream=None):
+    """Gradient of the SDM forward by undoing writes.
+
+    ctx: the dict of sdm_forward_train (or idx_w, wt_w, idx_r, wt_r, saved of
+    sdm_sparse_update_train).  M: the table after the forward, restored in place
+    to the table before it.  dy [B,T,H,d_v] (dtype of v); dM [B,H,N,d_v] fp32
+    gradient of the final table (zeros if None), updated in place to the
+    gradient of the initial table.  Returns dict(dv, dalpha, dbeta, dwt_w, dwt_r,
+    dM[, dsw1, dsw2, dsr1, dsr2]); score_grads=False skips the addressing
+    backward."""
+    idx_w, wt_w, idx_r, wt_r, saved = (ctx[k] for k in ("idx_w", "wt_w", "idx_r", "wt_r",
+                                                         "saved"))
+    B, T, H, W = idx_w.shape
+    R = idx_r.shape[-1]
+    d_v = v.shape[-1]
+    N = M.shape[2]
+    sqrt_n = int(round(N ** 0.5))
+    if sqrt_n * sqrt_n != N:
+        raise ValueError("M.shape[2] must be a perfect square")
+    dev = v.device
+    _need(wt_w, torch.float32, (B, T, H, W), "wt_w")
+    _need(idx_r, torch.int32, (B, T, H, R), "idx_r")
+    _need(wt_r, torch.float32, (B, T, H, R), "wt_r")
+    _need(alpha, torch.float32, (B, T, H), "alpha")
+    _need(beta, torch.float32, (B, T, H), "beta")
+    _need(M, torch.float32, (B, H, N, d_v), "M")
+    _need(saved, torch.float32, (B, T, H, W, d_v), "saved")
+    _need(dy, v.dtype, (B, T, H, d_v), "dy")
+    if dM is None:
+        dM = torch.zeros((B, H, N, d_v), dtype=torch.float32, device=dev)
+    _need(dM, torch.float32, (B, H, N, d_v), "dM")
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dv=torch.empty_like(v), dalpha=torch.empty((B, T, H), **f32),
+             dbeta=torch.empty((B, T, H), **f32), dwt_w=torch.empty((B, T, H, W), **f32),
+             dwt_r=torch.empty((B, T, H, R), **f32), dM=dM)
+    if score_grads:
+        for k in ("dsw1", "dsw2", "dsr1", "dsr2"):
+            g[k] = torch.empty((B, T, H, sqrt_n), **f32)
+    shape = sdm_shape(B, T, H, sqrt_n, d_v, 1, 1, W, R)
+    ws, nbytes = _workspace(lib().sdm_backward_workspace_size(ctypes.byref(shape)), workspace,
+                            dev)
+    rc = lib().sdm_backward(ctypes.byref(shape), _dtype_code(v), int(residual_mode), _ptr(idx_w),
+                            _ptr(wt_w), _ptr(idx_r), _ptr(wt_r), _ptr(v), _ptr(alpha),
+                            _ptr(beta), _ptr(M), _ptr(saved), _ptr(dy), _ptr(dM), _ptr(g["dv"]),
+                            _ptr(g["dalpha"]), _ptr(g["dbeta"]), _ptr(g["dwt_w"]),
+                            _ptr(g["dwt_r"]), _ptr(g.get("dsw1")), _ptr(g.get("dsw2")),
+                            _ptr(g.get("dsr1")), _ptr(g.get("dsr2")), _ptr(ws), nbytes,
+                            _stream(stream))
+    check("sdm_backward", rc)
+    return g
 
 
 # ---------------------------------------------------------------------------

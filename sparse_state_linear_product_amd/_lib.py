@@ -44,6 +44,10 @@ SIGNATURES = {
     "sdm_decode_step": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 14 + [_sz, _vp], _i),
     "sdm_address": ([ctypes.POINTER(SdmShape), _i, _vp, _vp, _i, _i, _vp, _vp, _vp], _i),
     "sdm_sparse_update": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 10 + [_sz, _vp], _i),
+    "sdm_forward_train": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 15, _i),
+    "sdm_sparse_update_train": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 11, _i),
+    "sdm_backward_workspace_size": ([ctypes.POINTER(SdmShape)], _sz),
+    "sdm_backward": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 21 + [_sz, _vp], _i),
     "gdn_workspace_size": ([ctypes.POINTER(GdnShape)], _sz),
     "gdn_chunk_forward": ([ctypes.POINTER(GdnShape), _i, _i] + [_vp] * 9 + [_sz, _vp], _i),
     "gdn2_chunk_forward": ([ctypes.POINTER(GdnShape), _i] + [_vp] * 10 + [_sz, _vp], _i),

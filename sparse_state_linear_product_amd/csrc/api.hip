@@ -280,6 +280,191 @@ int sdm_decode_step(const sslp_sdm_shape* s, int dtype, int residual_mode, const
 }
 
 // ---------------------------------------------------------------------------
+// SDM training: forward that keeps the pre-write rows, backward by undoing writes
+// ---------------------------------------------------------------------------
+
+static sslp::SdmUpdateArgs update_args(const sslp_sdm_shape* s, int dtype, int residual_mode,
+                                       const int32_t* idx_w, const float* wt_w,
+                                       const int32_t* idx_r, const float* wt_r, const void* v,
+                                       const float* alpha, const float* beta, float* M, void* y,
+                                       float* saved) {
+    sslp::SdmUpdateArgs a{};
+    a.B = s->B;
+    a.T = s->T;
+    a.H = s->H;
+    a.N = s->sqrtN * s->sqrtN;
+    a.dv = s->d_v;
+    a.W = s->W;
+    a.R = s->R;
+    a.dtype = dtype;
+    a.residual_mode = residual_mode;
+    a.idx_w = idx_w;
+    a.wt_w = wt_w;
+    a.idx_r = idx_r;
+    a.wt_r = wt_r;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.M = M;
+    a.y = y;
+    a.saved = saved;
+    return a;
+}
+
+static int check_common(const sslp_sdm_shape* s, bool need_k, int dtype, int residual_mode) {
+    if (int rc = check_sdm_shape(s, need_k)) return rc;
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE(residual_mode == SSLP_RESIDUAL_SHARED || residual_mode == SSLP_RESIDUAL_PER_SLOT,
+            SSLP_ERR_INVALID_ARG, "residual_mode must be 0 or 1 (got %d)", residual_mode);
+    return SSLP_OK;
+}
+
+size_t sdm_backward_workspace_size(const sslp_sdm_shape* s) {
+    if (check_sdm_shape(s, false) != SSLP_OK) return 0;
+    const size_t bth = (size_t)s->B * s->T * s->H;
+    return align_up(sslp::sdm_bwd_part_bytes(s->B, s->T, s->H, s->d_v, s->W, s->R)) +
+           align_up(bth * s->W * 4) + align_up(bth * s->R * 4);
+}
+
+int sdm_sparse_update_train(const sslp_sdm_shape* s, int dtype, int residual_mode,
+                            const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
+                            const float* wt_r, const void* v, const float* alpha,
+                            const float* beta, float* M, void* y, float* saved, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_common(s, false, dtype, residual_mode)) return rc;
+    REQUIRE_PTR(M);
+    if (s->T == 0) return SSLP_OK;
+    REQUIRE_PTR(idx_w);
+    REQUIRE_PTR(wt_w);
+    REQUIRE_PTR(idx_r);
+    REQUIRE_PTR(wt_r);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(alpha);
+    REQUIRE_PTR(beta);
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(saved);
+    const sslp::SdmUpdateArgs a = update_args(s, dtype, residual_mode, idx_w, wt_w, idx_r, wt_r, v,
+                                              alpha, beta, M, y, saved);
+    return hip_status(sslp::launch_sdm_update(a, (hipStream_t)stream), "sdm train update launch");
+}
+
+int sdm_forward_train(const sslp_sdm_shape* s, int dtype, int residual_mode, const void* sw1,
+                      const void* sw2, const void* sr1, const void* sr2, const void* v,
+                      const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
+                      float* wt_w, int32_t* idx_r, float* wt_r, float* saved, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_common(s, true, dtype, residual_mode)) return rc;
+    REQUIRE_PTR(M);
+    if (s->T == 0) return SSLP_OK;
+    REQUIRE_PTR(sw1);
+    REQUIRE_PTR(sw2);
+    REQUIRE_PTR(sr1);
+    REQUIRE_PTR(sr2);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(alpha);
+    REQUIRE_PTR(beta);
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(idx_w);
+    REQUIRE_PTR(wt_w);
+    REQUIRE_PTR(idx_r);
+    REQUIRE_PTR(wt_r);
+    REQUIRE_PTR(saved);
+    const long long P = (long long)s->B * s->T * s->H;
+    REQUIRE(P < (1ll << 31), SSLP_ERR_UNSUPPORTED, "too many problems");
+    hipStream_t st = (hipStream_t)stream;
+    if (int rc = hip_status(sslp::launch_sdm_address_pair((int)P, s->sqrtN, dtype, sw1, sw2, s->k_w,
+                                                          s->W, idx_w, wt_w, sr1, sr2, s->k_r,
+                                                          s->R, idx_r, wt_r, st),
+                            "sdm addressing launch"))
+        return rc;
+    const sslp::SdmUpdateArgs a = update_args(s, dtype, residual_mode, idx_w, wt_w, idx_r, wt_r, v,
+                                              alpha, beta, M, y, saved);
+    return hip_status(sslp::launch_sdm_update(a, st), "sdm train update launch");
+}
+
+int sdm_backward(const sslp_sdm_shape* s, int dtype, int residual_mode, const int32_t* idx_w,
+                 const float* wt_w, const int32_t* idx_r, const float* wt_r, const void* v,
+                 const float* alpha, const float* beta, float* M, const float* saved,
+                 const void* dy, float* dM, void* dv, float* dalpha, float* dbeta, float* dwt_w,
+                 float* dwt_r, float* dsw1, float* dsw2, float* dsr1, float* dsr2, void* workspace,
+                 size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_common(s, false, dtype, residual_mode)) return rc;
+    REQUIRE_PTR(M);
+    REQUIRE_PTR(dM);
+    if (s->T == 0) return SSLP_OK;
+    REQUIRE_PTR(idx_w);
+    REQUIRE_PTR(wt_w);
+    REQUIRE_PTR(idx_r);
+    REQUIRE_PTR(wt_r);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(alpha);
+    REQUIRE_PTR(beta);
+    REQUIRE_PTR(saved);
+    REQUIRE_PTR(dy);
+    REQUIRE_PTR(dv);
+    REQUIRE_PTR(dalpha);
+    REQUIRE_PTR(dbeta);
+    REQUIRE_ALIGNED(dwt_w);
+    REQUIRE_ALIGNED(dwt_r);
+    REQUIRE_ALIGNED(dsw1);
+    REQUIRE_ALIGNED(dsw2);
+    REQUIRE_ALIGNED(dsr1);
+    REQUIRE_ALIGNED(dsr2);
+    REQUIRE((dsw1 == nullptr) == (dsw2 == nullptr) && (dsr1 == nullptr) == (dsr2 == nullptr),
+            SSLP_ERR_INVALID_ARG, "score-half gradients come in pairs (dsw1 with dsw2, dsr1 with dsr2)");
+    REQUIRE_ALIGNED(workspace);
+    const size_t need = sdm_backward_workspace_size(s);
+    REQUIRE(workspace != nullptr && ws_bytes >= need, SSLP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    const long long P = (long long)s->B * s->T * s->H;
+    REQUIRE(P < (1ll << 31), SSLP_ERR_UNSUPPORTED, "too many problems");
+    char* ws = static_cast<char*>(workspace);
+    const size_t bp = align_up(sslp::sdm_bwd_part_bytes(s->B, s->T, s->H, s->d_v, s->W, s->R));
+    const size_t bw = align_up((size_t)P * s->W * 4);
+    sslp::SdmBwdArgs a{};
+    a.B = s->B;
+    a.T = s->T;
+    a.H = s->H;
+    a.N = s->sqrtN * s->sqrtN;
+    a.dv = s->d_v;
+    a.W = s->W;
+    a.R = s->R;
+    a.dtype = dtype;
+    a.residual_mode = residual_mode;
+    a.idx_w = idx_w;
+    a.wt_w = wt_w;
+    a.idx_r = idx_r;
+    a.wt_r = wt_r;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.M = M;
+    a.saved = saved;
+    a.dy = dy;
+    a.dM = dM;
+    a.dv_out = dv;
+    a.part = reinterpret_cast<float*>(ws);
+    a.dalpha = dalpha;
+    a.dbeta = dbeta;
+    a.dwt_w = dwt_w ? dwt_w : reinterpret_cast<float*>(ws + bp);
+    a.dwt_r = dwt_r ? dwt_r : reinterpret_cast<float*>(ws + bp + bw);
+    hipStream_t st = (hipStream_t)stream;
+    if (int rc = hip_status(sslp::launch_sdm_update_backward(a, st), "sdm backward launch"))
+        return rc;
+    if (dsw1)
+        if (int rc = hip_status(sslp::launch_sdm_address_backward((int)P, s->sqrtN, s->W, idx_w,
+                                                                  wt_w, a.dwt_w, dsw1, dsw2, st),
+                                "sdm address backward launch"))
+            return rc;
+    if (dsr1)
+        return hip_status(sslp::launch_sdm_address_backward((int)P, s->sqrtN, s->R, idx_r, wt_r,
+                                                            a.dwt_r, dsr1, dsr2, st),
+                          "sdm address backward launch");
+    return SSLP_OK;
+}
+
+// ---------------------------------------------------------------------------
 // GDN / KDA and SSE: argument checks (kernels follow)
 // ---------------------------------------------------------------------------
 static int check_gdn_shape(const sslp_gdn_shape* s) {

@@ -33,8 +33,42 @@ struct SdmUpdateArgs {
     const float* beta;
     float* M;
     void* y;
+    // [B,T,H,W,dv] fp32 or null: when set, each token's write rows as they were
+    // before the token (what a backward sweep restores); only the per-token
+    // kernel writes it
+    float* saved;
 };
 hipError_t launch_sdm_update(const SdmUpdateArgs& a, hipStream_t st);
+
+// ---- SDM backward (sdm_backward.hip) ----
+struct SdmBwdArgs {
+    int B, T, H, N, dv, W, R;
+    int dtype;          // 0 fp32, 1 bf16 for v, dy and dv
+    int residual_mode;  // 0 shared, 1 per-slot
+    const int32_t* idx_w;
+    const float* wt_w;
+    const int32_t* idx_r;
+    const float* wt_r;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    float* M;            // [B,H,N,dv] in: M_T; out: M_0 (writes undone)
+    const float* saved;  // [B,T,H,W,dv] pre-write rows
+    const void* dy;      // [B,T,H,dv]
+    float* dM;           // [B,H,N,dv] in: dL/dM_T; out: dL/dM_0
+    void* dv_out;        // [B,T,H,dv]
+    float* part;         // [B,T,H, nslice, 2 + W + R] per-slice partial sums
+    float* dalpha;       // [B,T,H]
+    float* dbeta;        // [B,T,H]
+    float* dwt_w;        // [B,T,H,W]
+    float* dwt_r;        // [B,T,H,R]
+};
+size_t sdm_bwd_part_bytes(int B, int T, int H, int dv, int W, int R);
+hipError_t launch_sdm_update_backward(const SdmBwdArgs& a, hipStream_t st);
+// gradient of the addressing softmax onto the score halves, P problems
+hipError_t launch_sdm_address_backward(int P, int sqrtN, int budget, const int32_t* idx,
+                                       const float* wt, const float* dwt, float* ds1, float* ds2,
+                                       hipStream_t st);
 
 // chunk-parallel recurrence (sdm_chunk.hip): supported shapes, workspace for
 // its per-chunk plans, and the launcher (plan kernel + apply kernel)

@@ -1,0 +1,264 @@
+// Backward of the Sparse Delta Memory recurrence by undoing writes, and of the
+// addressing softmax.
+//
+// Sparse Delta Memory slides: "Selected slots decay and update; other slots
+// persist" (Eqs. (3)-(5)), "A v1 inconsistency matters for reproducing the
+// update" (shared or per-slot residual) and the backup "Backup: undoing writes
+// avoids repeated full-table snapshots": the forward keeps each token's write
+// rows as they were before the token (T W d_v values per head instead of a
+// table per chunk); the backward walks the tokens in reverse with the table
+// at M_t and steps it back to M_{t-1} by restoring those rows, so on return
+// the table holds M_0 again.
+//
+// Per token t, in reverse, with G the running gradient of the table:
+//   read   y = sum_m e_m M_t[j_m]:  de_m = <M_t[j_m], dy>;  G[j_m] += e_m dy
+//   write  P_n = M_{t-1}[i_n] (saved), Mt_n = alpha P_n, G_n = G[i_n]:
+//     shared    r = v - sum_n w_n Mt_n;  dr = sum_n beta w_n G_n = dv;
+//               dbeta = sum_n w_n <G_n, r>;  dw_n = beta <G_n, r> - <Mt_n, dr>;
+//               dMt_n = G_n - w_n dr
+//     per-slot  dv = sum_n beta w_n G_n;  dbeta = sum_n w_n <G_n, v - Mt_n>;
+//               dw_n = beta <G_n, v - Mt_n>;  dMt_n = (1 - beta w_n) G_n
+//     dalpha = sum_n <P_n, dMt_n>;  G[i_n] = alpha dMt_n;  M[i_n] = P_n.
+//
+// Every operation on a d_v column is independent of the other columns except
+// the scalar gradients (dalpha, dbeta, dw, de), which are sums over d_v.  So
+// the sweep runs as in the per-token forward kernel: one wavefront per
+// 16-column slice of a (batch, head), lane (g, c) = (lane / 16, lane % 16)
+// owning column c of rows g, g + 4, ...; each wavefront writes its slice's
+// partial sums per token, and a second kernel adds the slices in a fixed order
+// (deterministic, no atomics).
+//
+// Ordering: all loads and stores of table and gradient rows are issued by the
+// one wavefront that owns the columns, in program order, so each token sees
+// the restores and gradient updates of the tokens after it.  Read slots must be
+// distinct within a token (the addressing guarantees it), as write slots are.
+#include "common.h"
+#include "kernels.h"
+
+namespace sslp {
+
+namespace {
+
+constexpr int kCols = 16;  // columns per wavefront
+
+SSLP_DEVICE int nslices(int dv) { return (dv + kCols - 1) / kCols; }
+
+template <typename io_t, int NL>
+__global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
+    const int nslice = nslices(a.dv);
+    const int slice = blockIdx.x % nslice;
+    const int bh = blockIdx.x / nslice;
+    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+    const int lane = threadIdx.x;
+    const int g = lane >> 4, c = lane & 15;
+    const int col = slice * kCols + c;
+    const bool colok = col < a.dv;
+    const int W = a.W, R = a.R;
+    const int NP = 2 + W + R;
+    const size_t tab0 = ((size_t)b * a.H + h) * (size_t)a.N * a.dv;
+    float* tab = a.M + tab0;
+    float* G = a.dM + tab0;
+    const io_t* vin = static_cast<const io_t*>(a.v);
+    const io_t* dyin = static_cast<const io_t*>(a.dy);
+    io_t* dvout = static_cast<io_t*>(a.dv_out);
+
+    for (int t = a.T - 1; t >= 0; --t) {
+        const size_t bth = ((size_t)b * a.T + t) * a.H + h;
+        const float al = a.alpha[bth];
+        const float be = a.beta[bth];
+        const float dyc = colok ? to_f32(dyin[bth * a.dv + col]) : 0.f;
+        const float vc = colok ? to_f32(vin[bth * a.dv + col]) : 0.f;
+        // ---- read after writing: de and the read contribution to G ----
+        float pe[NL];
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            const int m = g + 4 * r;
+            pe[r] = 0.f;
+            if (m < R && colok) {
+                const size_t off = (size_t)a.idx_r[bth * R + m] * a.dv + col;
+                const float e = a.wt_r[bth * R + m];
+                pe[r] = tab[off] * dyc;
+                G[off] += e * dyc;
+            }
+        }
+        wave_sync();
+        // ---- the write, from the saved rows ----
+        float P[NL], mt[NL], gn[NL], w[NL];
+        int slot[NL];
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            const int n = g + 4 * r;
+            const bool ok = n < W;
+            slot[r] = ok ? a.idx_w[bth * W + n] : 0;
+            w[r] = ok ? a.wt_w[bth * W + n] : 0.f;
+            const bool live = ok && colok;
+            P[r] = live ? a.saved[(bth * W + n) * a.dv + col] : 0.f;
+            gn[r] = live ? G[(size_t)slot[r] * a.dv + col] : 0.f;
+            mt[r] = al * P[r];
+        }
+        float vh = 0.f, dr = 0.f;
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            vh = fmaf(w[r], mt[r], vh);
+            dr = fmaf(be * w[r], gn[r], dr);
+        }
+        vh += __shfl_xor(vh, 16, 64);
+        vh += __shfl_xor(vh, 32, 64);
+        dr += __shfl_xor(dr, 16, 64);
+        dr += __shfl_xor(dr, 32, 64);
+        const bool shared = a.residual_mode == 0;
+        const float rres = vc - vh;
+        float pw[NL];
+        float pa = 0.f, pb = 0.f;
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            const float res = shared ? rres : vc - mt[r];
+            const float gres = gn[r] * res;
+            pw[r] = shared ? be * gres - mt[r] * dr : be * gres;
+            pb = fmaf(w[r], gres, pb);
+            const float dmt = shared ? gn[r] - w[r] * dr : (1.f - be * w[r]) * gn[r];
+            pa = fmaf(P[r], dmt, pa);
+            if (g + 4 * r < W && colok) {
+                const size_t off = (size_t)slot[r] * a.dv + col;
+                G[off] = al * dmt;
+                tab[off] = P[r];
+            }
+        }
+        if (g == 0 && colok) dvout[bth * a.dv + col] = from_f32<io_t>(dr);
+        // ---- partial sums over this slice's 16 columns ----
+#pragma unroll
+        for (int s = 1; s < 16; s <<= 1) {
+#pragma unroll
+            for (int r = 0; r < NL; ++r) {
+                pe[r] += __shfl_xor(pe[r], s, 64);
+                pw[r] += __shfl_xor(pw[r], s, 64);
+            }
+            pa += __shfl_xor(pa, s, 64);
+            pb += __shfl_xor(pb, s, 64);
+        }
+        pa += __shfl_xor(pa, 16, 64);
+        pa += __shfl_xor(pa, 32, 64);
+        pb += __shfl_xor(pb, 16, 64);
+        pb += __shfl_xor(pb, 32, 64);
+        float* pp = a.part + (bth * nslice + slice) * NP;
+        if (c == 0) {
+#pragma unroll
+            for (int r = 0; r < NL; ++r) {
+                if (g + 4 * r < W) pp[2 + g + 4 * r] = pw[r];
+                if (g + 4 * r < R) pp[2 + W + g + 4 * r] = pe[r];
+            }
+        }
+        if (lane == 0) {
+            pp[0] = pa;
+            pp[1] = pb;
+        }
+        wave_sync();
+    }
+}
+
+// Adds the slices' partial sums in slice order: one thread per (token, head, j).
+__global__ __launch_bounds__(256) void sdm_bwd_reduce_kernel(SdmBwdArgs a, long long total) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int W = a.W, R = a.R, NP = 2 + W + R;
+    const int nslice = nslices(a.dv);
+    const long long bth = i / NP;
+    const int j = (int)(i - bth * NP);
+    const float* pp = a.part + (size_t)bth * nslice * NP + j;
+    float s = 0.f;
+    for (int k = 0; k < nslice; ++k) s += pp[(size_t)k * NP];
+    if (j == 0) a.dalpha[bth] = s;
+    else if (j == 1) a.dbeta[bth] = s;
+    else if (j < 2 + W) a.dwt_w[bth * W + (j - 2)] = s;
+    else a.dwt_r[bth * R + (j - 2 - W)] = s;
+}
+
+// Softmax gradient with the selection fixed (slide "Product keys select
+// addresses without scoring every slot": weights are a softmax of the selected
+// candidate scores s1[a] + s2[b]):
+//   ds_m = wt_m (dwt_m - sum_j wt_j dwt_j);  ds1[a_m] += ds_m;  ds2[b_m] += ds_m.
+// One wavefront per problem; each output element adds its terms in rank order.
+constexpr int kAbWaves = 4;
+constexpr int kMaxBudget = 128;
+
+__global__ __launch_bounds__(64 * kAbWaves) void sdm_address_bwd_kernel(
+    int P, int sqrtN, int budget, const int32_t* __restrict__ idx, const float* __restrict__ wt,
+    const float* __restrict__ dwt, float* __restrict__ ds1, float* __restrict__ ds2) {
+    __shared__ float s_ds[kAbWaves][kMaxBudget];
+    __shared__ int s_a[kAbWaves][kMaxBudget], s_b[kAbWaves][kMaxBudget];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long long p = (long long)blockIdx.x * kAbWaves + wv;
+    if (p >= P) return;  // whole wavefronts leave together; no block barrier below
+    const int32_t* ip = idx + (size_t)p * budget;
+    const float* w = wt + (size_t)p * budget;
+    const float* dw = dwt + (size_t)p * budget;
+    float dot = 0.f;
+    for (int m = lane; m < budget; m += 64) dot = fmaf(w[m], dw[m], dot);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) dot += __shfl_xor(dot, s, 64);
+    for (int m = lane; m < budget; m += 64) {
+        const int n = ip[m];
+        s_ds[wv][m] = w[m] * (dw[m] - dot);
+        s_a[wv][m] = n / sqrtN;
+        s_b[wv][m] = n - (n / sqrtN) * sqrtN;
+    }
+    wave_sync();
+    for (int x = lane; x < sqrtN; x += 64) {
+        float g1 = 0.f, g2 = 0.f;
+        for (int m = 0; m < budget; ++m) {
+            const float d = s_ds[wv][m];
+            if (s_a[wv][m] == x) g1 += d;
+            if (s_b[wv][m] == x) g2 += d;
+        }
+        ds1[(size_t)p * sqrtN + x] = g1;
+        ds2[(size_t)p * sqrtN + x] = g2;
+    }
+}
+
+template <typename io_t>
+hipError_t dispatch_bwd(int NL, dim3 grid, hipStream_t st, const SdmBwdArgs& a) {
+    switch (NL) {
+        case 1: sdm_update_bwd_kernel<io_t, 1><<<grid, 64, 0, st>>>(a); break;
+        case 2: sdm_update_bwd_kernel<io_t, 2><<<grid, 64, 0, st>>>(a); break;
+        case 4: sdm_update_bwd_kernel<io_t, 4><<<grid, 64, 0, st>>>(a); break;
+        case 8: sdm_update_bwd_kernel<io_t, 8><<<grid, 64, 0, st>>>(a); break;
+        case 16: sdm_update_bwd_kernel<io_t, 16><<<grid, 64, 0, st>>>(a); break;
+        case 32: sdm_update_bwd_kernel<io_t, 32><<<grid, 64, 0, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t sdm_bwd_part_bytes(int B, int T, int H, int dv, int W, int R) {
+    return (size_t)B * T * H * ((dv + kCols - 1) / kCols) * (2 + W + R) * sizeof(float);
+}
+
+hipError_t launch_sdm_update_backward(const SdmBwdArgs& a, hipStream_t st) {
+    if (a.T <= 0 || a.B <= 0) return hipSuccess;
+    const int rows = a.W > a.R ? a.W : a.R;
+    int NL = 1;
+    while (4 * NL < rows) NL <<= 1;
+    const int nslice = (a.dv + kCols - 1) / kCols;
+    dim3 grid((unsigned)(a.B * a.H * nslice));
+    hipError_t e = a.dtype == 0 ? dispatch_bwd<float>(NL, grid, st, a)
+                                : dispatch_bwd<bf16_t>(NL, grid, st, a);
+    if (e != hipSuccess) return e;
+    const long long total = (long long)a.B * a.T * a.H * (2 + a.W + a.R);
+    sdm_bwd_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_sdm_address_backward(int P, int sqrtN, int budget, const int32_t* idx,
+                                       const float* wt, const float* dwt, float* ds1, float* ds2,
+                                       hipStream_t st) {
+    if (P <= 0) return hipSuccess;
+    if (budget < 1 || budget > kMaxBudget || sqrtN < 1) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)((P + kAbWaves - 1) / kAbWaves);
+    sdm_address_bwd_kernel<<<grid, 64 * kAbWaves, 0, st>>>(P, sqrtN, budget, idx, wt, dwt, ds1,
+                                                           ds2);
+    return hipGetLastError();
+}
+
+}  // namespace sslp

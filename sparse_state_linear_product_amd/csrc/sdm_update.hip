@@ -18,6 +18,11 @@
 // are issued by the same wavefront, whose memory operations complete in
 // program order, so token t+1 (and the read-after-write of token t) observe
 // token t's writes without a wait.
+//
+// For training, the kernel can also store each token's write rows as they were
+// before the token (the sparse update information from which a backward sweep
+// undoes the writes, Sparse Delta Memory slides, backup "Backup: undoing
+// writes avoids repeated full-table snapshots").
 #include "common.h"
 #include "kernels.h"
 
@@ -55,7 +60,9 @@ __global__ __launch_bounds__(64) void sdm_update_kernel(SdmUpdateArgs a) {
             const bool ok = n < W;
             slot[r] = ok ? a.idx_w[bth * W + n] : 0;
             w[r] = ok ? a.wt_w[bth * W + n] : 0.f;
-            mt[r] = (ok && colok) ? al * tab[(size_t)slot[r] * a.dv + col] : 0.f;
+            const float m0 = (ok && colok) ? tab[(size_t)slot[r] * a.dv + col] : 0.f;
+            if (a.saved != nullptr && ok && colok) a.saved[(bth * W + n) * a.dv + col] = m0;
+            mt[r] = al * m0;
         }
         const float vc = colok ? to_f32(vin[bth * a.dv + col]) : 0.f;
         if (a.residual_mode == 0) {
@@ -255,7 +262,8 @@ hipError_t dispatch_nl(int NL, dim3 grid, hipStream_t st, const SdmUpdateArgs& a
 
 hipError_t launch_sdm_update(const SdmUpdateArgs& a, hipStream_t st) {
     if (a.T <= 0 || a.B <= 0) return hipSuccess;
-    if (a.T == 1 && a.dv % 4 == 0 && a.W <= kDecMaxRows && a.R <= kDecMaxRows) {
+    if (a.T == 1 && a.saved == nullptr && a.dv % 4 == 0 && a.W <= kDecMaxRows &&
+        a.R <= kDecMaxRows) {
         const int nslice = (a.dv + kDecCols - 1) / kDecCols;
         dim3 grid((unsigned)(a.B * a.H * nslice));
         const int rows = a.W > a.R ? a.W : a.R;

@@ -96,6 +96,35 @@ def test_sdm_decode_requires_single_token():
     assert rc == _lib.SSLP_ERR_INVALID_ARG and "T == 1" in lib.sslp_last_error().decode()
 
 
+def test_sdm_training_entry_errors():
+    # argument checks of the training forward and the backward (no GPU call is made)
+    lib = _lib.lib()
+    s = _sdm()
+    # sdm_forward_train needs the addressing outputs and the saved rows
+    assert lib.sdm_forward_train(ctypes.byref(s), 0, 0, *([FAKE] * 13), None, None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+    assert "saved" in lib.sslp_last_error().decode()
+    assert lib.sdm_forward_train(ctypes.byref(s), 0, 0, *([FAKE] * 9), None, *([FAKE] * 4),
+                                 None) == _lib.SSLP_ERR_INVALID_ARG
+    assert lib.sdm_sparse_update_train(ctypes.byref(s), 0, 3, *([FAKE] * 10), None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+    need = lib.sdm_backward_workspace_size(ctypes.byref(s))
+    assert need > 0
+    ptrs = [FAKE] * 20
+    assert lib.sdm_backward(ctypes.byref(s), 0, 0, *ptrs, FAKE, need - 1, None) == \
+        _lib.SSLP_ERR_WORKSPACE
+    assert lib.sdm_backward(ctypes.byref(s), 0, 0, *ptrs, None, need, None) == \
+        _lib.SSLP_ERR_WORKSPACE
+    half = ptrs[:17] + [None] + ptrs[18:]  # dsw1 given, dsw2 NULL
+    assert lib.sdm_backward(ctypes.byref(s), 0, 0, *half, FAKE, need, None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+    assert "pairs" in lib.sslp_last_error().decode()
+    no_dy = ptrs[:9] + [None] + ptrs[10:]
+    assert lib.sdm_backward(ctypes.byref(s), 0, 0, *no_dy, FAKE, need, None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+    assert "dy" in lib.sslp_last_error().decode()
+
+
 def test_sdm_address_errors():
     lib = _lib.lib()
     s = _sdm()

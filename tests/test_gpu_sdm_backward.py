@@ -1,0 +1,179 @@
+"""GPU parity of the SDM training path (forward keeping pre-write rows, backward
+by undoing writes, addressing-softmax backward) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_state_linear_product_amd import workloads as wl
+from tests.helpers import TOL_BF16, TOL_FP32, announce, maxrel
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _cfg(B, T, H, sqrtN, d_v, k, W, R, dtype, seed):
+    return wl.SdmConfig("bwd", B, T, H, sqrtN, d_v, k, k, W, R, dtype, seed)
+
+
+def _upstream(cfg, T, seed, scale_dM=1.0):
+    g = torch.Generator().manual_seed(seed)
+    dy = torch.randn((cfg.B, T, cfg.H, cfg.d_v), generator=g).to(cfg.dtype)
+    dM = torch.randn((cfg.B, cfg.H, cfg.N, cfg.d_v), generator=g) * scale_dM
+    M0 = torch.randn((cfg.B, cfg.H, cfg.N, cfg.d_v), generator=g) * 0.5
+    return dy, dM, M0
+
+
+def _gpu_train(x, cfg, M0, dy, dM, mode):
+    import sparse_state_linear_product_amd as sslp
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    M = M0.clone().to(DEV)
+    y, ctx = sslp.sdm_forward_train(xd["sw1"], xd["sw2"], xd["sr1"], xd["sr2"], xd["v"],
+                                    xd["alpha"], xd["beta"], M, cfg.k_w, cfg.k_r, cfg.W, cfg.R,
+                                    residual_mode=mode)
+    M_T = M.clone()
+    g = sslp.sdm_backward(ctx, xd["v"], xd["alpha"], xd["beta"], M, dy.to(DEV),
+                          dM.clone().to(DEV), residual_mode=mode)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in g.items()}
+    out.update(y=y.cpu(), M_T=M_T.cpu(), M_restored=M.cpu(),
+               idx_w=ctx["idx_w"].cpu().numpy(), idx_r=ctx["idx_r"].cpu().numpy())
+    return out
+
+
+def _compare(got, ref, keys, tol, tag):
+    for k_got, k_ref in keys:
+        e = maxrel(got[k_got].double().numpy(), ref[k_ref])
+        print(f"  {tag} {k_got}: {e:.2e}", flush=True)
+        assert e <= tol, f"{tag} {k_got}: {e}"
+
+
+GRAD_KEYS = [("dv", "dv"), ("dalpha", "dalpha"), ("dbeta", "dbeta"), ("dwt_w", "dwt_w"),
+             ("dwt_r", "dwt_r"), ("dM", "dM0"), ("dsw1", "dsw1"), ("dsw2", "dsw2"),
+             ("dsr1", "dsr1"), ("dsr2", "dsr2")]
+
+
+def _check_full(cfg, mode, tol):
+    x = wl.sdm_inputs(cfg)
+    dy, dM, M0 = _upstream(cfg, cfg.T, cfg.seed + 1)
+    got = _gpu_train(x, cfg, M0, dy, dM, mode)
+    n = {k: wl.to_numpy_f32(v) for k, v in x.items()}
+    ref_f = oracle.sdm_forward(n["sw1"], n["sw2"], n["sr1"], n["sr2"], n["v"], n["alpha"],
+                               n["beta"], M0.double().numpy(), cfg.k_w, cfg.k_r, cfg.W, cfg.R,
+                               residual_mode=mode)
+    np.testing.assert_array_equal(got["idx_w"], ref_f["idx_w"])
+    np.testing.assert_array_equal(got["idx_r"], ref_f["idx_r"])
+    assert maxrel(got["y"].double().numpy(), ref_f["y"]) <= tol
+    # every write undone: the table is back to M0, bit for bit
+    assert torch.equal(got["M_restored"], M0)
+    ref = oracle.sdm_backward(n["sw1"], n["sw2"], n["sr1"], n["sr2"], n["v"], n["alpha"],
+                              n["beta"], M0.double().numpy(), cfg.k_w, cfg.k_r, cfg.W, cfg.R,
+                              wl.to_numpy_f32(dy).astype(np.float64), dM.double().numpy(),
+                              residual_mode=mode)
+    _compare(got, ref, GRAD_KEYS, tol, f"mode {mode}")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("T", [1, 37])
+def test_sdm_train_fp32_matches_oracle(mode, T):
+    announce(f"sdm_forward_train + sdm_backward fp32 mode={mode} T={T}")
+    # d_v = 40: two full 16-column slices and a ragged one of 8
+    _check_full(_cfg(2, T, 2, 16, 40, 8, 32, 32, torch.float32, 500 + T + mode), mode, TOL_FP32)
+
+
+def test_sdm_train_bf16_matches_oracle():
+    announce("sdm_forward_train + sdm_backward bf16")
+    _check_full(_cfg(1, 50, 2, 24, 64, 8, 32, 32, torch.bfloat16, 541), 0, TOL_BF16)
+
+
+def test_sdm_train_budget_shapes():
+    # W, R up to 64 (16 rows per lane), small d_v, unequal budgets
+    announce("sdm train W=64 R=8 d_v=4 and W=5 R=48")
+    _check_full(_cfg(1, 20, 1, 16, 4, 8, 64, 8, torch.float32, 551), 0, TOL_FP32)
+    _check_full(_cfg(1, 20, 2, 16, 20, 8, 5, 48, torch.float32, 552), 1, TOL_FP32)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_sdm_recurrence_backward_signed_weights(mode):
+    # the recurrence alone with raw signed weights and distinct slots, read and
+    # write sets overlapping within tokens
+    import sparse_state_linear_product_amd as sslp
+    announce(f"sdm_sparse_update_train + sdm_backward, signed weights, mode={mode}")
+    rng = np.random.default_rng(560 + mode)
+    B, T, H, N, dv, W, R = 1, 30, 2, 64, 24, 12, 10
+    perm = np.stack([rng.permutation(N)[:W + R] for _ in range(B * T * H)])
+    idx_w = perm[:, :W].reshape(B, T, H, W).astype(np.int32)
+    # half the read slots are also written by the same token
+    idx_r = np.concatenate([perm[:, :R // 2], perm[:, W:W + R - R // 2]], 1)
+    idx_r = idx_r.reshape(B, T, H, R).astype(np.int32)
+    wt_w = (rng.standard_normal((B, T, H, W)) * 0.4).astype(np.float32)
+    wt_r = rng.standard_normal((B, T, H, R)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    alpha = rng.uniform(0.7, 1.0, (B, T, H)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (B, T, H)).astype(np.float32)
+    M0 = rng.standard_normal((B, H, N, dv)).astype(np.float32)
+    dy = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    dM = rng.standard_normal((B, H, N, dv)).astype(np.float32)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    M = t(M0).clone()
+    y, saved = sslp.sdm_sparse_update_train(t(idx_w), t(wt_w), t(idx_r), t(wt_r), t(v), t(alpha),
+                                            t(beta), M, residual_mode=mode)
+    ctx = dict(idx_w=t(idx_w), wt_w=t(wt_w), idx_r=t(idx_r), wt_r=t(wt_r), saved=saved)
+    g = sslp.sdm_backward(ctx, t(v), t(alpha), t(beta), M, t(dy), t(dM).clone(),
+                          residual_mode=mode, score_grads=False)
+    torch.cuda.synchronize()
+    assert "dsw1" not in g
+    assert torch.equal(M.cpu(), torch.from_numpy(M0))
+    ref = oracle.sdm_recurrence_backward(idx_w, wt_w, idx_r, wt_r, v, alpha, beta,
+                                         M0.astype(np.float64), dy.astype(np.float64),
+                                         dM.astype(np.float64), residual_mode=mode)
+    got = {k: v.cpu() for k, v in g.items()}
+    _compare(got, ref, GRAD_KEYS[:6], TOL_FP32, f"signed mode {mode}")
+
+
+def test_sdm_backward_empty_sequence():
+    import sparse_state_linear_product_amd as sslp
+    announce("sdm_backward T=0")
+    B, H, N, dv, W, R = 1, 1, 16, 8, 4, 4
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt, device=DEV)
+    ctx = dict(idx_w=z(B, 0, H, W, dt=torch.int32), wt_w=z(B, 0, H, W),
+               idx_r=z(B, 0, H, R, dt=torch.int32), wt_r=z(B, 0, H, R), saved=z(B, 0, H, W, dv))
+    M = torch.randn((B, H, N, dv), device=DEV)
+    dM = torch.randn((B, H, N, dv), device=DEV)
+    M_in, dM_in = M.clone(), dM.clone()
+    g = sslp.sdm_backward(ctx, z(B, 0, H, dv), z(B, 0, H), z(B, 0, H), M, z(B, 0, H, dv), dM)
+    torch.cuda.synchronize()
+    assert torch.equal(M, M_in) and torch.equal(g["dM"], dM_in)
+
+
+def test_sdm_train_full_size_prefix_gradients():
+    # the 1.4B prefill layer (B=1, T=8192, H=2, N=57600, d_v=960, k=W=R=32) in
+    # the launch configuration the benchmark times.  With dy zero after the
+    # first 64 tokens and no final-table gradient, nothing flows back from the
+    # later tokens (every gradient there is exactly zero), so the first 64
+    # tokens' gradients equal those of the 64-token problem, which the oracle
+    # computes; the table must come back to M0 bit for bit.
+    import sparse_state_linear_product_amd as sslp
+    cfg = wl.SDM_14B
+    Tp = 64
+    announce(f"{cfg.name} training forward + backward, prefix {Tp} checked")
+    x = wl.sdm_inputs(cfg)
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    g0 = torch.Generator(device=DEV).manual_seed(cfg.seed + 5)
+    M = torch.randn((cfg.B, cfg.H, cfg.N, cfg.d_v), generator=g0, device=DEV) * 0.1
+    M0 = M.clone()
+    dy = torch.zeros((cfg.B, cfg.T, cfg.H, cfg.d_v), dtype=cfg.dtype, device=DEV)
+    dy[:, :Tp] = torch.randn((cfg.B, Tp, cfg.H, cfg.d_v), generator=g0, device=DEV).to(cfg.dtype)
+    y, ctx = sslp.sdm_forward_train(xd["sw1"], xd["sw2"], xd["sr1"], xd["sr2"], xd["v"],
+                                    xd["alpha"], xd["beta"], M, cfg.k_w, cfg.k_r, cfg.W, cfg.R)
+    g = sslp.sdm_backward(ctx, xd["v"], xd["alpha"], xd["beta"], M, dy)
+    torch.cuda.synchronize()
+    assert torch.equal(M, M0)
+    for k in ("dv", "dalpha", "dbeta", "dwt_w", "dwt_r", "dsw1", "dsw2", "dsr1", "dsr2"):
+        assert not torch.any(g[k][:, Tp:] != 0), k
+    n = {k: wl.to_numpy_f32(v[:, :Tp]) for k, v in x.items()}
+    ref = oracle.sdm_backward(n["sw1"], n["sw2"], n["sr1"], n["sr2"], n["v"], n["alpha"],
+                              n["beta"], M0.double().cpu().numpy(), cfg.k_w, cfg.k_r, cfg.W,
+                              cfg.R, dy[:, :Tp].double().cpu().numpy())
+    got = {k: (v[:, :Tp] if k != "dM" else v).cpu() for k, v in g.items()}
+    _compare(got, ref, GRAD_KEYS, TOL_BF16, "full-size prefix")
