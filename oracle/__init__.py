@@ -19,6 +19,8 @@ sdm_recurrence_backward  gradient of the recurrence by undoing writes (same
                 full-table snapshots")
 sdm_address_backward     gradient of the addressing softmax w.r.t. the halves
 sdm_backward    both, for the whole SDM forward
+norm_gate       RMS-Norm and output gate after the read (same slides, the
+                note after Eqs. (3)-(5))
 gdn             sequential Gated DeltaNet / KDA (Linear Attention
                 Architectures slides, Eqs. 14-20)
 gdn2            sequential GDN2: key-side erase b, value-side write w
@@ -77,6 +79,9 @@ def _load():
     lib.orc_sdm_address_backward.restype = ctypes.c_int
     lib.orc_sdm_address_backward.argtypes = [ctypes.c_int] * 3 + [_i32p, _f64p, _f64p, _f64p,
                                                                   _f64p]
+    lib.orc_norm_gate.restype = ctypes.c_int
+    lib.orc_norm_gate.argtypes = [ctypes.c_int, ctypes.c_int, _f32p, _Nullable(np.float32), _f32p,
+                                  ctypes.c_double, ctypes.c_int, _f64p]
     lib.orc_gdn.restype = ctypes.c_int
     lib.orc_gdn.argtypes = [ctypes.c_int] * 6 + [_f32p, _f32p, _f32p, _f32p, _f32p,
                                                  _Nullable(np.float64), _f64p, _f64p]
@@ -213,6 +218,26 @@ def sdm_backward(sw1, sw2, sr1, sr2, v, alpha, beta, M0, k_w, k_r, W, R, dy, dM=
     g["dsw1"], g["dsw2"] = sdm_address_backward(idx_w, wt_w, g["dwt_w"], sqrt_n)
     g["dsr1"], g["dsr2"] = sdm_address_backward(idx_r, wt_r, g["dwt_r"], sqrt_n)
     return g
+
+
+ACTS = {"none": 0, "silu": 1, "sigmoid": 2}
+
+
+def norm_gate(y, g, gamma, eps=1e-6, act="silu"):
+    """o = y / sqrt(mean(y^2) + eps) * gamma * act(g) over the last axis.
+
+    y, g: [..., d] (g may be None when act == "none"); gamma: [d].  float64 out."""
+    y = _f32(y)
+    d = y.shape[-1]
+    p = int(np.prod(y.shape[:-1])) if y.ndim > 1 else 1
+    g = None if g is None else _f32(g)
+    if g is None and act != "none":
+        raise ValueError("a gate is needed unless act == 'none'")
+    o = np.zeros(y.shape, np.float64)
+    rc = _load().orc_norm_gate(p, d, y, g, _f32(gamma), float(eps), ACTS[act], o)
+    if rc != 0:
+        raise ValueError("orc_norm_gate: invalid arguments")
+    return o
 
 
 def gdn(q, k, v, alpha, beta, S0=None, kda=False):

@@ -338,3 +338,39 @@ int orc_sdm_address_backward(int P, int sqrtN, int budget, const int32_t* idx, c
     }
     return 0;
 }
+
+/*
+ * The layer output after the read (Sparse Delta Memory slides, "Selected slots
+ * decay and update; other slots persist": the read is followed by RMS-Norm,
+ * output gating and head mixing).  The slides name the steps only; the plain
+ * reading taken here, per (token, head) row of d values:
+ *   o = y / sqrt(mean(y^2) + eps) * gamma * act(g)
+ * with gamma [d] a per-channel weight shared by the heads, g the gate
+ * pre-activation of the row, and act = SiLU (act 1, g * sigmoid(g)), the
+ * logistic sigmoid (act 2) or none (act 0, the factor is 1).  Head mixing is
+ * the dense output projection after this step and is not part of it.
+ *   y, g : [P, d];  gamma : [d];  o : [P, d] out.
+ * PARITY UNPINNED for the gate's activation choice (no printed value fixes
+ * it); the RMS normalisation itself is the textbook definition.
+ */
+int orc_norm_gate(int P, int d, const float* y, const float* g, const float* gamma, double eps,
+                  int act, double* o) {
+    if (P < 0 || d <= 0 || eps < 0.0 || act < 0 || act > 2) return -1;
+    for (int p = 0; p < P; ++p) {
+        const float* yr = y + (size_t)p * d;
+        const float* gr = g ? g + (size_t)p * d : NULL;
+        double ss = 0.0;
+        for (int c = 0; c < d; ++c) ss += (double)yr[c] * (double)yr[c];
+        double inv = 1.0 / sqrt(ss / d + eps);
+        for (int c = 0; c < d; ++c) {
+            double f = 1.0;
+            if (act != 0) {
+                double x = (double)gr[c];
+                double sg = 1.0 / (1.0 + exp(-x));
+                f = act == 1 ? x * sg : sg;
+            }
+            o[(size_t)p * d + c] = (double)yr[c] * inv * (double)gamma[c] * f;
+        }
+    }
+    return 0;
+}
