@@ -245,6 +245,19 @@ def bench_rows(args, torch, sslp, wl):
                           bytes_per_step=nbytes, steps=args.decode_steps)
     del M
     torch.cuda.empty_cache()
+    # read epilogue (RMS-Norm + SiLU output gate) on the 1.4B prefill read y [1,8192,2,960] bf16
+    cfg = wl.SDM_14B
+    gen = torch.Generator(device=dev).manual_seed(cfg.seed + 9)
+    yv = torch.randn((cfg.B, cfg.T, cfg.H, cfg.d_v), generator=gen, device=dev).to(cfg.dtype)
+    gv = torch.randn(yv.shape, generator=gen, device=dev).to(cfg.dtype)
+    gam = torch.rand((cfg.d_v,), generator=gen, device=dev) + 0.5
+    ov = torch.empty_like(yv)
+    ms = time_call(torch, lambda: sslp.sdm_norm_gate(yv, gam, gv, act="silu", o=ov), args.steps)
+    nbytes = 3 * yv.numel() * 2 + cfg.d_v * 4
+    rows["sdm_norm_gate_1p4b_T8192_H2_dv960"] = dict(
+        ms=round(ms, 4), gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+        hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_call=nbytes)
+    del yv, gv, gam, ov
     # SDM training on the 1.4B prefill layer: forward keeping the pre-write rows
     # (per-token kernel) and the backward by undoing writes (reverse sweep,
     # slice reduction, addressing-softmax backward)

@@ -163,6 +163,28 @@ int sdm_sparse_update(const sslp_sdm_shape* shape, int dtype, int residual_mode,
                       const float* wt_r, const void* v, const float* alpha, const float* beta,
                       float* M, void* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* output gate activation of sdm_norm_gate */
+#define SSLP_GATE_NONE 0
+#define SSLP_GATE_SILU 1    /* g * sigmoid(g) */
+#define SSLP_GATE_SIGMOID 2 /* 1 / (1 + exp(-g)) */
+
+/*
+ * sdm_norm_gate -- the layer output after the read (Sparse Delta Memory
+ * slides, "Selected slots decay and update; other slots persist": the read is
+ * followed by RMS-Norm, output gating and head mixing), RMS-Norm and gate in
+ * one pass over each row of d values:
+ *   o = y / sqrt(mean(y^2) + eps) * gamma * act(gate)
+ * Head mixing (the dense output projection) follows outside the library.
+ *   rows   number of rows (B*T*H for a [B,T,H,d] read), >= 0
+ *   d      row width (d_v), a multiple of 4, <= 4096
+ *   y      [rows, d] dtype;  gate [rows, d] dtype (NULL allowed with SSLP_GATE_NONE)
+ *   gamma  [d] fp32, shared by all rows;  eps >= 0
+ *   o      [rows, d] dtype out; may alias y (in place)
+ * The sum of squares, the scale and the gate are fp32.
+ */
+int sdm_norm_gate(long long rows, int d, int dtype, const void* y, const void* gate,
+                  const float* gamma, float eps, int act, void* o, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Sparse Delta Memory training: backward by undoing writes                 */
 /* ------------------------------------------------------------------------ */

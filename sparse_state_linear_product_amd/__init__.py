@@ -9,6 +9,7 @@ allocated with torch when the caller does not pass one.
 
 Functions (see include/sslp.h for the exact semantics):
   sdm_forward, sdm_decode_step, sdm_address, sdm_sparse_update   Sparse Delta Memory
+  sdm_norm_gate                                                  RMS-Norm + output gate after the read
   sdm_forward_train, sdm_sparse_update_train, sdm_backward       SDM training (undo writes)
   gdn_chunk_forward, gdn2_chunk_forward                          Gated DeltaNet / KDA / GDN2
   sse_forward (masking=True: sse_forward_masking), sse_decode_step  Sparse State Expansion
@@ -23,7 +24,7 @@ from ._lib import (DECAY_CHANNEL, DECAY_SCALAR, RESIDUAL_PER_SLOT, RESIDUAL_SHAR
 
 __all__ = ["sdm_forward", "sdm_decode_step", "sdm_address", "sdm_sparse_update",
            "sdm_forward_train", "sdm_sparse_update_train", "sdm_backward",
-           "sdm_backward_workspace_bytes",
+           "sdm_backward_workspace_bytes", "sdm_norm_gate",
            "gdn_chunk_forward", "gdn2_chunk_forward", "sse_forward", "sse_decode_step",
            "SslpError", "RESIDUAL_SHARED", "RESIDUAL_PER_SLOT", "DECAY_SCALAR", "DECAY_CHANNEL",
            "version"]
@@ -188,6 +189,28 @@ def sdm_sparse_update(idx_w, wt_w, idx_r, wt_r, v, alpha, beta, M, y=None,
                                  _stream(stream))
     check("sdm_sparse_update", rc)
     return y
+
+
+GATE_ACTS = {"none": 0, "silu": 1, "sigmoid": 2}
+
+
+def sdm_norm_gate(y, gamma, gate=None, eps=1e-6, act="silu", o=None, stream=None):
+    """RMS-Norm over the last axis of y, times gamma [d] fp32 and act(gate).
+
+    y, gate: [..., d] (same dtype, contiguous); returns o (y itself when o is y)."""
+    d = y.shape[-1]
+    rows = y.numel() // d if d else 0
+    _need(gamma, torch.float32, (d,), "gamma")
+    if gate is not None:
+        _need(gate, y.dtype, tuple(y.shape), "gate")
+    if o is None:
+        o = torch.empty_like(y)
+    _need(o, y.dtype, tuple(y.shape), "o")
+    _need(y, y.dtype, tuple(y.shape), "y")
+    rc = lib().sdm_norm_gate(rows, d, _dtype_code(y), _ptr(y), _ptr(gate), _ptr(gamma),
+                             float(eps), GATE_ACTS[act], _ptr(o), _stream(stream))
+    check("sdm_norm_gate", rc)
+    return o
 
 
 def sdm_backward_workspace_bytes(B, T, H, sqrtN, d_v, W, R):

@@ -464,6 +464,28 @@ int sdm_backward(const sslp_sdm_shape* s, int dtype, int residual_mode, const in
     return SSLP_OK;
 }
 
+int sdm_norm_gate(long long rows, int d, int dtype, const void* y, const void* gate,
+                  const float* gamma, float eps, int act, void* o, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE(rows >= 0 && d >= 1, SSLP_ERR_INVALID_ARG, "rows >= 0 and d >= 1 needed");
+    REQUIRE(d % 4 == 0 && d <= kMaxDv, SSLP_ERR_UNSUPPORTED,
+            "d must be a multiple of 4 and <= %d (got %d)", kMaxDv, d);
+    REQUIRE(act >= SSLP_GATE_NONE && act <= SSLP_GATE_SIGMOID, SSLP_ERR_INVALID_ARG,
+            "act must be SSLP_GATE_NONE, SSLP_GATE_SILU or SSLP_GATE_SIGMOID (got %d)", act);
+    REQUIRE(eps >= 0.f, SSLP_ERR_INVALID_ARG, "eps must be >= 0");
+    if (rows == 0) return SSLP_OK;
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(gamma);
+    REQUIRE_PTR(o);
+    if (act != SSLP_GATE_NONE) REQUIRE_PTR(gate);
+    REQUIRE_ALIGNED(gate);
+    REQUIRE(rows <= (1ll << 40), SSLP_ERR_UNSUPPORTED, "too many rows");
+    return hip_status(sslp::launch_norm_gate(rows, d, dtype, y, gate, gamma, eps, act, o,
+                                             (hipStream_t)stream),
+                      "sdm_norm_gate launch");
+}
+
 // ---------------------------------------------------------------------------
 // GDN / KDA and SSE: argument checks (kernels follow)
 // ---------------------------------------------------------------------------

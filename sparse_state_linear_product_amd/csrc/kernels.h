@@ -76,6 +76,11 @@ bool sdm_chunked_supported(int B, int T, int H, int W, int R, int dv, long long 
 size_t sdm_chunk_plan_bytes(int B, int T, int H);
 hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* plan, hipStream_t st);
 
+// RMS-Norm and output gate after the read (norm_gate.hip): rows x d, act 0 none,
+// 1 SiLU, 2 sigmoid; d a multiple of 4 up to 4096; o may alias y
+hipError_t launch_norm_gate(long long rows, int d, int dtype, const void* y, const void* g,
+                            const float* gamma, float eps, int act, void* o, hipStream_t st);
+
 // ---- Gated DeltaNet / KDA ----
 // per-chunk records of the state-independent part (workspace), and the
 // launcher (prep kernel over all chunks + state kernel over the chunk sequence)

@@ -125,6 +125,18 @@ def test_sdm_training_entry_errors():
     assert "dy" in lib.sslp_last_error().decode()
 
 
+def test_norm_gate_errors():
+    lib = _lib.lib()
+    ng = lib.sdm_norm_gate
+    assert ng(4, 6, 0, FAKE, FAKE, FAKE, 1e-6, 1, FAKE, None) == _lib.SSLP_ERR_UNSUPPORTED
+    assert ng(4, 8, 0, FAKE, FAKE, FAKE, 1e-6, 3, FAKE, None) == _lib.SSLP_ERR_INVALID_ARG
+    assert ng(4, 8, 0, FAKE, None, FAKE, 1e-6, 1, FAKE, None) == _lib.SSLP_ERR_INVALID_ARG
+    assert "gate" in lib.sslp_last_error().decode()
+    assert ng(4, 8, 0, FAKE, FAKE, FAKE, -1.0, 1, FAKE, None) == _lib.SSLP_ERR_INVALID_ARG
+    assert ng(4, 8, 2, FAKE, FAKE, FAKE, 1e-6, 1, FAKE, None) == _lib.SSLP_ERR_INVALID_ARG
+    assert ng(0, 8, 0, None, None, None, 1e-6, 1, None, None) == _lib.SSLP_OK
+
+
 def test_sdm_address_errors():
     lib = _lib.lib()
     s = _sdm()
