@@ -30,8 +30,12 @@
 //
 // Ordering: all loads and stores of table and gradient rows are issued by the
 // one wavefront that owns the columns, in program order, so each token sees
-// the restores and gradient updates of the tokens after it.  Read slots must be
-// distinct within a token (the addressing guarantees it), as write slots are.
+// the restores and gradient updates of the tokens after it.  Each token makes
+// one trip for its rows (M_t and G at the read slots, G at the write slots,
+// all requested together, with the next token's indices, weights and saved
+// rows already in flight); a write slot that the same token also reads gets
+// the read's contribution added in registers.  Read slots must be distinct
+// within a token (the addressing guarantees it), as write slots are.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,8 +47,40 @@ constexpr int kCols = 16;  // columns per wavefront
 
 SSLP_DEVICE int nslices(int dv) { return (dv + kCols - 1) / kCols; }
 
+// Everything a token needs that does not depend on the table (gates, indices,
+// weights, the saved rows, v and dy).  It is loaded one token ahead, from
+// clamped (always valid) addresses; out-of-range rows and columns are masked
+// where the values are used, so no load waits on a condition.
+template <int NL>
+struct BwdMeta {
+    float al, be, dyc, vc;
+    int sw[NL], sr[NL];
+    float w[NL], e[NL], P[NL];
+};
+
+template <typename io_t, int NL>
+SSLP_DEVICE void load_meta(BwdMeta<NL>& m, const SdmBwdArgs& a, size_t bth, int g, int colc) {
+    const io_t* vin = static_cast<const io_t*>(a.v);
+    const io_t* dyin = static_cast<const io_t*>(a.dy);
+    m.al = a.alpha[bth];
+    m.be = a.beta[bth];
+    m.dyc = to_f32(dyin[bth * a.dv + colc]);
+    m.vc = to_f32(vin[bth * a.dv + colc]);
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+        const int nw = min(g + 4 * r, a.W - 1), nr = min(g + 4 * r, a.R - 1);
+        m.sw[r] = a.idx_w[bth * a.W + nw];
+        m.w[r] = a.wt_w[bth * a.W + nw];
+        m.P[r] = a.saved[(bth * a.W + nw) * a.dv + colc];
+        m.sr[r] = a.idx_r[bth * a.R + nr];
+        m.e[r] = a.wt_r[bth * a.R + nr];
+    }
+}
+
 template <typename io_t, int NL>
 __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
+    __shared__ int s_rs[4 * NL];
+    __shared__ float s_re[4 * NL];
     const int nslice = nslices(a.dv);
     const int slice = blockIdx.x % nslice;
     const int bh = blockIdx.x / nslice;
@@ -53,47 +89,78 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
     const int g = lane >> 4, c = lane & 15;
     const int col = slice * kCols + c;
     const bool colok = col < a.dv;
+    const int colc = colok ? col : a.dv - 1;
     const int W = a.W, R = a.R;
     const int NP = 2 + W + R;
     const size_t tab0 = ((size_t)b * a.H + h) * (size_t)a.N * a.dv;
     float* tab = a.M + tab0;
     float* G = a.dM + tab0;
-    const io_t* vin = static_cast<const io_t*>(a.v);
-    const io_t* dyin = static_cast<const io_t*>(a.dy);
     io_t* dvout = static_cast<io_t*>(a.dv_out);
+    const bool shared = a.residual_mode == 0;
 
+    BwdMeta<NL> cur;
+    if (a.T > 0) load_meta<io_t, NL>(cur, a, ((size_t)b * a.T + (a.T - 1)) * a.H + h, g, colc);
     for (int t = a.T - 1; t >= 0; --t) {
         const size_t bth = ((size_t)b * a.T + t) * a.H + h;
-        const float al = a.alpha[bth];
-        const float be = a.beta[bth];
-        const float dyc = colok ? to_f32(dyin[bth * a.dv + col]) : 0.f;
-        const float vc = colok ? to_f32(vin[bth * a.dv + col]) : 0.f;
+        // ---- one trip for every row the token touches: M_t and G at the read
+        //      slots, G at the write slots ----
+        float mr[NL], gr[NL], gw[NL];
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            mr[r] = tab[(size_t)cur.sr[r] * a.dv + colc];
+            gr[r] = G[(size_t)cur.sr[r] * a.dv + colc];
+            gw[r] = G[(size_t)cur.sw[r] * a.dv + colc];
+        }
+        // the next token's table-independent data, in flight meanwhile
+        BwdMeta<NL> nxt;
+        load_meta<io_t, NL>(nxt, a, ((size_t)b * a.T + (t > 0 ? t - 1 : 0)) * a.H + h, g, colc);
+        // ---- a write slot that is also read by this token: its G must include
+        //      the read's e dy.  Lane (g, c) checks its write rows against read
+        //      rows c, c + 16, ...; the 16 lanes of the row group add up ----
+        if (c == 0) {
+#pragma unroll
+            for (int r = 0; r < NL; ++r)
+                if (g + 4 * r < R) {
+                    s_rs[g + 4 * r] = cur.sr[r];
+                    s_re[g + 4 * r] = cur.e[r];
+                }
+        }
+        wave_sync();
+        float fix[NL];
+#pragma unroll
+        for (int r = 0; r < NL; ++r) fix[r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < (4 * NL + 15) / 16; ++j) {
+            const int m = c + 16 * j;
+            if (m < R) {
+                const int sm = s_rs[m];
+                const float em = s_re[m];
+#pragma unroll
+                for (int r = 0; r < NL; ++r) fix[r] += sm == cur.sw[r] ? em : 0.f;
+            }
+        }
+#pragma unroll
+        for (int s = 1; s < 16; s <<= 1)
+#pragma unroll
+            for (int r = 0; r < NL; ++r) fix[r] += __shfl_xor(fix[r], s, 64);
+        const float dyc = colok ? cur.dyc : 0.f, vc = colok ? cur.vc : 0.f;
+        const float al = cur.al, be = cur.be;
         // ---- read after writing: de and the read contribution to G ----
         float pe[NL];
 #pragma unroll
         for (int r = 0; r < NL; ++r) {
-            const int m = g + 4 * r;
-            pe[r] = 0.f;
-            if (m < R && colok) {
-                const size_t off = (size_t)a.idx_r[bth * R + m] * a.dv + col;
-                const float e = a.wt_r[bth * R + m];
-                pe[r] = tab[off] * dyc;
-                G[off] += e * dyc;
-            }
+            const bool ok = g + 4 * r < R && colok;
+            pe[r] = ok ? mr[r] * dyc : 0.f;
+            if (ok) G[(size_t)cur.sr[r] * a.dv + col] = gr[r] + cur.e[r] * dyc;
         }
-        wave_sync();
         // ---- the write, from the saved rows ----
         float P[NL], mt[NL], gn[NL], w[NL];
-        int slot[NL];
 #pragma unroll
         for (int r = 0; r < NL; ++r) {
-            const int n = g + 4 * r;
-            const bool ok = n < W;
-            slot[r] = ok ? a.idx_w[bth * W + n] : 0;
-            w[r] = ok ? a.wt_w[bth * W + n] : 0.f;
-            const bool live = ok && colok;
-            P[r] = live ? a.saved[(bth * W + n) * a.dv + col] : 0.f;
-            gn[r] = live ? G[(size_t)slot[r] * a.dv + col] : 0.f;
+            const bool live = g + 4 * r < W && colok;
+            w[r] = g + 4 * r < W ? cur.w[r] : 0.f;
+            P[r] = live ? cur.P[r] : 0.f;
+            gn[r] = live ? gw[r] + fix[r] * dyc : 0.f;
             mt[r] = al * P[r];
         }
         float vh = 0.f, dr = 0.f;
@@ -106,7 +173,6 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
         vh += __shfl_xor(vh, 32, 64);
         dr += __shfl_xor(dr, 16, 64);
         dr += __shfl_xor(dr, 32, 64);
-        const bool shared = a.residual_mode == 0;
         const float rres = vc - vh;
         float pw[NL];
         float pa = 0.f, pb = 0.f;
@@ -119,7 +185,7 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
             const float dmt = shared ? gn[r] - w[r] * dr : (1.f - be * w[r]) * gn[r];
             pa = fmaf(P[r], dmt, pa);
             if (g + 4 * r < W && colok) {
-                const size_t off = (size_t)slot[r] * a.dv + col;
+                const size_t off = (size_t)cur.sw[r] * a.dv + col;
                 G[off] = al * dmt;
                 tab[off] = P[r];
             }
@@ -153,6 +219,7 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
             pp[1] = pb;
         }
         wave_sync();
+        cur = nxt;
     }
 }
 
