@@ -14,10 +14,13 @@
 // column c of the write rows n = g, g+4, ... and read rows m = g, g+4, ...;
 // row sums are reduced across the four lane groups with two shuffles.
 //
+// Each token makes one trip to the table: its write and read rows are
+// requested together, while the next token's gates, indices and weights are
+// already in flight.  A read slot that the token also writes takes the
+// updated value from LDS (write slots are distinct within a token).
 // Ordering: every store to the table and every later load of the same row
 // are issued by the same wavefront, whose memory operations complete in
-// program order, so token t+1 (and the read-after-write of token t) observe
-// token t's writes without a wait.
+// program order, so token t+1 observes token t's writes without a wait.
 //
 // For training, the kernel can also store each token's write rows as they were
 // before the token (the sparse update information from which a backward sweep
@@ -32,39 +35,74 @@ namespace {
 
 constexpr int kCols = 16;  // columns per wavefront
 
+// What a token needs that does not depend on the table (gates, v, indices and
+// weights), loaded one token ahead from clamped (always valid) addresses;
+// rows past W or R and columns past d_v are masked where the values are used,
+// so no load waits on a condition.
+template <int NL>
+struct FwdMeta {
+    float al, be, vc;
+    int sw[NL], sr[NL];
+    float w[NL], e[NL];
+};
+
+template <typename io_t, int NL>
+SSLP_DEVICE void load_fwd_meta(FwdMeta<NL>& m, const SdmUpdateArgs& a, size_t bth, int g,
+                               int colc) {
+    m.al = a.alpha[bth];
+    m.be = a.beta[bth];
+    m.vc = to_f32(static_cast<const io_t*>(a.v)[bth * a.dv + colc]);
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+        const int nw = min(g + 4 * r, a.W - 1), nr = min(g + 4 * r, a.R - 1);
+        m.sw[r] = a.idx_w[bth * a.W + nw];
+        m.w[r] = a.wt_w[bth * a.W + nw];
+        m.sr[r] = a.idx_r[bth * a.R + nr];
+        m.e[r] = a.wt_r[bth * a.R + nr];
+    }
+}
+
 template <typename io_t, int NL>
 __global__ __launch_bounds__(64) void sdm_update_kernel(SdmUpdateArgs a) {
+    __shared__ int s_ws[4 * NL];             // the token's write slots
+    __shared__ float s_new[4 * NL][kCols];   // their updated values, this slice's columns
     const int nslice = (a.dv + kCols - 1) / kCols;
     const int slice = blockIdx.x % nslice;
     const int bh = blockIdx.x / nslice;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const int lane = threadIdx.x;
-    const int g = lane >> 4;
-    const int col = slice * kCols + (lane & 15);
+    const int g = lane >> 4, c = lane & 15;
+    const int col = slice * kCols + c;
     const bool colok = col < a.dv;
+    const int colc = colok ? col : a.dv - 1;
     const int W = a.W, R = a.R;
     float* tab = a.M + ((size_t)b * a.H + h) * (size_t)a.N * a.dv;
-    const io_t* vin = static_cast<const io_t*>(a.v);
     io_t* yout = static_cast<io_t*>(a.y);
 
+    FwdMeta<NL> cur;
+    if (a.T > 0) load_fwd_meta<io_t, NL>(cur, a, ((size_t)b * a.T) * a.H + h, g, colc);
     for (int t = 0; t < a.T; ++t) {
         const size_t bth = ((size_t)b * a.T + t) * a.H + h;
-        const float al = a.alpha[bth];
-        const float be = a.beta[bth];
-        // gather the write rows and decay them (Eq. 3)
-        float mt[NL], w[NL];
-        int slot[NL];
+        // ---- one trip for the write and the read rows ----
+        float m0[NL], mr[NL];
 #pragma unroll
         for (int r = 0; r < NL; ++r) {
-            const int n = g + 4 * r;
-            const bool ok = n < W;
-            slot[r] = ok ? a.idx_w[bth * W + n] : 0;
-            w[r] = ok ? a.wt_w[bth * W + n] : 0.f;
-            const float m0 = (ok && colok) ? tab[(size_t)slot[r] * a.dv + col] : 0.f;
-            if (a.saved != nullptr && ok && colok) a.saved[(bth * W + n) * a.dv + col] = m0;
-            mt[r] = al * m0;
+            m0[r] = tab[(size_t)cur.sw[r] * a.dv + colc];
+            mr[r] = tab[(size_t)cur.sr[r] * a.dv + colc];
         }
-        const float vc = colok ? to_f32(vin[bth * a.dv + col]) : 0.f;
+        FwdMeta<NL> nxt;
+        load_fwd_meta<io_t, NL>(nxt, a, ((size_t)b * a.T + (t + 1 < a.T ? t + 1 : t)) * a.H + h,
+                                g, colc);
+        const float al = cur.al, be = cur.be, vc = colok ? cur.vc : 0.f;
+        // ---- decay the write rows (Eq. 3) and update them (Eq. 4 / figure form) ----
+        float mt[NL], w[NL], nv[NL];
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            const bool live = g + 4 * r < W && colok;
+            w[r] = g + 4 * r < W ? cur.w[r] : 0.f;
+            if (a.saved != nullptr && live) a.saved[(bth * W + g + 4 * r) * a.dv + col] = m0[r];
+            mt[r] = live ? al * m0[r] : 0.f;
+        }
         if (a.residual_mode == 0) {
             // shared prediction v_hat = sum_n wt_n M~[i_n]
             float acc = 0.f;
@@ -74,36 +112,53 @@ __global__ __launch_bounds__(64) void sdm_update_kernel(SdmUpdateArgs a) {
             acc += __shfl_xor(acc, 32, 64);
             const float res = vc - acc;
 #pragma unroll
-            for (int r = 0; r < NL; ++r) {
-                const int n = g + 4 * r;
-                if (n < W && colok)
-                    tab[(size_t)slot[r] * a.dv + col] = fmaf(be * w[r], res, mt[r]);
-            }
+            for (int r = 0; r < NL; ++r) nv[r] = fmaf(be * w[r], res, mt[r]);
         } else {
             // per-slot residual v - M~[i] (Eq. 4 as printed)
 #pragma unroll
-            for (int r = 0; r < NL; ++r) {
-                const int n = g + 4 * r;
-                if (n < W && colok)
-                    tab[(size_t)slot[r] * a.dv + col] = fmaf(be * w[r], vc - mt[r], mt[r]);
-            }
+            for (int r = 0; r < NL; ++r) nv[r] = fmaf(be * w[r], vc - mt[r], mt[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < NL; ++r)
+            if (g + 4 * r < W && colok) tab[(size_t)cur.sw[r] * a.dv + col] = nv[r];
+        // ---- read after writing (Eq. 5): a read slot that this token writes
+        //      takes the updated value.  Lane (g, c) checks its read rows
+        //      against write rows c, c + 16, ...; the row group combines ----
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            if (g + 4 * r < W) s_new[g + 4 * r][c] = nv[r];
+            if (c == 0 && g + 4 * r < W) s_ws[g + 4 * r] = cur.sw[r];
         }
         wave_sync();
-        // read after writing (Eq. 5)
+        int hit[NL];
+#pragma unroll
+        for (int r = 0; r < NL; ++r) hit[r] = 0;
+#pragma unroll
+        for (int j = 0; j < (4 * NL + 15) / 16; ++j) {
+            const int n = c + 16 * j;
+            if (n < W) {
+                const int sn = s_ws[n];
+#pragma unroll
+                for (int r = 0; r < NL; ++r) hit[r] = sn == cur.sr[r] ? n + 1 : hit[r];
+            }
+        }
+#pragma unroll
+        for (int s = 1; s < 16; s <<= 1)
+#pragma unroll
+            for (int r = 0; r < NL; ++r) hit[r] = max(hit[r], __shfl_xor(hit[r], s, 64));
         float acc = 0.f;
 #pragma unroll
         for (int r = 0; r < NL; ++r) {
-            const int m = g + 4 * r;
-            if (m < R) {
-                const int s = a.idx_r[bth * R + m];
-                const float wr = a.wt_r[bth * R + m];
-                if (colok) acc = fmaf(wr, tab[(size_t)s * a.dv + col], acc);
+            if (g + 4 * r < R) {
+                const float m = hit[r] > 0 ? s_new[hit[r] - 1][c] : mr[r];
+                acc = fmaf(cur.e[r], m, acc);
             }
         }
         acc += __shfl_xor(acc, 16, 64);
         acc += __shfl_xor(acc, 32, 64);
         if (g == 0 && colok) yout[bth * a.dv + col] = from_f32<io_t>(acc);
         wave_sync();
+        cur = nxt;
     }
 }
 
