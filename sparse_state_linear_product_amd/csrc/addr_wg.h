@@ -1,0 +1,192 @@
+// Product-key addressing of one problem by a group of 256 threads (slides
+// "Sparse Delta Memory: Scaling the State of Linear RNNs through Sparsity",
+// "Product keys select addresses without scoring every slot"): the steps of
+// the latency-oriented workgroup variant, as device functions so that the
+// standalone addressing kernel and the fused decode kernel run the same code.
+//
+// Ranking is (fp32 score desc, index asc) as a 64-bit key (common.h):
+//   1. per-half top-k: each wavefront sorts its 64 keys of each half in
+//      registers and keeps its top k; the half's top k is among those 4k keys
+//      and is ranked by counting (keys are distinct; padding keys are 0, below
+//      every key, and rank at or past k because sqrtN >= k);
+//   2. the dominance set D = {(i, j) : (i+1)(j+1) <= budget}, ranked by
+//      counting; tau = its budget-th key;
+//   3. F = #{k^2 candidates with key >= tau}; F == budget proves D's
+//      top-budget is the answer, else all k^2 candidates are ranked by
+//      counting (wg_addr_rank_all, the rare path of rounding ties);
+//   4. softmax over the selected scores.
+// Every function contains block-wide barriers: all threads of the workgroup
+// call it, each 256-thread group on its own problem and shared memory.
+// Limits: sqrtN <= 256, k <= 64, budget <= 64, |D| <= 256.
+#pragma once
+
+#include "common.h"
+
+namespace sslp {
+
+constexpr int kAddrGroup = 256;  // threads per addressing problem
+
+struct WgAddrSmem {
+    uint64_t top[2][kAddrGroup];  // per half: each wave's sorted top-k of its 64 keys
+    float hsc[2][64];
+    int hix[2][64];
+    uint64_t cand[4096];  // D, or all k^2 candidates on the rare path
+    uint64_t sel[64];
+    uint64_t tau;
+    int F;
+    int drow[kAddrGroup], doff[65];  // D: row of each entry, first entry of each row
+};
+
+struct WgAddrProblem {
+    const void* s1;  // [.., sqrtN] half scores of this problem
+    const void* s2;
+    int n, k, budget, nD;
+};
+
+inline int address_set_size_host(int k, int budget) {
+    int nD = 0;
+    for (int i = 0; i < k; ++i) {
+        int c = budget / (i + 1);
+        nD += c < k ? c : k;
+    }
+    return nD;
+}
+
+inline bool wg_address_fits(int sqrtN, int k, int budget) {
+    return sqrtN <= kAddrGroup && k <= 64 && budget <= 64 &&
+           address_set_size_host(k, budget) <= kAddrGroup;
+}
+
+// steps 1-3 up to F (ends with a barrier: sm.F is then valid for every thread)
+template <typename in_t>
+SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm) {
+    const int lane = t & 63, wv = t >> 6;
+    const int n = pr.n, k = pr.k, budget = pr.budget, nD = pr.nD;
+    const in_t* h1 = static_cast<const in_t*>(pr.s1);
+    const in_t* h2 = static_cast<const in_t*>(pr.s2);
+    uint64_t x1[1] = {0ull}, x2[1] = {0ull};
+    if (t < n) {
+        x1[0] = make_key(to_f32(h1[t]), (uint32_t)t);
+        x2[0] = make_key(to_f32(h2[t]), (uint32_t)t);
+    }
+    if (wv == 0) {
+        // D row by row: row i has min(budget / (i+1), k) entries; lane i
+        // writes its row's entries of the map
+        int c = lane < k ? budget / (lane + 1) : 0;
+        c = c < k ? c : k;
+        int incl = c;
+#pragma unroll
+        for (int s = 1; s < 64; s <<= 1) {
+            const int o = __shfl_up(incl, s, 64);
+            if (lane >= s) incl += o;
+        }
+        const int off = incl - c;
+        if (lane < k) sm.doff[lane] = off;
+        for (int e = 0; e < c; ++e) sm.drow[off + e] = lane;
+    }
+    if (t == 0) {
+        sm.F = 0;
+        sm.tau = 0ull;  // below every key: only read if D had fewer than budget entries
+    }
+    bitonic_sort_desc<1>(x1, lane);
+    bitonic_sort_desc<1>(x2, lane);
+    sm.top[0][t] = lane < k ? x1[0] : 0ull;
+    sm.top[1][t] = lane < k ? x2[0] : 0ull;
+    __syncthreads();
+    for (int x = t; x < 8 * k; x += kAddrGroup) {
+        const int hh = x >= 4 * k ? 1 : 0;
+        const int q = x - hh * 4 * k;
+        const uint64_t key = sm.top[hh][(q / k) * 64 + (q - (q / k) * k)];
+        int r = 0;
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const uint64_t* lst = &sm.top[hh][w2 * 64];
+            for (int u = 0; u < k; u += 8) {
+                uint64_t ku[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ku[e] = lst[u + e];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) r += ku[e] > key;
+            }
+        }
+        if (r < k) {
+            sm.hsc[hh][r] = key_score(key);
+            sm.hix[hh][r] = (int)key_index(key);
+        }
+    }
+    __syncthreads();
+    // 2. D ranked by counting; tau = its budget-th key
+    uint64_t dkey = 0ull;
+    if (t < nD) {
+        const int i = sm.drow[t];
+        const int j = t - sm.doff[i];
+        const float sum = sm.hsc[0][i] + sm.hsc[1][j];  // one fp32 RNE add
+        dkey = make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + (uint32_t)sm.hix[1][j]);
+    }
+    sm.cand[t] = dkey;  // every entry is written; those past nD hold key 0 (below all keys)
+    __syncthreads();
+    if (t < nD) {
+        int r = 0;
+        for (int u = 0; u < nD; u += 8) {  // entries past nD are 0
+            uint64_t ku[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ku[e] = sm.cand[u + e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r += ku[e] > dkey;
+        }
+        if (r < budget) sm.sel[r] = dkey;
+        if (r == budget - 1) sm.tau = dkey;
+    }
+    __syncthreads();
+    // 3. exact count of all k^2 candidates at or above tau
+    const uint64_t tau = sm.tau;
+    const int kk = k * k;
+    int F = 0;
+    for (int x = t; x < kk; x += kAddrGroup) {
+        const int i = x / k, j = x - (x / k) * k;
+        const float sum = sm.hsc[0][i] + sm.hsc[1][j];
+        F += make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + (uint32_t)sm.hix[1][j]) >= tau;
+    }
+    F = (int)wave_sum((float)F);
+    if (lane == 0) atomicAdd(&sm.F, F);
+    __syncthreads();
+}
+
+// the rare path: rank all k^2 candidates (three barriers)
+SSLP_DEVICE void wg_addr_rank_all(const WgAddrProblem& pr, int t, WgAddrSmem& sm) {
+    const int n = pr.n, k = pr.k, budget = pr.budget, kk = k * k;
+    __syncthreads();
+    for (int x = t; x < kk; x += kAddrGroup) {
+        const int i = x / k, j = x - (x / k) * k;
+        const float sum = sm.hsc[0][i] + sm.hsc[1][j];
+        sm.cand[x] = make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + (uint32_t)sm.hix[1][j]);
+    }
+    __syncthreads();
+    for (int x = t; x < kk; x += kAddrGroup) {
+        const uint64_t kx = sm.cand[x];
+        int r = 0;
+        for (int y = 0; y < kk; ++y) r += sm.cand[y] > kx;
+        if (r < budget) sm.sel[r] = kx;
+    }
+    __syncthreads();
+}
+
+// 4. softmax over the selected scores (rank 0 holds the maximum), by the
+// group's first wavefront; either output pair may be null
+SSLP_DEVICE void wg_addr_softmax(const WgAddrProblem& pr, int t, const WgAddrSmem& sm,
+                                 int32_t* idx, float* wt, int32_t* idx2, float* wt2) {
+    if (t < 64) {
+        const int budget = pr.budget;
+        const float smax = key_score(sm.sel[0]);
+        const float w = t < budget ? __expf(key_score(sm.sel[t]) - smax) : 0.f;
+        const float z = wave_sum(w);
+        if (t < budget) {
+            const int32_t slot = (int32_t)key_index(sm.sel[t]);
+            if (idx) idx[t] = slot;
+            if (wt) wt[t] = w / z;
+            if (idx2) idx2[t] = slot;
+            if (wt2) wt2[t] = w / z;
+        }
+    }
+}
+
+}  // namespace sslp

@@ -221,6 +221,35 @@ static int sdm_run(const sslp_sdm_shape* s, int T, int dtype, int residual_mode,
             "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     const long long P = (long long)s->B * T * s->H;
     REQUIRE(P < (1ll << 31), SSLP_ERR_UNSUPPORTED, "too many problems");
+    hipStream_t st = (hipStream_t)stream;
+    if (T == 1 && sslp::sdm_decode_fused_fits(s->sqrtN, s->d_v, s->k_w, s->W, s->k_r, s->R)) {
+        // one token per sequence: addressing and update in one launch
+        sslp::SdmDecodeArgs d{};
+        d.P = (int)P;
+        d.sqrtN = s->sqrtN;
+        d.N = s->sqrtN * s->sqrtN;
+        d.dv = s->d_v;
+        d.dtype = dtype;
+        d.residual_mode = residual_mode;
+        d.s1[0] = sw1;
+        d.s2[0] = sw2;
+        d.s1[1] = sr1;
+        d.s2[1] = sr2;
+        d.idx[0] = idx_w;
+        d.wt[0] = wt_w;
+        d.idx[1] = idx_r;
+        d.wt[1] = wt_r;
+        d.k[0] = s->k_w;
+        d.k[1] = s->k_r;
+        d.budget[0] = s->W;
+        d.budget[1] = s->R;
+        d.v = v;
+        d.alpha = alpha;
+        d.beta = beta;
+        d.M = M;
+        d.y = y;
+        return hip_status(sslp::launch_sdm_decode_fused(d, st), "sdm decode launch");
+    }
     // addressing outputs: caller buffers when given, else workspace
     char* ws = static_cast<char*>(workspace);
     const size_t bw = align_up((size_t)P * s->W * 4), br = align_up((size_t)P * s->R * 4);
@@ -228,7 +257,6 @@ static int sdm_run(const sslp_sdm_shape* s, int T, int dtype, int residual_mode,
     float* ww = wt_w ? wt_w : reinterpret_cast<float*>(ws + bw);
     int32_t* ir = idx_r ? idx_r : reinterpret_cast<int32_t*>(ws + 2 * bw);
     float* wr = wt_r ? wt_r : reinterpret_cast<float*>(ws + 2 * bw + br);
-    hipStream_t st = (hipStream_t)stream;
     if (int rc = hip_status(sslp::launch_sdm_address_pair((int)P, s->sqrtN, dtype, sw1, sw2, s->k_w,
                                                           s->W, iw, ww, sr1, sr2, s->k_r, s->R, ir,
                                                           wr, st),

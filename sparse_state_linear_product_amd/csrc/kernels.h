@@ -40,6 +40,27 @@ struct SdmUpdateArgs {
 };
 hipError_t launch_sdm_update(const SdmUpdateArgs& a, hipStream_t st);
 
+// ---- SDM decode step in one launch (sdm_decode.hip): addressing of both sets
+//      and the update / read of one token per (sequence, head) ----
+struct SdmDecodeArgs {
+    int P;  // B * H problems (one token each)
+    int sqrtN, N, dv;
+    int dtype;          // 0 fp32, 1 bf16 for the score halves, v and y
+    int residual_mode;  // 0 shared, 1 per-slot
+    const void* s1[2];  // [P, sqrtN] halves of the write (0) and read (1) scores
+    const void* s2[2];
+    int32_t* idx[2];    // [P, W] / [P, R] optional copies of the selections
+    float* wt[2];
+    int k[2], budget[2], nD[2];  // nD is filled in by the launcher
+    const void* v;      // [P, dv]
+    const float* alpha;  // [P]
+    const float* beta;
+    float* M;           // [P, N, dv]
+    void* y;            // [P, dv]
+};
+bool sdm_decode_fused_fits(int sqrtN, int dv, int k_w, int W, int k_r, int R);
+hipError_t launch_sdm_decode_fused(SdmDecodeArgs a, hipStream_t st);
+
 // ---- SDM backward (sdm_backward.hip) ----
 struct SdmBwdArgs {
     int B, T, H, N, dv, W, R;

@@ -21,6 +21,7 @@
 //     let a pair outside D win on the slot index) the exact top-budget is
 //     extracted from all k^2 candidates by repeated wave max;
 //  4. softmax in fp32 over the selected scores.
+#include "addr_wg.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -186,19 +187,10 @@ __global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
 
 // ---------------------------------------------------------------------------
 // Latency-oriented variant for small batches (a decode step): one workgroup of
-// 256 threads per problem, and the write and read problems of a step in one
-// launch.  Ranks are found by counting (rank of key x = number of keys above
-// it; keys are distinct), which is exact under the same total order as the
-// wavefront kernel:
-//   1. rank each half's sqrtN keys, keep ranks < k (the per-half top-k);
-//   2. the dominance set D (as above), ranked by counting; tau = its
-//      budget-th key;
-//   3. F = #{k^2 candidates with key >= tau}; F == budget proves D's top-budget
-//      is the answer, else all k^2 candidates are ranked by counting;
-//   4. softmax over the selected scores.
-// Limits: sqrtN <= 256, k <= 64, budget <= 64, |D| <= 256 (wg_address_fits).
+// 256 threads per problem (the steps of addr_wg.h), and the write and read
+// problems of a step in one launch.
 // ---------------------------------------------------------------------------
-constexpr int WG = 256;
+constexpr int WG = kAddrGroup;
 
 struct AddrPairArgs {
     const void* s1[2];
@@ -211,135 +203,18 @@ struct AddrPairArgs {
 
 template <typename in_t>
 __global__ __launch_bounds__(WG) void sdm_address_wg_kernel(AddrPairArgs a) {
-    __shared__ uint64_t s_half[2][WG];
-    __shared__ float s_hsc[2][64];
-    __shared__ int s_hix[2][64];
-    __shared__ uint64_t s_cand[4096];  // D, or all k^2 candidates on the rare path
-    __shared__ uint64_t s_sel[64];
-    __shared__ uint64_t s_tau;
-    __shared__ int s_F;
-    __shared__ float s_part[WG / 64];
-
+    __shared__ WgAddrSmem sm;
     const int t = threadIdx.x;
     const int set = blockIdx.x >= (unsigned)a.P ? 1 : 0;
     const int p = (int)blockIdx.x - set * a.P;
-    const int n = a.sqrtN, k = a.k[set], budget = a.budget[set], nD = a.nD[set];
-    const in_t* h1 = static_cast<const in_t*>(a.s1[set]) + (size_t)p * n;
-    const in_t* h2 = static_cast<const in_t*>(a.s2[set]) + (size_t)p * n;
-
-    // 1. per-half top-k by rank counting
-    uint64_t x1 = 0ull, x2 = 0ull;
-    if (t < n) {
-        x1 = make_key(to_f32(h1[t]), (uint32_t)t);
-        x2 = make_key(to_f32(h2[t]), (uint32_t)t);
-    }
-    s_half[0][t] = x1;
-    s_half[1][t] = x2;
-    if (t == 0) {
-        s_F = 0;
-        s_tau = 0ull;  // below every key: only read if D had fewer than budget entries
-    }
-    __syncthreads();
-    if (t < n) {
-        int r1 = 0, r2 = 0;
-        // 8 keys of each half per step (padding keys are 0, below every key)
-        for (int j = 0; j < n; j += 8) {
-            uint64_t ka[8], kb[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                ka[u] = s_half[0][j + u];
-                kb[u] = s_half[1][j + u];
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                r1 += ka[u] > x1;
-                r2 += kb[u] > x2;
-            }
-        }
-        if (r1 < k) {
-            s_hsc[0][r1] = key_score(x1);
-            s_hix[0][r1] = t;
-        }
-        if (r2 < k) {
-            s_hsc[1][r2] = key_score(x2);
-            s_hix[1][r2] = t;
-        }
-    }
-    __syncthreads();
-
-    // 2. D = {(i, j) : (i+1)(j+1) <= budget}, ranked by counting
-    uint64_t dkey = 0ull;
-    if (t < nD) {
-        int i = 0, off = 0;
-        for (;; ++i) {
-            int c = budget / (i + 1);
-            c = c < k ? c : k;
-            if (t < off + c) break;
-            off += c;
-        }
-        const int j = t - off;
-        const float sum = s_hsc[0][i] + s_hsc[1][j];  // one fp32 RNE add
-        dkey = make_key(sum, (uint32_t)s_hix[0][i] * (uint32_t)n + (uint32_t)s_hix[1][j]);
-    }
-    s_cand[t] = dkey;  // every entry is written; those past nD hold key 0 (below all keys)
-    __syncthreads();
-    if (t < nD) {
-        int r = 0;
-        for (int u = 0; u < nD; u += 8) {  // entries past nD are 0 (set below)
-            uint64_t ku[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ku[e] = s_cand[u + e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) r += ku[e] > dkey;
-        }
-        if (r < budget) s_sel[r] = dkey;
-        if (r == budget - 1) s_tau = dkey;
-    }
-    __syncthreads();
-
-    // 3. exact count of all k^2 candidates at or above tau
-    const uint64_t tau = s_tau;
-    const int kk = k * k;
-    int F = 0;
-    for (int x = t; x < kk; x += WG) {
-        const int i = x / k, j = x - (x / k) * k;
-        const float sum = s_hsc[0][i] + s_hsc[1][j];
-        F += make_key(sum, (uint32_t)s_hix[0][i] * (uint32_t)n + (uint32_t)s_hix[1][j]) >= tau;
-    }
-    F = (int)wave_sum((float)F);
-    if ((t & 63) == 0) atomicAdd(&s_F, F);
-    __syncthreads();
-    if (s_F != budget) {
-        // rare path (rounding ties): rank all k^2 candidates
-        __syncthreads();
-        for (int x = t; x < kk; x += WG) {
-            const int i = x / k, j = x - (x / k) * k;
-            const float sum = s_hsc[0][i] + s_hsc[1][j];
-            s_cand[x] = make_key(sum, (uint32_t)s_hix[0][i] * (uint32_t)n + (uint32_t)s_hix[1][j]);
-        }
-        __syncthreads();
-        for (int x = t; x < kk; x += WG) {
-            const uint64_t kx = s_cand[x];
-            int r = 0;
-            for (int y = 0; y < kk; ++y) r += s_cand[y] > kx;
-            if (r < budget) s_sel[r] = kx;
-        }
-        __syncthreads();
-    }
-
-    // 4. softmax over the selected scores (rank 0 holds the maximum)
-    int32_t* out_i = a.idx[set] + (size_t)p * budget;
-    float* out_w = a.wt[set] + (size_t)p * budget;
-    if (t < 64) {
-        const float smax = key_score(s_sel[0]);
-        const float w = t < budget ? __expf(key_score(s_sel[t]) - smax) : 0.f;
-        const float z = wave_sum(w);
-        if (t < budget) {
-            out_i[t] = (int32_t)key_index(s_sel[t]);
-            out_w[t] = w / z;
-        }
-    }
-    (void)s_part;
+    const size_t off = (size_t)p * a.sqrtN;
+    const WgAddrProblem pr{static_cast<const in_t*>(a.s1[set]) + off,
+                           static_cast<const in_t*>(a.s2[set]) + off, a.sqrtN, a.k[set],
+                           a.budget[set], a.nD[set]};
+    wg_addr_select<in_t>(pr, t, sm);
+    if (sm.F != pr.budget) wg_addr_rank_all(pr, t, sm);  // uniform over the workgroup
+    wg_addr_softmax(pr, t, sm, a.idx[set] + (size_t)p * pr.budget,
+                    a.wt[set] + (size_t)p * pr.budget, nullptr, nullptr);
 }
 
 int ceil_pow2_units(int n) {  // smallest power of two >= ceil(n/64), at least 1
@@ -375,18 +250,7 @@ hipError_t dispatch_eh(int EH, int ED, dim3 grid, hipStream_t st, const AddrArgs
 
 }  // namespace
 
-int address_set_size(int k, int budget) {
-    int nD = 0;
-    for (int i = 0; i < k; ++i) {
-        int c = budget / (i + 1);
-        nD += c < k ? c : k;
-    }
-    return nD;
-}
-
-static bool wg_address_fits(int sqrtN, int k, int budget) {
-    return sqrtN <= WG && k <= 64 && budget <= 64 && address_set_size(k, budget) <= WG;
-}
+int address_set_size(int k, int budget) { return address_set_size_host(k, budget); }
 
 // below this many problems the one-workgroup-per-problem kernel has the lower latency
 constexpr int kWgMaxProblems = 1024;
