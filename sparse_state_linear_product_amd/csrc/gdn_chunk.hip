@@ -146,6 +146,12 @@ struct GdnArgs {
 // side, slide "GDN2 separates key-side erase and value-side write"): the same
 // chunked form with beta = 1, the erase-side keys b (.) k in A and Wn, and
 // X = w (.) V in U0.
+// The off-diagonal 16x16 blocks (i, j) of the 64x64 triangular factor, in the
+// order (1,0), (2,1), (3,2), (2,0), (3,1), (3,0): p-th pair from nibbles of a
+// constant (a table indexed by a wave number would be read from memory).
+SSLP_DEVICE int pair_i(int p) { return (0x332321 >> (4 * p)) & 0xF; }
+SSLP_DEVICE int pair_j(int p) { return (0x010210 >> (4 * p)) & 0xF; }
+
 template <int MODE>
 __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
     constexpr bool KDA = MODE != 0;
@@ -166,39 +172,40 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
     uint4 pk[NSG], pq[NSG], pv[NSG];
     float4 pa[NSA > 0 ? NSA : 1];
     float pbeta = 0.f, palpha = 1.f;
+    // Loads come from clamped (always valid) token rows and are masked where
+    // they are stored, so no load waits on a condition (a conditional load
+    // would be followed by a wait for its value at the branch join).
+    int pt0 = 0;  // first token of the fetched chunk
     auto fetch = [&](int task) {
         const int c = task % nch, bh = task / nch;
         const int b = bh / H, h = bh - (bh / H) * H;
         const int t0 = c * C;
+        pt0 = t0;
         // piece i of a thread: token row = lane, columns 8 (w + 4 i) .. + 7, so that
         // the transposed stores of V below hit 64 different rows at once
 #pragma unroll
         for (int i = 0; i < NSG; ++i) {
             const int row = lane, col = 8 * (w + (NTH / 64) * i);
-            const int t = t0 + row;
-            pk[i] = pq[i] = pv[i] = make_uint4(0, 0, 0, 0);
-            if (t < T) {
-                const size_t off = (((size_t)b * T + t) * H + h) * DK + col;
-                pk[i] = *reinterpret_cast<const uint4*>(kg + off);
-                pq[i] = *reinterpret_cast<const uint4*>(qg + off);
-                pv[i] = *reinterpret_cast<const uint4*>(vg + (((size_t)b * T + t) * H + h) * dv + col);
-            }
+            const int t = min(t0 + row, T - 1);
+            const size_t off = (((size_t)b * T + t) * H + h) * DK + col;
+            pk[i] = *reinterpret_cast<const uint4*>(kg + off);
+            pq[i] = *reinterpret_cast<const uint4*>(qg + off);
+            pv[i] = *reinterpret_cast<const uint4*>(vg + (((size_t)b * T + t) * H + h) * dv + col);
         }
         if constexpr (KDA) {
 #pragma unroll
             for (int i = 0; i < NSA; ++i) {
                 const int seg = tid + NTH * i;
                 const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
-                const int t = t0 + row;
-                pa[i] = t < T ? *reinterpret_cast<const float4*>(a.alpha + (((size_t)b * T + t) * H + h) * DK + col)
-                              : make_float4(1.f, 1.f, 1.f, 1.f);
+                const int t = min(t0 + row, T - 1);
+                pa[i] = *reinterpret_cast<const float4*>(a.alpha + (((size_t)b * T + t) * H + h) * DK + col);
             }
         }
         {  // every wave: the gates of token row = lane
-            const int t = t0 + lane;
+            const int t = min(t0 + lane, T - 1);
             const size_t bth = ((size_t)b * T + t) * H + h;
-            pbeta = t < T ? (G2 ? 1.f : a.beta[bth]) : 0.f;
-            if (!KDA) palpha = t < T ? a.alpha[bth] : 1.f;
+            pbeta = G2 ? 1.f : a.beta[bth];
+            if (!KDA) palpha = a.alpha[bth];
         }
     };
     if ((int)blockIdx.x < ntask) fetch(blockIdx.x);
@@ -208,10 +215,18 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
 
     uint8_t* rec = a.rec + (size_t)task * REC_BYTES;
     block_sync_lds();  // the previous chunk's use of the shared arrays is over
-    // X = diag(beta) V, stored transposed (bf16); K, Q as they are
+    // X = diag(beta) V, stored transposed (bf16); K, Q as they are; rows past
+    // the sequence end are zero (alpha 1, beta 0)
+    const bool rowin = pt0 + lane < T;
+    if (!rowin) {
+        pbeta = 0.f;
+        palpha = 1.f;
+    }
 #pragma unroll
     for (int i = 0; i < NSG; ++i) {
         const int row = lane, col = 8 * (w + (NTH / 64) * i);
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        if (!rowin) pk[i] = pq[i] = pv[i] = z;
         *reinterpret_cast<uint4*>(&sm.k[row][col]) = pk[i];
         *reinterpret_cast<uint4*>(&sm.q[row][col]) = pq[i];
         const uint16_t* ve = reinterpret_cast<const uint16_t*>(&pv[i]);
@@ -238,14 +253,17 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
         for (int i = 0; i < NSA; ++i) {
             const int seg = tid + NTH * i;
             const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
-            *reinterpret_cast<float4*>(&sm.u.alpha[row][col]) = pa[i];
+            *reinterpret_cast<float4*>(&sm.u.alpha[row][col]) =
+                pt0 + row < T ? pa[i] : make_float4(1.f, 1.f, 1.f, 1.f);
         }
     }
     if (tid < C) {  // wave 0: lane = token
         sm.beta[tid] = pbeta;
         if (!KDA) sm.g[tid] = __logf(palpha);
     }
-    if (task + (int)gridDim.x < ntask) fetch(task + gridDim.x);  // in flight during this chunk
+    // the next chunk's inputs, in flight during this chunk (the last chunk
+    // fetches itself again: an unconditional fetch keeps the loads free of waits)
+    fetch(task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task);
     block_sync_lds();
 
         // ---------------- decay bookkeeping ----------------
@@ -445,12 +463,11 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
         block_sync_lds();
         {
             // stage 1: L_ij = T_ii A_ij (in place in A); pairs (1,0),(2,1),(3,2),(2,0),(3,1),(3,0)
-            const int pi[6] = {1, 2, 3, 2, 3, 3}, pj[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
             for (int rep = 0; rep < 2; ++rep) {
                 const int p = w + 4 * rep;
                 if (p < 6) {
-                    const int i = pi[p], j = pj[p];
+                    const int i = pair_i(p), j = pair_j(p);
                     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
                     acc = mm16_f32(&sm.u.s.Tm[16 * i][16 * i], LDF, &sm.u.s.A[16 * i][16 * j], LDF, acc, lane);
                     store16(&sm.u.s.A[16 * i][16 * j], LDF, acc, lane, 1.f);
@@ -483,14 +500,13 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
         block_sync_lds();
         {
             // stage 4: T_ij = M_ij T_jj with M = -L + L^2 - L^3 (block-wise)
-            const int pi[6] = {1, 2, 3, 2, 3, 3}, pj[6] = {0, 1, 2, 0, 1, 0};
             f32x4_t res[2];
 #pragma unroll
             for (int rep = 0; rep < 2; ++rep) {
                 res[rep] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 const int p = w + 4 * rep;
                 if (p < 6) {
-                    const int i = pi[p], j = pj[p];
+                    const int i = pair_i(p), j = pair_j(p);
                     const bool has2 = (p >= 3);
                     const bool has3 = (p == 5);
 #pragma unroll
@@ -508,7 +524,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
 #pragma unroll
             for (int rep = 0; rep < 2; ++rep) {
                 const int p = w + 4 * rep;
-                if (p < 6) store16(&sm.u.s.Tm[16 * pi[p]][16 * pj[p]], LDF, res[rep], lane, 1.f);
+                if (p < 6) store16(&sm.u.s.Tm[16 * pair_i(p)][16 * pair_j(p)], LDF, res[rep], lane, 1.f);
             }
         }
         block_sync_lds();
