@@ -148,3 +148,17 @@ def test_gdn2_empty_sequence_copies_state():
                                    S0=S0.to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(S.cpu(), S0)
+
+
+@pytest.mark.slow
+def test_gdn2_full_config():
+    # B=4, T=4096, H=16, d=128 against the sequential fp64 oracle
+    cfg = wl.GDN2
+    announce(f"{cfg.name} full size")
+    x = wl.gdn2_inputs(cfg)
+    o, S = _run2(x)
+    Sr, orf = _ref2(x)
+    e_o = maxrel(o.double().numpy(), orf)
+    e_S = maxrel(S.double().numpy(), Sr)
+    print(f"  {cfg.name}: o {e_o:.2e} S {e_S:.2e}", flush=True)
+    assert e_o <= TOL_BF16 and e_S <= TOL_BF16

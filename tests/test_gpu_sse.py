@@ -202,3 +202,29 @@ def test_sse_decode_touches_only_selected_states_and_separate_shared_qk():
             for i in range(N + 1):
                 if i not in used:
                     assert torch.equal(got["S"][b, h, i], S0[b, h, i]), (b, h, i)
+
+
+@pytest.mark.slow
+def test_sse_decode_full_size():
+    # the decode workload: 64 sequences x 16 heads, 8 routed + 1 shared states of
+    # 128 x 128 (seeded background), two steps in the configuration the
+    # benchmark times; every state slice, output and selection against the oracle
+    cfg = wl.SSE_DECODE
+    announce(f"{cfg.name} full size, 2 steps")
+    x = wl.sse_inputs(cfg, T=2)
+    g = torch.Generator().manual_seed(cfg.seed + 3)
+    S0 = torch.randn((cfg.B, cfg.H, cfg.N + 1, cfg.c, cfg.d), generator=g)
+    got = _decode_run(x, cfg.N, cfg.topk, S0)
+    ref = _ref(x, cfg.topk, S0)
+    np.testing.assert_array_equal(got["sel"], ref["sel"])
+    e_o = maxrel(got["o"].double().numpy(), ref["o"])
+    e_S = maxrel(got["S"].double().numpy(), ref["S"])
+    print(f"  {cfg.name}: o {e_o:.2e} S {e_S:.2e}", flush=True)
+    assert e_o <= TOL_BF16 and e_S <= TOL_BF16
+    # partitions selected by neither step are untouched
+    for b in range(0, cfg.B, 7):
+        for h in range(cfg.H):
+            used = set(got["sel"][b, :, h].ravel().tolist()) | {cfg.N}
+            for i in range(cfg.N + 1):
+                if i not in used:
+                    assert torch.equal(got["S"][b, h, i], S0[b, h, i])
