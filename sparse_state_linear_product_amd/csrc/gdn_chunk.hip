@@ -621,10 +621,22 @@ struct __align__(16) StateSmem {
 };
 static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// The next chunk's record, loaded a chunk ahead.  The loads are inline
+// assembly so that the compiler cannot sink them down to the LDS stores that
+// consume them (which left no overlap); the compiler does not track their
+// completion, so the consumer waits for them explicitly, with the registers
+// tied to that wait.
 struct StatePrefetch {
-    uint4 wn[4], qt[4], kh[4], p[2], u0[2];
-    float4 gc;
+    u32x4_t wn[4], qt[4], kh[4], p[2], u0[2], gc;
 };
+
+SSLP_DEVICE u32x4_t pinned_load16(const void* p) {
+    u32x4_t v;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
 
 template <typename io_t>
 __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
@@ -662,41 +674,49 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int seg = tid + NTH * s;  // 16-byte piece of a [C][DK] bf16 tile
-            pf.wn[s] = reinterpret_cast<const uint4*>(r + REC_WN)[seg];
-            pf.qt[s] = reinterpret_cast<const uint4*>(r + REC_QT)[seg];
-            pf.kh[s] = reinterpret_cast<const uint4*>(r + REC_KH)[seg];
+            pf.wn[s] = pinned_load16(r + REC_WN + 16 * seg);
+            pf.qt[s] = pinned_load16(r + REC_QT + 16 * seg);
+            pf.kh[s] = pinned_load16(r + REC_KH + 16 * seg);
         }
 #pragma unroll
-        for (int s = 0; s < 2; ++s) pf.p[s] = reinterpret_cast<const uint4*>(r + REC_P)[tid + NTH * s];
+        for (int s = 0; s < 2; ++s) pf.p[s] = pinned_load16(r + REC_P + 16 * (tid + NTH * s));
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int seg = tid + NTH * s;  // row seg / 8, columns 4 (seg % 8) .. of the slice
-            pf.u0[s] = *reinterpret_cast<const uint4*>(r + REC_U0 +
-                                                       ((seg >> 3) * DK + n0 + 4 * (seg & 7)) * 4);
+            pf.u0[s] = pinned_load16(r + REC_U0 + ((seg >> 3) * DK + n0 + 4 * (seg & 7)) * 4);
         }
-        if (tid < DK / 4) pf.gc = reinterpret_cast<const float4*>(r + REC_GC)[tid];
+        pf.gc = pinned_load16(r + REC_GC + 16 * (tid % (DK / 4)));  // used by tid < DK / 4
     };
-    auto commit = [&](const StatePrefetch& pf) {
+    auto commit = [&](StatePrefetch& pf) {
+        // the pinned loads are not tracked by the compiler: wait for them here,
+        // with every register they fill tied to the wait
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(pf.wn[0]), "+v"(pf.wn[1]), "+v"(pf.wn[2]), "+v"(pf.wn[3]),
+                       "+v"(pf.qt[0]), "+v"(pf.qt[1]), "+v"(pf.qt[2]), "+v"(pf.qt[3]),
+                       "+v"(pf.kh[0]), "+v"(pf.kh[1]), "+v"(pf.kh[2]), "+v"(pf.kh[3]),
+                       "+v"(pf.p[0]), "+v"(pf.p[1]), "+v"(pf.u0[0]), "+v"(pf.u0[1]), "+v"(pf.gc)
+                     :
+                     : "memory");
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int seg = tid + NTH * s;
             const int row = seg / (DK / 8), col = (seg % (DK / 8)) * 8;
-            *reinterpret_cast<uint4*>(&ss.wn[row][col]) = pf.wn[s];
-            *reinterpret_cast<uint4*>(&ss.qt[row][col]) = pf.qt[s];
-            *reinterpret_cast<uint4*>(&ss.kh[seg / (C / 8)][(seg % (C / 8)) * 8]) = pf.kh[s];
+            *reinterpret_cast<u32x4_t*>(&ss.wn[row][col]) = pf.wn[s];
+            *reinterpret_cast<u32x4_t*>(&ss.qt[row][col]) = pf.qt[s];
+            *reinterpret_cast<u32x4_t*>(&ss.kh[seg / (C / 8)][(seg % (C / 8)) * 8]) = pf.kh[s];
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int seg = tid + NTH * s;
             const int row = seg / (C / 8), col = (seg % (C / 8)) * 8;
-            *reinterpret_cast<uint4*>(&ss.p[row][col]) = pf.p[s];
+            *reinterpret_cast<u32x4_t*>(&ss.p[row][col]) = pf.p[s];
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int seg = tid + NTH * s;
-            *reinterpret_cast<uint4*>(&ss.u0[seg >> 3][4 * (seg & 7)]) = pf.u0[s];
+            *reinterpret_cast<u32x4_t*>(&ss.u0[seg >> 3][4 * (seg & 7)]) = pf.u0[s];
         }
-        if (tid < DK / 4) *reinterpret_cast<float4*>(&ss.gc[4 * tid]) = pf.gc;
+        if (tid < DK / 4) *reinterpret_cast<u32x4_t*>(&ss.gc[4 * tid]) = pf.gc;
     };
     auto publish_state = [&]() {
 #pragma unroll
@@ -722,7 +742,9 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
     for (int c = 0; c < nch; ++c) {
         const int t0 = c * C;
         const int Tc = (T - t0) < C ? (T - t0) : C;
-        if (c + 1 < nch) issue(pf, c + 1);  // next chunk's record, in flight
+        // the next chunk's record, in flight during this one; unconditional (the
+        // last chunk fetches its own record again) so the loads wait nowhere
+        issue(pf, c + 1 < nch ? c + 1 : c);
 
         // ---- U = U0 + Wn S0 and Qt S0 for rows block w ----
         f32x4_t u[2], o[2];
@@ -793,7 +815,7 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
             }
         }
         block_sync_lds();  // everyone is done with this chunk's LDS contents
-        if (c + 1 < nch) commit(pf);
+        commit(pf);
         publish_state();
         block_sync_lds();
     }
