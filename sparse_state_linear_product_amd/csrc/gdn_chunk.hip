@@ -231,14 +231,11 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
         *reinterpret_cast<uint4*>(&sm.q[row][col]) = pq[i];
         const uint16_t* ve = reinterpret_cast<const uint16_t*>(&pv[i]);
         float sc[8];
-        if constexpr (G2) {  // X = w (.) V
-            const int t = c * C + row;
-            float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), w1 = w0;
-            if (t < T) {
-                const float* wr = a.wvec + (((size_t)b * T + t) * H + h) * dv + col;
-                w0 = *reinterpret_cast<const float4*>(wr);
-                w1 = *reinterpret_cast<const float4*>(wr + 4);
-            }
+        if constexpr (G2) {  // X = w (.) V (rows past the end: V is zero already)
+            const int t = min(c * C + row, T - 1);
+            const float* wr = a.wvec + (((size_t)b * T + t) * H + h) * dv + col;
+            const float4 w0 = *reinterpret_cast<const float4*>(wr);
+            const float4 w1 = *reinterpret_cast<const float4*>(wr + 4);
             sc[0] = w0.x, sc[1] = w0.y, sc[2] = w0.z, sc[3] = w0.w;
             sc[4] = w1.x, sc[5] = w1.y, sc[6] = w1.z, sc[7] = w1.w;
         } else {
@@ -292,6 +289,15 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
             for (int bb = 0; bb < 2; ++bb) {
                 const int blk = 2 * hf + bb;
                 float ep = 1.f, em = 1.f, pall = 1.f;
+                // GDN2: the block's 16 erase values, all requested before any is used
+                float bv[16];
+                if constexpr (G2) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int tt = min(c * C + 16 * blk + r, T - 1);
+                        bv[r] = a.bvec[(((size_t)b * T + tt) * H + h) * DK + i];
+                    }
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int t = 16 * blk + r;
@@ -303,10 +309,7 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                     }
                     const float kv = bf2f(sm.k[t][i]), qv = bf2f(sm.q[t][i]);
                     float ke = kv;  // the key of A's rows and of Wn: b (.) k for GDN2
-                    if constexpr (G2) {
-                        const int tt = c * C + t;
-                        ke *= tt < T ? a.bvec[(((size_t)b * T + tt) * H + h) * DK + i] : 0.f;
-                    }
+                    if constexpr (G2) ke *= c * C + t < T ? bv[r] : 0.f;
                     sm.k[t][i] = f32_to_bf16(ke * ep).bits;
                     sm.km[t][i] = f32_to_bf16(kv * em).bits;
                     sm.q[t][i] = f32_to_bf16(qv * ep).bits;
