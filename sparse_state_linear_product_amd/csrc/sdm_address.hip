@@ -56,12 +56,21 @@ __global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
 
     // 1. per-half sort; key 0 is below every finite score's key (padding)
     {
+        // all scores requested at once, from clamped positions (a conditional
+        // load would be waited for one at a time); padding is applied after
         uint64_t x1[EH], x2[EH];
+        in_t r1[EH], r2[EH];
+#pragma unroll
+        for (int e = 0; e < EH; ++e) {
+            const int pos = min(e * 64 + lane, n - 1);
+            r1[e] = h1[pos];
+            r2[e] = h2[pos];
+        }
 #pragma unroll
         for (int e = 0; e < EH; ++e) {
             const int pos = e * 64 + lane;
-            x1[e] = pos < n ? make_key(to_f32(h1[pos]), (uint32_t)pos) : 0ull;
-            x2[e] = pos < n ? make_key(to_f32(h2[pos]), (uint32_t)pos) : 0ull;
+            x1[e] = pos < n ? make_key(to_f32(r1[e]), (uint32_t)pos) : 0ull;
+            x2[e] = pos < n ? make_key(to_f32(r2[e]), (uint32_t)pos) : 0ull;
         }
         bitonic_sort_desc<EH>(x1, lane);
         bitonic_sort_desc<EH>(x2, lane);
