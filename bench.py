@@ -331,7 +331,7 @@ def main():
                          "scaling hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the per-GPU shard is the single-GPU workload", file=sys.stderr)
         sys.exit(2)
 
