@@ -4,7 +4,8 @@
 // the latency-oriented workgroup variant, as device functions so that the
 // standalone addressing kernel and the fused decode kernel run the same code.
 //
-// Ranking is (fp32 score desc, index asc) as a 64-bit key (common.h):
+// Ranking is (fp32 score desc, index asc) as a 64-bit key (common.h; a 32-bit
+// key of the same order for bf16 half scores):
 //   1. per-half top-k: each wavefront sorts its 64 keys of each half in
 //      registers and keeps its top k; the half's top k is among those 4k keys
 //      and is ranked by counting (keys are distinct; padding keys are 0, below
@@ -20,6 +21,8 @@
 // Limits: sqrtN <= 256, k <= 64, budget <= 64, |D| <= 256.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace sslp {
@@ -27,7 +30,10 @@ namespace sslp {
 constexpr int kAddrGroup = 256;  // threads per addressing problem
 
 struct WgAddrSmem {
-    uint64_t top[2][kAddrGroup];  // per half: each wave's sorted top-k of its 64 keys
+    union {
+        uint64_t top[2][kAddrGroup];    // per half: each wave's sorted top-k of its 64 keys
+        uint32_t top32[2][kAddrGroup];  // the same as 32-bit keys (bf16 scores)
+    };
     float hsc[2][64];
     int hix[2][64];
     uint64_t cand[4096];  // D, or all k^2 candidates on the rare path
@@ -64,11 +70,8 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm) 
     const int n = pr.n, k = pr.k, budget = pr.budget, nD = pr.nD;
     const in_t* h1 = static_cast<const in_t*>(pr.s1);
     const in_t* h2 = static_cast<const in_t*>(pr.s2);
-    uint64_t x1[1] = {0ull}, x2[1] = {0ull};
-    if (t < n) {
-        x1[0] = make_key(to_f32(h1[t]), (uint32_t)t);
-        x2[0] = make_key(to_f32(h2[t]), (uint32_t)t);
-    }
+    // the half scores, requested before the wave 0 work below
+    in_t r1 = h1[min(t, n - 1)], r2 = h2[min(t, n - 1)];
     if (wv == 0) {
         // D row by row: row i has min(budget / (i+1), k) entries; lane i
         // writes its row's entries of the map
@@ -88,29 +91,62 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm) 
         sm.F = 0;
         sm.tau = 0ull;  // below every key: only read if D had fewer than budget entries
     }
-    bitonic_sort_desc<1>(x1, lane);
-    bitonic_sort_desc<1>(x2, lane);
-    sm.top[0][t] = lane < k ? x1[0] : 0ull;
-    sm.top[1][t] = lane < k ? x2[0] : 0ull;
-    __syncthreads();
-    for (int x = t; x < 8 * k; x += kAddrGroup) {
-        const int hh = x >= 4 * k ? 1 : 0;
-        const int q = x - hh * 4 * k;
-        const uint64_t key = sm.top[hh][(q / k) * 64 + (q - (q / k) * k)];
-        int r = 0;
-        for (int w2 = 0; w2 < 4; ++w2) {
-            const uint64_t* lst = &sm.top[hh][w2 * 64];
-            for (int u = 0; u < k; u += 8) {
-                uint64_t ku[8];
+    if constexpr (std::is_same<in_t, bf16_t>::value) {
+        // bf16 scores and indices below 2^16: 32-bit keys of the same order
+        uint32_t x1[1] = {t < n ? make_key32(to_f32(r1), (uint32_t)t) : 0u};
+        uint32_t x2[1] = {t < n ? make_key32(to_f32(r2), (uint32_t)t) : 0u};
+        bitonic_sort_desc32<1>(x1, lane);
+        bitonic_sort_desc32<1>(x2, lane);
+        sm.top32[0][t] = lane < k ? x1[0] : 0u;
+        sm.top32[1][t] = lane < k ? x2[0] : 0u;
+        __syncthreads();
+        for (int x = t; x < 8 * k; x += kAddrGroup) {
+            const int hh = x >= 4 * k ? 1 : 0;
+            const int q = x - hh * 4 * k;
+            const uint32_t key = sm.top32[hh][(q / k) * 64 + (q - (q / k) * k)];
+            int r = 0;
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const uint32_t* lst = &sm.top32[hh][w2 * 64];
+                for (int u = 0; u < k; u += 8) {
+                    uint32_t ku[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ku[e] = lst[u + e];
+                    for (int e = 0; e < 8; ++e) ku[e] = lst[u + e];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) r += ku[e] > key;
+                    for (int e = 0; e < 8; ++e) r += ku[e] > key;
+                }
+            }
+            if (r < k) {
+                sm.hsc[hh][r] = key32_score(key);
+                sm.hix[hh][r] = (int)key32_index(key);
             }
         }
-        if (r < k) {
-            sm.hsc[hh][r] = key_score(key);
-            sm.hix[hh][r] = (int)key_index(key);
+    } else {
+        uint64_t x1[1] = {t < n ? make_key(to_f32(r1), (uint32_t)t) : 0ull};
+        uint64_t x2[1] = {t < n ? make_key(to_f32(r2), (uint32_t)t) : 0ull};
+        bitonic_sort_desc<1>(x1, lane);
+        bitonic_sort_desc<1>(x2, lane);
+        sm.top[0][t] = lane < k ? x1[0] : 0ull;
+        sm.top[1][t] = lane < k ? x2[0] : 0ull;
+        __syncthreads();
+        for (int x = t; x < 8 * k; x += kAddrGroup) {
+            const int hh = x >= 4 * k ? 1 : 0;
+            const int q = x - hh * 4 * k;
+            const uint64_t key = sm.top[hh][(q / k) * 64 + (q - (q / k) * k)];
+            int r = 0;
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const uint64_t* lst = &sm.top[hh][w2 * 64];
+                for (int u = 0; u < k; u += 8) {
+                    uint64_t ku[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ku[e] = lst[u + e];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) r += ku[e] > key;
+                }
+            }
+            if (r < k) {
+                sm.hsc[hh][r] = key_score(key);
+                sm.hix[hh][r] = (int)key_index(key);
+            }
         }
     }
     __syncthreads();

@@ -52,6 +52,18 @@ SSLP_DEVICE uint64_t make_key(float score, uint32_t index) {
 SSLP_DEVICE float key_score(uint64_t key) { return order_bits_to_float((uint32_t)(key >> 32)); }
 SSLP_DEVICE uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
 
+// The same order in 32 bits for a score that is exactly a bf16 value and an
+// index below 2^16: the upper half of the order bits (the lower half is 0x0000
+// for a positive and 0xFFFF for a negative bf16 value) and the inverted index.
+SSLP_DEVICE uint32_t make_key32(float bf16_exact_score, uint32_t index) {
+    return (order_bits(bf16_exact_score) & 0xFFFF0000u) | (~index & 0xFFFFu);
+}
+SSLP_DEVICE float key32_score(uint32_t key) {
+    const uint32_t hi = key & 0xFFFF0000u;
+    return order_bits_to_float(hi | ((hi & 0x80000000u) ? 0u : 0xFFFFu));
+}
+SSLP_DEVICE uint32_t key32_index(uint32_t key) { return ~key & 0xFFFFu; }
+
 // ---------------------------------------------------------------------------
 // wave-level helpers
 // ---------------------------------------------------------------------------
@@ -132,6 +144,45 @@ SSLP_DEVICE void bitonic_sort_desc(uint64_t (&a)[E], int lane) {
                     const bool keep_max = (lower == desc);
                     const uint64_t mx = mine > other ? mine : other;
                     const uint64_t mn = mine > other ? other : mine;
+                    a[e] = keep_max ? mx : mn;
+                }
+            }
+        }
+    }
+}
+
+// The same sort for 32-bit keys (one shuffle per exchange instead of two).
+template <int E>
+SSLP_DEVICE void bitonic_sort_desc32(uint32_t (&a)[E], int lane) {
+    constexpr int n = 64 * E;
+#pragma unroll
+    for (int kk = 2; kk <= n; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            if (j >= 64) {
+                const int je = j >> 6;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int e2 = e ^ je;
+                    if (e2 > e) {
+                        const bool desc = (((e << 6) & kk) == 0);
+                        const uint32_t x = a[e], y = a[e2];
+                        const bool sw = desc ? (x < y) : (x > y);
+                        a[e] = sw ? y : x;
+                        a[e2] = sw ? x : y;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const uint32_t mine = a[e];
+                    const uint32_t other = __shfl_xor(mine, j, kWave);
+                    const int p = (e << 6) | lane;
+                    const bool desc = ((p & kk) == 0);
+                    const bool lower = ((lane & j) == 0);
+                    const bool keep_max = (lower == desc);
+                    const uint32_t mx = mine > other ? mine : other;
+                    const uint32_t mn = mine > other ? other : mine;
                     a[e] = keep_max ? mx : mn;
                 }
             }

@@ -21,6 +21,8 @@
 //     let a pair outside D win on the slot index) the exact top-budget is
 //     extracted from all k^2 candidates by repeated wave max;
 //  4. softmax in fp32 over the selected scores.
+#include <type_traits>
+
 #include "addr_wg.h"
 #include "common.h"
 #include "kernels.h"
@@ -58,7 +60,6 @@ __global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
     {
         // all scores requested at once, from clamped positions (a conditional
         // load would be waited for one at a time); padding is applied after
-        uint64_t x1[EH], x2[EH];
         in_t r1[EH], r2[EH];
 #pragma unroll
         for (int e = 0; e < EH; ++e) {
@@ -66,19 +67,39 @@ __global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
             r1[e] = h1[pos];
             r2[e] = h2[pos];
         }
+        if constexpr (std::is_same<in_t, bf16_t>::value) {
+            // bf16 scores and indices below 2^16 fit a 32-bit key of the same order
+            uint32_t x1[EH], x2[EH];
 #pragma unroll
-        for (int e = 0; e < EH; ++e) {
-            const int pos = e * 64 + lane;
-            x1[e] = pos < n ? make_key(to_f32(r1[e]), (uint32_t)pos) : 0ull;
-            x2[e] = pos < n ? make_key(to_f32(r2[e]), (uint32_t)pos) : 0ull;
-        }
-        bitonic_sort_desc<EH>(x1, lane);
-        bitonic_sort_desc<EH>(x2, lane);
-        if (lane < k) {
-            s_score[wv][0][lane] = key_score(x1[0]);
-            s_index[wv][0][lane] = (int)key_index(x1[0]);
-            s_score[wv][1][lane] = key_score(x2[0]);
-            s_index[wv][1][lane] = (int)key_index(x2[0]);
+            for (int e = 0; e < EH; ++e) {
+                const int pos = e * 64 + lane;
+                x1[e] = pos < n ? make_key32(to_f32(r1[e]), (uint32_t)pos) : 0u;
+                x2[e] = pos < n ? make_key32(to_f32(r2[e]), (uint32_t)pos) : 0u;
+            }
+            bitonic_sort_desc32<EH>(x1, lane);
+            bitonic_sort_desc32<EH>(x2, lane);
+            if (lane < k) {
+                s_score[wv][0][lane] = key32_score(x1[0]);
+                s_index[wv][0][lane] = (int)key32_index(x1[0]);
+                s_score[wv][1][lane] = key32_score(x2[0]);
+                s_index[wv][1][lane] = (int)key32_index(x2[0]);
+            }
+        } else {
+            uint64_t x1[EH], x2[EH];
+#pragma unroll
+            for (int e = 0; e < EH; ++e) {
+                const int pos = e * 64 + lane;
+                x1[e] = pos < n ? make_key(to_f32(r1[e]), (uint32_t)pos) : 0ull;
+                x2[e] = pos < n ? make_key(to_f32(r2[e]), (uint32_t)pos) : 0ull;
+            }
+            bitonic_sort_desc<EH>(x1, lane);
+            bitonic_sort_desc<EH>(x2, lane);
+            if (lane < k) {
+                s_score[wv][0][lane] = key_score(x1[0]);
+                s_index[wv][0][lane] = (int)key_index(x1[0]);
+                s_score[wv][1][lane] = key_score(x2[0]);
+                s_index[wv][1][lane] = (int)key_index(x2[0]);
+            }
         }
     }
     wave_sync();
