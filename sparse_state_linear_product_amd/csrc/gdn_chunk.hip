@@ -96,6 +96,38 @@ struct __align__(16) Smem {
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 
+// The scalar-decay (GDN) prep layout: K and Q are last read before A is
+// written, so A and T take their place, and T's bf16 copy takes A's once the
+// inverse is formed.  73.8 KB: two workgroups per compute unit.
+struct __align__(16) SmemG {
+    union {
+        struct {
+            uint16_t k[C][LDK];
+            uint16_t q[C][LDK];
+        };
+        struct {
+            union {
+                struct {
+                    float A[C][LDF];
+                    float Tm[C][LDF];
+                } s;
+            } u;
+        };
+        struct {
+            uint16_t tb[C][LDP];  // over A, after the last read of A
+        };
+    };
+    uint16_t xt[DK][LDP];
+    uint16_t kbt[DK][LDP];
+    float L3[16][17];
+    float g[C];
+    float beta[C];
+    float eg[C];
+    float ehg[C];
+};
+static_assert(sizeof(SmemG) <= 80 * 1024, "two scalar-decay prep workgroups per compute unit");
+static_assert(sizeof(uint16_t) * C * LDP <= sizeof(float) * C * LDF, "T in bf16 fits over A");
+
 SSLP_DEVICE __bf16 bf(float f) { return __builtin_bit_cast(__bf16, f32_to_bf16(f).bits); }
 SSLP_DEVICE float bf2f(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
 SSLP_DEVICE f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
@@ -152,11 +184,10 @@ struct GdnArgs {
 SSLP_DEVICE int pair_i(int p) { return (0x332321 >> (4 * p)) & 0xF; }
 SSLP_DEVICE int pair_j(int p) { return (0x010210 >> (4 * p)) & 0xF; }
 
-template <int MODE>
-__global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
+template <int MODE, typename SM>
+SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
     constexpr bool KDA = MODE != 0;
     constexpr bool G2 = MODE == 2;
-    __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nch = a.nch;
     const int T = a.T, H = a.H, dv = a.dv;
@@ -408,6 +439,60 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
             }
         }
         block_sync_lds();
+        // (diag(beta) Kt)^T for Wn: Kt = K e^{g_t} (GDN) or Kp F[block] (KDA)
+        for (int e = tid; e < C * DK; e += NTH) {
+            const int i = e / C, t = e % C;
+            float kt;
+            if constexpr (!KDA) kt = bf2f(sm.k[t][i]) * sm.eg[t];
+            else kt = bf2f(sm.k[t][i]) * sm.F[t >> 4][i];
+            sm.kbt[i][t] = f32_to_bf16(sm.beta[t] * kt).bits;
+        }
+        // ---- Qt, Kh^T, e^{g_C} into the record: the last reads of Q and K ----
+        {
+            uint16_t* qt = reinterpret_cast<uint16_t*>(rec + REC_QT);
+            uint16_t* kh = reinterpret_cast<uint16_t*>(rec + REC_KH);
+            for (int seg = tid; seg < C * DK / 8; seg += NTH) {
+                const int t = seg / (DK / 8), i0 = (seg % (DK / 8)) * 8;
+                uint32_t qw[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float q0, q1;
+                    if constexpr (!KDA) {
+                        const float fq = sm.eg[t];
+                        q0 = bf2f(sm.q[t][i0 + e]) * fq;
+                        q1 = bf2f(sm.q[t][i0 + e + 1]) * fq;
+                    } else {
+                        q0 = bf2f(sm.q[t][i0 + e]) * sm.F[t >> 4][i0 + e];
+                        q1 = bf2f(sm.q[t][i0 + e + 1]) * sm.F[t >> 4][i0 + e + 1];
+                    }
+                    qw[e / 2] = (uint32_t)f32_to_bf16(q0).bits | ((uint32_t)f32_to_bf16(q1).bits << 16);
+                }
+                *reinterpret_cast<uint4*>(qt + t * DK + i0) = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+            }
+            for (int seg = tid; seg < C * DK / 8; seg += NTH) {
+                const int i = seg / (C / 8), t0e = (seg % (C / 8)) * 8;
+                uint32_t kw[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float k0, k1;
+                    if constexpr (!KDA) {
+                        k0 = bf2f(sm.k[t0e + e][i]) * sm.ehg[t0e + e];
+                        k1 = bf2f(sm.k[t0e + e + 1][i]) * sm.ehg[t0e + e + 1];
+                    } else {
+                        k0 = bf2f(sm.km[t0e + e][i]) * sm.Hf[(t0e + e) >> 4][i];
+                        k1 = bf2f(sm.km[t0e + e + 1][i]) * sm.Hf[(t0e + e + 1) >> 4][i];
+                    }
+                    kw[e / 2] = (uint32_t)f32_to_bf16(k0).bits | ((uint32_t)f32_to_bf16(k1).bits << 16);
+                }
+                *reinterpret_cast<uint4*>(kh + i * C + t0e) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+            }
+            float* gc = reinterpret_cast<float*>(rec + REC_GC);
+            if (tid < DK) {
+                if constexpr (KDA) gc[tid] = sm.gC[tid];
+                else gc[tid] = decC_s;
+            }
+        }
+        block_sync_lds();
         // write A (strictly lower, beta and decay applied) and P (causal) tiles
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
@@ -429,14 +514,6 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                 }
                 reinterpret_cast<uint16_t*>(rec + REC_P)[tp * C + jj] = f32_to_bf16(pv).bits;
             }
-        }
-        // (diag(beta) Kt)^T for Wn: Kt = K e^{g_t} (GDN) or Kp F[block] (KDA)
-        for (int e = tid; e < C * DK; e += NTH) {
-            const int i = e / C, t = e % C;
-            float kt;
-            if constexpr (!KDA) kt = bf2f(sm.k[t][i]) * sm.eg[t];
-            else kt = bf2f(sm.k[t][i]) * sm.F[t >> 4][i];
-            sm.kbt[i][t] = f32_to_bf16(sm.beta[t] * kt).bits;
         }
         block_sync_lds();
 
@@ -564,49 +641,19 @@ __global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
                 }
             }
         }
-        // ---------------- Qt, Kh^T, e^{g_C} ----------------
-        {
-            uint16_t* qt = reinterpret_cast<uint16_t*>(rec + REC_QT);
-            uint16_t* kh = reinterpret_cast<uint16_t*>(rec + REC_KH);
-            for (int seg = tid; seg < C * DK / 8; seg += NTH) {
-                const int t = seg / (DK / 8), i0 = (seg % (DK / 8)) * 8;
-                uint32_t qw[4];
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    float q0, q1;
-                    if constexpr (!KDA) {
-                        const float fq = sm.eg[t];
-                        q0 = bf2f(sm.q[t][i0 + e]) * fq;
-                        q1 = bf2f(sm.q[t][i0 + e + 1]) * fq;
-                    } else {
-                        q0 = bf2f(sm.q[t][i0 + e]) * sm.F[t >> 4][i0 + e];
-                        q1 = bf2f(sm.q[t][i0 + e + 1]) * sm.F[t >> 4][i0 + e + 1];
-                    }
-                    qw[e / 2] = (uint32_t)f32_to_bf16(q0).bits | ((uint32_t)f32_to_bf16(q1).bits << 16);
-                }
-                *reinterpret_cast<uint4*>(qt + t * DK + i0) = make_uint4(qw[0], qw[1], qw[2], qw[3]);
-            }
-            for (int seg = tid; seg < C * DK / 8; seg += NTH) {
-                const int i = seg / (C / 8), t0e = (seg % (C / 8)) * 8;
-                uint32_t kw[4];
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    float k0, k1;
-                    if constexpr (!KDA) {
-                        k0 = bf2f(sm.k[t0e + e][i]) * sm.ehg[t0e + e];
-                        k1 = bf2f(sm.k[t0e + e + 1][i]) * sm.ehg[t0e + e + 1];
-                    } else {
-                        k0 = bf2f(sm.km[t0e + e][i]) * sm.Hf[(t0e + e) >> 4][i];
-                        k1 = bf2f(sm.km[t0e + e + 1][i]) * sm.Hf[(t0e + e + 1) >> 4][i];
-                    }
-                    kw[e / 2] = (uint32_t)f32_to_bf16(k0).bits | ((uint32_t)f32_to_bf16(k1).bits << 16);
-                }
-                *reinterpret_cast<uint4*>(kh + i * C + t0e) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-            }
-            float* gc = reinterpret_cast<float*>(rec + REC_GC);
-            if (tid < DK) gc[tid] = KDA ? sm.gC[tid] : decC_s;
-        }
     }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NTH) void gdn_prep_kernel(GdnArgs a, int ntask) {
+    __shared__ Smem sm;
+    gdn_prep_body<MODE>(a, ntask, sm);
+}
+
+// scalar decay: two workgroups per compute unit (LDS and registers sized for it)
+__global__ __launch_bounds__(NTH, 2) void gdn_prep_kernel_scalar(GdnArgs a, int ntask) {
+    __shared__ SmemG sm;
+    gdn_prep_body<0>(a, ntask, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -838,7 +885,8 @@ __global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
 
 }  // namespace
 
-// one prep workgroup per compute unit (its LDS footprint allows no more)
+// compute units of the current device (persistent prep grid: one workgroup per
+// unit with a per-channel decay, two with a scalar one)
 int prep_grid() {
     static int cus[64] = {0};
     int dev = 0;
@@ -866,10 +914,11 @@ hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, con
               bvec, wvec};
     if (nch > 0) {
         const int ntask = B * H * nch;
-        const int grid = ntask < prep_grid() ? ntask : prep_grid();
+        const int per_cu = kda == 0 ? 2 : 1;
+        const int grid = ntask < per_cu * prep_grid() ? ntask : per_cu * prep_grid();
         if (kda == 2) gdn_prep_kernel<2><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
         else if (kda == 1) gdn_prep_kernel<1><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
-        else gdn_prep_kernel<0><<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
+        else gdn_prep_kernel_scalar<<<(unsigned)grid, NTH, 0, st>>>(a, ntask);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
