@@ -7,11 +7,12 @@
 // Ranking is (fp32 score desc, index asc) as a 64-bit key (common.h; a 32-bit
 // key of the same order for bf16 half scores):
 //   1. per-half top-k: each wavefront sorts its 64 keys of each half in
-//      registers and keeps its top k; the half's top k is among those 4k keys
-//      and is ranked by counting (keys are distinct; padding keys are 0, below
-//      every key, and rank at or past k because sqrtN >= k);
-//   2. the dominance set D = {(i, j) : (i+1)(j+1) <= budget}, ranked by
-//      counting; tau = its budget-th key;
+//      registers; one wavefront per half merges the four sorted lists into the
+//      half's top 64 in rank order (merge4_top64; keys are distinct, padding
+//      keys are 0, below every key);
+//   2. the dominance set D = {(i, j) : (i+1)(j+1) <= budget}: each wavefront
+//      sorts its 64 entries, one wavefront merges them (merge4_top64);
+//      tau = the budget-th key;
 //   3. F = #{k^2 candidates with key >= tau}; F == budget proves D's
 //      top-budget is the answer, else all k^2 candidates are ranked by
 //      counting (wg_addr_rank_all, the rare path of rounding ties);
@@ -63,6 +64,43 @@ inline bool wg_address_fits(int sqrtN, int k, int budget) {
            address_set_size_host(k, budget) <= kAddrGroup;
 }
 
+// Descending order of a bitonic sequence of 64 keys held one per lane: at each
+// distance J = 32 .. 1 the lower lane of a pair keeps the larger key.
+template <typename Key>
+SSLP_DEVICE Key bitonic_merge64_desc(Key x, int lane) {
+    auto step = [&](auto jc) {
+        constexpr int J = decltype(jc)::value;
+        const Key o = xor_lane_c<J>(x, lane);
+        x = ((lane & J) == 0) ? (x > o ? x : o) : (x > o ? o : x);
+    };
+    step(std::integral_constant<int, 32>{});
+    step(std::integral_constant<int, 16>{});
+    step(std::integral_constant<int, 8>{});
+    step(std::integral_constant<int, 4>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 1>{});
+    return x;
+}
+
+// The 64 largest of four descending lists of 64 keys (lst[64 l + i], list l),
+// in rank order: lane r returns the rank-r key.  Run by one whole wavefront.
+// The elementwise maximum of a descending list and a reversed one holds the 64
+// largest of the two as a bitonic sequence; two rounds of that and a merge.
+template <typename Key>
+SSLP_DEVICE Key merge4_top64(const Key* lst, int lane) {
+    Key a0 = lst[lane], b0 = lst[64 + 63 - lane];
+    Key a1 = lst[128 + lane], b1 = lst[192 + 63 - lane];
+    a0 = bitonic_merge64_desc(a0 > b0 ? a0 : b0, lane);
+    a1 = bitonic_merge64_desc(a1 > b1 ? a1 : b1, lane);
+    Key r1;  // a1 reversed across the lanes
+    if constexpr (sizeof(Key) == 8) {
+        r1 = shfl_u64(a1, 63 - lane);
+    } else {
+        r1 = (Key)__shfl((uint32_t)a1, 63 - lane, 64);
+    }
+    return bitonic_merge64_desc(a0 > r1 ? a0 : r1, lane);
+}
+
 // steps 1-3 up to F (ends with a barrier: sm.F is then valid for every thread)
 template <typename in_t>
 SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm) {
@@ -97,27 +135,14 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm) 
         uint32_t x2[1] = {t < n ? make_key32(to_f32(r2), (uint32_t)t) : 0u};
         bitonic_sort_desc32<1>(x1, lane);
         bitonic_sort_desc32<1>(x2, lane);
-        sm.top32[0][t] = lane < k ? x1[0] : 0u;
-        sm.top32[1][t] = lane < k ? x2[0] : 0u;
+        sm.top32[0][t] = x1[0];
+        sm.top32[1][t] = x2[0];
         __syncthreads();
-        for (int x = t; x < 8 * k; x += kAddrGroup) {
-            const int hh = x >= 4 * k ? 1 : 0;
-            const int q = x - hh * 4 * k;
-            const uint32_t key = sm.top32[hh][(q / k) * 64 + (q - (q / k) * k)];
-            int r = 0;
-            for (int w2 = 0; w2 < 4; ++w2) {
-                const uint32_t* lst = &sm.top32[hh][w2 * 64];
-                for (int u = 0; u < k; u += 8) {
-                    uint32_t ku[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ku[e] = lst[u + e];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) r += ku[e] > key;
-                }
-            }
-            if (r < k) {
-                sm.hsc[hh][r] = key32_score(key);
-                sm.hix[hh][r] = (int)key32_index(key);
+        if (wv < 2) {  // wavefront hh ranks half hh
+            const uint32_t key = merge4_top64(&sm.top32[wv][0], lane);
+            if (lane < k) {
+                sm.hsc[wv][lane] = key32_score(key);
+                sm.hix[wv][lane] = (int)key32_index(key);
             }
         }
     } else {
@@ -125,52 +150,35 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm) 
         uint64_t x2[1] = {t < n ? make_key(to_f32(r2), (uint32_t)t) : 0ull};
         bitonic_sort_desc<1>(x1, lane);
         bitonic_sort_desc<1>(x2, lane);
-        sm.top[0][t] = lane < k ? x1[0] : 0ull;
-        sm.top[1][t] = lane < k ? x2[0] : 0ull;
+        sm.top[0][t] = x1[0];
+        sm.top[1][t] = x2[0];
         __syncthreads();
-        for (int x = t; x < 8 * k; x += kAddrGroup) {
-            const int hh = x >= 4 * k ? 1 : 0;
-            const int q = x - hh * 4 * k;
-            const uint64_t key = sm.top[hh][(q / k) * 64 + (q - (q / k) * k)];
-            int r = 0;
-            for (int w2 = 0; w2 < 4; ++w2) {
-                const uint64_t* lst = &sm.top[hh][w2 * 64];
-                for (int u = 0; u < k; u += 8) {
-                    uint64_t ku[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ku[e] = lst[u + e];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) r += ku[e] > key;
-                }
-            }
-            if (r < k) {
-                sm.hsc[hh][r] = key_score(key);
-                sm.hix[hh][r] = (int)key_index(key);
+        if (wv < 2) {  // wavefront hh ranks half hh
+            const uint64_t key = merge4_top64(&sm.top[wv][0], lane);
+            if (lane < k) {
+                sm.hsc[wv][lane] = key_score(key);
+                sm.hix[wv][lane] = (int)key_index(key);
             }
         }
     }
     __syncthreads();
-    // 2. D ranked by counting; tau = its budget-th key
-    uint64_t dkey = 0ull;
+    // 2. D in rank order: each wavefront sorts its 64 entries (past nD: key 0,
+    //    below all keys), one wavefront merges the four lists; tau = the
+    //    budget-th key (0 if D has fewer than budget entries)
+    uint64_t dkey[1] = {0ull};
     if (t < nD) {
         const int i = sm.drow[t];
         const int j = t - sm.doff[i];
         const float sum = sm.hsc[0][i] + sm.hsc[1][j];  // one fp32 RNE add
-        dkey = make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + (uint32_t)sm.hix[1][j]);
+        dkey[0] = make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + (uint32_t)sm.hix[1][j]);
     }
-    sm.cand[t] = dkey;  // every entry is written; those past nD hold key 0 (below all keys)
+    bitonic_sort_desc<1>(dkey, lane);
+    sm.cand[t] = dkey[0];
     __syncthreads();
-    if (t < nD) {
-        int r = 0;
-        for (int u = 0; u < nD; u += 8) {  // entries past nD are 0
-            uint64_t ku[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ku[e] = sm.cand[u + e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) r += ku[e] > dkey;
-        }
-        if (r < budget) sm.sel[r] = dkey;
-        if (r == budget - 1) sm.tau = dkey;
+    if (wv == 0) {
+        const uint64_t key = merge4_top64(&sm.cand[0], lane);
+        if (lane < budget) sm.sel[lane] = key;
+        if (lane == budget - 1) sm.tau = key;
     }
     __syncthreads();
     // 3. exact count of all k^2 candidates at or above tau

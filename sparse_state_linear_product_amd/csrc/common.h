@@ -67,12 +67,41 @@ SSLP_DEVICE uint32_t key32_index(uint32_t key) { return ~key & 0xFFFFu; }
 // ---------------------------------------------------------------------------
 // wave-level helpers
 // ---------------------------------------------------------------------------
-SSLP_DEVICE uint64_t shfl_xor_u64(uint64_t v, int mask) {
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = __shfl_xor(lo, mask, kWave);
-    hi = __shfl_xor(hi, mask, kWave);
+SSLP_DEVICE int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// The value of x held by lane ^ j (j a power of two below 64; a constant once
+// the callers' loops are unrolled), from DPP row moves (j <= 8) or the gfx950
+// lane-swap instructions (j = 16, 32) instead of a round trip through the LDS
+// crossbar.  Every lane of the wavefront must be active.
+SSLP_DEVICE uint32_t xor_lane(uint32_t x, int j, int lane) {
+    const int xi = (int)x;
+    switch (j) {
+        case 1:  // quad_perm [1,0,3,2]
+            return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false);
+        case 2:  // quad_perm [2,3,0,1]
+            return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false);
+        case 4: {  // rotations inside a row of 16: by 12 reads lane + 4, by 4 reads lane - 4
+            const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x12C, 0xF, 0xF, false);
+            const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x124, 0xF, 0xF, false);
+            return (lane & 4) ? dn : up;
+        }
+        case 8:  // row rotation by 8
+            return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, false);
+        case 16: {  // element 1 holds row r+1's values in even rows, element 0 row r-1's in odd rows
+            const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+            return (lane & 16) ? p[0] : p[1];
+        }
+        default: {  // 32: the same for the two halves of the wavefront
+            const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+            return (lane & 32) ? p[0] : p[1];
+        }
+    }
+}
+SSLP_DEVICE uint64_t xor_lane_u64(uint64_t v, int j, int lane) {
+    const uint32_t lo = xor_lane((uint32_t)v, j, lane), hi = xor_lane((uint32_t)(v >> 32), j, lane);
     return ((uint64_t)hi << 32) | lo;
 }
+SSLP_DEVICE uint64_t shfl_xor_u64(uint64_t v, int mask) { return xor_lane_u64(v, mask, lane_id()); }
 SSLP_DEVICE uint64_t shfl_u64(uint64_t v, int src) {
     uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
     lo = __shfl(lo, src, kWave);
@@ -80,8 +109,9 @@ SSLP_DEVICE uint64_t shfl_u64(uint64_t v, int src) {
     return ((uint64_t)hi << 32) | lo;
 }
 SSLP_DEVICE float wave_sum(float x) {
+    const int lane = lane_id();
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    for (int m = 32; m >= 1; m >>= 1) x += __uint_as_float(xor_lane(__float_as_uint(x), m, lane));
     return x;
 }
 SSLP_DEVICE uint64_t wave_max_u64(uint64_t x) {
@@ -109,85 +139,89 @@ SSLP_DEVICE void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Bitonic sort, descending, of 64*E keys held E per lane: element e of lane l
-// sits at position p = e*64 + l.  Compare-exchange partners at distance j < 64
-// live in another lane (exchanged with shuffles); larger distances are inside
-// the lane.
-template <int E>
-SSLP_DEVICE void bitonic_sort_desc(uint64_t (&a)[E], int lane) {
-    constexpr int n = 64 * E;
+// xor_lane with the distance as a template argument
+template <int J>
+SSLP_DEVICE uint32_t xor_lane_c(uint32_t x, int lane) {
+    static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16 || J == 32, "lane distance");
+    const int xi = (int)x;
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (J == 4) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x12C, 0xF, 0xF, false);
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x124, 0xF, 0xF, false);
+        return (lane & 4) ? dn : up;
+    } else if constexpr (J == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, false);
+    } else if constexpr (J == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? p[0] : p[1];
+    } else {
+        const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? p[0] : p[1];
+    }
+}
+template <int J>
+SSLP_DEVICE uint64_t xor_lane_c(uint64_t v, int lane) {
+    const uint32_t lo = xor_lane_c<J>((uint32_t)v, lane), hi = xor_lane_c<J>((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort, descending, of 64*E keys (uint64_t, or uint32_t for the
+// 32-bit order of bf16 scores) held E per lane: element e of lane l sits at
+// position p = e*64 + l.  Compare-exchange partners at distance J < 64 live in
+// another lane (exchanged with xor_lane_c); larger distances are inside the
+// lane.  The merge size KK and distance J are template arguments, so every
+// stage is resolved at compile time.
+template <int KK, int J, int E, typename Key>
+SSLP_DEVICE void bitonic_stage(Key (&a)[E], int lane) {
+    if constexpr (J >= 64) {
+        constexpr int je = J >> 6;
 #pragma unroll
-    for (int kk = 2; kk <= n; kk <<= 1) {
-#pragma unroll
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-            if (j >= 64) {
-                const int je = j >> 6;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int e2 = e ^ je;
-                    if (e2 > e) {
-                        const bool desc = (((e << 6) & kk) == 0);
-                        const uint64_t x = a[e], y = a[e2];
-                        const bool sw = desc ? (x < y) : (x > y);
-                        a[e] = sw ? y : x;
-                        a[e2] = sw ? x : y;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const uint64_t mine = a[e];
-                    const uint64_t other = shfl_xor_u64(mine, j);
-                    const int p = (e << 6) | lane;
-                    const bool desc = ((p & kk) == 0);
-                    const bool lower = ((lane & j) == 0);
-                    const bool keep_max = (lower == desc);
-                    const uint64_t mx = mine > other ? mine : other;
-                    const uint64_t mn = mine > other ? other : mine;
-                    a[e] = keep_max ? mx : mn;
-                }
+        for (int e = 0; e < E; ++e) {
+            const int e2 = e ^ je;
+            if (e2 > e) {
+                const bool desc = (((e << 6) & KK) == 0);
+                const Key x = a[e], y = a[e2];
+                const bool sw = desc ? (x < y) : (x > y);
+                a[e] = sw ? y : x;
+                a[e2] = sw ? x : y;
             }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const Key mine = a[e];
+            const Key other = xor_lane_c<J>(mine, lane);
+            const int p = (e << 6) | lane;
+            const bool desc = ((p & KK) == 0);
+            const bool lower = ((lane & J) == 0);
+            const bool keep_max = (lower == desc);
+            const Key mx = mine > other ? mine : other;
+            const Key mn = mine > other ? other : mine;
+            a[e] = keep_max ? mx : mn;
         }
     }
 }
-
-// The same sort for 32-bit keys (one shuffle per exchange instead of two).
+template <int KK, int J, int E, typename Key>
+SSLP_DEVICE void bitonic_stages(Key (&a)[E], int lane) {  // distances J, J/2, ..., 1 of merge KK
+    bitonic_stage<KK, J>(a, lane);
+    if constexpr (J > 1) bitonic_stages<KK, J / 2>(a, lane);
+}
+template <int KK, int N, int E, typename Key>
+SSLP_DEVICE void bitonic_merges(Key (&a)[E], int lane) {  // merges of size KK, 2 KK, ..., N
+    bitonic_stages<KK, KK / 2>(a, lane);
+    if constexpr (KK < N) bitonic_merges<KK * 2, N>(a, lane);
+}
+template <int E>
+SSLP_DEVICE void bitonic_sort_desc(uint64_t (&a)[E], int lane) {
+    bitonic_merges<2, 64 * E>(a, lane);
+}
+// The same sort for 32-bit keys (one lane exchange per step instead of two).
 template <int E>
 SSLP_DEVICE void bitonic_sort_desc32(uint32_t (&a)[E], int lane) {
-    constexpr int n = 64 * E;
-#pragma unroll
-    for (int kk = 2; kk <= n; kk <<= 1) {
-#pragma unroll
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-            if (j >= 64) {
-                const int je = j >> 6;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int e2 = e ^ je;
-                    if (e2 > e) {
-                        const bool desc = (((e << 6) & kk) == 0);
-                        const uint32_t x = a[e], y = a[e2];
-                        const bool sw = desc ? (x < y) : (x > y);
-                        a[e] = sw ? y : x;
-                        a[e2] = sw ? x : y;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const uint32_t mine = a[e];
-                    const uint32_t other = __shfl_xor(mine, j, kWave);
-                    const int p = (e << 6) | lane;
-                    const bool desc = ((p & kk) == 0);
-                    const bool lower = ((lane & j) == 0);
-                    const bool keep_max = (lower == desc);
-                    const uint32_t mx = mine > other ? mine : other;
-                    const uint32_t mn = mine > other ? other : mine;
-                    a[e] = keep_max ? mx : mn;
-                }
-            }
-        }
-    }
+    bitonic_merges<2, 64 * E>(a, lane);
 }
 
 // element at runtime position p (p = e*64 + lane) of a register-held array,
