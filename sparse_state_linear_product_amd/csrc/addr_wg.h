@@ -13,10 +13,12 @@
 //   2. the dominance set D = {(i, j) : (i+1)(j+1) <= budget}: each wavefront
 //      sorts its 64 entries, one wavefront merges them (merge4_top64);
 //      tau = the budget-th key;
-//   3. F = #{k^2 candidates with key >= tau}; F == budget proves D's
-//      top-budget is the answer, else all k^2 candidates are ranked by
-//      counting (wg_addr_rank_all, the rare path of rounding ties);
-//   4. softmax over the selected scores.
+//   3. F = #{k^2 candidates with key >= tau}, counted by the merging
+//      wavefront; F == budget proves D's top-budget is the answer, else all
+//      k^2 candidates are ranked by counting (wg_addr_rank_all, the rare path
+//      of rounding ties);
+//   4. softmax over the selected scores: on the common path by the same
+//      wavefront inside wg_addr_select, else by wg_addr_softmax.
 // Every function contains block-wide barriers: all threads of the workgroup
 // call it, each 256-thread group on its own problem and shared memory.
 // Limits: sqrtN <= 256, k <= 64, budget <= 64, |D| <= 256.
@@ -82,6 +84,14 @@ SSLP_DEVICE Key bitonic_merge64_desc(Key x, int lane) {
     return x;
 }
 
+// The 64 largest of two descending lists of 64 keys (lst[i], lst[64 + i]), in
+// rank order: lane r returns the rank-r key.  Run by one whole wavefront.
+template <typename Key>
+SSLP_DEVICE Key merge2_top64(const Key* lst, int lane) {
+    const Key a = lst[lane], b = lst[64 + 63 - lane];
+    return bitonic_merge64_desc(a > b ? a : b, lane);
+}
+
 // The 64 largest of four descending lists of 64 keys (lst[64 l + i], list l),
 // in rank order: lane r returns the rank-r key.  Run by one whole wavefront.
 // The elementwise maximum of a descending list and a reversed one holds the 64
@@ -101,9 +111,12 @@ SSLP_DEVICE Key merge4_top64(const Key* lst, int lane) {
     return bitonic_merge64_desc(a0 > r1 ? a0 : r1, lane);
 }
 
-// steps 1-3 up to F (ends with a barrier: sm.F is then valid for every thread)
+// Steps 1-3 and, when F == budget, step 4 into idx / wt (and idx2 / wt2; any
+// of them may be null).  Ends with a barrier: sm.F is then valid for every
+// thread, and F != budget calls for wg_addr_rank_all and wg_addr_softmax.
 template <typename in_t>
-SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm) {
+SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, int32_t* idx,
+                                float* wt, int32_t* idx2, float* wt2) {
     const int lane = t & 63, wv = t >> 6;
     const int n = pr.n, k = pr.k, budget = pr.budget, nD = pr.nD;
     const in_t* h1 = static_cast<const in_t*>(pr.s1);
@@ -162,8 +175,8 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm) 
         }
     }
     __syncthreads();
-    // 2. D in rank order: each wavefront sorts its 64 entries (past nD: key 0,
-    //    below all keys), one wavefront merges the four lists; tau = the
+    // 2. D in rank order: the wavefronts holding entries sort their 64 (past
+    //    nD: key 0, below all keys), one wavefront merges the lists; tau = the
     //    budget-th key (0 if D has fewer than budget entries)
     uint64_t dkey[1] = {0ull};
     if (t < nD) {
@@ -172,26 +185,46 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm) 
         const float sum = sm.hsc[0][i] + sm.hsc[1][j];  // one fp32 RNE add
         dkey[0] = make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + (uint32_t)sm.hix[1][j]);
     }
-    bitonic_sort_desc<1>(dkey, lane);
+    if (wv * 64 < nD) bitonic_sort_desc<1>(dkey, lane);  // uniform over the wavefront
     sm.cand[t] = dkey[0];
     __syncthreads();
     if (wv == 0) {
-        const uint64_t key = merge4_top64(&sm.cand[0], lane);
-        if (lane < budget) sm.sel[lane] = key;
-        if (lane == budget - 1) sm.tau = key;
+        const uint64_t key = nD <= 128 ? merge2_top64(&sm.cand[0], lane) : merge4_top64(&sm.cand[0], lane);
+        const uint64_t tau = shfl_u64(key, budget - 1);
+        // 3. exact count of all k^2 candidates at or above tau: lane column j
+        //    of the candidate matrix held in registers, rows i taken two at a
+        //    time (lanes 32..63 on row i + 1) when k <= 32
+        const bool two = k <= 32;
+        const int jl = two ? (lane & 31) : lane;
+        const int isub = two ? (lane >> 5) : 0;
+        const bool jok = jl < k;
+        const float bj = sm.hsc[1][jok ? jl : 0];
+        const uint32_t bix = (uint32_t)sm.hix[1][jok ? jl : 0];
+        const int step = two ? 2 : 1;
+        int F = 0;
+#pragma unroll 4
+        for (int i0 = 0; i0 < k; i0 += step) {
+            const int i = i0 + isub < k ? i0 + isub : 0;
+            const float sum = sm.hsc[0][i] + bj;  // one fp32 RNE add
+            const bool ge = jok && i0 + isub < k &&
+                            make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + bix) >= tau;
+            F += __popcll(__ballot(ge));
+        }
+        if (F == budget) {
+            // 4. softmax over the selected fp32 scores (rank 0 holds the maximum)
+            const float smax = key_score(shfl_u64(key, 0));
+            const float w = lane < budget ? __expf(key_score(key) - smax) : 0.f;
+            const float z = wave_sum(w);
+            if (lane < budget) {
+                const int32_t slot = (int32_t)key_index(key);
+                if (idx) idx[lane] = slot;
+                if (wt) wt[lane] = w / z;
+                if (idx2) idx2[lane] = slot;
+                if (wt2) wt2[lane] = w / z;
+            }
+        }
+        if (lane == 0) sm.F = F;
     }
-    __syncthreads();
-    // 3. exact count of all k^2 candidates at or above tau
-    const uint64_t tau = sm.tau;
-    const int kk = k * k;
-    int F = 0;
-    for (int x = t; x < kk; x += kAddrGroup) {
-        const int i = x / k, j = x - (x / k) * k;
-        const float sum = sm.hsc[0][i] + sm.hsc[1][j];
-        F += make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + (uint32_t)sm.hix[1][j]) >= tau;
-    }
-    F = (int)wave_sum((float)F);
-    if (lane == 0) atomicAdd(&sm.F, F);
     __syncthreads();
 }
 

@@ -241,10 +241,13 @@ __global__ __launch_bounds__(WG) void sdm_address_wg_kernel(AddrPairArgs a) {
     const WgAddrProblem pr{static_cast<const in_t*>(a.s1[set]) + off,
                            static_cast<const in_t*>(a.s2[set]) + off, a.sqrtN, a.k[set],
                            a.budget[set], a.nD[set]};
-    wg_addr_select<in_t>(pr, t, sm);
-    if (sm.F != pr.budget) wg_addr_rank_all(pr, t, sm);  // uniform over the workgroup
-    wg_addr_softmax(pr, t, sm, a.idx[set] + (size_t)p * pr.budget,
-                    a.wt[set] + (size_t)p * pr.budget, nullptr, nullptr);
+    int32_t* oi = a.idx[set] + (size_t)p * pr.budget;
+    float* ow = a.wt[set] + (size_t)p * pr.budget;
+    wg_addr_select<in_t>(pr, t, sm, oi, ow, nullptr, nullptr);
+    if (sm.F != pr.budget) {  // uniform over the workgroup
+        wg_addr_rank_all(pr, t, sm);
+        wg_addr_softmax(pr, t, sm, oi, ow, nullptr, nullptr);
+    }
 }
 
 int ceil_pow2_units(int n) {  // smallest power of two >= ceil(n/64), at least 1

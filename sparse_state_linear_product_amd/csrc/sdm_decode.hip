@@ -53,14 +53,17 @@ __global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecode
     const WgAddrProblem pr{static_cast<const io_t*>(a.s1[grp]) + soff,
                            static_cast<const io_t*>(a.s2[grp]) + soff, a.sqrtN, a.k[grp],
                            a.budget[grp], a.nD[grp]};
-    wg_addr_select<io_t>(pr, tt, sma[grp]);
-    // both groups take the rare path together, so their barriers stay matched
-    if (sma[0].F != a.budget[0] || sma[1].F != a.budget[1]) wg_addr_rank_all(pr, tt, sma[grp]);
     const bool first = slice == 0;
     int32_t* gi = first && a.idx[grp] ? a.idx[grp] + (size_t)p * pr.budget : nullptr;
     float* gw = first && a.wt[grp] ? a.wt[grp] + (size_t)p * pr.budget : nullptr;
-    wg_addr_softmax(pr, tt, sma[grp], s_idx[grp], s_wt[grp], gi, gw);
-    __syncthreads();
+    wg_addr_select<io_t>(pr, tt, sma[grp], s_idx[grp], s_wt[grp], gi, gw);
+    // both groups take the rare path together, so their barriers stay matched
+    // (a group whose common path already wrote its selection writes it again)
+    if (sma[0].F != a.budget[0] || sma[1].F != a.budget[1]) {
+        wg_addr_rank_all(pr, tt, sma[grp]);
+        wg_addr_softmax(pr, tt, sma[grp], s_idx[grp], s_wt[grp], gi, gw);
+        __syncthreads();
+    }
 
     // ---- the update and the read of this workgroup's columns ----
     UpdSmem& su = *reinterpret_cast<UpdSmem*>(s_raw);
