@@ -19,8 +19,9 @@
 //      of rounding ties);
 //   4. softmax over the selected scores: on the common path by the same
 //      wavefront inside wg_addr_select, else by wg_addr_softmax.
-// Every function contains block-wide barriers: all threads of the workgroup
-// call it, each 256-thread group on its own problem and shared memory.
+// Every function contains block-wide barriers (LDS-only: they do not wait for
+// global stores): all threads of the workgroup call it, each 256-thread group
+// on its own problem and shared memory.
 // Limits: sqrtN <= 256, k <= 64, budget <= 64, |D| <= 256.
 #pragma once
 
@@ -150,7 +151,7 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, 
         bitonic_sort_desc32<1>(x2, lane);
         sm.top32[0][t] = x1[0];
         sm.top32[1][t] = x2[0];
-        __syncthreads();
+        block_sync_lds();
         if (wv < 2) {  // wavefront hh ranks half hh
             const uint32_t key = merge4_top64(&sm.top32[wv][0], lane);
             if (lane < k) {
@@ -165,7 +166,7 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, 
         bitonic_sort_desc<1>(x2, lane);
         sm.top[0][t] = x1[0];
         sm.top[1][t] = x2[0];
-        __syncthreads();
+        block_sync_lds();
         if (wv < 2) {  // wavefront hh ranks half hh
             const uint64_t key = merge4_top64(&sm.top[wv][0], lane);
             if (lane < k) {
@@ -174,7 +175,7 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, 
             }
         }
     }
-    __syncthreads();
+    block_sync_lds();
     // 2. D in rank order: the wavefronts holding entries sort their 64 (past
     //    nD: key 0, below all keys), one wavefront merges the lists; tau = the
     //    budget-th key (0 if D has fewer than budget entries)
@@ -187,7 +188,7 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, 
     }
     if (wv * 64 < nD) bitonic_sort_desc<1>(dkey, lane);  // uniform over the wavefront
     sm.cand[t] = dkey[0];
-    __syncthreads();
+    block_sync_lds();
     if (wv == 0) {
         const uint64_t key = nD <= 128 ? merge2_top64(&sm.cand[0], lane) : merge4_top64(&sm.cand[0], lane);
         const uint64_t tau = shfl_u64(key, budget - 1);
@@ -200,14 +201,20 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, 
         const bool jok = jl < k;
         const float bj = sm.hsc[1][jok ? jl : 0];
         const uint32_t bix = (uint32_t)sm.hix[1][jok ? jl : 0];
+        // row values: lane l holds the first half's rank-l score and index,
+        // broadcast with readlane (no memory round trip per row)
+        const int al = lane < k ? lane : 0;
+        const int a_l = __float_as_int(sm.hsc[0][al]), x_l = sm.hix[0][al];
         const int step = two ? 2 : 1;
         int F = 0;
 #pragma unroll 4
         for (int i0 = 0; i0 < k; i0 += step) {
-            const int i = i0 + isub < k ? i0 + isub : 0;
-            const float sum = sm.hsc[0][i] + bj;  // one fp32 RNE add
+            const int i1 = i0 + 1 < k ? i0 + 1 : i0;
+            const int a0 = __builtin_amdgcn_readlane(a_l, i0), a1 = __builtin_amdgcn_readlane(a_l, i1);
+            const int x0 = __builtin_amdgcn_readlane(x_l, i0), x1 = __builtin_amdgcn_readlane(x_l, i1);
+            const float sum = __int_as_float(isub ? a1 : a0) + bj;  // one fp32 RNE add
             const bool ge = jok && i0 + isub < k &&
-                            make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + bix) >= tau;
+                            make_key(sum, (uint32_t)(isub ? x1 : x0) * (uint32_t)n + bix) >= tau;
             F += __popcll(__ballot(ge));
         }
         if (F == budget) {
@@ -225,26 +232,26 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, 
         }
         if (lane == 0) sm.F = F;
     }
-    __syncthreads();
+    block_sync_lds();
 }
 
 // the rare path: rank all k^2 candidates (three barriers)
 SSLP_DEVICE void wg_addr_rank_all(const WgAddrProblem& pr, int t, WgAddrSmem& sm) {
     const int n = pr.n, k = pr.k, budget = pr.budget, kk = k * k;
-    __syncthreads();
+    block_sync_lds();
     for (int x = t; x < kk; x += kAddrGroup) {
         const int i = x / k, j = x - (x / k) * k;
         const float sum = sm.hsc[0][i] + sm.hsc[1][j];
         sm.cand[x] = make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n + (uint32_t)sm.hix[1][j]);
     }
-    __syncthreads();
+    block_sync_lds();
     for (int x = t; x < kk; x += kAddrGroup) {
         const uint64_t kx = sm.cand[x];
         int r = 0;
         for (int y = 0; y < kk; ++y) r += sm.cand[y] > kx;
         if (r < budget) sm.sel[r] = kx;
     }
-    __syncthreads();
+    block_sync_lds();
 }
 
 // 4. softmax over the selected scores (rank 0 holds the maximum), by the

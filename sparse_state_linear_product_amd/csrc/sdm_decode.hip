@@ -15,7 +15,8 @@
 // the write and read rows of their 256 columns (lane l: columns 4l .. 4l+3, so
 // a wavefront moves a 1 KB row piece in one access), update the write rows and
 // read the read rows after the write; a read slot that the token writes takes
-// its updated value from LDS (write slots are distinct within a token).
+// its updated value from LDS (write slots are distinct within a token).  The
+// barriers wait for LDS operations only, so the table stores stay in flight.
 #include "addr_wg.h"
 #include "common.h"
 #include "kernels.h"
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecode
     if (sma[0].F != a.budget[0] || sma[1].F != a.budget[1]) {
         wg_addr_rank_all(pr, tt, sma[grp]);
         wg_addr_softmax(pr, tt, sma[grp], s_idx[grp], s_wt[grp], gi, gw);
-        __syncthreads();
+        block_sync_lds();
     }
 
     // ---- the update and the read of this workgroup's columns ----
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecode
         acc.w = fmaf(ww[r], mw[r].w, acc.w);
     }
     su.part[w][lane] = acc;
-    __syncthreads();
+    block_sync_lds();
     float4 vh = z4;
 #pragma unroll
     for (int u = 0; u < kWaves; ++u) {
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecode
             if (colok) *reinterpret_cast<float4*>(tab + (size_t)ws[r] * a.dv + col) = nv;
         }
     }
-    __syncthreads();
+    block_sync_lds();
     // read after writing (Eq. 5): lane q < W holds write slot q, so each read
     // row finds the write row holding its slot with one ballot
     const int myw = lane < W ? s_idx[0][lane] : -2;
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecode
         }
     }
     su.part[w][lane] = y;  // every wave read v_hat from su.part before the last barrier
-    __syncthreads();
+    block_sync_lds();
     if (w == 0 && colok) {
         float4 s = z4;
 #pragma unroll
