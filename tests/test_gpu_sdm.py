@@ -137,6 +137,12 @@ def _address_cases():
     g2 = r.standard_normal((2, 100, 2, 240)).astype(np.float32)
     cases.append(("gauss_240_k32_w32", g1, g2, 32, 32))
     cases.append(("gauss_240_k8_w64", g1, g2, 8, 64))
+    # one workgroup per problem with k > 32 (one candidate row per lane pass) and
+    # dominance sets of more than 128 entries (merged from four sorted lists)
+    cases.append(("gauss_240_k40_w40_D158", g1, g2, 40, 40))
+    cases.append(("quantized_240_k48_w64_D248", q1, q2, 48, 64))
+    cases.append(("quantized_240_k64_w48_D198", q1, q2, 64, 48))
+    cases.append(("gauss_240_k33_w33_D123", g1, g2, 33, 33))
     # more than 1024 problems: the one-wavefront-per-problem kernel (fewer: one
     # workgroup per problem); the same exact selection either way
     q3 = r.integers(-3, 4, (2, 400, 2, 240)).astype(np.float32)
