@@ -13,6 +13,7 @@ bandwidth using the algorithmic bytes it must move; `cpu_baseline` times the
 fp64 oracle on the host.
 """
 import argparse
+import dataclasses
 import json
 import os
 import re
@@ -196,6 +197,25 @@ def bench_rows(args, torch, sslp, wl):
                                        hbm_frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                        bytes_per_call=by)
     del x, S, o
+    # SSE grouped (varlen) against masked execution over sequence lengths, the
+    # comparison of the SSE slides' Fig. 6 (there: fwd+bwd on another GPU; here
+    # the forward): B=4, H=16, c=d=128, N routed partitions, top-k
+    sweep = {}
+    for N, topk in ((4, 1), (8, 1), (8, 2)):
+        for T in (256, 1024, 4096):
+            c2 = dataclasses.replace(wl.SSE, N=N, topk=topk, T=T)
+            x = {k: v.to(dev) for k, v in wl.sse_inputs(c2).items()}
+            S = torch.zeros((c2.B, c2.H, N + 1, c2.c, c2.d), dtype=torch.float32, device=dev)
+            o = torch.empty_like(x["v"])
+            reps = max(3, args.steps)
+            t_var = time_call(torch, lambda: sslp.sse_forward(x["logits"], x["q"], x["k"], x["v"],
+                                                              x["lam"], S, topk, o=o), reps)
+            t_msk = time_call(torch, lambda: sslp.sse_forward(x["logits"], x["q"], x["k"], x["v"],
+                                                              x["lam"], S, topk, o=o, masking=True),
+                              reps)
+            sweep[f"N{N}_k{topk}_T{T}"] = dict(varlen_ms=round(t_var, 4), masking_ms=round(t_msk, 4))
+            del x, S, o
+    rows["sse_masking_vs_varlen_B4_H16_c128"] = sweep
     # SSE decode: 64 independent sequences, N=8 routed + 1 shared states of 128x128 per head;
     # a step reads and writes the 2 selected and the shared state of every (sequence, head)
     cfg = wl.SSE_DECODE
