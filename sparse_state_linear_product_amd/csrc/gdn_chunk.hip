@@ -336,7 +336,8 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
                     pall *= al;
                     if (r > 0) {
                         ep *= al;
-                        em *= __frcp_rn(al);
+                        // hardware reciprocal (within 1 ulp): Km is rounded to bf16
+                        em *= __builtin_amdgcn_rcpf(al);
                     }
                     const float kv = bf2f(sm.k[t][i]), qv = bf2f(sm.q[t][i]);
                     float ke = kv;  // the key of A's rows and of Wn: b (.) k for GDN2

@@ -157,8 +157,10 @@ SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs&
                     } else {
                         ep0 *= l0;
                         ep1 *= l1;
-                        em0 *= __frcp_rn(l0);
-                        em1 *= __frcp_rn(l1);
+                        // hardware reciprocal (within 1 ulp, not an IEEE division):
+                        // the factor only scales a key that is rounded to bf16
+                        em0 *= __builtin_amdgcn_rcpf(l0);
+                        em1 *= __builtin_amdgcn_rcpf(l1);
                     }
                 }
                 *reinterpret_cast<uint32_t*>(&ws.qs[p][2 * lane]) =
