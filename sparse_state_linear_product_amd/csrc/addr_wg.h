@@ -207,7 +207,6 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, 
         const int a_l = __float_as_int(sm.hsc[0][al]), x_l = sm.hix[0][al];
         const int step = two ? 2 : 1;
         int F = 0;
-#pragma unroll 4
         for (int i0 = 0; i0 < k; i0 += step) {
             const int i1 = i0 + 1 < k ? i0 + 1 : i0;
             const int a0 = __builtin_amdgcn_readlane(a_l, i0), a1 = __builtin_amdgcn_readlane(a_l, i1);
