@@ -102,6 +102,10 @@ SSLP_DEVICE uint64_t xor_lane_u64(uint64_t v, int j, int lane) {
     return ((uint64_t)hi << 32) | lo;
 }
 SSLP_DEVICE uint64_t shfl_xor_u64(uint64_t v, int mask) { return xor_lane_u64(v, mask, lane_id()); }
+SSLP_DEVICE float xor_lane_f(float x, int j, int lane) {
+    return __uint_as_float(xor_lane(__float_as_uint(x), j, lane));
+}
+SSLP_DEVICE int xor_lane_i(int x, int j, int lane) { return (int)xor_lane((uint32_t)x, j, lane); }
 SSLP_DEVICE uint64_t shfl_u64(uint64_t v, int src) {
     uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
     lo = __shfl(lo, src, kWave);

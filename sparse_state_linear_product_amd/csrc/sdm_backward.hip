@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
 #pragma unroll
         for (int s = 1; s < 16; s <<= 1)
 #pragma unroll
-            for (int r = 0; r < NL; ++r) fix[r] += __shfl_xor(fix[r], s, 64);
+            for (int r = 0; r < NL; ++r) fix[r] += xor_lane_f(fix[r], s, lane_id());
         const float dyc = colok ? cur.dyc : 0.f, vc = colok ? cur.vc : 0.f;
         const float al = cur.al, be = cur.be;
         // ---- read after writing: de and the read contribution to G ----
@@ -169,10 +169,10 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
             vh = fmaf(w[r], mt[r], vh);
             dr = fmaf(be * w[r], gn[r], dr);
         }
-        vh += __shfl_xor(vh, 16, 64);
-        vh += __shfl_xor(vh, 32, 64);
-        dr += __shfl_xor(dr, 16, 64);
-        dr += __shfl_xor(dr, 32, 64);
+        vh += xor_lane_f(vh, 16, lane_id());
+        vh += xor_lane_f(vh, 32, lane_id());
+        dr += xor_lane_f(dr, 16, lane_id());
+        dr += xor_lane_f(dr, 32, lane_id());
         const float rres = vc - vh;
         float pw[NL];
         float pa = 0.f, pb = 0.f;
@@ -196,16 +196,16 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
         for (int s = 1; s < 16; s <<= 1) {
 #pragma unroll
             for (int r = 0; r < NL; ++r) {
-                pe[r] += __shfl_xor(pe[r], s, 64);
-                pw[r] += __shfl_xor(pw[r], s, 64);
+                pe[r] += xor_lane_f(pe[r], s, lane_id());
+                pw[r] += xor_lane_f(pw[r], s, lane_id());
             }
-            pa += __shfl_xor(pa, s, 64);
-            pb += __shfl_xor(pb, s, 64);
+            pa += xor_lane_f(pa, s, lane_id());
+            pb += xor_lane_f(pb, s, lane_id());
         }
-        pa += __shfl_xor(pa, 16, 64);
-        pa += __shfl_xor(pa, 32, 64);
-        pb += __shfl_xor(pb, 16, 64);
-        pb += __shfl_xor(pb, 32, 64);
+        pa += xor_lane_f(pa, 16, lane_id());
+        pa += xor_lane_f(pa, 32, lane_id());
+        pb += xor_lane_f(pb, 16, lane_id());
+        pb += xor_lane_f(pb, 32, lane_id());
         float* pp = a.part + (bth * nslice + slice) * NP;
         if (c == 0) {
 #pragma unroll
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(64 * kAbWaves) void sdm_address_bwd_kernel(
     float dot = 0.f;
     for (int m = lane; m < budget; m += 64) dot = fmaf(w[m], dw[m], dot);
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) dot += __shfl_xor(dot, s, 64);
+    for (int s = 32; s >= 1; s >>= 1) dot += xor_lane_f(dot, s, lane_id());
     for (int m = lane; m < budget; m += 64) {
         const int n = ip[m];
         s_ds[wv][m] = w[m] * (dw[m] - dot);

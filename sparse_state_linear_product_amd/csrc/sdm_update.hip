@@ -108,8 +108,8 @@ __global__ __launch_bounds__(64) void sdm_update_kernel(SdmUpdateArgs a) {
             float acc = 0.f;
 #pragma unroll
             for (int r = 0; r < NL; ++r) acc = fmaf(w[r], mt[r], acc);
-            acc += __shfl_xor(acc, 16, 64);
-            acc += __shfl_xor(acc, 32, 64);
+            acc += xor_lane_f(acc, 16, lane_id());
+            acc += xor_lane_f(acc, 32, lane_id());
             const float res = vc - acc;
 #pragma unroll
             for (int r = 0; r < NL; ++r) nv[r] = fmaf(be * w[r], res, mt[r]);
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(64) void sdm_update_kernel(SdmUpdateArgs a) {
 #pragma unroll
         for (int s = 1; s < 16; s <<= 1)
 #pragma unroll
-            for (int r = 0; r < NL; ++r) hit[r] = max(hit[r], __shfl_xor(hit[r], s, 64));
+            for (int r = 0; r < NL; ++r) hit[r] = max(hit[r], xor_lane_i(hit[r], s, lane_id()));
         float acc = 0.f;
 #pragma unroll
         for (int r = 0; r < NL; ++r) {
@@ -154,8 +154,8 @@ __global__ __launch_bounds__(64) void sdm_update_kernel(SdmUpdateArgs a) {
                 acc = fmaf(cur.e[r], m, acc);
             }
         }
-        acc += __shfl_xor(acc, 16, 64);
-        acc += __shfl_xor(acc, 32, 64);
+        acc += xor_lane_f(acc, 16, lane_id());
+        acc += xor_lane_f(acc, 32, lane_id());
         if (g == 0 && colok) yout[bth * a.dv + col] = from_f32<io_t>(acc);
         wave_sync();
         cur = nxt;
