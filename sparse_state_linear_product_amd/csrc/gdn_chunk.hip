@@ -203,6 +203,10 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
     uint4 pk[NSG], pq[NSG], pv[NSG];
     float4 pa[NSA > 0 ? NSA : 1];
     float pbeta = 0.f, palpha = 1.f;
+    // GDN2: the write vector of this thread's V pieces, and the erase values of
+    // its decay-pass tokens (channel tid % DK, tokens 32 (tid / DK) ..), also a chunk ahead
+    float4 pw[G2 ? NSG : 1][2];
+    float pbv[G2 ? 32 : 1];
     // Loads come from clamped (always valid) token rows and are masked where
     // they are stored, so no load waits on a condition (a conditional load
     // would be followed by a wait for its value at the branch join).
@@ -232,6 +236,22 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
                 pa[i] = *reinterpret_cast<const float4*>(a.alpha + (((size_t)b * T + t) * H + h) * DK + col);
             }
         }
+        if constexpr (G2) {
+#pragma unroll
+            for (int i = 0; i < NSG; ++i) {
+                const int col = 8 * (w + (NTH / 64) * i);
+                const int t = min(t0 + lane, T - 1);
+                const float* wr = a.wvec + (((size_t)b * T + t) * H + h) * dv + col;
+                pw[i][0] = *reinterpret_cast<const float4*>(wr);
+                pw[i][1] = *reinterpret_cast<const float4*>(wr + 4);
+            }
+            const int ch = tid & (DK - 1), hf = tid >> 7;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                const int t = min(t0 + 32 * hf + r, T - 1);
+                pbv[r] = a.bvec[(((size_t)b * T + t) * H + h) * DK + ch];
+            }
+        }
         {  // every wave: the gates of token row = lane
             const int t = min(t0 + lane, T - 1);
             const size_t bth = ((size_t)b * T + t) * H + h;
@@ -241,8 +261,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
     };
     if ((int)blockIdx.x < ntask) fetch(blockIdx.x);
     for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const int c = task % nch, bh = task / nch;
-    const int b = bh / H, h = bh - (bh / H) * H;
+    const int c = task % nch;
 
     uint8_t* rec = a.rec + (size_t)task * REC_BYTES;
     block_sync_lds();  // the previous chunk's use of the shared arrays is over
@@ -263,10 +282,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
         const uint16_t* ve = reinterpret_cast<const uint16_t*>(&pv[i]);
         float sc[8];
         if constexpr (G2) {  // X = w (.) V (rows past the end: V is zero already)
-            const int t = min(c * C + row, T - 1);
-            const float* wr = a.wvec + (((size_t)b * T + t) * H + h) * dv + col;
-            const float4 w0 = *reinterpret_cast<const float4*>(wr);
-            const float4 w1 = *reinterpret_cast<const float4*>(wr + 4);
+            const float4 w0 = pw[i][0], w1 = pw[i][1];
             sc[0] = w0.x, sc[1] = w0.y, sc[2] = w0.z, sc[3] = w0.w;
             sc[4] = w1.x, sc[5] = w1.y, sc[6] = w1.z, sc[7] = w1.w;
         } else {
@@ -290,8 +306,10 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
         if (!KDA) sm.g[tid] = __logf(palpha);
     }
     // the next chunk's inputs, in flight during this chunk (the last chunk
-    // fetches itself again: an unconditional fetch keeps the loads free of waits)
-    fetch(task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task);
+    // fetches itself again: an unconditional fetch keeps the loads free of
+    // waits); GDN2 fetches after the decay pass, which reads this chunk's
+    // prefetched erase values
+    if constexpr (!G2) fetch(task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task);
     block_sync_lds();
 
         // ---------------- decay bookkeeping ----------------
@@ -320,14 +338,11 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             for (int bb = 0; bb < 2; ++bb) {
                 const int blk = 2 * hf + bb;
                 float ep = 1.f, em = 1.f, pall = 1.f;
-                // GDN2: the block's 16 erase values, all requested before any is used
+                // GDN2: the block's 16 erase values (prefetched with the chunk)
                 float bv[16];
                 if constexpr (G2) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int tt = min(c * C + 16 * blk + r, T - 1);
-                        bv[r] = a.bvec[(((size_t)b * T + tt) * H + h) * DK + i];
-                    }
+                    for (int r = 0; r < 16; ++r) bv[r] = pbv[16 * bb + r];
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -352,6 +367,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             }
         }
         block_sync_lds();
+        if constexpr (G2) fetch(task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task);
         if constexpr (KDA) {
             // per channel: F[m] = e^{g_{16m}}, H[m] = e^{g_C - g_{16m}},
             // D[m][n] = e^{g_{16m} - g_{16n}}, all as products of alphas
