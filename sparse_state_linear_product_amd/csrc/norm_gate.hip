@@ -38,10 +38,13 @@ SSLP_DEVICE void store4(bf16_t* p, float4 v) {
     *reinterpret_cast<uint2*>(p) = u;
 }
 
+// The logistic factor 1 / (1 + e^-x) with the hardware exponential and
+// reciprocal (a few ulp in fp32, not an IEEE division): the kernel was bound by
+// the per-element division sequence, not by memory.
 template <int ACT>
 SSLP_DEVICE float gate_fn(float x) {
-    if constexpr (ACT == 1) return x / (1.f + expf(-x));
-    else if constexpr (ACT == 2) return 1.f / (1.f + expf(-x));
+    if constexpr (ACT == 1) return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+    else if constexpr (ACT == 2) return __builtin_amdgcn_rcpf(1.f + __expf(-x));
     else return 1.f;
 }
 
