@@ -331,11 +331,15 @@ def cpu_baseline_sdm(wl, torch):
         if el >= 10.0 or reps >= 20:
             break
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=round(cfg.B * cfg.T * reps / el, 1), unit="tokens/s", cores=threads,
+    # the addressing runs one problem per thread over all threads; the recurrence
+    # runs one (b, h, 64-column block) unit per thread
+    units = cfg.B * cfg.H * -(-cfg.d_v // 64)
+    used = min(threads, units)
+    return dict(value=round(cfg.B * cfg.T * reps / el, 1), unit="tokens/s", cores=used,
                 kind="oracle",
                 sample=f"full workload ({cfg.B * cfg.T} tokens x {cfg.H} heads) repeated {reps}x, "
-                       f"{el:.1f} s; fp64 C/OpenMP oracle (addressing over all threads, "
-                       f"recurrence over the {cfg.B * cfg.H} (b,h) units)")
+                       f"{el:.1f} s; fp64 C/OpenMP oracle on {used} threads (addressing: one "
+                       f"problem per thread; recurrence: {units} (b, h, 64-column) units)")
 
 
 def main():

@@ -117,59 +117,70 @@ int orc_sdm_address(int P, int sqrtN, const float* s1, const float* s2, int k, i
  *       M[i_n] = M~[i_n] + beta*wt_n*(v - M~[i_n])
  *   then y = sum_m wt_r_m M[j_m] on the updated table.
  * Slots not in the token's write set are never touched.
- * Parallel over (b,h) only; the token loop is the plain sequential order.
+ * Given the addressing every operation above acts on one column c of d_v at a
+ * time (the shared prediction v_hat[c] included), so the columns are separate
+ * recurrences; the loops run over (b, h, block of ORC_COLS columns) in
+ * parallel, the token loop inside in the plain sequential order.  Each
+ * column's arithmetic is the same sequence of fp64 operations whatever the
+ * block size.
  */
+#define ORC_COLS 64
 int orc_sdm_recurrence(int B, int T, int H, long long N, int dv, int W, int R, int residual_mode,
                        const int32_t* idx_w, const double* wt_w, const int32_t* idx_r,
                        const double* wt_r, const float* v, const float* alpha, const float* beta,
                        double* M, double* y) {
     if (B < 0 || T < 0 || H <= 0 || N <= 0 || dv <= 0 || W <= 0 || R <= 0) return -1;
     if (residual_mode != 0 && residual_mode != 1) return -1;
-#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    const int nblk = (dv + ORC_COLS - 1) / ORC_COLS;
+#pragma omp parallel for collapse(3) schedule(dynamic, 1)
     for (int b = 0; b < B; ++b)
-        for (int h = 0; h < H; ++h) {
-            double* tab = M + ((size_t)b * H + h) * (size_t)N * dv;
-            double* mt = (double*)malloc(sizeof(double) * (size_t)W * dv); /* M~ rows */
-            double* vhat = (double*)malloc(sizeof(double) * dv);
-            for (int t = 0; t < T; ++t) {
-                size_t bth = ((size_t)b * T + t) * H + h;
-                const int32_t* iw = idx_w + bth * W;
-                const double* gw = wt_w + bth * W;
-                const int32_t* ir = idx_r + bth * R;
-                const double* gr = wt_r + bth * R;
-                const float* vt = v + bth * dv;
-                double a = alpha[bth], be = beta[bth];
-                /* Eq. (3): decay of the selected write slots */
-                for (int n = 0; n < W; ++n)
-                    for (int c = 0; c < dv; ++c) mt[(size_t)n * dv + c] = a * tab[(size_t)iw[n] * dv + c];
-                if (residual_mode == 0) {
-                    for (int c = 0; c < dv; ++c) {
-                        double s = 0.0;
-                        for (int n = 0; n < W; ++n) s += gw[n] * mt[(size_t)n * dv + c];
-                        vhat[c] = s;
+        for (int h = 0; h < H; ++h)
+            for (int blk = 0; blk < nblk; ++blk) {
+                const int c0 = blk * ORC_COLS;
+                const int c1 = c0 + ORC_COLS < dv ? c0 + ORC_COLS : dv;
+                double* tab = M + ((size_t)b * H + h) * (size_t)N * dv;
+                double* mt = (double*)malloc(sizeof(double) * (size_t)W * dv); /* M~ rows */
+                double* vhat = (double*)malloc(sizeof(double) * dv);
+                for (int t = 0; t < T; ++t) {
+                    size_t bth = ((size_t)b * T + t) * H + h;
+                    const int32_t* iw = idx_w + bth * W;
+                    const double* gw = wt_w + bth * W;
+                    const int32_t* ir = idx_r + bth * R;
+                    const double* gr = wt_r + bth * R;
+                    const float* vt = v + bth * dv;
+                    double a = alpha[bth], be = beta[bth];
+                    /* Eq. (3): decay of the selected write slots */
+                    for (int n = 0; n < W; ++n)
+                        for (int c = c0; c < c1; ++c)
+                            mt[(size_t)n * dv + c] = a * tab[(size_t)iw[n] * dv + c];
+                    if (residual_mode == 0) {
+                        for (int c = c0; c < c1; ++c) {
+                            double s = 0.0;
+                            for (int n = 0; n < W; ++n) s += gw[n] * mt[(size_t)n * dv + c];
+                            vhat[c] = s;
+                        }
+                        for (int n = 0; n < W; ++n)
+                            for (int c = c0; c < c1; ++c)
+                                tab[(size_t)iw[n] * dv + c] =
+                                    mt[(size_t)n * dv + c] + be * gw[n] * ((double)vt[c] - vhat[c]);
+                    } else {
+                        for (int n = 0; n < W; ++n)
+                            for (int c = c0; c < c1; ++c)
+                                tab[(size_t)iw[n] * dv + c] =
+                                    mt[(size_t)n * dv + c] +
+                                    be * gw[n] * ((double)vt[c] - mt[(size_t)n * dv + c]);
                     }
-                    for (int n = 0; n < W; ++n)
-                        for (int c = 0; c < dv; ++c)
-                            tab[(size_t)iw[n] * dv + c] =
-                                mt[(size_t)n * dv + c] + be * gw[n] * ((double)vt[c] - vhat[c]);
-                } else {
-                    for (int n = 0; n < W; ++n)
-                        for (int c = 0; c < dv; ++c)
-                            tab[(size_t)iw[n] * dv + c] =
-                                mt[(size_t)n * dv + c] +
-                                be * gw[n] * ((double)vt[c] - mt[(size_t)n * dv + c]);
+                    /* Eq. (5): read after writing */
+                    double* yt = y + bth * dv;
+                    for (int c = c0; c < c1; ++c) {
+                        double s = 0.0;
+                        for (int m = 0; m < R; ++m) s += gr[m] * tab[(size_t)ir[m] * dv + c];
+                        yt[c] = s;
+                    }
                 }
-                /* Eq. (5): read after writing */
-                double* yt = y + bth * dv;
-                for (int c = 0; c < dv; ++c) {
-                    double s = 0.0;
-                    for (int m = 0; m < R; ++m) s += gr[m] * tab[(size_t)ir[m] * dv + c];
-                    yt[c] = s;
-                }
+                free(mt);
+                free(vhat);
             }
-            free(mt);
-            free(vhat);
-        }
     return 0;
 }
 

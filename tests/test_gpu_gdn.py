@@ -31,8 +31,8 @@ def _ref(x, S0, kda):
 def _check(x, kda, S0=None, inplace=False, tag=""):
     o, S = _run(x, S0, inplace)
     Sr, orf = _ref(x, S0, kda)
-    e_o = maxrel(o.double().numpy(), orf)
-    e_S = maxrel(S.double().numpy(), Sr)
+    e_o = maxrel(o.double().numpy(), orf, name="o")
+    e_S = maxrel(S.double().numpy(), Sr, name="S")
     print(f"  {tag}: o {e_o:.2e} S {e_S:.2e}", flush=True)
     assert np.isfinite(o.float().numpy()).all() and np.isfinite(S.numpy()).all()
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16, f"{tag}: o {e_o} S {e_S}"
@@ -66,8 +66,8 @@ def test_kda_uniform_channels_matches_gdn():
     o1, S1 = sslp.gdn_chunk_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"])
     o2, S2 = sslp.gdn_chunk_forward(xd["q"], xd["k"], xd["v"], a_ch, xd["beta"])
     torch.cuda.synchronize()
-    assert maxrel(o2.cpu().double().numpy(), o1.cpu().double().numpy()) <= 1e-2
-    assert maxrel(S2.cpu().double().numpy(), S1.cpu().double().numpy()) <= 1e-2
+    assert maxrel(o2.cpu().double().numpy(), o1.cpu().double().numpy(), name="o2") <= 1e-2
+    assert maxrel(S2.cpu().double().numpy(), S1.cpu().double().numpy(), name="S2") <= 1e-2
 
 
 def test_gdn_empty_sequence_copies_state():
@@ -112,7 +112,7 @@ def test_gdn2_small(T):
     x = wl.gdn2_inputs(wl.GDN2, T=T, B=2, H=3, seed=500 + T)
     o, S = _run2(x)
     Sr, orf = _ref2(x)
-    e_o, e_S = maxrel(o.double().numpy(), orf), maxrel(S.double().numpy(), Sr)
+    e_o, e_S = maxrel(o.double().numpy(), orf, name="o"), maxrel(S.double().numpy(), Sr, name="S")
     print(f"  gdn2 T={T}: o {e_o:.2e} S {e_S:.2e}", flush=True)
     assert np.isfinite(o.float().numpy()).all() and np.isfinite(S.numpy()).all()
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16
@@ -125,15 +125,15 @@ def test_gdn2_with_initial_state_and_kda_reduction():
     S0 = torch.randn((1, 2, 128, 128), generator=torch.Generator().manual_seed(42)) * 0.5
     o, S = _run2(x, S0)
     Sr, orf = _ref2(x, S0)
-    assert maxrel(o.double().numpy(), orf) <= TOL_BF16
-    assert maxrel(S.double().numpy(), Sr) <= TOL_BF16
+    assert maxrel(o.double().numpy(), orf, name="o") <= TOL_BF16
+    assert maxrel(S.double().numpy(), Sr, name="S") <= TOL_BF16
     x["erase"] = x["beta"][..., None].expand(-1, -1, -1, 128).contiguous()
     x["write"] = x["beta"][..., None].expand(-1, -1, -1, 128).contiguous()
     o, S = _run2(x, S0)
     n = {k: wl.to_numpy_f32(v) for k, v in x.items()}
     Sk, ok = oracle.gdn(n["q"], n["k"], n["v"], n["alpha"], n["beta"], S0=S0.double().numpy(),
                         kda=True)
-    e_o, e_S = maxrel(o.double().numpy(), ok), maxrel(S.double().numpy(), Sk)
+    e_o, e_S = maxrel(o.double().numpy(), ok, name="o"), maxrel(S.double().numpy(), Sk, name="S")
     print(f"  gdn2 as KDA: o {e_o:.2e} S {e_S:.2e}", flush=True)
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16
 
@@ -158,7 +158,7 @@ def test_gdn2_full_config():
     x = wl.gdn2_inputs(cfg)
     o, S = _run2(x)
     Sr, orf = _ref2(x)
-    e_o = maxrel(o.double().numpy(), orf)
-    e_S = maxrel(S.double().numpy(), Sr)
+    e_o = maxrel(o.double().numpy(), orf, name="o")
+    e_S = maxrel(S.double().numpy(), Sr, name="S")
     print(f"  {cfg.name}: o {e_o:.2e} S {e_S:.2e}", flush=True)
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16

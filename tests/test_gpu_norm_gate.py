@@ -31,7 +31,7 @@ def test_norm_gate_matches_oracle(dtype, tol, act, rows, d):
                            eps=1e-6, act=act)
     torch.cuda.synchronize()
     ref = oracle.norm_gate(wl.to_numpy_f32(y), wl.to_numpy_f32(gate), gamma.numpy(), 1e-6, act)
-    e = maxrel(o.cpu().double().numpy(), ref)
+    e = maxrel(o.cpu().double().numpy(), ref, name="o")
     print(f"  {act} {rows}x{d}: {e:.2e}", flush=True)
     assert e <= tol
 
@@ -46,7 +46,7 @@ def test_norm_gate_in_place_zero_rows_and_zero_row():
     out = sslp.sdm_norm_gate(yd, gamma.to(DEV), gate.to(DEV), eps=1e-5, act="silu", o=yd)
     torch.cuda.synchronize()
     assert out.data_ptr() == yd.data_ptr()
-    assert maxrel(yd.cpu().double().numpy(), ref) <= TOL_FP32
+    assert maxrel(yd.cpu().double().numpy(), ref, name="yd") <= TOL_FP32
     assert torch.all(yd[3] == 0)
     empty = torch.empty((0, 64), device=DEV)
     assert sslp.sdm_norm_gate(empty, gamma.to(DEV), empty, act="silu").shape == (0, 64)
@@ -75,4 +75,4 @@ def test_norm_gate_after_sdm_forward_full_size():
     ref = oracle.norm_gate(wl.to_numpy_f32(yf.cpu()), wl.to_numpy_f32(gf.cpu()),
                            gamma.cpu().numpy(), 1e-6, "silu")
     got = o.reshape(-1, cfg.d_v)[torch.from_numpy(rows).to(DEV)].cpu().double().numpy()
-    assert maxrel(got, ref) <= TOL_BF16
+    assert maxrel(got, ref, name="got") <= TOL_BF16

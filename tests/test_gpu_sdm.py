@@ -52,8 +52,8 @@ def _check(cfg, got, ref, M0, tag):
     np.testing.assert_array_equal(got["idx_r"], ref["idx_r"], err_msg=f"{tag}: read indices")
     e_w = np.abs(got["wt_w"] - ref["wt_w"]).max()
     e_r = np.abs(got["wt_r"] - ref["wt_r"]).max()
-    e_y = maxrel(got["y"].double().numpy(), ref["y"])
-    e_M = maxrel(got["M"].double().numpy(), ref["M"])
+    e_y = maxrel(got["y"].double().numpy(), ref["y"], name="y")
+    e_M = maxrel(got["M"].double().numpy(), ref["M"], name="M")
     print(f"  {tag}: wt_w {e_w:.2e} wt_r {e_r:.2e} y {e_y:.2e} M {e_M:.2e}", flush=True)
     assert e_w <= TOL_FP32 and e_r <= TOL_FP32
     # the table arithmetic is fp32 whatever the input dtype; y is rounded to the io dtype
@@ -197,7 +197,7 @@ def test_sparse_update_dense_limit_is_gdn():
     torch.cuda.synchronize()
     S, o = oracle.gdn(q.numpy(), k.numpy(), v.numpy(), alpha.numpy(), beta.numpy(),
                       S0=S0.double().numpy())
-    e_y, e_M = maxrel(y.cpu().double().numpy(), o), maxrel(M.cpu().double().numpy(), S)
+    e_y, e_M = maxrel(y.cpu().double().numpy(), o, name="y"), maxrel(M.cpu().double().numpy(), S, name="M")
     print(f"  dense limit: y {e_y:.2e} M {e_M:.2e}", flush=True)
     assert e_y <= TOL_FP32 and e_M <= TOL_FP32
 
@@ -226,8 +226,8 @@ def test_decode_steps_equal_forward_and_chaining():
     yc = [sslp.sdm_forward(p["sw1"], p["sw2"], p["sr1"], p["sr2"], p["v"], p["alpha"], p["beta"],
                            Mc, cfg.k_w, cfg.k_r, cfg.W, cfg.R) for p in part]
     torch.cuda.synchronize()
-    assert maxrel(yd.cpu().float().numpy(), yf.cpu().float().numpy()) <= 1e-6
-    assert maxrel(Md.cpu().numpy(), Mf.cpu().numpy()) <= 1e-6
+    assert maxrel(yd.cpu().float().numpy(), yf.cpu().float().numpy(), name="yd") <= 1e-6
+    assert maxrel(Md.cpu().numpy(), Mf.cpu().numpy(), name="Md") <= 1e-6
     assert torch.equal(torch.cat(yc, 1).cpu(), yf.cpu())
     assert torch.equal(Mc.cpu(), Mf.cpu())
 
@@ -319,8 +319,8 @@ def test_sdm_decode_full_size():
     post = torch.gather(M, 2, rows_t[..., None].expand(-1, -1, -1, cfg.d_v)).cpu().double().numpy()
     # rows of the compact reference in the same order as `rows`
     Mrows = np.take_along_axis(Mref, loc[..., None].astype(np.int64), axis=2)
-    e_y = maxrel(y.cpu().double().numpy(), yref[:, 0])
-    e_M = maxrel(post, Mrows)
+    e_y = maxrel(y.cpu().double().numpy(), yref[:, 0], name="y")
+    e_M = maxrel(post, Mrows, name="M_rows")
     print(f"  decode full: y {e_y:.2e} M rows {e_M:.2e}", flush=True)
     assert e_y <= TOL_BF16 and e_M <= TOL_FP32
     after = torch.gather(M, 2, sample_t[..., None].expand(-1, -1, -1, cfg.d_v)).cpu()

@@ -43,7 +43,7 @@ def _gpu_train(x, cfg, M0, dy, dM, mode):
 
 def _compare(got, ref, keys, tol, tag):
     for k_got, k_ref in keys:
-        e = maxrel(got[k_got].double().numpy(), ref[k_ref])
+        e = maxrel(got[k_got].double().numpy(), ref[k_ref], name=k_got)
         print(f"  {tag} {k_got}: {e:.2e}", flush=True)
         assert e <= tol, f"{tag} {k_got}: {e}"
 
@@ -63,7 +63,7 @@ def _check_full(cfg, mode, tol):
                                residual_mode=mode)
     np.testing.assert_array_equal(got["idx_w"], ref_f["idx_w"])
     np.testing.assert_array_equal(got["idx_r"], ref_f["idx_r"])
-    assert maxrel(got["y"].double().numpy(), ref_f["y"]) <= tol
+    assert maxrel(got["y"].double().numpy(), ref_f["y"], name="y") <= tol
     # every write undone: the table is back to M0, bit for bit
     assert torch.equal(got["M_restored"], M0)
     ref = oracle.sdm_backward(n["sw1"], n["sw2"], n["sr1"], n["sr2"], n["v"], n["alpha"],

@@ -39,8 +39,8 @@ def _check(x, N, topk, tag, S0=None, q_sh=None, k_sh=None, masking=False):
     ref = _ref(x, topk, S0, q_sh, k_sh, masking)
     np.testing.assert_array_equal(got["sel"], ref["sel"], err_msg=f"{tag}: selection")
     e_e = np.abs(got["e_sel"] - ref["e_sel"]).max()
-    e_o = maxrel(got["o"].double().numpy(), ref["o"])
-    e_S = maxrel(got["S"].double().numpy(), ref["S"])
+    e_o = maxrel(got["o"].double().numpy(), ref["o"], name="o")
+    e_S = maxrel(got["S"].double().numpy(), ref["S"], name="S")
     print(f"  {tag}: e_sel {e_e:.2e} o {e_o:.2e} S {e_S:.2e}", flush=True)
     assert e_e <= TOL_FP32
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16, f"{tag}: o {e_o} S {e_S}"
@@ -129,15 +129,15 @@ def test_sse_masking_agrees_with_varlen_and_keeps_idle_states():
     b = _run(x, 8, 2, S0, q_sh, k_sh, masking=False)
     np.testing.assert_array_equal(a["sel"], b["sel"])
     np.testing.assert_array_equal(a["e_sel"], b["e_sel"])
-    e_o = maxrel(a["o"].double().numpy(), b["o"].double().numpy())
-    e_S = maxrel(a["S"].double().numpy(), b["S"].double().numpy())
+    e_o = maxrel(a["o"].double().numpy(), b["o"].double().numpy(), name="o")
+    e_S = maxrel(a["S"].double().numpy(), b["S"].double().numpy(), name="S")
     print(f"  masking vs varlen: o {e_o:.2e} S {e_S:.2e}", flush=True)
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16
     assert torch.equal(a["S"][0, :, 6], S0[0, :, 6])
     # the shared partition runs the same steps in both executions
     assert torch.equal(a["S"][0, :, 8], b["S"][0, :, 8])
     ref = _ref(x, 2, S0, q_sh, k_sh, masking=True)
-    assert maxrel(a["o"].double().numpy(), ref["o"]) <= TOL_BF16
+    assert maxrel(a["o"].double().numpy(), ref["o"], name="o") <= TOL_BF16
 
 
 # ---------------- decode step (one token per sequence) ----------------
@@ -175,8 +175,8 @@ def test_sse_decode_steps_match_oracle(N, topk, B, H, T):
     ref = _ref(x, topk, S0)
     np.testing.assert_array_equal(got["sel"], ref["sel"], err_msg="decode selection")
     e_e = np.abs(got["e_sel"] - ref["e_sel"]).max()
-    e_o = maxrel(got["o"].double().numpy(), ref["o"])
-    e_S = maxrel(got["S"].double().numpy(), ref["S"])
+    e_o = maxrel(got["o"].double().numpy(), ref["o"], name="o")
+    e_S = maxrel(got["S"].double().numpy(), ref["S"], name="S")
     print(f"  decode N={N} k={topk}: e_sel {e_e:.2e} o {e_o:.2e} S {e_S:.2e}", flush=True)
     assert e_e <= TOL_FP32
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16
@@ -194,8 +194,8 @@ def test_sse_decode_touches_only_selected_states_and_separate_shared_qk():
     got = _decode_run(x, N, topk, S0, q_sh=q_sh, k_sh=k_sh)
     ref = _ref(x, topk, S0, q_sh=q_sh, k_sh=k_sh)
     np.testing.assert_array_equal(got["sel"], ref["sel"])
-    assert maxrel(got["o"].double().numpy(), ref["o"]) <= TOL_BF16
-    assert maxrel(got["S"].double().numpy(), ref["S"]) <= TOL_BF16
+    assert maxrel(got["o"].double().numpy(), ref["o"], name="o") <= TOL_BF16
+    assert maxrel(got["S"].double().numpy(), ref["S"], name="S") <= TOL_BF16
     for b in range(B):
         for h in range(H):
             used = set(got["sel"][b, 0, h].tolist()) | {N}
@@ -217,8 +217,8 @@ def test_sse_decode_full_size():
     got = _decode_run(x, cfg.N, cfg.topk, S0)
     ref = _ref(x, cfg.topk, S0)
     np.testing.assert_array_equal(got["sel"], ref["sel"])
-    e_o = maxrel(got["o"].double().numpy(), ref["o"])
-    e_S = maxrel(got["S"].double().numpy(), ref["S"])
+    e_o = maxrel(got["o"].double().numpy(), ref["o"], name="o")
+    e_S = maxrel(got["S"].double().numpy(), ref["S"], name="S")
     print(f"  {cfg.name}: o {e_o:.2e} S {e_S:.2e}", flush=True)
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16
     # partitions selected by neither step are untouched

@@ -1,6 +1,7 @@
 """Pins for the SSE oracle: the printed decay-clock example, the reduction to
-plain GLA (checked against the unrolled sum), the masking execution as a
-second algorithm, and the routing invariants."""
+plain GLA (checked against the unrolled sum), the shared partition and the
+routed partitions together against closed-form unrolled sums, the masking
+execution as a second algorithm, and the routing invariants."""
 import json
 import os
 
@@ -105,3 +106,109 @@ def test_unit_decay_channel_retains_exactly():
     S0 = np.random.default_rng(8).standard_normal((1, 1, 3, 4, 3))
     out = oracle.sse(logits, q, k, v, lam, topk=1, S0=S0)
     np.testing.assert_array_equal(out["S"][0, 0, :, 2], S0[0, 0, :, 2])
+
+
+def _sse_unrolled(logits, q, k, v, lam, topk, q_sh, k_sh, S0):
+    """SSE written out as closed-form sums, independent of the oracle's recursion.
+
+    For each (b, h) and partition i let V_i be the tokens that visit it (those
+    whose top-k of the logits holds i; every token for the shared partition N)
+    and w_t^i the write/read weight (the softmax gate e_t^i for a routed
+    partition, 1 for the shared one).  With the visit-restricted cumulative
+    log-decay L_i(t) = sum over s in V_i, s <= t of log Lambda_s (one value per
+    state row), the state after token t is
+        S^i_t = exp(L_i(t)) * S0^i + sum_{j in V_i, j <= t} exp(L_i(t) - L_i(j)) * (w_j^i k_j) v_j^T
+    (rows scaled), and o_t = sum_{i in T_t} e_t^i q_t S^i_t + q_sh_t S^N_t.
+    Sparse State Expansion slides, "One gate controls both writes and reads"
+    (Eqs. 9-14) and "A memory decays only when its partition is visited"; the
+    shared partition's weight 1, decay Lambda_t and own q/k are the reading
+    under test.
+    """
+    f64 = lambda a: np.asarray(a, np.float64)
+    logits32 = np.asarray(logits, np.float32)
+    q, k, v, lam, q_sh, k_sh = map(f64, (q, k, v, lam, q_sh, k_sh))
+    B, T, H, N = logits32.shape
+    c, d = q.shape[-1], v.shape[-1]
+    S = np.array(S0, np.float64, copy=True)
+    o = np.zeros((B, T, H, d))
+    g = logits32.astype(np.float64)
+    e = np.exp(g - g.max(-1, keepdims=True))
+    e /= e.sum(-1, keepdims=True)
+    # stable sort on the negated fp32 logits: ties keep the lower index first
+    sel = np.argsort(-logits32, axis=-1, kind="stable")[..., :topk]
+    loglam = np.log(lam)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N + 1):
+                if i < N:
+                    visits = [t for t in range(T) if i in sel[b, t, h]]
+                    w = {t: e[b, t, h, i] for t in visits}
+                    keys = k[b, :, h]
+                else:
+                    visits = list(range(T))
+                    w = {t: 1.0 for t in visits}
+                    keys = k_sh[b, :, h]
+                L = np.zeros((T, c))  # L_i(t), constant between visits
+                acc = np.zeros(c)
+                for t in range(T):
+                    if t in w:
+                        acc = acc + loglam[b, t, h]
+                    L[t] = acc
+                for t in visits:
+                    St = np.exp(L[t])[:, None] * S0[b, h, i]
+                    for j in visits:
+                        if j > t:
+                            break
+                        St += (np.exp(L[t] - L[j]) * w[j] * keys[j])[:, None] * v[b, j, h][None, :]
+                    if i < N:
+                        o[b, t, h] += e[b, t, h, i] * (q[b, t, h] @ St)
+                    else:
+                        o[b, t, h] += q_sh[b, t, h] @ St
+                    if t == visits[-1]:
+                        S[b, h, i] = St
+    return S, o, sel
+
+
+def test_shared_partition_unrolled_sum():
+    # Routed queries zeroed: o is the shared partition's read alone.  The shared
+    # partition gets its own key and query (k_sh != k, q_sh != q), a nonzero
+    # initial state, and must decay by Lambda_t and take weight 1 on every token.
+    B, T, H, N, c, d = 1, 19, 2, 4, 5, 3
+    logits, q, k, v, lam = _rand(11, B, T, H, N, c, d)
+    rng = np.random.default_rng(12)
+    q_sh = rng.standard_normal((B, T, H, c)).astype(np.float32)
+    kl = rng.standard_normal((B, T, H, c))
+    k_sh = (np.exp(kl) / np.exp(kl).sum(-1, keepdims=True)).astype(np.float32)
+    lam = rng.uniform(0.5, 1.0, (B, T, H, c)).astype(np.float32)  # strong decay: visible
+    S0 = rng.standard_normal((B, H, N + 1, c, d))
+    zq = np.zeros_like(q)
+    out = oracle.sse(logits, zq, k, v, lam, topk=2, q_sh=q_sh, k_sh=k_sh, S0=S0)
+    S_ref, o_ref, _ = _sse_unrolled(logits, zq, k, v, lam, 2, q_sh, k_sh, S0)
+    scale = np.abs(o_ref).max()
+    np.testing.assert_allclose(out["o"], o_ref, rtol=0, atol=1e-12 * scale)
+    np.testing.assert_allclose(out["S"][:, :, N], S_ref[:, :, N], rtol=0,
+                               atol=1e-12 * np.abs(S_ref[:, :, N]).max())
+    # the shared read alone: q_sh_t . S^N_t, with S^N_t from the closed form
+    assert np.abs(o_ref).max() > 0.1
+
+
+def test_routed_and_shared_together_unrolled_sum():
+    # Both contributions nonzero, several routed partitions with top-2 routing,
+    # a separate shared key/query, nonzero initial states in every partition.
+    B, T, H, N, c, d = 2, 23, 2, 5, 4, 3
+    logits, q, k, v, lam = _rand(13, B, T, H, N, c, d)
+    rng = np.random.default_rng(14)
+    q_sh = rng.standard_normal((B, T, H, c)).astype(np.float32)
+    k_sh = rng.uniform(0.0, 1.0, (B, T, H, c)).astype(np.float32)
+    lam = rng.uniform(0.6, 1.0, (B, T, H, c)).astype(np.float32)
+    S0 = rng.standard_normal((B, H, N + 1, c, d))
+    out = oracle.sse(logits, q, k, v, lam, topk=2, q_sh=q_sh, k_sh=k_sh, S0=S0)
+    S_ref, o_ref, sel = _sse_unrolled(logits, q, k, v, lam, 2, q_sh, k_sh, S0)
+    np.testing.assert_array_equal(out["sel"], sel)
+    np.testing.assert_allclose(out["o"], o_ref, rtol=0, atol=1e-12 * np.abs(o_ref).max())
+    np.testing.assert_allclose(out["S"], S_ref, rtol=0, atol=1e-12 * np.abs(S_ref).max())
+    # and with the shared projections left out (q_sh = q, k_sh = k by default)
+    out2 = oracle.sse(logits, q, k, v, lam, topk=2, S0=S0)
+    S_ref2, o_ref2, _ = _sse_unrolled(logits, q, k, v, lam, 2, q, k, S0)
+    np.testing.assert_allclose(out2["o"], o_ref2, rtol=0, atol=1e-12 * np.abs(o_ref2).max())
+    np.testing.assert_allclose(out2["S"], S_ref2, rtol=0, atol=1e-12 * np.abs(S_ref2).max())
