@@ -116,6 +116,27 @@ int sdm_forward(const sslp_sdm_shape* shape, int dtype, int residual_mode, const
                 void* stream);
 
 /*
+ * sdm_forward_noalloc -- sdm_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, semantics and kernels as sdm_forward,
+ * minus the workspace: the scratch it needs (the addressing arrays and the
+ * chunk plans) lives in a fixed array of SSLP_NOALLOC_SCRATCH_BYTES inside the
+ * library, one copy per GPU, held until the process ends.  The call allocates
+ * nothing and returns SSLP_ERR_WORKSPACE when sdm_workspace_size(shape)
+ * exceeds that maximum.  Every call on a GPU uses that GPU's one array:
+ * calls that overlap on the same GPU (other streams, other threads) race and
+ * must be serialised by the caller.  The array keeps whatever the last call
+ * left; nothing in it needs to start at zero.  sdm_noalloc_scratch_bytes()
+ * returns the maximum.
+ */
+#define SSLP_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t sdm_noalloc_scratch_bytes(void);
+int sdm_forward_noalloc(const sslp_sdm_shape* shape, int dtype, int residual_mode,
+                        const void* sw1, const void* sw2, const void* sr1, const void* sr2,
+                        const void* v, const float* alpha, const float* beta, float* M, void* y,
+                        int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r, void* stream);
+
+/*
  * sdm_decode_step -- one token for each of B independent sequences (shape->T
  * must be 1): addressing, update and read of each sequence's own table.  Same
  * arithmetic as sdm_forward with T = 1 (Sparse Delta Memory slides, same

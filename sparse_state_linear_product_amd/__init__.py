@@ -9,6 +9,7 @@ allocated with torch when the caller does not pass one.
 
 Functions (see include/sslp.h for the exact semantics):
   sdm_forward, sdm_decode_step, sdm_address, sdm_sparse_update   Sparse Delta Memory
+  sdm_forward_noalloc                                            the same, with the library's fixed scratch
   sdm_norm_gate                                                  RMS-Norm + output gate after the read
   sdm_forward_train, sdm_sparse_update_train, sdm_backward       SDM training (undo writes)
   gdn_chunk_forward, gdn2_chunk_forward                          Gated DeltaNet / KDA / GDN2
@@ -22,7 +23,7 @@ from . import _lib
 from ._lib import (DECAY_CHANNEL, DECAY_SCALAR, RESIDUAL_PER_SLOT, RESIDUAL_SHARED, GdnShape,
                    SdmShape, SseShape, SslpError, check, lib)
 
-__all__ = ["sdm_forward", "sdm_decode_step", "sdm_address", "sdm_sparse_update",
+__all__ = ["sdm_forward", "sdm_forward_noalloc", "sdm_noalloc_scratch_bytes", "sdm_decode_step", "sdm_address", "sdm_sparse_update",
            "sdm_forward_train", "sdm_sparse_update_train", "sdm_backward",
            "sdm_backward_workspace_bytes", "sdm_norm_gate",
            "gdn_chunk_forward", "gdn2_chunk_forward", "sse_forward", "sse_decode_step",
@@ -113,6 +114,42 @@ def sdm_forward(sw1, sw2, sr1, sr2, v, alpha, beta, M, k_w, k_r, W, R, y=None,
                            _ptr(M), _ptr(y), _ptr(idx_w), _ptr(wt_w), _ptr(idx_r), _ptr(wt_r),
                            _ptr(ws), nbytes, _stream(stream))
     check("sdm_forward", rc)
+    return y
+
+
+def sdm_noalloc_scratch_bytes():
+    """Fixed per-GPU scratch of sdm_forward_noalloc, in bytes."""
+    return lib().sdm_noalloc_scratch_bytes()
+
+
+def sdm_forward_noalloc(sw1, sw2, sr1, sr2, v, alpha, beta, M, y, k_w, k_r, W, R,
+                        residual_mode=RESIDUAL_SHARED, idx_w=None, wt_w=None, idx_r=None,
+                        wt_r=None, stream=None):
+    """sdm_forward with no workspace and no allocation anywhere in the call: y
+    [B,T,H,d_v] must be given; the scratch is the library's fixed per-GPU array
+    (calls that overlap on one GPU race).  Returns y."""
+    B, T, H, sqrt_n = sw1.shape
+    d_v = v.shape[-1]
+    dt = sw1.dtype
+    for name, t in (("sw2", sw2), ("sr1", sr1), ("sr2", sr2)):
+        _need(t, dt, (B, T, H, sqrt_n), name)
+    _need(v, dt, (B, T, H, d_v), "v")
+    _need(alpha, torch.float32, (B, T, H), "alpha")
+    _need(beta, torch.float32, (B, T, H), "beta")
+    _need(M, torch.float32, (B, H, sqrt_n * sqrt_n, d_v), "M")
+    _need(y, dt, (B, T, H, d_v), "y")
+    for name, t, n in (("idx_w", idx_w, W), ("idx_r", idx_r, R)):
+        if t is not None:
+            _need(t, torch.int32, (B, T, H, n), name)
+    for name, t, n in (("wt_w", wt_w, W), ("wt_r", wt_r, R)):
+        if t is not None:
+            _need(t, torch.float32, (B, T, H, n), name)
+    shape = sdm_shape(B, T, H, sqrt_n, d_v, k_w, k_r, W, R)
+    rc = lib().sdm_forward_noalloc(ctypes.byref(shape), _dtype_code(sw1), int(residual_mode),
+                                   _ptr(sw1), _ptr(sw2), _ptr(sr1), _ptr(sr2), _ptr(v),
+                                   _ptr(alpha), _ptr(beta), _ptr(M), _ptr(y), _ptr(idx_w),
+                                   _ptr(wt_w), _ptr(idx_r), _ptr(wt_r), _stream(stream))
+    check("sdm_forward_noalloc", rc)
     return y
 
 

@@ -42,6 +42,8 @@ SIGNATURES = {
     "sdm_decode_workspace_size": ([ctypes.POINTER(SdmShape)], _sz),
     "sdm_forward": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 14 + [_sz, _vp], _i),
     "sdm_decode_step": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 14 + [_sz, _vp], _i),
+    "sdm_noalloc_scratch_bytes": ([], _sz),
+    "sdm_forward_noalloc": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 14, _i),
     "sdm_address": ([ctypes.POINTER(SdmShape), _i, _vp, _vp, _i, _i, _vp, _vp, _vp], _i),
     "sdm_sparse_update": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 10 + [_sz, _vp], _i),
     "sdm_norm_gate": ([ctypes.c_longlong, _i, _i, _vp, _vp, _vp, ctypes.c_float, _i, _vp, _vp],

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/sslp.h"
 #include "kernels.h"
@@ -293,6 +294,89 @@ int sdm_forward(const sslp_sdm_shape* s, int dtype, int residual_mode, const voi
     if (int rc = check_sdm_shape(s, true)) return rc;
     return sdm_run(s, s->T, dtype, residual_mode, sw1, sw2, sr1, sr2, v, alpha, beta, M, y, idx_w,
                    wt_w, idx_r, wt_r, workspace, ws_bytes, sdm_workspace_size(s), stream);
+}
+
+// ---------------------------------------------------------------------------
+// sdm_forward without any allocation: the workspace is a fixed device array of
+// the library, one copy per GPU, shared by every call on that GPU.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+// In host code `scratch` names a host-side stand-in; the device address of each
+// GPU's copy comes from hipGetSymbolAddress with that GPU current, and only
+// that address is ever passed to kernels.
+__device__ __align__(256) unsigned char scratch[SSLP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the scratch array on the GPU that `stream` belongs to
+int scratch_for_stream(hipStream_t stream, void** out) {
+    int cur = 0;
+    if (hipError_t e = hipGetDevice(&cur); e != hipSuccess) return hip_status(e, "hipGetDevice");
+    int dev = cur;
+    if (stream != nullptr) {
+        hipDevice_t d = 0;
+        if (hipError_t e = hipStreamGetDevice(stream, &d); e != hipSuccess)
+            return hip_status(e, "hipStreamGetDevice");
+        dev = (int)d;
+    }
+    REQUIRE(dev >= 0 && dev < kMaxDevices, SSLP_ERR_UNSUPPORTED, "device index %d >= %d", dev,
+            kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur)
+            if (hipError_t e = hipSetDevice(dev); e != hipSuccess) return hip_status(e, "hipSetDevice");
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        REQUIRE(p != nullptr && ((uintptr_t)p & 255u) == 0, SSLP_ERR_HIP,
+                "scratch array address %p is not 256-byte aligned", p);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sdm_noalloc_scratch_bytes(void) { return (size_t)SSLP_NOALLOC_SCRATCH_BYTES; }
+
+int sdm_forward_noalloc(const sslp_sdm_shape* s, int dtype, int residual_mode, const void* sw1,
+                        const void* sw2, const void* sr1, const void* sr2, const void* v,
+                        const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
+                        float* wt_w, int32_t* idx_r, float* wt_r, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_sdm_shape(s, true)) return rc;
+    const size_t need = sdm_workspace_size(s);
+    REQUIRE(need <= (size_t)SSLP_NOALLOC_SCRATCH_BYTES, SSLP_ERR_WORKSPACE,
+            "sdm_forward_noalloc: this shape needs %zu bytes of scratch, above the fixed %zu "
+            "(use sdm_forward with a workspace)",
+            need, (size_t)SSLP_NOALLOC_SCRATCH_BYTES);
+    // the pointer checks of sdm_forward, before the first HIP call
+    if (int rc = check_dtype(dtype)) return rc;
+    REQUIRE_PTR(M);
+    if (s->T > 0) {
+        REQUIRE_PTR(sw1);
+        REQUIRE_PTR(sw2);
+        REQUIRE_PTR(sr1);
+        REQUIRE_PTR(sr2);
+        REQUIRE_PTR(v);
+        REQUIRE_PTR(alpha);
+        REQUIRE_PTR(beta);
+        REQUIRE_PTR(y);
+    }
+    void* ws = nullptr;
+    if (need > 0 && s->T > 0)
+        if (int rc = scratch_for_stream((hipStream_t)stream, &ws)) return rc;
+    return sdm_forward(s, dtype, residual_mode, sw1, sw2, sr1, sr2, v, alpha, beta, M, y, idx_w,
+                       wt_w, idx_r, wt_r, ws, need, stream);
 }
 
 int sdm_decode_step(const sslp_sdm_shape* s, int dtype, int residual_mode, const void* sw1,

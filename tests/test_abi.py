@@ -185,3 +185,22 @@ def test_gdn_and_sse_shape_errors():
     s = _lib.SseShape(2, 1, 1, 8, 2, 128, 128, 64)
     assert lib.sse_decode_step(ctypes.byref(s), 0, *([FAKE] * 11), None) == _lib.SSLP_ERR_UNSUPPORTED
     assert lib.sse_decode_step(ctypes.byref(s), 1, *([None] * 11), None) == _lib.SSLP_ERR_INVALID_ARG
+
+
+def test_sdm_forward_noalloc_rejects_oversize_before_any_hip_call():
+    lib = _lib.lib()
+    cap = lib.sdm_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    # a long 1.4B-layer sequence needs more chunk-plan scratch than the fixed array
+    big = _sdm(B=1, T=1 << 16, H=2, sqrtN=240, d_v=960, k_w=32, k_r=32, W=32, R=32)
+    need = lib.sdm_workspace_size(ctypes.byref(big))
+    assert need > cap
+    ptrs = [FAKE] * 9 + [None] * 4
+    rc = lib.sdm_forward_noalloc(ctypes.byref(big), 1, 0, *ptrs, None)
+    assert rc == _lib.SSLP_ERR_WORKSPACE
+    assert "scratch" in lib.sslp_last_error().decode()
+    # bad shapes are rejected as in sdm_forward
+    assert lib.sdm_forward_noalloc(ctypes.byref(_sdm(W=20)), 0, 0, *ptrs, None) == \
+        _lib.SSLP_ERR_INVALID_ARG
+    assert lib.sdm_forward_noalloc(ctypes.byref(_sdm()), 0, 0, *([None] + ptrs[1:]), None) == \
+        _lib.SSLP_ERR_INVALID_ARG
