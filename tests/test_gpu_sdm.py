@@ -349,3 +349,27 @@ def test_forward_equals_component_calls(T, W):
     y2 = sslp.sdm_sparse_update(iw, ww, ir, wr, x["v"], x["alpha"], x["beta"], M2)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(M1, M2)
+
+
+def test_side_stream_call_orders_its_own_allocations():
+    # sdm_forward enqueued on a stream other than the current one, with the
+    # binding's own workspace and output; the current stream then allocates and
+    # fills memory at once.  The binding allocates on the call's stream, so
+    # nothing it still uses can be handed out meanwhile: results equal a plain
+    # call on the current stream, bit for bit.
+    sslp = _sslp()
+    cfg = wl.SdmConfig("side", 1, 200, 2, 64, 64, 16, 16, 32, 32, torch.bfloat16, 66)
+    announce("sdm_forward on a side stream, allocations on the current stream meanwhile")
+    x = {k: v.to(DEV) for k, v in wl.sdm_inputs(cfg).items()}
+    M_ref = torch.zeros((cfg.B, cfg.H, cfg.N, cfg.d_v), device=DEV)
+    y_ref = sslp.sdm_forward(x["sw1"], x["sw2"], x["sr1"], x["sr2"], x["v"], x["alpha"],
+                             x["beta"], M_ref, cfg.k_w, cfg.k_r, cfg.W, cfg.R)
+    M = torch.zeros_like(M_ref)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    y = sslp.sdm_forward(x["sw1"], x["sw2"], x["sr1"], x["sr2"], x["v"], x["alpha"], x["beta"],
+                         M, cfg.k_w, cfg.k_r, cfg.W, cfg.R, stream=side)
+    junk = [torch.full((1 << 22,), float("nan"), device=DEV) for _ in range(16)]
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(y, y_ref) and torch.equal(M, M_ref)
