@@ -308,6 +308,9 @@ size_t gdn_workspace_size(const sslp_gdn_shape* shape);
  * No query scaling and no key normalisation inside (the caller normalises).
  *   q, k  [B,T,H,d_k] dtype;  v [B,T,H,d_v] dtype;
  *   alpha [B,T,H] fp32 (SCALAR) or [B,T,H,d_k] fp32 (CHANNEL), in (0,1];
+ *         CHANNEL: the chunked form factors each key channel's decay inside
+ *         16-token blocks, exact (to rounding) for alpha in [2^-4, 1]; smaller
+ *         per-channel decays give finite but less accurate results;
  *   beta  [B,T,H] fp32;
  *   S0    [B,H,d_k,d_v] fp32 initial state, or NULL for zeros;
  *   S_out [B,H,d_k,d_v] fp32 final state (may alias S0);
@@ -330,7 +333,8 @@ int gdn_chunk_forward(const sslp_gdn_shape* shape, int dtype, int decay_mode, co
  *   S = S~ + k_t r^T;      o_t = S^T q_t.
  * b = w = beta 1 is KDA.
  *   q, k [B,T,H,d_k] dtype; v [B,T,H,d_v] dtype;
- *   alpha, erase (b) [B,T,H,d_k] fp32; write (w) [B,T,H,d_v] fp32;
+ *   alpha, erase (b) [B,T,H,d_k] fp32; write (w) [B,T,H,d_v] fp32; alpha as
+ *   gdn_chunk_forward's CHANNEL mode (exact for alpha in [2^-4, 1]);
  *   S0, S_out, o, workspace (gdn_workspace_size), errors: as gdn_chunk_forward.
  */
 int gdn2_chunk_forward(const sslp_gdn_shape* shape, int dtype, const void* q, const void* k,

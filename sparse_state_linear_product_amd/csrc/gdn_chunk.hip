@@ -42,6 +42,9 @@ namespace sslp {
 
 namespace {
 
+// largest inverse product of per-channel decays inside a 16-token block
+constexpr float kMaxInvDecay = 0x1p64f;
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -351,8 +354,10 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
                     pall *= al;
                     if (r > 0) {
                         ep *= al;
-                        // hardware reciprocal (within 1 ulp): Km is rounded to bf16
-                        em *= __builtin_amdgcn_rcpf(al);
+                        // hardware reciprocal (within 1 ulp): Km is rounded to bf16.
+                        // Exact for decays >= 2^-4 (the block's inverse product stays
+                        // <= 2^60); below, the clamp keeps every factor finite
+                        em = fminf(em * __builtin_amdgcn_rcpf(al), kMaxInvDecay);
                     }
                     const float kv = bf2f(sm.k[t][i]), qv = bf2f(sm.q[t][i]);
                     float ke = kv;  // the key of A's rows and of Wn: b (.) k for GDN2

@@ -26,11 +26,14 @@
 //     o_p   = e_p [ (q_p * AF E+_p) S + sum_{p'<=p} e_p' (q_p * E+_p).(k_p' * E-_p') v_p' ]
 //     S_new = (AF PX) S + sum_p' (k_p' * PX E-_p')^T e_p' v_p'
 // with AF the first visit's decay, E+_p the product of decays after it
-// (E-_p = 1/E+_p, PX = E+ of the last visit): every factor is a product of at
-// most 15 decays.  The state stays in MFMA accumulator registers; the three
+// (E-_p = 1/E+_p, PX = E+ of the last visit).  A block ends early before the
+// visit that would take E+ below 2^-60 in any state row, so E- stays below
+// 2^60 whatever the decays in (0, 1] (a one-visit block takes no inverse).  The state stays in MFMA accumulator registers; the three
 // products run on 16x16x32 / 16x16x16 bf16 MFMA with fp32 accumulation.  The
 // k+1 contributions of a token are summed in a fixed order (routed in rank
-// order, then shared) once all partitions are done with the chunk.
+// order, then shared) once all partitions are done with the chunk.  The
+// column blocks of a (batch, head) are placed on one XCD, whose L2 then serves
+// their common q, k and Lambda reads.
 #include <type_traits>
 
 #include "common.h"
@@ -50,6 +53,7 @@ constexpr int DB = 32;    // columns of d per workgroup
 constexpr int MAXN = 8;   // routed partitions supported
 constexpr int LDQ = CR + 8;
 constexpr int LDV = 20;
+constexpr float kMinBlockDecay = 0x1p-60f;  // smallest product of decays inside a block
 
 struct __align__(16) WaveScratch {
     uint16_t qs[16][LDQ];  // q * E+ (bf16)
@@ -95,13 +99,17 @@ struct SseArgs {
     int masking;  // 1: every routed partition runs over every token (masked execution)
 };
 
-// One block of up to 16 visits of one partition on one wave.
+// One block of up to L <= 16 visits of one partition on one wave; returns the
+// number of visits taken.  The block ends early before a visit that would take
+// the product of decays after its first visit below kMinBlockDecay in any state
+// row, so that the inverse products stay below 2^60 whatever the decays in
+// (0, 1] (a block of one visit takes no inverse at all).
 //   NY      number of 16-column tiles this wave owns (2 routed, 1 shared)
 //   St      the partition state slice, accumulator layout: tile (m, y) holds
 //           rows 16m + 4(lane/16) + j, column 16y + lane%16
 //   visits  local token ids and gate weights of the visits (p < L)
 template <typename io_t, int NY>
-SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs& a,
+SSLP_DEVICE int gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs& a,
                            const io_t* qg, const io_t* kg, const io_t* vg, int b, int h, int t0,
                            int col0, const int16_t* vtok, const float* vgate, int tbase, int L,
                            int lane, f32x4_t (&ot)[NY], const int8_t* vmask = nullptr) {
@@ -111,6 +119,9 @@ SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs&
     auto gate = [&](int p) { return vgate ? vgate[p] : 1.f; };
     const int T = a.T, H = a.H;
     const int g4 = lane >> 4, l16 = lane & 15;
+    int Le = L;
+    bool alive = true;     // wave-uniform: the block still takes visits
+    bool careful = false;  // wave-uniform: visits are tested for the block end
     // ---- a. decay-scaled operands (lane owns rows 2 lane, 2 lane + 1); the
     //      loads of 8 visits are issued before any of them is used ----
     {
@@ -138,36 +149,62 @@ SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs&
                 qw[u] = *reinterpret_cast<const uint32_t*>(qg + bth * CR + 2 * lane);
                 kw[u] = *reinterpret_cast<const uint32_t*>(kg + bth * CR + 2 * lane);
             }
+            // the block-end test is needed only from the first half holding a decay
+            // below 2^-4 on (fifteen decays of at least 2^-4 keep the product >= 2^-60)
+            bool small = false;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int p = 8 * half + u;
-                float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
-                if (p < L) {
-                    // masked execution: a token that does not select the partition leaves
-                    // its state undecayed (and writes nothing: its gate is 0)
-                    const bool frozen = vmask != nullptr && vmask[p] < 0;
-                    const float l0 = frozen ? 1.f : lam[u].x, l1 = frozen ? 1.f : lam[u].y;
-                    q0 = __uint_as_float(qw[u] << 16);
-                    q1 = __uint_as_float(qw[u] & 0xFFFF0000u);
-                    k0 = __uint_as_float(kw[u] << 16);
-                    k1 = __uint_as_float(kw[u] & 0xFFFF0000u);
-                    if (p == 0) {
-                        af0 = l0;
-                        af1 = l1;
-                    } else {
-                        ep0 *= l0;
-                        ep1 *= l1;
-                        // hardware reciprocal (within 1 ulp, not an IEEE division):
-                        // the factor only scales a key that is rounded to bf16
-                        em0 *= __builtin_amdgcn_rcpf(l0);
-                        em1 *= __builtin_amdgcn_rcpf(l1);
+            for (int u = 0; u < 8; ++u)
+                small |= 8 * half + u < L && (lam[u].x < 0x1p-4f || lam[u].y < 0x1p-4f);
+            careful = careful || __ballot(small) != 0ull;
+            // one of two copies of the half, chosen once: without and with the test
+            auto stage_half = [&](auto test) __attribute__((always_inline)) {
+                constexpr bool TEST = decltype(test)::value;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int p = 8 * half + u;
+                    float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
+                    if (p < L) {
+                        // masked execution: a token that does not select the partition leaves
+                        // its state undecayed (and writes nothing: its gate is 0)
+                        const bool frozen = vmask != nullptr && vmask[p] < 0;
+                        const float l0 = frozen ? 1.f : lam[u].x, l1 = frozen ? 1.f : lam[u].y;
+                        if (p == 0) {
+                            af0 = l0;
+                            af1 = l1;
+                        } else if (!TEST) {
+                            ep0 *= l0;
+                            ep1 *= l1;
+                            // hardware reciprocal (within 1 ulp, not an IEEE division):
+                            // the factor only scales a key that is rounded to bf16
+                            em0 *= __builtin_amdgcn_rcpf(l0);
+                            em1 *= __builtin_amdgcn_rcpf(l1);
+                        } else if (alive) {
+                            const float n0 = ep0 * l0, n1 = ep1 * l1;
+                            if (__ballot(n0 < kMinBlockDecay || n1 < kMinBlockDecay) != 0ull) {
+                                alive = false;  // this visit starts the next block
+                                Le = p;
+                            } else {
+                                ep0 = n0;
+                                ep1 = n1;
+                                em0 *= __builtin_amdgcn_rcpf(l0);
+                                em1 *= __builtin_amdgcn_rcpf(l1);
+                            }
+                        }
+                        if (!TEST || alive) {
+                            q0 = __uint_as_float(qw[u] << 16);
+                            q1 = __uint_as_float(qw[u] & 0xFFFF0000u);
+                            k0 = __uint_as_float(kw[u] << 16);
+                            k1 = __uint_as_float(kw[u] & 0xFFFF0000u);
+                        }
                     }
+                    *reinterpret_cast<uint32_t*>(&ws.qs[p][2 * lane]) =
+                        (uint32_t)f32_to_bf16(q0 * ep0).bits | ((uint32_t)f32_to_bf16(q1 * ep1).bits << 16);
+                    *reinterpret_cast<uint32_t*>(&ws.ks[p][2 * lane]) =
+                        (uint32_t)f32_to_bf16(k0 * em0).bits | ((uint32_t)f32_to_bf16(k1 * em1).bits << 16);
                 }
-                *reinterpret_cast<uint32_t*>(&ws.qs[p][2 * lane]) =
-                    (uint32_t)f32_to_bf16(q0 * ep0).bits | ((uint32_t)f32_to_bf16(q1 * ep1).bits << 16);
-                *reinterpret_cast<uint32_t*>(&ws.ks[p][2 * lane]) =
-                    (uint32_t)f32_to_bf16(k0 * em0).bits | ((uint32_t)f32_to_bf16(k1 * em1).bits << 16);
-            }
+            };
+            if (careful) stage_half(std::true_type{});
+            else stage_half(std::false_type{});
         }
         *reinterpret_cast<float2*>(&ws.af[2 * lane]) = make_float2(af0, af1);
         *reinterpret_cast<float2*>(&ws.px[2 * lane]) = make_float2(ep0, ep1);
@@ -176,7 +213,7 @@ SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs&
         for (int e = 0; e < NV; ++e) {
             const int idx = lane + 64 * e;
             const int p = idx >> (NY == 2 ? 5 : 4), n = idx & (NY * 16 - 1);
-            ws.vt[n][p] = f32_to_bf16(p < L ? gate(p) * vv[e] : 0.f).bits;
+            ws.vt[n][p] = f32_to_bf16(p < Le ? gate(p) * vv[e] : 0.f).bits;
         }
     }
     wave_sync();
@@ -230,7 +267,7 @@ SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs&
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int pp = 4 * g4 + j;  // p' (row), column p = l16
-        bp[j] = bfs((pp <= l16 && l16 < L) ? pm[j] : 0.f);
+        bp[j] = bfs((pp <= l16 && l16 < Le) ? pm[j] : 0.f);
     }
     // ---- e. O^T += Ve^T Pm^T ----
     // (own accumulator, added with VALU: a 16x16x16 MFMA must not take the
@@ -267,6 +304,7 @@ SSLP_DEVICE void gla_block(f32x4_t (&St)[8][NY], WaveScratch& ws, const SseArgs&
         }
     }
     wave_sync();
+    return Le;
 }
 
 // Routing of every token (one thread per (b, t, h)): e = softmax(logits) over
@@ -306,8 +344,12 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
     __shared__ Smem<TOPK> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nblk = a.dv / DB;
-    const int cb = blockIdx.x % nblk;
-    const int bh = blockIdx.x / nblk;
+    // XCD-aware placement: workgroups x and x + 8 share an XCD; the nblk column
+    // blocks of a (batch, head) take consecutive multiples of 8 on one XCD, so
+    // that its L2 serves their common q, k and Lambda reads
+    const int x = blockIdx.x, xcd = x & 7, kq = x >> 3;
+    const int bh = (kq / nblk) * 8 + xcd, cb = kq % nblk;
+    if (bh >= a.B * a.H) return;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const int n0 = cb * DB;
     const int T = a.T, H = a.H, N = a.N, topk = a.topk, dv = a.dv;
@@ -399,26 +441,28 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
             if (active) {
                 WaveScratch& ws = sm.ws[w];
                 if constexpr (NY == 1) {
-                    for (int bb = 0; bb * 16 < Tc; ++bb) {
-                        const int L = (Tc - 16 * bb) < 16 ? (Tc - 16 * bb) : 16;
+                    for (int p0 = 0; p0 < Tc;) {
+                        const int L = (Tc - p0) < 16 ? (Tc - p0) : 16;
                         f32x4_t ot[1];
-                        gla_block<io_t, 1>(St, ws, a, qsh, ksh, vg, b, h, t0, n0 + colw, nullptr,
-                                           nullptr, 16 * bb, L, lane, ot);
+                        const int Le = gla_block<io_t, 1>(St, ws, a, qsh, ksh, vg, b, h, t0, n0 + colw,
+                                                          nullptr, nullptr, p0, L, lane, ot);
                         // O^T tile: column p = l16, rows n = 4 g4 + j
-                        if (l16 < L) {
+                        if (l16 < Le) {
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) sm.osh[16 * bb + l16][colw + 4 * g4 + j] = ot[0][j];
+                            for (int j = 0; j < 4; ++j) sm.osh[p0 + l16][colw + 4 * g4 + j] = ot[0][j];
                         }
+                        p0 += Le;
                     }
                 } else {
                     const int cnt = sm.cnt[part];
-                    for (int p0 = 0; p0 < cnt; p0 += 16) {
+                    for (int p0 = 0; p0 < cnt;) {
                         const int L = (cnt - p0) < 16 ? (cnt - p0) : 16;
                         f32x4_t ot[NY];
-                        gla_block<io_t, NY>(St, ws, a, qg, kg, vg, b, h, t0, n0, &sm.vis[part][p0],
-                                            &sm.vgate[part][p0], 0, L, lane, ot,
-                                            a.masking ? &sm.vrank[part][p0] : nullptr);
-                        const int rk = l16 < L ? sm.vrank[part][p0 + l16] : -1;
+                        const int Le = gla_block<io_t, NY>(St, ws, a, qg, kg, vg, b, h, t0, n0,
+                                                           &sm.vis[part][p0], &sm.vgate[part][p0], 0,
+                                                           L, lane, ot,
+                                                           a.masking ? &sm.vrank[part][p0] : nullptr);
+                        const int rk = l16 < Le ? sm.vrank[part][p0 + l16] : -1;
                         if (rk >= 0) {
                             const int tp = sm.vis[part][p0 + l16];
                             const float e = sm.vgate[part][p0 + l16];
@@ -428,6 +472,7 @@ __global__ __launch_bounds__(64 * (MAXN + 2)) void sse_chunk_kernel(SseArgs a) {
                                 for (int j = 0; j < 4; ++j)
                                     sm.contrib[tp][rk][16 * y + 4 * g4 + j] = e * ot[y][j];
                         }
+                        p0 += Le;
                     }
                 }
             }
@@ -477,7 +522,8 @@ hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
     sse_route_kernel<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(logits, P, N, topk, sel, e_sel);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(B * H * (dv / DB)));
+    // 8 * nblk consecutive workgroups hold 8 (batch, head) groups, one per XCD
+    dim3 grid((unsigned)(((B * H + 7) / 8) * 8 * (dv / DB)));
     dim3 block(64 * (N + 2));
     if (topk <= 2) sse_chunk_kernel<bf16_t, 2><<<grid, block, 0, st>>>(a);
     else sse_chunk_kernel<bf16_t, 4><<<grid, block, 0, st>>>(a);

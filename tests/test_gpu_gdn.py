@@ -162,3 +162,46 @@ def test_gdn2_full_config():
     e_S = maxrel(S.double().numpy(), Sr, name="S")
     print(f"  {cfg.name}: o {e_o:.2e} S {e_S:.2e}", flush=True)
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16
+
+
+@pytest.mark.parametrize("mode", ["gdn", "kda", "gdn2"])
+def test_strong_decays_at_the_documented_bound(mode):
+    # decays drawn from U(2^-4, 0.2) (per token for GDN, per channel for KDA and
+    # GDN2): products of decays within a 16-token block reach 2^-60, the edge of
+    # the range the chunked factorisation is exact for; parity must hold
+    announce(f"{mode} with decays ~ U(1/16, 0.2)")
+    g = torch.Generator().manual_seed(77)
+    S0 = torch.randn((1, 2, 128, 128), generator=g) * 0.5
+    if mode == "gdn2":
+        x = wl.gdn2_inputs(wl.GDN2, T=130, B=1, H=2, seed=78)
+        x["alpha"] = torch.empty(x["alpha"].shape).uniform_(1.0 / 16, 0.2, generator=g)
+        o, S = _run2(x, S0)
+        Sr, orf = _ref2(x, S0)
+        e_o, e_S = maxrel(o.double().numpy(), orf, name="o"), maxrel(S.double().numpy(), Sr, name="S")
+        assert np.isfinite(o.float().numpy()).all() and np.isfinite(S.numpy()).all()
+        assert e_o <= TOL_BF16 and e_S <= TOL_BF16, f"gdn2: o {e_o} S {e_S}"
+    else:
+        kda = mode == "kda"
+        x = wl.gdn_inputs(wl.KDA if kda else wl.GDN, T=130, B=1, H=2, seed=79)
+        x["alpha"] = torch.empty(x["alpha"].shape).uniform_(1.0 / 16, 0.2, generator=g)
+        _check(x, kda, S0=S0, tag=f"{mode} strong decay")
+
+
+@pytest.mark.parametrize("mode", ["gdn", "kda", "gdn2"])
+def test_tiny_decays_stay_finite(mode):
+    # below the documented bound (per-channel decays down to 1e-4) the chunked
+    # form must not produce inf or NaN; the scalar decay (GDN) stays exact there
+    announce(f"{mode} with decays ~ U(1e-4, 0.05)")
+    g = torch.Generator().manual_seed(80)
+    if mode == "gdn2":
+        x = wl.gdn2_inputs(wl.GDN2, T=100, B=1, H=2, seed=81)
+        x["alpha"] = torch.empty(x["alpha"].shape).uniform_(1e-4, 0.05, generator=g)
+        o, S = _run2(x)
+    else:
+        x = wl.gdn_inputs(wl.KDA if mode == "kda" else wl.GDN, T=100, B=1, H=2, seed=82)
+        x["alpha"] = torch.empty(x["alpha"].shape).uniform_(1e-4, 0.05, generator=g)
+        if mode == "gdn":
+            _check(x, False, tag="gdn tiny decay")
+            return
+        o, S = _run(x)
+    assert np.isfinite(o.float().numpy()).all() and np.isfinite(S.numpy()).all()
