@@ -16,7 +16,7 @@
  *   allocates, frees or synchronises.
  * - Each call validates its arguments on the host BEFORE any HIP call, then
  *   enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL is
- *   the default stream) and returns.  Results are valid once the stream has
+ *   the default stream) and returns (sslp_device_error alone synchronises).  Results are valid once the stream has
  *   completed.  States are updated in place in stream order.
  * - Tensors are dense, contiguous, row-major in the layouts written next to
  *   each argument; device pointers must be 16-byte aligned.  Inputs must not
@@ -423,6 +423,19 @@ int sse_decode_step(const sslp_sse_shape* shape, int dtype, const float* gate_lo
 
 /* Description of the last failure on the calling thread ("" if none). */
 const char* sslp_last_error(void);
+
+/*
+ * sslp_device_error -- whether a kernel met a caller-supplied SDM slot index
+ * outside [0, N) (sdm_sparse_update, sdm_sparse_update_train, sdm_backward)
+ * since the last query on this device: 1 if so, 0 if not, or a negative
+ * status.  Such a call leaves its results undefined but touches no memory
+ * outside the given tensors: a token's out-of-range slot is replaced by slot
+ * 0 (per-token kernels), and a 16-token chunk holding one is skipped (y = 0,
+ * the table unchanged; chunk-parallel kernel).  The query synchronises
+ * `stream` and clears the flag; it is the only entry point that synchronises.
+ */
+int sslp_device_error(void* stream);
+
 /* SSLP_VERSION of the built library. */
 int sslp_version(void);
 

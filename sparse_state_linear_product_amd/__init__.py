@@ -30,11 +30,21 @@ __all__ = ["sdm_forward", "sdm_forward_noalloc", "sdm_noalloc_scratch_bytes", "s
            "sdm_backward_workspace_bytes", "sdm_norm_gate",
            "gdn_chunk_forward", "gdn2_chunk_forward", "sse_forward", "sse_decode_step",
            "SslpError", "RESIDUAL_SHARED", "RESIDUAL_PER_SLOT", "DECAY_SCALAR", "DECAY_CHANNEL",
-           "version"]
+           "version", "device_error"]
 
 
 def version():
     return lib().sslp_version()
+
+
+def device_error(stream=None):
+    """True if an SDM kernel met a caller-supplied slot index outside [0, N) since
+    the last query on this device (that call's results are undefined; no memory
+    outside its tensors was touched).  Synchronises the stream; clears the flag."""
+    rc = lib().sslp_device_error(_stream(stream))
+    if rc < 0:
+        check("sslp_device_error", rc)
+    return rc == 1
 
 
 def _ptr(t):

@@ -60,6 +60,7 @@ SIGNATURES = {
     "sse_forward_masking": ([ctypes.POINTER(SseShape), _i] + [_vp] * 12 + [_sz, _vp], _i),
     "sse_decode_step": ([ctypes.POINTER(SseShape), _i] + [_vp] * 11 + [_vp], _i),
     "sslp_last_error": ([], ctypes.c_char_p),
+    "sslp_device_error": ([_vp], _i),
     "sslp_version": ([], _i),
 }
 

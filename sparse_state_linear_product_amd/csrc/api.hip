@@ -50,6 +50,30 @@ constexpr int kMaxTopK = 64;
 constexpr int kMaxBudget = 128;
 constexpr int kMaxDv = 4096;
 
+// Device word that the SDM recurrence kernels set to 1 when a caller-supplied
+// slot index lies outside [0, N) (sslp_device_error reads and clears it).  In
+// host code the name is a host-side stand-in; kernels get the device address
+// of each GPU's copy, taken once per device.
+__device__ unsigned int device_error_word;
+
+constexpr int kMaxErrDevices = 64;
+std::mutex g_errword_mu;
+unsigned* g_errword_ptr[kMaxErrDevices] = {};
+
+// device address of the error word on the current device (nullptr on failure:
+// the kernels then skip the report but still keep every access in the table)
+unsigned* error_word() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxErrDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_errword_mu);
+    if (g_errword_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(device_error_word)) != hipSuccess) return nullptr;
+        g_errword_ptr[dev] = static_cast<unsigned*>(p);
+    }
+    return g_errword_ptr[dev];
+}
+
 // checks shared by every SDM entry point; `need_k` checks k_w/k_r and W<=k^2
 int check_sdm_shape(const sslp_sdm_shape* s, bool need_k) {
     REQUIRE(s != nullptr, SSLP_ERR_INVALID_ARG, "shape must not be NULL");
@@ -112,6 +136,24 @@ extern "C" {
 
 const char* sslp_last_error(void) { return g_err; }
 int sslp_version(void) { return SSLP_VERSION; }
+
+int sslp_device_error(void* stream) {
+    g_err[0] = 0;
+    unsigned* w = error_word();
+    REQUIRE(w != nullptr, SSLP_ERR_HIP, "device error word not available on this device");
+    hipStream_t st = (hipStream_t)stream;
+    unsigned host = 0u;
+    if (int rc = hip_status(hipMemcpyAsync(&host, w, sizeof(host), hipMemcpyDeviceToHost, st),
+                            "read the device error word"))
+        return rc;
+    if (int rc = hip_status(hipStreamSynchronize(st), "hipStreamSynchronize")) return rc;
+    if (host != 0u) {
+        if (int rc = hip_status(hipMemsetAsync(w, 0, sizeof(unsigned), st), "clear the word"))
+            return rc;
+        if (int rc = hip_status(hipStreamSynchronize(st), "hipStreamSynchronize")) return rc;
+    }
+    return host != 0u ? 1 : 0;
+}
 
 size_t sdm_workspace_size(const sslp_sdm_shape* s) {
     if (check_sdm_shape(s, false) != SSLP_OK) return 0;
@@ -191,6 +233,7 @@ int sdm_sparse_update(const sslp_sdm_shape* s, int dtype, int residual_mode, con
     a.beta = beta;
     a.M = M;
     a.y = y;
+    a.err = error_word();
     return hip_status(run_recurrence(a, s, workspace, (hipStream_t)stream), "sdm update launch");
 }
 
@@ -282,6 +325,7 @@ static int sdm_run(const sslp_sdm_shape* s, int T, int dtype, int residual_mode,
     a.beta = beta;
     a.M = M;
     a.y = y;
+    a.err = error_word();
     return hip_status(run_recurrence(a, s, ws + addressing_bytes(s, T), st), "sdm update launch");
 }
 
@@ -420,6 +464,7 @@ static sslp::SdmUpdateArgs update_args(const sslp_sdm_shape* s, int dtype, int r
     a.M = M;
     a.y = y;
     a.saved = saved;
+    a.err = error_word();
     return a;
 }
 
@@ -561,6 +606,7 @@ int sdm_backward(const sslp_sdm_shape* s, int dtype, int residual_mode, const in
     a.dbeta = dbeta;
     a.dwt_w = dwt_w ? dwt_w : reinterpret_cast<float*>(ws + bp);
     a.dwt_r = dwt_r ? dwt_r : reinterpret_cast<float*>(ws + bp + bw);
+    a.err = error_word();
     hipStream_t st = (hipStream_t)stream;
     if (int rc = hip_status(sslp::launch_sdm_update_backward(a, st), "sdm backward launch"))
         return rc;

@@ -135,6 +135,15 @@ SSLP_DEVICE uint64_t wave_max_u64(uint64_t x) {
 // waits for every outstanding global load and store, it lets loads issued
 // ahead of time (register or LDS-DMA prefetch) stay in flight across it.  Any
 // wait for global memory a barrier must cover is written out before it.
+// A caller-supplied slot index, kept inside the table: an index outside
+// [0, N) becomes slot 0 and sets *err (when given) to 1, so that no access
+// leaves the table whatever the input; the call's results are then undefined.
+SSLP_DEVICE int checked_slot(int slot, long long N, unsigned* err) {
+    if ((unsigned long long)(unsigned)slot < (unsigned long long)N) return slot;
+    if (err != nullptr) atomicOr(err, 1u);
+    return 0;
+}
+
 SSLP_DEVICE void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
 
 SSLP_DEVICE void wave_sync() {

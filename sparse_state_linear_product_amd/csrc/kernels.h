@@ -37,6 +37,10 @@ struct SdmUpdateArgs {
     // before the token (what a backward sweep restores); only the per-token
     // kernel writes it
     float* saved;
+    // device word set to 1 when a slot index outside [0, N) is met (such a
+    // slot is replaced by slot 0, or the chunk holding it is skipped, so no
+    // access leaves the table); may be null
+    unsigned* err;
 };
 hipError_t launch_sdm_update(const SdmUpdateArgs& a, hipStream_t st);
 
@@ -83,6 +87,7 @@ struct SdmBwdArgs {
     float* dbeta;        // [B,T,H]
     float* dwt_w;        // [B,T,H,W]
     float* dwt_r;        // [B,T,H,R]
+    unsigned* err;       // as SdmUpdateArgs::err
 };
 size_t sdm_bwd_part_bytes(int B, int T, int H, int dv, int W, int R);
 hipError_t launch_sdm_update_backward(const SdmBwdArgs& a, hipStream_t st);

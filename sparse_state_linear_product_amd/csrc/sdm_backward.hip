@@ -69,10 +69,10 @@ SSLP_DEVICE void load_meta(BwdMeta<NL>& m, const SdmBwdArgs& a, size_t bth, int 
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
         const int nw = min(g + 4 * r, a.W - 1), nr = min(g + 4 * r, a.R - 1);
-        m.sw[r] = a.idx_w[bth * a.W + nw];
+        m.sw[r] = checked_slot(a.idx_w[bth * a.W + nw], a.N, a.err);
         m.w[r] = a.wt_w[bth * a.W + nw];
         m.P[r] = a.saved[(bth * a.W + nw) * a.dv + colc];
-        m.sr[r] = a.idx_r[bth * a.R + nr];
+        m.sr[r] = checked_slot(a.idx_r[bth * a.R + nr], a.N, a.err);
         m.e[r] = a.wt_r[bth * a.R + nr];
     }
 }

@@ -92,6 +92,7 @@ struct PlanArgs {
     const float* alpha;
     const float* beta;
     uint32_t* plan;  // [B, H, nch, PL_WORDS]
+    unsigned* err;   // set to 1 when a chunk holds a slot index outside [0, N); may be null
 };
 
 // ---------------------------------------------------------------------------
@@ -122,7 +123,24 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     const int c = blockIdx.x % nch, bh = blockIdx.x / nch;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const int t0 = c * CC;
-    const int ntok = a.T - t0 < CC ? a.T - t0 : CC;
+    // a chunk holding a slot index outside [0, N) is planned as an empty chunk:
+    // its tokens write nothing and read nothing (y = 0), and no row offset
+    // outside the table reaches the apply kernel
+    __shared__ int s_bad;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    {
+        const int nt = a.T - t0 < CC ? a.T - t0 : CC;
+        for (int e = tid; e < nt * NW; e += 256) {
+            const size_t bth = ((size_t)b * a.T + t0 + (e >> 5)) * a.H + h;
+            const unsigned sw = (unsigned)a.idx_w[bth * NW + (e & 31)];
+            const unsigned sr = (unsigned)a.idx_r[bth * NR + (e & 31)];
+            if (sw >= (unsigned)a.N || sr >= (unsigned)a.N) s_bad = 1;
+        }
+    }
+    __syncthreads();
+    if (s_bad && tid == 0 && a.err != nullptr) atomicOr(a.err, 1u);
+    const int ntok = s_bad ? 0 : (a.T - t0 < CC ? a.T - t0 : CC);
     uint32_t* out = a.plan + (size_t)blockIdx.x * PL_WORDS;
     const uint64_t NONE = ~0ull;
 
@@ -876,7 +894,7 @@ hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* planws, hipSt
     uint32_t* plan = static_cast<uint32_t*>(planws);
     const int nch = (a.T + CC - 1) / CC;
     PlanArgs pa{a.B, a.T, a.H, a.N, a.dv, nch, a.residual_mode, a.idx_w, a.wt_w, a.idx_r, a.wt_r,
-                a.alpha, a.beta, plan};
+                a.alpha, a.beta, plan, a.err};
     sdm_chunk_plan_kernel<<<(unsigned)(a.B * a.H * nch), 256, 0, st>>>(pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

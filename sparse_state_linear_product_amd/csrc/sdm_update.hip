@@ -55,9 +55,9 @@ SSLP_DEVICE void load_fwd_meta(FwdMeta<NL>& m, const SdmUpdateArgs& a, size_t bt
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
         const int nw = min(g + 4 * r, a.W - 1), nr = min(g + 4 * r, a.R - 1);
-        m.sw[r] = a.idx_w[bth * a.W + nw];
+        m.sw[r] = checked_slot(a.idx_w[bth * a.W + nw], a.N, a.err);
         m.w[r] = a.wt_w[bth * a.W + nw];
-        m.sr[r] = a.idx_r[bth * a.R + nr];
+        m.sr[r] = checked_slot(a.idx_r[bth * a.R + nr], a.N, a.err);
         m.e[r] = a.wt_r[bth * a.R + nr];
     }
 }
@@ -198,9 +198,9 @@ __global__ __launch_bounds__(256) void sdm_decode_update_kernel(SdmUpdateArgs a)
     for (int r = 0; r < NL; ++r) {
         const int n = w + 4 * r;
         const bool okw = n < W, okr = n < R;
-        ws[r] = okw ? a.idx_w[(size_t)bh * W + n] : 0;
+        ws[r] = okw ? checked_slot(a.idx_w[(size_t)bh * W + n], a.N, a.err) : 0;
         ww[r] = okw ? a.wt_w[(size_t)bh * W + n] : 0.f;
-        rs[r] = okr ? a.idx_r[(size_t)bh * R + n] : -1;
+        rs[r] = okr ? checked_slot(a.idx_r[(size_t)bh * R + n], a.N, a.err) : -1;
         wr[r] = okr ? a.wt_r[(size_t)bh * R + n] : 0.f;
         if (okw && threadIdx.x % 64 == 0) s_wslot[n] = ws[r];
     }

@@ -373,3 +373,45 @@ def test_side_stream_call_orders_its_own_allocations():
     torch.cuda.synchronize()
     del junk
     assert torch.equal(y, y_ref) and torch.equal(M, M_ref)
+
+
+@pytest.mark.parametrize("path", ["chunked", "per_token"])
+def test_out_of_range_slot_is_contained_and_reported(path):
+    # A caller index outside [0, N) must not reach memory outside the table: the
+    # table is a slice of a larger buffer whose guard regions must stay bitwise;
+    # the device error flag reports the call.  Chunk path: W = R = 32, T >= 64;
+    # per-token path: W = R = 9.
+    sslp = _sslp()
+    W = 32 if path == "chunked" else 9
+    B, T, H, sq, dv = 1, 80, 2, 16, 32
+    N = sq * sq
+    announce(f"out-of-range slot, {path} path")
+    assert not sslp.device_error()  # clear anything left over
+    g = torch.Generator().manual_seed(91)
+    idx = torch.stack([torch.randperm(N, generator=g)[:W] for _ in range(B * T * H)]).int()
+    idx = idx.view(B, T, H, W).contiguous()
+    idx[0, 70, 1, 3] = N + 5           # one bad write slot (chunk 4, head 1)
+    idx_r = idx.clone()
+    idx_r[0, 10, 0, 0] = -7            # one bad read slot (chunk 0, head 0)
+    wt = torch.full((B, T, H, W), 1.0 / W)
+    v = torch.randn((B, T, H, dv), generator=g)
+    alpha = torch.full((B, T, H), 0.95)
+    beta = torch.full((B, T, H), 0.5)
+    guard = 1 << 16
+    buf = torch.randn((2 * guard + B * H * N * dv,), generator=g).to(DEV)
+    before = buf.clone()
+    M = buf[guard:guard + B * H * N * dv].view(B, H, N, dv)
+    y = sslp.sdm_sparse_update(idx.to(DEV), wt.to(DEV), idx_r.to(DEV), wt.to(DEV), v.to(DEV),
+                               alpha.to(DEV), beta.to(DEV), M)
+    torch.cuda.synchronize()
+    assert sslp.device_error()
+    assert not sslp.device_error()  # the query cleared it
+    assert torch.equal(buf[:guard], before[:guard])
+    assert torch.equal(buf[-guard:], before[-guard:])
+    assert torch.isfinite(y).all()
+    # a clean call after it reports nothing
+    idx[0, 70, 1, 3] = 0 if 0 not in idx[0, 70, 1].tolist() else int(
+        [s for s in range(N) if s not in idx[0, 70, 1].tolist()][0])
+    sslp.sdm_sparse_update(idx.to(DEV), wt.to(DEV), idx.to(DEV), wt.to(DEV), v.to(DEV),
+                           alpha.to(DEV), beta.to(DEV), M)
+    assert not sslp.device_error()
