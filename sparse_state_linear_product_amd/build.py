@@ -49,6 +49,13 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    # the inline-asm loads' destination registers must stay untouched until
+    # their explicit waits in the generated code (fails the build otherwise)
+    if __package__:
+        from . import asm_check
+    else:  # run as a script: this directory is on sys.path
+        import asm_check
+    asm_check.run(verbose=verbose)
     return LIB
 
 
