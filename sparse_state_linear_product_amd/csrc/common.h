@@ -138,10 +138,17 @@ SSLP_DEVICE uint64_t wave_max_u64(uint64_t x) {
 // A caller-supplied slot index, kept inside the table: an index outside
 // [0, N) becomes slot 0 and sets *err (when given) to 1, so that no access
 // leaves the table whatever the input; the call's results are then undefined.
-SSLP_DEVICE int checked_slot(int slot, long long N, unsigned* err) {
-    if ((unsigned long long)(unsigned)slot < (unsigned long long)N) return slot;
-    if (err != nullptr) atomicOr(err, 1u);
-    return 0;
+// The check has no branch and no memory access: a branch on a prefetched index
+// would make the wavefront wait for that load where the branch stands.  The
+// caller accumulates `bad` and reports it once, at its end, with
+// report_slot_error.
+SSLP_DEVICE int keep_slot(int slot, long long N, bool& bad) {
+    const bool ok = (unsigned long long)(unsigned)slot < (unsigned long long)N;
+    bad |= !ok;
+    return ok ? slot : 0;
+}
+SSLP_DEVICE void report_slot_error(bool bad, unsigned* err) {
+    if (bad && err != nullptr) atomicOr(err, 1u);
 }
 
 SSLP_DEVICE void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }

@@ -69,10 +69,10 @@ SSLP_DEVICE void load_meta(BwdMeta<NL>& m, const SdmBwdArgs& a, size_t bth, int 
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
         const int nw = min(g + 4 * r, a.W - 1), nr = min(g + 4 * r, a.R - 1);
-        m.sw[r] = checked_slot(a.idx_w[bth * a.W + nw], a.N, a.err);
+        m.sw[r] = a.idx_w[bth * a.W + nw];  // range-checked where used (keep_slot)
         m.w[r] = a.wt_w[bth * a.W + nw];
         m.P[r] = a.saved[(bth * a.W + nw) * a.dv + colc];
-        m.sr[r] = checked_slot(a.idx_r[bth * a.R + nr], a.N, a.err);
+        m.sr[r] = a.idx_r[bth * a.R + nr];
         m.e[r] = a.wt_r[bth * a.R + nr];
     }
 }
@@ -99,9 +99,15 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
     const bool shared = a.residual_mode == 0;
 
     BwdMeta<NL> cur;
+    bool bad = false;  // a slot index outside [0, N) was seen (and replaced by 0)
     if (a.T > 0) load_meta<io_t, NL>(cur, a, ((size_t)b * a.T + (a.T - 1)) * a.H + h, g, colc);
     for (int t = a.T - 1; t >= 0; --t) {
         const size_t bth = ((size_t)b * a.T + t) * a.H + h;
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            cur.sw[r] = keep_slot(cur.sw[r], a.N, bad);
+            cur.sr[r] = keep_slot(cur.sr[r], a.N, bad);
+        }
         // ---- one trip for every row the token touches: M_t and G at the read
         //      slots, G at the write slots ----
         float mr[NL], gr[NL], gw[NL];
@@ -221,6 +227,7 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
         wave_sync();
         cur = nxt;
     }
+    report_slot_error(bad, a.err);
 }
 
 // Adds the slices' partial sums in slice order: one thread per (token, head, j).

@@ -55,9 +55,9 @@ SSLP_DEVICE void load_fwd_meta(FwdMeta<NL>& m, const SdmUpdateArgs& a, size_t bt
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
         const int nw = min(g + 4 * r, a.W - 1), nr = min(g + 4 * r, a.R - 1);
-        m.sw[r] = checked_slot(a.idx_w[bth * a.W + nw], a.N, a.err);
+        m.sw[r] = a.idx_w[bth * a.W + nw];  // range-checked where used (keep_slot)
         m.w[r] = a.wt_w[bth * a.W + nw];
-        m.sr[r] = checked_slot(a.idx_r[bth * a.R + nr], a.N, a.err);
+        m.sr[r] = a.idx_r[bth * a.R + nr];
         m.e[r] = a.wt_r[bth * a.R + nr];
     }
 }
@@ -80,9 +80,15 @@ __global__ __launch_bounds__(64) void sdm_update_kernel(SdmUpdateArgs a) {
     io_t* yout = static_cast<io_t*>(a.y);
 
     FwdMeta<NL> cur;
+    bool bad = false;  // a slot index outside [0, N) was seen (and replaced by 0)
     if (a.T > 0) load_fwd_meta<io_t, NL>(cur, a, ((size_t)b * a.T) * a.H + h, g, colc);
     for (int t = 0; t < a.T; ++t) {
         const size_t bth = ((size_t)b * a.T + t) * a.H + h;
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            cur.sw[r] = keep_slot(cur.sw[r], a.N, bad);
+            cur.sr[r] = keep_slot(cur.sr[r], a.N, bad);
+        }
         // ---- one trip for the write and the read rows ----
         float m0[NL], mr[NL];
 #pragma unroll
@@ -160,6 +166,7 @@ __global__ __launch_bounds__(64) void sdm_update_kernel(SdmUpdateArgs a) {
         wave_sync();
         cur = nxt;
     }
+    report_slot_error(bad, a.err);
 }
 
 // ---------------------------------------------------------------------------
@@ -191,6 +198,7 @@ __global__ __launch_bounds__(256) void sdm_decode_update_kernel(SdmUpdateArgs a)
     const float al = a.alpha[bh], be = a.beta[bh];
 
     // gather the write rows and the read rows of this wave
+    bool bad = false;  // a slot index outside [0, N) was seen (and replaced by 0)
     int ws[NL], rs[NL];
     float ww[NL], wr[NL];
     float4 mw[NL], mr[NL];
@@ -198,9 +206,9 @@ __global__ __launch_bounds__(256) void sdm_decode_update_kernel(SdmUpdateArgs a)
     for (int r = 0; r < NL; ++r) {
         const int n = w + 4 * r;
         const bool okw = n < W, okr = n < R;
-        ws[r] = okw ? checked_slot(a.idx_w[(size_t)bh * W + n], a.N, a.err) : 0;
+        ws[r] = okw ? keep_slot(a.idx_w[(size_t)bh * W + n], a.N, bad) : 0;
         ww[r] = okw ? a.wt_w[(size_t)bh * W + n] : 0.f;
-        rs[r] = okr ? checked_slot(a.idx_r[(size_t)bh * R + n], a.N, a.err) : -1;
+        rs[r] = okr ? keep_slot(a.idx_r[(size_t)bh * R + n], a.N, bad) : -1;
         wr[r] = okr ? a.wt_r[(size_t)bh * R + n] : 0.f;
         if (okw && threadIdx.x % 64 == 0) s_wslot[n] = ws[r];
     }
@@ -297,6 +305,7 @@ __global__ __launch_bounds__(256) void sdm_decode_update_kernel(SdmUpdateArgs a)
         yo[2] = from_f32<io_t>(t.z);
         yo[3] = from_f32<io_t>(t.w);
     }
+    report_slot_error(bad, a.err);
 }
 
 template <typename io_t>
