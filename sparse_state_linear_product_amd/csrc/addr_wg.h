@@ -13,12 +13,12 @@
 //   2. the dominance set D = {(i, j) : (i+1)(j+1) <= budget}: each wavefront
 //      sorts its 64 entries, one wavefront merges them (merge4_top64);
 //      tau = the budget-th key;
-//   3. F = #{k^2 candidates with key >= tau}, counted by the merging
-//      wavefront; F == budget proves D's top-budget is the answer, else all
+//   3. F = #{k^2 candidates with key >= tau}, counted by the group's four
+//      wavefronts; F == budget proves D's top-budget is the answer, else all
 //      k^2 candidates are ranked by counting (wg_addr_rank_all, the rare path
 //      of rounding ties);
-//   4. softmax over the selected scores: on the common path by the same
-//      wavefront inside wg_addr_select, else by wg_addr_softmax.
+//   4. softmax over the selected scores: on the common path by wavefront 0
+//      inside wg_addr_select, else by wg_addr_softmax.
 // Every function contains block-wide barriers (LDS-only: they do not wait for
 // global stores): all threads of the workgroup call it, each 256-thread group
 // on its own problem and shared memory.
@@ -33,19 +33,23 @@ namespace sslp {
 
 constexpr int kAddrGroup = 256;  // threads per addressing problem
 
-struct WgAddrSmem {
+// NCAND >= max(256, k^2): D on the common path, all k^2 candidates on the rare one
+template <int NCAND>
+struct WgAddrSmemT {
     union {
         uint64_t top[2][kAddrGroup];    // per half: each wave's sorted top-k of its 64 keys
         uint32_t top32[2][kAddrGroup];  // the same as 32-bit keys (bf16 scores)
     };
     float hsc[2][64];
     int hix[2][64];
-    uint64_t cand[4096];  // D, or all k^2 candidates on the rare path
+    uint64_t cand[NCAND];  // D, or all k^2 candidates on the rare path
     uint64_t sel[64];
     uint64_t tau;
     int F;
+    int Fw[kAddrGroup / 64];  // per-wavefront counts
     int drow[kAddrGroup], doff[65];  // D: row of each entry, first entry of each row
 };
+using WgAddrSmem = WgAddrSmemT<4096>;  // any k <= 64
 
 struct WgAddrProblem {
     const void* s1;  // [.., sqrtN] half scores of this problem
@@ -115,8 +119,8 @@ SSLP_DEVICE Key merge4_top64(const Key* lst, int lane) {
 // Steps 1-3 and, when F == budget, step 4 into idx / wt (and idx2 / wt2; any
 // of them may be null).  Ends with a barrier: sm.F is then valid for every
 // thread, and F != budget calls for wg_addr_rank_all and wg_addr_softmax.
-template <typename in_t>
-SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, int32_t* idx,
+template <typename in_t, typename Sm>
+SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, Sm& sm, int32_t* idx,
                                 float* wt, int32_t* idx2, float* wt2) {
     const int lane = t & 63, wv = t >> 6;
     const int n = pr.n, k = pr.k, budget = pr.budget, nD = pr.nD;
@@ -189,33 +193,34 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, 
     if (wv * 64 < nD) bitonic_sort_desc<1>(dkey, lane);  // uniform over the wavefront
     sm.cand[t] = dkey[0];
     block_sync_lds();
+    // tau = the budget-th key of D (0 if D has fewer than budget entries),
+    // merged by wavefront 0, which keeps D's ranked top 64 in `key`
+    uint64_t key = 0ull;
     if (wv == 0) {
-        const uint64_t key = nD <= 128 ? merge2_top64(&sm.cand[0], lane) : merge4_top64(&sm.cand[0], lane);
+        key = nD <= 128 ? merge2_top64(&sm.cand[0], lane) : merge4_top64(&sm.cand[0], lane);
         const uint64_t tau = shfl_u64(key, budget - 1);
-        // 3. exact count of all k^2 candidates at or above tau: lane column j
-        //    of the candidate matrix held in registers, rows i taken two at a
-        //    time (lanes 32..63 on row i + 1) when k <= 32
-        const bool two = k <= 32;
-        const int jl = two ? (lane & 31) : lane;
-        const int isub = two ? (lane >> 5) : 0;
-        const bool jok = jl < k;
-        const float bj = sm.hsc[1][jok ? jl : 0];
-        const uint32_t bix = (uint32_t)sm.hix[1][jok ? jl : 0];
-        // row values: lane l holds the first half's rank-l score and index,
-        // broadcast with readlane (no memory round trip per row)
-        const int al = lane < k ? lane : 0;
-        const int a_l = __float_as_int(sm.hsc[0][al]), x_l = sm.hix[0][al];
-        const int step = two ? 2 : 1;
-        int F = 0;
-        for (int i0 = 0; i0 < k; i0 += step) {
-            const int i1 = i0 + 1 < k ? i0 + 1 : i0;
-            const int a0 = __builtin_amdgcn_readlane(a_l, i0), a1 = __builtin_amdgcn_readlane(a_l, i1);
-            const int x0 = __builtin_amdgcn_readlane(x_l, i0), x1 = __builtin_amdgcn_readlane(x_l, i1);
-            const float sum = __int_as_float(isub ? a1 : a0) + bj;  // one fp32 RNE add
-            const bool ge = jok && i0 + isub < k &&
-                            make_key(sum, (uint32_t)(isub ? x1 : x0) * (uint32_t)n + bix) >= tau;
-            F += __popcll(__ballot(ge));
+        if (lane == 0) sm.tau = tau;
+    }
+    block_sync_lds();
+    // 3. exact count of all k^2 candidates at or above tau, spread over the
+    //    group's four wavefronts (candidate x = (i, j), i = x / k, j = x % k)
+    {
+        const uint64_t tau = sm.tau;
+        int cnt = 0;
+        for (int x0 = 0; x0 < k * k; x0 += kAddrGroup) {
+            const int x = x0 + t;
+            const bool in = x < k * k;
+            const int i = in ? x / k : 0, j = in ? x - (x / k) * k : 0;
+            const float sum = sm.hsc[0][i] + sm.hsc[1][j];  // one fp32 RNE add
+            const bool ge = in && make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n +
+                                                    (uint32_t)sm.hix[1][j]) >= tau;
+            cnt += __popcll(__ballot(ge));
         }
+        if (lane == 0) sm.Fw[wv] = cnt;
+    }
+    block_sync_lds();
+    if (wv == 0) {
+        const int F = sm.Fw[0] + sm.Fw[1] + sm.Fw[2] + sm.Fw[3];
         if (F == budget) {
             // 4. softmax over the selected fp32 scores (rank 0 holds the maximum)
             const float smax = key_score(shfl_u64(key, 0));
@@ -235,7 +240,8 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, WgAddrSmem& sm, 
 }
 
 // the rare path: rank all k^2 candidates (three barriers)
-SSLP_DEVICE void wg_addr_rank_all(const WgAddrProblem& pr, int t, WgAddrSmem& sm) {
+template <typename Sm>
+SSLP_DEVICE void wg_addr_rank_all(const WgAddrProblem& pr, int t, Sm& sm) {
     const int n = pr.n, k = pr.k, budget = pr.budget, kk = k * k;
     block_sync_lds();
     for (int x = t; x < kk; x += kAddrGroup) {
@@ -255,7 +261,8 @@ SSLP_DEVICE void wg_addr_rank_all(const WgAddrProblem& pr, int t, WgAddrSmem& sm
 
 // 4. softmax over the selected scores (rank 0 holds the maximum), by the
 // group's first wavefront; either output pair may be null
-SSLP_DEVICE void wg_addr_softmax(const WgAddrProblem& pr, int t, const WgAddrSmem& sm,
+template <typename Sm>
+SSLP_DEVICE void wg_addr_softmax(const WgAddrProblem& pr, int t, const Sm& sm,
                                  int32_t* idx, float* wt, int32_t* idx2, float* wt2) {
     if (t < 64) {
         const int budget = pr.budget;

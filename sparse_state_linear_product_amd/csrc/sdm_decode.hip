@@ -29,27 +29,39 @@ constexpr int kCols = 256;    // columns per workgroup
 constexpr int kWaves = 8;     // wavefronts per workgroup
 constexpr int kMaxRows = 64;  // W, R <= 64
 
-struct UpdSmem {
-    float4 nw[kMaxRows][64];   // updated write rows, this workgroup's columns
-    float4 part[kWaves][64];   // per-wave partial sums
-};
-constexpr size_t kAddrBytes = 2 * sizeof(WgAddrSmem);
-constexpr size_t kRawBytes = kAddrBytes > sizeof(UpdSmem) ? kAddrBytes : sizeof(UpdSmem);
-
-template <typename io_t, int NL>
-__global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecodeArgs a) {
+// LDS of one workgroup, sized for at most 8 NL rows per set and a per-half
+// top-k of at most KMAX (the rare path ranks all k^2 candidates): 41 KB at
+// the 1.4B-layer shape (k = W = R = 32)
+template <int NL, int KMAX>
+struct DecSmem {
+    static constexpr int kRows = kWaves * NL;
+    static constexpr int kCand = KMAX * KMAX > kAddrGroup ? KMAX * KMAX : kAddrGroup;
+    struct Upd {
+        float4 nw[kRows][64];     // updated write rows, this workgroup's columns
+        float4 part[kWaves][64];  // per-wave partial sums
+    };
     // the addressing scratch of both sets, reused by the update once the
-    // selections sit in s_idx / s_wt
-    __shared__ __align__(16) unsigned char s_raw[kRawBytes];
-    __shared__ int s_idx[2][kMaxRows];
-    __shared__ float s_wt[2][kMaxRows];
+    // selections sit in idx / wt
+    union {
+        WgAddrSmemT<kCand> addr[2];
+        Upd upd;
+    };
+    int idx[2][kRows];
+    float wt[2][kRows];
+};
+
+template <typename io_t, int NL, int KMAX>
+__global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecodeArgs a) {
+    __shared__ DecSmem<NL, KMAX> sm;
+    auto& s_idx = sm.idx;
+    auto& s_wt = sm.wt;
     const int t = threadIdx.x, grp = t >> 8, tt = t & 255;
     const int nblk = (a.dv + kCols - 1) / kCols;
     const int slice = blockIdx.x % nblk;
     const int p = blockIdx.x / nblk;  // = b * H + h
 
     // ---- addressing: group 0 the write set, group 1 the read set ----
-    WgAddrSmem* sma = reinterpret_cast<WgAddrSmem*>(s_raw);
+    auto* sma = sm.addr;
     const size_t soff = (size_t)p * a.sqrtN;
     const WgAddrProblem pr{static_cast<const io_t*>(a.s1[grp]) + soff,
                            static_cast<const io_t*>(a.s2[grp]) + soff, a.sqrtN, a.k[grp],
@@ -67,7 +79,7 @@ __global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecode
     }
 
     // ---- the update and the read of this workgroup's columns ----
-    UpdSmem& su = *reinterpret_cast<UpdSmem*>(s_raw);
+    auto& su = sm.upd;
     const int lane = t & 63, w = t >> 6;
     const int col = slice * kCols + 4 * lane;
     const bool colok = col < a.dv;  // dv % 4 == 0: a lane's 4 columns are all in or all out
@@ -87,11 +99,19 @@ __global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecode
         rs[r] = okr ? s_idx[1][n] : -1;
         wr[r] = okr ? s_wt[1][n] : 0.f;
     }
+    // every load is issued from a valid address (row 0, the last 4 columns)
+    // and masked afterwards, so that none of them waits on a condition
+    const int cc = colok ? col : a.dv - 4;
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+        mw[r] = *reinterpret_cast<const float4*>(tab + (size_t)ws[r] * a.dv + cc);
+        mr[r] = *reinterpret_cast<const float4*>(tab + (size_t)(rs[r] < 0 ? 0 : rs[r]) * a.dv + cc);
+    }
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
         const int n = w + kWaves * r;
-        mw[r] = (n < W && colok) ? *reinterpret_cast<const float4*>(tab + (size_t)ws[r] * a.dv + col) : z4;
-        mr[r] = (n < R && colok) ? *reinterpret_cast<const float4*>(tab + (size_t)rs[r] * a.dv + col) : z4;
+        if (!(n < W && colok)) mw[r] = z4;
+        if (!(n < R && colok)) mr[r] = z4;
     }
     float4 vc = z4;
     if (colok) {
@@ -181,13 +201,19 @@ __global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecode
     }
 }
 
-template <typename io_t>
+template <typename io_t, int KMAX>
 hipError_t dispatch_rows(int rows, unsigned grid, hipStream_t st, const SdmDecodeArgs& a) {
-    if (rows <= 8) sdm_decode_fused_kernel<io_t, 1><<<grid, 64 * kWaves, 0, st>>>(a);
-    else if (rows <= 16) sdm_decode_fused_kernel<io_t, 2><<<grid, 64 * kWaves, 0, st>>>(a);
-    else if (rows <= 32) sdm_decode_fused_kernel<io_t, 4><<<grid, 64 * kWaves, 0, st>>>(a);
-    else sdm_decode_fused_kernel<io_t, 8><<<grid, 64 * kWaves, 0, st>>>(a);
+    if (rows <= 8) sdm_decode_fused_kernel<io_t, 1, KMAX><<<grid, 64 * kWaves, 0, st>>>(a);
+    else if (rows <= 16) sdm_decode_fused_kernel<io_t, 2, KMAX><<<grid, 64 * kWaves, 0, st>>>(a);
+    else if (rows <= 32) sdm_decode_fused_kernel<io_t, 4, KMAX><<<grid, 64 * kWaves, 0, st>>>(a);
+    else sdm_decode_fused_kernel<io_t, 8, KMAX><<<grid, 64 * kWaves, 0, st>>>(a);
     return hipGetLastError();
+}
+
+template <typename io_t>
+hipError_t dispatch_k(int kmax, int rows, unsigned grid, hipStream_t st, const SdmDecodeArgs& a) {
+    if (kmax <= 32) return dispatch_rows<io_t, 32>(rows, grid, st, a);
+    return dispatch_rows<io_t, 64>(rows, grid, st, a);
 }
 
 }  // namespace
@@ -207,8 +233,9 @@ hipError_t launch_sdm_decode_fused(SdmDecodeArgs a, hipStream_t st) {
     const long long grid = (long long)a.P * ((a.dv + kCols - 1) / kCols);
     if (grid > 0x7fffffffll) return hipErrorInvalidValue;
     const int rows = a.budget[0] > a.budget[1] ? a.budget[0] : a.budget[1];
-    if (a.dtype == 0) return dispatch_rows<float>(rows, (unsigned)grid, st, a);
-    return dispatch_rows<bf16_t>(rows, (unsigned)grid, st, a);
+    const int kmax = a.k[0] > a.k[1] ? a.k[0] : a.k[1];
+    if (a.dtype == 0) return dispatch_k<float>(kmax, rows, (unsigned)grid, st, a);
+    return dispatch_k<bf16_t>(kmax, rows, (unsigned)grid, st, a);
 }
 
 }  // namespace sslp

@@ -232,6 +232,50 @@ def test_decode_steps_equal_forward_and_chaining():
     assert torch.equal(Mc.cpu(), Mf.cpu())
 
 
+def test_decode_steps_replayed_from_a_graph_match_eager():
+    # a serving loop captures its decode steps in a HIP graph and replays them;
+    # every replay (the table reset eagerly in between, with synchronisations)
+    # must give the eager steps' outputs and table bit for bit
+    sslp = _sslp()
+    cfg = wl.SdmConfig("decode_graph", 5, 4, 2, 20, 300, 8, 8, 16, 16, torch.bfloat16, 52)
+    announce("decode steps: HIP graph replays == eager steps")
+    x = {k: v.to(DEV) for k, v in wl.sdm_inputs(cfg).items()}
+    sl = [{k: v[:, t].contiguous() for k, v in x.items()} for t in range(cfg.T)]
+    M0 = torch.randn((cfg.B, cfg.H, cfg.N, cfg.d_v), generator=torch.Generator().manual_seed(5))
+    M0 = M0.to(DEV)
+
+    def steps(M, ys):
+        for t, s in enumerate(sl):
+            sslp.sdm_decode_step(s["sw1"], s["sw2"], s["sr1"], s["sr2"], s["v"], s["alpha"],
+                                 s["beta"], M, cfg.k_w, cfg.k_r, cfg.W, cfg.R, y=ys[t])
+
+    Me = M0.clone()
+    ye = [torch.empty((cfg.B, cfg.H, cfg.d_v), dtype=cfg.dtype, device=DEV) for _ in sl]
+    steps(Me, ye)
+    torch.cuda.synchronize()
+    Mg = M0.clone()
+    yg = [torch.empty_like(y) for y in ye]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        steps(Mg, yg)  # eager warm-up before the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps(Mg, yg)
+    for rep in range(3):
+        Mg.copy_(M0)
+        for y in yg:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Mg, Me), f"replay {rep}: table"
+        for t in range(cfg.T):
+            assert torch.equal(yg[t], ye[t]), f"replay {rep}: y of step {t}"
+
+
 def test_repeatable_bitwise():
     sslp = _sslp()
     cfg = wl.SdmConfig("rep", 1, 64, 2, 64, 64, 16, 16, 32, 32, torch.bfloat16, 44)
