@@ -352,9 +352,11 @@ typedef struct {
     int B, T, H, N, topk, c, d, chunk;
 } sslp_sse_shape;
 
-/* Workspace bytes of sse_forward: the routing of every token (B*T*H*topk
- * partition indices and gates), used when the caller passes sel or e_sel as
- * NULL.  0 for an invalid shape. */
+/* Workspace bytes of sse_forward and sse_forward_masking: the routing of
+ * every token (B*T*H*topk partition indices and gates, used when the caller
+ * passes sel or e_sel as NULL), every routed partition's visit list
+ * (B*H*N*T int32) and the token's contributions by slot before they are summed
+ * (B*T*H*(topk+1)*d bf16).  0 for an invalid shape. */
 size_t sse_workspace_size(const sslp_sse_shape* shape);
 
 /*
@@ -375,10 +377,12 @@ size_t sse_workspace_size(const sslp_sse_shape* shape);
  *   q_sh, k_sh [B,T,H,c] dtype or NULL (then q, k are used);
  *   S [B,H,N+1,c,d] fp32 states in/out (index N = shared partition);
  *   o [B,T,H,d] dtype out;  sel [B,T,H,topk] int32 and e_sel [B,T,H,topk] fp32 optional.
- *   workspace, ws_bytes >= sse_workspace_size(shape) when sel or e_sel is NULL
- *   (may be NULL otherwise); SSLP_ERR_WORKSPACE if too small.
- * The routing runs first over all tokens (its own kernel), then the chunked
- * recurrence reads it back.
+ *   workspace, ws_bytes >= sse_workspace_size(shape) (may be NULL when T = 0);
+ *   SSLP_ERR_WORKSPACE if too small.
+ * Execution follows the varlen layout: the routing of all tokens, then every
+ * routed partition's visits grouped in time order, one chunked pass over every
+ * partition sequence (shared included), and the sum of each token's
+ * contributions in rank order, then shared.
  */
 int sse_forward(const sslp_sse_shape* shape, int dtype, const float* gate_logits, const void* q,
                 const void* k, const void* v, const float* lambda, const void* q_sh,

@@ -757,7 +757,7 @@ static size_t sse_route_bytes(const sslp_sse_shape* s) {
 
 size_t sse_workspace_size(const sslp_sse_shape* s) {
     if (check_sse_shape(s) != SSLP_OK) return 0;
-    return 2 * sse_route_bytes(s);
+    return 2 * sse_route_bytes(s) + sslp::sse_scratch_bytes(s->B, s->T, s->H, s->N, s->topk, s->d);
 }
 
 static int sse_run(const char* name, int masking, const sslp_sse_shape* s, int dtype,
@@ -781,17 +781,15 @@ static int sse_run(const char* name, int masking, const sslp_sse_shape* s, int d
     REQUIRE_PTR(v);
     REQUIRE_PTR(lambda);
     REQUIRE_PTR(o);
-    if (sel == nullptr || e_sel == nullptr) {
-        REQUIRE(workspace != nullptr && ws_bytes >= sse_workspace_size(s), SSLP_ERR_WORKSPACE,
-                "workspace of %zu bytes needed (got %zu)", sse_workspace_size(s), ws_bytes);
-        REQUIRE_ALIGNED(workspace);
-        char* ws = static_cast<char*>(workspace);
-        if (sel == nullptr) sel = reinterpret_cast<int32_t*>(ws);
-        if (e_sel == nullptr) e_sel = reinterpret_cast<float*>(ws + sse_route_bytes(s));
-    }
+    REQUIRE(workspace != nullptr && ws_bytes >= sse_workspace_size(s), SSLP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", sse_workspace_size(s), ws_bytes);
+    REQUIRE_ALIGNED(workspace);
+    char* ws = static_cast<char*>(workspace);
+    if (sel == nullptr) sel = reinterpret_cast<int32_t*>(ws);
+    if (e_sel == nullptr) e_sel = reinterpret_cast<float*>(ws + sse_route_bytes(s));
     return hip_status(sslp::launch_sse(s->B, s->T, s->H, s->N, s->topk, s->d, dtype, gate_logits,
                                        q, k, v, lambda, q_sh, k_sh, S, o, sel, e_sel,
-                                       (hipStream_t)stream, masking),
+                                       ws + 2 * sse_route_bytes(s), (hipStream_t)stream, masking),
                       name);
 }
 

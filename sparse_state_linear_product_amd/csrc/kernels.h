@@ -119,12 +119,15 @@ hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, con
                             const float* bvec = nullptr, const float* wvec = nullptr);
 
 // ---- Sparse State Expansion ----
+// scratch of launch_sse: the visit lists and counts of every routed partition
+// and the per-slot contributions of every token
+size_t sse_scratch_bytes(int B, int T, int H, int N, int topk, int dv);
 // masking = 1: the masked execution (every routed partition over every token,
 // unselected tokens with gate 0 and decay 1) instead of the grouped visits
 hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
                       const float* logits, const void* q, const void* k, const void* v,
                       const float* lam, const void* q_sh, const void* k_sh, float* S, void* o,
-                      int32_t* sel, float* e_sel, hipStream_t st, int masking = 0);
+                      int32_t* sel, float* e_sel, void* scratch, hipStream_t st, int masking = 0);
 // one decode step (one token per sequence), touching only the selected states
 hipError_t launch_sse_decode(int B, int H, int N, int topk, int dv, const float* logits,
                              const void* q, const void* k, const void* v, const float* lam,

@@ -177,6 +177,11 @@ def test_gdn_and_sse_shape_errors():
     assert lib.sse_forward_masking(ctypes.byref(s), 0, *([FAKE] * 12), 0, None) == \
         _lib.SSLP_ERR_UNSUPPORTED
     assert b"sse_forward_masking" in lib.sslp_last_error()
+    # the grouped execution needs its workspace (visit lists, contributions by
+    # slot) even when the caller takes the routing
+    s = _lib.SseShape(1, 8, 1, 8, 2, 128, 128, 64)
+    assert lib.sse_workspace_size(ctypes.byref(s)) >= 8 * 3 * 128 * 2
+    assert lib.sse_forward(ctypes.byref(s), 1, *([FAKE] * 12), 0, None) == _lib.SSLP_ERR_WORKSPACE
     # the decode step takes exactly one token per sequence
     s = _lib.SseShape(2, 2, 1, 8, 2, 128, 128, 64)
     assert lib.sse_decode_step(ctypes.byref(s), 1, *([FAKE] * 11), None) == _lib.SSLP_ERR_INVALID_ARG
