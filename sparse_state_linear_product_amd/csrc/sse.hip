@@ -82,10 +82,17 @@ struct __align__(16) SubBlock {
 struct __align__(16) GlaSmem {
     SubBlock sb[NWV];             // sub-block r staged by wavefront r (slow path: private)
     uint16_t vt[NWV][16][LDV];    // per wavefront: gated values of its 16 columns [column][visit]
-    int vtok[CH];                 // token of each visit of the chunk
-    float vgate[CH];              // its gate (1 for the shared partition, 0 when masked)
-    int vslot[CH];                // its contribution slot, -1 for a masked visit
+    int vtok[2][CH];              // token of each visit of the chunk (two chunks in flight)
+    float vgate[2][CH];           // its gate (1 for the shared partition, 0 when masked)
+    int vslot[2][CH];             // its contribution slot, -1 for a masked visit
     int small[NWV];
+};
+
+// the visits of one chunk (one of the two buffers)
+struct Meta {
+    const int* tok;
+    const float* gate;
+    const int* slot;
 };
 static_assert(sizeof(GlaSmem) <= 80 * 1024, "two workgroups per compute unit");
 
@@ -107,6 +114,7 @@ struct SseArgs {
     float* e_sel;
     int masking;      // 1: every routed partition runs over every token (masked execution)
     uint32_t* vis;    // [B*H][N][T] visits, token << 3 | rank
+    float* vgl;       // [B*H][N][T] their gates (0 for a masked visit)
     int* cnt;         // [B*H][N] visits per routed partition
     bf16_t* opart;    // [B*T*H][topk + 1][dv] contributions by slot
 };
@@ -144,82 +152,161 @@ __global__ __launch_bounds__(256) void sse_route_kernel(const float* __restrict_
 }
 
 // Visit lists of every routed partition of one (batch, head), in time order.
-// Wave w scans a quarter of the sequence twice: first counting each
-// partition's visits (ballot + popcount), then, from the counts of the waves
-// before it, placing them.
-__global__ __launch_bounds__(256) void sse_bucket_kernel(SseArgs a) {
-    __shared__ int s_cnt[4][MAXN];
+// Wave w (of 16) takes a sixteenth of the sequence, loads its routing at once,
+// and scans it twice: first counting each partition's visits (ballot +
+// popcount), then, from the counts of the waves before it, placing them.
+constexpr int BKW = 16;  // wavefronts of the bucket kernel
+constexpr int BKI = 4;   // 64-token steps a wavefront holds at once
+
+__global__ __launch_bounds__(64 * BKW) void sse_bucket_kernel(SseArgs a) {
+    __shared__ int s_cnt[BKW][MAXN];
     const int bh = blockIdx.x;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int T = a.T, N = a.N, topk = a.topk;
     uint32_t* vis = a.vis + (size_t)bh * N * T;
-    auto ranks = [&](int t, int (&sl)[MAXK]) {
-#pragma unroll
-        for (int r = 0; r < MAXK; ++r) sl[r] = -1;
-        if (t < T) {
-            const size_t bth = ((size_t)b * T + t) * a.H + h;
-#pragma unroll
-            for (int r = 0; r < MAXK; ++r)
-                if (r < topk) sl[r] = a.sel[bth * topk + r];
-        }
-    };
+    float* vgl = a.vgl + (size_t)bh * N * T;
     if (a.masking) {
-        for (int t = threadIdx.x; t < T; t += 256) {
+        for (int t = threadIdx.x; t < T; t += 64 * BKW) {
+            const size_t bth = ((size_t)b * T + t) * a.H + h;
             int sl[MAXK];
-            ranks(t, sl);
+            float ge[MAXK];
+#pragma unroll
+            for (int r = 0; r < MAXK; ++r) {
+                sl[r] = r < topk ? a.sel[bth * topk + r] : -1;
+                ge[r] = r < topk ? a.e_sel[bth * topk + r] : 0.f;
+            }
             for (int i = 0; i < N; ++i) {
                 uint32_t rk = kNoRank;
+                float g = 0.f;
 #pragma unroll
                 for (int r = 0; r < MAXK; ++r)
-                    if (sl[r] == i) rk = (uint32_t)r;
+                    if (sl[r] == i) {
+                        rk = (uint32_t)r;
+                        g = ge[r];
+                    }
                 vis[(size_t)i * T + t] = ((uint32_t)t << 3) | rk;
+                vgl[(size_t)i * T + t] = g;
             }
         }
         if (threadIdx.x < N) a.cnt[bh * N + threadIdx.x] = T;
         return;
     }
-    const int per = ((T + 255) / 256) * 64;  // tokens per wave, a multiple of 64
+    const int per = ((T + 64 * BKW - 1) / (64 * BKW)) * 64;  // tokens per wave, a multiple of 64
     const int t_beg = min(w * per, T), t_end = min(t_beg + per, T);
-    int mine = 0;  // lane i < N: visits of partition i in this wave's range
-    for (int t0 = t_beg; t0 < t_end; t0 += 64) {
-        const int t = t0 + lane;
-        int sl[MAXK];
-        ranks(t < t_end ? t : T, sl);
-        for (int i = 0; i < N; ++i) {
-            bool hit = false;
-#pragma unroll
-            for (int r = 0; r < MAXK; ++r) hit |= sl[r] == i;
-            const int c = __popcll(__ballot(hit));
-            if (lane == i) mine += c;
-        }
-    }
-    if (lane < N) s_cnt[w][lane] = mine;
-    __syncthreads();
-    int pos[MAXN];
-#pragma unroll
-    for (int i = 0; i < MAXN; ++i) {
-        pos[i] = 0;
-        for (int u = 0; u < w; ++u) pos[i] += i < N ? s_cnt[u][i] : 0;
-    }
     const unsigned long long below = (1ull << lane) - 1ull;
-    for (int t0 = t_beg; t0 < t_end; t0 += 64) {
-        const int t = t0 + lane;
-        int sl[MAXK];
-        ranks(t < t_end ? t : T, sl);
+    int pos[MAXN];
+    for (int pass = 0; pass < 2; ++pass) {
+        int mine = 0;  // pass 0, lane i < N: visits of partition i in this wave's range
+        for (int t0 = t_beg; t0 < t_end; t0 += 64 * BKI) {
+            // the routing of BKI steps of 64 tokens, loaded before any is used
+            int sl[BKI][MAXK];
 #pragma unroll
-        for (int i = 0; i < MAXN; ++i) {
-            if (i >= N) break;
-            int rk = -1;
+            for (int s = 0; s < BKI; ++s) {
+                const int t = t0 + 64 * s + lane;
+                const size_t bth = ((size_t)b * T + (t < t_end ? t : 0)) * a.H + h;
 #pragma unroll
-            for (int r = 0; r < MAXK; ++r)
-                if (sl[r] == i) rk = r;
-            const unsigned long long m = __ballot(rk >= 0);
-            if (rk >= 0) vis[(size_t)i * T + pos[i] + __popcll(m & below)] = ((uint32_t)t << 3) | (uint32_t)rk;
-            pos[i] += __popcll(m);
+                for (int r = 0; r < MAXK; ++r) sl[s][r] = r < topk ? a.sel[bth * topk + r] : -1;
+            }
+            float ge[BKI][MAXK];  // the gates, needed by the placing pass only
+            if (pass == 1) {
+#pragma unroll
+                for (int s = 0; s < BKI; ++s) {
+                    const int t = t0 + 64 * s + lane;
+                    const size_t bth = ((size_t)b * T + (t < t_end ? t : 0)) * a.H + h;
+#pragma unroll
+                    for (int r = 0; r < MAXK; ++r) ge[s][r] = r < topk ? a.e_sel[bth * topk + r] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < BKI; ++s) {
+                const int t = t0 + 64 * s + lane;
+                const bool ok = t < t_end;
+#pragma unroll
+                for (int i = 0; i < MAXN; ++i) {
+                    if (i >= N) break;
+                    int rk = -1;
+#pragma unroll
+                    for (int r = 0; r < MAXK; ++r)
+                        if (ok && sl[s][r] == i) rk = r;
+                    const unsigned long long m = __ballot(rk >= 0);
+                    if (pass == 0) {
+                        if (lane == i) mine += __popcll(m);
+                    } else {
+                        if (rk >= 0) {
+                            const size_t at = (size_t)i * T + pos[i] + __popcll(m & below);
+                            vis[at] = ((uint32_t)t << 3) | (uint32_t)rk;
+                            float g = 0.f;
+#pragma unroll
+                            for (int r = 0; r < MAXK; ++r)
+                                if (r == rk) g = ge[s][r];
+                            vgl[at] = g;
+                        }
+                        pos[i] += __popcll(m);
+                    }
+                }
+            }
+        }
+        if (pass == 0) {
+            if (lane < N) s_cnt[w][lane] = mine;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < MAXN; ++i) {
+                pos[i] = 0;
+                for (int u = 0; u < w; ++u) pos[i] += i < N ? s_cnt[u][i] : 0;
+            }
         }
     }
-    if (w == 0 && lane < N) a.cnt[bh * N + lane] = s_cnt[0][lane] + s_cnt[1][lane] + s_cnt[2][lane] + s_cnt[3][lane];
+    if (w == 0 && lane < N) {
+        int c = 0;
+        for (int u = 0; u < BKW; ++u) c += s_cnt[u][lane];
+        a.cnt[bh * N + lane] = c;
+    }
+}
+
+// The raw inputs of one sub-block (lane l: state rows 2l, 2l+1) and of the
+// gated values (lane: 4 columns of 4 visits), loaded together before any of
+// them is used so that the chunk's staging waits for one memory round trip.
+struct SubIn {
+    float2 lam[16];
+    uint32_t qw[16], kw[16];
+};
+struct ValIn {
+    uint2 raw[4];
+};
+
+// Row addresses as a batch base (uniform) plus a 32-bit byte offset, so that
+// each load needs one address register (the launcher keeps T*H*c*4 < 2^31).
+struct RowBases {
+    const char* q;    // q (or q_sh) rows of batch b
+    const char* k;    // k (or k_sh) rows
+    const char* lam;  // Lambda rows (fp32)
+    const char* v;    // v rows
+};
+
+SSLP_DEVICE void load_sub(SubIn& in, const SseArgs& a, const RowBases& rb, int h, const Meta& mt,
+                          int p0, int L, int lane) {
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const int tp = mt.tok[p0 + (p < L ? p : L - 1)];
+        const uint32_t off = ((uint32_t)tp * (uint32_t)a.H + (uint32_t)h) * (CR * 2) + 4u * lane;
+        in.lam[p] = *reinterpret_cast<const float2*>(rb.lam + 2u * off);
+        in.qw[p] = *reinterpret_cast<const uint32_t*>(rb.q + off);
+        in.kw[p] = *reinterpret_cast<const uint32_t*>(rb.k + off);
+    }
+}
+
+SSLP_DEVICE void load_values(ValIn& in, const SseArgs& a, const RowBases& rb, int h, const Meta& mt,
+                             int L, int col0, int lane) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = lane + 64 * e;  // visit idx >> 2, columns 4 (idx & 3) ..
+        const int p = idx >> 2;
+        const int tp = mt.tok[p < L ? p : L - 1];
+        const uint32_t off = (((uint32_t)tp * (uint32_t)a.H + (uint32_t)h) * (uint32_t)a.dv +
+                              (uint32_t)(col0 + 4 * (idx & 3))) * 2u;
+        in.raw[e] = *reinterpret_cast<const uint2*>(rb.v + off);
+    }
 }
 
 // Stages visits p0 .. p0+L-1 (L <= 16) of the chunk as one sub-block (lane l
@@ -227,79 +314,62 @@ __global__ __launch_bounds__(256) void sse_bucket_kernel(SseArgs a) {
 // decay below 2^-4 was met.  CUT = true: ends the block before the visit that
 // would take the product of decays after the first visit below 2^-60 in any
 // row; returns the number of visits taken.
-template <bool CUT, typename io_t>
-SSLP_DEVICE int stage_sub(SubBlock& sb, const SseArgs& a, const io_t* qg, const io_t* kg, int b,
-                          int h, const GlaSmem& sm, int p0, int L, int lane) {
-    const int T = a.T, H = a.H;
+template <bool CUT>
+SSLP_DEVICE int stage_sub(SubBlock& sb, const SubIn& in, const Meta& mt, int p0, int L, int lane) {
     float ep0 = 1.f, ep1 = 1.f, em0 = 1.f, em1 = 1.f, af0 = 1.f, af1 = 1.f;
     int Le = L;
     bool alive = true, small = false;
     uint32_t kt0[8], kt1[8];  // rows 2l, 2l+1: bf16 pairs of visits (2u, 2u+1)
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        float2 lam[8];
-        uint32_t qw[8], kw[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int p = 8 * half + u;
-            const int tp = sm.vtok[p0 + (p < L ? p : L - 1)];
-            const size_t bth = ((size_t)b * T + tp) * H + h;
-            lam[u] = *reinterpret_cast<const float2*>(a.lam + bth * CR + 2 * lane);
-            qw[u] = *reinterpret_cast<const uint32_t*>(qg + bth * CR + 2 * lane);
-            kw[u] = *reinterpret_cast<const uint32_t*>(kg + bth * CR + 2 * lane);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int p = 8 * half + u;
-            float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
-            if (p < L) {
-                // masked execution: a token that does not select the partition
-                // leaves its state undecayed (and writes nothing: its gate is 0)
-                const bool frozen = sm.vslot[p0 + p] < 0;
-                const float l0 = frozen ? 1.f : lam[u].x, l1 = frozen ? 1.f : lam[u].y;
-                small |= l0 < kSmallDecay || l1 < kSmallDecay;
-                bool take = true;
-                if (p == 0) {
-                    af0 = l0;
-                    af1 = l1;
-                } else if (!CUT) {
-                    ep0 *= l0;
-                    ep1 *= l1;
-                    // hardware reciprocal (within 1 ulp, not an IEEE division):
-                    // the factor only scales a key that is rounded to bf16
+    for (int p = 0; p < 16; ++p) {
+        float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
+        if (p < L) {
+            // masked execution: a token that does not select the partition
+            // leaves its state undecayed (and writes nothing: its gate is 0)
+            const bool frozen = mt.slot[p0 + p] < 0;
+            const float l0 = frozen ? 1.f : in.lam[p].x, l1 = frozen ? 1.f : in.lam[p].y;
+            small |= l0 < kSmallDecay || l1 < kSmallDecay;
+            bool take = true;
+            if (p == 0) {
+                af0 = l0;
+                af1 = l1;
+            } else if (!CUT) {
+                ep0 *= l0;
+                ep1 *= l1;
+                // hardware reciprocal (within 1 ulp, not an IEEE division):
+                // the factor only scales a key that is rounded to bf16
+                em0 *= __builtin_amdgcn_rcpf(l0);
+                em1 *= __builtin_amdgcn_rcpf(l1);
+            } else if (alive) {
+                const float n0 = ep0 * l0, n1 = ep1 * l1;
+                if (__ballot(n0 < kMinBlockDecay || n1 < kMinBlockDecay) != 0ull) {
+                    alive = false;  // this visit starts the next block
+                    Le = p;
+                } else {
+                    ep0 = n0;
+                    ep1 = n1;
                     em0 *= __builtin_amdgcn_rcpf(l0);
                     em1 *= __builtin_amdgcn_rcpf(l1);
-                } else if (alive) {
-                    const float n0 = ep0 * l0, n1 = ep1 * l1;
-                    if (__ballot(n0 < kMinBlockDecay || n1 < kMinBlockDecay) != 0ull) {
-                        alive = false;  // this visit starts the next block
-                        Le = p;
-                    } else {
-                        ep0 = n0;
-                        ep1 = n1;
-                        em0 *= __builtin_amdgcn_rcpf(l0);
-                        em1 *= __builtin_amdgcn_rcpf(l1);
-                    }
-                }
-                if (CUT) take = alive;
-                if (take) {
-                    q0 = __uint_as_float(qw[u] << 16);
-                    q1 = __uint_as_float(qw[u] & 0xFFFF0000u);
-                    k0 = __uint_as_float(kw[u] << 16);
-                    k1 = __uint_as_float(kw[u] & 0xFFFF0000u);
                 }
             }
-            const uint32_t kb0 = f32_to_bf16(k0 * em0).bits, kb1 = f32_to_bf16(k1 * em1).bits;
-            *reinterpret_cast<uint32_t*>(&sb.qs[p][2 * lane]) =
-                (uint32_t)f32_to_bf16(q0 * ep0).bits | ((uint32_t)f32_to_bf16(q1 * ep1).bits << 16);
-            *reinterpret_cast<uint32_t*>(&sb.ks[p][2 * lane]) = kb0 | (kb1 << 16);
-            if (p & 1) {
-                kt0[p >> 1] |= kb0 << 16;
-                kt1[p >> 1] |= kb1 << 16;
-            } else {
-                kt0[p >> 1] = kb0;
-                kt1[p >> 1] = kb1;
+            if (CUT) take = alive;
+            if (take) {
+                q0 = __uint_as_float(in.qw[p] << 16);
+                q1 = __uint_as_float(in.qw[p] & 0xFFFF0000u);
+                k0 = __uint_as_float(in.kw[p] << 16);
+                k1 = __uint_as_float(in.kw[p] & 0xFFFF0000u);
             }
+        }
+        const uint32_t kb0 = f32_to_bf16(k0 * em0).bits, kb1 = f32_to_bf16(k1 * em1).bits;
+        *reinterpret_cast<uint32_t*>(&sb.qs[p][2 * lane]) =
+            (uint32_t)f32_to_bf16(q0 * ep0).bits | ((uint32_t)f32_to_bf16(q1 * ep1).bits << 16);
+        *reinterpret_cast<uint32_t*>(&sb.ks[p][2 * lane]) = kb0 | (kb1 << 16);
+        if (p & 1) {
+            kt0[p >> 1] |= kb0 << 16;
+            kt1[p >> 1] |= kb1 << 16;
+        } else {
+            kt0[p >> 1] = kb0;
+            kt1[p >> 1] = kb1;
         }
     }
     *reinterpret_cast<uint4*>(&sb.kt[2 * lane][0]) = make_uint4(kt0[0], kt0[1], kt0[2], kt0[3]);
@@ -313,30 +383,18 @@ SSLP_DEVICE int stage_sub(SubBlock& sb, const SseArgs& a, const io_t* qg, const 
 }
 
 // The gated values of this wavefront's 16 columns for the chunk's L visits
-// (zero past L), transposed: vt[n][p] = e_p v_p[col0 + n].  Lane: 4 columns
-// of 4 visits.
-template <typename io_t>
-SSLP_DEVICE void stage_values(uint16_t (&vt)[16][LDV], const SseArgs& a, const io_t* vg, int b,
-                              int h, const GlaSmem& sm, int L, int col0, int lane) {
-    const int T = a.T, H = a.H;
-    uint2 raw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = lane + 64 * e;  // visit idx >> 2, columns 4 (idx & 3) ..
-        const int p = idx >> 2;
-        const int tp = sm.vtok[p < L ? p : L - 1];
-        const size_t bth = ((size_t)b * T + tp) * H + h;
-        raw[e] = *reinterpret_cast<const uint2*>(vg + bth * a.dv + col0 + 4 * (idx & 3));
-    }
+// (zero past L), transposed: vt[n][p] = e_p v_p[col0 + n].
+SSLP_DEVICE void stage_values(uint16_t (&vt)[16][LDV], const ValIn& in, const Meta& mt, int L,
+                              int lane) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int idx = lane + 64 * e;
         const int p = idx >> 2, n = 4 * (idx & 3);
-        const float g = p < L ? sm.vgate[p] : 0.f;
-        vt[n][p] = f32_to_bf16(g * __uint_as_float(raw[e].x << 16)).bits;
-        vt[n + 1][p] = f32_to_bf16(g * __uint_as_float(raw[e].x & 0xFFFF0000u)).bits;
-        vt[n + 2][p] = f32_to_bf16(g * __uint_as_float(raw[e].y << 16)).bits;
-        vt[n + 3][p] = f32_to_bf16(g * __uint_as_float(raw[e].y & 0xFFFF0000u)).bits;
+        const float g = p < L ? mt.gate[p] : 0.f;
+        vt[n][p] = f32_to_bf16(g * __uint_as_float(in.raw[e].x << 16)).bits;
+        vt[n + 1][p] = f32_to_bf16(g * __uint_as_float(in.raw[e].x & 0xFFFF0000u)).bits;
+        vt[n + 2][p] = f32_to_bf16(g * __uint_as_float(in.raw[e].y << 16)).bits;
+        vt[n + 3][p] = f32_to_bf16(g * __uint_as_float(in.raw[e].y & 0xFFFF0000u)).bits;
     }
 }
 
@@ -427,16 +485,15 @@ SSLP_DEVICE f32x4_t sub_products(f32x4_t (&St)[8], const SubBlock& sb, const uin
 }
 
 // e_p o_p of the sub-block's visits into their contribution slots
-template <typename io_t>
-SSLP_DEVICE void write_contrib(const SseArgs& a, const GlaSmem& sm, f32x4_t ot, int b, int h,
-                               int vofs, int L, int col, int lane) {
+SSLP_DEVICE void write_contrib(const SseArgs& a, const Meta& mt, f32x4_t ot, int b, int h, int vofs,
+                               int L, int col, int lane) {
     const int g4 = lane >> 4, l16 = lane & 15;
     if (l16 >= L) return;
     const int vp = vofs + l16;
-    const int slot = sm.vslot[vp];
+    const int slot = mt.slot[vp];
     if (slot < 0) return;
-    const float e = sm.vgate[vp];
-    const size_t bth = ((size_t)b * a.T + sm.vtok[vp]) * a.H + h;
+    const float e = mt.gate[vp];
+    const size_t bth = ((size_t)b * a.T + mt.tok[vp]) * a.H + h;
     bf16_t* dst = a.opart + (bth * (a.topk + 1) + slot) * a.dv + col + 4 * g4;
     const uint32_t lo = (uint32_t)f32_to_bf16(e * ot[0]).bits | ((uint32_t)f32_to_bf16(e * ot[1]).bits << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16(e * ot[2]).bits | ((uint32_t)f32_to_bf16(e * ot[3]).bits << 16);
@@ -461,76 +518,122 @@ __global__ __launch_bounds__(64 * NWV, 2) void sse_gla_kernel(SseArgs a) {
     const int part = shared ? N : (inst - BH) - ((inst - BH) / N) * N;
     const int cnt = shared ? T : a.cnt[bh * N + part];
     if (cnt == 0) return;  // an idle partition keeps its state untouched
+    // the shared sequences (every token) are the kernel's critical path: their
+    // wavefronts win the issue arbitration against the routed ones on a unit
+    if (shared) __builtin_amdgcn_s_setprio(3);
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const io_t* qg = static_cast<const io_t*>(shared && a.q_sh ? a.q_sh : a.q);
     const io_t* kg = static_cast<const io_t*>(shared && a.k_sh ? a.k_sh : a.k);
     const io_t* vg = static_cast<const io_t*>(a.v);
     const uint32_t* vis = a.vis + ((size_t)bh * N + part) * T;
+    const float* vgl = a.vgl + ((size_t)bh * N + part) * T;
     const int col = cb * DB + 16 * w;  // this wavefront's 16 columns
+    const size_t brow = (size_t)b * T * a.H;  // first (token, head) row of batch b
+    const RowBases rb{reinterpret_cast<const char*>(qg + brow * CR), reinterpret_cast<const char*>(kg + brow * CR),
+                      reinterpret_cast<const char*>(a.lam + brow * CR), reinterpret_cast<const char*>(vg + brow * dv)};
     float* Sg = a.S + ((size_t)bh * (N + 1) + part) * CR * dv;
 
+    // state element (row 16m + 4 g4 + j, column col + l16): a uniform row base
+    // plus one per-lane offset, so no address is held through the chunk loop
+    const uint32_t soff = (uint32_t)(4 * g4) * (uint32_t)dv + (uint32_t)(col + l16);
     f32x4_t St[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) St[m][j] = Sg[(size_t)(16 * m + 4 * g4 + j) * dv + col + l16];
+        for (int j = 0; j < 4; ++j) St[m][j] = (Sg + (size_t)(16 * m + j) * dv)[soff];
 
-    for (int c0 = 0; c0 < cnt; c0 += CH) {
-        const int L = cnt - c0 < CH ? cnt - c0 : CH;
-        // ---- the chunk's visits ----
-        if (w == 0 && lane < L) {
+    // The visits of chunk c sit in LDS buffer c & 1.  Wavefront 0 holds the
+    // next chunk's list in registers (requested a chunk ahead) and writes it
+    // out while the current chunk is staged.
+    const int nch = (cnt + CH - 1) / CH;
+    uint32_t nx_ent = 0;  // wavefront 0, lane p: visit p of the chunk to come
+    float nx_gate = 0.f;
+    auto fetch_list = [&](int c) {
+        const int p = c * CH + lane;
+        if (!shared && p < cnt) {
+            nx_ent = vis[p];
+            nx_gate = vgl[p];
+        }
+    };
+    auto put_list = [&](int c) {
+        const int p = c * CH + lane;
+        if (p < cnt) {
             int t, slot;
             float gate;
             if (shared) {
-                t = c0 + lane;
+                t = p;
                 slot = a.topk;
                 gate = 1.f;
             } else {
-                const uint32_t e = vis[c0 + lane];
-                const uint32_t rk = e & 7u;
-                t = (int)(e >> 3);
+                const uint32_t rk = nx_ent & 7u;
+                t = (int)(nx_ent >> 3);
                 slot = rk == kNoRank ? -1 : (int)rk;
-                gate = slot < 0 ? 0.f : a.e_sel[(((size_t)b * T + t) * a.H + h) * a.topk + rk];
+                gate = nx_gate;
             }
-            sm.vtok[lane] = t;
-            sm.vslot[lane] = slot;
-            sm.vgate[lane] = gate;
+            sm.vtok[c & 1][lane] = t;
+            sm.vslot[c & 1][lane] = slot;
+            sm.vgate[c & 1][lane] = gate;
         }
-        block_sync_lds();
-        // ---- sub-block w (shared by all columns) and this wave's values ----
+    };
+    if (w == 0) {
+        fetch_list(0);
+        put_list(0);
+        if (nch > 1) fetch_list(1);
+    }
+    block_sync_lds();
+    for (int c = 0; c < nch; ++c) {
+        const int L = cnt - c * CH < CH ? cnt - c * CH : CH;
+        const Meta mc{sm.vtok[c & 1], sm.vgate[c & 1], sm.vslot[c & 1]};
+        // ---- sub-block w (shared by all columns) and this wave's values, from
+        //      one batch of loads ----
         {
             const int Lw = L - 16 * w < 16 ? L - 16 * w : 16;
+            SubIn in;
+            ValIn vin;
+            if (Lw > 0) load_sub(in, a, rb, h, mc, 16 * w, Lw, lane);
+            load_values(vin, a, rb, h, mc, L, col, lane);
             int small = 0;
-            if (Lw > 0) small = stage_sub<false, io_t>(sm.sb[w], a, qg, kg, b, h, sm, 16 * w, Lw, lane);
+            if (Lw > 0) small = stage_sub<false>(sm.sb[w], in, mc, 16 * w, Lw, lane);
             if (lane == 0) sm.small[w] = small;
-            stage_values<io_t>(sm.vt[w], a, vg, b, h, sm, L, col, lane);
+            stage_values(sm.vt[w], vin, mc, L, lane);
+        }
+        if (w == 0 && c + 1 < nch) {
+            put_list(c + 1);
+            if (c + 2 < nch) fetch_list(c + 2);
         }
         block_sync_lds();
         if ((sm.small[0] | sm.small[1] | sm.small[2] | sm.small[3]) == 0) {
             for (int r = 0; r < NWV && 16 * r < L; ++r) {
                 const int Lr = L - 16 * r < 16 ? L - 16 * r : 16;
                 const f32x4_t ot = sub_products<true>(St, sm.sb[r], sm.vt[w], 16 * r, Lr, lane);
-                write_contrib<io_t>(a, sm, ot, b, h, 16 * r, Lr, col, lane);
+                write_contrib(a, mc, ot, b, h, 16 * r, Lr, col, lane);
             }
         } else {
             // a decay below 2^-4 in the chunk: blocks that end before the product
             // of decays falls below 2^-60, each wavefront staging its own
             for (int p0 = 0; p0 < L;) {
                 const int Lb = L - p0 < 16 ? L - p0 : 16;
-                const int Le = stage_sub<true, io_t>(sm.sb[w], a, qg, kg, b, h, sm, p0, Lb, lane);
+                SubIn in;
+                load_sub(in, a, rb, h, mc, p0, Lb, lane);
+                const int Le = stage_sub<true>(sm.sb[w], in, mc, p0, Lb, lane);
                 wave_sync();
                 const f32x4_t ot = sub_products<false>(St, sm.sb[w], sm.vt[w], p0, Le, lane);
-                write_contrib<io_t>(a, sm, ot, b, h, p0, Le, col, lane);
+                write_contrib(a, mc, ot, b, h, p0, Le, col, lane);
                 wave_sync();
                 p0 += Le;
             }
         }
         block_sync_lds();
     }
+    // the store addresses are formed here, not kept from the loads through the
+    // chunk loop (the compiler otherwise holds all 32 of them in registers)
+    float* Sout = Sg;
+    uint32_t sout = soff;
+    asm volatile("" : "+s"(Sout), "+v"(sout));
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Sg[(size_t)(16 * m + 4 * g4 + j) * dv + col + l16] = St[m][j];
+        for (int j = 0; j < 4; ++j) (Sout + (size_t)(16 * m + j) * dv)[sout] = St[m][j];
 }
 
 // o_t = its topk routed contributions in rank order, then the shared one
@@ -561,7 +664,7 @@ __global__ __launch_bounds__(256) void sse_combine_kernel(const bf16_t* __restri
 
 size_t sse_scratch_bytes(int B, int T, int H, int N, int topk, int dv) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    return al((size_t)B * H * N * T * 4) + al((size_t)B * H * N * 4) +
+    return 2 * al((size_t)B * H * N * T * 4) + al((size_t)B * H * N * 4) +
            al((size_t)B * T * H * (topk + 1) * dv * 2);
 }
 
@@ -570,19 +673,24 @@ hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
                       const float* lam, const void* q_sh, const void* k_sh, float* S, void* o,
                       int32_t* sel, float* e_sel, void* scratch, hipStream_t st, int masking) {
     if (dtype != 1 || N > MAXN || topk > MAXK || dv % DB != 0) return hipErrorInvalidValue;
+    // row offsets inside a batch are 32-bit (fp32 Lambda rows: T*H*c*4 bytes)
+    if ((long long)T * H * CR * 4 >= (1ll << 31) || (long long)T * H * dv * 2 >= (1ll << 31))
+        return hipErrorInvalidValue;
     if (T == 0) return hipSuccess;
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     char* ws = static_cast<char*>(scratch);
+    const size_t lb = al((size_t)B * H * N * T * 4);
     uint32_t* vis = reinterpret_cast<uint32_t*>(ws);
-    int* cnt = reinterpret_cast<int*>(ws + al((size_t)B * H * N * T * 4));
-    bf16_t* opart = reinterpret_cast<bf16_t*>(ws + al((size_t)B * H * N * T * 4) + al((size_t)B * H * N * 4));
+    float* vgl = reinterpret_cast<float*>(ws + lb);
+    int* cnt = reinterpret_cast<int*>(ws + 2 * lb);
+    bf16_t* opart = reinterpret_cast<bf16_t*>(ws + 2 * lb + al((size_t)B * H * N * 4));
     SseArgs a{B, T, H, N, topk, dv, logits, q, k, v, lam, q_sh, k_sh, S, o, sel, e_sel, masking,
-              vis, cnt, opart};
+              vis, vgl, cnt, opart};
     const int P = B * T * H;
     sse_route_kernel<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(logits, P, N, topk, sel, e_sel);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    sse_bucket_kernel<<<(unsigned)(B * H), 256, 0, st>>>(a);
+    sse_bucket_kernel<<<(unsigned)(B * H), 64 * BKW, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 8 * ncb consecutive workgroups hold 8 partition sequences, one per XCD
     const long long nseq = (long long)B * H * (N + 1);
