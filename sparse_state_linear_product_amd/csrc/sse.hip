@@ -309,6 +309,89 @@ SSLP_DEVICE void load_values(ValIn& in, const SseArgs& a, const RowBases& rb, in
     }
 }
 
+// The chunk-start form of load_sub and stage_sub<false> (p0 a multiple of
+// 16): the visit list is read with vector reads, row offsets are one 24-bit
+// multiply, and every per-visit decision is a select (visits past L load the
+// first visit's rows and stage zeros; a masked visit decays by 1).  Frozen
+// visits exist only in the masking execution (may_freeze).
+SSLP_DEVICE void load_sub16(SubIn& in, const SseArgs& a, const RowBases& rb, int h, const Meta& mt,
+                            int p0, int L, int lane) {
+    int tk[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int4 t4 = *reinterpret_cast<const int4*>(&mt.tok[p0 + 4 * q]);
+        tk[4 * q] = t4.x;
+        tk[4 * q + 1] = t4.y;
+        tk[4 * q + 2] = t4.z;
+        tk[4 * q + 3] = t4.w;
+    }
+    const uint32_t stride = (uint32_t)a.H * (CR * 2);  // bytes between tokens of a bf16 row array
+    const uint32_t base = (uint32_t)h * (CR * 2) + 4u * lane;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const int tp = p < L ? tk[p] : tk[0];
+        const uint32_t off = __umul24((uint32_t)tp, stride) + base;
+        in.lam[p] = *reinterpret_cast<const float2*>(rb.lam + 2u * off);
+        in.qw[p] = *reinterpret_cast<const uint32_t*>(rb.q + off);
+        in.kw[p] = *reinterpret_cast<const uint32_t*>(rb.k + off);
+    }
+}
+
+SSLP_DEVICE int stage_sub16(SubBlock& sb, const SubIn& in, const Meta& mt, int p0, int L, int lane,
+                            bool may_freeze) {
+    uint32_t frozen = 0;  // bit p: visit p does not select the partition (masking)
+    if (may_freeze) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int4 s4 = *reinterpret_cast<const int4*>(&mt.slot[p0 + 4 * q]);
+            frozen |= ((s4.x < 0 ? 1u : 0u) | (s4.y < 0 ? 2u : 0u) | (s4.z < 0 ? 4u : 0u) |
+                       (s4.w < 0 ? 8u : 0u)) << (4 * q);
+        }
+    }
+    float ep0 = 1.f, ep1 = 1.f, em0 = 1.f, em1 = 1.f, af0 = 1.f, af1 = 1.f;
+    bool small = false;
+    uint32_t kt0[8], kt1[8];  // rows 2l, 2l+1: bf16 pairs of visits (2u, 2u+1)
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const bool valid = p < L;
+        const bool live = valid && ((frozen >> p) & 1u) == 0u;
+        const float l0 = live ? in.lam[p].x : 1.f, l1 = live ? in.lam[p].y : 1.f;
+        small |= l0 < kSmallDecay || l1 < kSmallDecay;
+        if (p == 0) {
+            af0 = l0;
+            af1 = l1;
+        } else {
+            ep0 *= l0;
+            ep1 *= l1;
+            // hardware reciprocal (within 1 ulp, not an IEEE division): the
+            // factor only scales a key that is rounded to bf16
+            em0 *= __builtin_amdgcn_rcpf(l0);
+            em1 *= __builtin_amdgcn_rcpf(l1);
+        }
+        const uint32_t qw = valid ? in.qw[p] : 0u, kw = valid ? in.kw[p] : 0u;
+        const float q0 = __uint_as_float(qw << 16), q1 = __uint_as_float(qw & 0xFFFF0000u);
+        const float k0 = __uint_as_float(kw << 16), k1 = __uint_as_float(kw & 0xFFFF0000u);
+        const uint32_t kb0 = f32_to_bf16(k0 * em0).bits, kb1 = f32_to_bf16(k1 * em1).bits;
+        *reinterpret_cast<uint32_t*>(&sb.qs[p][2 * lane]) =
+            (uint32_t)f32_to_bf16(q0 * ep0).bits | ((uint32_t)f32_to_bf16(q1 * ep1).bits << 16);
+        *reinterpret_cast<uint32_t*>(&sb.ks[p][2 * lane]) = kb0 | (kb1 << 16);
+        if (p & 1) {
+            kt0[p >> 1] |= kb0 << 16;
+            kt1[p >> 1] |= kb1 << 16;
+        } else {
+            kt0[p >> 1] = kb0;
+            kt1[p >> 1] = kb1;
+        }
+    }
+    *reinterpret_cast<uint4*>(&sb.kt[2 * lane][0]) = make_uint4(kt0[0], kt0[1], kt0[2], kt0[3]);
+    *reinterpret_cast<uint4*>(&sb.kt[2 * lane][8]) = make_uint4(kt0[4], kt0[5], kt0[6], kt0[7]);
+    *reinterpret_cast<uint4*>(&sb.kt[2 * lane + 1][0]) = make_uint4(kt1[0], kt1[1], kt1[2], kt1[3]);
+    *reinterpret_cast<uint4*>(&sb.kt[2 * lane + 1][8]) = make_uint4(kt1[4], kt1[5], kt1[6], kt1[7]);
+    *reinterpret_cast<float2*>(&sb.af[2 * lane]) = make_float2(af0, af1);
+    *reinterpret_cast<float2*>(&sb.px[2 * lane]) = make_float2(ep0, ep1);
+    return __ballot(small) != 0ull ? 1 : 0;
+}
+
 // Stages visits p0 .. p0+L-1 (L <= 16) of the chunk as one sub-block (lane l
 // owns state rows 2l, 2l+1).  CUT = false: all L visits; returns whether a
 // decay below 2^-4 was met.  CUT = true: ends the block before the visit that
@@ -546,6 +629,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void sse_gla_kernel(SseArgs a) {
     // next chunk's list in registers (requested a chunk ahead) and writes it
     // out while the current chunk is staged.
     const int nch = (cnt + CH - 1) / CH;
+    const bool may_freeze = a.masking && !shared;
     uint32_t nx_ent = 0;  // wavefront 0, lane p: visit p of the chunk to come
     float nx_gate = 0.f;
     auto fetch_list = [&](int c) {
@@ -590,10 +674,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void sse_gla_kernel(SseArgs a) {
             const int Lw = L - 16 * w < 16 ? L - 16 * w : 16;
             SubIn in;
             ValIn vin;
-            if (Lw > 0) load_sub(in, a, rb, h, mc, 16 * w, Lw, lane);
+            if (Lw > 0) load_sub16(in, a, rb, h, mc, 16 * w, Lw, lane);
             load_values(vin, a, rb, h, mc, L, col, lane);
             int small = 0;
-            if (Lw > 0) small = stage_sub<false>(sm.sb[w], in, mc, 16 * w, Lw, lane);
+            if (Lw > 0) small = stage_sub16(sm.sb[w], in, mc, 16 * w, Lw, lane, may_freeze);
             if (lane == 0) sm.small[w] = small;
             stage_values(sm.vt[w], vin, mc, L, lane);
         }
