@@ -96,7 +96,14 @@ struct Meta {
 };
 static_assert(sizeof(GlaSmem) <= 80 * 1024, "two workgroups per compute unit");
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 SSLP_DEVICE short bfs(float f) { return (short)f32_to_bf16(f).bits; }
+// two fp32 values rounded to bf16 in one instruction: lo in bits 0-15
+SSLP_DEVICE uint32_t pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
 SSLP_DEVICE __bf16 bfv(float f) { return __builtin_bit_cast(__bf16, f32_to_bf16(f).bits); }
 
 struct SseArgs {
@@ -371,16 +378,16 @@ SSLP_DEVICE int stage_sub16(SubBlock& sb, const SubIn& in, const Meta& mt, int p
         const uint32_t qw = valid ? in.qw[p] : 0u, kw = valid ? in.kw[p] : 0u;
         const float q0 = __uint_as_float(qw << 16), q1 = __uint_as_float(qw & 0xFFFF0000u);
         const float k0 = __uint_as_float(kw << 16), k1 = __uint_as_float(kw & 0xFFFF0000u);
-        const uint32_t kb0 = f32_to_bf16(k0 * em0).bits, kb1 = f32_to_bf16(k1 * em1).bits;
-        *reinterpret_cast<uint32_t*>(&sb.qs[p][2 * lane]) =
-            (uint32_t)f32_to_bf16(q0 * ep0).bits | ((uint32_t)f32_to_bf16(q1 * ep1).bits << 16);
-        *reinterpret_cast<uint32_t*>(&sb.ks[p][2 * lane]) = kb0 | (kb1 << 16);
+        const uint32_t kp = pk_bf16(k0 * em0, k1 * em1);  // rows 2l (lo), 2l+1 (hi)
+        *reinterpret_cast<uint32_t*>(&sb.qs[p][2 * lane]) = pk_bf16(q0 * ep0, q1 * ep1);
+        *reinterpret_cast<uint32_t*>(&sb.ks[p][2 * lane]) = kp;
         if (p & 1) {
-            kt0[p >> 1] |= kb0 << 16;
-            kt1[p >> 1] |= kb1 << 16;
+            // visits p-1 (lo) and p of row 2l, of row 2l+1: byte selects of the two pairs
+            kt0[p >> 1] = __builtin_amdgcn_perm(kp, kt0[p >> 1], 0x05040100u);
+            kt1[p >> 1] = __builtin_amdgcn_perm(kp, kt1[p >> 1], 0x07060302u);
         } else {
-            kt0[p >> 1] = kb0;
-            kt1[p >> 1] = kb1;
+            kt0[p >> 1] = kp;  // completed by the next visit
+            kt1[p >> 1] = kp;
         }
     }
     *reinterpret_cast<uint4*>(&sb.kt[2 * lane][0]) = make_uint4(kt0[0], kt0[1], kt0[2], kt0[3]);
