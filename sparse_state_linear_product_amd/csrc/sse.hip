@@ -16,7 +16,8 @@
 //
 // Four launches:
 //  * sse_route_kernel: every token on its own thread (fp32 softmax and top-k,
-//    ties to the lowest index) into sel / e_sel.
+//    ties to the lowest index) into sel / e_sel, and a (batch, head)-major
+//    copy (ranks packed in 4 bits each, gates) for the bucket kernel.
 //  * sse_bucket_kernel: one workgroup per (batch, head) lists every routed
 //    partition's visits in time order (token << 3 | rank), with its count --
 //    the grouped sequences of the varlen layout.  The masking execution lists
@@ -122,6 +123,8 @@ struct SseArgs {
     int masking;      // 1: every routed partition runs over every token (masked execution)
     uint32_t* vis;    // [B*H][N][T] visits, token << 3 | rank
     float* vgl;       // [B*H][N][T] their gates (0 for a masked visit)
+    uint32_t* rsel;   // [B*H][T] the routing, (b, h)-major: 4 bits per rank
+    float4* rgate;    // [B*H][T] the selected gates by rank
     int* cnt;         // [B*H][N] visits per routed partition
     bf16_t* opart;    // [B*T*H][topk + 1][dv] contributions by slot
 };
@@ -129,9 +132,13 @@ struct SseArgs {
 // Routing of every token (one thread per (b, t, h)): e = softmax(logits) over
 // the N partitions in fp32, top-k by logit with ties to the lowest index
 // (the selected gate values are not renormalised).
+// Besides sel / e_sel ([B,T,H,k]) it writes a (b, h)-major copy for the
+// bucket kernel, whose reads of a head's tokens are then contiguous.
 __global__ __launch_bounds__(256) void sse_route_kernel(const float* __restrict__ logits, int P,
                                                         int N, int topk, int32_t* __restrict__ sel,
-                                                        float* __restrict__ esel) {
+                                                        float* __restrict__ esel, int T, int H,
+                                                        uint32_t* __restrict__ rsel,
+                                                        float4* __restrict__ rgate) {
     const int p = blockIdx.x * 256 + threadIdx.x;
     if (p >= P) return;
     const float* lg = logits + (size_t)p * N;
@@ -147,15 +154,26 @@ __global__ __launch_bounds__(256) void sse_route_kernel(const float* __restrict_
     for (int i = 0; i < MAXN; ++i)
         if (i < N) z += __expf(lv[i] - mx);
     unsigned taken = 0;
-    for (int r = 0; r < topk; ++r) {
+    uint32_t packed = 0;
+    float g4[MAXK] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < MAXK; ++r) {
+        if (r >= topk) break;
         int best = -1;
 #pragma unroll
         for (int i = 0; i < MAXN; ++i)
             if (i < N && !((taken >> i) & 1u) && (best < 0 || lv[i] > lv[best])) best = i;
         taken |= 1u << best;
+        const float g = __expf(lv[best] - mx) / z;
         sel[(size_t)p * topk + r] = best;
-        esel[(size_t)p * topk + r] = __expf(lv[best] - mx) / z;
+        esel[(size_t)p * topk + r] = g;
+        packed |= (uint32_t)best << (4 * r);
+        g4[r] = g;
     }
+    const int h = p % H, t = (p / H) % T, b = p / (H * T);
+    const size_t q = ((size_t)b * H + h) * T + t;
+    rsel[q] = packed;
+    rgate[q] = make_float4(g4[0], g4[1], g4[2], g4[3]);
 }
 
 // Visit lists of every routed partition of one (batch, head), in time order.
@@ -175,14 +193,12 @@ __global__ __launch_bounds__(64 * BKW) void sse_bucket_kernel(SseArgs a) {
     float* vgl = a.vgl + (size_t)bh * N * T;
     if (a.masking) {
         for (int t = threadIdx.x; t < T; t += 64 * BKW) {
-            const size_t bth = ((size_t)b * T + t) * a.H + h;
+            const uint32_t pk = a.rsel[(size_t)bh * T + t];
+            const float4 g4 = a.rgate[(size_t)bh * T + t];
             int sl[MAXK];
-            float ge[MAXK];
+            const float ge[MAXK] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-            for (int r = 0; r < MAXK; ++r) {
-                sl[r] = r < topk ? a.sel[bth * topk + r] : -1;
-                ge[r] = r < topk ? a.e_sel[bth * topk + r] : 0.f;
-            }
+            for (int r = 0; r < MAXK; ++r) sl[r] = r < topk ? (int)((pk >> (4 * r)) & 15u) : -1;
             for (int i = 0; i < N; ++i) {
                 uint32_t rk = kNoRank;
                 float g = 0.f;
@@ -211,18 +227,20 @@ __global__ __launch_bounds__(64 * BKW) void sse_bucket_kernel(SseArgs a) {
 #pragma unroll
             for (int s = 0; s < BKI; ++s) {
                 const int t = t0 + 64 * s + lane;
-                const size_t bth = ((size_t)b * T + (t < t_end ? t : 0)) * a.H + h;
+                const uint32_t pk = a.rsel[(size_t)bh * T + (t < t_end ? t : 0)];
 #pragma unroll
-                for (int r = 0; r < MAXK; ++r) sl[s][r] = r < topk ? a.sel[bth * topk + r] : -1;
+                for (int r = 0; r < MAXK; ++r) sl[s][r] = r < topk ? (int)((pk >> (4 * r)) & 15u) : -1;
             }
             float ge[BKI][MAXK];  // the gates, needed by the placing pass only
             if (pass == 1) {
 #pragma unroll
                 for (int s = 0; s < BKI; ++s) {
                     const int t = t0 + 64 * s + lane;
-                    const size_t bth = ((size_t)b * T + (t < t_end ? t : 0)) * a.H + h;
-#pragma unroll
-                    for (int r = 0; r < MAXK; ++r) ge[s][r] = r < topk ? a.e_sel[bth * topk + r] : 0.f;
+                    const float4 g4 = a.rgate[(size_t)bh * T + (t < t_end ? t : 0)];
+                    ge[s][0] = g4.x;
+                    ge[s][1] = g4.y;
+                    ge[s][2] = g4.z;
+                    ge[s][3] = g4.w;
                 }
             }
 #pragma unroll
@@ -756,7 +774,8 @@ __global__ __launch_bounds__(256) void sse_combine_kernel(const bf16_t* __restri
 size_t sse_scratch_bytes(int B, int T, int H, int N, int topk, int dv) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return 2 * al((size_t)B * H * N * T * 4) + al((size_t)B * H * N * 4) +
-           al((size_t)B * T * H * (topk + 1) * dv * 2);
+           al((size_t)B * T * H * (topk + 1) * dv * 2) + al((size_t)B * H * T * 4) +
+           al((size_t)B * H * T * 16);
 }
 
 hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
@@ -774,11 +793,16 @@ hipError_t launch_sse(int B, int T, int H, int N, int topk, int dv, int dtype,
     uint32_t* vis = reinterpret_cast<uint32_t*>(ws);
     float* vgl = reinterpret_cast<float*>(ws + lb);
     int* cnt = reinterpret_cast<int*>(ws + 2 * lb);
-    bf16_t* opart = reinterpret_cast<bf16_t*>(ws + 2 * lb + al((size_t)B * H * N * 4));
+    const size_t lo = 2 * lb + al((size_t)B * H * N * 4);
+    bf16_t* opart = reinterpret_cast<bf16_t*>(ws + lo);
+    const size_t lr = lo + al((size_t)B * T * H * (topk + 1) * dv * 2);
+    uint32_t* rsel = reinterpret_cast<uint32_t*>(ws + lr);
+    float4* rgate = reinterpret_cast<float4*>(ws + lr + al((size_t)B * H * T * 4));
     SseArgs a{B, T, H, N, topk, dv, logits, q, k, v, lam, q_sh, k_sh, S, o, sel, e_sel, masking,
-              vis, vgl, cnt, opart};
+              vis, vgl, rsel, rgate, cnt, opart};
     const int P = B * T * H;
-    sse_route_kernel<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(logits, P, N, topk, sel, e_sel);
+    sse_route_kernel<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(logits, P, N, topk, sel, e_sel, T,
+                                                                   H, rsel, rgate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     sse_bucket_kernel<<<(unsigned)(B * H), 64 * BKW, 0, st>>>(a);
