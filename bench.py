@@ -299,6 +299,24 @@ def bench_rows(args, torch, sslp, wl):
                           bytes_per_step=nbytes, steps=args.decode_steps)
     del M
     torch.cuda.empty_cache()
+    # the 1.4B prefill layer at batch 8 (1,920 column slices: the chunk-parallel
+    # path runs them in rounds) and at the pages' W = R = 64 budget (per-token
+    # path), each as one sdm_forward call (addressing + update)
+    for tag, c2 in (("B8", dataclasses.replace(wl.SDM_14B, B=8)),
+                    ("W64_k64", dataclasses.replace(wl.SDM_14B, k_w=64, k_r=64, W=64, R=64))):
+        x = {k: v.to(dev) for k, v in wl.sdm_inputs(c2).items()}
+        M = torch.zeros((c2.B, c2.H, c2.N, c2.d_v), dtype=torch.float32, device=dev)
+        y = torch.empty_like(x["v"])
+        ms = time_call(torch, lambda: sslp.sdm_forward(x["sw1"], x["sw2"], x["sr1"], x["sr2"], x["v"],
+                                                       x["alpha"], x["beta"], M, c2.k_w, c2.k_r,
+                                                       c2.W, c2.R, y=y), 2, warmup=1)
+        nbytes, _ = sdm_kernel_bytes(c2, 2)
+        rows[f"sdm_prefill_1p4b_{tag}_T8192_H2_N57600_dv960"] = dict(
+            ms=round(ms, 4), tokens_per_s=round(c2.B * c2.T / (ms * 1e-3), 1),
+            gbs_forward=round(nbytes / (ms * 1e-3) / 1e9, 1),
+            path="chunk-parallel" if c2.W == 32 else "per-token")
+        del x, M, y
+        torch.cuda.empty_cache()
     # read epilogue (RMS-Norm + SiLU output gate) on the 1.4B prefill read y [1,8192,2,960] bf16
     cfg = wl.SDM_14B
     gen = torch.Generator(device=dev).manual_seed(cfg.seed + 9)
