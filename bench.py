@@ -300,8 +300,8 @@ def bench_rows(args, torch, sslp, wl):
     del M
     torch.cuda.empty_cache()
     # the 1.4B prefill layer at batch 8 (1,920 column slices: the chunk-parallel
-    # path runs them in rounds) and at the pages' W = R = 64 budget (per-token
-    # path), each as one sdm_forward call (addressing + update)
+    # path runs them in rounds) and at the pages' W = R = 64 budget (chunks of 8
+    # tokens), each as one sdm_forward call (addressing + update)
     for tag, c2 in (("B8", dataclasses.replace(wl.SDM_14B, B=8)),
                     ("W64_k64", dataclasses.replace(wl.SDM_14B, k_w=64, k_r=64, W=64, R=64))):
         x = {k: v.to(dev) for k, v in wl.sdm_inputs(c2).items()}
@@ -314,7 +314,7 @@ def bench_rows(args, torch, sslp, wl):
         rows[f"sdm_prefill_1p4b_{tag}_T8192_H2_N57600_dv960"] = dict(
             ms=round(ms, 4), tokens_per_s=round(c2.B * c2.T / (ms * 1e-3), 1),
             gbs_forward=round(nbytes / (ms * 1e-3) / 1e9, 1),
-            path="chunk-parallel" if c2.W == 32 else "per-token")
+            path=f"chunk-parallel, {16 if c2.W == 32 else 8}-token chunks")
         del x, M, y
         torch.cuda.empty_cache()
     # read epilogue (RMS-Norm + SiLU output gate) on the 1.4B prefill read y [1,8192,2,960] bf16

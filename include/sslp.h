@@ -176,8 +176,11 @@ int sdm_address(const sslp_sdm_shape* shape, int dtype, const void* s1, const vo
  *   v, alpha, beta, M, y as in sdm_forward;  shape->k_w, k_r are ignored and
  *   W, R may be up to 128 regardless of k.
  *   workspace, ws_bytes >= sdm_workspace_size(shape).
- * Indices outside [0,N) are rejected only if detected on the host, which is
- * never: the caller must guarantee the range.
+ * Indices are not range-checked on the host; one outside [0,N) is contained
+ * on the device and reported by sslp_device_error.  Execution: with T >= 64
+ * and W = R = 32 or W = R = 64 the recurrence runs chunk-parallel (chunks of
+ * 16 or 8 tokens; its plans take the workspace after the addressing), other
+ * shapes one token at a time.
  */
 int sdm_sparse_update(const sslp_sdm_shape* shape, int dtype, int residual_mode,
                       const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
@@ -434,8 +437,8 @@ const char* sslp_last_error(void);
  * since the last query on this device: 1 if so, 0 if not, or a negative
  * status.  Such a call leaves its results undefined but touches no memory
  * outside the given tensors: a token's out-of-range slot is replaced by slot
- * 0 (per-token kernels), and a 16-token chunk holding one is skipped (y = 0,
- * the table unchanged; chunk-parallel kernel).  The query synchronises
+ * 0 (per-token kernels), and a chunk (16 or 8 tokens) holding one is skipped
+ * (y = 0, the table unchanged; chunk-parallel kernel).  The query synchronises
  * `stream` and clears the flag; it is the only entry point that synchronises.
  */
 int sslp_device_error(void* stream);

@@ -120,7 +120,7 @@ long long slots(const sslp_sdm_shape* s) { return (long long)s->sqrtN * s->sqrtN
 // bytes the recurrence itself needs (the chunk plans of the chunk-parallel kernel)
 size_t recurrence_bytes(const sslp_sdm_shape* s, int T) {
     if (!sslp::sdm_chunked_supported(s->B, T, s->H, s->W, s->R, s->d_v, slots(s))) return 0;
-    return align_up(sslp::sdm_chunk_plan_bytes(s->B, T, s->H));
+    return align_up(sslp::sdm_chunk_plan_bytes(s->B, T, s->H, s->W));
 }
 
 hipError_t run_recurrence(const sslp::SdmUpdateArgs& a, const sslp_sdm_shape* s, void* plan,

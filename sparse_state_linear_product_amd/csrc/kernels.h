@@ -99,7 +99,7 @@ hipError_t launch_sdm_address_backward(int P, int sqrtN, int budget, const int32
 // chunk-parallel recurrence (sdm_chunk.hip): supported shapes, workspace for
 // its per-chunk plans, and the launcher (plan kernel + apply kernel)
 bool sdm_chunked_supported(int B, int T, int H, int W, int R, int dv, long long N);
-size_t sdm_chunk_plan_bytes(int B, int T, int H);
+size_t sdm_chunk_plan_bytes(int B, int T, int H, int W);
 hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* plan, hipStream_t st);
 
 // RMS-Norm and output gate after the read (norm_gate.hip): rows x d, act 0 none,

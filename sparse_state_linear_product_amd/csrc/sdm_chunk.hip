@@ -1,11 +1,12 @@
 // K2 (chunk-parallel): the Sparse Delta Memory recurrence given the addressing,
-// computed 16 tokens at a time.
+// computed a chunk of tokens at a time (16 tokens with 32 write and 32 read
+// rows each, or 8 tokens with 64 and 64).
 //
 // Same operation as the per-token kernel in sdm_update.hip (slides "Sparse
 // Delta Memory: Scaling the State of Linear RNNs through Sparsity", Eqs.
 // (3)-(5), with the shared-prediction figure form or the per-slot form of the
-// residual); here the token recurrence is unrolled over a chunk of C = 16
-// tokens so that no per-token dependency chain remains.
+// residual); here the token recurrence is unrolled over a chunk of C tokens
+// so that no per-token dependency chain remains.
 //
 // Within a chunk every quantity is linear in the chunk-start table M0 and the
 // residuals.  For a slot s, let its write visits in the chunk be tokens
@@ -23,8 +24,8 @@
 // A plan kernel derives, per (b, h, chunk), everything that does not depend on
 // the table (row offsets, c, e, T = (I + A)^-1, Bm, per-slot final
 // coefficients, and which rows of the NEXT chunk hold a slot this chunk
-// writes); the apply kernel then streams the table: one wavefront per 8-column
-// slice of a head gathers the chunk's 16 x 64 rows with LDS-DMA
+// writes); the apply kernel then streams the table: one workgroup per 8-column
+// slice of a head gathers the chunk's C x (W + R) = 1024 rows with LDS-DMA
 // (global_load_lds_dwordx4), forms g, h, res = T (v - g), y = h + Bm res,
 // and writes every written slot once with its final value.
 //
@@ -34,6 +35,7 @@
 // DMA has landed.  Rows written by earlier chunks were stored before the DMA
 // was issued, by the same wavefront, whose vector memory operations are
 // performed in order.
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -43,45 +45,64 @@ namespace sslp {
 
 namespace {
 
-constexpr int CC = 16;        // tokens per chunk
-constexpr int CW = 8;         // columns per wavefront
-constexpr int NW = 32;        // write rows per token
-constexpr int NR = 32;        // read rows per token
-constexpr int NQ = NW + NR;   // rows per token
-constexpr int NE = CC * NW;   // write entries per chunk
+constexpr int CW = 8;                // columns per apply workgroup (one 32-byte row piece)
+constexpr int NWAVE = 8;             // wavefronts per apply workgroup
+constexpr int NE = 512;              // write entries per chunk (C x W)
+constexpr int JW = 32 / NWAVE;       // row DMAs per wavefront and chunk (32 per chunk)
 
-// plan block of one (b, h, chunk), 32-bit words.  Rows are padded so that the
-// apply kernel's LDS reads of them are free of bank conflicts.  The fixed part
-// and the first PL_TAILWIN words of the tail are staged in LDS; tail words past
-// that (only with heavy slot reuse) are read from memory.
-constexpr int OFFS_LD = 36, COEF_LD = 68, TB_LD = 20;
-constexpr int PL_OFFS = 0;                          // row byte offsets (see offs_word)
-constexpr int PL_COEF = PL_OFFS + 32 * OFFS_LD;     // [t][q] (ld 68): c (q < 32) or e (q >= 32)
-constexpr int PL_TM = PL_COEF + CC * COEF_LD;       // [t][tau] (ld 20): (I + A)^-1
-constexpr int PL_BM = PL_TM + CC * TB_LD;           // [t][tau] (ld 20)
-constexpr int PL_FIN = PL_BM + CC * TB_LD;          // [i][t][2]: P, f of write entry (t, i)
-constexpr int PL_LAST = PL_FIN + NE * 2;            // [t] bit i: entry (t, i) is its slot's last visit
-constexpr int PL_EXC = PL_LAST + CC;                // [t] bit i: entry (t, i) has an exception record
-constexpr int PL_EXCB = PL_EXC + CC;                // [t] index of token t's first exception record
-constexpr int PL_HDR = PL_EXCB + CC;                // tail offsets of the extra pairs and forward rows
-constexpr int PL_TAIL = 4096;                       // exception records, extra pairs, forward rows
+// plan block of one (b, h, chunk), 32-bit words: a fixed part (layout below),
+// then a tail of exception records, extra pairs and forward rows.  The fixed
+// part and the first PL_TAILWIN words of the tail are staged in LDS; tail words
+// past that (only with heavy slot reuse) are read from memory.
+constexpr int PL_TAIL = 4096;
 constexpr int PL_TAILWIN = 2048;
 constexpr int PL_DMA_WORDS = PL_TAIL + PL_TAILWIN;  // 24 KB staged per chunk
 constexpr int PL_WORDS = PL_TAIL + 2 * NE + 2 * NE + 2 * NE;  // worst-case tail
-static_assert(PL_HDR + 4 <= PL_TAIL, "plan layout");
 static_assert((PL_DMA_WORDS * 4) % 1024 == 0 && (PL_WORDS * 4) % 16 == 0, "plan DMA pieces");
 // exception record: (first, packed); packed = extra index (9 bits) | extra count << 9
 // (5 bits) | forward index << 14 (10 bits) | forward count << 24 (6 bits)
 
-constexpr int NWAVE = 8;             // wavefronts per apply workgroup
-constexpr int JW = 32 / NWAVE;       // row DMAs per wavefront and chunk
-// row (q, t) is staged by DMA j = q/2 of wave j % NWAVE; a lane's JW offsets for
-// its wave are contiguous
-SSLP_DEVICE int offs_word(int q, int t) {
-    const int j = q >> 1;
-    return PL_OFFS + ((q & 1) * 16 + t) * OFFS_LD + (j % NWAVE) * JW + j / NWAVE;
-}
-SSLP_DEVICE int coef_word(int t, int q) { return PL_COEF + t * COEF_LD + q; }
+// Chunk geometry: CC_ tokens per chunk, NW_ write rows and as many read rows
+// per token.  Both configurations (16 x 32 and 8 x 64) have 512 write entries
+// and 1024 staged rows per chunk, so the LDS budgets, the plan's size and the
+// DMA pattern (32 DMAs of 32 rows of 32 bytes) are shared; only the index maps
+// differ.  Rows of the fixed plan part are padded so that the apply kernel's
+// LDS reads of them are free of bank conflicts.
+template <int CC_, int NW_>
+struct Geo {
+    static constexpr int CC = CC_;         // tokens per chunk
+    static constexpr int NW = NW_;         // write rows per token
+    static constexpr int NR = NW_;         // read rows per token
+    static constexpr int NQ = NW + NR;     // rows per token
+    static constexpr int LOGNW = NW == 32 ? 5 : 6;
+    static constexpr int RPD = 32 / CC;    // row indices q per DMA
+    static constexpr int NMW = NW / 32;    // mask words per token
+    static constexpr int OFFS_LD = 36, COEF_LD = NQ + 4, TB_LD = CC + 4;
+    static constexpr int PL_OFFS = 0;                          // row byte offsets (see offs_word)
+    static constexpr int PL_COEF = PL_OFFS + 32 * OFFS_LD;     // [t][q]: c (q < NW) or e (q >= NW)
+    static constexpr int PL_TM = PL_COEF + CC * COEF_LD;       // [t][tau]: (I + A)^-1
+    static constexpr int PL_BM = PL_TM + CC * TB_LD;           // [t][tau]
+    static constexpr int PL_FIN = PL_BM + CC * TB_LD;          // [i][t][2]: P, f of write entry (t, i)
+    static constexpr int PL_LAST = PL_FIN + NE * 2;            // [t][NMW] bit i: entry (t, i) is its slot's last visit
+    static constexpr int PL_EXC = PL_LAST + CC * NMW;          // [t][NMW] bit i: entry (t, i) has an exception record
+    static constexpr int PL_EXCB = PL_EXC + CC * NMW;          // [t] index of token t's first exception record
+    static constexpr int PL_HDR = PL_EXCB + CC;                // tail offsets of the extra pairs and forward rows
+    static_assert(CC * NW == NE && CC * NQ == 2 * NE && 32 % CC == 0 && NW % 32 == 0, "chunk geometry");
+    static_assert(PL_HDR + 4 <= PL_TAIL, "plan layout");
+    static_assert(PL_COEF % 4 == 0 && COEF_LD % 4 == 0 && PL_TM % 4 == 0 && PL_BM % 4 == 0 &&
+                      TB_LD % 4 == 0 && PL_FIN % 2 == 0 && PL_LAST % 2 == 0 && PL_HDR % 4 == 0,
+                  "aligned vector reads of the plan");
+    // row (q, t) is staged by DMA j = q / RPD of wave j % NWAVE, as row
+    // (q % RPD) C + t of that DMA's 32; a lane's JW offsets for its wave are
+    // contiguous
+    static SSLP_DEVICE int offs_word(int q, int t) {
+        const int j = q / RPD;
+        return PL_OFFS + ((q % RPD) * CC + t) * OFFS_LD + (j % NWAVE) * JW + j / NWAVE;
+    }
+    static SSLP_DEVICE int coef_word(int t, int q) { return PL_COEF + t * COEF_LD + q; }
+};
+using GeoW32 = Geo<16, 32>;
+using GeoW64 = Geo<8, 64>;
 
 struct PlanArgs {
     int B, T, H, N, dv, nch, mode;
@@ -98,11 +119,15 @@ struct PlanArgs {
 // ---------------------------------------------------------------------------
 // plan kernel: one workgroup of 256 threads per (b, h, chunk)
 // ---------------------------------------------------------------------------
+template <class G>
 __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
+    constexpr int CC = G::CC, NW = G::NW, NR = G::NR, NQ = G::NQ, LOGNW = G::LOGNW;
+    constexpr int PL_LAST = G::PL_LAST, PL_EXC = G::PL_EXC, PL_EXCB = G::PL_EXCB, PL_HDR = G::PL_HDR;
+    constexpr int PL_FIN = G::PL_FIN, PL_BM = G::PL_BM, PL_TM = G::PL_TM, TB_LD = G::TB_LD;
     __shared__ uint64_t key[NE];       // write entries sorted by (slot, token, rank)
     __shared__ float s_d[NE];          // decay of the visit at sorted position p
     __shared__ int s_gs[NE], s_ge[NE];  // slot group [gs, ge) of sorted position p
-    __shared__ int s_pos[NE];          // sorted position of write entry e = t*32 + i
+    __shared__ int s_pos[NE];          // sorted position of write entry e = t*NW + i
     __shared__ int s_scan[NE];         // group starts, then their inclusive prefix count
     __shared__ float s_ww[NE];         // write weights by entry
     __shared__ int s_ir[CC * NR];      // read slots by entry (-1: no token)
@@ -132,9 +157,9 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     {
         const int nt = a.T - t0 < CC ? a.T - t0 : CC;
         for (int e = tid; e < nt * NW; e += 256) {
-            const size_t bth = ((size_t)b * a.T + t0 + (e >> 5)) * a.H + h;
-            const unsigned sw = (unsigned)a.idx_w[bth * NW + (e & 31)];
-            const unsigned sr = (unsigned)a.idx_r[bth * NR + (e & 31)];
+            const size_t bth = ((size_t)b * a.T + t0 + (e >> LOGNW)) * a.H + h;
+            const unsigned sw = (unsigned)a.idx_w[bth * NW + (e & (NW - 1))];
+            const unsigned sr = (unsigned)a.idx_r[bth * NR + (e & (NW - 1))];
             if (sw >= (unsigned)a.N || sr >= (unsigned)a.N) s_bad = 1;
         }
     }
@@ -146,7 +171,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
 
     // S1: load the chunk's addressing
     for (int e = tid; e < NE; e += 256) {
-        const int t = e >> 5, i = e & 31;
+        const int t = e >> LOGNW, i = e & (NW - 1);
         if (t < ntok) {
             const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
             key[e] = ((uint64_t)(uint32_t)a.idx_w[bth * NW + i] << 9) | (uint64_t)e;
@@ -194,7 +219,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         const uint64_t kp = key[p];
         const bool valid = kp != NONE;
         const int e = (int)(kp & 511u);
-        const int t = e >> 5;
+        const int t = e >> LOGNW;
         int gs = p, ge = p + 1;
         if (valid) {
             const uint64_t sl = kp >> 9;
@@ -224,7 +249,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
 
     // S4: read entries: the write visits of their slot at or before their token
     for (int e = tid; e < CC * NR; e += 256) {
-        const int t = e >> 5;
+        const int t = e >> LOGNW;
         const int sl = s_ir[e];
         int rgs = 0, rend = 0;
         if (sl >= 0) {
@@ -240,7 +265,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
                 rgs = lo;
                 rend = lo;
                 const int ge = s_ge[lo];
-                while (rend < ge && (int)((key[rend] & 511u) >> 5) <= t) ++rend;
+                while (rend < ge && (int)((key[rend] & 511u) >> LOGNW) <= t) ++rend;
             }
         }
         s_rgs[e] = rgs;
@@ -253,8 +278,8 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     const int ntok1 = c + 1 < nch ? (a.T - t1 < CC ? a.T - t1 : CC) : 0;
     int fgrp[4];
     for (int x = 0; x < 4; ++x) {
-        const int ne = tid + 256 * x;  // 0..1023: q = ne / 16 ... as (t, q)
-        const int t = ne >> 6, q = ne & 63;
+        const int ne = tid + 256 * x;  // 0..1023 as (t, q)
+        const int t = ne / NQ, q = ne & (NQ - 1);
         fgrp[x] = -1;
         if (t < ntok1) {
             const size_t bth = ((size_t)b * a.T + t1 + t) * a.H + h;
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     for (int x = 0; x < 4; ++x) {
         if (fgrp[x] >= 0) {
             const int ne = tid + 256 * x;
-            const int t = ne >> 6, q = ne & 63;
+            const int t = ne / NQ, q = ne & (NQ - 1);
             const int g = fgrp[x];
             const int slot = atomicAdd(&s_ffill[g], 1);
             s_fwdl[s_fbeg[g] - s_fcnt[g] + slot] = q * CC + t;
@@ -297,14 +322,14 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
 
     // S6: per write entry: gather coefficient, final-value data at the last visit
     for (int e = tid; e < NE; e += 256) {
-        const int t = e >> 5, i = e & 31;
+        const int t = e >> LOGNW, i = e & (NW - 1);
         s_P[e] = 0.f;
         s_f[e] = 0.f;
         s_exc[e] = 0;
         s_first[e] = 0u;
         s_pk[e] = 0u;
         if (t >= ntok) {
-            out[coef_word(t, i)] = 0u;
+            out[G::coef_word(t, i)] = 0u;
             continue;
         }
         const int p = s_pos[e];
@@ -313,7 +338,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         for (int l = gs; l < p; ++l) pre *= s_d[l];
         for (int l = p + 1; l < ge; ++l) post *= s_d[l];
         const float w = s_ww[e];
-        out[coef_word(t, i)] = __float_as_uint(a.mode == 0 ? s_al[t] * w * pre : 0.f);
+        out[G::coef_word(t, i)] = __float_as_uint(a.mode == 0 ? s_al[t] * w * pre : 0.f);
         if (p != ge - 1) continue;  // the slot is written once, at its last visit
         s_P[e] = pre * s_d[p];
         s_f[e] = post * s_be[t] * w;
@@ -323,24 +348,26 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         for (int l = ge - 2; l >= gs; --l) {
             suf *= s_d[l + 1];
             const int el = (int)(key[l] & 511u);
-            s_xt[xstart + (l - gs)] = (uint32_t)(el >> 5);
-            s_xf[xstart + (l - gs)] = suf * s_be[el >> 5] * s_ww[el];
+            s_xt[xstart + (l - gs)] = (uint32_t)(el >> LOGNW);
+            s_xf[xstart + (l - gs)] = suf * s_be[el >> LOGNW] * s_ww[el];
         }
         const int fcnt = s_fcnt[p], fbeg = s_fbeg[p] - fcnt;
         if (xcnt > 0 || fcnt > 0) {
             const int e1 = (int)(key[gs] & 511u);
             s_exc[e] = 1;
-            s_first[e] = (uint32_t)((e1 & 31) * CC + (e1 >> 5));
+            s_first[e] = (uint32_t)((e1 & (NW - 1)) * CC + (e1 >> LOGNW));
             s_pk[e] = (uint32_t)xstart | ((uint32_t)xcnt << 9) | ((uint32_t)fbeg << 14) |
                       ((uint32_t)fcnt << 24);
         }
     }
     __syncthreads();
-    // token masks of last visits and exception records
-    if (tid < CC) {
+    // token masks of last visits and exception records, word wd of token t
+    // covering entries (t, 32 wd + i)
+    if (tid < CC * G::NMW) {
+        const int t = tid / G::NMW, wd = tid % G::NMW;
         uint32_t lm = 0u, em = 0u;
-        for (int i = 0; i < NW && tid < ntok; ++i) {
-            const int e = tid * NW + i, p = s_pos[e];
+        for (int i = 0; i < 32 && t < ntok; ++i) {
+            const int e = t * NW + 32 * wd + i, p = s_pos[e];
             lm |= (s_ge[p] - 1 == p) ? (1u << i) : 0u;
             em |= s_exc[e] ? (1u << i) : 0u;
         }
@@ -372,7 +399,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         }
         if (tid < CC) out[PL_EXCB + tid] = (uint32_t)(tid == 0 ? 0 : s_exc[tid * NW - 1]);
         for (int e = tid; e < NE; e += 256) {
-            const int t = e >> 5, i = e & 31;
+            const int t = e >> LOGNW, i = e & (NW - 1);
             out[PL_FIN + (i * CC + t) * 2 + 0] = __float_as_uint(s_P[e]);
             out[PL_FIN + (i * CC + t) * 2 + 1] = __float_as_uint(s_f[e]);
             const int prev = e == 0 ? 0 : s_exc[e - 1];
@@ -390,15 +417,15 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
 
     // S7: read coefficients e = w * P(m, <= t)
     for (int e = tid; e < CC * NR; e += 256) {
-        const int t = e >> 5, k = e & 31;
+        const int t = e >> LOGNW, k = e & (NR - 1);
         float pr = 1.f;
         for (int l = s_rgs[e]; l < s_rend[e]; ++l) pr *= s_d[l];
-        out[coef_word(t, NW + k)] = __float_as_uint(t < ntok ? s_wr[e] * pr : 0.f);
+        out[G::coef_word(t, NW + k)] = __float_as_uint(t < ntok ? s_wr[e] * pr : 0.f);
     }
 
     // S8: A[t][tau] (shared form) and Bm[t][tau], one thread per pair, sums in a fixed order
-    {
-        const int t = tid >> 4, tau = tid & 15;
+    if (tid < CC * CC) {
+        const int t = tid / CC, tau = tid % CC;
         float av = 0.f, bv = 0.f;
         if (t < ntok && tau <= t) {
             if (a.mode == 0 && tau < t) {
@@ -408,7 +435,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
                     float between = 1.f;  // decays of the visits strictly between
                     for (int l = p - 1; l >= s_gs[p]; --l) {
                         const int el = (int)(key[l] & 511u);
-                        if ((el >> 5) == tau) {
+                        if ((el >> LOGNW) == tau) {
                             av += s_al[t] * s_ww[e] * between * s_be[tau] * s_ww[el];
                             break;
                         }
@@ -421,7 +448,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
                 float after = 1.f;  // decays of the visits after tau's, up to token t
                 for (int l = s_rend[e] - 1; l >= s_rgs[e]; --l) {
                     const int el = (int)(key[l] & 511u);
-                    if ((el >> 5) == tau) {
+                    if ((el >> LOGNW) == tau) {
                         bv += s_wr[e] * after * s_be[tau] * s_ww[el];
                         break;
                     }
@@ -450,14 +477,14 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
 
     // S10: byte offsets of every staged row
     for (int x = tid; x < CC * NQ; x += 256) {
-        const int t = x >> 6, q = x & 63;
+        const int t = x / NQ, q = x & (NQ - 1);
         uint32_t off = 0u;
         if (t < ntok) {
             const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
             const int sl = q < NW ? a.idx_w[bth * NW + q] : a.idx_r[bth * NR + (q - NW)];
             off = (uint32_t)sl * (uint32_t)a.dv * 4u;
         }
-        out[offs_word(q, t)] = off;
+        out[G::offs_word(q, t)] = off;
     }
 }
 
@@ -520,11 +547,48 @@ SSLP_DEVICE u32x4 lds_u32x4(uint32_t a) {
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF) : "memory");
     return v;
 }
+SSLP_DEVICE uint32_t lds_u16(uint32_t a) {
+    uint32_t v;
+    asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"(a) : "memory");
+    return v;
+}
+// reads of N consecutive floats (N = 1, 2, 4) as one value
+template <int N>
+struct VecOf;
+template <>
+struct VecOf<1> {
+    using type = float;
+};
+template <>
+struct VecOf<2> {
+    using type = f32x2;
+};
+template <>
+struct VecOf<4> {
+    using type = f32x4;
+};
+template <int N, int OFF = 0>
+SSLP_DEVICE typename VecOf<N>::type lds_vec(uint32_t a) {
+    if constexpr (N == 1) return lds_f32<OFF>(a);
+    else if constexpr (N == 2) return lds_f32x2<OFF>(a);
+    else return lds_f32x4<OFF>(a);
+}
+SSLP_DEVICE float elem(float v, int) { return v; }
+SSLP_DEVICE float elem(f32x2 v, int i) { return v[i]; }
+SSLP_DEVICE float elem(f32x4 v, int i) { return v[i]; }
+SSLP_DEVICE void lds_write_f32(uint32_t a, float v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
 SSLP_DEVICE void lds_write_f32x2(uint32_t a, f32x2 v) {
     asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v) : "memory");
 }
 SSLP_DEVICE void lds_write_f32x4(uint32_t a, f32x4 v) {
     asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+template <int N>
+SSLP_DEVICE void lds_write_cols(uint32_t a, const float (&x)[N]) {
+    if constexpr (N == 1) lds_write_f32(a, x[0]);
+    else lds_write_f32x2(a, f32x2{x[0], x[1]});
 }
 // wait for all LDS operations; each operand then passes through an empty
 // volatile asm ordered after the wait, so that no use of it is scheduled before
@@ -558,27 +622,35 @@ SSLP_DEVICE void static_for(F&& f) {
 
 // ---------------------------------------------------------------------------
 // apply kernel: one workgroup of NWAVE wavefronts per (b, h, 8-column slice).
-// DMA j (j = 0..31) stages rows q = 2j, 2j+1 of the chunk's 16 tokens; wave w
-// owns the DMAs j = w + NWAVE m: it gathers those rows, forms the partial row
-// sums over them, and writes back the write rows among them.  Several
-// wavefronts per CU keep that many times more gathers in flight than one, and
-// split the compute.
+// DMA j (j = 0..31) stages rows q = RPD j .. RPD j + RPD - 1 of the chunk's C
+// tokens (RPD = 32 / C); wave w owns the DMAs j = w + NWAVE m: it gathers those
+// rows, forms the partial row sums over them, and writes back the write rows
+// among them (j < 16).  Several wavefronts per CU keep that many times more
+// gathers in flight than one, and split the compute.
 // ---------------------------------------------------------------------------
-template <typename io_t>
+template <typename io_t, class G>
 __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateArgs a,
                                                                      const uint32_t* __restrict__ plan,
                                                                      int nslice, int total, int nch) {
+    constexpr int CC = G::CC, NQ = G::NQ, RPD = G::RPD, NMW = G::NMW;
+    constexpr int LPT = 64 / CC;                     // compute lanes per token
+    constexpr int CPL = CW / LPT;                    // columns per compute lane (2 or 1)
     constexpr int VB = CC * CW * (int)sizeof(io_t);  // value bytes of a chunk
-    constexpr int VDMA = VB / 256;                   // dword DMAs per chunk
-    constexpr int ROWB = CC * CW * 4;                // bytes of one staged row index q (16 tokens)
+    constexpr int VBP = (VB + 255) / 256 * 256;      // padded to whole dword DMAs
+    constexpr int VDMA = VBP / 256;                  // dword DMAs per chunk
+    constexpr int ROWB = CC * CW * 4;                // bytes of one staged row index q (C tokens)
     constexpr int NPIECE = PL_DMA_WORDS / 256;       // 1 KB plan pieces per chunk
-    constexpr int WB = 16 / NWAVE;                   // write-row DMAs per wave (j < 16)
-    static_assert(VB % 256 == 0, "values are DMA'd in 256-byte pieces");
+    constexpr int NWD = 16;                          // DMAs holding write rows (j < 16)
+    constexpr int WB = NWD / NWAVE;                  // write-row DMAs per wave
+    using cv = typename VecOf<CPL>::type;            // a compute lane's columns
+    using mask_t = typename std::conditional<NMW == 1, uint32_t, uint64_t>::type;
+    static_assert(RPD * NWD == G::NW && NWD % NWAVE == 0, "write rows fill the first 16 DMAs");
+    static_assert(CPL * LPT == CW && (CPL == 1 || CPL == 2), "compute mapping");
     static_assert(NPIECE % NWAVE == 0 && JW == 4 && WB >= 1, "work split over the wavefronts");
 
     __shared__ __align__(16) float stage[2][NQ * CC][CW];  // rows (q, t) at q*16 + t
     __shared__ __align__(16) uint32_t pbuf[3][PL_DMA_WORDS];
-    __shared__ __align__(16) uint32_t vbuf[2][VB / 4];
+    __shared__ __align__(16) uint32_t vbuf[2][VBP / 4];
     __shared__ __align__(16) float part[NWAVE][2][CC][CW];  // partial g, h per wave
     __shared__ __align__(16) float xr[CC][CW];             // v - g
     __shared__ __align__(16) float xs[CC][CW];             // residuals
@@ -609,11 +681,11 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
     constexpr uint32_t PLAN_BYTES = PL_DMA_WORDS * 4;
 
     // DMA lane mapping (also the write-back mapping): lane l covers 16 bytes
-    // (half l%2) of row (q = 2j + l/32, t = (l/2) % 16)
-    const int dq = lane >> 5, dt = (lane >> 1) & 15, dh = lane & 1;
+    // (half l%2) of row (q = RPD j + (l/2) / C, t = (l/2) % C)
+    const int dq = (lane >> 1) / CC, dt = (lane >> 1) % CC, dh = lane & 1;
     const uint32_t colbyte = 4u * (uint32_t)(col0 + 4 * dh);
     // this lane's JW row offsets for its wave's DMAs j = wave + NWAVE m
-    const uint32_t offs_lane = 4u * (uint32_t)(PL_OFFS + (dq * 16 + dt) * OFFS_LD + wave * JW);
+    const uint32_t offs_lane = 4u * (uint32_t)(G::PL_OFFS + (lane >> 1) * G::OFFS_LD + wave * JW);
 
     auto plan_dma = [&](int ch) {  // this wave's pieces of chunk ch's plan -> pbuf[ch % 3]
         const uint32_t* src = planb + (size_t)ch * PL_WORDS;
@@ -634,9 +706,9 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
             const int tb = ch * CC;
 #pragma unroll
             for (int s = 0; s < VDMA; ++s) {
-                const int byte = (s * 64 + lane) * 4;
+                const int byte = (s * 64 + lane) * 4;  // bytes past VB fill the padding
                 const int tt = tb + byte / (CW * (int)sizeof(io_t));
-                const char* src = tt < T ? vin + ((((size_t)b * T + tt) * H + h) * dv + col0) * sizeof(io_t) +
+                const char* src = byte < VB && tt < T ? vin + ((((size_t)b * T + tt) * H + h) * dv + col0) * sizeof(io_t) +
                                                byte % (CW * (int)sizeof(io_t))
                                          : vin;
                 dma4(src, &vbuf[ch % 2][s * 64]);
@@ -653,10 +725,11 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
     wait_vm0();
     block_sync_lds();
 
-    // compute mapping: lane (t, qt) = (lane/4, lane%4) owns columns 2qt, 2qt+1 of token t
-    const int ct = lane >> 2, qt = lane & 3;
-    const uint32_t cofs = (uint32_t)((ct * CW + 2 * qt) * 4);  // (token, column pair) in a row
-    const uint32_t xq = (uint32_t)(2 * qt * 4);
+    // compute mapping: lane (t, qt) = (lane / LPT, lane % LPT) owns the CPL
+    // columns CPL qt .. CPL qt + CPL - 1 of token t
+    const int ct = lane / LPT, qt = lane % LPT;
+    const uint32_t cofs = (uint32_t)((ct * CW + CPL * qt) * 4);  // (token, columns) in a row
+    const uint32_t xq = (uint32_t)(CPL * qt * 4);
 
     for (int c = 0; c < nch; ++c) {
         const int ntok = T - c * CC < CC ? T - c * CC : CC;
@@ -665,113 +738,142 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
         if (c + 1 < nch) row_dma(c + 1);
         if (c + 2 < nch) plan_dma(c + 2);
 
-        // ---- partial g, h over this wave's rows: q = 2j, 2j+1 for j = wave + NWAVE m ----
+        // ---- partial g, h over this wave's rows: q = RPD j + r for j = wave + NWAVE m ----
         {
-            f32x2 cf[JW], rw[2 * JW];
-            const uint32_t cfa = P + 4u * (uint32_t)coef_word(ct, 2 * wave);  // + 2 NWAVE words per m
-            const uint32_t rowa = S + cofs + (uint32_t)(2 * wave * ROWB);     // + 2 NWAVE rows per m
+            typename VecOf<RPD>::type cf[JW];
+            cv rw[RPD * JW];
+            const uint32_t cfa = P + 4u * (uint32_t)G::coef_word(ct, RPD * wave);  // + RPD NWAVE words per m
+            const uint32_t rowa = S + cofs + (uint32_t)(RPD * wave * ROWB);        // + RPD NWAVE rows per m
             static_for<JW>([&](auto m) {
-                cf[m] = lds_f32x2<8 * NWAVE * m>(cfa);
-                rw[2 * m] = lds_f32x2<2 * NWAVE * m * ROWB>(rowa);
-                rw[2 * m + 1] = lds_f32x2<(2 * NWAVE * m + 1) * ROWB>(rowa);
+                constexpr int M = decltype(m)::value;
+                cf[M] = lds_vec<RPD, 4 * RPD * NWAVE * M>(cfa);
+                static_for<RPD>([&](auto r) {
+                    constexpr int R = decltype(r)::value;
+                    rw[RPD * M + R] = lds_vec<CPL, (RPD * NWAVE * M + R) * ROWB>(rowa);
+                });
             });
             lds_wait();
             tie_all(cf);
             tie_all(rw);
-            f32x2 g = {0.f, 0.f}, hh = {0.f, 0.f};
+            float g[CPL], hh[CPL];
 #pragma unroll
-            for (int m = 0; m < JW; ++m) {
-                f32x2& acc = (wave + NWAVE * m) < 16 ? g : hh;  // write rows are q < 32
-                acc.x = fmaf(cf[m].x, rw[2 * m].x, acc.x);
-                acc.y = fmaf(cf[m].x, rw[2 * m].y, acc.y);
-                acc.x = fmaf(cf[m].y, rw[2 * m + 1].x, acc.x);
-                acc.y = fmaf(cf[m].y, rw[2 * m + 1].y, acc.y);
-            }
-            lds_write_f32x2(part0 + (uint32_t)((wave * 2 + 0) * CC * CW * 4) + cofs, g);
-            lds_write_f32x2(part0 + (uint32_t)((wave * 2 + 1) * CC * CW * 4) + cofs, hh);
+            for (int k = 0; k < CPL; ++k) g[k] = hh[k] = 0.f;
+            static_for<JW>([&](auto m) {
+                constexpr int M = decltype(m)::value;
+                auto step = [&](float(&acc)[CPL]) {
+#pragma unroll
+                    for (int r = 0; r < RPD; ++r)
+#pragma unroll
+                        for (int k = 0; k < CPL; ++k)
+                            acc[k] = fmaf(elem(cf[M], r), elem(rw[RPD * M + r], k), acc[k]);
+                };
+                // DMA j = wave + NWAVE M holds write rows iff j < 16, i.e. NWAVE M < 16
+                if constexpr (NWAVE * M < NWD) step(g);
+                else step(hh);
+            });
+            lds_write_cols(part0 + (uint32_t)((wave * 2 + 0) * CC * CW * 4) + cofs, g);
+            lds_write_cols(part0 + (uint32_t)((wave * 2 + 1) * CC * CW * 4) + cofs, hh);
         }
         block_sync_lds();
 
         // ---- wave 0: g, h, r = v - g, res = T r, y = h + Bm res ----
         const bool tok_ok = ct < ntok;
         if (wave == 0) {
-            f32x2 pg[NWAVE], ph[NWAVE];
+            cv pg[NWAVE], ph[NWAVE];
             static_for<NWAVE>([&](auto w) {
-                pg[w] = lds_f32x2<(w * 2 + 0) * CC * CW * 4>(part0 + cofs);
-                ph[w] = lds_f32x2<(w * 2 + 1) * CC * CW * 4>(part0 + cofs);
+                pg[w] = lds_vec<CPL, (w * 2 + 0) * CC * CW * 4>(part0 + cofs);
+                ph[w] = lds_vec<CPL, (w * 2 + 1) * CC * CW * 4>(part0 + cofs);
             });
-            float v0, v1;
-            const uint32_t va = vbuf0 + (uint32_t)((c % 2) * VB + (ct * CW + 2 * qt) * (int)sizeof(io_t));
-            if (sizeof(io_t) == 2) {
+            float vv[CPL];
+            const uint32_t va = vbuf0 + (uint32_t)((c % 2) * VBP + (ct * CW + CPL * qt) * (int)sizeof(io_t));
+            if constexpr (sizeof(io_t) == 2 && CPL == 2) {
                 uint32_t w = lds_u32(va);
                 lds_wait(w);
-                v0 = bf16lo(w);
-                v1 = bf16hi(w);
-            } else {
-                f32x2 w = lds_f32x2(va);
+                vv[0] = bf16lo(w);
+                vv[1] = bf16hi(w);
+            } else if constexpr (sizeof(io_t) == 2) {
+                uint32_t w = lds_u16(va);
                 lds_wait(w);
-                v0 = w.x;
-                v1 = w.y;
+                vv[0] = bf16lo(w);
+            } else {
+                cv w = lds_vec<CPL>(va);
+                lds_wait(w);
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) vv[k] = elem(w, k);
             }
             tie_all(pg);
             tie_all(ph);
-            float g0 = 0.f, g1 = 0.f, h0 = 0.f, h1 = 0.f;
+            float gs[CPL], hs[CPL], r[CPL];
 #pragma unroll
-            for (int w = 0; w < NWAVE; ++w) {
-                g0 += pg[w].x;
-                g1 += pg[w].y;
-                h0 += ph[w].x;
-                h1 += ph[w].y;
+            for (int k = 0; k < CPL; ++k) {
+                gs[k] = hs[k] = 0.f;
+#pragma unroll
+                for (int w = 0; w < NWAVE; ++w) {
+                    gs[k] += elem(pg[w], k);
+                    hs[k] += elem(ph[w], k);
+                }
+                r[k] = tok_ok ? vv[k] - gs[k] : 0.f;
             }
-            f32x2 r;
-            r.x = tok_ok ? v0 - g0 : 0.f;
-            r.y = tok_ok ? v1 - g1 : 0.f;
-            lds_write_f32x2(xr0 + cofs, r);
-            f32x2 res;
+            lds_write_cols(xr0 + cofs, r);
+            float res[CPL];
             {
-                f32x4 tm[4];
-                f32x2 rr[CC];
-                const uint32_t ta = P + 4u * (uint32_t)(PL_TM + ct * TB_LD);
-                static_for<4>([&](auto k) { tm[k] = lds_f32x4<16 * k>(ta); });
-                static_for<CC>([&](auto k) { rr[k] = lds_f32x2<k * CW * 4>(xr0 + xq); });
+                f32x4 tm[CC / 4];
+                cv rr[CC];
+                const uint32_t ta = P + 4u * (uint32_t)(G::PL_TM + ct * G::TB_LD);
+                static_for<CC / 4>([&](auto k) { tm[k] = lds_f32x4<16 * k>(ta); });
+                static_for<CC>([&](auto k) { rr[k] = lds_vec<CPL, k * CW * 4>(xr0 + xq); });
                 lds_wait();
                 tie_all(tm);
                 tie_all(rr);
-                float s0[2] = {0.f, 0.f}, s1[2] = {0.f, 0.f};
+                float sacc[CPL][2];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) sacc[k][0] = sacc[k][1] = 0.f;
 #pragma unroll
                 for (int tau = 0; tau < CC; ++tau) {
                     const float tv = tm[tau >> 2][tau & 3];
-                    s0[tau & 1] = fmaf(tv, rr[tau].x, s0[tau & 1]);
-                    s1[tau & 1] = fmaf(tv, rr[tau].y, s1[tau & 1]);
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k)
+                        sacc[k][tau & 1] = fmaf(tv, elem(rr[tau], k), sacc[k][tau & 1]);
                 }
-                res.x = s0[0] + s0[1];
-                res.y = s1[0] + s1[1];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) res[k] = sacc[k][0] + sacc[k][1];
             }
-            lds_write_f32x2(xs0 + cofs, res);
+            lds_write_cols(xs0 + cofs, res);
             {
-                f32x4 bm[4];
-                f32x2 rs[CC];
-                const uint32_t ba = P + 4u * (uint32_t)(PL_BM + ct * TB_LD);
-                static_for<4>([&](auto k) { bm[k] = lds_f32x4<16 * k>(ba); });
-                static_for<CC>([&](auto k) { rs[k] = lds_f32x2<k * CW * 4>(xs0 + xq); });
+                f32x4 bm[CC / 4];
+                cv rs[CC];
+                const uint32_t ba = P + 4u * (uint32_t)(G::PL_BM + ct * G::TB_LD);
+                static_for<CC / 4>([&](auto k) { bm[k] = lds_f32x4<16 * k>(ba); });
+                static_for<CC>([&](auto k) { rs[k] = lds_vec<CPL, k * CW * 4>(xs0 + xq); });
                 lds_wait();
                 tie_all(bm);
                 tie_all(rs);
-                float s0[2] = {h0, 0.f}, s1[2] = {h1, 0.f};
+                float sacc[CPL][2], yv[CPL];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) {
+                    sacc[k][0] = hs[k];
+                    sacc[k][1] = 0.f;
+                }
 #pragma unroll
                 for (int tau = 0; tau < CC; ++tau) {
                     const float bv = bm[tau >> 2][tau & 3];
-                    s0[tau & 1] = fmaf(bv, rs[tau].x, s0[tau & 1]);
-                    s1[tau & 1] = fmaf(bv, rs[tau].y, s1[tau & 1]);
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k)
+                        sacc[k][tau & 1] = fmaf(bv, elem(rs[tau], k), sacc[k][tau & 1]);
                 }
-                const float y0 = s0[0] + s0[1], y1 = s1[0] + s1[1];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) yv[k] = sacc[k][0] + sacc[k][1];
                 if (tok_ok) {
-                    char* dst = yout + ((((size_t)b * T + c * CC + ct) * H + h) * dv + col0 + 2 * qt) * sizeof(io_t);
-                    if (sizeof(io_t) == 2) {
-                        const uint32_t w = (uint32_t)f32_to_bf16(y0).bits | ((uint32_t)f32_to_bf16(y1).bits << 16);
+                    char* dst = yout + ((((size_t)b * T + c * CC + ct) * H + h) * dv + col0 + CPL * qt) * sizeof(io_t);
+                    if constexpr (sizeof(io_t) == 2 && CPL == 2) {
+                        const uint32_t w = (uint32_t)f32_to_bf16(yv[0]).bits | ((uint32_t)f32_to_bf16(yv[1]).bits << 16);
                         *reinterpret_cast<uint32_t*>(dst) = w;
+                    } else if constexpr (sizeof(io_t) == 2) {
+                        *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(yv[0]).bits;
+                    } else if constexpr (CPL == 2) {
+                        *reinterpret_cast<float2*>(dst) = make_float2(yv[0], yv[1]);
                     } else {
-                        *reinterpret_cast<float2*>(dst) = make_float2(y0, y1);
+                        *reinterpret_cast<float*>(dst) = yv[0];
                     }
                 }
             }
@@ -791,31 +893,41 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
             }
             return tailg[k];
         };
-        const uint32_t q0 = (uint32_t)(2 * wave + dq);  // + 2 NWAVE per m
+        const uint32_t q0 = (uint32_t)(RPD * wave + dq);  // + RPD NWAVE per m
         f32x4 rj = lds_f32x4(xs0 + (uint32_t)((dt * CW + 4 * dh) * 4));
         u32x4 offv = lds_u32x4(P + offs_lane);
-        u32x4 hdr = lds_u32x4(P + 4u * PL_HDR);
-        uint32_t lm = lds_u32(P + 4u * (uint32_t)(PL_LAST + dt));
-        uint32_t em = lds_u32(P + 4u * (uint32_t)(PL_EXC + dt));
-        uint32_t eb = lds_u32(P + 4u * (uint32_t)(PL_EXCB + dt));
+        u32x4 hdr = lds_u32x4(P + 4u * G::PL_HDR);
+        uint32_t lmw[NMW], emw[NMW];
+        static_for<NMW>([&](auto k) {
+            lmw[k] = lds_u32(P + 4u * (uint32_t)(G::PL_LAST + dt * NMW + k));
+            emw[k] = lds_u32(P + 4u * (uint32_t)(G::PL_EXC + dt * NMW + k));
+        });
+        uint32_t eb = lds_u32(P + 4u * (uint32_t)(G::PL_EXCB + dt));
         f32x2 pf[WB];
         f32x4 m0[WB];
-        const uint32_t fina = P + 4u * (uint32_t)(PL_FIN + (q0 * CC + dt) * 2);  // + 2 NWAVE rows per m
+        const uint32_t fina = P + 4u * (uint32_t)(G::PL_FIN + (q0 * CC + dt) * 2);  // + RPD NWAVE rows per m
         const uint32_t own = S + (uint32_t)(((q0 * CC + dt) * CW + 4 * dh) * 4);
         static_for<WB>([&](auto m) {
-            pf[m] = lds_f32x2<2 * NWAVE * m * CC * 8>(fina);
-            m0[m] = lds_f32x4<2 * NWAVE * m * ROWB>(own);
+            pf[m] = lds_f32x2<RPD * NWAVE * m * CC * 8>(fina);
+            m0[m] = lds_f32x4<RPD * NWAVE * m * ROWB>(own);
         });
-        lds_wait(rj, offv, hdr, lm, em, eb);
+        lds_wait(rj, offv, hdr, eb);
+        tie_all(lmw);
+        tie_all(emw);
         tie_all(pf);
         tie_all(m0);
+        mask_t lm = lmw[0], em = emw[0];
+        if constexpr (NMW == 2) {
+            lm |= (mask_t)lmw[NMW - 1] << 32;
+            em |= (mask_t)emw[NMW - 1] << 32;
+        }
         const uint32_t extra_base = hdr.x, fwd_base = hdr.y;
         bool any_fwd = false;
         f32x4 keep[WB];
         uint32_t kpk[WB];
 #pragma unroll
         for (int m = 0; m < WB; ++m) {
-            const uint32_t q = q0 + 2 * NWAVE * m;
+            const uint32_t q = q0 + RPD * NWAVE * m;
             kpk[m] = 0u;
             keep[m] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (!wb_ok || !((lm >> q) & 1u)) continue;
@@ -823,7 +935,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
             const float Pv = pf[m].x, f = pf[m].y;
             uint32_t pk = 0u;
             if ((em >> q) & 1u) {
-                const uint32_t k = eb + (uint32_t)__builtin_popcount(em & ((1u << q) - 1u));
+                const uint32_t k = eb + (uint32_t)__builtin_popcountll((uint64_t)(em & (((mask_t)1 << q) - 1u)));
                 const uint32_t first = tail(2 * k);
                 pk = tail(2 * k + 1);
                 if (first != q * CC + dt) {
@@ -879,37 +991,47 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
 // slices than compute units they run in rounds, which still beats the
 // per-token kernel (1.4B-layer shape, B = 5: 12.0 against 22.3 ms; B = 8:
 // 18.7 against 26.6 ms).  Sequences shorter than 64 tokens (decode steps,
-// short prompts) are left to the per-token kernel.
+// short prompts) are left to the per-token kernel.  W = R = 32 runs in chunks
+// of 16 tokens, W = R = 64 in chunks of 8.
 bool sdm_chunked_supported(int B, int T, int H, int W, int R, int dv, long long N) {
     (void)B;
     (void)H;
-    if (W != NW || R != NR || dv % CW != 0) return false;
+    if (!((W == 32 || W == 64) && R == W) || dv % CW != 0) return false;
     if ((unsigned long long)N * (unsigned long long)dv * 4ull >= (1ull << 31)) return false;
     if (N >= (1ll << 31)) return false;
     return T >= 64;
 }
 
-size_t sdm_chunk_plan_bytes(int B, int T, int H) {
-    const long long nch = (T + CC - 1) / CC;
+size_t sdm_chunk_plan_bytes(int B, int T, int H, int W) {
+    const int cc = W == 64 ? GeoW64::CC : GeoW32::CC;
+    const long long nch = (T + cc - 1) / cc;
     return (size_t)B * H * nch * PL_WORDS * 4;
 }
 
-hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* planws, hipStream_t st) {
-    uint32_t* plan = static_cast<uint32_t*>(planws);
-    const int nch = (a.T + CC - 1) / CC;
+namespace {
+template <class G>
+hipError_t launch_chunked(const SdmUpdateArgs& a, uint32_t* plan, hipStream_t st) {
+    const int nch = (a.T + G::CC - 1) / G::CC;
     PlanArgs pa{a.B, a.T, a.H, a.N, a.dv, nch, a.residual_mode, a.idx_w, a.wt_w, a.idx_r, a.wt_r,
                 a.alpha, a.beta, plan, a.err};
-    sdm_chunk_plan_kernel<<<(unsigned)(a.B * a.H * nch), 256, 0, st>>>(pa);
+    sdm_chunk_plan_kernel<G><<<(unsigned)(a.B * a.H * nch), 256, 0, st>>>(pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nslice = a.dv / CW;
     const int total = a.B * a.H * nslice;
     const int grid = ((total + 127) / 128) * 128;
     if (a.dtype != 0)
-        sdm_chunk_apply_kernel<bf16_t><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
+        sdm_chunk_apply_kernel<bf16_t, G><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
     else
-        sdm_chunk_apply_kernel<float><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
+        sdm_chunk_apply_kernel<float, G><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* planws, hipStream_t st) {
+    uint32_t* plan = static_cast<uint32_t*>(planws);
+    if (a.W == 64) return launch_chunked<GeoW64>(a, plan, st);
+    return launch_chunked<GeoW32>(a, plan, st);
 }
 
 }  // namespace sslp

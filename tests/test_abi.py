@@ -88,6 +88,23 @@ def test_sdm_forward_workspace_and_flags():
     assert lib.sdm_workspace_size(ctypes.byref(_sdm(W=65))) == 0  # W > N
 
 
+@pytest.mark.parametrize("W,k,chunk", [(32, 6, 16), (64, 8, 8), (40, 7, None)])
+def test_sdm_workspace_holds_the_chunk_plans(W, k, chunk):
+    # W = R = 32 and W = R = 64 with T >= 64 take the chunk-parallel recurrence
+    # (chunks of 16 and 8 tokens), whose per-chunk plans (7168 words each) live
+    # in the workspace after the addressing; other shapes need the addressing only
+    lib = _lib.lib()
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    for T in (63, 100):
+        s = _sdm(B=2, T=T, H=3, sqrtN=16, d_v=16, k_w=k, k_r=k, W=W, R=W)
+        addressing = 4 * a256(2 * T * 3 * W * 4)
+        plans = 0 if chunk is None or T < 64 else a256(2 * 3 * -(-T // chunk) * 7168 * 4)
+        assert lib.sdm_workspace_size(ctypes.byref(s)) == addressing + plans, (W, T)
+
+
 def test_sdm_decode_requires_single_token():
     lib = _lib.lib()
     s = _sdm(T=3)

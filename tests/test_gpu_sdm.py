@@ -1,5 +1,7 @@
 """GPU parity of the Sparse Delta Memory path (addressing, update/read, decode)
 against the fp64 oracle, through the C ABI."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -103,6 +105,16 @@ SMALL = [
     # more column slices (B*H*d_v/8 = 1200) than the chip holds workgroups at
     # once: the slices run in several rounds
     (5, 80, 2, 64, 960, 32, 32, 32, 32, "bf16", 0),
+    # W = R = 64 and T >= 64: the pipelined kernel in chunks of 8 tokens (a
+    # 64-bit mask per token, one column per compute lane): tiny tables where
+    # nearly every row is forwarded, ragged tails, mid-size and 1.4B-size tables
+    (2, 100, 2, 10, 24, 10, 10, 64, 64, "f32", 0),
+    (1, 67, 1, 9, 16, 9, 9, 64, 64, "bf16", 1),
+    (1, 64, 2, 12, 8, 12, 12, 64, 64, "f32", 1),
+    (1, 200, 2, 100, 16, 64, 64, 64, 64, "f32", 0),
+    (1, 161, 1, 64, 24, 64, 64, 64, 64, "bf16", 1),
+    (1, 300, 3, 240, 40, 64, 64, 64, 64, "bf16", 0),
+    (2, 72, 2, 64, 960, 64, 64, 64, 64, "bf16", 0),
 ]
 
 
@@ -307,9 +319,12 @@ def test_empty_sequence_is_noop():
 
 
 @pytest.mark.slow
-def test_sdm_1p4b_layer_full_size():
-    cfg = wl.SDM_14B
-    announce(f"sdm 1.4B-layer full size T={cfg.T} N={cfg.N} d_v={cfg.d_v}")
+@pytest.mark.parametrize("budget", [32, 64])
+def test_sdm_1p4b_layer_full_size(budget):
+    # the 1.4B-layer prefill at k = W = R = 32 (16-token chunks) and at the
+    # pages' larger budget k = W = R = 64 (8-token chunks)
+    cfg = dataclasses.replace(wl.SDM_14B, k_w=budget, k_r=budget, W=budget, R=budget)
+    announce(f"sdm 1.4B-layer full size T={cfg.T} N={cfg.N} d_v={cfg.d_v} W=R={budget}")
     x = wl.sdm_inputs(cfg)
     M0 = torch.zeros((cfg.B, cfg.H, cfg.N, cfg.d_v))
     got = _run_forward(cfg, x, M0, 0)
@@ -422,14 +437,14 @@ def test_side_stream_call_orders_its_own_allocations():
     assert torch.equal(y, y_ref) and torch.equal(M, M_ref)
 
 
-@pytest.mark.parametrize("path", ["chunked", "per_token"])
+@pytest.mark.parametrize("path", ["chunked", "chunked_w64", "per_token"])
 def test_out_of_range_slot_is_contained_and_reported(path):
     # A caller index outside [0, N) must not reach memory outside the table: the
     # table is a slice of a larger buffer whose guard regions must stay bitwise;
-    # the device error flag reports the call.  Chunk path: W = R = 32, T >= 64;
-    # per-token path: W = R = 9.
+    # the device error flag reports the call.  Chunk path: W = R = 32 or 64,
+    # T >= 64; per-token path: W = R = 9.
     sslp = _sslp()
-    W = 32 if path == "chunked" else 9
+    W = {"chunked": 32, "chunked_w64": 64, "per_token": 9}[path]
     B, T, H, sq, dv = 1, 80, 2, 16, 32
     N = sq * sq
     announce(f"out-of-range slot, {path} path")
@@ -437,9 +452,9 @@ def test_out_of_range_slot_is_contained_and_reported(path):
     g = torch.Generator().manual_seed(91)
     idx = torch.stack([torch.randperm(N, generator=g)[:W] for _ in range(B * T * H)]).int()
     idx = idx.view(B, T, H, W).contiguous()
-    idx[0, 70, 1, 3] = N + 5           # one bad write slot (chunk 4, head 1)
+    idx[0, 70, 1, 3] = N + 5           # one bad write slot (token 70, head 1)
     idx_r = idx.clone()
-    idx_r[0, 10, 0, 0] = -7            # one bad read slot (chunk 0, head 0)
+    idx_r[0, 10, 0, 0] = -7            # one bad read slot (token 10, head 0)
     wt = torch.full((B, T, H, W), 1.0 / W)
     v = torch.randn((B, T, H, dv), generator=g)
     alpha = torch.full((B, T, H), 0.95)
