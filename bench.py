@@ -331,7 +331,7 @@ def bench_rows(args, torch, sslp, wl):
         hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_call=nbytes)
     del yv, gv, gam, ov
     # SDM training on the 1.4B prefill layer: forward keeping the pre-write rows
-    # (per-token kernel) and the backward by undoing writes (reverse sweep,
+    # (chunk-parallel kernel) and the backward by undoing writes (reverse sweep,
     # slice reduction, addressing-softmax backward)
     cfg = wl.SDM_14B
     x = {k: v.to(dev) for k, v in wl.sdm_inputs(cfg).items()}
@@ -343,10 +343,13 @@ def bench_rows(args, torch, sslp, wl):
     ws = torch.empty(sslp.sdm_backward_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.sqrtN, cfg.d_v,
                                                        cfg.W, cfg.R), dtype=torch.uint8,
                      device=dev)
+    ws_f = torch.empty(max(1, sslp.sdm_train_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.sqrtN,
+                                                             cfg.d_v, cfg.W, cfg.R)),
+                       dtype=torch.uint8, device=dev)
     reps = max(2, args.steps // 5)
     ms_f = time_call(torch, lambda: sslp.sdm_forward_train(
         x["sw1"], x["sw2"], x["sr1"], x["sr2"], x["v"], x["alpha"], x["beta"], M, cfg.k_w,
-        cfg.k_r, cfg.W, cfg.R, y=y, out=ctx), reps, warmup=1)
+        cfg.k_r, cfg.W, cfg.R, y=y, out=ctx, workspace=ws_f), reps, warmup=1)
     ms_b = time_call(torch, lambda: sslp.sdm_backward(ctx, x["v"], x["alpha"], x["beta"], M, dy,
                                                       dM, workspace=ws), reps, warmup=1)
     ntok = cfg.B * cfg.T * cfg.H
@@ -357,10 +360,11 @@ def bench_rows(args, torch, sslp, wl):
         fwd_ms=round(ms_f, 4), bwd_ms=round(ms_b, 4),
         tokens_per_s=round(cfg.B * cfg.T / ((ms_f + ms_b) * 1e-3), 1),
         fwd_gbs=round(per_f * ntok / (ms_f * 1e-3) / 1e9, 1),
+        fwd_hbm_frac=round(per_f * ntok / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         bwd_gbs=round(per_b * ntok / (ms_b * 1e-3) / 1e9, 1),
         bwd_hbm_frac=round(per_b * ntok / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         fwd_bytes_per_token_head=per_f, bwd_bytes_per_token_head=per_b)
-    del x, M, y, ctx, dy, dM, ws
+    del x, M, y, ctx, dy, dM, ws, ws_f
     torch.cuda.empty_cache()
     return rows
 

@@ -221,22 +221,35 @@ int sdm_norm_gate(long long rows, int d, int dtype, const void* y, const void* g
  * updates the table in place and retains the sparse update information).
  *   saved [B,T,H,W,d_v] fp32 out: saved[b,t,h,n,:] = M_{t-1}[idx_w[b,t,h,n], :]
  *   (T W d_v values per head, instead of one table per chunk).
- * Other arguments as sdm_forward; no workspace.  The recurrence runs one token
- * at a time (the chunk-parallel kernel has no per-token states to keep).
+ *   workspace, ws_bytes >= sdm_train_workspace_size(shape) (may be 0 / NULL
+ *   when that is 0), 256-byte aligned, owned by the caller.
+ * Other arguments as sdm_forward.  The recurrence runs as in sdm_forward: in
+ * chunks (slides "Training parallelizes within chunks and recurs across
+ * chunks") for T >= 64 and W = R = 32 or 64, each chunk's pre-write rows
+ * coming out of the walk over every slot's visits; one token at a time
+ * otherwise.  Errors: as sdm_forward, SSLP_ERR_WORKSPACE for a short workspace.
  */
 int sdm_forward_train(const sslp_sdm_shape* shape, int dtype, int residual_mode, const void* sw1,
                       const void* sw2, const void* sr1, const void* sr2, const void* v,
                       const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
-                      float* wt_w, int32_t* idx_r, float* wt_r, float* saved, void* stream);
+                      float* wt_w, int32_t* idx_r, float* wt_r, float* saved, void* workspace,
+                      size_t ws_bytes, void* stream);
 
 /*
  * sdm_sparse_update_train -- sdm_sparse_update that also writes `saved` as
- * sdm_forward_train does (addressing given by the caller; W, R up to 128).
+ * sdm_forward_train does (addressing given by the caller; W, R up to 128;
+ * workspace as sdm_forward_train).
  */
 int sdm_sparse_update_train(const sslp_sdm_shape* shape, int dtype, int residual_mode,
                             const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
                             const float* wt_r, const void* v, const float* alpha,
-                            const float* beta, float* M, void* y, float* saved, void* stream);
+                            const float* beta, float* M, void* y, float* saved, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/* Workspace bytes of sdm_forward_train and sdm_sparse_update_train: the
+ * per-chunk plans of the chunk-parallel recurrence (0 for shapes that run one
+ * token at a time, and for an invalid shape). */
+size_t sdm_train_workspace_size(const sslp_sdm_shape* shape);
 
 /* Workspace bytes of sdm_backward: per-token partial sums of the scalar
  * gradients for each 16-column slice of d_v, and the weight gradients when the

@@ -27,7 +27,7 @@ from ._lib import (DECAY_CHANNEL, DECAY_SCALAR, RESIDUAL_PER_SLOT, RESIDUAL_SHAR
 
 __all__ = ["sdm_forward", "sdm_forward_noalloc", "sdm_noalloc_scratch_bytes", "sdm_decode_step", "sdm_address", "sdm_sparse_update",
            "sdm_forward_train", "sdm_sparse_update_train", "sdm_backward",
-           "sdm_backward_workspace_bytes", "sdm_norm_gate",
+           "sdm_train_workspace_bytes", "sdm_backward_workspace_bytes", "sdm_norm_gate",
            "gdn_chunk_forward", "gdn2_chunk_forward", "sse_forward", "sse_decode_step",
            "SslpError", "RESIDUAL_SHARED", "RESIDUAL_PER_SLOT", "DECAY_SCALAR", "DECAY_CHANNEL",
            "version", "device_error"]
@@ -276,13 +276,18 @@ def sdm_norm_gate(y, gamma, gate=None, eps=1e-6, act="silu", o=None, stream=None
         return o
 
 
+def sdm_train_workspace_bytes(B, T, H, sqrtN, d_v, W, R):
+    """Workspace bytes of sdm_forward_train / sdm_sparse_update_train (chunk plans)."""
+    return lib().sdm_train_workspace_size(ctypes.byref(sdm_shape(B, T, H, sqrtN, d_v, 1, 1, W, R)))
+
+
 def sdm_backward_workspace_bytes(B, T, H, sqrtN, d_v, W, R):
     return lib().sdm_backward_workspace_size(ctypes.byref(sdm_shape(B, T, H, sqrtN, d_v, 1, 1,
                                                                      W, R)))
 
 
 def sdm_forward_train(sw1, sw2, sr1, sr2, v, alpha, beta, M, k_w, k_r, W, R, y=None,
-                      residual_mode=RESIDUAL_SHARED, out=None, stream=None):
+                      residual_mode=RESIDUAL_SHARED, out=None, workspace=None, stream=None):
     """sdm_forward that keeps what sdm_backward needs.  M is updated in place.
 
     Returns (y, dict(idx_w, wt_w, idx_r, wt_r, saved)); saved [B,T,H,W,d_v] fp32
@@ -315,17 +320,19 @@ def sdm_forward_train(sw1, sw2, sr1, sr2, v, alpha, beta, M, k_w, k_r, W, R, y=N
         _need(ctx["wt_r"], torch.float32, (B, T, H, R), "wt_r")
         _need(ctx["saved"], torch.float32, (B, T, H, W, d_v), "saved")
         shape = sdm_shape(B, T, H, sqrt_n, d_v, k_w, k_r, W, R)
+        ws, nbytes = _workspace(lib().sdm_train_workspace_size(ctypes.byref(shape)), workspace,
+                                v.device)
         rc = lib().sdm_forward_train(ctypes.byref(shape), _dtype_code(sw1), int(residual_mode),
                                      _ptr(sw1), _ptr(sw2), _ptr(sr1), _ptr(sr2), _ptr(v), _ptr(alpha),
                                      _ptr(beta), _ptr(M), _ptr(y), _ptr(ctx["idx_w"]),
                                      _ptr(ctx["wt_w"]), _ptr(ctx["idx_r"]), _ptr(ctx["wt_r"]),
-                                     _ptr(ctx["saved"]), _stream(stream))
+                                     _ptr(ctx["saved"]), _ptr(ws), nbytes, _stream(stream))
         check("sdm_forward_train", rc)
         return y, ctx
 
 
 def sdm_sparse_update_train(idx_w, wt_w, idx_r, wt_r, v, alpha, beta, M, y=None, saved=None,
-                            residual_mode=RESIDUAL_SHARED, stream=None):
+                            residual_mode=RESIDUAL_SHARED, workspace=None, stream=None):
     """sdm_sparse_update that also returns saved [B,T,H,W,d_v] (pre-write rows)."""
     with _on_stream(stream):
         B, T, H, W = idx_w.shape
@@ -349,10 +356,12 @@ def sdm_sparse_update_train(idx_w, wt_w, idx_r, wt_r, v, alpha, beta, M, y=None,
         _need(y, v.dtype, (B, T, H, d_v), "y")
         _need(saved, torch.float32, (B, T, H, W, d_v), "saved")
         shape = sdm_shape(B, T, H, sqrt_n, d_v, 1, 1, W, R)
+        ws, nbytes = _workspace(lib().sdm_train_workspace_size(ctypes.byref(shape)), workspace,
+                                v.device)
         rc = lib().sdm_sparse_update_train(ctypes.byref(shape), _dtype_code(v), int(residual_mode),
                                            _ptr(idx_w), _ptr(wt_w), _ptr(idx_r), _ptr(wt_r), _ptr(v),
                                            _ptr(alpha), _ptr(beta), _ptr(M), _ptr(y), _ptr(saved),
-                                           _stream(stream))
+                                           _ptr(ws), nbytes, _stream(stream))
         check("sdm_sparse_update_train", rc)
         return y, saved
 

@@ -48,8 +48,10 @@ SIGNATURES = {
     "sdm_sparse_update": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 10 + [_sz, _vp], _i),
     "sdm_norm_gate": ([ctypes.c_longlong, _i, _i, _vp, _vp, _vp, ctypes.c_float, _i, _vp, _vp],
                       _i),
-    "sdm_forward_train": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 15, _i),
-    "sdm_sparse_update_train": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 11, _i),
+    "sdm_forward_train": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 15 + [_sz, _vp], _i),
+    "sdm_sparse_update_train": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 11 + [_sz, _vp],
+                                _i),
+    "sdm_train_workspace_size": ([ctypes.POINTER(SdmShape)], _sz),
     "sdm_backward_workspace_size": ([ctypes.POINTER(SdmShape)], _sz),
     "sdm_backward": ([ctypes.POINTER(SdmShape), _i, _i] + [_vp] * 21 + [_sz, _vp], _i),
     "gdn_workspace_size": ([ctypes.POINTER(GdnShape)], _sz),

@@ -483,13 +483,20 @@ size_t sdm_backward_workspace_size(const sslp_sdm_shape* s) {
            align_up(bth * s->W * 4) + align_up(bth * s->R * 4);
 }
 
+size_t sdm_train_workspace_size(const sslp_sdm_shape* s) {
+    if (check_sdm_shape(s, false) != SSLP_OK) return 0;
+    return recurrence_bytes(s, s->T);
+}
+
 int sdm_sparse_update_train(const sslp_sdm_shape* s, int dtype, int residual_mode,
                             const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
                             const float* wt_r, const void* v, const float* alpha,
-                            const float* beta, float* M, void* y, float* saved, void* stream) {
+                            const float* beta, float* M, void* y, float* saved, void* workspace,
+                            size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     if (int rc = check_common(s, false, dtype, residual_mode)) return rc;
     REQUIRE_PTR(M);
+    REQUIRE_ALIGNED(workspace);
     if (s->T == 0) return SSLP_OK;
     REQUIRE_PTR(idx_w);
     REQUIRE_PTR(wt_w);
@@ -500,18 +507,24 @@ int sdm_sparse_update_train(const sslp_sdm_shape* s, int dtype, int residual_mod
     REQUIRE_PTR(beta);
     REQUIRE_PTR(y);
     REQUIRE_PTR(saved);
+    const size_t need = sdm_train_workspace_size(s);
+    REQUIRE(ws_bytes >= need && (need == 0 || workspace != nullptr), SSLP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     const sslp::SdmUpdateArgs a = update_args(s, dtype, residual_mode, idx_w, wt_w, idx_r, wt_r, v,
                                               alpha, beta, M, y, saved);
-    return hip_status(sslp::launch_sdm_update(a, (hipStream_t)stream), "sdm train update launch");
+    return hip_status(run_recurrence(a, s, workspace, (hipStream_t)stream),
+                      "sdm train update launch");
 }
 
 int sdm_forward_train(const sslp_sdm_shape* s, int dtype, int residual_mode, const void* sw1,
                       const void* sw2, const void* sr1, const void* sr2, const void* v,
                       const float* alpha, const float* beta, float* M, void* y, int32_t* idx_w,
-                      float* wt_w, int32_t* idx_r, float* wt_r, float* saved, void* stream) {
+                      float* wt_w, int32_t* idx_r, float* wt_r, float* saved, void* workspace,
+                      size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     if (int rc = check_common(s, true, dtype, residual_mode)) return rc;
     REQUIRE_PTR(M);
+    REQUIRE_ALIGNED(workspace);
     if (s->T == 0) return SSLP_OK;
     REQUIRE_PTR(sw1);
     REQUIRE_PTR(sw2);
@@ -526,6 +539,9 @@ int sdm_forward_train(const sslp_sdm_shape* s, int dtype, int residual_mode, con
     REQUIRE_PTR(idx_r);
     REQUIRE_PTR(wt_r);
     REQUIRE_PTR(saved);
+    const size_t need = sdm_train_workspace_size(s);
+    REQUIRE(ws_bytes >= need && (need == 0 || workspace != nullptr), SSLP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     const long long P = (long long)s->B * s->T * s->H;
     REQUIRE(P < (1ll << 31), SSLP_ERR_UNSUPPORTED, "too many problems");
     hipStream_t st = (hipStream_t)stream;
@@ -536,7 +552,7 @@ int sdm_forward_train(const sslp_sdm_shape* s, int dtype, int residual_mode, con
         return rc;
     const sslp::SdmUpdateArgs a = update_args(s, dtype, residual_mode, idx_w, wt_w, idx_r, wt_r, v,
                                               alpha, beta, M, y, saved);
-    return hip_status(sslp::launch_sdm_update(a, st), "sdm train update launch");
+    return hip_status(run_recurrence(a, s, workspace, st), "sdm train update launch");
 }
 
 int sdm_backward(const sslp_sdm_shape* s, int dtype, int residual_mode, const int32_t* idx_w,

@@ -20,21 +20,27 @@
 //   A[t][tau] = sum over slots written by both: alpha_t w_ti P(n, (tau,t)) beta_tau w_tau,n;
 //   per-slot form: res_t = v_t (A = 0, c = 0), the per-slot factor lives in d.
 //   reads  y_t = sum_k e_tk M0[m_tk] + sum_{tau<=t} Bm[t][tau] res_tau
-//   final  M_C[s] = P(s, all) M0[s] + sum_visits P(s, (tau, end]) beta_tau w res_tau.
+//   final  M_C[s] = P(s, all) M0[s] + sum_visits P(s, (tau, end]) beta_tau w res_tau,
+//          formed at the slot's last visit by carrying M0[s] through its visits
+//          in order (row <- d row + beta_tau w res_tau), which passes every
+//          visit's pre-write row M_{tau-1}[s] on the way (kept for the backward
+//          by undoing writes when the caller asks for them).
 // A plan kernel derives, per (b, h, chunk), everything that does not depend on
-// the table (row offsets, c, e, T = (I + A)^-1, Bm, per-slot final
-// coefficients, and which rows of the NEXT chunk hold a slot this chunk
-// writes); the apply kernel then streams the table: one workgroup per 8-column
-// slice of a head gathers the chunk's C x (W + R) = 1024 rows with LDS-DMA
-// (global_load_lds_dwordx4), forms g, h, res = T (v - g), y = h + Bm res,
-// and writes every written slot once with its final value.
+// the table (row offsets, c, e, T = (I + A)^-1, Bm, each visit's decay and
+// beta w, the visit order of every slot, and which rows of the NEXT chunk hold
+// a slot this chunk writes); the apply kernel then streams the table: one
+// workgroup per 8-column slice of a head gathers the chunk's C x (W + R) =
+// 1024 rows with LDS-DMA (global_load_lds_dwordx4), forms g, h,
+// res = T (v - g), y = h + Bm res, and writes every written slot once with its
+// final value.
 //
 // Pipelining: the rows of chunk c+1 are DMA'd while chunk c is computed, i.e.
 // before chunk c's write-back; rows of chunk c+1 that chunk c writes are then
 // overwritten in LDS with their final values (the plan lists them), after the
 // DMA has landed.  Rows written by earlier chunks were stored before the DMA
-// was issued, by the same wavefront, whose vector memory operations are
-// performed in order.
+// was issued: every wavefront waits for its stores to complete before the
+// barrier that ends a chunk step, and the DMAs of chunk c+2 are issued after
+// it.
 #include <type_traits>
 #include <utility>
 
@@ -57,10 +63,12 @@ constexpr int JW = 32 / NWAVE;       // row DMAs per wavefront and chunk (32 per
 constexpr int PL_TAIL = 4096;
 constexpr int PL_TAILWIN = 2048;
 constexpr int PL_DMA_WORDS = PL_TAIL + PL_TAILWIN;  // 24 KB staged per chunk
-constexpr int PL_WORDS = PL_TAIL + 2 * NE + 2 * NE + 2 * NE;  // worst-case tail
+constexpr int PL_WORDS = PL_TAIL + 2 * NE + 3 * NE + 2 * NE;  // worst-case tail
 static_assert((PL_DMA_WORDS * 4) % 1024 == 0 && (PL_WORDS * 4) % 16 == 0, "plan DMA pieces");
 // exception record: (first, packed); packed = extra index (9 bits) | extra count << 9
-// (5 bits) | forward index << 14 (10 bits) | forward count << 24 (6 bits)
+// (5 bits) | forward index << 14 (10 bits) | forward count << 24 (6 bits).
+// extra record (one per earlier visit of a slot, in visit order): (token | row << 8,
+// decay d of the visit, beta w of the visit)
 
 // Chunk geometry: CC_ tokens per chunk, NW_ write rows and as many read rows
 // per token.  Both configurations (16 x 32 and 8 x 64) have 512 write entries
@@ -82,9 +90,10 @@ struct Geo {
     static constexpr int PL_COEF = PL_OFFS + 32 * OFFS_LD;     // [t][q]: c (q < NW) or e (q >= NW)
     static constexpr int PL_TM = PL_COEF + CC * COEF_LD;       // [t][tau]: (I + A)^-1
     static constexpr int PL_BM = PL_TM + CC * TB_LD;           // [t][tau]
-    static constexpr int PL_FIN = PL_BM + CC * TB_LD;          // [i][t][2]: P, f of write entry (t, i)
+    static constexpr int PL_FIN = PL_BM + CC * TB_LD;          // [i][t][2]: decay d, beta w of write entry (t, i)
     static constexpr int PL_LAST = PL_FIN + NE * 2;            // [t][NMW] bit i: entry (t, i) is its slot's last visit
-    static constexpr int PL_EXC = PL_LAST + CC * NMW;          // [t][NMW] bit i: entry (t, i) has an exception record
+    static constexpr int PL_FIRST = PL_LAST + CC * NMW;        // [t][NMW] bit i: entry (t, i) is its slot's first visit
+    static constexpr int PL_EXC = PL_FIRST + CC * NMW;         // [t][NMW] bit i: entry (t, i) has an exception record
     static constexpr int PL_EXCB = PL_EXC + CC * NMW;          // [t] index of token t's first exception record
     static constexpr int PL_HDR = PL_EXCB + CC;                // tail offsets of the extra pairs and forward rows
     static_assert(CC * NW == NE && CC * NQ == 2 * NE && 32 % CC == 0 && NW % 32 == 0, "chunk geometry");
@@ -122,7 +131,8 @@ struct PlanArgs {
 template <class G>
 __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     constexpr int CC = G::CC, NW = G::NW, NR = G::NR, NQ = G::NQ, LOGNW = G::LOGNW;
-    constexpr int PL_LAST = G::PL_LAST, PL_EXC = G::PL_EXC, PL_EXCB = G::PL_EXCB, PL_HDR = G::PL_HDR;
+    constexpr int PL_LAST = G::PL_LAST, PL_FIRST = G::PL_FIRST, PL_EXC = G::PL_EXC, PL_EXCB = G::PL_EXCB,
+                  PL_HDR = G::PL_HDR;
     constexpr int PL_FIN = G::PL_FIN, PL_BM = G::PL_BM, PL_TM = G::PL_TM, TB_LD = G::TB_LD;
     __shared__ uint64_t key[NE];       // write entries sorted by (slot, token, rank)
     __shared__ float s_d[NE];          // decay of the visit at sorted position p
@@ -137,11 +147,11 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     __shared__ float s_A[CC][CC + 1];
     __shared__ int s_fcnt[NE], s_fbeg[NE], s_ffill[NE];
     __shared__ int s_fwdl[2 * NE];                      // forward rows, grouped per slot
-    __shared__ float s_P[NE], s_f[NE];                  // by entry
+    __shared__ float s_P[NE], s_f[NE];                  // decay and beta w, by entry
     __shared__ uint32_t s_first[NE], s_pk[NE];          // by entry (exception data)
     __shared__ int s_exc[NE];                           // exception flags, then their prefix count
-    __shared__ uint32_t s_xt[NE];                       // extra pairs (tau, f), by extra index
-    __shared__ float s_xf[NE];
+    __shared__ uint32_t s_xt[NE];                       // extra records, by extra index
+    __shared__ float s_xd[NE], s_xb[NE];
 
     const int tid = threadIdx.x;
     const int nch = a.nch;
@@ -320,7 +330,9 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         }
     }
 
-    // S6: per write entry: gather coefficient, final-value data at the last visit
+    // S6: per write entry: gather coefficient, the visit's decay and beta w; at a
+    // slot's last visit, its earlier visits in order (the final value and the
+    // pre-write rows follow them as a chain from the chunk-start row)
     for (int e = tid; e < NE; e += 256) {
         const int t = e >> LOGNW, i = e & (NW - 1);
         s_P[e] = 0.f;
@@ -334,22 +346,20 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         }
         const int p = s_pos[e];
         const int gs = s_gs[p], ge = s_ge[p];
-        float pre = 1.f, post = 1.f;
+        float pre = 1.f;
         for (int l = gs; l < p; ++l) pre *= s_d[l];
-        for (int l = p + 1; l < ge; ++l) post *= s_d[l];
         const float w = s_ww[e];
         out[G::coef_word(t, i)] = __float_as_uint(a.mode == 0 ? s_al[t] * w * pre : 0.f);
+        s_P[e] = s_d[p];
+        s_f[e] = s_be[t] * w;
         if (p != ge - 1) continue;  // the slot is written once, at its last visit
-        s_P[e] = pre * s_d[p];
-        s_f[e] = post * s_be[t] * w;
         const int xstart = gs - (s_scan[gs] - 1);  // earlier visits of earlier groups
         const int xcnt = ge - gs - 1;
-        float suf = 1.f;  // product of decays after visit l
-        for (int l = ge - 2; l >= gs; --l) {
-            suf *= s_d[l + 1];
+        for (int l = gs; l < ge - 1; ++l) {
             const int el = (int)(key[l] & 511u);
-            s_xt[xstart + (l - gs)] = (uint32_t)(el >> LOGNW);
-            s_xf[xstart + (l - gs)] = suf * s_be[el >> LOGNW] * s_ww[el];
+            s_xt[xstart + (l - gs)] = (uint32_t)(el >> LOGNW) | ((uint32_t)(el & (NW - 1)) << 8);
+            s_xd[xstart + (l - gs)] = s_d[l];
+            s_xb[xstart + (l - gs)] = s_be[el >> LOGNW] * s_ww[el];
         }
         const int fcnt = s_fcnt[p], fbeg = s_fbeg[p] - fcnt;
         if (xcnt > 0 || fcnt > 0) {
@@ -361,17 +371,19 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         }
     }
     __syncthreads();
-    // token masks of last visits and exception records, word wd of token t
-    // covering entries (t, 32 wd + i)
+    // token masks of last and first visits and of exception records, word wd of
+    // token t covering entries (t, 32 wd + i)
     if (tid < CC * G::NMW) {
         const int t = tid / G::NMW, wd = tid % G::NMW;
-        uint32_t lm = 0u, em = 0u;
+        uint32_t lm = 0u, fm = 0u, em = 0u;
         for (int i = 0; i < 32 && t < ntok; ++i) {
             const int e = t * NW + 32 * wd + i, p = s_pos[e];
             lm |= (s_ge[p] - 1 == p) ? (1u << i) : 0u;
+            fm |= (s_gs[p] == p) ? (1u << i) : 0u;
             em |= s_exc[e] ? (1u << i) : 0u;
         }
         out[PL_LAST + tid] = lm;
+        out[PL_FIRST + tid] = fm;
         out[PL_EXC + tid] = em;
     }
     __syncthreads();
@@ -389,7 +401,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         const int n_exc = s_exc[NE - 1];
         const int extra_base = 2 * n_exc;
         const int nxp = ntok * NW - s_scan[NE - 1];  // valid entries - slot groups = extra pairs
-        const int fwd_base = extra_base + 2 * nxp;
+        const int fwd_base = extra_base + 3 * nxp;
         const int n_fwd = s_fbeg[NE - 1];
         if (tid == 0) {
             out[PL_HDR + 0] = (uint32_t)extra_base;
@@ -409,8 +421,9 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
             }
         }
         for (int x = tid; x < nxp; x += 256) {
-            out[PL_TAIL + extra_base + 2 * x + 0] = s_xt[x];
-            out[PL_TAIL + extra_base + 2 * x + 1] = __float_as_uint(s_xf[x]);
+            out[PL_TAIL + extra_base + 3 * x + 0] = s_xt[x];
+            out[PL_TAIL + extra_base + 3 * x + 1] = __float_as_uint(s_xd[x]);
+            out[PL_TAIL + extra_base + 3 * x + 2] = __float_as_uint(s_xb[x]);
         }
         for (int x = tid; x < n_fwd; x += 256) out[PL_TAIL + fwd_base + x] = (uint32_t)s_fwdl[x];
     }
@@ -628,7 +641,7 @@ SSLP_DEVICE void static_for(F&& f) {
 // among them (j < 16).  Several wavefronts per CU keep that many times more
 // gathers in flight than one, and split the compute.
 // ---------------------------------------------------------------------------
-template <typename io_t, class G>
+template <typename io_t, class G, bool SAVE>
 __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateArgs a,
                                                                      const uint32_t* __restrict__ plan,
                                                                      int nslice, int total, int nch) {
@@ -882,7 +895,10 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
 
         // ---- write-back of this wave's write rows (j = wave + NWAVE m < 16): each
         //      written slot once, at its last visit; entries with an exception
-        //      record were visited earlier in the chunk or feed the next chunk ----
+        //      record were visited earlier in the chunk or feed the next chunk.
+        //      With SAVE (a.saved set), every write entry's pre-write row too: a
+        //      first visit stores the chunk-start row, a last visit the rows of
+        //      the later visits, as it walks the slot's visits in order ----
         const bool wb_ok = dt < ntok;
         const uint32_t* tailg = planb + (size_t)c * PL_WORDS + PL_TAIL;
         auto tail = [&](uint32_t k) -> uint32_t {  // tail word k (LDS window, else memory)
@@ -897,9 +913,10 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
         f32x4 rj = lds_f32x4(xs0 + (uint32_t)((dt * CW + 4 * dh) * 4));
         u32x4 offv = lds_u32x4(P + offs_lane);
         u32x4 hdr = lds_u32x4(P + 4u * G::PL_HDR);
-        uint32_t lmw[NMW], emw[NMW];
+        uint32_t lmw[NMW], fmw[NMW], emw[NMW];
         static_for<NMW>([&](auto k) {
             lmw[k] = lds_u32(P + 4u * (uint32_t)(G::PL_LAST + dt * NMW + k));
+            fmw[k] = SAVE ? lds_u32(P + 4u * (uint32_t)(G::PL_FIRST + dt * NMW + k)) : 0u;
             emw[k] = lds_u32(P + 4u * (uint32_t)(G::PL_EXC + dt * NMW + k));
         });
         uint32_t eb = lds_u32(P + 4u * (uint32_t)(G::PL_EXCB + dt));
@@ -913,14 +930,21 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
         });
         lds_wait(rj, offv, hdr, eb);
         tie_all(lmw);
+        tie_all(fmw);
         tie_all(emw);
         tie_all(pf);
         tie_all(m0);
-        mask_t lm = lmw[0], em = emw[0];
+        mask_t lm = lmw[0], fm = fmw[0], em = emw[0];
         if constexpr (NMW == 2) {
             lm |= (mask_t)lmw[NMW - 1] << 32;
+            fm |= (mask_t)fmw[NMW - 1] << 32;
             em |= (mask_t)emw[NMW - 1] << 32;
         }
+        // this lane's 16 bytes of the pre-write row of write entry (tok, row)
+        auto saved_at = [&](uint32_t tok, uint32_t row) -> f32x4* {
+            return reinterpret_cast<f32x4*>(
+                a.saved + ((((size_t)b * T + c * CC + tok) * H + h) * G::NW + row) * dv + col0 + 4 * dh);
+        };
         const uint32_t extra_base = hdr.x, fwd_base = hdr.y;
         bool any_fwd = false;
         f32x4 keep[WB];
@@ -930,9 +954,11 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
             const uint32_t q = q0 + RPD * NWAVE * m;
             kpk[m] = 0u;
             keep[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (!wb_ok || !((lm >> q) & 1u)) continue;
+            if (!wb_ok) continue;
             f32x4 mv = m0[m];
-            const float Pv = pf[m].x, f = pf[m].y;
+            if (SAVE && ((fm >> q) & 1u)) *saved_at(dt, q) = mv;
+            if (!((lm >> q) & 1u)) continue;
+            const float dec = pf[m].x, bw = pf[m].y;  // this visit's decay and beta w
             uint32_t pk = 0u;
             if ((em >> q) & 1u) {
                 const uint32_t k = eb + (uint32_t)__builtin_popcountll((uint64_t)(em & (((mask_t)1 << q) - 1u)));
@@ -943,22 +969,28 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_apply_kernel(SdmUpdateAr
                     lds_wait(mv);
                 }
             }
-            f32x4 val;
-            val.x = fmaf(f, rj.x, Pv * mv.x);
-            val.y = fmaf(f, rj.y, Pv * mv.y);
-            val.z = fmaf(f, rj.z, Pv * mv.z);
-            val.w = fmaf(f, rj.w, Pv * mv.w);
+            // the slot's earlier visits in order: the row before each is the
+            // chunk-start row carried through the visits before it
             const uint32_t xst = pk & 511u, xcnt = (pk >> 9) & 31u;
             for (uint32_t x = 0; x < xcnt; ++x) {
-                const uint32_t tau = tail(extra_base + 2 * (xst + x));
-                const float fx = __uint_as_float(tail(extra_base + 2 * (xst + x) + 1));
+                const uint32_t tr = tail(extra_base + 3 * (xst + x));
+                const float dx = __uint_as_float(tail(extra_base + 3 * (xst + x) + 1));
+                const float bx = __uint_as_float(tail(extra_base + 3 * (xst + x) + 2));
+                const uint32_t tau = tr & 255u;
+                if (SAVE && x > 0) *saved_at(tau, tr >> 8) = mv;
                 f32x4 rt = lds_f32x4(xs0 + (tau * CW + 4 * dh) * 4);
                 lds_wait(rt);
-                val.x = fmaf(fx, rt.x, val.x);
-                val.y = fmaf(fx, rt.y, val.y);
-                val.z = fmaf(fx, rt.z, val.z);
-                val.w = fmaf(fx, rt.w, val.w);
+                mv.x = fmaf(bx, rt.x, dx * mv.x);
+                mv.y = fmaf(bx, rt.y, dx * mv.y);
+                mv.z = fmaf(bx, rt.z, dx * mv.z);
+                mv.w = fmaf(bx, rt.w, dx * mv.w);
             }
+            if (SAVE && xcnt > 0) *saved_at(dt, q) = mv;
+            f32x4 val;
+            val.x = fmaf(bw, rj.x, dec * mv.x);
+            val.y = fmaf(bw, rj.y, dec * mv.y);
+            val.z = fmaf(bw, rj.z, dec * mv.z);
+            val.w = fmaf(bw, rj.w, dec * mv.w);
             *reinterpret_cast<f32x4*>(tabw + offv[m] + colbyte) = val;
             keep[m] = val;
             kpk[m] = pk;
@@ -1020,10 +1052,15 @@ hipError_t launch_chunked(const SdmUpdateArgs& a, uint32_t* plan, hipStream_t st
     const int nslice = a.dv / CW;
     const int total = a.B * a.H * nslice;
     const int grid = ((total + 127) / 128) * 128;
-    if (a.dtype != 0)
-        sdm_chunk_apply_kernel<bf16_t, G><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
+    const bool save = a.saved != nullptr;
+    if (a.dtype != 0 && save)
+        sdm_chunk_apply_kernel<bf16_t, G, true><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
+    else if (a.dtype != 0)
+        sdm_chunk_apply_kernel<bf16_t, G, false><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
+    else if (save)
+        sdm_chunk_apply_kernel<float, G, true><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
     else
-        sdm_chunk_apply_kernel<float, G><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
+        sdm_chunk_apply_kernel<float, G, false><<<grid, 64 * NWAVE, 0, st>>>(a, plan, nslice, total, nch);
     return hipGetLastError();
 }
 }  // namespace

@@ -91,7 +91,7 @@ def test_sdm_forward_workspace_and_flags():
 @pytest.mark.parametrize("W,k,chunk", [(32, 6, 16), (64, 8, 8), (40, 7, None)])
 def test_sdm_workspace_holds_the_chunk_plans(W, k, chunk):
     # W = R = 32 and W = R = 64 with T >= 64 take the chunk-parallel recurrence
-    # (chunks of 16 and 8 tokens), whose per-chunk plans (7168 words each) live
+    # (chunks of 16 and 8 tokens), whose per-chunk plans (7680 words each) live
     # in the workspace after the addressing; other shapes need the addressing only
     lib = _lib.lib()
 
@@ -101,7 +101,7 @@ def test_sdm_workspace_holds_the_chunk_plans(W, k, chunk):
     for T in (63, 100):
         s = _sdm(B=2, T=T, H=3, sqrtN=16, d_v=16, k_w=k, k_r=k, W=W, R=W)
         addressing = 4 * a256(2 * T * 3 * W * 4)
-        plans = 0 if chunk is None or T < 64 else a256(2 * 3 * -(-T // chunk) * 7168 * 4)
+        plans = 0 if chunk is None or T < 64 else a256(2 * 3 * -(-T // chunk) * 7680 * 4)
         assert lib.sdm_workspace_size(ctypes.byref(s)) == addressing + plans, (W, T)
 
 
@@ -118,13 +118,25 @@ def test_sdm_training_entry_errors():
     lib = _lib.lib()
     s = _sdm()
     # sdm_forward_train needs the addressing outputs and the saved rows
-    assert lib.sdm_forward_train(ctypes.byref(s), 0, 0, *([FAKE] * 13), None, None) == \
+    assert lib.sdm_forward_train(ctypes.byref(s), 0, 0, *([FAKE] * 13), None, None, 0, None) == \
         _lib.SSLP_ERR_INVALID_ARG
     assert "saved" in lib.sslp_last_error().decode()
     assert lib.sdm_forward_train(ctypes.byref(s), 0, 0, *([FAKE] * 9), None, *([FAKE] * 4),
-                                 None) == _lib.SSLP_ERR_INVALID_ARG
-    assert lib.sdm_sparse_update_train(ctypes.byref(s), 0, 3, *([FAKE] * 10), None) == \
+                                 None, 0, None) == _lib.SSLP_ERR_INVALID_ARG
+    assert lib.sdm_sparse_update_train(ctypes.byref(s), 0, 3, *([FAKE] * 10), None, 0, None) == \
         _lib.SSLP_ERR_INVALID_ARG
+    # a shape on the chunk-parallel path needs its plans: short or misaligned
+    # workspaces are refused before any launch
+    assert lib.sdm_train_workspace_size(ctypes.byref(s)) == 0  # per-token shape
+    c = _sdm(T=64, sqrtN=16, k_w=6, k_r=6, W=32, R=32)
+    need = lib.sdm_train_workspace_size(ctypes.byref(c))
+    assert need == 4 * 7680 * 4  # B = H = 1: 4 chunks of 7,680 words
+    assert lib.sdm_forward_train(ctypes.byref(c), 0, 0, *([FAKE] * 14), FAKE, need - 1, None) == \
+        _lib.SSLP_ERR_WORKSPACE
+    assert lib.sdm_sparse_update_train(ctypes.byref(c), 0, 0, *([FAKE] * 10), None, need,
+                                       None) == _lib.SSLP_ERR_WORKSPACE
+    assert lib.sdm_sparse_update_train(ctypes.byref(c), 0, 0, *([FAKE] * 10), MISALIGNED, need,
+                                       None) == _lib.SSLP_ERR_INVALID_ARG
     need = lib.sdm_backward_workspace_size(ctypes.byref(s))
     assert need > 0
     ptrs = [FAKE] * 20

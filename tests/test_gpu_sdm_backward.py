@@ -93,6 +93,55 @@ def test_sdm_train_budget_shapes():
     _check_full(_cfg(1, 20, 2, 16, 20, 8, 5, 48, torch.float32, 552), 1, TOL_FP32)
 
 
+CHUNK_TRAIN = [
+    # B, T, H, sqrtN, d_v, k, W = R, dtype, mode: T >= 64 and W = R = 32 or 64, so
+    # the training forward runs chunk-parallel (16- or 8-token chunks).  Tables
+    # of 144 and 400 slots: most slots are visited by several tokens of a chunk,
+    # so later visits' pre-write rows come from the walk over the slot's visits
+    (1, 100, 2, 12, 24, 8, 32, "f32", 0),
+    (2, 67, 1, 12, 16, 8, 32, "f32", 1),
+    (1, 72, 2, 12, 24, 8, 64, "f32", 0),
+    (1, 81, 1, 20, 32, 10, 64, "f32", 1),
+    (1, 80, 2, 20, 40, 8, 32, "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_TRAIN)
+def test_sdm_train_chunk_path(case):
+    import sparse_state_linear_product_amd as sslp
+    B, T, H, sq, dv, k, W, dt, mode = case
+    dtype = torch.float32 if dt == "f32" else torch.bfloat16
+    cfg = _cfg(B, T, H, sq, dv, k, W, W, dtype, 610 + sum(case[:7]) + mode)
+    announce(f"sdm_forward_train chunk path {case}")
+    tol = TOL_FP32 if dt == "f32" else TOL_BF16
+    # gradients, the forward read and the restored table
+    _check_full(cfg, mode, tol)
+    # the pre-write rows against the oracle's table after each prefix
+    x = wl.sdm_inputs(cfg)
+    _, _, M0 = _upstream(cfg, T, cfg.seed + 1)
+    xd = {kk: v.to(DEV) for kk, v in x.items()}
+    M = M0.clone().to(DEV)
+    _, ctx = sslp.sdm_forward_train(xd["sw1"], xd["sw2"], xd["sr1"], xd["sr2"], xd["v"],
+                                    xd["alpha"], xd["beta"], M, cfg.k_w, cfg.k_r, cfg.W, cfg.R,
+                                    residual_mode=mode)
+    torch.cuda.synchronize()
+    saved = ctx["saved"].cpu().double().numpy()
+    n = {kk: wl.to_numpy_f32(v) for kk, v in x.items()}
+    iw, ww = oracle.sdm_address(n["sw1"], n["sw2"], cfg.k_w, cfg.W)
+    ir, wr = oracle.sdm_address(n["sr1"], n["sr2"], cfg.k_r, cfg.R)
+    ref = np.empty_like(saved)
+    for t in range(T):
+        Mt, _ = oracle.sdm_recurrence(iw[:, :t], ww[:, :t], ir[:, :t], wr[:, :t], n["v"][:, :t],
+                                      n["alpha"][:, :t], n["beta"][:, :t], M0.double().numpy(),
+                                      residual_mode=mode)
+        for b in range(B):
+            for h in range(H):
+                ref[b, t, h] = Mt[b, h, iw[b, t, h]]
+    e = maxrel(saved, ref, name="saved")
+    print(f"  saved: {e:.2e}", flush=True)
+    assert e <= TOL_FP32, f"saved rows: {e}"
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 def test_sdm_recurrence_backward_signed_weights(mode):
     # the recurrence alone with raw signed weights and distinct slots, read and
