@@ -476,11 +476,26 @@ static int check_common(const sslp_sdm_shape* s, bool need_k, int dtype, int res
     return SSLP_OK;
 }
 
+// the backward runs chunk-parallel where the forward does
+bool backward_chunked(const sslp_sdm_shape* s) {
+    return sslp::sdm_chunked_supported(s->B, s->T, s->H, s->W, s->R, s->d_v, slots(s));
+}
+
+// workspace of sdm_backward: slice partial sums | weight gradients the caller
+// does not keep | (chunk-parallel) forward plans | backward plans
+size_t bwd_part_bytes(const sslp_sdm_shape* s) {
+    const int cols = backward_chunked(s) ? sslp::kChunkBwdSliceCols : 16;
+    return align_up(sslp::sdm_bwd_part_bytes(s->B, s->T, s->H, s->d_v, s->W, s->R, cols));
+}
+
 size_t sdm_backward_workspace_size(const sslp_sdm_shape* s) {
     if (check_sdm_shape(s, false) != SSLP_OK) return 0;
     const size_t bth = (size_t)s->B * s->T * s->H;
-    return align_up(sslp::sdm_bwd_part_bytes(s->B, s->T, s->H, s->d_v, s->W, s->R)) +
-           align_up(bth * s->W * 4) + align_up(bth * s->R * 4);
+    size_t n = bwd_part_bytes(s) + align_up(bth * s->W * 4) + align_up(bth * s->R * 4);
+    if (backward_chunked(s))
+        n += align_up(sslp::sdm_chunk_plan_bytes(s->B, s->T, s->H, s->W)) +
+             align_up(sslp::sdm_chunk_bwd_plan_bytes(s->B, s->T, s->H, s->W));
+    return n;
 }
 
 size_t sdm_train_workspace_size(const sslp_sdm_shape* s) {
@@ -593,8 +608,9 @@ int sdm_backward(const sslp_sdm_shape* s, int dtype, int residual_mode, const in
     const long long P = (long long)s->B * s->T * s->H;
     REQUIRE(P < (1ll << 31), SSLP_ERR_UNSUPPORTED, "too many problems");
     char* ws = static_cast<char*>(workspace);
-    const size_t bp = align_up(sslp::sdm_bwd_part_bytes(s->B, s->T, s->H, s->d_v, s->W, s->R));
+    const size_t bp = bwd_part_bytes(s);
     const size_t bw = align_up((size_t)P * s->W * 4);
+    const size_t br = align_up((size_t)P * s->R * 4);
     sslp::SdmBwdArgs a{};
     a.B = s->B;
     a.T = s->T;
@@ -624,8 +640,15 @@ int sdm_backward(const sslp_sdm_shape* s, int dtype, int residual_mode, const in
     a.dwt_r = dwt_r ? dwt_r : reinterpret_cast<float*>(ws + bp + bw);
     a.err = error_word();
     hipStream_t st = (hipStream_t)stream;
-    if (int rc = hip_status(sslp::launch_sdm_update_backward(a, st), "sdm backward launch"))
+    if (backward_chunked(s)) {
+        char* fplan = ws + bp + bw + br;
+        char* bplan = fplan + align_up(sslp::sdm_chunk_plan_bytes(s->B, s->T, s->H, s->W));
+        if (int rc = hip_status(sslp::launch_sdm_backward_chunked(a, fplan, bplan, st),
+                                "sdm backward launch"))
+            return rc;
+    } else if (int rc = hip_status(sslp::launch_sdm_update_backward(a, st), "sdm backward launch")) {
         return rc;
+    }
     if (dsw1)
         if (int rc = hip_status(sslp::launch_sdm_address_backward((int)P, s->sqrtN, s->W, idx_w,
                                                                   wt_w, a.dwt_w, dsw1, dsw2, st),

@@ -89,7 +89,11 @@ struct SdmBwdArgs {
     float* dwt_r;        // [B,T,H,R]
     unsigned* err;       // as SdmUpdateArgs::err
 };
-size_t sdm_bwd_part_bytes(int B, int T, int H, int dv, int W, int R);
+// per-token partial sums of the scalar gradients, one set per slice of
+// slice_cols columns of d_v, and their sum over the slices (in slice order)
+size_t sdm_bwd_part_bytes(int B, int T, int H, int dv, int W, int R, int slice_cols);
+hipError_t launch_sdm_bwd_reduce(const SdmBwdArgs& a, int slice_cols, hipStream_t st);
+// per-token reverse sweep (16-column slices) + the reduction
 hipError_t launch_sdm_update_backward(const SdmBwdArgs& a, hipStream_t st);
 // gradient of the addressing softmax onto the score halves, P problems
 hipError_t launch_sdm_address_backward(int P, int sqrtN, int budget, const int32_t* idx,
@@ -101,6 +105,15 @@ hipError_t launch_sdm_address_backward(int P, int sqrtN, int budget, const int32
 bool sdm_chunked_supported(int B, int T, int H, int W, int R, int dv, long long N);
 size_t sdm_chunk_plan_bytes(int B, int T, int H, int W);
 hipError_t launch_sdm_update_chunked(const SdmUpdateArgs& a, void* plan, hipStream_t st);
+// the plan kernel alone (the backward reuses the forward's plans)
+hipError_t launch_sdm_chunk_plans(const SdmUpdateArgs& a, void* plan, hipStream_t st);
+// chunk-parallel backward (sdm_chunk_bwd.hip), same shapes as the forward:
+// its own per-chunk plans, and the launcher (forward plans, backward plans,
+// the reverse sweep over chunks with 8-column slices, the slice reduction)
+size_t sdm_chunk_bwd_plan_bytes(int B, int T, int H, int W);
+constexpr int kChunkBwdSliceCols = 8;
+hipError_t launch_sdm_backward_chunked(const SdmBwdArgs& a, void* fplan, void* bplan,
+                                       hipStream_t st);
 
 // RMS-Norm and output gate after the read (norm_gate.hip): rows x d, act 0 none,
 // 1 SiLU, 2 sigmoid; d a multiple of 4 up to 4096; o may alias y

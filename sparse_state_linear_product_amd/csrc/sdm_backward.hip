@@ -231,11 +231,11 @@ __global__ __launch_bounds__(64) void sdm_update_bwd_kernel(SdmBwdArgs a) {
 }
 
 // Adds the slices' partial sums in slice order: one thread per (token, head, j).
-__global__ __launch_bounds__(256) void sdm_bwd_reduce_kernel(SdmBwdArgs a, long long total) {
+__global__ __launch_bounds__(256) void sdm_bwd_reduce_kernel(SdmBwdArgs a, long long total,
+                                                             int nslice) {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
     const int W = a.W, R = a.R, NP = 2 + W + R;
-    const int nslice = nslices(a.dv);
     const long long bth = i / NP;
     const int j = (int)(i - bth * NP);
     const float* pp = a.part + (size_t)bth * nslice * NP + j;
@@ -305,8 +305,15 @@ hipError_t dispatch_bwd(int NL, dim3 grid, hipStream_t st, const SdmBwdArgs& a) 
 
 }  // namespace
 
-size_t sdm_bwd_part_bytes(int B, int T, int H, int dv, int W, int R) {
-    return (size_t)B * T * H * ((dv + kCols - 1) / kCols) * (2 + W + R) * sizeof(float);
+size_t sdm_bwd_part_bytes(int B, int T, int H, int dv, int W, int R, int slice_cols) {
+    return (size_t)B * T * H * ((dv + slice_cols - 1) / slice_cols) * (2 + W + R) * sizeof(float);
+}
+
+hipError_t launch_sdm_bwd_reduce(const SdmBwdArgs& a, int slice_cols, hipStream_t st) {
+    const long long total = (long long)a.B * a.T * a.H * (2 + a.W + a.R);
+    const int nslice = (a.dv + slice_cols - 1) / slice_cols;
+    sdm_bwd_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a, total, nslice);
+    return hipGetLastError();
 }
 
 hipError_t launch_sdm_update_backward(const SdmBwdArgs& a, hipStream_t st) {
@@ -319,9 +326,7 @@ hipError_t launch_sdm_update_backward(const SdmBwdArgs& a, hipStream_t st) {
     hipError_t e = a.dtype == 0 ? dispatch_bwd<float>(NL, grid, st, a)
                                 : dispatch_bwd<bf16_t>(NL, grid, st, a);
     if (e != hipSuccess) return e;
-    const long long total = (long long)a.B * a.T * a.H * (2 + a.W + a.R);
-    sdm_bwd_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a, total);
-    return hipGetLastError();
+    return launch_sdm_bwd_reduce(a, kCols, st);
 }
 
 hipError_t launch_sdm_address_backward(int P, int sqrtN, int budget, const int32_t* idx,
