@@ -21,7 +21,7 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-CHECKED = ["sdm_chunk.hip", "gdn_chunk.hip"]
+CHECKED = ["sdm_chunk.hip", "sdm_chunk_bwd.hip", "gdn_chunk.hip"]
 
 _VREG = re.compile(r"\b([va])(\d+)\b|\b([va])\[(\d+):(\d+)\]")
 _LABEL = re.compile(r"^(\.?L?BB[\w.]+|\.LBB[\w.]+):")

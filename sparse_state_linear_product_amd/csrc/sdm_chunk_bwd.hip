@@ -216,6 +216,21 @@ __global__ __launch_bounds__(256) void sdm_chunk_bwd_plan_kernel(BwdPlanArgs a) 
 // ---------------------------------------------------------------------------
 // sweep kernel helpers
 // ---------------------------------------------------------------------------
+// The next chunk's plans and inputs are loaded a chunk ahead with loads written
+// as inline assembly, so that the compiler cannot sink them down to the LDS
+// stores that consume them at the end of the step; the compiler does not track
+// their completion, so that consumer waits for them explicitly, with every
+// register they fill tied to the wait.
+SSLP_DEVICE u32x4 pinned_load16(const void* p) {
+    u32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
+SSLP_DEVICE uint32_t pinned_load4(const void* p) {
+    uint32_t v;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
 SSLP_DEVICE float dot4(f32x4 x, f32x4 y) {
     return fmaf(x.w, y.w, fmaf(x.z, y.z, fmaf(x.y, y.y, x.x * y.x)));
 }
@@ -237,18 +252,28 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
     constexpr int CC = G::CC, NW = G::NW, NR = G::NR, NQ = G::NQ, RPD = G::RPD;
     constexpr int LPT = 64 / CC;   // compute lanes per token
     constexpr int CPL = CW / LPT;  // columns per compute lane
-    constexpr int FPW = G::PL_FIN; // forward-plan words used: offsets, coefficients, T, Bm
+    // forward-plan words kept per chunk: the row offsets, then T and Bm
+    constexpr int FOFF = 32 * G::OFFS_LD, FTM = FOFF, FBM = FOFF + CC * G::TB_LD;
+    constexpr int FPC = FOFF + 2 * CC * G::TB_LD;
     constexpr int NP = 2 + NW + NR;
-    static_assert(FPW % 4 == 0 && JW == 4 && NW % NWAVE == 0, "sweep layout");
+    constexpr int DWT = CW * (int)sizeof(io_t) / 4;  // dwords of a token's dy (or v) slice
+    static_assert(FPC % 4 == 0 && FPC / 4 <= 64 * NWAVE && FOFF <= G::PL_COEF &&
+                      G::PL_BM == G::PL_TM + CC * G::TB_LD && G::PL_TM % 4 == 0,
+                  "forward-plan copy");
+    static_assert(BPL_WORDS / 4 <= 2 * 64 * NWAVE && NE == 64 * NWAVE && CC * DWT <= 64 * NWAVE,
+                  "one chunk's prefetch: two plan pieces, one weight of each kind per thread");
+    static_assert(JW == 4 && NW % NWAVE == 0, "sweep layout");
 
     __shared__ __align__(16) float gst[NQ * CC][CW];  // gradient-table rows of every entry
     __shared__ __align__(16) float mst[NR * CC][CW];  // table rows of the read entries
     __shared__ __align__(16) float pst[NW * CC][CW];  // pre-write rows of the write entries
-    __shared__ __align__(16) uint32_t fpl[FPW];
-    __shared__ __align__(16) uint32_t bpl[BPL_WORDS];
-    __shared__ float s_w[NE], s_e[NE];  // write / read weights [t][i]
-    __shared__ float s_al[CC], s_be[CC];
-    __shared__ __align__(16) float s_dy[CC][CW], s_v[CC][CW], s_res[CC][CW], s_dr[CC][CW];
+    // plans and inputs, double-buffered by chunk parity
+    __shared__ __align__(16) uint32_t fpl[2][FPC];
+    __shared__ __align__(16) uint32_t bpl[2][BPL_WORDS];
+    __shared__ float s_w[2][NE], s_e[2][NE];  // write / read weights [t][i]
+    __shared__ float s_al[2][CC], s_be[2][CC];
+    __shared__ __align__(16) float s_dy[2][CC][CW], s_v[2][CC][CW];
+    __shared__ __align__(16) float s_res[CC][CW], s_dr[CC][CW];
     __shared__ __align__(16) float s_s[CC][CW];
     __shared__ __align__(16) float part[NWAVE][2][CC][CW];
     __shared__ float s_pa[NE][2], s_pb[NE][2], s_pw[NE][2], s_pe[NE][2];
@@ -281,43 +306,87 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
     const int ct = lane / LPT, qt = lane % LPT;
     const uint32_t row_end = (uint32_t)a.N * (uint32_t)dv * 4u;  // < 2^31 on this path
 
+    // one chunk's plans and inputs: loaded by every thread (clamped, always
+    // valid addresses), kept by the threads that own a piece
+    struct Pref {
+        u32x4 f, b0, b1;
+        uint32_t w, e, al, be, dy, v;
+    };
+    auto prefetch = [&](int cn, Pref& r) {
+        const int t0n = cn * CC;
+        const int ntn = T - t0n < CC ? T - t0n : CC;
+        const uint32_t* fp = fplan + ((size_t)bh * nch + cn) * PL_WORDS;
+        const uint32_t* bp = bplan + ((size_t)bh * nch + cn) * BPL_WORDS;
+        const int u = tid < FPC / 4 ? tid : FPC / 4 - 1;
+        r.f = pinned_load16(u < FOFF / 4 ? fp + 4 * u : fp + G::PL_TM + 4 * (u - FOFF / 4));
+        r.b0 = pinned_load16(bp + 4 * (tid < BPL_WORDS / 4 ? tid : BPL_WORDS / 4 - 1));
+        r.b1 = pinned_load16(bp + 4 * (tid + 64 * NWAVE < BPL_WORDS / 4 ? tid + 64 * NWAVE
+                                                                          : BPL_WORDS / 4 - 1));
+        const int te = tid / NW < ntn ? tid / NW : ntn - 1, ie = tid % NW;
+        const size_t bte = ((size_t)b * T + t0n + te) * H + h;
+        r.w = pinned_load4(a.wt_w + bte * NW + ie);
+        r.e = pinned_load4(a.wt_r + bte * NR + ie);
+        const size_t btg = ((size_t)b * T + t0n + (tid < ntn ? tid : ntn - 1)) * H + h;
+        r.al = pinned_load4(a.alpha + btg);
+        r.be = pinned_load4(a.beta + btg);
+        const int d = tid < CC * DWT ? tid : CC * DWT - 1;
+        const int td = d / DWT < ntn ? d / DWT : ntn - 1;
+        const size_t btd = ((size_t)b * T + t0n + td) * H + h;
+        r.dy = pinned_load4(reinterpret_cast<const uint32_t*>(dyin + btd * dv + col0) + d % DWT);
+        r.v = pinned_load4(reinterpret_cast<const uint32_t*>(vin + btd * dv + col0) + d % DWT);
+    };
+    auto commit = [&](int cn, Pref& r) {
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(r.f), "+v"(r.b0), "+v"(r.b1), "+v"(r.w), "+v"(r.e), "+v"(r.al),
+                       "+v"(r.be), "+v"(r.dy), "+v"(r.v)
+                     :
+                     : "memory");
+        const int nb = cn & 1;
+        const int ntn = T - cn * CC < CC ? T - cn * CC : CC;
+        if (tid < FPC / 4) *reinterpret_cast<u32x4*>(&fpl[nb][4 * tid]) = r.f;
+        if (tid < BPL_WORDS / 4) *reinterpret_cast<u32x4*>(&bpl[nb][4 * tid]) = r.b0;
+        if (tid + 64 * NWAVE < BPL_WORDS / 4)
+            *reinterpret_cast<u32x4*>(&bpl[nb][4 * (tid + 64 * NWAVE)]) = r.b1;
+        const bool okw = tid / NW < ntn;
+        s_w[nb][tid] = okw ? __uint_as_float(r.w) : 0.f;
+        s_e[nb][tid] = okw ? __uint_as_float(r.e) : 0.f;
+        if (tid < CC) {
+            s_al[nb][tid] = tid < ntn ? __uint_as_float(r.al) : 1.f;
+            s_be[nb][tid] = tid < ntn ? __uint_as_float(r.be) : 0.f;
+        }
+        if (tid < CC * DWT) {
+            const int t = tid / DWT, o = tid % DWT;
+            const bool ok = t < ntn;
+            if constexpr (sizeof(io_t) == 2) {
+                s_dy[nb][t][2 * o] = ok ? bf16lo(r.dy) : 0.f;
+                s_dy[nb][t][2 * o + 1] = ok ? bf16hi(r.dy) : 0.f;
+                s_v[nb][t][2 * o] = ok ? bf16lo(r.v) : 0.f;
+                s_v[nb][t][2 * o + 1] = ok ? bf16hi(r.v) : 0.f;
+            } else {
+                s_dy[nb][t][o] = ok ? __uint_as_float(r.dy) : 0.f;
+                s_v[nb][t][o] = ok ? __uint_as_float(r.v) : 0.f;
+            }
+        }
+    };
+    {
+        Pref r;
+        prefetch(nch - 1, r);
+        commit(nch - 1, r);
+        __syncthreads();
+    }
+
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * CC;
         const int ntok = T - t0 < CC ? T - t0 : CC;
-        const uint32_t* fp = fplan + ((size_t)bh * nch + c) * PL_WORDS;
-        const uint32_t* bp = bplan + ((size_t)bh * nch + c) * BPL_WORDS;
-
-        // ---- plans, weights, gates, dy and v of the chunk into LDS ----
-        for (int x = tid; x < FPW / 4; x += 64 * NWAVE)
-            reinterpret_cast<uint4*>(fpl)[x] = reinterpret_cast<const uint4*>(fp)[x];
-        for (int x = tid; x < BPL_WORDS / 4; x += 64 * NWAVE)
-            reinterpret_cast<uint4*>(bpl)[x] = reinterpret_cast<const uint4*>(bp)[x];
-        for (int e = tid; e < NE; e += 64 * NWAVE) {
-            const int t = e / NW, i = e - (e / NW) * NW;
-            const bool ok = t < ntok;
-            const size_t bth = ((size_t)b * T + t0 + (ok ? t : 0)) * H + h;
-            s_w[e] = ok ? a.wt_w[bth * NW + i] : 0.f;
-            s_e[e] = ok ? a.wt_r[bth * NR + i] : 0.f;
-        }
-        if (tid < CC) {
-            const bool ok = tid < ntok;
-            const size_t bth = ((size_t)b * T + t0 + (ok ? tid : 0)) * H + h;
-            s_al[tid] = ok ? a.alpha[bth] : 1.f;
-            s_be[tid] = ok ? a.beta[bth] : 0.f;
-        }
-        if (tid < CC * CW) {
-            const int t = tid / CW, cc = tid - (tid / CW) * CW;
-            const bool ok = t < ntok;
-            const size_t bth = ((size_t)b * T + t0 + (ok ? t : 0)) * H + h;
-            s_dy[t][cc] = ok ? to_f32(dyin[bth * dv + col0 + cc]) : 0.f;
-            s_v[t][cc] = ok ? to_f32(vin[bth * dv + col0 + cc]) : 0.f;
-        }
-        __syncthreads();
+        const int cb = c & 1;
+        // the earlier chunk's plans and inputs, in flight during this step
+        Pref pre;
+        if (c > 0) prefetch(c - 1, pre);
 
         // ---- row DMAs: gradient rows of all entries, table rows of the reads
         //      (DMAs j >= 16), pre-write rows of the writes (DMAs j < 16) ----
         {
-            const uint32_t* ow = fpl + G::PL_OFFS + (lane >> 1) * G::OFFS_LD + wave * JW;
+            const uint32_t* ow = &fpl[cb][G::PL_OFFS + (lane >> 1) * G::OFFS_LD + wave * JW];
             const uint4 o = *reinterpret_cast<const uint4*>(ow);
             const uint32_t om[JW] = {o.x, o.y, o.z, o.w};
             const int tt = dt < ntok ? dt : 0;  // rows of tokens past the end: any valid row
@@ -344,12 +413,12 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
             float rs[CPL], us[CPL];
 #pragma unroll
             for (int k = 0; k < CPL; ++k) rs[k] = us[k] = 0.f;
-            const float al = s_al[ct];
+            const float al = s_al[cb][ct];
 #pragma unroll
             for (int m = 0; m < NW / NWAVE; ++m) {
                 const int i = wave + NWAVE * m;
-                const float aw = shared ? al * s_w[ct * NW + i] : 0.f;
-                const float f = __uint_as_float(bpl[BPL_F + ct * NW + i]);
+                const float aw = shared ? al * s_w[cb][ct * NW + i] : 0.f;
+                const float f = __uint_as_float(bpl[cb][BPL_F + ct * NW + i]);
 #pragma unroll
                 for (int k = 0; k < CPL; ++k) {
                     rs[k] = fmaf(aw, pst[i * CC + ct][CPL * qt + k], rs[k]);
@@ -376,19 +445,22 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
                     rsum += part[w][0][ct][cc];
                     usum += part[w][1][ct][cc];
                 }
-                s_res[ct][cc] = ok ? (shared ? s_v[ct][cc] - rsum : s_v[ct][cc]) : 0.f;
+                s_res[ct][cc] = ok ? (shared ? s_v[cb][ct][cc] - rsum : s_v[cb][ct][cc]) : 0.f;
+                // Bm[tau][t] is zero for tau < t: the loop runs over every tau
                 float z = usum;
-                for (int tau = ct; tau < CC; ++tau)
-                    z = fmaf(__uint_as_float(fpl[G::PL_BM + tau * G::TB_LD + ct]), s_dy[tau][cc], z);
+#pragma unroll
+                for (int tau = 0; tau < CC; ++tau)
+                    z = fmaf(__uint_as_float(fpl[cb][FBM + tau * G::TB_LD + ct]), s_dy[cb][tau][cc], z);
                 s_s[ct][cc] = z;
             }
             wave_sync();
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
                 const int cc = CPL * qt + k;
-                float dr = 0.f;
-                for (int tau = ct; tau < CC; ++tau)
-                    dr = fmaf(__uint_as_float(fpl[G::PL_TM + tau * G::TB_LD + ct]), s_s[tau][cc], dr);
+                float dr = 0.f;  // T lower triangular: T[tau][t] = 0 for tau < t
+#pragma unroll
+                for (int tau = 0; tau < CC; ++tau)
+                    dr = fmaf(__uint_as_float(fpl[cb][FTM + tau * G::TB_LD + ct]), s_s[tau][cc], dr);
                 s_dr[ct][cc] = dr;
                 if (ok)
                     dvout[(((size_t)b * T + t0 + ct) * H + h) * dv + col0 + cc] = from_f32<io_t>(dr);
@@ -398,28 +470,28 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
 
         // ---- every slot's gradient row through its events (two lanes per
         //      slot), then each read's row value ----
-        const int ng = (int)bpl[BPL_NG];
+        const int ng = (int)bpl[cb][BPL_NG];
         for (int task = tid; task < 2 * ng; task += 64 * NWAVE) {
             const int g = task >> 1, hf = task & 1;
-            const int gs = (int)bpl[BPL_GS + g], ge = (int)bpl[BPL_GS + g + 1];
-            const uint32_t ev0 = bpl[BPL_EV + gs];
+            const int gs = (int)bpl[cb][BPL_GS + g], ge = (int)bpl[cb][BPL_GS + g + 1];
+            const uint32_t ev0 = bpl[cb][BPL_EV + gs];
             const int q0 = ((ev0 >> 5) & 1u) ? NW + (int)(ev0 >> 6) : (int)(ev0 >> 6);
             const int r0 = q0 * CC + (int)(ev0 & 31u);
             f32x4 gr = *reinterpret_cast<const f32x4*>(&gst[r0][4 * hf]);
-            const uint32_t off = fpl[G::offs_word(q0, (int)(ev0 & 31u))];
+            const uint32_t off = fpl[cb][G::offs_word(q0, (int)(ev0 & 31u))];
             int firstw = -1;  // row of the slot's earliest write in the chunk
             for (int p = ge - 1; p >= gs; --p) {
-                const uint32_t ev = bpl[BPL_EV + p];
+                const uint32_t ev = bpl[cb][BPL_EV + p];
                 const int t = (int)(ev & 31u), i = (int)(ev >> 6);
-                const f32x4 dy4 = *reinterpret_cast<const f32x4*>(&s_dy[t][4 * hf]);
+                const f32x4 dy4 = *reinterpret_cast<const f32x4*>(&s_dy[cb][t][4 * hf]);
                 if ((ev >> 5) & 1u) {
-                    gr = axpy4(s_e[t * NR + i], dy4, gr);
+                    gr = axpy4(s_e[cb][t * NR + i], dy4, gr);
                     continue;
                 }
                 const f32x4 P = *reinterpret_cast<const f32x4*>(&pst[i * CC + t][4 * hf]);
                 const f32x4 x = *reinterpret_cast<const f32x4*>(&s_res[t][4 * hf]);
                 const f32x4 drt = *reinterpret_cast<const f32x4*>(&s_dr[t][4 * hf]);
-                const float al = s_al[t], be = s_be[t], w = s_w[t * NW + i];
+                const float al = s_al[cb][t], be = s_be[cb][t], w = s_w[cb][t * NW + i];
                 f32x4 dmt;
                 float pb, pw;
                 if (shared) {
@@ -451,7 +523,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
             const int er = task >> 1, hf = task & 1;
             const int t = er / NR, k = er - (er / NR) * NR;
             if (t >= ntok) continue;
-            const uint32_t rec = bpl[BPL_Y + er];
+            const uint32_t rec = bpl[cb][BPL_Y + er];
             const int tt = (int)((rec >> 2) & 31u), ii = (int)(rec >> 7);
             f32x4 y;
             if ((rec & 3u) == 0u) {
@@ -462,33 +534,53 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
                     y = P;
                 } else {
                     const f32x4 x = *reinterpret_cast<const f32x4*>(&s_res[tt][4 * hf]);
-                    const float al = s_al[tt], bw = s_be[tt] * s_w[tt * NW + ii];
+                    const float al = s_al[cb][tt], bw = s_be[cb][tt] * s_w[cb][tt * NW + ii];
                     const float d = shared ? al : al * (1.f - bw);
                     y = axpy4(bw, x, scale4(d, P));
                 }
             }
-            s_pe[er][hf] = dot4(y, *reinterpret_cast<const f32x4*>(&s_dy[t][4 * hf]));
+            s_pe[er][hf] = dot4(y, *reinterpret_cast<const f32x4*>(&s_dy[cb][t][4 * hf]));
         }
         __syncthreads();
 
         // ---- this slice's per-token partial sums (fixed order); a chunk without
-        //      events (one holding an out-of-range slot) leaves zeros ----
-        for (int x = tid; x < ntok * NP; x += 64 * NWAVE) {
-            const int t = x / NP, j = x - (x / NP) * NP;
+        //      events (one holding an out-of-range slot) leaves zeros.  dalpha and
+        //      dbeta: one wavefront per token adds its 2 W entry halves (lane l
+        //      takes values l, l + 64, ..., then a butterfly over the lanes) ----
+        for (int t = wave; t < ntok; t += NWAVE) {
+            const float* fa = &s_pa[t * NW][0];
+            const float* fb = &s_pb[t * NW][0];
+            float sa = 0.f, sb = 0.f;
+#pragma unroll
+            for (int r = 0; r < 2 * NW / 64; ++r) {
+                sa += fa[lane + 64 * r];
+                sb += fb[lane + 64 * r];
+            }
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) {
+                sa += xor_lane_f(sa, m, lane);
+                sb += xor_lane_f(sb, m, lane);
+            }
+            float* pp = a.part + ((((size_t)b * T + t0 + t) * H + h) * nslice + slice) * NP;
+            if (lane == 0) {
+                pp[0] = ng > 0 ? sa : 0.f;
+                pp[1] = ng > 0 ? sb : 0.f;
+            }
+        }
+        for (int x = tid; x < ntok * (NW + NR); x += 64 * NWAVE) {
+            const int t = x / (NW + NR), j = x - (x / (NW + NR)) * (NW + NR);
             float s = 0.f;
             if (ng == 0) {
-            } else if (j < 2) {
-                const float(*src)[2] = j == 0 ? s_pa : s_pb;
-                for (int i = 0; i < NW; ++i) s += src[t * NW + i][0] + src[t * NW + i][1];
-            } else if (j < 2 + NW) {
-                s = s_pw[t * NW + j - 2][0] + s_pw[t * NW + j - 2][1];
+            } else if (j < NW) {
+                s = s_pw[t * NW + j][0] + s_pw[t * NW + j][1];
             } else {
-                s = s_pe[t * NR + j - 2 - NW][0] + s_pe[t * NR + j - 2 - NW][1];
+                s = s_pe[t * NR + j - NW][0] + s_pe[t * NR + j - NW][1];
             }
-            a.part[((((size_t)b * T + t0 + t) * H + h) * nslice + slice) * NP + j] = s;
+            a.part[((((size_t)b * T + t0 + t) * H + h) * nslice + slice) * NP + 2 + j] = s;
         }
-        // this chunk's table and gradient stores land before the earlier
-        // chunk's gathers are issued
+        // the earlier chunk's plans and inputs into the other buffers; this
+        // chunk's table and gradient stores land before its gathers are issued
+        if (c > 0) commit(c - 1, pre);
         wait_vm0();
         __syncthreads();
     }
