@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
                                                                    const uint32_t* __restrict__ fplan,
                                                                    const uint32_t* __restrict__ bplan,
                                                                    int nslice, int total, int nch) {
-    constexpr int CC = G::CC, NW = G::NW, NR = G::NR, NQ = G::NQ, RPD = G::RPD;
+    constexpr int CC = G::CC, NW = G::NW, NR = G::NR, NQ = G::NQ;
     constexpr int LPT = 64 / CC;   // compute lanes per token
     constexpr int CPL = CW / LPT;  // columns per compute lane
     // forward-plan words kept per chunk: the row offsets, then T and Bm
@@ -262,11 +262,12 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
                   "forward-plan copy");
     static_assert(BPL_WORDS / 4 <= 2 * 64 * NWAVE && NE == 64 * NWAVE && CC * DWT <= 64 * NWAVE,
                   "one chunk's prefetch: two plan pieces, one weight of each kind per thread");
+    static_assert(2 * NW * CC == 2 * 64 * NWAVE, "two 16-byte pieces of pre-write rows per thread");
     static_assert(JW == 4 && NW % NWAVE == 0, "sweep layout");
 
     __shared__ __align__(16) float gst[NQ * CC][CW];  // gradient-table rows of every entry
     __shared__ __align__(16) float mst[NR * CC][CW];  // table rows of the read entries
-    __shared__ __align__(16) float pst[NW * CC][CW];  // pre-write rows of the write entries
+    __shared__ __align__(16) float pst[2][NW * CC][CW];  // pre-write rows of the writes, by chunk parity
     // plans and inputs, double-buffered by chunk parity
     __shared__ __align__(16) uint32_t fpl[2][FPC];
     __shared__ __align__(16) uint32_t bpl[2][BPL_WORDS];
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
 
     // DMA lane mapping: lane l covers 16 bytes (half l%2) of row
     // (q = RPD j + (l/2) / C, t = (l/2) % C) of DMA j
-    const int dq = (lane >> 1) / CC, dt = (lane >> 1) % CC, dh = lane & 1;
+    const int dh = lane & 1;
     const uint32_t colbyte = 4u * (uint32_t)(col0 + 4 * dh);
     // compute mapping: lane (t, qt) owns columns CPL qt .. CPL qt + CPL - 1 of token t
     const int ct = lane / LPT, qt = lane % LPT;
@@ -309,8 +310,14 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
     // one chunk's plans and inputs: loaded by every thread (clamped, always
     // valid addresses), kept by the threads that own a piece
     struct Pref {
-        u32x4 f, b0, b1;
+        u32x4 f, b0, b1, p0, p1;
         uint32_t w, e, al, be, dy, v;
+    };
+    // piece x of the pre-write rows: row x / 2 = i C + t, half x % 2
+    auto saved_piece = [&](int t0n, int ntn, int x) -> const float* {
+        const int row = x >> 1, i = row / CC, t = row - (row / CC) * CC;
+        const int tc = t < ntn ? t : ntn - 1;
+        return a.saved + ((((size_t)b * T + t0n + tc) * H + h) * NW + i) * dv + col0 + 4 * (x & 1);
     };
     auto prefetch = [&](int cn, Pref& r) {
         const int t0n = cn * CC;
@@ -334,14 +341,18 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
         const size_t btd = ((size_t)b * T + t0n + td) * H + h;
         r.dy = pinned_load4(reinterpret_cast<const uint32_t*>(dyin + btd * dv + col0) + d % DWT);
         r.v = pinned_load4(reinterpret_cast<const uint32_t*>(vin + btd * dv + col0) + d % DWT);
+        r.p0 = pinned_load16(saved_piece(t0n, ntn, tid));
+        r.p1 = pinned_load16(saved_piece(t0n, ntn, tid + 64 * NWAVE));
     };
     auto commit = [&](int cn, Pref& r) {
         asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(r.f), "+v"(r.b0), "+v"(r.b1), "+v"(r.w), "+v"(r.e), "+v"(r.al),
-                       "+v"(r.be), "+v"(r.dy), "+v"(r.v)
+                     : "+v"(r.f), "+v"(r.b0), "+v"(r.b1), "+v"(r.p0), "+v"(r.p1), "+v"(r.w),
+                       "+v"(r.e), "+v"(r.al), "+v"(r.be), "+v"(r.dy), "+v"(r.v)
                      :
                      : "memory");
         const int nb = cn & 1;
+        *reinterpret_cast<u32x4*>(&pst[nb][tid >> 1][4 * (tid & 1)]) = r.p0;
+        *reinterpret_cast<u32x4*>(&pst[nb][(tid + 64 * NWAVE) >> 1][4 * (tid & 1)]) = r.p1;
         const int ntn = T - cn * CC < CC ? T - cn * CC : CC;
         if (tid < FPC / 4) *reinterpret_cast<u32x4*>(&fpl[nb][4 * tid]) = r.f;
         if (tid < BPL_WORDS / 4) *reinterpret_cast<u32x4*>(&bpl[nb][4 * tid]) = r.b0;
@@ -379,33 +390,27 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
         const int t0 = c * CC;
         const int ntok = T - t0 < CC ? T - t0 : CC;
         const int cb = c & 1;
-        // the earlier chunk's plans and inputs, in flight during this step
-        Pref pre;
-        if (c > 0) prefetch(c - 1, pre);
 
         // ---- row DMAs: gradient rows of all entries, table rows of the reads
-        //      (DMAs j >= 16), pre-write rows of the writes (DMAs j < 16) ----
+        //      (DMAs j >= 16); the pre-write rows came with the prefetch ----
         {
             const uint32_t* ow = &fpl[cb][G::PL_OFFS + (lane >> 1) * G::OFFS_LD + wave * JW];
             const uint4 o = *reinterpret_cast<const uint4*>(ow);
             const uint32_t om[JW] = {o.x, o.y, o.z, o.w};
-            const int tt = dt < ntok ? dt : 0;  // rows of tokens past the end: any valid row
 #pragma unroll
             for (int m = 0; m < JW; ++m) {
                 const int j = wave + NWAVE * m;
                 dma16(Gc + om[m] + colbyte, &gst[j * 32][0]);
-                if (NWAVE * m >= 16) {
-                    dma16(Mc + om[m] + colbyte, &mst[(j - 16) * 32][0]);
-                } else {
-                    const int q = RPD * j + dq;
-                    const float* src =
-                        a.saved + ((((size_t)b * T + t0 + tt) * H + h) * NW + q) * dv + col0 + 4 * dh;
-                    dma16(src, &pst[j * 32][0]);
-                }
+                if (NWAVE * m >= 16) dma16(Mc + om[m] + colbyte, &mst[(j - 16) * 32][0]);
             }
         }
         wait_vm0();
         block_sync_lds();
+        // the earlier chunk's plans, inputs and pre-write rows: in flight during
+        // this step's arithmetic (issued after the wait above, so that no wait
+        // of the compiler's, which does not see them, covers them)
+        Pref pre;
+        if (c > 0) prefetch(c - 1, pre);
 
         // ---- partial sums over this wave's write rows i = wave + NWAVE m:
         //      alpha w P (shared residual) and f G (u) ----
@@ -421,7 +426,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
                 const float f = __uint_as_float(bpl[cb][BPL_F + ct * NW + i]);
 #pragma unroll
                 for (int k = 0; k < CPL; ++k) {
-                    rs[k] = fmaf(aw, pst[i * CC + ct][CPL * qt + k], rs[k]);
+                    rs[k] = fmaf(aw, pst[cb][i * CC + ct][CPL * qt + k], rs[k]);
                     us[k] = fmaf(f, gst[i * CC + ct][CPL * qt + k], us[k]);
                 }
             }
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
                     gr = axpy4(s_e[cb][t * NR + i], dy4, gr);
                     continue;
                 }
-                const f32x4 P = *reinterpret_cast<const f32x4*>(&pst[i * CC + t][4 * hf]);
+                const f32x4 P = *reinterpret_cast<const f32x4*>(&pst[cb][i * CC + t][4 * hf]);
                 const f32x4 x = *reinterpret_cast<const f32x4*>(&s_res[t][4 * hf]);
                 const f32x4 drt = *reinterpret_cast<const f32x4*>(&s_dr[t][4 * hf]);
                 const float al = s_al[cb][t], be = s_be[cb][t], w = s_w[cb][t * NW + i];
@@ -516,7 +521,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
                 *reinterpret_cast<f32x4*>(Gw + off + 16u * hf + 4u * col0) = gr;
                 if (firstw >= 0)
                     *reinterpret_cast<f32x4*>(Mw + off + 16u * hf + 4u * col0) =
-                        *reinterpret_cast<const f32x4*>(&pst[firstw][4 * hf]);
+                        *reinterpret_cast<const f32x4*>(&pst[cb][firstw][4 * hf]);
             }
         }
         for (int task = tid; task < 2 * CC * NR; task += 64 * NWAVE) {
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
             if ((rec & 3u) == 0u) {
                 y = *reinterpret_cast<const f32x4*>(&mst[k * CC + t][4 * hf]);
             } else {
-                const f32x4 P = *reinterpret_cast<const f32x4*>(&pst[ii * CC + tt][4 * hf]);
+                const f32x4 P = *reinterpret_cast<const f32x4*>(&pst[cb][ii * CC + tt][4 * hf]);
                 if ((rec & 3u) == 1u) {
                     y = P;
                 } else {
