@@ -331,8 +331,8 @@ def bench_rows(args, torch, sslp, wl):
         hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_call=nbytes)
     del yv, gv, gam, ov
     # SDM training on the 1.4B prefill layer: forward keeping the pre-write rows
-    # (chunk-parallel kernel) and the backward by undoing writes (reverse sweep,
-    # slice reduction, addressing-softmax backward)
+    # and the backward by undoing writes (both chunk-parallel; the backward's
+    # slice reduction and addressing-softmax backward included)
     cfg = wl.SDM_14B
     x = {k: v.to(dev) for k, v in wl.sdm_inputs(cfg).items()}
     M = torch.zeros((cfg.B, cfg.H, cfg.N, cfg.d_v), dtype=torch.float32, device=dev)

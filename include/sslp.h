@@ -252,8 +252,10 @@ int sdm_sparse_update_train(const sslp_sdm_shape* shape, int dtype, int residual
 size_t sdm_train_workspace_size(const sslp_sdm_shape* shape);
 
 /* Workspace bytes of sdm_backward: per-token partial sums of the scalar
- * gradients for each 16-column slice of d_v, and the weight gradients when the
- * caller does not ask for them.  0 for an invalid shape. */
+ * gradients for each slice of d_v (8 columns on the chunk-parallel path, 16
+ * otherwise), the weight gradients when the caller does not ask for them, and
+ * on the chunk-parallel path the per-chunk plans of both directions.  0 for an
+ * invalid shape. */
 size_t sdm_backward_workspace_size(const sslp_sdm_shape* shape);
 
 /*
@@ -290,6 +292,14 @@ size_t sdm_backward_workspace_size(const sslp_sdm_shape* shape);
  *                             neither (NULL skips that addressing backward);
  *   workspace, ws_bytes >= sdm_backward_workspace_size(shape).
  * The scalar gradients are added over d_v in a fixed order (deterministic).
+ * Execution: with T >= 64 and W = R = 32 or 64 (the shapes whose forward is
+ * chunk-parallel) the same gradients are formed chunk by chunk in reverse
+ * (slides "Training parallelizes within chunks and recurs across chunks"): the
+ * transpose of the chunk's linear map gives every token's dr at once, and each
+ * slot's gradient row is carried backwards through its events in the chunk;
+ * other shapes take the per-token sweep above.  A chunk holding a slot index
+ * outside [0, N) is skipped (its gradients are 0, the tables keep their rows)
+ * and reported through sslp_device_error.
  */
 int sdm_backward(const sslp_sdm_shape* shape, int dtype, int residual_mode, const int32_t* idx_w,
                  const float* wt_w, const int32_t* idx_r, const float* wt_r, const void* v,
