@@ -48,14 +48,21 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
     # the inline-asm loads' destination registers must stay untouched until
-    # their explicit waits in the generated code (fails the build otherwise)
+    # their explicit waits in the generated code: a build that fails the check
+    # leaves no library behind (neither the new one nor a stale older one)
     if __package__:
         from . import asm_check
     else:  # run as a script: this directory is on sys.path
         import asm_check
-    asm_check.run(verbose=verbose)
+    try:
+        asm_check.run(verbose=verbose)
+    except Exception:
+        for f in (LIB + ".tmp", LIB):
+            if os.path.exists(f):
+                os.remove(f)
+        raise
+    os.replace(LIB + ".tmp", LIB)
     return LIB
 
 
