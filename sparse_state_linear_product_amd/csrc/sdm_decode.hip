@@ -25,6 +25,8 @@ namespace sslp {
 
 namespace {
 
+typedef float f32v4 __attribute__((ext_vector_type(4)));
+
 constexpr int kCols = 256;    // columns per workgroup
 constexpr int kWaves = 8;     // wavefronts per workgroup
 constexpr int kMaxRows = 64;  // W, R <= 64
@@ -160,7 +162,10 @@ __global__ __launch_bounds__(64 * kWaves) void sdm_decode_fused_kernel(SdmDecode
             nv.z = fmaf(c, res.z, mw[r].z);
             nv.w = fmaf(c, res.w, mw[r].w);
             su.nw[n][lane] = nv;
-            if (colok) *reinterpret_cast<float4*>(tab + (size_t)ws[r] * a.dv + col) = nv;
+            // a streaming store: the step does not read the row from memory again
+            if (colok)
+                __builtin_nontemporal_store(f32v4{nv.x, nv.y, nv.z, nv.w},
+                                            reinterpret_cast<f32v4*>(tab + (size_t)ws[r] * a.dv + col));
         }
     }
     block_sync_lds();
