@@ -333,6 +333,25 @@ def test_sdm_1p4b_layer_full_size(budget):
 
 
 @pytest.mark.slow
+def test_sdm_1p4b_layer_batch8_sampled():
+    # the batch-8 row of the benchmark (1,920 column slices: the chunk path
+    # runs them in rounds), all eight sequences in one call; sequences are
+    # independent, so the oracle checks the first and the last one
+    cfg = dataclasses.replace(wl.SDM_14B, B=8)
+    announce(f"sdm 1.4B-layer B=8 T={cfg.T}, sequences 0 and 7 checked")
+    x = wl.sdm_inputs(cfg)
+    M0 = torch.zeros((cfg.B, cfg.H, cfg.N, cfg.d_v))
+    got = _run_forward(cfg, x, M0, 0)
+    sub = [0, cfg.B - 1]
+    c2 = dataclasses.replace(cfg, B=len(sub))
+    xs = {k: v[sub] for k, v in x.items()}
+    ref = _oracle_forward(c2, xs, M0[sub], 0)
+    gs = dict(y=got["y"][sub], M=got["M"][sub], idx_w=got["idx_w"][sub], wt_w=got["wt_w"][sub],
+              idx_r=got["idx_r"][sub], wt_r=got["wt_r"][sub])
+    _check(c2, gs, ref, M0[sub], "1.4B layer, B=8 (sequences 0, 7)")
+
+
+@pytest.mark.slow
 def test_sdm_decode_full_size():
     # 64 independent sequences on the 1.4B-layer table shape (28.3 GB state).  The
     # pre-step table is drawn by torch on the device; the oracle recomputes the
