@@ -142,6 +142,54 @@ def test_sdm_train_chunk_path(case):
     assert e <= TOL_FP32, f"saved rows: {e}"
 
 
+@pytest.mark.parametrize("W", [32, 64, 9])
+def test_backward_out_of_range_slot_is_contained_and_reported(W):
+    # sdm_backward with a caller index outside [0, N): W = 32, 64 take the
+    # chunk-parallel backward, W = 9 the per-token sweep.  The table and its
+    # gradient are slices of larger buffers whose guard regions must stay
+    # bitwise; the device error flag reports the call; gradients stay finite.
+    import sparse_state_linear_product_amd as sslp
+    announce(f"sdm_backward with an out-of-range slot, W = R = {W}")
+    assert not sslp.device_error()
+    B, T, H, sq, dv = 1, 80, 2, 16, 16
+    N = sq * sq
+    g = torch.Generator().manual_seed(95 + W)
+    idx = torch.stack([torch.randperm(N, generator=g)[:W] for _ in range(B * T * H)]).int()
+    idx = idx.view(B, T, H, W).contiguous()
+    wt = torch.full((B, T, H, W), 1.0 / W)
+    v = torch.randn((B, T, H, dv), generator=g)
+    alpha = torch.full((B, T, H), 0.95)
+    beta = torch.full((B, T, H), 0.5)
+    dy = torch.randn((B, T, H, dv), generator=g)
+    t = lambda x: x.to(DEV)
+    M = torch.randn((B, H, N, dv), generator=g).to(DEV)
+    _, saved = sslp.sdm_sparse_update_train(t(idx), t(wt), t(idx), t(wt), t(v), t(alpha),
+                                            t(beta), M)
+    torch.cuda.synchronize()
+    assert not sslp.device_error()
+    bad = idx.clone()
+    bad[0, 70, 1, 3] = N + 5   # a bad write slot
+    bad_r = idx.clone()
+    bad_r[0, 10, 0, 0] = -7    # a bad read slot
+    guard = 1 << 16
+    n = B * H * N * dv
+    mbuf = torch.randn((2 * guard + n,), generator=g).to(DEV)
+    gbuf = torch.randn((2 * guard + n,), generator=g).to(DEV)
+    mbuf[guard:guard + n] = M.reshape(-1)
+    m0, g0 = mbuf.clone(), gbuf.clone()
+    Mv = mbuf[guard:guard + n].view(B, H, N, dv)
+    Gv = gbuf[guard:guard + n].view(B, H, N, dv)
+    ctx = dict(idx_w=t(bad), wt_w=t(wt), idx_r=t(bad_r), wt_r=t(wt), saved=saved)
+    out = sslp.sdm_backward(ctx, t(v), t(alpha), t(beta), Mv, t(dy), Gv, score_grads=False)
+    torch.cuda.synchronize()
+    assert sslp.device_error()
+    assert not sslp.device_error()  # the query cleared it
+    for buf, ref in ((mbuf, m0), (gbuf, g0)):
+        assert torch.equal(buf[:guard], ref[:guard]) and torch.equal(buf[-guard:], ref[-guard:])
+    for k in ("dv", "dalpha", "dbeta", "dwt_w", "dwt_r"):
+        assert torch.isfinite(out[k]).all(), k
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 def test_sdm_recurrence_backward_signed_weights(mode):
     # the recurrence alone with raw signed weights and distinct slots, read and
