@@ -33,13 +33,13 @@
 // A plan kernel lists, per (b, h, chunk), every slot's events in token order,
 // f for every write entry and the source of every read's row; the sweep kernel
 // runs one workgroup per 8-column slice of a head through the chunks in
-// reverse: it gathers the gradient-table rows of every entry, the table rows
-// of the reads and the pre-write rows of the writes (LDS-DMA), forms r, u,
-// dr (dv), then carries each slot's row through its events (two lanes per
-// slot), writes the slot's gradient and restored table row once, and leaves
-// per-token partial sums of the scalar gradients for the slice reduction.
-// Every store of a chunk completes before the next (earlier) chunk's gathers
-// are issued.
+// reverse: it gathers the gradient-table rows of every entry and the table
+// rows of the reads (LDS-DMA), forms r, u, dr (dv), then carries each slot's
+// row through its events (two lanes per slot), writes the slot's gradient and
+// restored table row once, and leaves per-token partial sums of the scalar
+// gradients for the slice reduction.  The next chunk's plans, inputs and
+// pre-write rows are loaded during the step's arithmetic.  Every store of a
+// chunk completes before the next (earlier) chunk's gathers are issued.
 #include "common.h"
 #include "kernels.h"
 #include "sdm_chunk.h"
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(64 * NWAVE) void sdm_chunk_bwd_kernel(SdmBwdArgs a,
     io_t* dvout = static_cast<io_t*>(a.dv_out);
 
     // DMA lane mapping: lane l covers 16 bytes (half l%2) of row
-    // (q = RPD j + (l/2) / C, t = (l/2) % C) of DMA j
+    // (q = G::RPD j + (l/2) / C, t = (l/2) % C) of DMA j
     const int dh = lane & 1;
     const uint32_t colbyte = 4u * (uint32_t)(col0 + 4 * dh);
     // compute mapping: lane (t, qt) owns columns CPL qt .. CPL qt + CPL - 1 of token t
