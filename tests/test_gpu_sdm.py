@@ -333,6 +333,23 @@ def test_sdm_1p4b_layer_full_size(budget):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("sqrt_n", [362, 363])
+def test_sdm_row_offsets_at_the_32_bit_limit(sqrt_n):
+    # the largest tables d_v allows (4096 columns): 362^2 slots keep every row
+    # offset below 2^31 bytes (the chunk path's 32-bit offsets, the largest
+    # ones it takes), 363^2 slots cross it (the per-token path, 64-bit offsets)
+    cfg = wl.SdmConfig("offsets", 1, 64, 1, sqrt_n, 4096, 32, 32, 32, 32, torch.bfloat16,
+                       800 + sqrt_n)
+    announce(f"sdm table of {cfg.N} x 4096 fp32 ({cfg.N * 4096 * 4 / 2**31:.4f} x 2^31 bytes)")
+    x = wl.sdm_inputs(cfg)
+    M0 = torch.zeros((1, 1, cfg.N, cfg.d_v))
+    got = _run_forward(cfg, x, M0, 0)
+    ref = _oracle_forward(cfg, x, M0, 0)
+    assert int(ref["idx_w"].max()) * 4096 * 4 > 2**31 - 2**24  # rows near the end were written
+    _check(cfg, got, ref, M0, f"offsets sqrtN={sqrt_n}")
+
+
+@pytest.mark.slow
 def test_sdm_1p4b_layer_batch8_sampled():
     # the batch-8 row of the benchmark (1,920 column slices: the chunk path
     # runs them in rounds), all eight sequences in one call; sequences are
