@@ -1,10 +1,12 @@
 """Build-time check of the kernels' inline-assembly loads.
 
-Two kernels issue some of their loads as inline assembly so that the compiler
-cannot move them: the GDN state kernel's record prefetch (global_load_dwordx4,
-waited for by an explicit `s_waitcnt vmcnt(0)`) and the SDM chunk kernel's
-reads of LDS that an LDS-DMA may be filling (ds_read_*, waited for by an
-explicit `s_waitcnt lgkmcnt(0)`).  The compiler treats the destination
+The kernels that stage memory through LDS with LDS-DMA (the chunk-parallel
+SDM kernels, the GDN state kernel) read that LDS with inline-assembly loads
+(ds_read_*, waited for by an explicit `s_waitcnt lgkmcnt(0)`), and the SDM
+chunked backward prefetches with inline-assembly global loads
+(global_load_dwordx4, waited for by an explicit `s_waitcnt vmcnt(0)`), so
+that the compiler cannot move them or wait for the DMAs in flight before
+them.  The compiler treats the destination
 registers of such a load as written when the asm statement ends, so nothing
 in the language stops the register allocator from copying, spilling or
 reusing them before the data has arrived.  This check reads the generated

@@ -26,21 +26,26 @@
 //    fp32 (16x16 diagonal blocks by forward substitution, off-diagonal blocks
 //    through I + A = D (I + L), L = D^{-1} A_off, T = (I - L + L^2 - L^3) D^{-1}
 //    on v_mfma_f32_16x16x4_f32), then U0, Wn (MFMA) and the decayed operands
-//    Qt, Kh, P, e^{g_C} into a per-chunk record.
-//  * gdn_state_kernel, one workgroup (4 waves) per (batch, head, 32-column
-//    block of d_v), walks the chunks in order with its [128 x 32] fp32 state
-//    slice in MFMA accumulators: U = U0 + Wn S0, O = Qt S0 + P U,
-//    S = e^{g_C} S0 + Kh^T U, prefetching the next chunk's record.
+//    Qt, Kh, P, e^{g_C} into a per-chunk record laid out as MFMA operand
+//    fragments (71 KB per chunk).
+//  * gdn_state_kernel, per (batch, head, 16-column tile of d_v) a chain
+//    wavefront that walks the chunks in order with its [128 x 16] fp32 state
+//    slice in MFMA accumulators (U = U0 + Wn S0, S = e^{g_C} S0 + Kh^T U) and
+//    an output wavefront one chunk behind (O = Qt S0 + P U), the next
+//    chunk's record DMA'd into LDS during the current one.
 // KDA factors the per-channel decay of K K^T and Q K^T into the operands
 // relative to the first token of each 16-token block, so every scale factor
 // is a product of alphas bounded by alpha_min^-15; Qt, Kh, e^{g_C} are
 // products of alphas at most 1.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace sslp {
 
 namespace {
+
+using namespace lds;
 
 // largest inverse product of per-channel decays inside a 16-token block
 constexpr float kMaxInvDecay = 0x1p64f;
@@ -50,21 +55,36 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;     // chunk length
 constexpr int DK = 128;   // key width
-constexpr int DVB = 32;   // d_v columns per state workgroup
-constexpr int NTH = 256;  // threads per workgroup
+constexpr int NTH = 256;  // threads per prep workgroup
 constexpr int LDK = DK + 8;   // bf16 row stride of [C][DK] tiles
 constexpr int LDF = C + 4;    // fp32 row stride of [C][C] tiles
-constexpr int LDX = DVB + 4;  // fp32 row stride of [C][DVB] tiles
 constexpr int LDP = C + 8;    // bf16 row stride of [C][C] tiles
 
-// per-chunk record written by gdn_prep_kernel (bytes)
-constexpr int REC_WN = 0;                      // [C][DK] bf16: -T diag(beta) Kt
-constexpr int REC_QT = REC_WN + C * DK * 2;    // [C][DK] bf16: Qt
-constexpr int REC_KH = REC_QT + C * DK * 2;    // [DK][C] bf16: Kh transposed
-constexpr int REC_P = REC_KH + C * DK * 2;     // [C][C] bf16: P (causal)
-constexpr int REC_U0 = REC_P + C * C * 2;      // [C][DK] fp32: T diag(beta) V  (d_v = DK)
-constexpr int REC_GC = REC_U0 + C * DK * 4;    // [DK] fp32: e^{g_C}
-constexpr int REC_BYTES = REC_GC + DK * 4;
+// Per-chunk record written by the prep kernel and read by the state kernel,
+// in MFMA operand order.  A fragment is one 16x32 bf16 A operand of
+// v_mfma_f32_16x16x32_bf16 as the 64 lanes hold it (16 bytes per lane, lane
+// order), so the state kernel stages a fragment with one LDS-DMA and reads it
+// with one conflict-free ds_read_b128.  Lane l holds row l % 16 and the 8 k
+// values of k-slot group g = l / 16; the slots run over the k indices
+// 4g .. 4g+3 and 16+4g .. 16+4g+3 of the 32-wide k block (kperm below), which
+// are the rows that lane holds of two 16x16 accumulator tiles, so that the
+// state kernel's accumulators (S, U) serve as B operands without leaving
+// their registers.
+constexpr int FRAG = 1024;
+constexpr int REC_WN = 0;                  // 16 (row tile rt, k block kb): -T diag(beta) Kt, rows t, k = key channel
+constexpr int REC_KH = REC_WN + 16 * FRAG; // 16 (it, kb): Kh^T, rows = key channel, k = token
+constexpr int REC_GC = REC_KH + 16 * FRAG; // e^{g_C} per key channel (128 floats, one fragment's room)
+constexpr int REC_QT = REC_GC + FRAG;      // 16 (rt, kb): Qt, rows t, k = key channel
+constexpr int REC_P = REC_QT + 16 * FRAG;  // 6 (rt, kb <= rt / 2): P (causal), rows t, k = token
+constexpr int REC_NSH = REC_P / FRAG + 6;  // fragments every column block reads (55)
+constexpr int REC_U0 = REC_NSH * FRAG;     // U0 = T diag(beta) V in accumulator order:
+                                           // [8 column tiles][4 row tiles][64 lanes][4] bf16
+constexpr int REC_BYTES = REC_U0 + 8 * 4 * 64 * 4 * 2;
+static_assert(REC_BYTES % FRAG == 0, "whole fragments");
+// k index (within a 32-wide block) of slot s of k-slot group g
+SSLP_DEVICE constexpr int kperm(int g, int s) { return s < 4 ? 4 * g + s : 16 + 4 * g + (s - 4); }
+// P fragment index of (rt, kb): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+SSLP_DEVICE constexpr int pfrag(int rt, int kb) { return rt < 2 ? rt : 2 * rt - 2 + kb; }
 
 struct __align__(16) Smem {
     uint16_t k[C][LDK];   // GDN: K;  KDA: Kp = K * e^{g_t - g_r}
@@ -413,7 +433,10 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
 
 
         // ---------------- K K^T and Q K^T ----------------
-        // G rows block w (tiles tn <= w) and P' rows block 3-w (tiles tn <= 3-w)
+        // G rows block w (tiles tn <= w), and P' rows block 3-w (tiles tn <= 3-w)
+        // as its transpose (operands swapped): pt[tn] holds P'[t][j] for t in
+        // block 3-w at lane column, j in block tn at accumulator row, the order
+        // of P's A-operand fragments
         f32x4_t gt[4], pt[4];
         const int pr = 3 - w;
 #pragma unroll
@@ -432,7 +455,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
                 if constexpr (!KDA) {
                     const bf16x8_t bk = load_bf16x8(&sm.k[jrow][kc]);
                     if (tn <= w) gt[tn] = mfma_bf16(ak, bk, gt[tn]);
-                    if (tn <= pr) pt[tn] = mfma_bf16(aq, bk, pt[tn]);
+                    if (tn <= pr) pt[tn] = mfma_bf16(bk, aq, pt[tn]);
                 } else {
                     const uint16_t* kmr = &sm.km[jrow][kc];
                     if (tn <= w) {
@@ -455,7 +478,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
 #pragma unroll
                             for (int e = 0; e < 8; ++e) bb[e] = bf(bf2f(kmr[e]) * sm.D[p][kc + e]);
                         }
-                        pt[tn] = mfma_bf16(aq, bb, pt[tn]);
+                        pt[tn] = mfma_bf16(bb, aq, pt[tn]);
                     }
                 }
             }
@@ -469,44 +492,54 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             else kt = bf2f(sm.k[t][i]) * sm.F[t >> 4][i];
             sm.kbt[i][t] = f32_to_bf16(sm.beta[t] * kt).bits;
         }
-        // ---- Qt, Kh^T, e^{g_C} into the record: the last reads of Q and K ----
+        // ---- Qt, Kh^T fragments and e^{g_C} into the record: the last reads of
+        //      Q and K.  Wave w writes Qt's row tile w and Kh^T's row tiles 2w, 2w+1 ----
         {
-            uint16_t* qt = reinterpret_cast<uint16_t*>(rec + REC_QT);
-            uint16_t* kh = reinterpret_cast<uint16_t*>(rec + REC_KH);
-            for (int seg = tid; seg < C * DK / 8; seg += NTH) {
-                const int t = seg / (DK / 8), i0 = (seg % (DK / 8)) * 8;
-                uint32_t qw[4];
+            const int g = lane >> 4, r16 = lane & 15;
+            {
+                const int t = 16 * w + r16;
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    float q0, q1;
-                    if constexpr (!KDA) {
-                        const float fq = sm.eg[t];
-                        q0 = bf2f(sm.q[t][i0 + e]) * fq;
-                        q1 = bf2f(sm.q[t][i0 + e + 1]) * fq;
-                    } else {
-                        q0 = bf2f(sm.q[t][i0 + e]) * sm.F[t >> 4][i0 + e];
-                        q1 = bf2f(sm.q[t][i0 + e + 1]) * sm.F[t >> 4][i0 + e + 1];
+                for (int kb = 0; kb < 4; ++kb) {
+                    uint32_t qw[4];
+#pragma unroll
+                    for (int s = 0; s < 8; s += 2) {
+                        const int i0 = 32 * kb + kperm(g, s), i1 = 32 * kb + kperm(g, s + 1);
+                        float q0, q1;
+                        if constexpr (!KDA) {
+                            q0 = bf2f(sm.q[t][i0]) * sm.eg[t];
+                            q1 = bf2f(sm.q[t][i1]) * sm.eg[t];
+                        } else {
+                            q0 = bf2f(sm.q[t][i0]) * sm.F[t >> 4][i0];
+                            q1 = bf2f(sm.q[t][i1]) * sm.F[t >> 4][i1];
+                        }
+                        qw[s / 2] = (uint32_t)f32_to_bf16(q0).bits | ((uint32_t)f32_to_bf16(q1).bits << 16);
                     }
-                    qw[e / 2] = (uint32_t)f32_to_bf16(q0).bits | ((uint32_t)f32_to_bf16(q1).bits << 16);
+                    *reinterpret_cast<uint4*>(rec + REC_QT + (4 * w + kb) * FRAG + 16 * lane) =
+                        make_uint4(qw[0], qw[1], qw[2], qw[3]);
                 }
-                *reinterpret_cast<uint4*>(qt + t * DK + i0) = make_uint4(qw[0], qw[1], qw[2], qw[3]);
             }
-            for (int seg = tid; seg < C * DK / 8; seg += NTH) {
-                const int i = seg / (C / 8), t0e = (seg % (C / 8)) * 8;
-                uint32_t kw[4];
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    float k0, k1;
-                    if constexpr (!KDA) {
-                        k0 = bf2f(sm.k[t0e + e][i]) * sm.ehg[t0e + e];
-                        k1 = bf2f(sm.k[t0e + e + 1][i]) * sm.ehg[t0e + e + 1];
-                    } else {
-                        k0 = bf2f(sm.km[t0e + e][i]) * sm.Hf[(t0e + e) >> 4][i];
-                        k1 = bf2f(sm.km[t0e + e + 1][i]) * sm.Hf[(t0e + e + 1) >> 4][i];
+            for (int x = 0; x < 2; ++x) {
+                const int it = 2 * w + x, i = 16 * it + r16;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    uint32_t kw[4];
+#pragma unroll
+                    for (int s = 0; s < 8; s += 2) {
+                        const int t0e = 32 * kb + kperm(g, s), t1e = 32 * kb + kperm(g, s + 1);
+                        float k0, k1;
+                        if constexpr (!KDA) {
+                            k0 = bf2f(sm.k[t0e][i]) * sm.ehg[t0e];
+                            k1 = bf2f(sm.k[t1e][i]) * sm.ehg[t1e];
+                        } else {
+                            k0 = bf2f(sm.km[t0e][i]) * sm.Hf[t0e >> 4][i];
+                            k1 = bf2f(sm.km[t1e][i]) * sm.Hf[t1e >> 4][i];
+                        }
+                        kw[s / 2] = (uint32_t)f32_to_bf16(k0).bits | ((uint32_t)f32_to_bf16(k1).bits << 16);
                     }
-                    kw[e / 2] = (uint32_t)f32_to_bf16(k0).bits | ((uint32_t)f32_to_bf16(k1).bits << 16);
+                    *reinterpret_cast<uint4*>(rec + REC_KH + (2 * it + kb) * FRAG + 16 * lane) =
+                        make_uint4(kw[0], kw[1], kw[2], kw[3]);
                 }
-                *reinterpret_cast<uint4*>(kh + i * C + t0e) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
             }
             float* gc = reinterpret_cast<float*>(rec + REC_GC);
             if (tid < DK) {
@@ -515,26 +548,46 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             }
         }
         block_sync_lds();
-        // write A (strictly lower, beta and decay applied) and P (causal) tiles
+        // write A (strictly lower, beta and decay applied) to LDS, and P's
+        // fragments (row tile 3-w) to the record
+        {
+            float pv[4][4];
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
+            for (int tn = 0; tn < 4; ++tn) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 16 * w + (lane >> 4) * 4 + j;
-                const int jj = 16 * tn + (lane & 15);
-                float av = 0.f;
-                if (tn <= w && jj < t) {
-                    av = gt[tn][j] * sm.beta[t];
-                    if (!KDA) av *= __expf(sm.g[t] - sm.g[jj]);
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 16 * w + (lane >> 4) * 4 + j;
+                    const int jj = 16 * tn + (lane & 15);
+                    float av = 0.f;
+                    if (tn <= w && jj < t) {
+                        av = gt[tn][j] * sm.beta[t];
+                        if (!KDA) av *= __expf(sm.g[t] - sm.g[jj]);
+                    }
+                    sm.u.s.A[t][jj] = av;
+                    // pt: token tp (lane column) against token jp (accumulator row)
+                    const int tp = 16 * pr + (lane & 15);
+                    const int jp = 16 * tn + (lane >> 4) * 4 + j;
+                    float p = 0.f;
+                    if (tn <= pr && jp <= tp) {
+                        p = pt[tn][j];
+                        if (!KDA) p *= __expf(sm.g[tp] - sm.g[jp]);
+                    }
+                    pv[tn][j] = p;
                 }
-                sm.u.s.A[t][jj] = av;
-                const int tp = 16 * pr + (lane >> 4) * 4 + j;
-                float pv = 0.f;
-                if (tn <= pr && jj <= tp) {
-                    pv = pt[tn][j];
-                    if (!KDA) pv *= __expf(sm.g[tp] - sm.g[jj]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (2 * kb > pr) continue;  // the fragment (pr, 1) exists for pr >= 2
+                uint32_t pw[4];
+#pragma unroll
+                for (int s = 0; s < 4; s += 2) {
+                    pw[s / 2] = (uint32_t)f32_to_bf16(pv[2 * kb][s]).bits |
+                                ((uint32_t)f32_to_bf16(pv[2 * kb][s + 1]).bits << 16);
+                    pw[2 + s / 2] = (uint32_t)f32_to_bf16(pv[2 * kb + 1][s]).bits |
+                                    ((uint32_t)f32_to_bf16(pv[2 * kb + 1][s + 1]).bits << 16);
                 }
-                reinterpret_cast<uint16_t*>(rec + REC_P)[tp * C + jj] = f32_to_bf16(pv).bits;
+                *reinterpret_cast<uint4*>(rec + REC_P + pfrag(pr, kb) * FRAG + 16 * lane) =
+                    make_uint4(pw[0], pw[1], pw[2], pw[3]);
             }
         }
         block_sync_lds();
@@ -639,28 +692,35 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
         }
         block_sync_lds();
         {
-            float* u0 = reinterpret_cast<float*>(rec + REC_U0);
-            uint16_t* wn = reinterpret_cast<uint16_t*>(rec + REC_WN);
+            // U0 tiles (rows block w, column tile y) in accumulator order, and
+            // Wn^T tiles (key channels block y, tokens block w; operands swapped),
+            // whose pairs (2kb, 2kb+1) are Wn's fragments (w, kb)
             bf16x8_t at[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) at[s] = load_bf16x8(&sm.tb[16 * w + (lane & 15)][32 * s + (lane >> 4) * 8]);
-#pragma unroll 2
-            for (int y = 0; y < DK / 16; ++y) {
-                f32x4_t au = f32x4_t{0.f, 0.f, 0.f, 0.f}, aw = au;
-                const int n = 16 * y + (lane & 15);
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    if (s == 1 && w < 2) continue;  // T[t][j] = 0 for j >= 32 when t < 32
-                    const int kc = 32 * s + (lane >> 4) * 8;
-                    au = mfma_bf16(at[s], load_bf16x8(&sm.xt[n][kc]), au);
-                    aw = mfma_bf16(at[s], load_bf16x8(&sm.kbt[n][kc]), aw);
-                }
+            for (int kb = 0; kb < 4; ++kb) {
+                uint32_t ww[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * w + (lane >> 4) * 4 + j;
-                    u0[t * DK + n] = au[j];
-                    wn[t * DK + n] = f32_to_bf16(-aw[j]).bits;
+                for (int x = 0; x < 2; ++x) {
+                    const int y = 2 * kb + x;
+                    f32x4_t au = f32x4_t{0.f, 0.f, 0.f, 0.f}, aw = au;
+                    const int n = 16 * y + (lane & 15);
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        if (s == 1 && w < 2) continue;  // T[t][j] = 0 for j >= 32 when t < 32
+                        const int kc = 32 * s + (lane >> 4) * 8;
+                        au = mfma_bf16(at[s], load_bf16x8(&sm.xt[n][kc]), au);
+                        aw = mfma_bf16(load_bf16x8(&sm.kbt[n][kc]), at[s], aw);
+                    }
+                    const uint32_t u01 = (uint32_t)f32_to_bf16(au[0]).bits | ((uint32_t)f32_to_bf16(au[1]).bits << 16);
+                    const uint32_t u23 = (uint32_t)f32_to_bf16(au[2]).bits | ((uint32_t)f32_to_bf16(au[3]).bits << 16);
+                    *reinterpret_cast<uint2*>(rec + REC_U0 + ((4 * y + w) * 64 + lane) * 8) = make_uint2(u01, u23);
+                    ww[2 * x] = (uint32_t)f32_to_bf16(-aw[0]).bits | ((uint32_t)f32_to_bf16(-aw[1]).bits << 16);
+                    ww[2 * x + 1] = (uint32_t)f32_to_bf16(-aw[2]).bits | ((uint32_t)f32_to_bf16(-aw[3]).bits << 16);
                 }
+                *reinterpret_cast<uint4*>(rec + REC_WN + (4 * w + kb) * FRAG + 16 * lane) =
+                    make_uint4(ww[0], ww[1], ww[2], ww[3]);
             }
         }
     }
@@ -679,230 +739,251 @@ __global__ __launch_bounds__(NTH, 2) void gdn_prep_kernel_scalar(GdnArgs a, int 
 }
 
 // ---------------------------------------------------------------------------
-// state kernel: one workgroup (4 waves) per (b, h, 32-column block of d_v)
+// state kernel: per (b, h, 16-column tile of d_v) a chain wavefront and an
+// output wavefront; NT tiles per workgroup
 // ---------------------------------------------------------------------------
-struct __align__(16) StateSmem {
-    uint16_t wn[C][LDK];
-    uint16_t qt[C][LDK];
-    uint16_t kh[DK][LDP];   // Kh^T
-    uint16_t p[C][LDP];
-    float u0[C][LDX];
-    uint16_t ut[DVB][LDP];  // U^T, bf16
-    float gc[DK];
-    uint16_t St[DVB][LDK];  // incoming state, transposed, bf16
-};
-static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// The next chunk's record, loaded a chunk ahead.  The loads are inline
-// assembly so that the compiler cannot sink them down to the LDS stores that
-// consume them (which left no overlap); the compiler does not track their
-// completion, so the consumer waits for them explicitly, with the registers
-// tied to that wait.
-struct StatePrefetch {
-    u32x4_t wn[4], qt[4], kh[4], p[2], u0[2], gc;
-};
-
-SSLP_DEVICE u32x4_t pinned_load16(const void* p) {
-    u32x4_t v;
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-    return v;
-}
+// The chain wavefront keeps the tile's [128 x 16] fp32 state slice in MFMA
+// accumulators (8 tiles of 16 key channels) and walks the chunks:
+//     U = U0 + Wn S,   S = e^{g_C} S + Kh^T U.
+// S and U enter these products as B operands straight from their
+// accumulators (the record's k order matches, kperm), and it leaves both, as
+// bf16 operands, in LDS.  The output wavefront follows one chunk behind:
+//     O = Qt S + P U
+// from those operands, and stores O; it also issues the record DMAs (the
+// next chunk's chain part, this chunk's output part).  One barrier per chunk
+// step; every LDS buffer is double-buffered across it.  Fragments are read
+// with inline-assembly LDS reads (lds_dma.h): compiler-visible reads would
+// each wait for the DMAs in flight.
+// A step's DMAs (59 KB per workgroup) are bound by the misses a compute unit
+// keeps in flight, so their latency sets the step time.  The chain
+// wavefronts, idle for most of a step, therefore pull the record of chunk
+// c + WARM into L2 during step c: one dword per 128-byte line, each of the
+// NCB workgroups of a (b, h) a quarter of the lines, so that the DMAs a step
+// or two later hit L2 (170 -> 141 us for the kernel at B=4, T=4096, H=16).
+constexpr int NT = 2;                             // column tiles per state workgroup
+constexpr int RA_FR = REC_QT / FRAG + 2 * NT;     // chain part: Wn, Kh^T, e^{g_C}, U0 of the NT tiles (37)
+constexpr int RB_FR = REC_NSH - REC_QT / FRAG;    // output part: Qt, P (22)
+constexpr int X_BYTES = 6 * FRAG;                 // S (4 k blocks) and U (2) as B operands, per tile
+constexpr int WARM = 2;                           // chunks ahead that the chain wavefronts pull into L2
 
 template <typename io_t>
-__global__ __launch_bounds__(NTH) void gdn_state_kernel(GdnArgs a) {
-    __shared__ StateSmem ss;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int nblk = a.dv / DVB;
+__global__ __launch_bounds__(128 * NT) void gdn_state_kernel(GdnArgs a) {
+    constexpr int NCB = DK / (16 * NT);  // workgroups per (b, h) (d_v = DK)
+    static_assert(NCB * 16 * NT == DK && NT == 2, "column split");
+    __shared__ __align__(16) uint8_t RA[2][RA_FR * FRAG];
+    __shared__ __align__(16) uint8_t RB[2][RB_FR * FRAG];
+    __shared__ __align__(16) uint8_t X[2][NT][X_BYTES];
+    __shared__ __align__(16) uint32_t junk[64];  // destination of the L2 warming DMAs, never read
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const bool chain = w < NT;
+    const int tw = chain ? w : w - NT;  // the wavefront's tile within the workgroup
     // XCD-aware placement: consecutive workgroup ids go to the 8 XCDs in turn,
-    // so renumber them to keep the column blocks of one (batch, head) -- which
+    // so renumber them to keep the workgroups of one (batch, head) -- which
     // read the same chunk records at the same pace -- inside one XCD's L2.
     int id = blockIdx.x;
     if ((gridDim.x & 7u) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-    const int cb = id % nblk;
-    const int bh = id / nblk;
+    const int cb = id % NCB, bh = id / NCB;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-    const int n0 = cb * DVB;
+    const int n = 16 * (cb * NT + tw) + (lane & 15);  // this lane's column of d_v
     const int T = a.T, H = a.H, dv = a.dv, nch = a.nch;
     io_t* og = static_cast<io_t*>(a.o);
     const uint8_t* recb = a.rec + (size_t)bh * nch * REC_BYTES;
+    const size_t sbase = ((size_t)b * H + h) * DK * dv + n;  // S[b, h, i, n] at sbase + i dv
 
-    // state slice in accumulator layout: tiles (tm = 2w + x, tn = y)
-    f32x4_t S[2][2];
+    // state slice (chain wavefronts): tile it holds key channels 16 it + 4g + j of column n
+    f32x4_t S[8];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int it = 0; it < 8; ++it) S[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (chain && a.S0) {
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+        for (int it = 0; it < 8; ++it)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
-                const int n = 16 * y + (lane & 15);
-                S[x][y][j] = a.S0 ? a.S0[(((size_t)b * H + h) * DK + i) * dv + n0 + n] : 0.f;
-            }
+            for (int j = 0; j < 4; ++j) S[it][j] = a.S0[sbase + (size_t)(16 * it + 4 * g + j) * dv];
+    }
 
-    auto issue = [&](StatePrefetch& pf, int c) {
-        const uint8_t* r = recb + (size_t)c * REC_BYTES;
+    // record DMAs, issued by the output wavefronts (pieces split between them):
+    // the chain part of chunk ca and the output part of chunk cq (when < nch)
+    auto issue = [&](int ca, int cq) {
+        if (ca < nch) {
+            const uint8_t* r = recb + (size_t)ca * REC_BYTES;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int seg = tid + NTH * s;  // 16-byte piece of a [C][DK] bf16 tile
-            pf.wn[s] = pinned_load16(r + REC_WN + 16 * seg);
-            pf.qt[s] = pinned_load16(r + REC_QT + 16 * seg);
-            pf.kh[s] = pinned_load16(r + REC_KH + 16 * seg);
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) pf.p[s] = pinned_load16(r + REC_P + 16 * (tid + NTH * s));
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int seg = tid + NTH * s;  // row seg / 8, columns 4 (seg % 8) .. of the slice
-            pf.u0[s] = pinned_load16(r + REC_U0 + ((seg >> 3) * DK + n0 + 4 * (seg & 7)) * 4);
-        }
-        pf.gc = pinned_load16(r + REC_GC + 16 * (tid % (DK / 4)));  // used by tid < DK / 4
-    };
-    auto commit = [&](StatePrefetch& pf) {
-        // the pinned loads are not tracked by the compiler: wait for them here,
-        // with every register they fill tied to the wait
-        asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(pf.wn[0]), "+v"(pf.wn[1]), "+v"(pf.wn[2]), "+v"(pf.wn[3]),
-                       "+v"(pf.qt[0]), "+v"(pf.qt[1]), "+v"(pf.qt[2]), "+v"(pf.qt[3]),
-                       "+v"(pf.kh[0]), "+v"(pf.kh[1]), "+v"(pf.kh[2]), "+v"(pf.kh[3]),
-                       "+v"(pf.p[0]), "+v"(pf.p[1]), "+v"(pf.u0[0]), "+v"(pf.u0[1]), "+v"(pf.gc)
-                     :
-                     : "memory");
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int seg = tid + NTH * s;
-            const int row = seg / (DK / 8), col = (seg % (DK / 8)) * 8;
-            *reinterpret_cast<u32x4_t*>(&ss.wn[row][col]) = pf.wn[s];
-            *reinterpret_cast<u32x4_t*>(&ss.qt[row][col]) = pf.qt[s];
-            *reinterpret_cast<u32x4_t*>(&ss.kh[seg / (C / 8)][(seg % (C / 8)) * 8]) = pf.kh[s];
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int seg = tid + NTH * s;
-            const int row = seg / (C / 8), col = (seg % (C / 8)) * 8;
-            *reinterpret_cast<u32x4_t*>(&ss.p[row][col]) = pf.p[s];
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int seg = tid + NTH * s;
-            *reinterpret_cast<u32x4_t*>(&ss.u0[seg >> 3][4 * (seg & 7)]) = pf.u0[s];
-        }
-        if (tid < DK / 4) *reinterpret_cast<u32x4_t*>(&ss.gc[4 * tid]) = pf.gc;
-    };
-    auto publish_state = [&]() {
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int y = 0; y < 2; ++y)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
-                    const int n = 16 * y + (lane & 15);
-                    ss.St[n][i] = f32_to_bf16(S[x][y][j]).bits;
+            for (int k = 0; k < (RA_FR + NT - 1) / NT; ++k) {
+                const int pc = tw + NT * k;
+                if (pc < RA_FR) {
+                    const uint8_t* src = pc < REC_QT / FRAG ? r + pc * FRAG
+                                                            : r + REC_U0 + (cb * 2 * NT + pc - REC_QT / FRAG) * FRAG;
+                    dma16(src + 16 * lane, &RA[ca & 1][pc * FRAG]);
                 }
+            }
+        }
+        if (cq < nch) {
+            const uint8_t* r = recb + (size_t)cq * REC_BYTES + REC_QT;
+#pragma unroll
+            for (int k = 0; k < (RB_FR + NT - 1) / NT; ++k) {
+                const int pc = tw + NT * k;
+                if (pc < RB_FR) dma16(r + pc * FRAG + 16 * lane, &RB[cq & 1][pc * FRAG]);
+            }
+        }
+    };
+    auto bfpack = [](const f32x4_t& lo, const f32x4_t& hi) {  // two accumulator tiles as one B operand
+        bf16x8_t v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = bf(lo[j]);
+            v[4 + j] = bf(hi[j]);
+        }
+        return v;
+    };
+    auto frag = [](const u32x4& x) { return __builtin_bit_cast(bf16x8_t, x); };
+    auto put = [](uint32_t addr, const bf16x8_t& v) { lds_write_f32x4(addr, __builtin_bit_cast(f32x4, v)); };
+
+    f32x4_t O[4];  // output wavefronts: the last chunk's O, stored at the start of the next step
+    auto store_o = [&](int q) {
+        const int tq = q * C;
+        const int Tq = (T - tq) < C ? (T - tq) : C;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * rt + 4 * g + j;
+                if (t < Tq) og[(((size_t)b * T + tq + t) * H + h) * dv + n] = from_f32<io_t>(O[rt][j]);
+            }
     };
 
-    StatePrefetch pf;
     if (nch > 0) {  // T = 0: no records (the workspace may be empty); the state is copied
-        issue(pf, 0);
-        commit(pf);
-    }
-    publish_state();
-    block_sync_lds();
-
-    for (int c = 0; c < nch; ++c) {
-        const int t0 = c * C;
-        const int Tc = (T - t0) < C ? (T - t0) : C;
-        // the next chunk's record, in flight during this one; unconditional (the
-        // last chunk fetches its own record again) so the loads wait nowhere
-        issue(pf, c + 1 < nch ? c + 1 : c);
-
-        // ---- U = U0 + Wn S0 and Qt S0 for rows block w ----
-        f32x4_t u[2], o[2];
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            o[y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) u[y][j] = ss.u0[16 * w + (lane >> 4) * 4 + j][16 * y + (lane & 15)];
-        }
-#pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-            const int kc = 32 * s + (lane >> 4) * 8;
-            const bf16x8_t aw = load_bf16x8(&ss.wn[16 * w + (lane & 15)][kc]);
-            const bf16x8_t aq = load_bf16x8(&ss.qt[16 * w + (lane & 15)][kc]);
-#pragma unroll
-            for (int y = 0; y < 2; ++y) {
-                const bf16x8_t bs = load_bf16x8(&ss.St[16 * y + (lane & 15)][kc]);
-                u[y] = mfma_bf16(aw, bs, u[y]);
-                o[y] = mfma_bf16(aq, bs, o[y]);
-            }
-        }
-        // U^T (bf16): element (t, n) -> ut[n][t]
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                ss.ut[16 * y + (lane & 15)][16 * w + (lane >> 4) * 4 + j] = f32_to_bf16(u[y][j]).bits;
-        block_sync_lds();
-
-        // ---- O = Qt S0 + P U (causal) ----
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if (s == 1 && w < 2) continue;
-            const int kc = 32 * s + (lane >> 4) * 8;
-            const bf16x8_t ap = load_bf16x8(&ss.p[16 * w + (lane & 15)][kc]);
-#pragma unroll
-            for (int y = 0; y < 2; ++y) {
-                o[y] = mfma_bf16(ap, load_bf16x8(&ss.ut[16 * y + (lane & 15)][kc]), o[y]);
-            }
-        }
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 16 * w + (lane >> 4) * 4 + j;
-                const int n = 16 * y + (lane & 15);
-                if (t < Tc) og[(((size_t)b * T + t0 + t) * H + h) * dv + n0 + n] = from_f32<io_t>(o[y][j]);
-            }
-
-        // ---- S = e^{g_C} S0 + Kh^T U ----
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int y = 0; y < 2; ++y)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) S[x][y][j] *= ss.gc[16 * (2 * w + x) + (lane >> 4) * 4 + j];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int kc = 32 * s + (lane >> 4) * 8;  // tokens
-            bf16x8_t bu[2];
-#pragma unroll
-            for (int y = 0; y < 2; ++y) bu[y] = load_bf16x8(&ss.ut[16 * y + (lane & 15)][kc]);
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const bf16x8_t ak = load_bf16x8(&ss.kh[16 * (2 * w + x) + (lane & 15)][kc]);
-#pragma unroll
-                for (int y = 0; y < 2; ++y) S[x][y] = mfma_bf16(ak, bu[y], S[x][y]);
-            }
-        }
-        block_sync_lds();  // everyone is done with this chunk's LDS contents
-        commit(pf);
-        publish_state();
+        if (!chain) issue(0, nch);
+        wait_vm0();
         block_sync_lds();
     }
-
-    // final state slice
+    for (int c = 0; c <= nch && nch > 0; ++c) {
+        if (chain) {
+            if (c + WARM < nch) {  // this workgroup's quarter of chunk c + WARM's record into L2
+                constexpr int NL = REC_BYTES / 128, PER = (NL + NCB - 1) / NCB;
+                const uint8_t* r = recb + (size_t)(c + WARM) * REC_BYTES;
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 16 * (2 * w + x) + (lane >> 4) * 4 + j;
-                const int n = 16 * y + (lane & 15);
-                a.S_out[(((size_t)b * H + h) * DK + i) * dv + n0 + n] = S[x][y][j];
+                for (int k = 0; k < (PER + 63) / 64; ++k) {
+                    if ((k & 1) != tw) continue;  // the two chain wavefronts alternate
+                    const int e = 64 * k + lane;
+                    const int L = e < PER && cb * PER + e < NL ? cb * PER + e : cb * PER;
+                    dma4(r + (size_t)L * 128, &junk[0]);
+                }
             }
+            if (c < nch) {
+                const uint32_t ra = lds_addr(&RA[c & 1][0]);
+                const uint32_t fa = ra + 16 * lane;                              // lane's piece of fragment 0
+                const uint32_t ua = ra + (REC_QT / FRAG) * FRAG + tw * 2048 + 8 * lane;  // U0, row tile 0
+                const uint32_t ga = ra + REC_GC + 16 * g;                        // e^{g_C} of channels 4g ..
+                const uint32_t xa = lds_addr(&X[c & 1][tw][0]) + 16 * lane;
+
+                // S (before it decays) as B operands, kept for the output wavefront too
+                bf16x8_t sb[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    sb[kb] = bfpack(S[2 * kb], S[2 * kb + 1]);
+                    put(xa + kb * FRAG, sb[kb]);
+                }
+                u32x4 fr[2][8];
+                f32x2 u0v[4];
+                f32x4 gcv[8];
+                static_for<4>([&](auto rt) { u0v[rt] = lds_f32x2<rt * 512>(ua); });
+                static_for<8>([&](auto it) { gcv[it] = lds_f32x4<it * 64>(ga); });
+                static_for<8>([&](auto q) {  // Wn (rt, kb) for kb = 0, 1 at q = 2 rt + kb
+                    fr[0][q] = lds_u32x4<REC_WN + (4 * (q / 2) + q % 2) * FRAG>(fa);
+                });
+                lds_wait();
+                tie_all(u0v);
+                tie_all(gcv);
+                tie_all(fr[0]);
+                f32x4_t U[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const uint32_t x = __float_as_uint(u0v[rt][0]), y = __float_as_uint(u0v[rt][1]);
+                    U[rt] = f32x4_t{bf16lo(x), bf16hi(x), bf16lo(y), bf16hi(y)};
+                }
+#pragma unroll
+                for (int it = 0; it < 8; ++it)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) S[it][j] *= gcv[it][j];
+
+                // ---- U = U0 + Wn S: k blocks 0, 1, then 2, 3 ----
+                static_for<8>([&](auto q) { fr[1][q] = lds_u32x4<REC_WN + (4 * (q / 2) + 2 + q % 2) * FRAG>(fa); });
+#pragma unroll
+                for (int q = 0; q < 8; ++q) U[q / 2] = mfma_bf16(frag(fr[0][q]), sb[q % 2], U[q / 2]);
+                lds_wait();
+                tie_all(fr[1]);
+                static_for<8>([&](auto q) { fr[0][q] = lds_u32x4<REC_KH + q * FRAG>(fa); });  // Kh^T row tiles 0..3
+#pragma unroll
+                for (int q = 0; q < 8; ++q) U[q / 2] = mfma_bf16(frag(fr[1][q]), sb[2 + q % 2], U[q / 2]);
+                bf16x8_t ub[2];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    ub[kb] = bfpack(U[2 * kb], U[2 * kb + 1]);
+                    put(xa + (4 + kb) * FRAG, ub[kb]);
+                }
+                lds_wait();
+                tie_all(fr[0]);
+
+                // ---- S = e^{g_C} S + Kh^T U ----
+                static_for<8>([&](auto q) { fr[1][q] = lds_u32x4<REC_KH + (8 + q) * FRAG>(fa); });  // row tiles 4..7
+#pragma unroll
+                for (int q = 0; q < 8; ++q) S[q / 2] = mfma_bf16(frag(fr[0][q]), ub[q % 2], S[q / 2]);
+                lds_wait();
+                tie_all(fr[1]);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) S[4 + q / 2] = mfma_bf16(frag(fr[1][q]), ub[q % 2], S[4 + q / 2]);
+            }
+        } else {
+            // the previous chunk's outputs go out first, so that they complete during this step
+            if (c >= 2) store_o(c - 2);
+            issue(c + 1, c);
+            if (c >= 1) {
+                // ---- O = Qt S + P U for chunk c - 1 ----
+                const int q1 = c - 1;
+                const uint32_t fb = lds_addr(&RB[q1 & 1][0]) + 16 * lane;
+                const uint32_t xb = lds_addr(&X[q1 & 1][tw][0]) + 16 * lane;
+                u32x4 sv[4], uv[2], fr[2][8];
+                static_for<4>([&](auto kb) { sv[kb] = lds_u32x4<kb * FRAG>(xb); });
+                static_for<8>([&](auto q) {  // Qt (rt, kb) for kb = 0, 1 at q = 2 rt + kb
+                    fr[0][q] = lds_u32x4<(4 * (q / 2) + q % 2) * FRAG>(fb);
+                });
+                lds_wait();
+                tie_all(sv);
+                tie_all(fr[0]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                static_for<8>([&](auto q) { fr[1][q] = lds_u32x4<(4 * (q / 2) + 2 + q % 2) * FRAG>(fb); });
+#pragma unroll
+                for (int q = 0; q < 8; ++q) O[q / 2] = mfma_bf16(frag(fr[0][q]), frag(sv[q % 2]), O[q / 2]);
+                lds_wait();
+                tie_all(fr[1]);
+                static_for<2>([&](auto kb) { uv[kb] = lds_u32x4<(4 + kb) * FRAG>(xb); });
+                static_for<6>([&](auto q) { fr[0][q] = lds_u32x4<(16 + q) * FRAG>(fb); });  // P
+#pragma unroll
+                for (int q = 0; q < 8; ++q) O[q / 2] = mfma_bf16(frag(fr[1][q]), frag(sv[2 + q % 2]), O[q / 2]);
+                lds_wait();
+                tie_all(uv);
+                static_for<6>([&](auto q) { tie(fr[0][q]); });
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int kb = 0; kb <= rt / 2; ++kb) O[rt] = mfma_bf16(frag(fr[0][pfrag(rt, kb)]), frag(uv[kb]), O[rt]);
+            }
+            // this wavefront's DMAs have landed (and its stores completed)
+            wait_vm0();
+        }
+        block_sync_lds();
+    }
+
+    wait_vm0();  // no LDS-DMA may still be in flight when the workgroup ends
+    if (chain) {
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.S_out[sbase + (size_t)(16 * it + 4 * g + j) * dv] = S[it][j];
+    } else if (nch > 0) {
+        store_o(nch - 1);
+    }
 }
 
 }  // namespace
@@ -944,7 +1025,7 @@ hipError_t launch_gdn_chunk(int B, int T, int H, int dv, int dtype, int kda, con
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    gdn_state_kernel<bf16_t><<<(unsigned)(B * H * (dv / DVB)), NTH, 0, st>>>(a);
+    gdn_state_kernel<bf16_t><<<(unsigned)(B * H * (DK / (16 * NT))), 128 * NT, 0, st>>>(a);
     return hipGetLastError();
 }
 
