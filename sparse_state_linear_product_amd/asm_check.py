@@ -27,6 +27,8 @@ CHECKED = ["sdm_chunk.hip", "sdm_chunk_bwd.hip", "gdn_chunk.hip"]
 
 _VREG = re.compile(r"\b([va])(\d+)\b|\b([va])\[(\d+):(\d+)\]")
 _LABEL = re.compile(r"^(\.?L?BB[\w.]+|\.LBB[\w.]+):")
+# a basic block that no branch targets carries its label only as a comment
+_FALL_LABEL = re.compile(r"^;\s*(%bb\.\d+):")
 _BRANCH = re.compile(r"^\s*(s_branch|s_cbranch_\w+)\s+(\S+)")
 
 
@@ -73,7 +75,7 @@ def _blocks(lines):
         if in_asm:
             asm_buf.append(raw.strip())
             continue
-        m = _LABEL.match(raw.strip())
+        m = _LABEL.match(raw.strip()) or _FALL_LABEL.match(raw.strip())
         if m:
             blocks.append([label, cur, None])
             label, cur = m.group(1), []

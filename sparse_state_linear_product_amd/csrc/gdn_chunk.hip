@@ -159,6 +159,18 @@ SSLP_DEVICE f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 SSLP_DEVICE f32x4_t mfma_f32(float a, float b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// global loads written as inline assembly (the prep kernel's prefetch): the
+// compiler does not track them, so each is waited for explicitly (fetch_wait)
+SSLP_DEVICE u32x4 pin16(const void* p) {
+    u32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
+SSLP_DEVICE uint32_t pin4(const void* p) {
+    uint32_t v;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
 SSLP_DEVICE bf16x8_t load_bf16x8(const uint16_t* p) {
     return *reinterpret_cast<const bf16x8_t*>(p);
 }
@@ -223,13 +235,13 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
     // computed (zero past the sequence end, alpha 1, beta 0).
     constexpr int NSG = C * DK / 8 / NTH;      // 16-byte pieces of q, k, v per thread
     constexpr int NSA = KDA ? C * DK / 4 / NTH : 0;  // float4 pieces of alpha per thread
-    uint4 pk[NSG], pq[NSG], pv[NSG];
-    float4 pa[NSA > 0 ? NSA : 1];
-    float pbeta = 0.f, palpha = 1.f;
+    u32x4 pk[NSG], pq[NSG], pv[NSG];
+    u32x4 pa[NSA > 0 ? NSA : 1];
+    uint32_t pbeta_u = 0u, palpha_u = 0u;  // bits of beta and alpha of token row lane
     // GDN2: the write vector of this thread's V pieces, and the erase values of
     // its decay-pass tokens (channel tid % DK, tokens 32 (tid / DK) ..), also a chunk ahead
-    float4 pw[G2 ? NSG : 1][2];
-    float pbv[G2 ? 32 : 1];
+    u32x4 pw[G2 ? NSG : 1][2];
+    uint32_t pbv[G2 ? 32 : 1];
     // Loads come from clamped (always valid) token rows and are masked where
     // they are stored, so no load waits on a condition (a conditional load
     // would be followed by a wait for its value at the branch join).
@@ -239,16 +251,19 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
         const int b = bh / H, h = bh - (bh / H) * H;
         const int t0 = c * C;
         pt0 = t0;
-        // piece i of a thread: token row = lane, columns 8 (w + 4 i) .. + 7, so that
-        // the transposed stores of V below hit 64 different rows at once
+        // K and Q piece i of a thread: 16 lanes per token row (one contiguous
+        // 256-byte row, rows (tid + NTH i) / 16), so that a load touches 8 lines;
+        // V piece i: token row = lane, columns 8 (w + 4 i) .. + 7, so that the
+        // transposed stores of V below hit 64 different rows at once
 #pragma unroll
         for (int i = 0; i < NSG; ++i) {
-            const int row = lane, col = 8 * (w + (NTH / 64) * i);
-            const int t = min(t0 + row, T - 1);
-            const size_t off = (((size_t)b * T + t) * H + h) * DK + col;
-            pk[i] = *reinterpret_cast<const uint4*>(kg + off);
-            pq[i] = *reinterpret_cast<const uint4*>(qg + off);
-            pv[i] = *reinterpret_cast<const uint4*>(vg + (((size_t)b * T + t) * H + h) * dv + col);
+            const int seg = tid + NTH * i;
+            const int tk = min(t0 + (seg >> 4), T - 1);
+            const size_t koff = (((size_t)b * T + tk) * H + h) * DK + (seg & 15) * 8;
+            pk[i] = pin16(kg + koff);
+            pq[i] = pin16(qg + koff);
+            const int t = min(t0 + lane, T - 1);
+            pv[i] = pin16(vg + (((size_t)b * T + t) * H + h) * dv + 8 * (w + (NTH / 64) * i));
         }
         if constexpr (KDA) {
 #pragma unroll
@@ -256,7 +271,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
                 const int seg = tid + NTH * i;
                 const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
                 const int t = min(t0 + row, T - 1);
-                pa[i] = *reinterpret_cast<const float4*>(a.alpha + (((size_t)b * T + t) * H + h) * DK + col);
+                pa[i] = pin16(a.alpha + (((size_t)b * T + t) * H + h) * DK + col);
             }
         }
         if constexpr (G2) {
@@ -265,24 +280,46 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
                 const int col = 8 * (w + (NTH / 64) * i);
                 const int t = min(t0 + lane, T - 1);
                 const float* wr = a.wvec + (((size_t)b * T + t) * H + h) * dv + col;
-                pw[i][0] = *reinterpret_cast<const float4*>(wr);
-                pw[i][1] = *reinterpret_cast<const float4*>(wr + 4);
+                pw[i][0] = pin16(wr);
+                pw[i][1] = pin16(wr + 4);
             }
             const int ch = tid & (DK - 1), hf = tid >> 7;
 #pragma unroll
             for (int r = 0; r < 32; ++r) {
                 const int t = min(t0 + 32 * hf + r, T - 1);
-                pbv[r] = a.bvec[(((size_t)b * T + t) * H + h) * DK + ch];
+                pbv[r] = pin4(a.bvec + (((size_t)b * T + t) * H + h) * DK + ch);
             }
         }
         {  // every wave: the gates of token row = lane
             const int t = min(t0 + lane, T - 1);
             const size_t bth = ((size_t)b * T + t) * H + h;
-            pbeta = G2 ? 1.f : a.beta[bth];
-            if (!KDA) palpha = a.alpha[bth];
+            // GDN2 has no beta (its pointer is null), KDA's alphas are per channel
+            if constexpr (!G2) pbeta_u = pin4(a.beta + bth);
+            if constexpr (!KDA) palpha_u = pin4(a.alpha + bth);
+        }
+    };
+    // The fetch is issued with inline-assembly loads, which the compiler does
+    // not track: it would otherwise wait for them, at their first use in the
+    // next chunk, with a count that also covers every record store issued
+    // after them (loads and stores share the counter), exposing the stores'
+    // completion.  Instead the loads are waited for explicitly, before the
+    // chunk's last record stores (U0 and Wn), by when they have long landed.
+    auto fetch_wait = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        tie_all(pk);
+        tie_all(pq);
+        tie_all(pv);
+        tie_all(pa);
+        tie(pbeta_u);
+        tie(palpha_u);
+        if constexpr (G2) {
+#pragma unroll
+            for (int i = 0; i < NSG; ++i) tie_all(pw[i]);
+            tie_all(pbv);
         }
     };
     if ((int)blockIdx.x < ntask) fetch(blockIdx.x);
+    fetch_wait();
     for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int c = task % nch;
 
@@ -291,23 +328,25 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
     // X = diag(beta) V, stored transposed (bf16); K, Q as they are; rows past
     // the sequence end are zero (alpha 1, beta 0)
     const bool rowin = pt0 + lane < T;
-    if (!rowin) {
-        pbeta = 0.f;
-        palpha = 1.f;
-    }
+    const float pbeta = !rowin ? 0.f : G2 ? 1.f : __uint_as_float(pbeta_u);
+    const float palpha = !rowin || KDA ? 1.f : __uint_as_float(palpha_u);
 #pragma unroll
     for (int i = 0; i < NSG; ++i) {
         const int row = lane, col = 8 * (w + (NTH / 64) * i);
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        if (!rowin) pk[i] = pq[i] = pv[i] = z;
-        *reinterpret_cast<uint4*>(&sm.k[row][col]) = pk[i];
-        *reinterpret_cast<uint4*>(&sm.q[row][col]) = pq[i];
+        const int seg = tid + NTH * i, krow = seg >> 4, kcol = (seg & 15) * 8;
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        if (pt0 + krow >= T) pk[i] = pq[i] = z;
+        if (!rowin) pv[i] = z;
+        *reinterpret_cast<u32x4*>(&sm.k[krow][kcol]) = pk[i];
+        *reinterpret_cast<u32x4*>(&sm.q[krow][kcol]) = pq[i];
         const uint16_t* ve = reinterpret_cast<const uint16_t*>(&pv[i]);
         float sc[8];
         if constexpr (G2) {  // X = w (.) V (rows past the end: V is zero already)
-            const float4 w0 = pw[i][0], w1 = pw[i][1];
-            sc[0] = w0.x, sc[1] = w0.y, sc[2] = w0.z, sc[3] = w0.w;
-            sc[4] = w1.x, sc[5] = w1.y, sc[6] = w1.z, sc[7] = w1.w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sc[e] = __uint_as_float(pw[i][0][e]);
+                sc[4 + e] = __uint_as_float(pw[i][1][e]);
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) sc[e] = pbeta;
@@ -320,8 +359,8 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
         for (int i = 0; i < NSA; ++i) {
             const int seg = tid + NTH * i;
             const int row = seg / (DK / 4), col = (seg % (DK / 4)) * 4;
-            *reinterpret_cast<float4*>(&sm.u.alpha[row][col]) =
-                pt0 + row < T ? pa[i] : make_float4(1.f, 1.f, 1.f, 1.f);
+            *reinterpret_cast<u32x4*>(&sm.u.alpha[row][col]) =
+                pt0 + row < T ? pa[i] : u32x4{0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u};
         }
     }
     if (tid < C) {  // wave 0: lane = token
@@ -365,7 +404,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
                 float bv[16];
                 if constexpr (G2) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) bv[r] = pbv[16 * bb + r];
+                    for (int r = 0; r < 16; ++r) bv[r] = __uint_as_float(pbv[16 * bb + r]);
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -551,7 +590,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
         // write A (strictly lower, beta and decay applied) to LDS, and P's
         // fragments (row tile 3-w) to the record
         {
-            float pv[4][4];
+            float pvals[4][4];
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) {
 #pragma unroll
@@ -572,22 +611,22 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
                         p = pt[tn][j];
                         if (!KDA) p *= __expf(sm.g[tp] - sm.g[jp]);
                     }
-                    pv[tn][j] = p;
+                    pvals[tn][j] = p;
                 }
             }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (2 * kb > pr) continue;  // the fragment (pr, 1) exists for pr >= 2
-                uint32_t pw[4];
+                uint32_t pwd[4];
 #pragma unroll
                 for (int s = 0; s < 4; s += 2) {
-                    pw[s / 2] = (uint32_t)f32_to_bf16(pv[2 * kb][s]).bits |
-                                ((uint32_t)f32_to_bf16(pv[2 * kb][s + 1]).bits << 16);
-                    pw[2 + s / 2] = (uint32_t)f32_to_bf16(pv[2 * kb + 1][s]).bits |
-                                    ((uint32_t)f32_to_bf16(pv[2 * kb + 1][s + 1]).bits << 16);
+                    pwd[s / 2] = (uint32_t)f32_to_bf16(pvals[2 * kb][s]).bits |
+                                 ((uint32_t)f32_to_bf16(pvals[2 * kb][s + 1]).bits << 16);
+                    pwd[2 + s / 2] = (uint32_t)f32_to_bf16(pvals[2 * kb + 1][s]).bits |
+                                     ((uint32_t)f32_to_bf16(pvals[2 * kb + 1][s + 1]).bits << 16);
                 }
                 *reinterpret_cast<uint4*>(rec + REC_P + pfrag(pr, kb) * FRAG + 16 * lane) =
-                    make_uint4(pw[0], pw[1], pw[2], pw[3]);
+                    make_uint4(pwd[0], pwd[1], pwd[2], pwd[3]);
             }
         }
         block_sync_lds();
@@ -690,6 +729,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             const int t = e / C, j = e % C;
             sm.tb[t][j] = f32_to_bf16(sm.u.s.Tm[t][j]).bits;
         }
+        fetch_wait();  // the next chunk's inputs (issued a chunk ago) before the last stores
         block_sync_lds();
         {
             // U0 tiles (rows block w, column tile y) in accumulator order, and

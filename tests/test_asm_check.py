@@ -53,6 +53,26 @@ v_mov_b32 v21, v7
     assert _check(body.replace("v_mov_b32 v21, v7", f"{WAIT}\nv_mov_b32 v21, v7")) == []
 
 
+def test_fallthrough_blocks_labelled_by_comments_are_separate():
+    # the compiler labels a block that no branch targets only in a comment; the
+    # branch around it must not carry its load into the branch target
+    body = f"""
+s_cbranch_scc1 .LBB0_2
+; %bb.1:
+{LOAD}
+s_branch .LBB0_3
+.LBB0_2:
+v_mov_b32 v4, 0
+.LBB0_3:
+{WAIT}
+v_mov_b32 v9, v4
+"""
+    assert _check(body) == []
+    # falling through from the load block into a use is still reported
+    rep = _check(body.replace("s_branch .LBB0_3\n", "v_mov_b32 v10, v5\n"))
+    assert rep and ("v", 5) in rep[0][1]
+
+
 def test_lds_reads_are_tracked_by_lgkmcnt():
     rd = ";;#ASMSTART\nds_read_b64 v[2:3], v1 offset:16\n;;#ASMEND"
     assert _check(f"{rd}\ns_waitcnt vmcnt(0)\nv_mov_b32 v9, v2") != []
