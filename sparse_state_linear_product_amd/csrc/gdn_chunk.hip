@@ -394,40 +394,49 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             }
         } else {
             // thread (channel i, half hf) walks the 32 tokens of blocks 2hf, 2hf+1:
-            // E+ = product of alphas after the block's first token, E- = 1/E+
+            // E+ = product of alphas after the block's first token, E- = 1/E+.
+            // All 32 tokens' alphas, keys and queries are read before the two
+            // blocks' product chains run side by side.
             const int i = tid & (DK - 1), hf = tid >> 7;
+            float al[2][16], kv[2][16], qv[2][16];
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const int blk = 2 * hf + bb;
-                float ep = 1.f, em = 1.f, pall = 1.f;
-                // GDN2: the block's 16 erase values (prefetched with the chunk)
-                float bv[16];
-                if constexpr (G2) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) bv[r] = __uint_as_float(pbv[16 * bb + r]);
-                }
+            for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int t = 16 * blk + r;
-                    const float al = sm.u.alpha[t][i];
-                    pall *= al;
+                    const int t = 16 * (2 * hf + bb) + r;
+                    al[bb][r] = sm.u.alpha[t][i];
+                    kv[bb][r] = bf2f(sm.k[t][i]);
+                    qv[bb][r] = bf2f(sm.q[t][i]);
+                }
+            float ep[2] = {1.f, 1.f}, em[2] = {1.f, 1.f}, pall[2] = {1.f, 1.f};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {
+                    const int t = 16 * (2 * hf + bb) + r;
+                    const float a_ = al[bb][r];
+                    pall[bb] *= a_;
                     if (r > 0) {
-                        ep *= al;
+                        ep[bb] *= a_;
                         // hardware reciprocal (within 1 ulp): Km is rounded to bf16.
                         // Exact for decays >= 2^-4 (the block's inverse product stays
                         // <= 2^60); below, the clamp keeps every factor finite
-                        em = fminf(em * __builtin_amdgcn_rcpf(al), kMaxInvDecay);
+                        em[bb] = fminf(em[bb] * __builtin_amdgcn_rcpf(a_), kMaxInvDecay);
                     }
-                    const float kv = bf2f(sm.k[t][i]), qv = bf2f(sm.q[t][i]);
-                    float ke = kv;  // the key of A's rows and of Wn: b (.) k for GDN2
-                    if constexpr (G2) ke *= c * C + t < T ? bv[r] : 0.f;
-                    sm.k[t][i] = f32_to_bf16(ke * ep).bits;
-                    sm.km[t][i] = f32_to_bf16(kv * em).bits;
-                    sm.q[t][i] = f32_to_bf16(qv * ep).bits;
+                    float ke = kv[bb][r];  // the key of A's rows and of Wn: b (.) k for GDN2
+                    // GDN2: the erase value of this token (prefetched with the chunk)
+                    if constexpr (G2) ke *= c * C + t < T ? __uint_as_float(pbv[16 * bb + r]) : 0.f;
+                    sm.k[t][i] = f32_to_bf16(ke * ep[bb]).bits;
+                    sm.km[t][i] = f32_to_bf16(kv[bb][r] * em[bb]).bits;
+                    sm.q[t][i] = f32_to_bf16(qv[bb][r] * ep[bb]).bits;
                 }
-                sm.uw.blk.pa[blk][i] = pall;
-                sm.uw.blk.px[blk][i] = ep;
-                sm.uw.blk.af[blk][i] = sm.u.alpha[16 * blk][i];
+            }
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const int blk = 2 * hf + bb;
+                sm.uw.blk.pa[blk][i] = pall[bb];
+                sm.uw.blk.px[blk][i] = ep[bb];
+                sm.uw.blk.af[blk][i] = al[bb][0];
             }
         }
         block_sync_lds();
