@@ -239,8 +239,18 @@ __global__ __launch_bounds__(256) void sdm_bwd_reduce_kernel(SdmBwdArgs a, long 
     const long long bth = i / NP;
     const int j = (int)(i - bth * NP);
     const float* pp = a.part + (size_t)bth * nslice * NP + j;
+    // slices added in order; their loads are issued 16 at a time (a loop of
+    // single loads waited for one memory round trip per slice)
     float s = 0.f;
-    for (int k = 0; k < nslice; ++k) s += pp[(size_t)k * NP];
+    int k = 0;
+    for (; k + 16 <= nslice; k += 16) {
+        float x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x[u] = pp[(size_t)(k + u) * NP];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += x[u];
+    }
+    for (; k < nslice; ++k) s += pp[(size_t)k * NP];
     if (j == 0) a.dalpha[bth] = s;
     else if (j == 1) a.dbeta[bth] = s;
     else if (j < 2 + W) a.dwt_w[bth * W + (j - 2)] = s;

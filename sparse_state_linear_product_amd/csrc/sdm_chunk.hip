@@ -96,36 +96,44 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     const int c = blockIdx.x % nch, bh = blockIdx.x / nch;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const int t0 = c * CC;
-    // a chunk holding a slot index outside [0, N) is planned as an empty chunk:
-    // its tokens write nothing and read nothing (y = 0), and no row offset
-    // outside the table reaches the apply kernel
+    // S1: load the chunk's addressing (every load of a thread issued before any
+    // is used).  A chunk holding a slot index outside [0, N) is planned as an
+    // empty chunk: its tokens write nothing and read nothing (y = 0), and no
+    // row offset outside the table reaches the apply kernel.
+    static_assert(NE % 256 == 0, "whole passes of the 256 threads");
+    const uint64_t NONE = ~0ull;
     __shared__ int s_bad;
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    {
-        const int nt = a.T - t0 < CC ? a.T - t0 : CC;
-        for (int e = tid; e < nt * NW; e += 256) {
-            const size_t bth = ((size_t)b * a.T + t0 + (e >> LOGNW)) * a.H + h;
-            const unsigned sw = (unsigned)a.idx_w[bth * NW + (e & (NW - 1))];
-            const unsigned sr = (unsigned)a.idx_r[bth * NR + (e & (NW - 1))];
-            if (sw >= (unsigned)a.N || sr >= (unsigned)a.N) s_bad = 1;
-        }
+    const int nt = a.T - t0 < CC ? a.T - t0 : CC;
+    bool bad = false;
+    // (rows past the sequence end load the last token's values, then unused)
+    unsigned sw[NE / 256], sr[NE / 256];
+    float ww[NE / 256], wr[NE / 256], al = 1.f, be = 0.f;
+#pragma unroll
+    for (int r = 0; r < NE / 256; ++r) {
+        const int e = tid + 256 * r;
+        const int t = e >> LOGNW < nt ? e >> LOGNW : nt - 1, i = e & (NW - 1);
+        const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
+        sw[r] = (unsigned)a.idx_w[bth * NW + i];
+        sr[r] = (unsigned)a.idx_r[bth * NR + i];
+        ww[r] = a.wt_w[bth * NW + i];
+        wr[r] = a.wt_r[bth * NR + i];
     }
-    __syncthreads();
-    if (s_bad && tid == 0 && a.err != nullptr) atomicOr(a.err, 1u);
-    const int ntok = s_bad ? 0 : (a.T - t0 < CC ? a.T - t0 : CC);
-    uint32_t* out = a.plan + (size_t)blockIdx.x * PL_WORDS;
-    const uint64_t NONE = ~0ull;
-
-    // S1: load the chunk's addressing
-    for (int e = tid; e < NE; e += 256) {
-        const int t = e >> LOGNW, i = e & (NW - 1);
-        if (t < ntok) {
-            const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
-            key[e] = ((uint64_t)(uint32_t)a.idx_w[bth * NW + i] << 9) | (uint64_t)e;
-            s_ww[e] = a.wt_w[bth * NW + i];
-            s_ir[e] = a.idx_r[bth * NR + i];
-            s_wr[e] = a.wt_r[bth * NR + i];
+    if (tid < CC) {
+        const size_t bth = ((size_t)b * a.T + t0 + (tid < nt ? tid : nt - 1)) * a.H + h;
+        al = a.alpha[bth];
+        be = a.beta[bth];
+    }
+#pragma unroll
+    for (int r = 0; r < NE / 256; ++r) {
+        const int e = tid + 256 * r;
+        if ((e >> LOGNW) < nt) {
+            bad |= sw[r] >= (unsigned)a.N || sr[r] >= (unsigned)a.N;
+            key[e] = ((uint64_t)sw[r] << 9) | (uint64_t)e;
+            s_ww[e] = ww[r];
+            s_ir[e] = (int)sr[r];
+            s_wr[e] = wr[r];
         } else {
             key[e] = NONE;
             s_ww[e] = 0.f;
@@ -136,12 +144,30 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         s_ffill[e] = 0;
     }
     if (tid < CC) {
-        const bool ok = tid < ntok;
-        const size_t bth = ((size_t)b * a.T + t0 + tid) * a.H + h;
-        s_al[tid] = ok ? a.alpha[bth] : 1.f;
-        s_be[tid] = ok ? a.beta[bth] : 0.f;
+        const bool ok = tid < nt;
+        s_al[tid] = ok ? al : 1.f;
+        s_be[tid] = ok ? be : 0.f;
     }
+    if (bad) s_bad = 1;
     __syncthreads();
+    if (s_bad) {  // (a uniform branch) plan the chunk as empty
+        if (tid == 0 && a.err != nullptr) atomicOr(a.err, 1u);
+#pragma unroll
+        for (int r = 0; r < NE / 256; ++r) {
+            const int e = tid + 256 * r;
+            key[e] = NONE;
+            s_ww[e] = 0.f;
+            s_ir[e] = -1;
+            s_wr[e] = 0.f;
+        }
+        if (tid < CC) {
+            s_al[tid] = 1.f;
+            s_be[tid] = 0.f;
+        }
+        __syncthreads();
+    }
+    const int ntok = s_bad ? 0 : nt;
+    uint32_t* out = a.plan + (size_t)blockIdx.x * PL_WORDS;
 
     // S2: bitonic sort of the 512 keys, ascending
     for (int k = 2; k <= NE; k <<= 1) {

@@ -96,11 +96,24 @@ __global__ __launch_bounds__(256) void sdm_chunk_bwd_plan_kernel(BwdPlanArgs a) 
     if (tid == 0) s_bad = 0;
     __syncthreads();
     const int nt = a.T - t0 < CC ? a.T - t0 : CC;
-    for (int e = tid; e < nt * NW; e += 256) {
-        const size_t bth = ((size_t)b * a.T + t0 + (e >> LOGNW)) * a.H + h;
-        const unsigned sw = (unsigned)a.idx_w[bth * NW + (e & (NW - 1))];
-        const unsigned sr = (unsigned)a.idx_r[bth * NR + (e & (NW - 1))];
-        if (sw >= (unsigned)a.N || sr >= (unsigned)a.N) s_bad = 1;
+    {
+        // every load issued before any test (rows past the end load the last
+        // token's indices, then unused)
+        static_assert(NE % 256 == 0, "whole passes of the 256 threads");
+        unsigned sw[NE / 256], sr[NE / 256];
+#pragma unroll
+        for (int r = 0; r < NE / 256; ++r) {
+            const int e = tid + 256 * r;
+            const int t = (e >> LOGNW) < nt ? (e >> LOGNW) : nt - 1;
+            const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
+            sw[r] = (unsigned)a.idx_w[bth * NW + (e & (NW - 1))];
+            sr[r] = (unsigned)a.idx_r[bth * NR + (e & (NW - 1))];
+        }
+        bool bad = false;
+#pragma unroll
+        for (int r = 0; r < NE / 256; ++r)
+            bad |= ((tid + 256 * r) >> LOGNW) < nt && (sw[r] >= (unsigned)a.N || sr[r] >= (unsigned)a.N);
+        if (bad) s_bad = 1;
     }
     __syncthreads();
     const int ntok = s_bad ? 0 : nt;

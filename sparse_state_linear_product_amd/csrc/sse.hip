@@ -754,13 +754,20 @@ __global__ __launch_bounds__(256) void sse_combine_kernel(const bf16_t* __restri
     if (idx >= nquad) return;
     const long long pth = idx / (dv / 4);
     const int c = (int)(idx - pth * (dv / 4)) * 4;
+    // every slot's load is issued before the sums (slots past K1 re-read the
+    // last one and are not added), which are taken in slot order
+    uint2 u[MAXK + 1];
+#pragma unroll
+    for (int r = 0; r <= MAXK; ++r)
+        u[r] = *reinterpret_cast<const uint2*>(opart + ((size_t)pth * K1 + (r < K1 ? r : K1 - 1)) * dv + c);
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    for (int r = 0; r < K1; ++r) {
-        const uint2 u = *reinterpret_cast<const uint2*>(opart + ((size_t)pth * K1 + r) * dv + c);
-        s0 += __uint_as_float(u.x << 16);
-        s1 += __uint_as_float(u.x & 0xFFFF0000u);
-        s2 += __uint_as_float(u.y << 16);
-        s3 += __uint_as_float(u.y & 0xFFFF0000u);
+#pragma unroll
+    for (int r = 0; r <= MAXK; ++r) {
+        const bool in = r < K1;  // adding +0 for the slots past K1 leaves each sum unchanged
+        s0 += in ? __uint_as_float(u[r].x << 16) : 0.f;
+        s1 += in ? __uint_as_float(u[r].x & 0xFFFF0000u) : 0.f;
+        s2 += in ? __uint_as_float(u[r].y << 16) : 0.f;
+        s3 += in ? __uint_as_float(u[r].y & 0xFFFF0000u) : 0.f;
     }
     io_t* dst = o + (size_t)pth * dv + c;
     dst[0] = from_f32<io_t>(s0);
