@@ -819,6 +819,7 @@ template <typename io_t>
 __global__ __launch_bounds__(128 * NT) void gdn_state_kernel(GdnArgs a) {
     constexpr int NCB = DK / (16 * NT);  // workgroups per (b, h) (d_v = DK)
     static_assert(NCB * 16 * NT == DK && NT == 2, "column split");
+    static_assert((2 * (RA_FR + RB_FR) * FRAG + 2 * NT * X_BYTES + 256) <= 160 * 1024, "LDS budget");
     __shared__ __align__(16) uint8_t RA[2][RA_FR * FRAG];
     __shared__ __align__(16) uint8_t RB[2][RB_FR * FRAG];
     __shared__ __align__(16) uint8_t X[2][NT][X_BYTES];
