@@ -118,6 +118,26 @@ def test_gdn2_small(T):
     assert e_o <= TOL_BF16 and e_S <= TOL_BF16
 
 
+@pytest.mark.parametrize("mode", ["gdn", "kda", "gdn2"])
+@pytest.mark.parametrize("B,H,T", [(1, 3, 129), (3, 1, 260), (1, 1, 64 * 7 + 5)])
+def test_gdn_head_counts_off_the_xcd_grouping(mode, B, H, T):
+    # an odd number of (batch, head) pairs gives a state grid that is not a
+    # multiple of the 8 XCDs (workgroups keep their launch order), and 3 to 8
+    # chunks exercise the record pulled into L2 two chunks ahead near the end
+    announce(f"{mode} B={B} H={H} T={T}")
+    if mode == "gdn2":
+        x = wl.gdn2_inputs(wl.GDN2, T=T, B=B, H=H, seed=700 + T)
+        o, S = _run2(x)
+        Sr, orf = _ref2(x)
+        e_o, e_S = maxrel(o.double().numpy(), orf, name="o"), maxrel(S.double().numpy(), Sr, name="S")
+        assert np.isfinite(o.float().numpy()).all() and np.isfinite(S.numpy()).all()
+        assert e_o <= TOL_BF16 and e_S <= TOL_BF16, f"o {e_o} S {e_S}"
+    else:
+        kda = mode == "kda"
+        x = wl.gdn_inputs(wl.KDA if kda else wl.GDN, T=T, B=B, H=H, seed=600 + T)
+        _check(x, kda, tag=f"{mode} B={B} H={H} T={T}")
+
+
 def test_gdn2_with_initial_state_and_kda_reduction():
     # with S0; and b = w = beta on every channel, which the slide states is KDA
     announce("gdn2_chunk_forward with S0; b = w = beta 1 vs the KDA oracle")
