@@ -533,12 +533,20 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
         }
         block_sync_lds();
         // (diag(beta) Kt)^T for Wn: Kt = K e^{g_t} (GDN) or Kp F[block] (KDA)
-        for (int e = tid; e < C * DK; e += NTH) {
-            const int i = e / C, t = e % C;
-            float kt;
-            if constexpr (!KDA) kt = bf2f(sm.k[t][i]) * sm.eg[t];
-            else kt = bf2f(sm.k[t][i]) * sm.F[t >> 4][i];
-            sm.kbt[i][t] = f32_to_bf16(sm.beta[t] * kt).bits;
+        // (four key channels of one token per step: one 8-byte read of K)
+#pragma unroll 2
+        for (int e = tid; e < C * DK / 4; e += NTH) {
+            const int i4 = (e / C) * 4, t = e % C;
+            const uint2 kr = *reinterpret_cast<const uint2*>(&sm.k[t][i4]);
+            const float kv[4] = {bf16lo(kr.x), bf16hi(kr.x), bf16lo(kr.y), bf16hi(kr.y)};
+            const float bt = sm.beta[t];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float kt;
+                if constexpr (!KDA) kt = kv[u] * sm.eg[t];
+                else kt = kv[u] * sm.F[t >> 4][i4 + u];
+                sm.kbt[i4 + u][t] = f32_to_bf16(bt * kt).bits;
+            }
         }
         // ---- Qt, Kh^T fragments and e^{g_C} into the record: the last reads of
         //      Q and K.  Wave w writes Qt's row tile w and Kh^T's row tiles 2w, 2w+1 ----
