@@ -245,12 +245,15 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
     // Loads come from clamped (always valid) token rows and are masked where
     // they are stored, so no load waits on a condition (a conditional load
     // would be followed by a wait for its value at the branch join).
+    // The fetch goes out in three parts at three points of the chunk (after
+    // the staging, after the decay pass, after K K^T), so that no wavefront
+    // stalls on all of its 48 KB of requests at once.
     int pt0 = 0;  // first token of the fetched chunk
-    auto fetch = [&](int task) {
+    auto fetch = [&](int task, int part) {
         const int c = task % nch, bh = task / nch;
         const int b = bh / H, h = bh - (bh / H) * H;
         const int t0 = c * C;
-        pt0 = t0;
+        if (part == 0) pt0 = t0;
         // K and Q piece i of a thread: 16 lanes per token row (one contiguous
         // 256-byte row, rows (tid + NTH i) / 16), so that a load touches 8 lines;
         // V piece i: token row = lane, columns 8 (w + 4 i) .. + 7, so that the
@@ -260,10 +263,24 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             const int seg = tid + NTH * i;
             const int tk = min(t0 + (seg >> 4), T - 1);
             const size_t koff = (((size_t)b * T + tk) * H + h) * DK + (seg & 15) * 8;
-            pk[i] = pin16(kg + koff);
-            pq[i] = pin16(qg + koff);
+            if (part == 0) pk[i] = pin16(kg + koff);
+            if (part == 1) pq[i] = pin16(qg + koff);
             const int t = min(t0 + lane, T - 1);
-            pv[i] = pin16(vg + (((size_t)b * T + t) * H + h) * dv + 8 * (w + (NTH / 64) * i));
+            if (part == 2) pv[i] = pin16(vg + (((size_t)b * T + t) * H + h) * dv + 8 * (w + (NTH / 64) * i));
+        }
+        if (part != 2) {
+            // GDN2: the erase values, read by this chunk's decay pass, go out after it
+            if constexpr (G2) {
+                if (part == 1) {
+                    const int ch = tid & (DK - 1), hf = tid >> 7;
+#pragma unroll
+                    for (int r = 0; r < 32; ++r) {
+                        const int t = min(t0 + 32 * hf + r, T - 1);
+                        pbv[r] = pin4(a.bvec + (((size_t)b * T + t) * H + h) * DK + ch);
+                    }
+                }
+            }
+            return;
         }
         if constexpr (KDA) {
 #pragma unroll
@@ -282,12 +299,6 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
                 const float* wr = a.wvec + (((size_t)b * T + t) * H + h) * dv + col;
                 pw[i][0] = pin16(wr);
                 pw[i][1] = pin16(wr + 4);
-            }
-            const int ch = tid & (DK - 1), hf = tid >> 7;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                const int t = min(t0 + 32 * hf + r, T - 1);
-                pbv[r] = pin4(a.bvec + (((size_t)b * T + t) * H + h) * DK + ch);
             }
         }
         {  // every wave: the gates of token row = lane
@@ -318,7 +329,11 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             tie_all(pbv);
         }
     };
-    if ((int)blockIdx.x < ntask) fetch(blockIdx.x);
+    if ((int)blockIdx.x < ntask) {
+        fetch(blockIdx.x, 0);
+        fetch(blockIdx.x, 1);
+        fetch(blockIdx.x, 2);
+    }
     fetch_wait();
     for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int c = task % nch;
@@ -369,9 +384,10 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
     }
     // the next chunk's inputs, in flight during this chunk (the last chunk
     // fetches itself again: an unconditional fetch keeps the loads free of
-    // waits); GDN2 fetches after the decay pass, which reads this chunk's
-    // prefetched erase values
-    if constexpr (!G2) fetch(task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task);
+    // waits); its K now, Q (and GDN2's erase values, which this chunk's decay
+    // pass reads) after the decay pass, the rest after K K^T
+    const int nxt = task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task;
+    fetch(nxt, 0);
     block_sync_lds();
 
         // ---------------- decay bookkeeping ----------------
@@ -440,7 +456,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             }
         }
         block_sync_lds();
-        if constexpr (G2) fetch(task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task);
+        fetch(nxt, 1);
         if constexpr (KDA) {
             // per channel: F[m] = e^{g_{16m}}, H[m] = e^{g_C - g_{16m}},
             // D[m][n] = e^{g_{16m} - g_{16n}}, all as products of alphas
@@ -532,6 +548,7 @@ SSLP_DEVICE void gdn_prep_body(const GdnArgs& a, int ntask, SM& sm) {
             }
         }
         block_sync_lds();
+        fetch(nxt, 2);
         // (diag(beta) Kt)^T for Wn: Kt = K e^{g_t} (GDN) or Kp F[block] (KDA)
         // (four key channels of one token per step: one 8-byte read of K)
 #pragma unroll 2
