@@ -218,9 +218,8 @@ SSLP_DEVICE void bitonic_stage(Key (&a)[E], int lane) {
             const bool desc = ((p & KK) == 0);
             const bool lower = ((lane & J) == 0);
             const bool keep_max = (lower == desc);
-            const Key mx = mine > other ? mine : other;
-            const Key mn = mine > other ? other : mine;
-            a[e] = keep_max ? mx : mn;
+            // one compare and one select (equal keys: either is the same value)
+            a[e] = ((mine > other) == keep_max) ? mine : other;
         }
     }
 }
@@ -242,6 +241,65 @@ SSLP_DEVICE void bitonic_sort_desc(uint64_t (&a)[E], int lane) {
 template <int E>
 SSLP_DEVICE void bitonic_sort_desc32(uint32_t (&a)[E], int lane) {
     bitonic_merges<2, 64 * E>(a, lane);
+}
+
+// One compare-exchange step at lane distance J < 64 on registers 0..R-1, each
+// register's direction given by desc_of(e) (true: the larger key to the lower
+// lane of each pair).
+template <int J, int R, int E, typename Key, typename Desc>
+SSLP_DEVICE void cx_stage_dir(Key (&a)[E], int lane, Desc desc_of) {
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+        const Key mine = a[e];
+        const Key other = xor_lane_c<J>(mine, lane);
+        const bool keep_max = (((lane & J) == 0) == desc_of(e));
+        a[e] = ((mine > other) == keep_max) ? mine : other;
+    }
+}
+// Sorts the bitonic runs of 2J lanes in registers 0..R-1 (distances J, ..., 1).
+template <int J, int R, int E, typename Key, typename Desc>
+SSLP_DEVICE void merge_runs(Key (&a)[E], int lane, Desc desc_of) {
+    cx_stage_dir<J, R>(a, lane, desc_of);
+    if constexpr (J > 1) merge_runs<J / 2, R>(a, lane, desc_of);
+}
+// Registers 0..M-1 hold sorted runs of KC keys, register e descending when e
+// is even and ascending when odd: pairs of registers are pruned to the KC
+// largest keys of each run pair until one register remains, whose runs are
+// left descending in lanes 0..31 and ascending in lanes 32..63 (KC = 32) or
+// descending (KC = 64).
+template <int KC, int M, int E, typename Key>
+SSLP_DEVICE void topk_prune(Key (&a)[E], int lane) {
+    if constexpr (M > 1) {
+#pragma unroll
+        for (int r = 0; r < M / 2; ++r) a[r] = a[2 * r] > a[2 * r + 1] ? a[2 * r] : a[2 * r + 1];
+        if constexpr (M / 2 > 1) {
+            merge_runs<KC / 2, M / 2>(a, lane, [](int e) { return (e & 1) == 0; });
+        } else {
+            merge_runs<KC / 2, 1>(a, lane, [lane](int) { return KC == 64 || (lane & 32) == 0; });
+        }
+        topk_prune<KC, M / 2>(a, lane);
+    }
+}
+// The KC largest (KC = 32 or 64) of 64*E keys, sorted descending into lanes
+// 0..KC-1 of a[0]; the rest of a[] is left holding keys of no meaning.  Runs of
+// KC keys are sorted as in the full sort, then registers are pruned in pairs:
+// with run A descending and run B ascending, the lane-wise max(A_l, B_l) holds
+// the KC largest keys of A and B as a bitonic sequence (the upper half of the
+// first compare-exchange of a bitonic merge), which log2(KC) more steps sort.
+// For E = 4 and KC = 32 that is 81 register-steps against the full sort's 132.
+template <int KC, int E, typename Key>
+SSLP_DEVICE void bitonic_topk_desc(Key (&a)[E], int lane) {
+    static_assert(KC == 32 || KC == 64, "run length");
+    bitonic_merges<2, KC / 2>(a, lane);  // runs of KC/2, alternating in direction
+    merge_runs<KC / 2, E>(a, lane, [lane](int e) {
+        return E > 1 ? (e & 1) == 0 : (KC == 64 || (lane & 32) == 0);
+    });
+    topk_prune<KC, E>(a, lane);
+    if constexpr (KC == 32) {  // the two halves of a[0] pruned into one run, then sorted
+        const Key other = xor_lane_c<32>(a[0], lane);
+        a[0] = a[0] > other ? a[0] : other;
+        merge_runs<16, 1>(a, lane, [](int) { return true; });
+    }
 }
 
 // element at runtime position p (p = e*64 + lane) of a register-held array,

@@ -10,12 +10,16 @@
 //
 // Algorithm per problem (one wave64):
 //  1. both halves -> keys, wave bitonic sort (EH keys per lane), top-k of each
-//     half is then held by lanes 0..k-1 (k <= 64) and staged in LDS;
+//     half is then held by lanes 0..k-1 (k <= 64) and staged in LDS; with k
+//     and the budget at most KC (32 or 64) only the top KC of each half and of
+//     D (step 2) are sorted (bitonic_topk_desc), else everything is;
 //  2. D = {(i,j) : (i+1)(j+1) <= budget} over the two sorted top-k lists.  With
 //     no rounding ties the top-budget candidates all lie in D, because a pair
 //     outside D is dominated (both ranks smaller or equal) by more than
-//     `budget` pairs whose fp32 sums are >= its own.  D is sorted (ED keys
-//     per lane) and tau = its budget-th key;
+//     `budget` pairs whose fp32 sums are >= its own.  D depends on k and the
+//     budget only: the host lists its (i, j) pairs in the launch arguments
+//     (DMap), lane l forms the keys of positions e*64 + l.  D is sorted (ED
+//     keys per lane) and tau = its budget-th key;
 //  3. F = #{all k^2 candidates with key >= tau} is counted exactly.  F ==
 //     budget proves D's top-budget is the answer.  Otherwise (rounding ties
 //     let a pair outside D win on the slot index) the exact top-budget is
@@ -41,11 +45,17 @@ struct AddrArgs {
 
 constexpr int kWavesPerBlock = 4;
 
-template <typename in_t, int EH, int ED>
-__global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
+// the pairs of D, (i << 8) | j at position p < nD (i, j < 64)
+template <int ED>
+struct DMap {
+    uint16_t ij[64 * ED];
+};
+
+// KC: 32 or 64 when k and the budget are at most KC (top-KC sorts), 0 otherwise
+template <typename in_t, int EH, int ED, int KC>
+__global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a, DMap<ED> dm) {
     __shared__ float s_score[kWavesPerBlock][2][64];
     __shared__ int s_index[kWavesPerBlock][2][64];
-    __shared__ uint64_t s_d[kWavesPerBlock][64 * ED];
 
     const int wv = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -76,8 +86,13 @@ __global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
                 x1[e] = pos < n ? make_key32(to_f32(r1[e]), (uint32_t)pos) : 0u;
                 x2[e] = pos < n ? make_key32(to_f32(r2[e]), (uint32_t)pos) : 0u;
             }
-            bitonic_sort_desc32<EH>(x1, lane);
-            bitonic_sort_desc32<EH>(x2, lane);
+            if constexpr (KC == 0) {
+                bitonic_sort_desc32<EH>(x1, lane);
+                bitonic_sort_desc32<EH>(x2, lane);
+            } else {
+                bitonic_topk_desc<KC>(x1, lane);
+                bitonic_topk_desc<KC>(x2, lane);
+            }
             if (lane < k) {
                 s_score[wv][0][lane] = key32_score(x1[0]);
                 s_index[wv][0][lane] = (int)key32_index(x1[0]);
@@ -92,8 +107,13 @@ __global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
                 x1[e] = pos < n ? make_key(to_f32(r1[e]), (uint32_t)pos) : 0ull;
                 x2[e] = pos < n ? make_key(to_f32(r2[e]), (uint32_t)pos) : 0ull;
             }
-            bitonic_sort_desc<EH>(x1, lane);
-            bitonic_sort_desc<EH>(x2, lane);
+            if constexpr (KC == 0) {
+                bitonic_sort_desc<EH>(x1, lane);
+                bitonic_sort_desc<EH>(x2, lane);
+            } else {
+                bitonic_topk_desc<KC>(x1, lane);
+                bitonic_topk_desc<KC>(x2, lane);
+            }
             if (lane < k) {
                 s_score[wv][0][lane] = key_score(x1[0]);
                 s_index[wv][0][lane] = (int)key_index(x1[0]);
@@ -104,57 +124,39 @@ __global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
     }
     wave_sync();
 
-    // 2. the dominance set D, row i of the first half's ranks holding
-    //    j < min(k, budget / (i+1)) entries
-    {
-        int cnt = 0;
-        if (lane < k) {
-            cnt = budget / (lane + 1);
-            cnt = cnt < k ? cnt : k;
-        }
-        // exclusive prefix sum of cnt over the lanes
-        int incl = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int o = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += o;
-        }
-        const int off = incl - cnt;
-        if (lane < k) {
-            const float sa = s_score[wv][0][lane];
-            const uint32_t ia = (uint32_t)s_index[wv][0][lane];
-            for (int j = 0; j < cnt; ++j) {
-                const float sum = sa + s_score[wv][1][j];  // one fp32 RNE add
-                const uint32_t slot = ia * (uint32_t)n + (uint32_t)s_index[wv][1][j];
-                s_d[wv][off + j] = make_key(sum, slot);
-            }
-        }
-    }
-    wave_sync();
-
+    // 2. the keys of D's pairs, positions e*64 + lane
     uint64_t d[ED];
 #pragma unroll
     for (int e = 0; e < ED; ++e) {
         const int pos = e * 64 + lane;
-        d[e] = pos < a.nD ? s_d[wv][pos] : 0ull;
+        const uint32_t ij = dm.ij[pos];
+        const int i = (int)(ij >> 8), j = (int)(ij & 255u);
+        const float sum = s_score[wv][0][i] + s_score[wv][1][j];  // one fp32 RNE add
+        const uint32_t slot = (uint32_t)s_index[wv][0][i] * (uint32_t)n + (uint32_t)s_index[wv][1][j];
+        d[e] = pos < a.nD ? make_key(sum, slot) : 0ull;
     }
-    bitonic_sort_desc<ED>(d, lane);
+    if constexpr (KC == 0) bitonic_sort_desc<ED>(d, lane);
+    else bitonic_topk_desc<KC>(d, lane);  // (only d[0] is kept: budget <= KC <= 64)
     const uint64_t tau = wave_get<ED>(d, budget - 1);
 
-    // 3. exact count of candidates at or above tau
+    // 3. exact count of candidates at or above tau: 64 / k rows of the k x k
+    //    candidates per pass, lane = (row in pass) * k + column, the column's
+    //    score and index held in registers
     int F = 0;
-    const int kk = k * k;
-    for (int base = 0; base < kk; base += 64) {
-        const int x = base + lane;
-        bool ge = false;
-        if (x < kk) {
-            const int i = x / k, j = x - (x / k) * k;
-            const float sum = s_score[wv][0][i] + s_score[wv][1][j];
-            const uint32_t slot =
-                (uint32_t)s_index[wv][0][i] * (uint32_t)n + (uint32_t)s_index[wv][1][j];
-            ge = make_key(sum, slot) >= tau;
+    {
+        const int rpp = 64 / k;  // rows per pass
+        const int li = lane / k, lj = lane - li * k;
+        const bool lane_ok = li < rpp;
+        const float sb = s_score[wv][1][lane_ok ? lj : 0];
+        const uint32_t ib = (uint32_t)s_index[wv][1][lane_ok ? lj : 0];
+        for (int i0 = 0; i0 < k; i0 += rpp) {
+            const int i = i0 + li;
+            const bool ok = lane_ok && i < k;
+            const int ic = ok ? i : 0;
+            const float sum = s_score[wv][0][ic] + sb;  // one fp32 RNE add, as in step 2
+            const uint32_t slot = (uint32_t)s_index[wv][0][ic] * (uint32_t)n + ib;
+            F += __popcll(__ballot(ok && make_key(sum, slot) >= tau));
         }
-        F += __popcll(__ballot(ge));
     }
 
     int32_t* out_i = a.idx + (size_t)p * budget;
@@ -183,6 +185,7 @@ __global__ __launch_bounds__(256) void sdm_address_kernel(AddrArgs a) {
     }
 
     // rare path: exact top-`budget` of all k^2 candidates by repeated maximum
+    const int kk = k * k;
     uint64_t bound = ~0ull;  // exclusive upper bound (no finite key reaches it)
     float smax = 0.f, z = 0.f;
     float wl0 = 0.f, wl1 = 0.f;  // weight of rank r kept by lane r % 64 (budget <= 128)
@@ -256,29 +259,56 @@ int ceil_pow2_units(int n) {  // smallest power of two >= ceil(n/64), at least 1
     return e;
 }
 
-template <typename in_t, int EH>
+// Set sizes that each KC can meet: with k, budget <= 32 the set D holds at
+// most 119 keys (ED <= 2), with budget <= 64 at most 512; KC = 0 takes every
+// size (dispatch_kc falls back to it).
+constexpr bool ed_instantiated(int KC, int ED) { return KC == 0 || ED <= (KC == 32 ? 2 : 8); }
+
+template <typename in_t, int EH, int ED, int KC>
+void launch_one(dim3 grid, hipStream_t st, const AddrArgs& a) {
+    if constexpr (ed_instantiated(KC, ED)) {
+        DMap<ED> dm{};  // pairs row by row; positions past nD stay (0, 0) and are padded
+        int p = 0;
+        for (int i = 0; i < a.k; ++i) {
+            const int c = a.budget / (i + 1) < a.k ? a.budget / (i + 1) : a.k;
+            for (int j = 0; j < c; ++j) dm.ij[p++] = (uint16_t)((i << 8) | j);
+        }
+        sdm_address_kernel<in_t, EH, ED, KC><<<grid, 256, 0, st>>>(a, dm);
+    }
+}
+
+template <typename in_t, int EH, int KC>
 hipError_t dispatch_ed(int ED, dim3 grid, hipStream_t st, const AddrArgs& a) {
     switch (ED) {
-        case 1: sdm_address_kernel<in_t, EH, 1><<<grid, 256, 0, st>>>(a); break;
-        case 2: sdm_address_kernel<in_t, EH, 2><<<grid, 256, 0, st>>>(a); break;
-        case 4: sdm_address_kernel<in_t, EH, 4><<<grid, 256, 0, st>>>(a); break;
-        case 8: sdm_address_kernel<in_t, EH, 8><<<grid, 256, 0, st>>>(a); break;
-        case 16: sdm_address_kernel<in_t, EH, 16><<<grid, 256, 0, st>>>(a); break;
+        case 1: launch_one<in_t, EH, 1, KC>(grid, st, a); break;
+        case 2: launch_one<in_t, EH, 2, KC>(grid, st, a); break;
+        case 4: launch_one<in_t, EH, 4, KC>(grid, st, a); break;
+        case 8: launch_one<in_t, EH, 8, KC>(grid, st, a); break;
+        case 16: launch_one<in_t, EH, 16, KC>(grid, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <typename in_t>
+template <typename in_t, int KC>
 hipError_t dispatch_eh(int EH, int ED, dim3 grid, hipStream_t st, const AddrArgs& a) {
     switch (EH) {
-        case 1: return dispatch_ed<in_t, 1>(ED, grid, st, a);
-        case 2: return dispatch_ed<in_t, 2>(ED, grid, st, a);
-        case 4: return dispatch_ed<in_t, 4>(ED, grid, st, a);
-        case 8: return dispatch_ed<in_t, 8>(ED, grid, st, a);
-        case 16: return dispatch_ed<in_t, 16>(ED, grid, st, a);
+        case 1: return dispatch_ed<in_t, 1, KC>(ED, grid, st, a);
+        case 2: return dispatch_ed<in_t, 2, KC>(ED, grid, st, a);
+        case 4: return dispatch_ed<in_t, 4, KC>(ED, grid, st, a);
+        case 8: return dispatch_ed<in_t, 8, KC>(ED, grid, st, a);
+        case 16: return dispatch_ed<in_t, 16, KC>(ED, grid, st, a);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <typename in_t>
+hipError_t dispatch_kc(int EH, int ED, dim3 grid, hipStream_t st, const AddrArgs& a) {
+    // top-KC sorts where k and the budget allow them (k <= 64 always)
+    if (a.k <= 32 && a.budget <= 32 && ed_instantiated(32, ED))
+        return dispatch_eh<in_t, 32>(EH, ED, grid, st, a);
+    if (a.budget <= 64 && ed_instantiated(64, ED)) return dispatch_eh<in_t, 64>(EH, ED, grid, st, a);
+    return dispatch_eh<in_t, 0>(EH, ED, grid, st, a);
 }
 
 }  // namespace
@@ -320,8 +350,8 @@ hipError_t launch_sdm_address(int P, int sqrtN, int dtype, const void* s1, const
     const int EH = ceil_pow2_units(sqrtN);
     const int ED = ceil_pow2_units(a.nD);
     dim3 grid((P + kWavesPerBlock - 1) / kWavesPerBlock);
-    if (dtype == 0) return dispatch_eh<float>(EH, ED, grid, st, a);
-    return dispatch_eh<bf16_t>(EH, ED, grid, st, a);
+    if (dtype == 0) return dispatch_kc<float>(EH, ED, grid, st, a);
+    return dispatch_kc<bf16_t>(EH, ED, grid, st, a);
 }
 
 }  // namespace sslp

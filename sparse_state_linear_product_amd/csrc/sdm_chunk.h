@@ -75,5 +75,109 @@ using GeoW64 = Geo<8, 64>;
 
 using namespace lds;  // the LDS / LDS-DMA helpers of the apply kernels
 
+// Workgroup helpers of the plan kernels (256 threads, R elements each at
+// positions p = tid + 256 r, r < R).
+
+// Inclusive prefix sums of the 256 R values v[r] (position tid + 256 r): a
+// scan inside each wavefront (lane shuffles), then the totals of the
+// wavefronts before it from s_tot[4 R] behind one barrier.  s_tot must not be
+// written again before every thread has passed a later barrier.
+template <int R>
+SSLP_DEVICE void block_scan(int (&v)[R], int* s_tot) {
+    const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int o = __shfl_up(v[r], d, 64);
+            v[r] += lane >= d ? o : 0;
+        }
+    }
+    if (lane == 63) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) s_tot[4 * r + w] = v[r];
+    }
+    __syncthreads();
+    int before = 0;  // the totals of position blocks r' < r
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int mine = before, all = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int t = s_tot[4 * r + x];
+            mine += x < w ? t : 0;
+            all += t;
+        }
+        v[r] += mine;
+        before += all;
+    }
+}
+
+// One step (merge size KK, distance J) of the ascending bitonic sort of the
+// 256 R keys k[r] at positions p = tid + 256 r: partners at distances up to
+// 32 are exchanged inside the wavefront (xor_lane_c), at 256 and more inside
+// the thread, at 64 and 128 through LDS (xbuf[] and key[] in turn, one
+// barrier each: a buffer is rewritten only after a barrier that follows every
+// read of it).
+template <int R, int KK, int J>
+SSLP_DEVICE void sort_step(uint64_t (&k)[R], uint64_t* key, uint64_t* xbuf, int& nx) {
+    const int tid = (int)threadIdx.x;
+    auto cx = [&](int r, uint64_t other) {
+        const int p = tid + 256 * r;
+        const bool keep_min = (((p & J) == 0) == ((p & KK) == 0));
+        k[r] = ((k[r] < other) == keep_min) ? k[r] : other;
+    };
+    if constexpr (J >= 256) {
+        constexpr int JR = J / 256;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if constexpr (JR < R) {
+                if ((r & JR) == 0) {
+                    const bool up = ((tid + 256 * r) & KK) == 0;
+                    const uint64_t x = k[r], y = k[r | JR];
+                    const uint64_t lo = x < y ? x : y, hi = x < y ? y : x;
+                    k[r] = up ? lo : hi;
+                    k[r | JR] = up ? hi : lo;
+                }
+            }
+        }
+    } else if constexpr (J >= 64) {
+        uint64_t* buf = (nx++ & 1) ? xbuf : key;
+#pragma unroll
+        for (int r = 0; r < R; ++r) buf[tid + 256 * r] = k[r];
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) cx(r, buf[(tid + 256 * r) ^ J]);
+    } else {
+        const int lane = tid & 63;
+#pragma unroll
+        for (int r = 0; r < R; ++r) cx(r, xor_lane_c<J>(k[r], lane));
+    }
+}
+template <int R, int KK, int J>
+SSLP_DEVICE void sort_steps(uint64_t (&k)[R], uint64_t* key, uint64_t* xbuf, int& nx) {
+    sort_step<R, KK, J>(k, key, xbuf, nx);
+    if constexpr (J > 1) sort_steps<R, KK, J / 2>(k, key, xbuf, nx);
+}
+template <int R, int KK>
+SSLP_DEVICE void sort_merges(uint64_t (&k)[R], uint64_t* key, uint64_t* xbuf, int& nx) {
+    sort_steps<R, KK, KK / 2>(k, key, xbuf, nx);
+    if constexpr (KK < 256 * R) sort_merges<R, KK * 2>(k, key, xbuf, nx);
+}
+// Ascending bitonic sort of the 256 R keys k[r] (position tid + 256 r), every
+// stage resolved at compile time, left in key[] by position (the caller puts a
+// barrier before reading it).  The LDS exchanges number 2 log2(R) + 3, an odd
+// count starting on xbuf[], so the last one reads xbuf[] and key[] is free.
+template <int R>
+SSLP_DEVICE void block_sort_asc(uint64_t (&k)[R], uint64_t* key, uint64_t* xbuf) {
+    static_assert(R == 2 || R == 4, "512 or 1024 keys");
+    int nx = 1;
+    sort_merges<R, 2>(k, key, xbuf, nx);
+    // (key[] was last read in the exchange before the last one, which every
+    // thread finished before the last one's barrier)
+#pragma unroll
+    for (int r = 0; r < R; ++r) key[(int)threadIdx.x + 256 * r] = k[r];
+}
+
 }  // namespace chunk
 }  // namespace sslp

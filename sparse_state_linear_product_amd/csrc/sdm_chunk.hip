@@ -85,7 +85,9 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     __shared__ float s_al[CC], s_be[CC];
     __shared__ float s_A[CC][CC + 1];
     __shared__ int s_fcnt[NE], s_fbeg[NE], s_ffill[NE];
-    __shared__ int s_fwdl[2 * NE];                      // forward rows, grouped per slot
+    __shared__ __align__(8) int s_fwdl[2 * NE];         // forward rows, grouped per slot (first
+                                                        // the sort's exchange buffer)
+    __shared__ int s_tot[8];                            // wavefront totals of the scans
     __shared__ float s_P[NE], s_f[NE];                  // decay and beta w, by entry
     __shared__ uint32_t s_first[NE], s_pk[NE];          // by entry (exception data)
     __shared__ int s_exc[NE];                           // exception flags, then their prefix count
@@ -171,21 +173,11 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     uint32_t* out = a.plan + (size_t)blockIdx.x * PL_WORDS;
 
     // S2: bitonic sort of the 512 keys, ascending
-    for (int k = 2; k <= NE; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int x = tid; x < NE; x += 256) {
-                const int y = x ^ j;
-                if (y > x) {
-                    const uint64_t kx = key[x], ky = key[y];
-                    const bool up = (x & k) == 0;
-                    if ((kx > ky) == up) {
-                        key[x] = ky;
-                        key[y] = kx;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+    static_assert(NE == 512, "two keys per thread");
+    {
+        uint64_t kr[2] = {key[tid], key[tid + 256]};
+        chunk::block_sort_asc<2>(kr, key, reinterpret_cast<uint64_t*>(s_fwdl));
+        __syncthreads();
     }
 
     // S3: groups of equal slot (a slot is written at most once per token, so
@@ -210,15 +202,12 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         s_scan[p] = (valid && gs == p) ? 1 : 0;
     }
     __syncthreads();
-    // inclusive prefix count of group starts (Hillis-Steele)
-    for (int off = 1; off < NE; off <<= 1) {
-        int v0 = 0, v1 = 0;
-        const int p0 = tid, p1 = tid + 256;
-        v0 = s_scan[p0] + (p0 >= off ? s_scan[p0 - off] : 0);
-        v1 = s_scan[p1] + (p1 >= off ? s_scan[p1 - off] : 0);
-        __syncthreads();
-        s_scan[p0] = v0;
-        s_scan[p1] = v1;
+    // inclusive prefix count of group starts
+    {
+        int v[2] = {s_scan[tid], s_scan[tid + 256]};
+        chunk::block_scan<2>(v, s_tot);
+        s_scan[tid] = v[0];
+        s_scan[tid + 256] = v[1];
         __syncthreads();
     }
 
@@ -273,16 +262,12 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         }
     }
     __syncthreads();
-    // exclusive prefix of the forward counts over sorted positions
-    for (int p = tid; p < NE; p += 256) s_fbeg[p] = s_fcnt[p];
-    __syncthreads();
-    for (int off = 1; off < NE; off <<= 1) {
-        const int p0 = tid, p1 = tid + 256;
-        const int v0 = s_fbeg[p0] + (p0 >= off ? s_fbeg[p0 - off] : 0);
-        const int v1 = s_fbeg[p1] + (p1 >= off ? s_fbeg[p1 - off] : 0);
-        __syncthreads();
-        s_fbeg[p0] = v0;
-        s_fbeg[p1] = v1;
+    // inclusive prefix of the forward counts over sorted positions
+    {
+        int v[2] = {s_fcnt[tid], s_fcnt[tid + 256]};
+        chunk::block_scan<2>(v, s_tot);
+        s_fbeg[tid] = v[0];
+        s_fbeg[tid + 256] = v[1];
         __syncthreads();
     }
     for (int x = 0; x < 4; ++x) {
@@ -353,13 +338,11 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     }
     __syncthreads();
     // inclusive prefix count of exception flags (entry order)
-    for (int off = 1; off < NE; off <<= 1) {
-        const int p0 = tid, p1 = tid + 256;
-        const int v0 = s_exc[p0] + (p0 >= off ? s_exc[p0 - off] : 0);
-        const int v1 = s_exc[p1] + (p1 >= off ? s_exc[p1 - off] : 0);
-        __syncthreads();
-        s_exc[p0] = v0;
-        s_exc[p1] = v1;
+    {
+        int v[2] = {s_exc[tid], s_exc[tid + 256]};
+        chunk::block_scan<2>(v, s_tot);
+        s_exc[tid] = v[0];
+        s_exc[tid + 256] = v[1];
         __syncthreads();
     }
     {

@@ -81,6 +81,8 @@ __global__ __launch_bounds__(256) void sdm_chunk_bwd_plan_kernel(BwdPlanArgs a) 
     constexpr int CC = G::CC, NW = G::NW, NR = G::NR, LOGNW = G::LOGNW;
     __shared__ uint64_t key[NEV];  // (slot << 12 | token << 7 | kind << 6 | index), sorted
     __shared__ int s_scan[NEV];    // group starts, then their inclusive prefix count
+    __shared__ uint64_t s_xbuf[NEV];  // the sort's exchange buffer
+    __shared__ int s_tot[4 * (NEV / 256)];  // wavefront totals of the scan
     __shared__ float s_d[NE], s_bw[NE];  // decay and beta w of write entry t*NW + i
     __shared__ float s_al[CC], s_be[CC];
     __shared__ int s_bad;
@@ -148,21 +150,13 @@ __global__ __launch_bounds__(256) void sdm_chunk_bwd_plan_kernel(BwdPlanArgs a) 
     __syncthreads();
 
     // S2: bitonic sort of the keys, ascending (invalid keys last)
-    for (int k = 2; k <= NEV; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int x = tid; x < NEV; x += 256) {
-                const int y = x ^ j;
-                if (y > x) {
-                    const uint64_t kx = key[x], ky = key[y];
-                    const bool up = (x & k) == 0;
-                    if ((kx > ky) == up) {
-                        key[x] = ky;
-                        key[y] = kx;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+    static_assert(NEV == 1024, "four keys per thread");
+    {
+        uint64_t kr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kr[r] = key[tid + 256 * r];
+        chunk::block_sort_asc<4>(kr, key, s_xbuf);
+        __syncthreads();
     }
 
     // S3: slot groups (equal slot) and their inclusive prefix count
@@ -170,14 +164,11 @@ __global__ __launch_bounds__(256) void sdm_chunk_bwd_plan_kernel(BwdPlanArgs a) 
     for (int p = tid; p < NEV; p += 256)
         s_scan[p] = (p < nev && (p == 0 || (key[p - 1] >> 12) != (key[p] >> 12))) ? 1 : 0;
     __syncthreads();
-    for (int off = 1; off < NEV; off <<= 1) {
+    {
         int v[NEV / 256];
 #pragma unroll
-        for (int x = 0; x < NEV / 256; ++x) {
-            const int p = tid + 256 * x;
-            v[x] = s_scan[p] + (p >= off ? s_scan[p - off] : 0);
-        }
-        __syncthreads();
+        for (int x = 0; x < NEV / 256; ++x) v[x] = s_scan[tid + 256 * x];
+        chunk::block_scan<NEV / 256>(v, s_tot);
 #pragma unroll
         for (int x = 0; x < NEV / 256; ++x) s_scan[tid + 256 * x] = v[x];
         __syncthreads();
