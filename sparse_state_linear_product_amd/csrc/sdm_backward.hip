@@ -299,6 +299,60 @@ __global__ __launch_bounds__(64 * kAbWaves) void sdm_address_bwd_kernel(
     }
 }
 
+// The same gradients for sqrtN <= 256: lane m (entry m < budget <= 64) sums
+// the d of every entry of its row a_m (and of its column b_m) in entry order,
+// so each sum is the one the loop above forms; the first entry of a row
+// writes it into the wavefront's zeroed LDS copy of ds1 (ds2), which is then
+// stored whole.  About a fifth of the instructions of the loop above.
+constexpr int kAbMaxN = 256;
+__global__ __launch_bounds__(64 * kAbWaves) void sdm_address_bwd_small_kernel(
+    int P, int sqrtN, int budget, const int32_t* __restrict__ idx, const float* __restrict__ wt,
+    const float* __restrict__ dwt, float* __restrict__ ds1, float* __restrict__ ds2) {
+    __shared__ float s_g[kAbWaves][2][kAbMaxN];
+    __shared__ float s_ds[kAbWaves][64];
+    __shared__ int s_ab[kAbWaves][64];  // a_m | b_m << 16
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long long p = (long long)blockIdx.x * kAbWaves + wv;
+    if (p >= P) return;  // whole wavefronts leave together; no block barrier below
+    const bool on = lane < budget;
+    const int m = on ? lane : 0;
+    const int n = idx[(size_t)p * budget + m];
+    const float w = wt[(size_t)p * budget + m], dw = dwt[(size_t)p * budget + m];
+    float dot = on ? w * dw : 0.f;  // the first fmaf of the loop above is this product
+    // (the wave sum in the same lane pattern as the loop above: one term per lane)
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) dot += xor_lane_f(dot, s, lane);
+    // an entry whose slot lies outside [0, sqrtN^2) joins no row or column
+    const bool ok = on && (unsigned)n < (unsigned)(sqrtN * sqrtN);
+    const int am = ok ? n / sqrtN : 0, bm = ok ? n - am * sqrtN : 0;
+    const float d = w * (dw - dot);
+    s_ds[wv][lane] = on ? d : 0.f;
+    s_ab[wv][lane] = ok ? (am | (bm << 16)) : -1;
+    for (int x = lane; x < sqrtN; x += 64) {
+        s_g[wv][0][x] = 0.f;
+        s_g[wv][1][x] = 0.f;
+    }
+    wave_sync();
+    float g1 = 0.f, g2 = 0.f;
+    bool first1 = true, first2 = true;
+    for (int q = 0; q < budget; ++q) {
+        const int ab = s_ab[wv][q];
+        const float dq = s_ds[wv][q];
+        const bool same1 = (ab & 0xFFFF) == am, same2 = (ab >> 16) == bm;
+        g1 += same1 ? dq : 0.f;
+        g2 += same2 ? dq : 0.f;
+        first1 = first1 && !(same1 && q < lane);
+        first2 = first2 && !(same2 && q < lane);
+    }
+    if (ok && first1) s_g[wv][0][am] = g1;
+    if (ok && first2) s_g[wv][1][bm] = g2;
+    wave_sync();
+    for (int x = lane; x < sqrtN; x += 64) {
+        ds1[(size_t)p * sqrtN + x] = s_g[wv][0][x];
+        ds2[(size_t)p * sqrtN + x] = s_g[wv][1][x];
+    }
+}
+
 template <typename io_t>
 hipError_t dispatch_bwd(int NL, dim3 grid, hipStream_t st, const SdmBwdArgs& a) {
     switch (NL) {
@@ -345,8 +399,12 @@ hipError_t launch_sdm_address_backward(int P, int sqrtN, int budget, const int32
     if (P <= 0) return hipSuccess;
     if (budget < 1 || budget > kMaxBudget || sqrtN < 1) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((P + kAbWaves - 1) / kAbWaves);
-    sdm_address_bwd_kernel<<<grid, 64 * kAbWaves, 0, st>>>(P, sqrtN, budget, idx, wt, dwt, ds1,
-                                                           ds2);
+    if (sqrtN <= kAbMaxN && budget <= 64)
+        sdm_address_bwd_small_kernel<<<grid, 64 * kAbWaves, 0, st>>>(P, sqrtN, budget, idx, wt, dwt,
+                                                                     ds1, ds2);
+    else
+        sdm_address_bwd_kernel<<<grid, 64 * kAbWaves, 0, st>>>(P, sqrtN, budget, idx, wt, dwt, ds1,
+                                                               ds2);
     return hipGetLastError();
 }
 
