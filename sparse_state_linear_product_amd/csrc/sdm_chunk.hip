@@ -88,6 +88,8 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     __shared__ __align__(8) int s_fwdl[2 * NE];         // forward rows, grouped per slot (first
                                                         // the sort's exchange buffer)
     __shared__ int s_tot[8];                            // wavefront totals of the scans
+    __shared__ uint32_t s_fm[NE / 32];                  // bit i of word e / 32: entry e is its slot's first visit
+    __shared__ uint32_t s_rnz[NE / 32];                 // bit i of word e / 32: read entry e follows a write visit
     __shared__ float s_P[NE], s_f[NE];                  // decay and beta w, by entry
     __shared__ uint32_t s_first[NE], s_pk[NE];          // by entry (exception data)
     __shared__ int s_exc[NE];                           // exception flags, then their prefix count
@@ -212,51 +214,78 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     }
 
     // S4: read entries: the write visits of their slot at or before their token
-    for (int e = tid; e < CC * NR; e += 256) {
-        const int t = e >> LOGNW;
-        const int sl = s_ir[e];
-        int rgs = 0, rend = 0;
-        if (sl >= 0) {
-            // lower bound of (slot << 9) among the sorted keys
-            const uint64_t want = (uint64_t)(uint32_t)sl << 9;
-            int lo = 0, hi = NE;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (key[mid] < want) lo = mid + 1;
-                else hi = mid;
-            }
-            if (lo < NE && key[lo] != NONE && (key[lo] >> 9) == (uint64_t)(uint32_t)sl) {
-                rgs = lo;
-                rend = lo;
-                const int ge = s_ge[lo];
+    // (two entries per thread, their lower bounds of (slot << 9) among the
+    // sorted keys found side by side in log2(NE) fixed steps)
+    static_assert(CC * NR == 2 * 256, "two read entries per thread");
+    {
+        const int lane = tid & 63;
+        int sl[2], lo[2] = {0, 0};
+        uint64_t want[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            sl[r] = s_ir[tid + 256 * r];
+            want[r] = (uint64_t)(uint32_t)sl[r] << 9;
+        }
+#pragma unroll
+        for (int step = NE / 2; step >= 1; step >>= 1) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) lo[r] += key[lo[r] + step - 1] < want[r] ? step : 0;
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int e = tid + 256 * r;
+            const int t = e >> LOGNW;
+            int rgs = 0, rend = 0;
+            if (sl[r] >= 0 && lo[r] < NE && key[lo[r]] != NONE &&
+                (key[lo[r]] >> 9) == (uint64_t)(uint32_t)sl[r]) {
+                rgs = lo[r];
+                rend = lo[r];
+                const int ge = s_ge[lo[r]];
                 while (rend < ge && (int)((key[rend] & 511u) >> LOGNW) <= t) ++rend;
             }
+            s_rgs[e] = rgs;
+            s_rend[e] = rend;
+            const uint64_t bal = __ballot(rend > rgs);
+            if ((lane & 31) == 0) s_rnz[e >> 5] = (uint32_t)(bal >> (lane & 32));
         }
-        s_rgs[e] = rgs;
-        s_rend[e] = rend;
     }
 
     // S5: forward targets: rows of the next chunk whose slot this chunk writes
     // (counted per group, at the group's last visit)
     const int t1 = t0 + CC;
     const int ntok1 = c + 1 < nch ? (a.T - t1 < CC ? a.T - t1 : CC) : 0;
+    // (the four rows of a thread loaded first, then searched side by side)
     int fgrp[4];
-    for (int x = 0; x < 4; ++x) {
-        const int ne = tid + 256 * x;  // 0..1023 as (t, q)
-        const int t = ne / NQ, q = ne & (NQ - 1);
-        fgrp[x] = -1;
-        if (t < ntok1) {
-            const size_t bth = ((size_t)b * a.T + t1 + t) * a.H + h;
-            const int sl = q < NW ? a.idx_w[bth * NW + q] : a.idx_r[bth * NR + (q - NW)];
-            const uint64_t want = (uint64_t)(uint32_t)sl << 9;
-            int lo = 0, hi = NE;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (key[mid] < want) lo = mid + 1;
-                else hi = mid;
+    {
+        int slv[4], lo[4];
+        uint64_t want[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int ne = tid + 256 * x;  // 0..1023 as (t, q)
+            const int t = ne / NQ, q = ne & (NQ - 1);
+            slv[x] = -1;
+            if (t < ntok1) {
+                const size_t bth = ((size_t)b * a.T + t1 + t) * a.H + h;
+                slv[x] = q < NW ? a.idx_w[bth * NW + q] : a.idx_r[bth * NR + (q - NW)];
             }
-            if (lo < NE && key[lo] != NONE && (key[lo] >> 9) == (uint64_t)(uint32_t)sl) {
-                fgrp[x] = s_ge[lo] - 1;
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            want[x] = (uint64_t)(uint32_t)slv[x] << 9;
+            lo[x] = 0;
+        }
+#pragma unroll
+        for (int step = NE / 2; step >= 1; step >>= 1) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) lo[x] += key[lo[x] + step - 1] < want[x] ? step : 0;
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int t = (tid + 256 * x) / NQ;
+            fgrp[x] = -1;
+            if (t < ntok1 && lo[x] < NE && key[lo[x]] != NONE &&
+                (key[lo[x]] >> 9) == (uint64_t)(uint32_t)slv[x]) {
+                fgrp[x] = s_ge[lo[x]] - 1;
                 atomicAdd(&s_fcnt[fgrp[x]], 1);
             }
         }
@@ -323,18 +352,26 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
     __syncthreads();
     // token masks of last and first visits and of exception records, word wd of
     // token t covering entries (t, 32 wd + i)
-    if (tid < CC * G::NMW) {
-        const int t = tid / G::NMW, wd = tid % G::NMW;
-        uint32_t lm = 0u, fm = 0u, em = 0u;
-        for (int i = 0; i < 32 && t < ntok; ++i) {
-            const int e = t * NW + 32 * wd + i, p = s_pos[e];
-            lm |= (s_ge[p] - 1 == p) ? (1u << i) : 0u;
-            fm |= (s_gs[p] == p) ? (1u << i) : 0u;
-            em |= s_exc[e] ? (1u << i) : 0u;
+    // (one entry per lane, words from wavefront ballots: word e / 32 holds
+    // entries 32 (e / 32) .. + 31, i.e. word t * NMW + wd of token t)
+    {
+        const int lane = tid & 63;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int e = tid + 256 * r;
+            const bool valid = (e >> LOGNW) < ntok;
+            const int p = valid ? s_pos[e] : 0;
+            const uint64_t bl = __ballot(valid && s_ge[p] - 1 == p);
+            const uint64_t bf = __ballot(valid && s_gs[p] == p);
+            const uint64_t bx = __ballot(valid && s_exc[e] != 0);
+            if ((lane & 31) == 0) {
+                const int wdi = e >> 5, sh = lane & 32;
+                out[PL_LAST + wdi] = (uint32_t)(bl >> sh);
+                out[PL_FIRST + wdi] = (uint32_t)(bf >> sh);
+                out[PL_EXC + wdi] = (uint32_t)(bx >> sh);
+                s_fm[wdi] = (uint32_t)(bf >> sh);
+            }
         }
-        out[PL_LAST + tid] = lm;
-        out[PL_FIRST + tid] = fm;
-        out[PL_EXC + tid] = em;
     }
     __syncthreads();
     // inclusive prefix count of exception flags (entry order)
@@ -389,31 +426,38 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         const int t = tid / CC, tau = tid % CC;
         float av = 0.f, bv = 0.f;
         if (t < ntok && tau <= t) {
+            // (only entries with an earlier visit of their slot in the chunk,
+            // and read entries after a write visit, contribute: the others
+            // are skipped by their mask bits, in the same entry order)
             if (a.mode == 0 && tau < t) {
-                for (int i = 0; i < NW; ++i) {
-                    const int e = t * NW + i;
-                    const int p = s_pos[e];
-                    float between = 1.f;  // decays of the visits strictly between
-                    for (int l = p - 1; l >= s_gs[p]; --l) {
-                        const int el = (int)(key[l] & 511u);
-                        if ((el >> LOGNW) == tau) {
-                            av += s_al[t] * s_ww[e] * between * s_be[tau] * s_ww[el];
-                            break;
+                for (int wd = 0; wd < G::NMW; ++wd) {
+                    for (uint32_t todo = ~s_fm[t * G::NMW + wd]; todo != 0u; todo &= todo - 1u) {
+                        const int e = t * NW + 32 * wd + __builtin_ctz(todo);
+                        const int p = s_pos[e];
+                        float between = 1.f;  // decays of the visits strictly between
+                        for (int l = p - 1; l >= s_gs[p]; --l) {
+                            const int el = (int)(key[l] & 511u);
+                            if ((el >> LOGNW) == tau) {
+                                av += s_al[t] * s_ww[e] * between * s_be[tau] * s_ww[el];
+                                break;
+                            }
+                            between *= s_d[l];
                         }
-                        between *= s_d[l];
                     }
                 }
             }
-            for (int k = 0; k < NR; ++k) {
-                const int e = t * NR + k;
-                float after = 1.f;  // decays of the visits after tau's, up to token t
-                for (int l = s_rend[e] - 1; l >= s_rgs[e]; --l) {
-                    const int el = (int)(key[l] & 511u);
-                    if ((el >> LOGNW) == tau) {
-                        bv += s_wr[e] * after * s_be[tau] * s_ww[el];
-                        break;
+            for (int wd = 0; wd < NR / 32; ++wd) {
+                for (uint32_t todo = s_rnz[t * (NR / 32) + wd]; todo != 0u; todo &= todo - 1u) {
+                    const int e = t * NR + 32 * wd + __builtin_ctz(todo);
+                    float after = 1.f;  // decays of the visits after tau's, up to token t
+                    for (int l = s_rend[e] - 1; l >= s_rgs[e]; --l) {
+                        const int el = (int)(key[l] & 511u);
+                        if ((el >> LOGNW) == tau) {
+                            bv += s_wr[e] * after * s_be[tau] * s_ww[el];
+                            break;
+                        }
+                        after *= s_d[l];
                     }
-                    after *= s_d[l];
                 }
             }
         }
