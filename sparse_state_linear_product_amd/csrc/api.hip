@@ -649,6 +649,11 @@ int sdm_backward(const sslp_sdm_shape* s, int dtype, int residual_mode, const in
     } else if (int rc = hip_status(sslp::launch_sdm_update_backward(a, st), "sdm backward launch")) {
         return rc;
     }
+    if (dsw1 && dsr1)
+        return hip_status(sslp::launch_sdm_address_backward_pair(
+                              (int)P, s->sqrtN, s->W, idx_w, wt_w, a.dwt_w, dsw1, dsw2, s->R,
+                              idx_r, wt_r, a.dwt_r, dsr1, dsr2, st),
+                          "sdm address backward launch");
     if (dsw1)
         if (int rc = hip_status(sslp::launch_sdm_address_backward((int)P, s->sqrtN, s->W, idx_w,
                                                                   wt_w, a.dwt_w, dsw1, dsw2, st),

@@ -99,6 +99,12 @@ hipError_t launch_sdm_update_backward(const SdmBwdArgs& a, hipStream_t st);
 hipError_t launch_sdm_address_backward(int P, int sqrtN, int budget, const int32_t* idx,
                                        const float* wt, const float* dwt, float* ds1, float* ds2,
                                        hipStream_t st);
+// the same for the write and the read sets of a step, in one launch where they fit
+hipError_t launch_sdm_address_backward_pair(int P, int sqrtN, int W, const int32_t* idx_w,
+                                            const float* wt_w, const float* dwt_w, float* dsw1,
+                                            float* dsw2, int R, const int32_t* idx_r,
+                                            const float* wt_r, const float* dwt_r, float* dsr1,
+                                            float* dsr2, hipStream_t st);
 
 // chunk-parallel recurrence (sdm_chunk.hip): supported shapes, workspace for
 // its per-chunk plans, and the launcher (plan kernel + apply kernel)

@@ -304,15 +304,35 @@ __global__ __launch_bounds__(64 * kAbWaves) void sdm_address_bwd_kernel(
 // so each sum is the one the loop above forms; the first entry of a row
 // writes it into the wavefront's zeroed LDS copy of ds1 (ds2), which is then
 // stored whole.  About a fifth of the instructions of the loop above.
+// The write and read sets of a step go in one launch: workgroups below nblk0
+// take set 0, the others set 1.
 constexpr int kAbMaxN = 256;
-__global__ __launch_bounds__(64 * kAbWaves) void sdm_address_bwd_small_kernel(
-    int P, int sqrtN, int budget, const int32_t* __restrict__ idx, const float* __restrict__ wt,
-    const float* __restrict__ dwt, float* __restrict__ ds1, float* __restrict__ ds2) {
+struct AbSet {
+    const int32_t* idx;
+    const float* wt;
+    const float* dwt;
+    float* ds1;
+    float* ds2;
+    int budget;
+};
+struct AbPair {
+    AbSet set[2];
+    int P, sqrtN, nblk0;
+};
+__global__ __launch_bounds__(64 * kAbWaves) void sdm_address_bwd_small_kernel(AbPair ab) {
     __shared__ float s_g[kAbWaves][2][kAbMaxN];
     __shared__ float s_ds[kAbWaves][64];
     __shared__ int s_ab[kAbWaves][64];  // a_m | b_m << 16
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long long p = (long long)blockIdx.x * kAbWaves + wv;
+    const int si = (int)blockIdx.x >= ab.nblk0 ? 1 : 0;
+    const AbSet& S = ab.set[si];
+    const int P = ab.P, sqrtN = ab.sqrtN, budget = S.budget;
+    const int32_t* __restrict__ idx = S.idx;
+    const float* __restrict__ wt = S.wt;
+    const float* __restrict__ dwt = S.dwt;
+    float* __restrict__ ds1 = S.ds1;
+    float* __restrict__ ds2 = S.ds2;
+    const long long p = (long long)((int)blockIdx.x - si * ab.nblk0) * kAbWaves + wv;
     if (p >= P) return;  // whole wavefronts leave together; no block barrier below
     const bool on = lane < budget;
     const int m = on ? lane : 0;
@@ -399,12 +419,32 @@ hipError_t launch_sdm_address_backward(int P, int sqrtN, int budget, const int32
     if (P <= 0) return hipSuccess;
     if (budget < 1 || budget > kMaxBudget || sqrtN < 1) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((P + kAbWaves - 1) / kAbWaves);
-    if (sqrtN <= kAbMaxN && budget <= 64)
-        sdm_address_bwd_small_kernel<<<grid, 64 * kAbWaves, 0, st>>>(P, sqrtN, budget, idx, wt, dwt,
-                                                                     ds1, ds2);
-    else
+    if (sqrtN <= kAbMaxN && budget <= 64) {
+        const AbSet one{idx, wt, dwt, ds1, ds2, budget};
+        sdm_address_bwd_small_kernel<<<grid, 64 * kAbWaves, 0, st>>>(AbPair{{one, one}, P, sqrtN, (int)grid});
+    } else
         sdm_address_bwd_kernel<<<grid, 64 * kAbWaves, 0, st>>>(P, sqrtN, budget, idx, wt, dwt, ds1,
                                                                ds2);
+    return hipGetLastError();
+}
+
+hipError_t launch_sdm_address_backward_pair(int P, int sqrtN, int W, const int32_t* idx_w,
+                                            const float* wt_w, const float* dwt_w, float* dsw1,
+                                            float* dsw2, int R, const int32_t* idx_r,
+                                            const float* wt_r, const float* dwt_r, float* dsr1,
+                                            float* dsr2, hipStream_t st) {
+    if (P <= 0) return hipSuccess;
+    if (sqrtN > kAbMaxN || W > 64 || R > 64) {  // the looped kernel, one launch per set
+        const hipError_t e =
+            launch_sdm_address_backward(P, sqrtN, W, idx_w, wt_w, dwt_w, dsw1, dsw2, st);
+        if (e != hipSuccess) return e;
+        return launch_sdm_address_backward(P, sqrtN, R, idx_r, wt_r, dwt_r, dsr1, dsr2, st);
+    }
+    if (W < 1 || R < 1 || sqrtN < 1) return hipErrorInvalidValue;
+    const int nblk = (P + kAbWaves - 1) / kAbWaves;
+    const AbPair ab{{AbSet{idx_w, wt_w, dwt_w, dsw1, dsw2, W}, AbSet{idx_r, wt_r, dwt_r, dsr1, dsr2, R}},
+                    P, sqrtN, nblk};
+    sdm_address_bwd_small_kernel<<<(unsigned)(2 * nblk), 64 * kAbWaves, 0, st>>>(ab);
     return hipGetLastError();
 }
 

@@ -480,14 +480,15 @@ __global__ __launch_bounds__(256) void sdm_chunk_plan_kernel(PlanArgs a) {
         }
     }
 
-    // S10: byte offsets of every staged row
+    // S10: byte offsets of every staged row (the slots from LDS: a write
+    // entry's in its sorted key, a read entry's in s_ir)
     for (int x = tid; x < CC * NQ; x += 256) {
         const int t = x / NQ, q = x & (NQ - 1);
         uint32_t off = 0u;
         if (t < ntok) {
-            const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
-            const int sl = q < NW ? a.idx_w[bth * NW + q] : a.idx_r[bth * NR + (q - NW)];
-            off = (uint32_t)sl * (uint32_t)a.dv * 4u;
+            const uint32_t sl = q < NW ? (uint32_t)(key[s_pos[t * NW + q]] >> 9)
+                                       : (uint32_t)s_ir[t * NR + (q - NW)];
+            off = sl * (uint32_t)a.dv * 4u;
         }
         out[G::offs_word(q, t)] = off;
     }

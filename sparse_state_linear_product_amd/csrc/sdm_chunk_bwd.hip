@@ -98,11 +98,12 @@ __global__ __launch_bounds__(256) void sdm_chunk_bwd_plan_kernel(BwdPlanArgs a) 
     if (tid == 0) s_bad = 0;
     __syncthreads();
     const int nt = a.T - t0 < CC ? a.T - t0 : CC;
+    // every load issued before any test (rows past the end load the last
+    // token's indices and weights, then unused); the keys below reuse them
+    static_assert(NE % 256 == 0, "whole passes of the 256 threads");
+    unsigned sw[NE / 256], sr[NE / 256];
+    float ww[NE / 256];
     {
-        // every load issued before any test (rows past the end load the last
-        // token's indices, then unused)
-        static_assert(NE % 256 == 0, "whole passes of the 256 threads");
-        unsigned sw[NE / 256], sr[NE / 256];
 #pragma unroll
         for (int r = 0; r < NE / 256; ++r) {
             const int e = tid + 256 * r;
@@ -110,6 +111,7 @@ __global__ __launch_bounds__(256) void sdm_chunk_bwd_plan_kernel(BwdPlanArgs a) 
             const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
             sw[r] = (unsigned)a.idx_w[bth * NW + (e & (NW - 1))];
             sr[r] = (unsigned)a.idx_r[bth * NR + (e & (NW - 1))];
+            ww[r] = a.wt_w[bth * NW + (e & (NW - 1))];
         }
         bool bad = false;
 #pragma unroll
@@ -129,17 +131,19 @@ __global__ __launch_bounds__(256) void sdm_chunk_bwd_plan_kernel(BwdPlanArgs a) 
     __syncthreads();
 
     // S1: one key per entry: writes (kind 0) at x < NE, reads (kind 1) above
-    for (int x = tid; x < NEV; x += 256) {
+    static_assert(NEV == 4 * 256 && NE == 2 * 256, "x = tid + 256 j: writes for j < 2");
+#pragma unroll
+    for (int jx = 0; jx < NEV / 256; ++jx) {
+        const int x = tid + 256 * jx;
         const int rd = x >= NE ? 1 : 0;
         const int e = x - rd * NE;
         const int t = e >> LOGNW, i = e & (NW - 1);
         uint64_t k = NONE;
         float w = 0.f;
         if (t < ntok) {
-            const size_t bth = ((size_t)b * a.T + t0 + t) * a.H + h;
-            const uint32_t sl = (uint32_t)(rd ? a.idx_r[bth * NR + i] : a.idx_w[bth * NW + i]);
+            const uint32_t sl = rd ? sr[jx & 1] : sw[jx & 1];
             k = ((uint64_t)sl << 12) | ((uint64_t)t << 7) | ((uint64_t)rd << 6) | (uint64_t)i;
-            if (!rd) w = a.wt_w[bth * NW + i];
+            if (!rd) w = ww[jx & 1];
         }
         key[x] = k;
         if (!rd) {
