@@ -203,17 +203,22 @@ SSLP_DEVICE void wg_addr_select(const WgAddrProblem& pr, int t, Sm& sm, int32_t*
     }
     block_sync_lds();
     // 3. exact count of all k^2 candidates at or above tau, spread over the
-    //    group's four wavefronts (candidate x = (i, j), i = x / k, j = x % k)
+    //    group's four wavefronts: kAddrGroup / k rows of candidates (i, j) per
+    //    pass, thread t on row t / k of the pass and column t % k
     {
         const uint64_t tau = sm.tau;
+        const int rpp = kAddrGroup / k;
+        const int li = t / k, lj = t - li * k;
+        const bool t_ok = li < rpp;
+        const float sb = sm.hsc[1][t_ok ? lj : 0];
+        const uint32_t ib = (uint32_t)sm.hix[1][t_ok ? lj : 0];
         int cnt = 0;
-        for (int x0 = 0; x0 < k * k; x0 += kAddrGroup) {
-            const int x = x0 + t;
-            const bool in = x < k * k;
-            const int i = in ? x / k : 0, j = in ? x - (x / k) * k : 0;
-            const float sum = sm.hsc[0][i] + sm.hsc[1][j];  // one fp32 RNE add
-            const bool ge = in && make_key(sum, (uint32_t)sm.hix[0][i] * (uint32_t)n +
-                                                    (uint32_t)sm.hix[1][j]) >= tau;
+        for (int i0 = 0; i0 < k; i0 += rpp) {
+            const int i = i0 + li;
+            const bool in = t_ok && i < k;
+            const int ic = in ? i : 0;
+            const float sum = sm.hsc[0][ic] + sb;  // one fp32 RNE add
+            const bool ge = in && make_key(sum, (uint32_t)sm.hix[0][ic] * (uint32_t)n + ib) >= tau;
             cnt += __popcll(__ballot(ge));
         }
         if (lane == 0) sm.Fw[wv] = cnt;
