@@ -166,6 +166,18 @@ def _address_cases():
     g3 = r.standard_normal((3, 300, 2, 240)).astype(np.float32)
     g4 = r.standard_normal((3, 300, 2, 240)).astype(np.float32)
     cases.append(("gauss_240_k32_w32_P1800", g3, g4, 32, 32))
+    # the wavefront kernel's top-64 sorts (k, budget <= 64) with dominance sets of
+    # one, two and four registers, its full sorts (budget > 64), a budget below k,
+    # and halves of 100 scores (two keys per lane)
+    cases.append(("quantized_240_k48_w64_P1600", q3, q4, 48, 64))
+    cases.append(("gauss_240_k64_w48_P1800", g3, g4, 64, 48))
+    cases.append(("gauss_240_k8_w64_P1800", g3, g4, 8, 64))
+    cases.append(("gauss_240_k33_w33_P1800", g3, g4, 33, 33))
+    cases.append(("quantized_240_k16_w100_P1600", q3, q4, 16, 100))
+    cases.append(("quantized_240_k32_w20_P1600", q3, q4, 32, 20))
+    g5 = r.standard_normal((2, 300, 2, 100)).astype(np.float32)
+    g6 = r.standard_normal((2, 300, 2, 100)).astype(np.float32)
+    cases.append(("gauss_100_k32_w32_P1200", g5, g6, 32, 32))
     return cases
 
 
